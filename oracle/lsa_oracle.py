@@ -1,0 +1,328 @@
+"""Float64 numpy oracle of the LSA hot path (index -> select -> attend).
+
+TEST INFRASTRUCTURE ONLY: used by tests/, the smoke check and the benchmark's
+CPU baseline; never by the product path.  Shares no code with the HIP library.
+
+Sources (page title, section):
+  [P3]  "LongCat-2.0: how Meituan trained a 1.6T coding model without Nvidia GPUs"
+        (molayo1419.me), section "The sparse attention problem at 1M tokens":
+        LSA extends DeepSeek Sparse Attention with Streaming-aware Indexing (SI),
+        Cross-Layer Indexing (CLI) and Hierarchical Indexing (HI); MTP extension.
+  [P5]  "LongCat-Flash-Lite-Sparse" summary (aitrends.kr), sections "Good to know"
+        and "Technical features": SI splits the selection budget into a fixed sink
+        and a local sliding window; CLI reuses one index result in several adjacent
+        layers; HI retrieves coarse candidate blocks, then selects fine tokens inside
+        them, and can be switched on at inference without retraining.
+  [P1]  "LongCat-2.0" summary (aitrends.kr), "Technical features": LSA avoids full
+        attention over all token pairs and attends over a selected set.
+
+Readings where the pages are silent (the pages give no formula at all):
+  R1  indexer score I[t,s] = sum_h w[t,h] * ReLU(q[t,h] . k[s])  (DSA-style);
+      fp8 keys are dequantised k = scale[s] * e4m3fn(byte).
+  R3  the budget K includes sink and window; the rest is filled by top-k.
+  R4  sink = positions [0, S); window = the W positions ending at p_t inclusive.
+  R5  sink/window overlap is a union; fill = K - |forced|.
+  R6  ties: the lower position wins (blocks: the lower block index wins).
+  R7  output ascending, padded with -1.
+  R9  HI ranks only complete, causally visible blocks holding at least one
+      non-forced candidate; candidates of an incomplete visible block are always
+      kept (empty whenever W >= block size - 1).
+  R10 coarse block score = max over heads of w * ReLU(q . mean key of the block).
+  R11 query t of T sits at p_t = ctx_len - T + t.
+  R2/R16 one selection per query token shared by all heads; query head hq reads
+      KV head hq // (Hq/Hkv).
+  R15 MLA: one latent row per token; K = the whole row, V = its first d_v columns.
+"""
+from __future__ import annotations
+
+import numpy as np
+
+NEG_INF = -np.inf
+
+
+# ----------------------------------------------------------------------------- O1 decode
+
+def decode_bf16(bits: np.ndarray) -> np.ndarray:
+    """bf16 bit patterns -> float64 (exact: bf16 is the top half of an fp32)."""
+    u = np.asarray(bits, dtype=np.uint16).astype(np.uint32) << np.uint32(16)
+    return u.view(np.float32).astype(np.float64)
+
+
+def decode_e4m3fn(codes: np.ndarray) -> np.ndarray:
+    """OCP fp8 E4M3 ("fn": no infinities) bytes -> float64, from the format definition.
+
+    sign bit, 4 exponent bits with bias 7, 3 mantissa bits; exponent field 0 is
+    subnormal m * 2^-9; S.1111.111 is NaN; largest finite value 448.
+    """
+    c = np.asarray(codes, dtype=np.uint8).astype(np.int64)
+    sign = (c >> 7) & 1
+    e = (c >> 3) & 0xF
+    m = c & 0x7
+    normal = (1.0 + m / 8.0) * np.exp2(e - 7.0)
+    sub = m * 2.0 ** -9
+    val = np.where(e == 0, sub, normal)
+    val = np.where((e == 15) & (m == 7), np.nan, val)
+    return np.where(sign == 1, -val, val)
+
+
+def index_keys_f64(kI: np.ndarray, kI_scale) -> np.ndarray:
+    """Indexer-key cache -> float64 keys: bf16 bits, or fp8 bytes times the per-token scale (R1)."""
+    if kI_scale is None:
+        return decode_bf16(kI)
+    return decode_e4m3fn(kI) * np.asarray(kI_scale, dtype=np.float64)[..., None]
+
+
+# ----------------------------------------------------------------------------- O2 positions
+
+def query_positions(ctx_len: np.ndarray, T: int) -> np.ndarray:
+    """p[b, t] = ctx_len[b] - T + t  (R11: the T queries are the last T visible rows)."""
+    ctx = np.asarray(ctx_len, dtype=np.int64)
+    return ctx[:, None] - T + np.arange(T, dtype=np.int64)[None, :]
+
+
+# ----------------------------------------------------------------------------- O3 indexer
+
+def indexer_scores(q: np.ndarray, w: np.ndarray, keys: np.ndarray, p: int) -> np.ndarray:
+    """Token scores of one query token over keys[0:n] (R1, DSA-style indexer named in [P3]).
+
+    q [H, D], w [H], keys [n, D] (float64).  I[s] = sum_h w[h] * max(0, q[h] . keys[s]).
+    Positions s > p are not visible: -inf.
+    """
+    dots = keys @ np.asarray(q, dtype=np.float64).T            # [n, H]
+    score = np.maximum(dots, 0.0) @ np.asarray(w, dtype=np.float64)
+    n = keys.shape[0]
+    if p + 1 < n:
+        score = score.copy()
+        score[p + 1:] = NEG_INF
+    return score
+
+
+def indexer_scores_at(q, w, keys_rows: np.ndarray) -> np.ndarray:
+    """The same score for an explicit list of key rows (used on HI fine candidates)."""
+    dots = keys_rows @ np.asarray(q, dtype=np.float64).T
+    return np.maximum(dots, 0.0) @ np.asarray(w, dtype=np.float64)
+
+
+# ----------------------------------------------------------------------------- O4-O6 SI select
+
+def forced_positions(p: int, S: int, W: int) -> np.ndarray:
+    """SI forced set [P5 'technical features', first bullet; R4, R5]:
+    sink [0, S) and window [p-W+1, p], both clipped to [0, p], as a union."""
+    sink = np.arange(0, min(S, p + 1), dtype=np.int64)
+    win = np.arange(max(0, p - W + 1), p + 1, dtype=np.int64) if W > 0 else np.zeros(0, np.int64)
+    return np.union1d(sink, win)
+
+
+def top_fill(cand_pos: np.ndarray, cand_score: np.ndarray, m: int) -> np.ndarray:
+    """The first m candidates in (score descending, position ascending) order (R6).
+    All candidates when there are no more than m of them."""
+    cand_pos = np.asarray(cand_pos, dtype=np.int64)
+    if cand_pos.size <= m:
+        return cand_pos
+    order = np.lexsort((cand_pos, -np.asarray(cand_score, dtype=np.float64)))
+    return cand_pos[order[:m]]
+
+
+def pad_sorted(sel: np.ndarray, K: int) -> np.ndarray:
+    """Ascending positions padded with -1 to length K (R7)."""
+    out = np.full(K, -1, dtype=np.int64)
+    s = np.sort(np.asarray(sel, dtype=np.int64))
+    out[: s.size] = s
+    return out
+
+
+def select_tokens(scores: np.ndarray, p: int, K: int, S: int, W: int) -> np.ndarray:
+    """Flat SI selection of one query token [P5 'good to know' and 'technical features'; R3-R7].
+
+    scores [n] over positions 0..n-1 (-inf beyond p).  Forced F = sink U window;
+    candidates C = [0, p] minus F; fill m = K - |F| from C by (score desc, pos asc).
+    """
+    if S + W > K:
+        raise ValueError("sink + window exceed the budget")
+    F = forced_positions(p, S, W)
+    allpos = np.arange(p + 1, dtype=np.int64)
+    C = np.setdiff1d(allpos, F, assume_unique=True)
+    fill = top_fill(C, scores[C], K - F.size)
+    return pad_sorted(np.concatenate([F, fill]), K)
+
+
+# ----------------------------------------------------------------------------- O7 HI
+
+def block_means(keys: np.ndarray, Bs: int, n_blocks: int) -> np.ndarray:
+    """Mean key of each complete block j < n_blocks: (1/Bs) sum_{s in block j} k[s]
+    [P3 HI paragraph: a fast block-level pass; R10].  keys [>= n_blocks*Bs, D] float64."""
+    return keys[: n_blocks * Bs].reshape(n_blocks, Bs, keys.shape[1]).mean(axis=1)
+
+
+def eligible_blocks(p: int, S: int, W: int, Bs: int, n_blocks: int) -> np.ndarray:
+    """R9: complete, causally visible blocks (j*Bs + Bs - 1 <= p) that contain at least
+    one non-forced candidate position."""
+    F = forced_positions(p, S, W)
+    n_vis = min(n_blocks, (p + 1) // Bs)
+    ok = np.zeros(n_blocks, dtype=bool)
+    for j in range(n_vis):
+        lo, hi = j * Bs, j * Bs + Bs
+        n_forced = np.count_nonzero((F >= lo) & (F < hi))
+        ok[j] = n_forced < Bs
+    return ok
+
+
+def coarse_block_scores(q, w, kbar: np.ndarray, p: int, S: int, W: int, Bs: int) -> np.ndarray:
+    """c[j] = max_h w[h] * ReLU(q[h] . kbar[j]) over eligible blocks, -inf elsewhere (R9, R10)."""
+    dots = kbar @ np.asarray(q, dtype=np.float64).T                       # [NB, H]
+    c = np.max(np.asarray(w, dtype=np.float64)[None, :] * np.maximum(dots, 0.0), axis=1)
+    ok = eligible_blocks(p, S, W, Bs, kbar.shape[0])
+    return np.where(ok, c, NEG_INF)
+
+
+def keep_blocks(c: np.ndarray, n_keep: int) -> np.ndarray:
+    """Coarse stage of HI [P5 'technical features', third bullet]: the n_keep eligible
+    blocks with the highest coarse score, lower block index first on ties; ascending,
+    -1 padded."""
+    j = np.nonzero(np.isfinite(c))[0]
+    kept = top_fill(j, c[j], n_keep)
+    return pad_sorted(kept, n_keep)
+
+
+def hi_candidates(p: int, S: int, W: int, Bs: int, kept: np.ndarray) -> np.ndarray:
+    """Fine candidates C' = C restricted to the kept blocks, plus the candidates of the
+    incomplete visible block (R9)."""
+    F = forced_positions(p, S, W)
+    kept = kept[kept >= 0]
+    inside = (kept[:, None] * Bs + np.arange(Bs)[None, :]).reshape(-1)
+    tail_lo = ((p + 1) // Bs) * Bs
+    tail = np.arange(tail_lo, p + 1, dtype=np.int64)
+    pool = np.union1d(inside, tail)
+    pool = pool[pool <= p]
+    return np.setdiff1d(pool, F, assume_unique=False)
+
+
+def select_tokens_hi(q, w, keys: np.ndarray, kbar: np.ndarray, p: int, K: int, S: int,
+                     W: int, Bs: int, n_keep: int):
+    """Two-stage HI selection of one query token: coarse blocks, then fine top-k inside
+    the kept blocks, plus the SI forced set.  Returns (idx [K], kept [n_keep],
+    fine candidate positions, their scores)."""
+    c = coarse_block_scores(q, w, kbar, p, S, W, Bs)
+    kept = keep_blocks(c, n_keep)
+    cand = hi_candidates(p, S, W, Bs, kept)
+    sc = indexer_scores_at(q, w, keys[cand]) if cand.size else np.zeros(0)
+    F = forced_positions(p, S, W)
+    fill = top_fill(cand, sc, K - F.size)
+    return pad_sorted(np.concatenate([F, fill]), K), kept, cand, sc
+
+
+def select_fine_given_kept(q, w, keys, kept, p, K, S, W, Bs):
+    """Fine stage alone, for a given kept list (stage-wise checking of a GPU kept list)."""
+    cand = hi_candidates(p, S, W, Bs, np.asarray(kept))
+    sc = indexer_scores_at(q, w, keys[cand]) if cand.size else np.zeros(0)
+    F = forced_positions(p, S, W)
+    fill = top_fill(cand, sc, K - F.size)
+    return pad_sorted(np.concatenate([F, fill]), K), cand, sc
+
+
+# ----------------------------------------------------------------------------- O8 attention
+
+def attend(q: np.ndarray, k_rows: np.ndarray, v_rows: np.ndarray, idx: np.ndarray, tau: float):
+    """Softmax attention of one query token over the selected rows only [P1 'technical
+    features': no attention over all token pairs; R2, R16].
+
+    q [Hq, d_qk]; k_rows [N, Hkv, d_qk]; v_rows [N, Hkv, d_v] (float64); idx [K] with
+    -1 padding.  z_s = tau * q[hq] . K[s, hq // g]; o = sum_s softmax(z)_s V[s, hq // g];
+    lse = log sum_s exp(z_s).  Returns (o [Hq, d_v], lse [Hq]).
+    """
+    sel = np.asarray(idx, dtype=np.int64)
+    sel = sel[sel >= 0]
+    Hq = q.shape[0]
+    Hkv = k_rows.shape[1]
+    g = Hq // Hkv
+    o = np.zeros((Hq, v_rows.shape[2]))
+    lse = np.full(Hq, NEG_INF)
+    if sel.size == 0:
+        return o, lse
+    for kvh in range(Hkv):
+        Ks = k_rows[sel, kvh, :]                       # [n, d_qk]
+        Vs = v_rows[sel, kvh, :]                       # [n, d_v]
+        qs = q[kvh * g:(kvh + 1) * g]                  # [g, d_qk]
+        z = tau * (qs @ Ks.T)                          # [g, n]
+        zmax = z.max(axis=1, keepdims=True)
+        e = np.exp(z - zmax)
+        den = e.sum(axis=1, keepdims=True)
+        o[kvh * g:(kvh + 1) * g] = (e @ Vs) / den
+        lse[kvh * g:(kvh + 1) * g] = (zmax + np.log(den))[:, 0]
+    return o, lse
+
+
+def mla_kv(rows: np.ndarray, d_v: int):
+    """R15: MLA latent rows [N, 1, d_qk] -> (K rows, V rows = first d_v columns)."""
+    return rows, rows[..., :d_v]
+
+
+# ----------------------------------------------------------------------------- pipeline
+
+def reference_step(inp: dict, rows=None, layers=None, with_attend: bool = True) -> dict:
+    """Run the whole path for the (b, t) pairs in ``rows`` (default: all).
+
+    CLI [P3 CLI paragraph; P5 'technical features', second bullet]: the selection is
+    computed once per query token and reused by every layer; each layer attends with
+    its own q/K/V.  Returns dict with per-row idx (and kept for HI), out [L][...],
+    lse [L][...], plus flat scores (non-HI) keyed by (b, t).
+    """
+    cfg = inp["cfg"]
+    B, T = cfg.B, cfg.T
+    P = query_positions(inp["ctx_len"], T)
+    if rows is None:
+        rows = [(b, t) for b in range(B) for t in range(T)]
+    L = cfg.layers if layers is None else layers
+    res = {"idx": {}, "kept": {}, "scores": {}, "cand": {}, "out": {}, "lse": {}}
+    by_b = {}
+    for b, t in rows:
+        by_b.setdefault(b, []).append(t)
+    for b, ts in by_b.items():
+        keys = index_keys_f64(inp["kI"][b], None if inp["kI_scale"] is None else inp["kI_scale"][b])
+        kbar = block_means(keys, cfg.Bs, int(inp["ctx_len"][b]) // cfg.Bs) if cfg.hi else None
+        kv = {}
+        for t in ts:
+            p = int(P[b, t])
+            qI = decode_bf16(inp["qI"][b, t])
+            w = np.asarray(inp["w"][b, t], dtype=np.float64)
+            if cfg.hi:
+                idx, kept, cand, sc = select_tokens_hi(qI, w, keys, kbar, p, cfg.K, cfg.S,
+                                                       cfg.W, cfg.Bs, cfg.n_keep)
+                res["kept"][(b, t)] = kept
+                res["cand"][(b, t)] = (cand, sc)
+            else:
+                sc = indexer_scores(qI, w, keys[: p + 1], p)
+                idx = select_tokens(sc, p, cfg.K, cfg.S, cfg.W)
+                res["scores"][(b, t)] = sc
+            res["idx"][(b, t)] = idx
+            if not with_attend:
+                continue
+            for layer in range(L):
+                if layer not in kv:
+                    kv[layer] = _layer_kv(inp, cfg, layer, b)
+                k_rows, v_rows = kv[layer]
+                q = decode_bf16(inp["q"][layer, b, t])
+                o, lse = attend(q, k_rows, v_rows, idx, cfg.tau)
+                res["out"][(layer, b, t)] = o
+                res["lse"][(layer, b, t)] = lse
+    return res
+
+
+class _LazyRows:
+    """Decode KV rows on first access (full caches at 1M context are large in float64)."""
+
+    def __init__(self, bits: np.ndarray, last: int = None):
+        self.bits = bits
+        self.last = last
+        self.shape = bits.shape if last is None else bits.shape[:-1] + (last,)
+
+    def __getitem__(self, key):
+        sel, h, sl = key
+        rows = decode_bf16(self.bits[sel, h, :])
+        return rows if self.last is None else rows[..., : self.last]
+
+
+def _layer_kv(inp, cfg, layer, b):
+    if cfg.mla:
+        return _LazyRows(inp["k"][layer, b]), _LazyRows(inp["k"][layer, b], cfg.d_v)
+    return _LazyRows(inp["k"][layer, b]), _LazyRows(inp["v"][layer, b])

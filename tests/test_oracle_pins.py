@@ -1,0 +1,367 @@
+"""Pins of the CPU oracle against things other than itself.
+
+Each test ties one oracle step to a fixed point: a hand-worked example (golden
+fixture), a library routine on a special case, a closed form, an invariant the
+pages imply, or an independent brute-force restatement on tiny inputs.
+"""
+import json
+import math
+import os
+
+import numpy as np
+import pytest
+import torch
+
+from oracle import lsa_oracle as O
+from oracle import loops as L
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+
+
+def _golden(name):
+    with open(os.path.join(GOLDEN, name)) as f:
+        return json.load(f)
+
+
+# ----------------------------------------------------------------------------- P1 decode
+
+def test_e4m3fn_matches_torch_all_codes():
+    codes = np.arange(256, dtype=np.uint8)
+    ours = O.decode_e4m3fn(codes)
+    ref = torch.from_numpy(codes.copy()).view(torch.float8_e4m3fn).to(torch.float64).numpy()
+    assert np.array_equal(np.isnan(ours), np.isnan(ref))
+    fin = ~np.isnan(ref)
+    assert np.array_equal(ours[fin], ref[fin])
+    assert np.array_equal(np.signbit(ours[fin]), np.signbit(ref[fin]))
+
+
+def test_e4m3fn_closed_forms():
+    d = O.decode_e4m3fn(np.array([0x7E, 0x08, 0x01, 0x7F, 0xFF, 0x80, 0x38, 0xFE], dtype=np.uint8))
+    assert d[0] == 448.0
+    assert d[1] == 2.0 ** -6
+    assert d[2] == 2.0 ** -9
+    assert math.isnan(d[3]) and math.isnan(d[4])
+    assert d[5] == 0.0 and math.copysign(1.0, d[5]) == -1.0
+    assert d[6] == 1.0
+    assert d[7] == -448.0
+
+
+def test_bf16_decode_matches_torch():
+    rng = np.random.default_rng(0)
+    x = rng.standard_normal(4096).astype(np.float32) * 100
+    b = torch.from_numpy(x).to(torch.bfloat16)
+    bits = b.view(torch.int16).numpy().view(np.uint16)
+    assert np.array_equal(O.decode_bf16(bits), b.to(torch.float64).numpy())
+
+
+def test_fp8_dequant_scale_multiplies():
+    codes = np.array([[0x38, 0x40, 0xB8]], dtype=np.uint8)        # 1.0, 2.0, -1.0
+    k = O.index_keys_f64(codes, np.array([0.25], dtype=np.float32))
+    assert np.array_equal(k, np.array([[0.25, 0.5, -0.25]]))
+
+
+# ----------------------------------------------------------------------------- P2 indexer
+
+def test_indexer_single_head_is_relu_dot():
+    rng = np.random.default_rng(1)
+    q = rng.standard_normal((1, 16))
+    keys = rng.standard_normal((50, 16))
+    s = O.indexer_scores(q, np.array([1.0]), keys, 49)
+    assert np.allclose(s, np.maximum(np.dot(keys, q[0]), 0.0), rtol=0, atol=1e-13)
+
+
+def test_indexer_zero_weights_and_masking():
+    rng = np.random.default_rng(2)
+    q = rng.standard_normal((4, 8))
+    keys = rng.standard_normal((20, 8))
+    s = O.indexer_scores(q, np.zeros(4), keys, 11)
+    assert np.all(s[:12] == 0.0) and np.all(np.isneginf(s[12:]))
+
+
+def test_indexer_weight_linearity_and_head_additivity():
+    rng = np.random.default_rng(3)
+    q = rng.standard_normal((3, 8))
+    w = rng.random(3)
+    keys = rng.standard_normal((30, 8))
+    tot = O.indexer_scores(q, w, keys, 29)
+    per_head = sum(O.indexer_scores(q[h:h + 1], w[h:h + 1], keys, 29) for h in range(3))
+    assert np.allclose(tot, per_head, atol=1e-13)
+    assert np.allclose(O.indexer_scores(q, 2 * w, keys, 29), 2 * tot, atol=1e-13)
+
+
+@pytest.mark.parametrize("seed", range(4))
+def test_indexer_matches_brute_force(seed):
+    rng = np.random.default_rng(10 + seed)
+    H, D, N = 3, 5, 40
+    q = rng.standard_normal((H, D))
+    w = rng.random(H) - 0.3                 # any sign is accepted
+    keys = rng.standard_normal((N, D))
+    p = N - 1 - seed
+    s = O.indexer_scores(q, w, keys, p)
+    for i in range(N):
+        want = L.score(q.tolist(), w.tolist(), keys[i].tolist()) if i <= p else -math.inf
+        assert s[i] == pytest.approx(want, abs=1e-12) if i <= p else s[i] == want
+
+
+# ----------------------------------------------------------------------------- golden
+
+def test_golden_hand_worked_flat_and_hi():
+    g = _golden("hand_worked_select.json")
+    q, w, keys = np.array(g["q"]), np.array(g["w"]), np.array(g["keys"])
+    s = O.indexer_scores(q, w, keys, len(keys) - 1)
+    assert np.array_equal(s, np.array(g["scores"]))
+    for c in g["flat_cases"]:
+        sc = O.indexer_scores(q, w, keys[: c["p"] + 1], c["p"])
+        idx = O.select_tokens(sc, c["p"], c["K"], c["S"], c["W"])
+        assert idx.tolist() == c["idx"], c["why"]
+    for c in g["hi_cases"]:
+        nb = len(keys) // c["Bs"]
+        kbar = O.block_means(keys, c["Bs"], nb)
+        idx, kept, _, _ = O.select_tokens_hi(q, w, keys, kbar, c["p"], c["K"], c["S"], c["W"],
+                                             c["Bs"], c["n_keep"])
+        assert kept[kept >= 0].tolist() == c["kept"], c["why"]
+        assert idx.tolist() == c["idx"], c["why"]
+    c = g["hi_max_case"]
+    k2 = np.array(c["keys"])
+    kbar = O.block_means(k2, c["Bs"], len(k2) // c["Bs"])
+    idx, kept, _, _ = O.select_tokens_hi(q, w, k2, kbar, c["p"], c["K"], c["S"], c["W"],
+                                         c["Bs"], c["n_keep"])
+    assert kept[kept >= 0].tolist() == c["kept"], c["why"]
+    assert idx.tolist() == c["idx"], c["why"]
+
+
+# ----------------------------------------------------------------------------- P3 selection
+
+def _rand_scores(rng, n, ties=False):
+    if ties:
+        return rng.integers(0, 6, size=n).astype(np.float64)
+    return rng.standard_normal(n)
+
+
+@pytest.mark.parametrize("seed", range(12))
+def test_selection_invariants(seed):
+    rng = np.random.default_rng(100 + seed)
+    n = int(rng.integers(1, 300))
+    p = n - 1
+    K = int(rng.integers(1, 80))
+    S = int(rng.integers(0, K + 1))
+    W = int(rng.integers(0, K - S + 1))
+    sc = _rand_scores(rng, n, ties=seed % 2 == 0)
+    idx = O.select_tokens(sc, p, K, S, W)
+    valid = idx[idx >= 0]
+    F = set(range(min(S, p + 1))) | set(range(max(0, p - W + 1), p + 1))
+    assert len(idx) == K
+    assert np.all(idx[len(valid):] == -1)
+    assert np.all(np.diff(valid) > 0)                          # ascending, unique
+    assert len(valid) == min(K, p + 1)                          # budget filled
+    assert F <= set(valid.tolist())                             # sink and window always in
+    C = [s for s in range(p + 1) if s not in F]
+    chosen = [s for s in valid if s not in F]
+    rest = [s for s in C if s not in set(chosen)]
+    if chosen and rest:
+        assert min(sc[chosen]) >= max(sc[rest])
+        # ties at the boundary go to the lower position
+        lo = min(sc[chosen])
+        tied_out = [s for s in rest if sc[s] == lo]
+        tied_in = [s for s in chosen if sc[s] == lo]
+        if tied_out:
+            assert max(tied_in) < min(tied_out)
+
+
+@pytest.mark.parametrize("seed", range(6))
+def test_selection_without_forced_is_lexsort_and_partition(seed):
+    rng = np.random.default_rng(200 + seed)
+    n, K = 257, 31
+    sc = rng.standard_normal(n)
+    idx = O.select_tokens(sc, n - 1, K, 0, 0)
+    want = np.sort(np.lexsort((np.arange(n), -sc))[:K])
+    assert np.array_equal(idx, want)
+    kth = -np.partition(-sc, K - 1)[K - 1]
+    assert sc[idx].min() == kth
+
+
+@pytest.mark.parametrize("seed", range(10))
+def test_selection_matches_rank_counting(seed):
+    rng = np.random.default_rng(300 + seed)
+    n = int(rng.integers(1, 60))
+    p = n - 1 - int(rng.integers(0, min(n, 5)))
+    K = int(rng.integers(1, 20))
+    S = int(rng.integers(0, K + 1))
+    W = int(rng.integers(0, K - S + 1))
+    sc = _rand_scores(rng, n, ties=True)
+    got = O.select_tokens(sc, p, K, S, W)
+    want = L.select({i: sc[i] for i in range(n)}, p, K, S, W)
+    assert got.tolist() == want
+
+
+def test_selection_budget_precondition():
+    with pytest.raises(ValueError):
+        O.select_tokens(np.zeros(10), 9, 4, 3, 2)
+
+
+# ----------------------------------------------------------------------------- P4 HI
+
+def test_block_means_is_numpy_mean():
+    rng = np.random.default_rng(7)
+    keys = rng.standard_normal((640, 8))
+    kb = O.block_means(keys, 64, 10)
+    for j in range(10):
+        assert np.allclose(kb[j], np.mean(keys[j * 64:(j + 1) * 64], axis=0), atol=1e-15)
+
+
+@pytest.mark.parametrize("seed", range(6))
+def test_hi_all_blocks_kept_equals_flat(seed):
+    rng = np.random.default_rng(400 + seed)
+    Bs = 8
+    N = int(rng.integers(4, 40)) * Bs + int(rng.integers(0, Bs))
+    H, D = 3, 6
+    q, w = rng.standard_normal((H, D)), rng.random(H)
+    keys = rng.standard_normal((N, D))
+    p = N - 1
+    K, S, W = 24, 3, Bs + 2                   # W >= Bs - 1: the incomplete block is forced
+    kbar = O.block_means(keys, Bs, N // Bs)
+    flat = O.select_tokens(O.indexer_scores(q, w, keys, p), p, K, S, W)
+    hi, kept, _, _ = O.select_tokens_hi(q, w, keys, kbar, p, K, S, W, Bs, N // Bs)
+    assert np.array_equal(flat, hi)
+
+
+@pytest.mark.parametrize("seed", range(6))
+def test_hi_matches_brute_force(seed):
+    rng = np.random.default_rng(500 + seed)
+    Bs = 4
+    N = int(rng.integers(3, 12)) * Bs + int(rng.integers(0, Bs))
+    H, D = 2, 3
+    q, w = rng.standard_normal((H, D)), rng.random(H)
+    keys = rng.standard_normal((N, D))
+    p = N - 1 - int(rng.integers(0, 3))
+    K, S, W, n_keep = 9, 2, int(rng.integers(1, 6)), int(rng.integers(1, 4))
+    kbar = O.block_means(keys, Bs, N // Bs)
+    idx, kept, _, _ = O.select_tokens_hi(q, w, keys, kbar, p, K, S, W, Bs, n_keep)
+    bidx, bkept = L.hi_select(q.tolist(), w.tolist(), keys.tolist(), p, K, S, W, Bs, n_keep)
+    assert kept.tolist() == bkept
+    assert idx.tolist() == bidx
+
+
+def test_hi_recovers_planted_blocks():
+    rng = np.random.default_rng(8)
+    Bs, nb, H, D = 16, 64, 2, 16
+    keys = rng.standard_normal((Bs * nb, D)) / 4
+    q = rng.standard_normal((H, D))
+    planted = [5, 17, 33, 40]
+    for j in planted:
+        keys[j * Bs:(j + 1) * Bs] += 2.0 * q[0] / np.linalg.norm(q[0])
+    kbar = O.block_means(keys, Bs, nb)
+    p = Bs * nb - 1
+    c = O.coarse_block_scores(q, np.array([1.0, 0.0]), kbar, p, 4, 16, Bs)
+    kept = O.keep_blocks(c, 4)
+    assert kept.tolist() == planted
+
+
+# ----------------------------------------------------------------------------- P5 attention
+
+def _sdpa_dense(q, k, v, tau):
+    qt = torch.from_numpy(q)[None, :, None, :]           # [1, H, 1, d]
+    kt = torch.from_numpy(k)[None, None].expand(1, q.shape[0], -1, -1)
+    vt = torch.from_numpy(v)[None, None].expand(1, q.shape[0], -1, -1)
+    return torch.nn.functional.scaled_dot_product_attention(qt, kt, vt, scale=tau)[0, :, 0].numpy()
+
+
+@pytest.mark.parametrize("seed", range(4))
+def test_budget_covers_context_equals_dense_causal(seed):
+    rng = np.random.default_rng(600 + seed)
+    N, Hq, Hkv, d = 37, 4, 2, 8
+    keys_i = rng.standard_normal((N, 5))
+    qi, wi = rng.standard_normal((2, 5)), rng.random(2)
+    k = rng.standard_normal((N, Hkv, d))
+    v = rng.standard_normal((N, Hkv, d))
+    q = rng.standard_normal((Hq, d))
+    p = N - 1 - seed
+    idx = O.select_tokens(O.indexer_scores(qi, wi, keys_i[: p + 1], p), p, N + 3, 2, 3)
+    assert idx[idx >= 0].tolist() == list(range(p + 1))
+    o, lse = O.attend(q, k, v, idx, 0.3)
+    g = Hq // Hkv
+    for hq in range(Hq):
+        kvh = hq // g
+        want = _sdpa_dense(q[hq:hq + 1], k[: p + 1, kvh], v[: p + 1, kvh], 0.3)[0]
+        assert np.allclose(o[hq], want, atol=1e-12)
+        z = 0.3 * k[: p + 1, kvh] @ q[hq]
+        assert lse[hq] == pytest.approx(np.log(np.sum(np.exp(z))), abs=1e-12)
+
+
+def test_attention_closed_forms():
+    # one selected row: o = V[s]
+    k = np.arange(12, dtype=np.float64).reshape(6, 1, 2)
+    v = np.arange(18, dtype=np.float64).reshape(6, 1, 3) * 0.5
+    q = np.array([[0.3, -0.2]])
+    o, _ = O.attend(q, k, v, np.array([4, -1, -1]), 1.0)
+    assert np.array_equal(o[0], v[4, 0])
+    # equal logits (q = 0): o = mean of selected V rows, lse = log(count)
+    o, lse = O.attend(np.zeros((1, 2)), k, v, np.array([0, 2, 5, -1]), 1.0)
+    assert np.allclose(o[0], v[[0, 2, 5], 0].mean(axis=0), atol=1e-15)
+    assert lse[0] == pytest.approx(math.log(3))
+    # logits 0,1,2 and one-hot values: o = e^s / (1 + e + e^2)
+    k1 = np.array([[[0.0]], [[1.0]], [[2.0]]])
+    v1 = np.eye(3)[:, None, :]
+    o, lse = O.attend(np.array([[1.0]]), k1, v1, np.array([0, 1, 2]), 1.0)
+    den = 1 + math.e + math.e ** 2
+    assert np.allclose(o[0], [1 / den, math.e / den, math.e ** 2 / den], atol=1e-15)
+    assert lse[0] == pytest.approx(math.log(den), abs=1e-14)
+
+
+def test_attention_permutation_invariant_and_gqa_mapping():
+    rng = np.random.default_rng(9)
+    N, Hq, Hkv, d = 20, 8, 2, 4
+    k, v = rng.standard_normal((N, Hkv, d)), rng.standard_normal((N, Hkv, d + 1))
+    q = rng.standard_normal((Hq, d))
+    idx = np.array([1, 3, 4, 9, 15, -1])
+    o1, l1 = O.attend(q, k, v, idx, 0.5)
+    o2, l2 = O.attend(q, k, v, np.array([15, 4, 1, 9, 3, -1]), 0.5)
+    assert np.allclose(o1, o2, atol=1e-14) and np.allclose(l1, l2, atol=1e-14)
+    lo, ll = L.attend(q.tolist(), k.tolist(), v.tolist(), idx.tolist(), 0.5, Hkv)
+    assert np.allclose(o1, np.array(lo), atol=1e-12) and np.allclose(l1, ll, atol=1e-12)
+    # head 3 reads KV head 0, head 4 reads KV head 1 (kvh = hq // g)
+    o_h3, _ = O.attend(q[3:4], k[:, :1], v[:, :1], idx, 0.5)
+    o_h4, _ = O.attend(q[4:5], k[:, 1:], v[:, 1:], idx, 0.5)
+    assert np.allclose(o1[3], o_h3[0]) and np.allclose(o1[4], o_h4[0])
+
+
+def test_mla_value_is_row_prefix():
+    rows = np.arange(2 * 1 * 6, dtype=np.float64).reshape(2, 1, 6)
+    kr, vr = O.mla_kv(rows, 4)
+    assert np.array_equal(vr, rows[..., :4]) and kr is rows
+
+
+# ----------------------------------------------------------------------------- P6 CLI
+
+def test_cli_reuse_equals_per_layer_recompute():
+    from synth import config, make_inputs
+    cfg = config(5, B=2, N=300, K=40, S=4, W=8, Hq=8, Hkv=2, H_I=4, D_I=16, d_qk=16, d_v=16)
+    inp = make_inputs(cfg)
+    res = O.reference_step(inp)
+    for layer in range(cfg.layers):
+        one = dict(inp)
+        one["q"], one["k"], one["v"] = inp["q"][layer:layer + 1], inp["k"][layer:layer + 1], inp["v"][layer:layer + 1]
+        one["cfg"] = cfg.scaled(layers=1)
+        r1 = O.reference_step(one)
+        for b in range(cfg.B):
+            assert np.array_equal(r1["idx"][(b, 0)], res["idx"][(b, 0)])
+            assert np.array_equal(r1["out"][(0, b, 0)], res["out"][(layer, b, 0)])
+    # distinct layers do give distinct outputs for the same selection
+    assert not np.allclose(res["out"][(0, 0, 0)], res["out"][(1, 0, 0)])
+
+
+def test_reference_step_small_c1_shape_consistency():
+    from synth import config, make_inputs
+    cfg = config(1, N=600, K=64, S=4, W=16)
+    inp = make_inputs(cfg)
+    res = O.reference_step(inp)
+    P = O.query_positions(inp["ctx_len"], cfg.T)
+    for t in range(cfg.T):
+        idx = res["idx"][(0, t)]
+        assert idx.max() == P[0, t]
+        assert res["out"][(0, 0, t)].shape == (cfg.Hq, cfg.d_v)
+    # salient keys are chosen far above the chance rate of the fill
+    sal = set(inp["salient"][0].tolist())
+    chosen = set(res["idx"][(0, 0)].tolist())
+    chance = (cfg.K - cfg.S - cfg.W) / (cfg.N - cfg.T - cfg.S - cfg.W)
+    assert len(sal & chosen) / len(sal) > 4 * chance
