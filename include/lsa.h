@@ -1,0 +1,235 @@
+/*
+ * lsa.h — C ABI of liblsa.so, the MI355X (gfx950) hot path of LongCat Sparse
+ * Attention (LSA): index -> select -> attend.
+ *
+ * The method, as the LongCat pages state it:
+ *   - LSA extends DeepSeek Sparse Attention with three indexing mechanisms
+ *     ("LongCat-2.0: how Meituan trained a 1.6T coding model without Nvidia GPUs",
+ *     molayo1419.me, section "The sparse attention problem at 1M tokens").
+ *   - Streaming-aware Indexing (SI) spends part of each query token's selection
+ *     budget on a fixed sink and a local sliding window, so that KV reads become
+ *     contiguous ("LongCat-Flash-Lite-Sparse" summary, aitrends.kr, sections
+ *     "Good to know" and "Technical features", first bullet).
+ *   - Hierarchical Indexing (HI) first picks coarse candidate blocks, then
+ *     selects fine tokens inside them; it can be switched on at inference (same
+ *     page, "Technical features", third bullet; "Training").
+ *   - Cross-Layer Indexing (CLI) reuses one index result in several consecutive
+ *     layers (same page, second bullet; molayo1419.me, CLI paragraph).
+ *   - Attention runs over the selected tokens only, never over all token pairs
+ *     ("LongCat-2.0" summary, aitrends.kr, "Technical features").
+ * The pages give no formula for the indexer; this library computes the DSA-style
+ * score  I[t,s] = scale[s] * sum_h w[t,h] * ReLU(q[t,h] . k[s])  (reading R1).
+ *
+ * Conventions (all functions):
+ *   - Every pointer inside a descriptor is a DEVICE pointer unless stated; every
+ *     array is dense row-major with the stated shape unless strides are given.
+ *     Tensors read with vector loads (q, w, k, v, scores, kbar) must be 16-byte
+ *     aligned.
+ *   - `stream` is a hipStream_t passed as void* (NULL = the default stream). Work
+ *     is enqueued on it; no call synchronises, allocates device memory, or keeps
+ *     a pointer after it returns. The library has no mutable global state.
+ *   - Query token t of sequence b sits at position p = ctx_len[b] - T + t
+ *     (reading R11); ctx_len NULL means every sequence has N visible rows.
+ *     Positions s > p are never visible to query t.
+ *   - Return value: LSA_OK (0) or a negative status. On a negative status nothing
+ *     was enqueued, except LSA_E_HIP (a launch failed; lsa_last_error() tells
+ *     which). Argument checks run on the host before any HIP call.
+ *   - Determinism: repeated calls on identical inputs give identical bytes (no
+ *     floating-point atomics; every reduction has a fixed order).
+ */
+#ifndef LSA_H
+#define LSA_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define LSA_VERSION 1
+
+/* status codes */
+#define LSA_OK 0
+#define LSA_E_NULL (-1)        /* a required pointer is NULL */
+#define LSA_E_SHAPE (-2)       /* a size is out of range or inconsistent */
+#define LSA_E_DTYPE (-3)       /* unknown or unsupported dtype code */
+#define LSA_E_BUDGET (-4)      /* K < 1, or sink + window > K */
+#define LSA_E_ALIGN (-5)       /* a pointer or stride breaks the 16-byte rule */
+#define LSA_E_UNSUPPORTED (-6) /* no compiled kernel for this shape (no slow fallback exists) */
+#define LSA_E_WORKSPACE (-7)   /* workspace NULL or smaller than the *_workspace_bytes() answer */
+#define LSA_E_HIP (-8)         /* a HIP launch failed */
+
+/* element types */
+#define LSA_BF16 1
+#define LSA_FP8_E4M3FN 2 /* OCP E4M3 without infinities (gfx950 native), max 448 */
+#define LSA_F32 3
+
+/* lsa_index modes */
+#define LSA_INDEX_TOKENS 0
+#define LSA_INDEX_BLOCKS 1
+
+/*
+ * lsa_index — indexer scores (the DSA-style indexer the LSA pages build on).
+ *
+ * TOKENS, flat (kept == NULL): for every query token (b,t) and position s < N
+ *   scores[b][t][s] = k_scale[b][s] * sum_h w[b][t][h] * max(0, q[b][t][h] . k[b][s])
+ *   for s <= p, and -inf for s > p. k_scale is NULL for bf16 keys (scale 1).
+ *   The contraction runs as bf16 x bf16 products with fp32 accumulation; fp8 keys
+ *   are widened exactly to bf16.
+ * TOKENS, HI fine stage (kept != NULL): column c of query (b,t) stands for position
+ *   s = kept[b][t][c / block_size] * block_size + c % block_size, c < n_keep *
+ *   block_size; the score is as above. Columns whose kept entry is -1 or outside
+ *   [0, N / block_size), or whose position is > p, get -inf.
+ * BLOCKS, HI coarse stage: k is the fp32 block-mean cache kbar[b][n_blocks][D]
+ *   (from lsa_block_means) and
+ *   scores[b][t][j] = max_h w[b][t][h] * max(0, q[b][t][h] . kbar[b][j])
+ *   in fp32 for every block j that is complete and visible (j*block_size +
+ *   block_size - 1 <= p) and holds at least one position outside the forced set
+ *   sink [0,sink) U window [p-window+1, p]; -inf for every other block (reading R9).
+ *
+ * Shapes: q bf16 [B][T][H][D]; w fp32 [B][T][H]; k per k_dtype: bf16 or fp8 [B][N][D]
+ * (TOKENS) or fp32 [B][n_blocks][D] (BLOCKS); k_scale fp32 [B][N] (fp8 keys only);
+ * kept int32 [B][T][n_keep]; scores fp32 [B][T][n_out] with n_out = N (flat),
+ * n_keep*block_size (HI fine) or n_blocks (BLOCKS).
+ * Supported: TOKENS D in {64,128}, H in {4,8,16,32,64}, k_dtype bf16 or fp8;
+ * BLOCKS D in {64,128}, 1 <= H <= 64, k_dtype f32.
+ */
+typedef struct lsa_index_desc {
+    int32_t mode;            /* LSA_INDEX_TOKENS or LSA_INDEX_BLOCKS */
+    int32_t B, T, N;         /* sequences, query tokens per sequence, cache rows per sequence */
+    const int32_t *ctx_len;  /* [B] visible rows per sequence, or NULL (= N) */
+    int32_t H, D;            /* indexer heads and head dim */
+    const void *q;           /* bf16 [B][T][H][D] */
+    const float *w;          /* fp32 [B][T][H] */
+    const void *k;           /* key cache, see above */
+    int32_t k_dtype;         /* LSA_BF16, LSA_FP8_E4M3FN (TOKENS) or LSA_F32 (BLOCKS) */
+    const float *k_scale;    /* fp32 [B][N] per-token scale for fp8 keys, else NULL */
+    const int32_t *kept;     /* HI fine stage: int32 [B][T][n_keep], else NULL */
+    int32_t n_keep;          /* kept blocks per query token (HI fine stage) */
+    int32_t block_size;      /* HI block size (HI fine stage and BLOCKS) */
+    int32_t n_blocks;        /* BLOCKS: block-mean rows per sequence */
+    int32_t sink, window;    /* BLOCKS: forced set used for block eligibility */
+    float *scores;           /* fp32 [B][T][n_out], written in full */
+} lsa_index_desc;
+
+int32_t lsa_index(const lsa_index_desc *desc, void *stream);
+
+/*
+ * lsa_block_means — the block summaries of the HI coarse stage: the mean
+ * indexer key of each block of block_size consecutive rows,
+ *   kbar[b][j][d] = (1/block_size) * sum_{s=j*bs}^{j*bs+bs-1} k_scale[b][s] * k[b][s][d]
+ * computed in fp32 (reading R10), for j < n_blocks (n_blocks * block_size <= N).
+ * The cost is amortised: it is recomputed only when the cache changes.
+ * Shapes: k bf16 or fp8 [B][N][D]; k_scale fp32 [B][N] (fp8) or NULL; kbar fp32
+ * [B][n_blocks][D]. Supported: D in {64,128}, block_size >= 1.
+ */
+typedef struct lsa_block_means_desc {
+    int32_t B, N, D;
+    const void *k;
+    int32_t k_dtype;         /* LSA_BF16 or LSA_FP8_E4M3FN */
+    const float *k_scale;
+    int32_t block_size;
+    int32_t n_blocks;
+    float *kbar;
+} lsa_block_means_desc;
+
+int32_t lsa_block_means(const lsa_block_means_desc *desc, void *stream);
+
+/*
+ * lsa_select — the SI selection of one budget of K positions per query token
+ * (LongCat-Flash-Lite-Sparse summary: the selection budget is split into a fixed
+ * sink and a local window; the rest is a top-k fill).
+ *
+ * causal = 1 (token selection): forced F = [0, min(sink, p+1)) U [max(0, p-window+1), p];
+ *   candidates = visible columns whose position is not in F and whose score is
+ *   finite; fill m = K - |F| candidates by (score descending, position ascending)
+ *   (reading R6; -0.0 and +0.0 are equal), or all of them when there are at most m.
+ * causal = 0 (block stage of HI, or any plain top-K): sink and window must be 0;
+ *   candidates = every column with a finite score; fill m = K.
+ * Positions: column c is position c, or with a candidate map (kept != NULL)
+ *   kept[b][t][c / block_size] * block_size + c % block_size (entries -1 or
+ *   outside [0, N / block_size) make the column no candidate).
+ * Output idx int32 [B][T][K]: the selected positions in ascending order, then -1.
+ *
+ * Workspace: lsa_select_workspace_bytes(desc) bytes of device memory, 256-byte
+ * aligned, ZERO-FILLED before its first use (e.g. by lsa_workspace_clear). Every
+ * lsa_select call returns it to all-zero at its end (stream-ordered), so it can be
+ * reused across calls without clearing; after a failed call clear it again.
+ * Calls that share one workspace must be ordered on one stream.
+ * Supported: 1 <= K <= 4096, n_cols >= 1.
+ */
+typedef struct lsa_select_desc {
+    int32_t B, T, N;         /* N: cache rows (bounds positions and the kept map) */
+    const int32_t *ctx_len;  /* [B] or NULL (= N) */
+    const float *scores;     /* fp32 [B][T][n_cols] */
+    int32_t n_cols;
+    const int32_t *kept;     /* optional column -> position map, int32 [B][T][n_keep] */
+    int32_t n_keep, block_size;
+    int32_t K, sink, window;
+    int32_t causal;          /* 1 token selection at p with forced set, 0 plain top-K */
+    int32_t *idx;            /* int32 [B][T][K] */
+} lsa_select_desc;
+
+size_t lsa_select_workspace_bytes(const lsa_select_desc *desc);
+int32_t lsa_select(const lsa_select_desc *desc, void *workspace, size_t workspace_bytes, void *stream);
+
+/*
+ * lsa_attend — softmax attention of each query token over its selected rows only
+ * ("LongCat-2.0" summary: no attention over all token pairs), for n_layers
+ * consecutive layers that share one selection (CLI).
+ *
+ * For layer l, query (b,t), query head hq, KV head kvh = hq / (Hq/Hkv) (reading R16):
+ *   z_s = softmax_scale * q[l][b][t][hq] . K[l][b][s][kvh]   for s in idx[b][t] (s >= 0)
+ *   out[l][b][t][hq] = sum_s softmax(z)_s V[l][b][s][kvh];  lse = log sum_s exp(z_s)
+ * bf16 inputs, fp32 accumulation and softmax, bf16 or fp32 output.
+ * K element (b,s,h,d) is at k[l*layer_stride_k + b*k_stride_b + s*k_stride_n +
+ * h*k_stride_h + d] (elements), d < d_qk; V likewise with the v_* strides, d < d_v.
+ * MLA latent rows (reading R15) are expressed with strides: v = k, d_qk = 576,
+ * d_v = 512, one KV head.
+ * idx int32 [B][T][K]: entries -1 or outside [0, N) are skipped; a query token with no
+ * valid entry gets out = 0 and lse = -inf.
+ * q bf16 [n_layers][B][T][Hq][d_qk] (layer stride layer_stride_q); out [n_layers][B][T]
+ * [Hq][d_v] (layer_stride_out); lse fp32 [n_layers][B][T][Hq] (layer_stride_lse) or NULL.
+ * n_splits: how many parts the K rows of one query are split into (0 = library
+ * choice); partial results are merged in a fixed order.
+ * Workspace: lsa_attend_workspace_bytes(desc) bytes (may be 0), 256-byte aligned;
+ * no initial contents needed.
+ * Supported: (d_qk, d_v) in {(128,128), (576,512)}, Hq % Hkv == 0, Hq/Hkv <= 64,
+ * K >= 1, strides multiples of 8 elements.
+ */
+typedef struct lsa_attend_desc {
+    int32_t B, T, N;
+    int32_t Hq, Hkv, d_qk, d_v;
+    const void *q;
+    const void *k;
+    int64_t k_stride_b, k_stride_n, k_stride_h;
+    const void *v;
+    int64_t v_stride_b, v_stride_n, v_stride_h;
+    const int32_t *idx;
+    int32_t K;
+    float softmax_scale;
+    void *out;
+    int32_t out_dtype;       /* LSA_BF16 or LSA_F32 */
+    float *lse;              /* optional */
+    int32_t n_layers;        /* >= 1 */
+    int64_t layer_stride_q, layer_stride_k, layer_stride_v, layer_stride_out, layer_stride_lse;
+    int32_t n_splits;
+} lsa_attend_desc;
+
+size_t lsa_attend_workspace_bytes(const lsa_attend_desc *desc);
+int32_t lsa_attend(const lsa_attend_desc *desc, void *workspace, size_t workspace_bytes, void *stream);
+
+/* Zero-fill `bytes` of device memory at `ptr` with a fill kernel (for workspaces). */
+int32_t lsa_workspace_clear(void *ptr, size_t bytes, void *stream);
+
+/* Static text for a status code; the last error text of the calling thread. */
+const char *lsa_status_str(int32_t status);
+const char *lsa_last_error(void);
+int32_t lsa_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* LSA_H */

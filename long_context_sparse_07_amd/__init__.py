@@ -1,0 +1,250 @@
+"""Thin Python binding of liblsa.so, the MI355X hot path of LongCat Sparse Attention.
+
+The functions carry the C ABI's names (lsa_index, lsa_block_means, lsa_select,
+lsa_attend, lsa_workspace_clear) and only marshal arguments: they read shapes and
+device pointers off torch tensors, allocate outputs/workspaces with torch (device
+memory is the only thing torch provides here), pass the current HIP stream, and
+raise on a non-zero status. All computation happens in the library's kernels;
+there is no fallback path. See include/lsa.h for the contract of each call.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from ctypes import POINTER, c_float, c_int32, c_int64, c_size_t, c_void_p
+
+__all__ = ["lib", "LSAError", "lsa_index", "lsa_block_means", "lsa_select", "lsa_attend",
+           "lsa_workspace_clear", "lsa_select_workspace_bytes", "lsa_attend_workspace_bytes",
+           "LSA_BF16", "LSA_FP8_E4M3FN", "LSA_F32", "LSA_INDEX_TOKENS", "LSA_INDEX_BLOCKS",
+           "IndexDesc", "BlockMeansDesc", "SelectDesc", "AttendDesc", "STATUS"]
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(HERE, "liblsa.so")
+
+LSA_BF16, LSA_FP8_E4M3FN, LSA_F32 = 1, 2, 3
+LSA_INDEX_TOKENS, LSA_INDEX_BLOCKS = 0, 1
+STATUS = {0: "LSA_OK", -1: "LSA_E_NULL", -2: "LSA_E_SHAPE", -3: "LSA_E_DTYPE", -4: "LSA_E_BUDGET",
+          -5: "LSA_E_ALIGN", -6: "LSA_E_UNSUPPORTED", -7: "LSA_E_WORKSPACE", -8: "LSA_E_HIP"}
+
+
+class IndexDesc(ctypes.Structure):
+    _fields_ = [("mode", c_int32), ("B", c_int32), ("T", c_int32), ("N", c_int32),
+                ("ctx_len", c_void_p), ("H", c_int32), ("D", c_int32), ("q", c_void_p),
+                ("w", c_void_p), ("k", c_void_p), ("k_dtype", c_int32), ("k_scale", c_void_p),
+                ("kept", c_void_p), ("n_keep", c_int32), ("block_size", c_int32),
+                ("n_blocks", c_int32), ("sink", c_int32), ("window", c_int32), ("scores", c_void_p)]
+
+
+class BlockMeansDesc(ctypes.Structure):
+    _fields_ = [("B", c_int32), ("N", c_int32), ("D", c_int32), ("k", c_void_p), ("k_dtype", c_int32),
+                ("k_scale", c_void_p), ("block_size", c_int32), ("n_blocks", c_int32), ("kbar", c_void_p)]
+
+
+class SelectDesc(ctypes.Structure):
+    _fields_ = [("B", c_int32), ("T", c_int32), ("N", c_int32), ("ctx_len", c_void_p),
+                ("scores", c_void_p), ("n_cols", c_int32), ("kept", c_void_p), ("n_keep", c_int32),
+                ("block_size", c_int32), ("K", c_int32), ("sink", c_int32), ("window", c_int32),
+                ("causal", c_int32), ("idx", c_void_p)]
+
+
+class AttendDesc(ctypes.Structure):
+    _fields_ = [("B", c_int32), ("T", c_int32), ("N", c_int32), ("Hq", c_int32), ("Hkv", c_int32),
+                ("d_qk", c_int32), ("d_v", c_int32), ("q", c_void_p), ("k", c_void_p),
+                ("k_stride_b", c_int64), ("k_stride_n", c_int64), ("k_stride_h", c_int64),
+                ("v", c_void_p), ("v_stride_b", c_int64), ("v_stride_n", c_int64), ("v_stride_h", c_int64),
+                ("idx", c_void_p), ("K", c_int32), ("softmax_scale", c_float), ("out", c_void_p),
+                ("out_dtype", c_int32), ("lse", c_void_p), ("n_layers", c_int32),
+                ("layer_stride_q", c_int64), ("layer_stride_k", c_int64), ("layer_stride_v", c_int64),
+                ("layer_stride_out", c_int64), ("layer_stride_lse", c_int64), ("n_splits", c_int32)]
+
+
+class LSAError(RuntimeError):
+    def __init__(self, fn: str, status: int, msg: str):
+        super().__init__(f"{fn} -> {STATUS.get(status, status)}: {msg}")
+        self.status = status
+
+
+_lib = None
+
+
+def lib():
+    """The loaded liblsa.so (raises when it has not been built)."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(f"{LIB_PATH} is missing: build it with `python -m long_context_sparse_07_amd.build`")
+        L = ctypes.CDLL(LIB_PATH)
+        for name, desc in (("lsa_index", IndexDesc), ("lsa_block_means", BlockMeansDesc)):
+            getattr(L, name).argtypes = [POINTER(desc), c_void_p]
+            getattr(L, name).restype = c_int32
+        L.lsa_select.argtypes = [POINTER(SelectDesc), c_void_p, c_size_t, c_void_p]
+        L.lsa_select.restype = c_int32
+        L.lsa_attend.argtypes = [POINTER(AttendDesc), c_void_p, c_size_t, c_void_p]
+        L.lsa_attend.restype = c_int32
+        L.lsa_select_workspace_bytes.argtypes = [POINTER(SelectDesc)]
+        L.lsa_select_workspace_bytes.restype = c_size_t
+        L.lsa_attend_workspace_bytes.argtypes = [POINTER(AttendDesc)]
+        L.lsa_attend_workspace_bytes.restype = c_size_t
+        L.lsa_workspace_clear.argtypes = [c_void_p, c_size_t, c_void_p]
+        L.lsa_workspace_clear.restype = c_int32
+        L.lsa_status_str.argtypes = [c_int32]
+        L.lsa_status_str.restype = ctypes.c_char_p
+        L.lsa_last_error.argtypes = []
+        L.lsa_last_error.restype = ctypes.c_char_p
+        L.lsa_version.argtypes = []
+        L.lsa_version.restype = c_int32
+        _lib = L
+    return _lib
+
+
+def _check(fn: str, rc: int):
+    if rc != 0:
+        raise LSAError(fn, rc, lib().lsa_last_error().decode())
+
+
+def _ptr(t):
+    return None if t is None else t.data_ptr()
+
+
+def _stream(stream):
+    import torch
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return ctypes.c_void_p(stream.cuda_stream)
+
+
+def _kdtype(t):
+    import torch
+    if t.dtype == torch.bfloat16:
+        return LSA_BF16
+    if t.dtype in (torch.float8_e4m3fn, torch.uint8):
+        return LSA_FP8_E4M3FN
+    if t.dtype == torch.float32:
+        return LSA_F32
+    raise TypeError(f"unsupported key dtype {t.dtype}")
+
+
+# Workspaces are cached per (device, kind) and grown on demand. The select workspace
+# must be all-zero before first use; it is cleared by the library's fill kernel.
+_ws = {}
+
+
+def _workspace(kind: str, nbytes: int, device, stream):
+    import torch
+    key = (kind, str(device))
+    buf = _ws.get(key)
+    if buf is None or buf.numel() < nbytes:
+        buf = torch.empty(max(nbytes, 256), dtype=torch.uint8, device=device)
+        if kind == "select":
+            _check("lsa_workspace_clear", lib().lsa_workspace_clear(buf.data_ptr(), buf.numel(), stream))
+        _ws[key] = buf
+    return buf
+
+
+def lsa_workspace_clear(buf, stream=None):
+    _check("lsa_workspace_clear", lib().lsa_workspace_clear(buf.data_ptr(), buf.numel() * buf.element_size(), _stream(stream)))
+
+
+def lsa_index(q, w, k, *, k_scale=None, ctx_len=None, kept=None, block_size=0, mode=LSA_INDEX_TOKENS,
+              N=None, n_blocks=0, sink=0, window=0, scores=None, stream=None):
+    """Indexer scores. q bf16 [B,T,H,D], w fp32 [B,T,H]; k bf16/fp8 [B,N,D] (tokens) or
+    fp32 block means [B,n_blocks,D] (mode=LSA_INDEX_BLOCKS, N = cache rows)."""
+    import torch
+    B, T, H, D = q.shape
+    if mode == LSA_INDEX_TOKENS:
+        N = k.shape[1] if N is None else N
+        n_keep = kept.shape[-1] if kept is not None else 0
+        n_out = n_keep * block_size if kept is not None else N
+    else:
+        n_blocks = n_blocks or k.shape[1]
+        n_keep = 0
+        n_out = n_blocks
+    if scores is None:
+        scores = torch.empty((B, T, n_out), dtype=torch.float32, device=q.device)
+    d = IndexDesc(mode=mode, B=B, T=T, N=N, ctx_len=_ptr(ctx_len), H=H, D=D, q=_ptr(q), w=_ptr(w), k=_ptr(k),
+                  k_dtype=_kdtype(k), k_scale=_ptr(k_scale), kept=_ptr(kept), n_keep=n_keep,
+                  block_size=block_size, n_blocks=n_blocks, sink=sink, window=window, scores=_ptr(scores))
+    _check("lsa_index", lib().lsa_index(ctypes.byref(d), _stream(stream)))
+    return scores
+
+
+def lsa_block_means(k, block_size, *, k_scale=None, n_blocks=None, kbar=None, stream=None):
+    import torch
+    B, N, D = k.shape
+    n_blocks = N // block_size if n_blocks is None else n_blocks
+    if kbar is None:
+        kbar = torch.empty((B, n_blocks, D), dtype=torch.float32, device=k.device)
+    d = BlockMeansDesc(B=B, N=N, D=D, k=_ptr(k), k_dtype=_kdtype(k), k_scale=_ptr(k_scale),
+                       block_size=block_size, n_blocks=n_blocks, kbar=_ptr(kbar))
+    _check("lsa_block_means", lib().lsa_block_means(ctypes.byref(d), _stream(stream)))
+    return kbar
+
+
+def _select_desc(scores, K, sink, window, N, ctx_len, kept, block_size, causal, idx):
+    B, T, n_cols = scores.shape
+    return SelectDesc(B=B, T=T, N=N, ctx_len=_ptr(ctx_len), scores=_ptr(scores), n_cols=n_cols,
+                      kept=_ptr(kept), n_keep=kept.shape[-1] if kept is not None else 0,
+                      block_size=block_size, K=K, sink=sink, window=window, causal=int(causal),
+                      idx=_ptr(idx))
+
+
+def lsa_select_workspace_bytes(scores, K, sink=0, window=0, *, N=None, kept=None, block_size=0, causal=True):
+    d = _select_desc(scores, K, sink, window, N or scores.shape[-1], None, kept, block_size, causal, None)
+    return lib().lsa_select_workspace_bytes(ctypes.byref(d))
+
+
+def lsa_select(scores, K, sink=0, window=0, *, N=None, ctx_len=None, kept=None, block_size=0, causal=True,
+               idx=None, workspace=None, stream=None):
+    """SI selection: idx int32 [B,T,K], ascending, -1 padded."""
+    import torch
+    B, T, n_cols = scores.shape
+    N = n_cols if N is None else N
+    if idx is None:
+        idx = torch.empty((B, T, K), dtype=torch.int32, device=scores.device)
+    d = _select_desc(scores, K, sink, window, N, ctx_len, kept, block_size, causal, idx)
+    s = _stream(stream)
+    need = lib().lsa_select_workspace_bytes(ctypes.byref(d))
+    ws = workspace if workspace is not None else _workspace("select", need, scores.device, s)
+    _check("lsa_select", lib().lsa_select(ctypes.byref(d), ws.data_ptr(), ws.numel() * ws.element_size(), s))
+    return idx
+
+
+def _attend_desc(q, k, v, idx, softmax_scale, out, lse, mla, n_splits):
+    """q [L,B,T,Hq,dqk]; k,v [L,B,N,Hkv,d] (contiguous per layer). MLA: k [L,B,N,1,576], v=None."""
+    L, B, T, Hq, dqk = q.shape
+    N, Hkv = k.shape[2], k.shape[3]
+    if mla:
+        v = k
+        dv = 512
+    else:
+        dv = v.shape[-1]
+    K = idx.shape[-1]
+    return AttendDesc(B=B, T=T, N=N, Hq=Hq, Hkv=Hkv, d_qk=dqk, d_v=dv, q=_ptr(q), k=_ptr(k),
+                      k_stride_b=k.stride(1), k_stride_n=k.stride(2), k_stride_h=k.stride(3),
+                      v=_ptr(v), v_stride_b=v.stride(1), v_stride_n=v.stride(2), v_stride_h=v.stride(3),
+                      idx=_ptr(idx), K=K, softmax_scale=softmax_scale, out=_ptr(out),
+                      out_dtype=LSA_F32 if out is not None and out.dtype.is_floating_point and out.element_size() == 4 else LSA_BF16,
+                      lse=_ptr(lse), n_layers=L, layer_stride_q=q.stride(0), layer_stride_k=k.stride(0),
+                      layer_stride_v=v.stride(0), layer_stride_out=out.stride(0) if out is not None else 0,
+                      layer_stride_lse=lse.stride(0) if lse is not None else 0, n_splits=n_splits)
+
+
+def lsa_attend(q, k, v, idx, softmax_scale, *, out=None, lse=None, out_dtype=None, with_lse=True,
+               n_splits=0, workspace=None, stream=None):
+    """Sparse attention for L layers sharing idx. q bf16 [L,B,T,Hq,dqk]; k, v bf16
+    [L,B,N,Hkv,d] (v=None: MLA latent rows, V = k[..., :512]); idx int32 [B,T,K].
+    Returns (out [L,B,T,Hq,dv], lse fp32 [L,B,T,Hq] or None)."""
+    import torch
+    L, B, T, Hq, dqk = q.shape
+    mla = v is None
+    dv = 512 if mla else v.shape[-1]
+    if out is None:
+        out = torch.empty((L, B, T, Hq, dv), dtype=out_dtype or torch.bfloat16, device=q.device)
+    if lse is None and with_lse:
+        lse = torch.empty((L, B, T, Hq), dtype=torch.float32, device=q.device)
+    d = _attend_desc(q, k, v, idx, softmax_scale, out, lse, mla, n_splits)
+    s = _stream(stream)
+    need = lib().lsa_attend_workspace_bytes(ctypes.byref(d))
+    ws = workspace if workspace is not None else (_workspace("attend", need, q.device, s) if need else None)
+    _check("lsa_attend", lib().lsa_attend(ctypes.byref(d), _ptr(ws), 0 if ws is None else ws.numel(), s))
+    return out, lse

@@ -1,0 +1,300 @@
+// C ABI of liblsa.so: argument validation (host only, before any HIP call) and
+// dispatch to the gfx950 kernels. See include/lsa.h for the contract.
+#include <hip/hip_runtime.h>
+
+#include <cstdarg>
+#include <cstdint>
+#include <cstdio>
+#include <cstring>
+
+#include "../../include/lsa.h"
+#include "kernels.h"
+
+namespace {
+
+thread_local char g_err[512] = "";
+
+int32_t fail(int32_t code, const char *fmt, ...) {
+    va_list ap;
+    va_start(ap, fmt);
+    vsnprintf(g_err, sizeof(g_err), fmt, ap);
+    va_end(ap);
+    return code;
+}
+
+int32_t hip_status(hipError_t e, const char *what) {
+    if (e == hipSuccess) return LSA_OK;
+    return fail(LSA_E_HIP, "%s: %s", what, hipGetErrorString(e));
+}
+
+bool aligned16(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+bool aligned4(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 3u) == 0; }
+
+constexpr int64_t kMaxGridY = 65535;
+
+}  // namespace
+
+extern "C" {
+
+int32_t lsa_version(void) { return LSA_VERSION; }
+
+const char *lsa_status_str(int32_t s) {
+    switch (s) {
+        case LSA_OK: return "LSA_OK";
+        case LSA_E_NULL: return "LSA_E_NULL: a required pointer is NULL";
+        case LSA_E_SHAPE: return "LSA_E_SHAPE: a size is out of range or inconsistent";
+        case LSA_E_DTYPE: return "LSA_E_DTYPE: unknown or unsupported dtype";
+        case LSA_E_BUDGET: return "LSA_E_BUDGET: K < 1 or sink + window > K";
+        case LSA_E_ALIGN: return "LSA_E_ALIGN: pointer or stride not 16-byte aligned";
+        case LSA_E_UNSUPPORTED: return "LSA_E_UNSUPPORTED: no kernel for this shape";
+        case LSA_E_WORKSPACE: return "LSA_E_WORKSPACE: workspace missing or too small";
+        case LSA_E_HIP: return "LSA_E_HIP: a HIP launch failed";
+        default: return "unknown lsa status";
+    }
+}
+
+const char *lsa_last_error(void) { return g_err; }
+
+// ----------------------------------------------------------------------------- index
+
+int32_t lsa_index(const lsa_index_desc *d, void *stream) {
+    if (!d) return fail(LSA_E_NULL, "lsa_index: desc is NULL");
+    if (!d->q || !d->w || !d->k || !d->scores) return fail(LSA_E_NULL, "lsa_index: q, w, k and scores are required");
+    if (d->B < 1 || d->T < 1 || d->N < 1 || d->H < 1 || d->D < 1)
+        return fail(LSA_E_SHAPE, "lsa_index: B, T, N, H, D must be >= 1 (got %d %d %d %d %d)", d->B, d->T, d->N, d->H, d->D);
+    if (d->T > d->N) return fail(LSA_E_SHAPE, "lsa_index: T=%d exceeds N=%d", d->T, d->N);
+    if (!aligned16(d->q) || !aligned16(d->k) || !aligned4(d->w) || !aligned16(d->scores))
+        return fail(LSA_E_ALIGN, "lsa_index: q, k, scores must be 16-byte aligned");
+    if (d->B > kMaxGridY) return fail(LSA_E_UNSUPPORTED, "lsa_index: B=%d too large", d->B);
+    hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+    if (d->mode == LSA_INDEX_TOKENS) {
+        if (d->k_dtype != LSA_BF16 && d->k_dtype != LSA_FP8_E4M3FN)
+            return fail(LSA_E_DTYPE, "lsa_index: TOKENS keys must be bf16 or fp8-e4m3fn (got %d)", d->k_dtype);
+        const bool fp8 = d->k_dtype == LSA_FP8_E4M3FN;
+        if (fp8 && !d->k_scale) return fail(LSA_E_NULL, "lsa_index: fp8 keys need k_scale");
+        const bool hi = d->kept != nullptr;
+        if (hi) {
+            if (d->n_keep < 1 || d->block_size < 1)
+                return fail(LSA_E_SHAPE, "lsa_index: HI fine stage needs n_keep >= 1 and block_size >= 1");
+            if ((int64_t)d->n_keep * d->block_size > INT32_MAX / 2)
+                return fail(LSA_E_SHAPE, "lsa_index: n_keep * block_size too large");
+            if (d->T > kMaxGridY) return fail(LSA_E_UNSUPPORTED, "lsa_index: T=%d too large", d->T);
+        }
+        if (!lsa::index_tokens_supported(d->H, d->D, hi))
+            return fail(LSA_E_UNSUPPORTED, "lsa_index: no token kernel for H=%d D=%d%s", d->H, d->D, hi ? " (HI)" : "");
+        lsa::IndexTokensArgs a{};
+        a.B = d->B;
+        a.T = d->T;
+        a.N = d->N;
+        a.H = d->H;
+        a.D = d->D;
+        a.ctx_len = d->ctx_len;
+        a.q = reinterpret_cast<const uint16_t *>(d->q);
+        a.w = d->w;
+        a.k = d->k;
+        a.fp8 = fp8;
+        a.k_scale = fp8 ? d->k_scale : nullptr;
+        a.kept = d->kept;
+        a.n_keep = hi ? d->n_keep : 0;
+        a.block_size = hi ? d->block_size : 0;
+        a.scores = d->scores;
+        a.n_out = hi ? d->n_keep * d->block_size : d->N;
+        return hip_status(lsa::launch_index_tokens(a, s), "lsa_index");
+    }
+    if (d->mode == LSA_INDEX_BLOCKS) {
+        if (d->k_dtype != LSA_F32) return fail(LSA_E_DTYPE, "lsa_index: BLOCKS mode reads fp32 block means");
+        if (d->block_size < 1 || d->n_blocks < 1 || (int64_t)d->n_blocks * d->block_size > d->N)
+            return fail(LSA_E_SHAPE, "lsa_index: BLOCKS needs block_size >= 1, 1 <= n_blocks <= N / block_size");
+        if (d->sink < 0 || d->window < 0) return fail(LSA_E_SHAPE, "lsa_index: sink and window must be >= 0");
+        if (d->D != 64 && d->D != 128) return fail(LSA_E_UNSUPPORTED, "lsa_index: BLOCKS needs D in {64,128}");
+        if (d->H > 64) return fail(LSA_E_UNSUPPORTED, "lsa_index: BLOCKS needs H <= 64");
+        if (d->T > kMaxGridY) return fail(LSA_E_UNSUPPORTED, "lsa_index: T=%d too large", d->T);
+        lsa::IndexBlocksArgs a{};
+        a.B = d->B;
+        a.T = d->T;
+        a.N = d->N;
+        a.H = d->H;
+        a.D = d->D;
+        a.ctx_len = d->ctx_len;
+        a.q = reinterpret_cast<const uint16_t *>(d->q);
+        a.w = d->w;
+        a.kbar = reinterpret_cast<const float *>(d->k);
+        a.n_blocks = d->n_blocks;
+        a.block_size = d->block_size;
+        a.sink = d->sink;
+        a.window = d->window;
+        a.scores = d->scores;
+        return hip_status(lsa::launch_index_blocks(a, s), "lsa_index");
+    }
+    return fail(LSA_E_SHAPE, "lsa_index: unknown mode %d", d->mode);
+}
+
+int32_t lsa_block_means(const lsa_block_means_desc *d, void *stream) {
+    if (!d) return fail(LSA_E_NULL, "lsa_block_means: desc is NULL");
+    if (!d->k || !d->kbar) return fail(LSA_E_NULL, "lsa_block_means: k and kbar are required");
+    if (d->k_dtype != LSA_BF16 && d->k_dtype != LSA_FP8_E4M3FN)
+        return fail(LSA_E_DTYPE, "lsa_block_means: keys must be bf16 or fp8-e4m3fn");
+    const bool fp8 = d->k_dtype == LSA_FP8_E4M3FN;
+    if (fp8 && !d->k_scale) return fail(LSA_E_NULL, "lsa_block_means: fp8 keys need k_scale");
+    if (d->B < 1 || d->N < 1 || d->block_size < 1 || d->n_blocks < 1 ||
+        (int64_t)d->n_blocks * d->block_size > d->N)
+        return fail(LSA_E_SHAPE, "lsa_block_means: need B, N, block_size, n_blocks >= 1 and n_blocks*block_size <= N");
+    if (d->D != 64 && d->D != 128) return fail(LSA_E_UNSUPPORTED, "lsa_block_means: D must be 64 or 128");
+    if (d->B > kMaxGridY) return fail(LSA_E_UNSUPPORTED, "lsa_block_means: B too large");
+    lsa::BlockMeansArgs a{};
+    a.B = d->B;
+    a.N = d->N;
+    a.D = d->D;
+    a.k = d->k;
+    a.fp8 = fp8;
+    a.k_scale = fp8 ? d->k_scale : nullptr;
+    a.block_size = d->block_size;
+    a.n_blocks = d->n_blocks;
+    a.kbar = d->kbar;
+    return hip_status(lsa::launch_block_means(a, reinterpret_cast<hipStream_t>(stream)), "lsa_block_means");
+}
+
+// ----------------------------------------------------------------------------- select
+
+static int32_t select_check(const lsa_select_desc *d, lsa::SelectArgs &a) {
+    if (!d) return fail(LSA_E_NULL, "lsa_select: desc is NULL");
+    if (d->B < 1 || d->T < 1 || d->N < 1 || d->n_cols < 1)
+        return fail(LSA_E_SHAPE, "lsa_select: B, T, N, n_cols must be >= 1");
+    if (d->K < 1 || d->sink < 0 || d->window < 0 || (int64_t)d->sink + d->window > d->K)
+        return fail(LSA_E_BUDGET, "lsa_select: need K >= 1 and 0 <= sink + window <= K (K=%d sink=%d window=%d)", d->K,
+                    d->sink, d->window);
+    if (d->K > 4096) return fail(LSA_E_UNSUPPORTED, "lsa_select: K=%d above 4096", d->K);
+    if (!d->causal && (d->sink || d->window))
+        return fail(LSA_E_BUDGET, "lsa_select: sink and window need causal = 1");
+    if (d->kept && (d->n_keep < 1 || d->block_size < 1 || (int64_t)d->n_keep * d->block_size < d->n_cols))
+        return fail(LSA_E_SHAPE, "lsa_select: a kept map needs n_keep * block_size >= n_cols");
+    if ((int64_t)d->B * d->T > kMaxGridY) return fail(LSA_E_UNSUPPORTED, "lsa_select: B*T too large");
+    a = lsa::SelectArgs{};
+    a.B = d->B;
+    a.T = d->T;
+    a.N = d->N;
+    a.ctx_len = d->ctx_len;
+    a.scores = d->scores;
+    a.n_cols = d->n_cols;
+    a.kept = d->kept;
+    a.n_keep = d->kept ? d->n_keep : 0;
+    a.block_size = d->kept ? d->block_size : 1;
+    a.K = d->K;
+    a.sink = d->sink;
+    a.window = d->window;
+    a.causal = d->causal != 0;
+    a.idx = d->idx;
+    return LSA_OK;
+}
+
+size_t lsa_select_workspace_bytes(const lsa_select_desc *d) {
+    lsa::SelectArgs a;
+    if (select_check(d, a) != LSA_OK) return 0;
+    return lsa::select_workspace_bytes(a);
+}
+
+int32_t lsa_select(const lsa_select_desc *d, void *ws, size_t ws_bytes, void *stream) {
+    lsa::SelectArgs a;
+    int32_t rc = select_check(d, a);
+    if (rc != LSA_OK) return rc;
+    if (!d->scores || !d->idx) return fail(LSA_E_NULL, "lsa_select: scores and idx are required");
+    if (!aligned4(d->scores) || !aligned4(d->idx)) return fail(LSA_E_ALIGN, "lsa_select: misaligned scores or idx");
+    const size_t need = lsa::select_workspace_bytes(a);
+    if (!ws || ws_bytes < need)
+        return fail(LSA_E_WORKSPACE, "lsa_select: workspace of %zu bytes needed, %zu given", need, ws_bytes);
+    if ((reinterpret_cast<uintptr_t>(ws) & 255u) != 0) return fail(LSA_E_ALIGN, "lsa_select: workspace not 256-byte aligned");
+    return hip_status(lsa::launch_select(a, ws, reinterpret_cast<hipStream_t>(stream)), "lsa_select");
+}
+
+// ----------------------------------------------------------------------------- attend
+
+static int32_t attend_check(const lsa_attend_desc *d, lsa::AttendArgs &a) {
+    if (!d) return fail(LSA_E_NULL, "lsa_attend: desc is NULL");
+    if (d->B < 1 || d->T < 1 || d->N < 1 || d->Hq < 1 || d->Hkv < 1 || d->n_layers < 1)
+        return fail(LSA_E_SHAPE, "lsa_attend: B, T, N, Hq, Hkv, n_layers must be >= 1");
+    if (d->K < 1) return fail(LSA_E_BUDGET, "lsa_attend: K must be >= 1");
+    if (d->Hq % d->Hkv) return fail(LSA_E_SHAPE, "lsa_attend: Hq=%d not a multiple of Hkv=%d", d->Hq, d->Hkv);
+    const int g = d->Hq / d->Hkv;
+    if (!lsa::attend_supported(d->d_qk, d->d_v, g))
+        return fail(LSA_E_UNSUPPORTED, "lsa_attend: no kernel for d_qk=%d d_v=%d group=%d", d->d_qk, d->d_v, g);
+    if (d->out_dtype != LSA_BF16 && d->out_dtype != LSA_F32) return fail(LSA_E_DTYPE, "lsa_attend: out must be bf16 or f32");
+    const int64_t strides[] = {d->k_stride_b, d->k_stride_n, d->k_stride_h, d->v_stride_b, d->v_stride_n, d->v_stride_h,
+                               d->layer_stride_k, d->layer_stride_v, d->layer_stride_q};
+    for (int64_t st : strides)
+        if (st < 0 || st % 8) return fail(LSA_E_ALIGN, "lsa_attend: strides must be non-negative multiples of 8 elements");
+    if (d->n_layers > 1 && (d->layer_stride_out % 8 || d->layer_stride_lse < 0 || d->layer_stride_out < 0))
+        return fail(LSA_E_ALIGN, "lsa_attend: output layer stride must be a multiple of 8 elements");
+    if (d->d_qk == 576 && (d->v != d->k || d->v_stride_b != d->k_stride_b || d->v_stride_n != d->k_stride_n ||
+                           d->v_stride_h != d->k_stride_h || d->layer_stride_v != d->layer_stride_k))
+        return fail(LSA_E_UNSUPPORTED, "lsa_attend: d_qk=576 is the MLA latent layout: v must alias k with equal strides");
+    if ((int64_t)d->T * d->Hkv > kMaxGridY || (int64_t)d->B * d->n_layers > kMaxGridY)
+        return fail(LSA_E_UNSUPPORTED, "lsa_attend: grid too large");
+    if (d->n_splits < 0) return fail(LSA_E_SHAPE, "lsa_attend: n_splits must be >= 0");
+    a = lsa::AttendArgs{};
+    a.B = d->B;
+    a.T = d->T;
+    a.N = d->N;
+    a.Hq = d->Hq;
+    a.Hkv = d->Hkv;
+    a.d_qk = d->d_qk;
+    a.d_v = d->d_v;
+    a.q = reinterpret_cast<const uint16_t *>(d->q);
+    a.k = reinterpret_cast<const uint16_t *>(d->k);
+    a.ksb = d->k_stride_b;
+    a.ksn = d->k_stride_n;
+    a.ksh = d->k_stride_h;
+    a.v = reinterpret_cast<const uint16_t *>(d->v);
+    a.vsb = d->v_stride_b;
+    a.vsn = d->v_stride_n;
+    a.vsh = d->v_stride_h;
+    a.idx = d->idx;
+    a.K = d->K;
+    a.scale = d->softmax_scale;
+    a.out = d->out;
+    a.out_f32 = d->out_dtype == LSA_F32;
+    a.lse = d->lse;
+    a.L = d->n_layers;
+    a.lsq = d->layer_stride_q;
+    a.lsk = d->layer_stride_k;
+    a.lsv = d->layer_stride_v;
+    a.lso = d->layer_stride_out;
+    a.lsl = d->layer_stride_lse;
+    a.n_splits = 1;
+    int sp = d->n_splits > 0 ? d->n_splits : lsa::attend_default_splits(a);
+    const int smin = (d->K + 2047) / 2048;
+    if (sp < smin) sp = smin;
+    if (sp > (d->K + 31) / 32) sp = (d->K + 31) / 32;
+    a.n_splits = sp;
+    return LSA_OK;
+}
+
+size_t lsa_attend_workspace_bytes(const lsa_attend_desc *d) {
+    lsa::AttendArgs a;
+    if (attend_check(d, a) != LSA_OK) return 0;
+    return lsa::attend_workspace_bytes(a);
+}
+
+int32_t lsa_attend(const lsa_attend_desc *d, void *ws, size_t ws_bytes, void *stream) {
+    lsa::AttendArgs a;
+    int32_t rc = attend_check(d, a);
+    if (rc != LSA_OK) return rc;
+    if (!d->q || !d->k || !d->v || !d->idx || !d->out) return fail(LSA_E_NULL, "lsa_attend: q, k, v, idx, out are required");
+    if (!aligned16(d->q) || !aligned16(d->k) || !aligned16(d->v) || !aligned16(d->out) || !aligned4(d->idx) ||
+        (d->lse && !aligned4(d->lse)))
+        return fail(LSA_E_ALIGN, "lsa_attend: q, k, v, out must be 16-byte aligned");
+    const size_t need = lsa::attend_workspace_bytes(a);
+    if (need && (!ws || ws_bytes < need))
+        return fail(LSA_E_WORKSPACE, "lsa_attend: workspace of %zu bytes needed, %zu given", need, ws_bytes);
+    if (need && (reinterpret_cast<uintptr_t>(ws) & 255u) != 0)
+        return fail(LSA_E_ALIGN, "lsa_attend: workspace not 256-byte aligned");
+    return hip_status(lsa::launch_attend(a, ws, reinterpret_cast<hipStream_t>(stream)), "lsa_attend");
+}
+
+int32_t lsa_workspace_clear(void *ptr, size_t bytes, void *stream) {
+    if (bytes == 0) return LSA_OK;
+    if (!ptr) return fail(LSA_E_NULL, "lsa_workspace_clear: ptr is NULL");
+    if (!aligned16(ptr)) return fail(LSA_E_ALIGN, "lsa_workspace_clear: ptr must be 16-byte aligned");
+    return hip_status(lsa::launch_clear(ptr, bytes, reinterpret_cast<hipStream_t>(stream)), "lsa_workspace_clear");
+}
+
+}  // extern "C"

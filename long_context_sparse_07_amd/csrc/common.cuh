@@ -1,0 +1,87 @@
+// Device helpers shared by the LSA kernels (gfx950 / CDNA4, wave64).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace lsa {
+
+typedef __attribute__((__vector_size__(8 * sizeof(__bf16)))) __bf16 bf16x8;
+typedef __attribute__((__vector_size__(4 * sizeof(float)))) float f32x4;
+typedef __attribute__((__vector_size__(16 * sizeof(float)))) float f32x16;
+typedef __attribute__((__vector_size__(2 * sizeof(float)))) float f32x2;
+typedef __attribute__((__vector_size__(4 * sizeof(uint32_t)))) uint32_t u32x4;
+
+constexpr float kNegInf = -__builtin_inff();
+
+__device__ __forceinline__ int lane_id() { return __lane_id(); }
+
+// ---- MFMA (gfx950). Lane layouts verified on the device:
+// 16x16x32: A lane l holds A[l%16][8*(l/16)+e], B lane l holds B[8*(l/16)+e][l%16],
+//           D lane l holds D[4*(l/16)+r][l%16], r = 0..3.
+// 32x32x16: A lane l holds A[l%32][8*(l/32)+e], B lane l holds B[8*(l/32)+e][l%32],
+//           D lane l holds D[8*(r/4)+4*(l/32)+r%4][l%32], r = 0..15.
+__device__ __forceinline__ f32x4 mfma16(bf16x8 a, bf16x8 b, f32x4 c) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+}
+__device__ __forceinline__ f32x16 mfma32(bf16x8 a, bf16x8 b, f32x16 c) {
+    return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+}
+
+// ---- bit casts
+__device__ __forceinline__ uint32_t f2u(float x) { return __builtin_bit_cast(uint32_t, x); }
+__device__ __forceinline__ float u2f(uint32_t x) { return __builtin_bit_cast(float, x); }
+
+// bf16 bits -> fp32 (exact)
+__device__ __forceinline__ float bf16lo(uint32_t two) { return u2f(two << 16); }
+__device__ __forceinline__ float bf16hi(uint32_t two) { return u2f(two & 0xFFFF0000u); }
+
+// fp32 -> bf16 bits, round to nearest even (finite values)
+__device__ __forceinline__ uint32_t f2bf(float x) {
+    uint32_t u = f2u(x);
+    u += 0x7FFFu + ((u >> 16) & 1u);
+    return u >> 16;
+}
+__device__ __forceinline__ uint32_t pack_bf16(float lo, float hi) { return f2bf(lo) | (f2bf(hi) << 16); }
+
+// Upper halves of two fp32 words -> one packed bf16 pair (exact for values that are
+// already bf16-representable, e.g. widened fp8).
+__device__ __forceinline__ uint32_t hi_halves(uint32_t lo_word, uint32_t hi_word) {
+    return __builtin_amdgcn_perm(hi_word, lo_word, 0x07060302u);
+}
+
+// Four OCP e4m3fn bytes (one dword) -> four bf16 (two dwords), exact.
+__device__ __forceinline__ void fp8x4_to_bf16x4(uint32_t v, uint32_t &o0, uint32_t &o1) {
+    f32x2 a = __builtin_amdgcn_cvt_pk_f32_fp8(v, false);
+    f32x2 b = __builtin_amdgcn_cvt_pk_f32_fp8(v, true);
+    o0 = hi_halves(f2u(a[0]), f2u(a[1]));
+    o1 = hi_halves(f2u(b[0]), f2u(b[1]));
+}
+
+// 16 fp8 bytes -> two bf16x8 fragments (first 8 bytes, last 8 bytes).
+__device__ __forceinline__ void fp8x16_to_frags(u32x4 v, bf16x8 &f0, bf16x8 &f1) {
+    uint32_t a0, a1, a2, a3, b0, b1, b2, b3;
+    fp8x4_to_bf16x4(v[0], a0, a1);
+    fp8x4_to_bf16x4(v[1], a2, a3);
+    fp8x4_to_bf16x4(v[2], b0, b1);
+    fp8x4_to_bf16x4(v[3], b2, b3);
+    u32x4 a = {a0, a1, a2, a3};
+    u32x4 b = {b0, b1, b2, b3};
+    f0 = __builtin_bit_cast(bf16x8, a);
+    f1 = __builtin_bit_cast(bf16x8, b);
+}
+
+// ---- order-preserving fp32 -> uint32 map (larger float -> larger key).
+// -0.0 is folded onto +0.0 first so that the two compare equal.
+__device__ __forceinline__ uint32_t order_key(float x) {
+    uint32_t u = f2u(x + 0.0f);
+    return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+}
+
+// ---- wave reductions (wave64)
+__device__ __forceinline__ float wave_xor_f(float v, int mask) { return __shfl_xor(v, mask, 64); }
+
+template <typename T>
+__device__ __forceinline__ T ld_nt(const T *p) { return __builtin_nontemporal_load(p); }
+
+}  // namespace lsa

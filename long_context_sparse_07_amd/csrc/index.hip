@@ -1,0 +1,409 @@
+// Indexer kernels of the LSA hot path on gfx950.
+//
+// index_tokens_kernel: I[t,s] = scale[s] * sum_h w[t,h] * ReLU(q[t,h] . k[s]) (reading R1
+// of the DSA-style indexer that LSA extends, molayo1419.me LongCat-2.0 article, section
+// "The sparse attention problem at 1M tokens"). The key cache is streamed once, HBM
+// coalesced, into an LDS tile; the (query-head rows) x (keys) contraction runs on
+// v_mfma_f32_32x32x16_bf16 with fp8 keys widened exactly to bf16 in registers; the
+// ReLU, head weights, head sum, per-token scale and causal mask are fused into the
+// MFMA epilogue.
+//
+// index_blocks_kernel: coarse HI block scores max_h w * ReLU(q . kbar) in fp32 (VALU),
+// so that the block means are not rounded to bf16 (LongCat-Flash-Lite-Sparse summary,
+// "Technical features", third bullet: coarse candidate blocks first).
+//
+// block_means_kernel: kbar[j] = mean of the dequantised keys of block j, fp32.
+#include "common.cuh"
+#include "kernels.h"
+
+namespace lsa {
+namespace {
+
+constexpr int kThreads = 256;
+constexpr int kKT = 128;  // keys per LDS tile (4 waves x 32)
+
+// Query-row layouts of one MFMA row group.
+enum { ONEQ = 0, Q4 = 4, Q8 = 8, Q16 = 16 };
+
+template <int D, bool FP8>
+struct Tile {
+    static constexpr int RB = FP8 ? D : 2 * D;        // bytes per key row
+    static constexpr int CPR = RB / 16;               // 16-byte chunks per row
+    static constexpr int NCH = kKT * CPR / kThreads;  // chunks per thread per tile
+    static constexpr int BYTES = kKT * RB;
+    static constexpr int RPB = CPR >= 16 ? 1 : 16 / CPR;  // rows per 256-byte bank row
+    // XOR swizzle of the 16-byte chunks: 16 lanes reading the same logical chunk of
+    // 16 consecutive rows land on 16 distinct groups of 4 banks.
+    __device__ static __forceinline__ int swz(int row, int c) { return c ^ ((row / RPB) & (CPR - 1)); }
+};
+
+// Row i of the (query, head) row space of group `grp` -> (t, h); ok = a real row.
+template <int MODE>
+__device__ __forceinline__ void row_to_th(int grp, int i, int H, int T, int &t, int &h, bool &ok) {
+    if constexpr (MODE == ONEQ) {
+        t = grp;
+        h = i;
+        ok = (i < H) && (t < T);
+    } else {
+        constexpr int QPG = 32 / MODE;
+        t = grp * QPG + i / MODE;
+        h = i % MODE;
+        ok = t < T;
+    }
+}
+
+template <int D, bool FP8, int MODE, int HB, bool HI, bool PRE>
+__global__ __launch_bounds__(kThreads) void index_tokens_kernel(IndexTokensArgs a, int groups, int chunk) {
+    using G = Tile<D, FP8>;
+    constexpr int KSTEPS = D / 16;
+    constexpr int QPG = MODE == ONEQ ? 1 : 32 / MODE;
+    __shared__ __attribute__((aligned(16))) unsigned char tile[G::BYTES];
+    __shared__ float tscale[kKT];
+    __shared__ int tpos[kKT];
+
+    const int tid = threadIdx.x;
+    const int lane = tid & 63, wave = tid >> 6, half = lane >> 5, l32 = lane & 31;
+    const int b = blockIdx.z;
+    const int c0 = blockIdx.x * chunk;
+    if (c0 >= a.n_out) return;
+    const int c1 = min(a.n_out, c0 + chunk);
+    const int T = a.T, H = a.H, N = a.N;
+    int ctx = a.ctx_len ? a.ctx_len[b] : N;
+    ctx = min(max(ctx, 0), N);
+
+    const int grp = PRE ? blockIdx.y * 4 + wave : blockIdx.y;
+    const bool active = grp < groups;
+
+    // ---- query fragments (A operand, rows = query heads) and head weights
+    bf16x8 aq[HB][KSTEPS];
+    float wreg[HB][16];
+#pragma unroll
+    for (int hb = 0; hb < HB; ++hb) {
+        int t, h;
+        bool ok;
+        row_to_th<MODE>(grp, 32 * hb + l32, H, T, t, h, ok);
+        ok = ok && active;
+        const uint16_t *qrow = a.q + ((int64_t)(b * T + t) * H + h) * D + (D / 2) * half;
+#pragma unroll
+        for (int ks = 0; ks < KSTEPS; ++ks) {
+            u32x4 v = {0, 0, 0, 0};
+            if (ok) v = *reinterpret_cast<const u32x4 *>(qrow + 8 * ks);
+            aq[hb][ks] = __builtin_bit_cast(bf16x8, v);
+        }
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+            int i = 32 * hb + 8 * (r / 4) + 4 * half + (r % 4);
+            row_to_th<MODE>(grp, i, H, T, t, h, ok);
+            wreg[hb][r] = (ok && active) ? a.w[(int64_t)(b * T + t) * H + h] : 0.0f;
+        }
+    }
+
+    // Last visible position over every query of this workgroup (flat mode skips tiles past it).
+    int last_t;
+    if constexpr (PRE) last_t = min(T - 1, (int)blockIdx.y * 4 + 3);
+    else last_t = min(T - 1, grp * QPG + QPG - 1);
+    const int maxp = ctx - T + last_t;
+
+    // HI: the query whose kept list maps columns to positions (one query per group).
+    const int32_t *kept_row = HI ? a.kept + (int64_t)(b * T + grp) * a.n_keep : nullptr;
+    const int nblk_cache = HI ? N / a.block_size : 0;
+
+    auto col_pos = [&](int col) -> int {  // position of a column, -1 if none
+        if (col >= c1) return -1;
+        if constexpr (HI) {
+            int blk = col / a.block_size;
+            int kb = kept_row[blk];
+            if (kb < 0 || kb >= nblk_cache) return -1;
+            return kb * a.block_size + (col - blk * a.block_size);
+        } else {
+            return col < N ? col : -1;
+        }
+    };
+
+    const unsigned char *kbase = reinterpret_cast<const unsigned char *>(a.k) + (int64_t)b * N * G::RB;
+    u32x4 pre[G::NCH];
+    float pscale = 0.0f;
+    int ppos = -1;
+
+    auto load_tile = [&](int tc0) {
+#pragma unroll
+        for (int j = 0; j < G::NCH; ++j) {
+            int id = j * kThreads + tid;
+            int row = id / G::CPR, c = id % G::CPR;
+            int pos = col_pos(tc0 + row);
+            u32x4 v = {0, 0, 0, 0};
+            if (pos >= 0) v = *reinterpret_cast<const u32x4 *>(kbase + (int64_t)pos * G::RB + c * 16);
+            pre[j] = v;
+        }
+        if (tid < kKT) {
+            ppos = col_pos(tc0 + tid);
+            if constexpr (FP8) pscale = ppos >= 0 ? a.k_scale[(int64_t)b * N + ppos] : 0.0f;
+        }
+    };
+    auto store_tile = [&]() {
+#pragma unroll
+        for (int j = 0; j < G::NCH; ++j) {
+            int id = j * kThreads + tid;
+            int row = id / G::CPR, c = id % G::CPR;
+            *reinterpret_cast<u32x4 *>(tile + row * G::RB + G::swz(row, c) * 16) = pre[j];
+        }
+        if (tid < kKT) {
+            tscale[tid] = pscale;
+            tpos[tid] = ppos;
+        }
+    };
+
+    auto write_score = [&](int t, int col, float v) {
+        a.scores[(int64_t)(b * T + t) * a.n_out + col] = v;
+    };
+
+    const int ntiles = (c1 - c0 + kKT - 1) / kKT;
+    // Flat mode: a tile is skipped when its first column lies past every query's
+    // position; visibility only shrinks with the column, so skipped tiles form a suffix.
+    int nvis = ntiles;
+    if constexpr (!HI) nvis = maxp < c0 ? 0 : min(ntiles, (maxp - c0) / kKT + 1);
+    {
+        constexpr int NQ = PRE ? 4 : QPG;
+        for (int e = nvis * kKT + tid; e < ntiles * kKT * NQ; e += kThreads) {
+            // e runs over (query q, column offset) of the skipped tiles
+            int q = e / (ntiles * kKT);
+            int off = e % (ntiles * kKT);
+            if (off < nvis * kKT) continue;
+            int col = c0 + off;
+            int t = PRE ? ((int)blockIdx.y * 4 + q) : grp * QPG + q;
+            if (col < c1 && t < T) write_score(t, col, kNegInf);
+        }
+    }
+    if (nvis > 0) load_tile(c0);
+
+    for (int it = 0; it < nvis; ++it) {
+        const int tc0 = c0 + it * kKT;
+        __syncthreads();
+        store_tile();
+        __syncthreads();
+        if (it + 1 < nvis) load_tile(tc0 + kKT);  // next tile in flight during this compute
+
+        if (active) {
+            constexpr int NSUB = PRE ? 4 : 1;
+#pragma unroll
+            for (int sb = 0; sb < NSUB; ++sb) {
+                const int sub = PRE ? sb : wave;
+                const int row = sub * 32 + l32;
+                const unsigned char *trow = tile + row * G::RB;
+                f32x16 acc[HB];
+#pragma unroll
+                for (int hb = 0; hb < HB; ++hb)
+#pragma unroll
+                    for (int r = 0; r < 16; ++r) acc[hb][r] = 0.0f;
+                if constexpr (FP8) {
+#pragma unroll
+                    for (int kk = 0; kk < KSTEPS / 2; ++kk) {
+                        int c = (D / 32) * half + kk;
+                        u32x4 v = *reinterpret_cast<const u32x4 *>(trow + G::swz(row, c) * 16);
+                        bf16x8 f0, f1;
+                        fp8x16_to_frags(v, f0, f1);
+#pragma unroll
+                        for (int hb = 0; hb < HB; ++hb) {
+                            acc[hb] = mfma32(aq[hb][2 * kk], f0, acc[hb]);
+                            acc[hb] = mfma32(aq[hb][2 * kk + 1], f1, acc[hb]);
+                        }
+                    }
+                } else {
+#pragma unroll
+                    for (int ks = 0; ks < KSTEPS; ++ks) {
+                        int c = (D / 16) * half + ks;  // bytes D*half + 16*ks
+                        u32x4 v = *reinterpret_cast<const u32x4 *>(trow + G::swz(row, c) * 16);
+                        bf16x8 f = __builtin_bit_cast(bf16x8, v);
+#pragma unroll
+                        for (int hb = 0; hb < HB; ++hb) acc[hb] = mfma32(aq[hb][ks], f, acc[hb]);
+                    }
+                }
+                // ---- epilogue: ReLU, head weights, head sum, scale, causal mask
+                const int col = tc0 + sub * 32 + l32;
+                const int pos = tpos[row];
+                const float sc = FP8 ? tscale[row] : 1.0f;
+                if constexpr (MODE == ONEQ) {
+                    float s = 0.0f;
+#pragma unroll
+                    for (int hb = 0; hb < HB; ++hb)
+#pragma unroll
+                        for (int r = 0; r < 16; ++r) s += wreg[hb][r] * fmaxf(acc[hb][r], 0.0f);
+                    s += __shfl_xor(s, 32, 64);
+                    const int t = grp;
+                    const int p = ctx - T + t;
+                    if (half == 0 && col < c1) write_score(t, col, (pos >= 0 && pos <= p) ? s * sc : kNegInf);
+                } else if constexpr (MODE == Q4) {
+                    float part[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+                    for (int r = 0; r < 16; ++r) part[r / 4] += wreg[0][r] * fmaxf(acc[0][r], 0.0f);
+#pragma unroll
+                    for (int j = 0; j < 4; ++j) {
+                        const int t = grp * QPG + 2 * j + half;
+                        const int p = ctx - T + t;
+                        if (t < T && col < c1) write_score(t, col, (pos >= 0 && pos <= p) ? part[j] * sc : kNegInf);
+                    }
+                } else {
+                    float part[QPG];
+#pragma unroll
+                    for (int j = 0; j < QPG; ++j) part[j] = 0.0f;
+#pragma unroll
+                    for (int r = 0; r < 16; ++r) part[(8 * (r / 4)) / MODE] += wreg[0][r] * fmaxf(acc[0][r], 0.0f);
+#pragma unroll
+                    for (int j = 0; j < QPG; ++j) {
+                        part[j] += __shfl_xor(part[j], 32, 64);
+                        const int t = grp * QPG + j;
+                        const int p = ctx - T + t;
+                        if (half == 0 && t < T && col < c1)
+                            write_score(t, col, (pos >= 0 && pos <= p) ? part[j] * sc : kNegInf);
+                    }
+                }
+            }
+        }
+    }
+}
+
+// ---------------------------------------------------------------------------- blocks
+
+// One thread per block j; the query token's (H x D) rows staged in LDS as fp32.
+__global__ __launch_bounds__(256) void index_blocks_kernel(IndexBlocksArgs a) {
+    extern __shared__ float qs[];  // [H][D]
+    const int b = blockIdx.z, t = blockIdx.y;
+    const int H = a.H, D = a.D, T = a.T;
+    const int64_t qoff = ((int64_t)b * T + t) * H * D;
+    for (int e = threadIdx.x; e < H * D; e += blockDim.x) {
+        uint16_t bits = a.q[qoff + e];
+        qs[e] = u2f((uint32_t)bits << 16);
+    }
+    __syncthreads();
+    const int j = blockIdx.x * blockDim.x + threadIdx.x;
+    if (j >= a.n_blocks) return;
+    int ctx = a.ctx_len ? a.ctx_len[b] : a.N;
+    ctx = min(max(ctx, 0), a.N);
+    const int p = ctx - T + t;
+    const int Bs = a.block_size;
+    // eligibility: complete, visible, and at least one non-forced position (reading R9)
+    const int64_t lo = (int64_t)j * Bs, hi = lo + Bs - 1;  // inclusive
+    bool ok = hi <= p;
+    if (ok) {
+        int64_t nf = 0;
+        const int64_t s_hi = min((int64_t)a.sink, (int64_t)p + 1) - 1;  // sink [0, s_hi]
+        const int64_t w_lo = a.window > 0 ? max((int64_t)0, (int64_t)p - a.window + 1) : (int64_t)p + 1;
+        auto overlap = [](int64_t a0, int64_t a1, int64_t b0, int64_t b1) -> int64_t {
+            int64_t l = max(a0, b0), r = min(a1, b1);
+            return r >= l ? r - l + 1 : 0;
+        };
+        nf += overlap(lo, hi, 0, s_hi);
+        nf += overlap(lo, hi, w_lo, p);
+        nf -= overlap(lo, hi, max((int64_t)0, w_lo), min(s_hi, (int64_t)p));  // sink and window overlap
+        ok = nf < Bs;
+    }
+    float best = kNegInf;
+    if (ok) {
+        const float *kb = a.kbar + ((int64_t)b * a.n_blocks + j) * D;
+        const float *wt = a.w + ((int64_t)b * T + t) * H;
+        best = 0.0f;
+        bool first = true;
+        for (int h = 0; h < H; ++h) {
+            float dot = 0.0f;
+            const float *qh = qs + h * D;
+            for (int d = 0; d < D; d += 4) {
+                float4 kv = *reinterpret_cast<const float4 *>(kb + d);
+                dot = fmaf(qh[d], kv.x, dot);
+                dot = fmaf(qh[d + 1], kv.y, dot);
+                dot = fmaf(qh[d + 2], kv.z, dot);
+                dot = fmaf(qh[d + 3], kv.w, dot);
+            }
+            float v = wt[h] * fmaxf(dot, 0.0f);
+            best = first ? v : fmaxf(best, v);
+            first = false;
+        }
+    }
+    a.scores[((int64_t)b * T + t) * a.n_blocks + j] = best;
+}
+
+// ---------------------------------------------------------------------------- block means
+
+// One workgroup of D threads per (block j, sequence b); thread d sums dimension d.
+__global__ __launch_bounds__(128) void block_means_kernel(BlockMeansArgs a) {
+    const int j = blockIdx.x, b = blockIdx.y, d = threadIdx.x;
+    if (d >= a.D) return;
+    const int Bs = a.block_size, D = a.D;
+    const int64_t row0 = (int64_t)b * a.N + (int64_t)j * Bs;
+    float acc = 0.0f;
+    if (a.fp8) {
+        const uint8_t *k = reinterpret_cast<const uint8_t *>(a.k);
+        for (int s = 0; s < Bs; ++s) {
+            uint32_t byte = k[(row0 + s) * D + d];
+            float v = __builtin_amdgcn_cvt_pk_f32_fp8(byte, false)[0];
+            acc += a.k_scale[row0 + s] * v;
+        }
+    } else {
+        const uint16_t *k = reinterpret_cast<const uint16_t *>(a.k);
+        for (int s = 0; s < Bs; ++s) acc += u2f((uint32_t)k[(row0 + s) * D + d] << 16);
+    }
+    a.kbar[((int64_t)b * a.n_blocks + j) * D + d] = acc / (float)Bs;
+}
+
+template <int D, bool FP8, int MODE, int HB, bool HI, bool PRE>
+hipError_t launch_tokens_t(const IndexTokensArgs &a, hipStream_t s) {
+    const int QPG = MODE == ONEQ ? 1 : 32 / MODE;
+    const int groups = (a.T + QPG - 1) / QPG;
+    const int gy = PRE ? (groups + 3) / 4 : groups;
+    const int max_chunks = (a.n_out + kKT - 1) / kKT;
+    int want = (2048 + a.B * gy - 1) / (a.B * gy);
+    int chunks = want < 1 ? 1 : (want > max_chunks ? max_chunks : want);
+    int chunk = (a.n_out + chunks - 1) / chunks;
+    chunk = (chunk + kKT - 1) / kKT * kKT;
+    chunks = (a.n_out + chunk - 1) / chunk;
+    dim3 grid(chunks, gy, a.B);
+    hipLaunchKernelGGL((index_tokens_kernel<D, FP8, MODE, HB, HI, PRE>), grid, dim3(kThreads), 0, s, a, groups, chunk);
+    return hipGetLastError();
+}
+
+template <int D, bool FP8>
+hipError_t launch_tokens_d(const IndexTokensArgs &a, hipStream_t s) {
+    const bool hi = a.kept != nullptr;
+    if (hi) {
+        if (a.H <= 32) return launch_tokens_t<D, FP8, ONEQ, 1, true, false>(a, s);
+        return launch_tokens_t<D, FP8, ONEQ, 2, true, false>(a, s);
+    }
+    switch (a.H) {
+        case 4: return launch_tokens_t<D, FP8, Q4, 1, false, false>(a, s);
+        case 8: return launch_tokens_t<D, FP8, Q8, 1, false, false>(a, s);
+        case 16: return launch_tokens_t<D, FP8, Q16, 1, false, false>(a, s);
+        case 32:
+            if (a.T >= 64) return launch_tokens_t<D, FP8, ONEQ, 1, false, true>(a, s);
+            return launch_tokens_t<D, FP8, ONEQ, 1, false, false>(a, s);
+        default:
+            if (a.T >= 64) return launch_tokens_t<D, FP8, ONEQ, 2, false, true>(a, s);
+            return launch_tokens_t<D, FP8, ONEQ, 2, false, false>(a, s);
+    }
+}
+
+}  // namespace
+
+bool index_tokens_supported(int H, int D, bool hi) {
+    if (D != 64 && D != 128) return false;
+    if (hi) return H >= 1 && H <= 64;
+    return H == 4 || H == 8 || H == 16 || H == 32 || H == 64;
+}
+
+hipError_t launch_index_tokens(const IndexTokensArgs &a, hipStream_t s) {
+    if (a.D == 64) return a.fp8 ? launch_tokens_d<64, true>(a, s) : launch_tokens_d<64, false>(a, s);
+    return a.fp8 ? launch_tokens_d<128, true>(a, s) : launch_tokens_d<128, false>(a, s);
+}
+
+hipError_t launch_index_blocks(const IndexBlocksArgs &a, hipStream_t s) {
+    dim3 grid((a.n_blocks + 255) / 256, a.T, a.B);
+    size_t lds = (size_t)a.H * a.D * sizeof(float);
+    hipLaunchKernelGGL(index_blocks_kernel, grid, dim3(256), lds, s, a);
+    return hipGetLastError();
+}
+
+hipError_t launch_block_means(const BlockMeansArgs &a, hipStream_t s) {
+    dim3 grid(a.n_blocks, a.B);
+    hipLaunchKernelGGL(block_means_kernel, grid, dim3(128), 0, s, a);
+    return hipGetLastError();
+}
+
+}  // namespace lsa

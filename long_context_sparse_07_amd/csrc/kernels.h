@@ -1,0 +1,87 @@
+// Internal launcher interface between the C ABI (api.cpp) and the HIP kernels.
+// Arguments arrive already validated; launchers only pick a specialisation,
+// size the grid and enqueue. Each returns hipSuccess or the launch error.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace lsa {
+
+struct IndexTokensArgs {
+    int B, T, N, H, D;
+    const int32_t *ctx_len;
+    const uint16_t *q;      // bf16 [B][T][H][D]
+    const float *w;         // [B][T][H]
+    const void *k;          // bf16 or fp8 [B][N][D]
+    bool fp8;
+    const float *k_scale;   // [B][N] or null
+    const int32_t *kept;    // HI fine: [B][T][n_keep] or null
+    int n_keep, block_size;
+    float *scores;          // [B][T][n_out]
+    int n_out;
+};
+hipError_t launch_index_tokens(const IndexTokensArgs &a, hipStream_t s);
+bool index_tokens_supported(int H, int D, bool hi);
+
+struct IndexBlocksArgs {
+    int B, T, N, H, D;
+    const int32_t *ctx_len;
+    const uint16_t *q;
+    const float *w;
+    const float *kbar;      // [B][n_blocks][D]
+    int n_blocks, block_size, sink, window;
+    float *scores;          // [B][T][n_blocks]
+};
+hipError_t launch_index_blocks(const IndexBlocksArgs &a, hipStream_t s);
+
+struct BlockMeansArgs {
+    int B, N, D;
+    const void *k;
+    bool fp8;
+    const float *k_scale;
+    int block_size, n_blocks;
+    float *kbar;
+};
+hipError_t launch_block_means(const BlockMeansArgs &a, hipStream_t s);
+
+struct SelectArgs {
+    int B, T, N;
+    const int32_t *ctx_len;
+    const float *scores;
+    int n_cols;
+    const int32_t *kept;
+    int n_keep, block_size;
+    int K, sink, window;
+    bool causal;
+    int32_t *idx;
+};
+size_t select_workspace_bytes(const SelectArgs &a);
+hipError_t launch_select(const SelectArgs &a, void *ws, hipStream_t s);
+
+struct AttendArgs {
+    int B, T, N, Hq, Hkv, d_qk, d_v;
+    const uint16_t *q;
+    const uint16_t *k;
+    int64_t ksb, ksn, ksh;
+    const uint16_t *v;
+    int64_t vsb, vsn, vsh;
+    const int32_t *idx;
+    int K;
+    float scale;
+    void *out;
+    bool out_f32;
+    float *lse;
+    int L;
+    int64_t lsq, lsk, lsv, lso, lsl;
+    int n_splits;           // resolved (>= 1)
+};
+int attend_default_splits(const AttendArgs &a);
+size_t attend_workspace_bytes(const AttendArgs &a);
+bool attend_supported(int d_qk, int d_v, int g);
+hipError_t launch_attend(const AttendArgs &a, void *ws, hipStream_t s);
+
+hipError_t launch_clear(void *p, size_t bytes, hipStream_t s);
+
+}  // namespace lsa

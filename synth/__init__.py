@@ -31,8 +31,10 @@ Distributions (readings where the statement is silent are marked R):
 """
 from __future__ import annotations
 
+import concurrent.futures as cf
 import dataclasses
 import hashlib
+import os
 from dataclasses import dataclass
 from typing import Optional
 
@@ -103,10 +105,11 @@ def config(cid: int, **overrides) -> LSAConfig:
 # ----------------------------------------------------------------------------- casts
 
 def to_bf16_bits(x: np.ndarray) -> np.ndarray:
-    """float32 -> bf16 bit patterns (uint16), round to nearest even (finite inputs)."""
-    u = np.ascontiguousarray(x, dtype=np.float32).view(np.uint32)
-    rounded = u + np.uint32(0x7FFF) + ((u >> np.uint32(16)) & np.uint32(1))
-    return (rounded >> np.uint32(16)).astype(np.uint16)
+    """float32 -> bf16 bit patterns (uint16), round to nearest even (torch's cast,
+    used here only as a format converter on the CPU)."""
+    import torch
+    x = np.ascontiguousarray(x, dtype=np.float32)
+    return torch.from_numpy(x).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
 
 
 def to_e4m3fn(x: np.ndarray):
@@ -117,23 +120,37 @@ def to_e4m3fn(x: np.ndarray):
     torch's cast (torch is used here only as a format converter on the CPU).
     """
     import torch
-    x = np.ascontiguousarray(x, dtype=np.float32)
-    amax = np.max(np.abs(x), axis=-1)
-    scale = (np.maximum(amax, np.float32(1e-12)) / np.float32(448.0)).astype(np.float32)
-    y = np.clip(x / scale[..., None], np.float32(-448.0), np.float32(448.0)).astype(np.float32)
-    b = torch.from_numpy(y).to(torch.float8_e4m3fn).view(torch.uint8).numpy().copy()
-    return b, scale
+    xt = torch.from_numpy(np.ascontiguousarray(x, dtype=np.float32))
+    amax = xt.abs().amax(dim=-1)
+    scale = torch.clamp(amax, min=1e-12) / 448.0
+    y = torch.clamp(xt / scale.unsqueeze(-1), -448.0, 448.0)
+    b = y.to(torch.float8_e4m3fn).view(torch.uint8).numpy().copy()
+    return b, scale.numpy().astype(np.float32)
 
 
 # ----------------------------------------------------------------------------- draws
 
-def _normal(rng: np.random.Generator, shape, std: float, chunk: int = 1 << 24) -> np.ndarray:
-    """N(0, std^2) float32 drawn in fixed-size chunks (same values for any machine)."""
+_CHUNK = 1 << 22
+
+
+def _normal(ss: np.random.SeedSequence, shape, std: float) -> np.ndarray:
+    """N(0, std^2) float32.  Chunk i of 2^22 values is drawn from its own PCG64 stream
+    (the i-th child of `ss`), so the values do not depend on how many threads fill them."""
     n = int(np.prod(shape))
     out = np.empty(n, dtype=np.float32)
-    for s in range(0, n, chunk):
-        e = min(n, s + chunk)
-        rng.standard_normal(e - s, dtype=np.float32, out=out[s:e])
+    kids = ss.spawn((n + _CHUNK - 1) // _CHUNK)
+
+    def fill(i):
+        s, e = i * _CHUNK, min(n, (i + 1) * _CHUNK)
+        np.random.Generator(np.random.PCG64(kids[i])).standard_normal(e - s, dtype=np.float32, out=out[s:e])
+
+    workers = min(len(kids), 16, os.cpu_count() or 1)
+    if workers > 1:
+        with cf.ThreadPoolExecutor(workers) as ex:
+            list(ex.map(fill, range(len(kids))))
+    else:
+        for i in range(len(kids)):
+            fill(i)
     if std != 1.0:
         out *= np.float32(std)
     return out.reshape(shape)
@@ -176,13 +193,15 @@ def make_inputs(cfg: LSAConfig, seed: Optional[int] = None, with_kv: bool = True
     seed = 1000 + cfg.cid if seed is None else seed
     ss = np.random.SeedSequence(seed)
     kids = ss.spawn(4 + 3 * cfg.layers)
-    rq, rw, rk, rs = (np.random.Generator(np.random.PCG64(k)) for k in kids[:4])
+    sq, sw, sk, ssal = kids[:4]
+    rw = np.random.Generator(np.random.PCG64(sw))
+    rs = np.random.Generator(np.random.PCG64(ssal))
     B, T, N = cfg.B, cfg.T, cfg.N
     out = {"cfg": cfg, "seed": seed}
-    qI = _normal(rq, (B, T, cfg.H_I, cfg.D_I), 1.0 / np.sqrt(cfg.D_I))
+    qI = _normal(sq, (B, T, cfg.H_I, cfg.D_I), 1.0 / np.sqrt(cfg.D_I))
     out["qI"] = to_bf16_bits(qI)
     out["w"] = rw.random((B, T, cfg.H_I), dtype=np.float32)
-    kI = _normal(rk, (B, N, cfg.D_I), 1.0 / np.sqrt(cfg.D_I))
+    kI = _normal(sk, (B, N, cfg.D_I), 1.0 / np.sqrt(cfg.D_I))
     sal = []
     for b in range(B):
         pos = _salient_positions(rs, cfg, b)
@@ -198,8 +217,7 @@ def make_inputs(cfg: LSAConfig, seed: Optional[int] = None, with_kv: bool = True
     if with_kv:
         qs, ks, vs = [], [], []
         for layer in range(cfg.layers):
-            r_q, r_k, r_v = (np.random.Generator(np.random.PCG64(k))
-                             for k in kids[4 + 3 * layer: 7 + 3 * layer])
+            r_q, r_k, r_v = kids[4 + 3 * layer: 7 + 3 * layer]
             if cfg.mla:
                 qs.append(to_bf16_bits(_normal(r_q, (B, T, cfg.Hq, cfg.d_qk), 1.0 / np.sqrt(cfg.d_qk))))
                 ks.append(to_bf16_bits(_normal(r_k, (B, N, 1, cfg.d_qk), 1.0)))

@@ -1,0 +1,171 @@
+"""GPU edge cases and invariants of the HIP path (through the C ABI), against the oracle.
+
+Short and ragged contexts, per-sequence context lengths, ties everywhere (zero
+weights: every score equal), an empty fill (K = sink + window), K = 1, padded and
+out-of-range idx entries, explicit split counts, HI with every block kept equal to
+flat selection, CLI reuse equal to per-layer calls, fp32 output, workspace reuse.
+"""
+import numpy as np
+import pytest
+import torch
+
+import long_context_sparse_07_amd as L
+from oracle import lsa_oracle as O
+from synth import config, make_inputs
+from gpu_harness import upload, gpu_index_select, gpu_attend, check_band, check_attn
+
+pytestmark = pytest.mark.gpu
+
+
+def _np(t):
+    return t.detach().float().cpu().numpy() if t.dtype == torch.bfloat16 else t.detach().cpu().numpy()
+
+
+def _flat_check(inp, d, r):
+    cfg = inp["cfg"]
+    ora = O.reference_step(inp)
+    P = O.query_positions(inp["ctx_len"], cfg.T)
+    idx = _np(r["idx"])
+    for b in range(cfg.B):
+        for t in range(cfg.T):
+            p = int(P[b, t])
+            F = O.forced_positions(p, cfg.S, cfg.W)
+            C = np.setdiff1d(np.arange(max(p + 1, 0)), F)
+            check_band(idx[b, t], C, ora["scores"][(b, t)][C] if C.size else np.zeros(0), F, cfg.K,
+                       what=f"{cfg.name} {b},{t}")
+    out, _ = gpu_attend(d, r["idx"])
+    o = _np(out)
+    for layer in range(cfg.layers):
+        for b in range(cfg.B):
+            for t in range(cfg.T):
+                check_attn(o[layer, b, t], ora["out"][(layer, b, t)], f"{cfg.name} L{layer} {b},{t}")
+    return ora
+
+
+@pytest.mark.parametrize("N", [50, 200, 511, 700])
+def test_short_context(N):
+    # p < K (everything visible selected), p < S + W (sink and window overlap)
+    cfg = config(1, N=N, K=512, S=16, W=128, salient="none")
+    inp = make_inputs(cfg)
+    d = upload(inp)
+    r = gpu_index_select(d)
+    _flat_check(inp, d, r)
+
+
+def test_per_sequence_context_lengths():
+    cfg = config(5, B=3, T=2, N=3000, K=256, S=16, W=64, layers=1)
+    inp = make_inputs(cfg)
+    inp["ctx_len"] = np.array([3000, 1234, 130], dtype=np.int32)
+    d = upload(inp)
+    r = gpu_index_select(d)
+    _flat_check(inp, d, r)
+
+
+def test_all_scores_equal_tie_break_and_list_overflow():
+    # w = 0: every score is 0; the fill is the lowest candidate positions. 40000 equal
+    # keys overflow the composite list, so the resolve stage rescans the row.
+    cfg = config(1, N=40000, K=512, S=16, W=128, salient="none", T=2)
+    inp = make_inputs(cfg)
+    inp["w"][:] = 0.0
+    d = upload(inp)
+    r = gpu_index_select(d)
+    idx = _np(r["idx"])
+    P = O.query_positions(inp["ctx_len"], cfg.T)
+    for t in range(cfg.T):
+        p = int(P[0, t])
+        want = O.select_tokens(np.zeros(p + 1), p, cfg.K, cfg.S, cfg.W)
+        assert np.array_equal(idx[0, t], want)
+
+
+def test_fill_empty_and_k_one():
+    cfg = config(1, N=1000, K=144, S=16, W=128, salient="none")     # K == S + W: no fill
+    inp = make_inputs(cfg)
+    d = upload(inp)
+    r = gpu_index_select(d)
+    _flat_check(inp, d, r)
+    sc = L.lsa_index(d["qI"], d["w"], d["kI"], ctx_len=d["ctx_len"])
+    one = _np(L.lsa_select(sc, 1, 0, 0, ctx_len=d["ctx_len"]))
+    ora = O.reference_step(inp, with_attend=False)
+    for t in range(cfg.T):
+        s = ora["scores"][(0, t)]
+        best = int(np.lexsort((np.arange(len(s)), -s))[0])
+        assert one[0, t, 0] == best
+
+
+def test_attend_padding_and_out_of_range_rows():
+    cfg = config(5, B=2, N=2000, K=300, S=16, W=64, layers=1)
+    inp = make_inputs(cfg)
+    d = upload(inp)
+    rng = np.random.default_rng(5)
+    idx = np.full((cfg.B, 1, cfg.K), -1, dtype=np.int32)
+    idx[0, 0, :100] = np.sort(rng.choice(cfg.N, 100, replace=False))
+    idx[0, 0, 100:110] = cfg.N + 5            # out of range: skipped like -1
+    # sequence 1: every entry padding -> out 0, lse -inf
+    out, lse = gpu_attend(d, torch.from_numpy(idx).cuda(), n_splits=3)
+    o, l = _np(out), _np(lse)
+    want, wl = O.attend(O.decode_bf16(inp["q"][0, 0, 0]), O._LazyRows(inp["k"][0, 0]),
+                        O._LazyRows(inp["v"][0, 0]), idx[0, 0, :100], cfg.tau)
+    check_attn(o[0, 0, 0], want, "padded")
+    assert np.allclose(l[0, 0, 0], wl, atol=2e-3)
+    assert np.all(o[0, 1, 0] == 0) and np.all(np.isneginf(l[0, 1, 0]))
+
+
+@pytest.mark.parametrize("splits", [1, 2, 7, 0])
+def test_attend_split_counts(splits):
+    cfg = config(2, B=2, N=6000, K=512, S=32, W=128)
+    inp = make_inputs(cfg)
+    d = upload(inp)
+    r = gpu_index_select(d)
+    ora = O.reference_step(inp)
+    idx_o = torch.from_numpy(np.stack([[ora["idx"][(b, 0)] for b in range(cfg.B)]]).transpose(1, 0, 2).astype(np.int32)).cuda()
+    out, lse = gpu_attend(d, idx_o, n_splits=splits)
+    o = _np(out)
+    for b in range(cfg.B):
+        check_attn(o[0, b, 0], ora["out"][(0, b, 0)], f"splits={splits} b={b}")
+
+
+def test_fp32_output_matches_bf16_output():
+    cfg = config(5, B=2, N=3000, K=256, S=16, W=64, layers=2)
+    inp = make_inputs(cfg)
+    d = upload(inp)
+    r = gpu_index_select(d)
+    ob, lb = gpu_attend(d, r["idx"])
+    of, lf = gpu_attend(d, r["idx"], out_dtype=torch.float32)
+    assert torch.equal(lb, lf)
+    assert torch.equal(of.to(torch.bfloat16), ob)
+
+
+def test_hi_with_all_blocks_kept_equals_flat():
+    base = config(3, N=64 * 200, K=512, S=64, W=128, n_keep=200)
+    inp = make_inputs(base)
+    d = upload(inp)
+    r_hi = gpu_index_select(d)
+    flat = dict(d)
+    flat["cfg"] = base.scaled(hi=False)
+    r_flat = gpu_index_select(flat)
+    assert torch.equal(r_hi["idx"], r_flat["idx"])
+
+
+def test_cli_reuse_equals_per_layer_calls():
+    cfg = config(5, B=4, N=4000, K=512, S=32, W=128)
+    inp = make_inputs(cfg)
+    d = upload(inp)
+    r = gpu_index_select(d)
+    out, lse = gpu_attend(d, r["idx"])
+    for layer in range(cfg.layers):
+        o1, l1 = L.lsa_attend(d["q"][layer:layer + 1], d["k"][layer:layer + 1], d["v"][layer:layer + 1],
+                              r["idx"], cfg.tau)
+        assert torch.equal(o1[0], out[layer]) and torch.equal(l1[0], lse[layer])
+
+
+def test_select_workspace_reuse_is_clean():
+    cfg = config(2, B=2, N=7000, K=512, S=32, W=128)
+    inp = make_inputs(cfg)
+    d = upload(inp)
+    sc = L.lsa_index(d["qI"], d["w"], d["kI"], k_scale=d["kI_scale"])
+    a = L.lsa_select(sc, cfg.K, cfg.S, cfg.W)
+    b = L.lsa_select(sc, cfg.K, cfg.S, cfg.W)
+    c = L.lsa_select(sc[:, :, :5000].contiguous(), 300, 10, 20)   # a different shape on the same workspace
+    e = L.lsa_select(sc, cfg.K, cfg.S, cfg.W)
+    assert torch.equal(a, b) and torch.equal(a, e)
+    assert c.shape == (2, 1, 300)
