@@ -1,0 +1,238 @@
+"""Benchmark of the LSA decode step on one MI355X.
+
+One step = the whole hot path on one batch: lsa_index (indexer sweep over the fp8
+key cache) -> lsa_select (sink + window + top-k fill) -> lsa_attend (MLA sparse
+attention over the 2048 selected rows), for the 128K-context decode workload:
+B=8 sequences, N=131072 cached tokens each, one query token, indexer 64 heads x 128
+(fp8-e4m3 keys + per-token fp32 scale), MLA 64 heads over 576-wide latent rows
+(V = first 512 columns), K=2048 with sink 64 and window 512.
+
+Inputs are synthetic (seeded, see synth/) and resident in HBM before timing starts.
+R input replicas (default 4, 5.4 GB) are rotated step by step so that every step
+reads cold data (the 256 MB MALL cannot hold them). The headline runs the step as a
+captured HIP graph (one graph per replica); the plain stream-launch rate is reported
+beside it. Prints one JSON line.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "LSA decode steps/sec at 128K ctx (1 GPU); achieved HBM GB/s vs peak"
+PEAK_HBM_GBS = 8000.0
+PROFILE_PMC = os.path.join(ROOT, "profiles", "index_fp8_c2_pmc.json")
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=500)
+    ap.add_argument("--warmup", type=int, default=50)
+    ap.add_argument("--replicas", type=int, default=4)
+    ap.add_argument("--no-graph", action="store_true", help="headline from plain stream launches")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--profile-only", action="store_true", help="few plain steps, no graphs (for rocprofv3)")
+    return ap.parse_args()
+
+
+def algorithmic_bytes(cfg):
+    """Bytes the method must move per step (index keys + scales, the K selected MLA rows,
+    indexer q/w, attention q and output)."""
+    B, N = cfg.B, cfg.N
+    index = B * N * (cfg.D_I * (1 if cfg.k_fp8 else 2) + (4 if cfg.k_fp8 else 0))
+    gather = B * cfg.T * cfg.K * cfg.d_qk * 2
+    small = B * cfg.T * (cfg.H_I * cfg.D_I * 2 + cfg.H_I * 4 + cfg.Hq * cfg.d_qk * 2 + cfg.Hq * cfg.d_v * 2)
+    return index, gather, small
+
+
+def cpu_baseline(inp, cfg):
+    """The oracle as it stands, timed on this host: one whole step (all 8 sequences)."""
+    from oracle import lsa_oracle as O
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    except Exception:
+        threads = 1
+    cores = len(os.sched_getaffinity(0))
+    t0 = time.perf_counter()
+    O.reference_step(inp)
+    dt = time.perf_counter() - t0
+    return {"value": 1.0 / dt, "unit": "steps/s", "cores": threads, "kind": "oracle",
+            "sample": f"one full step (8 sequences x 131072 keys, index+select+attend) in float64 numpy, "
+                      f"{dt:.2f} s wall; {cores} host cores visible, BLAS threads {threads}"}
+
+
+def pmc_traffic(index_bytes_per_launch):
+    """HBM traffic of the indexer from committed rocprofv3 counter runs, if they were
+    taken on the current kernel source; else None."""
+    try:
+        with open(PROFILE_PMC) as f:
+            rec = json.load(f)
+        src = open(os.path.join(ROOT, "long_context_sparse_07_amd", "csrc", "index.hip"), "rb").read()
+        if rec.get("index_hip_sha256") != hashlib.sha256(src).hexdigest():
+            return None
+        return rec["traffic_bytes_per_launch"]
+    except Exception:
+        return None
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only (got --gpus {args.gpus}); this build has no multi-GPU path.",
+              file=sys.stderr)
+        sys.exit(2)
+    import ctypes
+    import numpy as np
+    import torch
+    import long_context_sparse_07_amd as L
+    from synth import config, make_inputs
+
+    cfg = config(2)
+    dev = torch.device("cuda:0")
+    t_gen = time.perf_counter()
+    inp = make_inputs(cfg)
+    print(f"[bench] inputs generated in {time.perf_counter() - t_gen:.1f}s", file=sys.stderr, flush=True)
+
+    def bf16(a):
+        return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).view(torch.bfloat16)
+
+    host = {"qI": bf16(inp["qI"]), "w": torch.from_numpy(inp["w"]), "kI": torch.from_numpy(inp["kI"]),
+            "ks": torch.from_numpy(inp["kI_scale"]), "q": bf16(inp["q"]), "k": bf16(inp["k"])}
+    R = max(1, args.replicas)
+    reps = []
+    for r in range(R):
+        reps.append({k: v.to(dev) for k, v in host.items()})
+        reps[-1]["kI"] = reps[-1]["kI"].view(torch.float8_e4m3fn)
+    del host
+    B, T, N = cfg.B, cfg.T, cfg.N
+    scores = torch.empty((B, T, N), dtype=torch.float32, device=dev)
+    idx = torch.empty((B, T, cfg.K), dtype=torch.int32, device=dev)
+    out = torch.empty((1, B, T, cfg.Hq, cfg.d_v), dtype=torch.bfloat16, device=dev)
+    lse = torch.empty((1, B, T, cfg.Hq), dtype=torch.float32, device=dev)
+    stream = torch.cuda.current_stream()
+    sptr = ctypes.c_void_p(stream.cuda_stream)
+    lib = L.lib()
+
+    # prebuilt descriptors per replica (the timed loop only makes the three C calls)
+    descs = []
+    for rp in reps:
+        di = L.IndexDesc(mode=L.LSA_INDEX_TOKENS, B=B, T=T, N=N, H=cfg.H_I, D=cfg.D_I, q=rp["qI"].data_ptr(),
+                         w=rp["w"].data_ptr(), k=rp["kI"].data_ptr(), k_dtype=L.LSA_FP8_E4M3FN,
+                         k_scale=rp["ks"].data_ptr(), scores=scores.data_ptr())
+        ds = L.SelectDesc(B=B, T=T, N=N, scores=scores.data_ptr(), n_cols=N, K=cfg.K, sink=cfg.S,
+                          window=cfg.W, causal=1, idx=idx.data_ptr())
+        da = L._attend_desc(rp["q"], rp["k"], None, idx, cfg.tau, out, lse, True, 0)
+        descs.append((di, ds, da))
+    ws_sel = torch.empty(max(256, lib.lsa_select_workspace_bytes(ctypes.byref(descs[0][1]))), dtype=torch.uint8, device=dev)
+    ws_att = torch.empty(max(256, lib.lsa_attend_workspace_bytes(ctypes.byref(descs[0][2]))), dtype=torch.uint8, device=dev)
+
+    def c_index(r):
+        L._check("lsa_index", lib.lsa_index(ctypes.byref(descs[r][0]), sptr))
+
+    def c_select(r):
+        L._check("lsa_select", lib.lsa_select(ctypes.byref(descs[r][1]), ws_sel.data_ptr(), ws_sel.numel(), sptr))
+
+    def c_attend(r):
+        L._check("lsa_attend", lib.lsa_attend(ctypes.byref(descs[r][2]), ws_att.data_ptr(), ws_att.numel(), sptr))
+
+    def step(r):
+        c_index(r)
+        c_select(r)
+        c_attend(r)
+
+    # the first call clears the select workspace; every later call (same shape) finds it clean
+    step(0)
+    torch.cuda.synchronize()
+    for d in descs:
+        d[1].workspace_state = L.LSA_WS_CLEAN
+
+    def timed(fn, n, warm):
+        for i in range(warm):
+            fn(i % R)
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for i in range(n):
+            fn(i % R)
+        e1.record(stream)
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / n
+
+    if args.profile_only:
+        ms = timed(step, args.steps, args.warmup)
+        print(json.dumps({"profile_only": True, "ms_per_step_plain": ms}))
+        return
+
+    # plain stream launches
+    ms_plain = timed(step, args.steps, args.warmup)
+    # per-kernel-call times (live, same stream, same replica rotation)
+    ms_index = timed(c_index, args.steps, args.warmup)
+    ms_select = timed(c_select, args.steps, args.warmup)
+    ms_attend = timed(c_attend, args.steps, args.warmup)
+
+    # HIP graphs: one captured step per replica
+    ms_graph = None
+    if not args.no_graph:
+        graphs = []
+        side = torch.cuda.Stream()
+        side.wait_stream(stream)
+        with torch.cuda.stream(side):
+            for r in range(R):
+                g = torch.cuda.CUDAGraph()
+                gptr = ctypes.c_void_p(side.cuda_stream)
+                with torch.cuda.graph(g, stream=side):
+                    lib.lsa_index(ctypes.byref(descs[r][0]), gptr)
+                    lib.lsa_select(ctypes.byref(descs[r][1]), ws_sel.data_ptr(), ws_sel.numel(), gptr)
+                    lib.lsa_attend(ctypes.byref(descs[r][2]), ws_att.data_ptr(), ws_att.numel(), gptr)
+                graphs.append(g)
+        stream.wait_stream(side)
+        torch.cuda.synchronize()
+        ms_graph = timed(lambda r: graphs[r].replay(), args.steps, args.warmup)
+
+    ms = ms_graph if ms_graph is not None else ms_plain
+    idx_b, gat_b, small_b = algorithmic_bytes(cfg)
+    step_bytes = idx_b + gat_b + small_b
+    achieved_index = idx_b / (ms_index * 1e-3) / 1e9
+    traffic = pmc_traffic(idx_b)
+    res = {
+        "metric": METRIC,
+        "value": 1e3 / ms,
+        "unit": "steps/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": "c2 LSA decode: B=8, 128K context, T=1, indexer 64x128 fp8-e4m3 + fp32 scale, "
+                               "MLA 64 heads 576/512 bf16, K=2048 (sink 64, window 512)",
+                   "batch": B, "context": N, "query_tokens": T, "topk": cfg.K,
+                   "launch": "hip graph replay" if ms_graph is not None else "stream launches",
+                   "input_replicas": R},
+        "roofline": {"bound": "hbm", "kernel": "index_tokens_kernel (lsa_index, fp8 keys)",
+                     "achieved": achieved_index, "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                     "frac": achieved_index / PEAK_HBM_GBS, "traffic": traffic},
+        "extra": {"step_algorithmic_bytes": step_bytes, "step_hbm_gbs": step_bytes / (ms * 1e-3) / 1e9,
+                  "step_frac_of_peak": step_bytes / (ms * 1e-3) / 1e9 / PEAK_HBM_GBS,
+                  "ms_per_step_plain": ms_plain, "ms_per_step_graph": ms_graph,
+                  "ms_index": ms_index, "ms_select": ms_select, "ms_attend": ms_attend,
+                  "index_bytes_per_launch": idx_b, "gather_bytes": gat_b},
+    }
+    if not args.no_cpu_baseline:
+        res["cpu_baseline"] = cpu_baseline(inp, cfg)
+    print(json.dumps(res))
+
+
+if __name__ == "__main__":
+    main()

@@ -65,6 +65,10 @@ extern "C" {
 #define LSA_FP8_E4M3FN 2 /* OCP E4M3 without infinities (gfx950 native), max 448 */
 #define LSA_F32 3
 
+/* lsa_select workspace states */
+#define LSA_WS_UNKNOWN 0
+#define LSA_WS_CLEAN 1
+
 /* lsa_index modes */
 #define LSA_INDEX_TOKENS 0
 #define LSA_INDEX_BLOCKS 1
@@ -153,10 +157,11 @@ int32_t lsa_block_means(const lsa_block_means_desc *desc, void *stream);
  * Output idx int32 [B][T][K]: the selected positions in ascending order, then -1.
  *
  * Workspace: lsa_select_workspace_bytes(desc) bytes of device memory, 256-byte
- * aligned, ZERO-FILLED before its first use (e.g. by lsa_workspace_clear). Every
- * lsa_select call returns it to all-zero at its end (stream-ordered), so it can be
- * reused across calls without clearing; after a failed call clear it again.
- * Calls that share one workspace must be ordered on one stream.
+ * aligned. With workspace_state = LSA_WS_UNKNOWN the call first clears the state it
+ * needs (one small fill kernel), so no initial contents are needed. Every successful
+ * call leaves that state zeroed; a caller that reuses a workspace for a call with the
+ * same B, T and n_cols (or right after lsa_workspace_clear) may pass LSA_WS_CLEAN to
+ * skip the clear. Calls that share one workspace must be ordered on one stream.
  * Supported: 1 <= K <= 4096, n_cols >= 1.
  */
 typedef struct lsa_select_desc {
@@ -169,6 +174,7 @@ typedef struct lsa_select_desc {
     int32_t K, sink, window;
     int32_t causal;          /* 1 token selection at p with forced set, 0 plain top-K */
     int32_t *idx;            /* int32 [B][T][K] */
+    int32_t workspace_state; /* LSA_WS_UNKNOWN (0) or LSA_WS_CLEAN (1), see above */
 } lsa_select_desc;
 
 size_t lsa_select_workspace_bytes(const lsa_select_desc *desc);

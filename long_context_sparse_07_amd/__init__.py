@@ -16,6 +16,7 @@ from ctypes import POINTER, c_float, c_int32, c_int64, c_size_t, c_void_p
 __all__ = ["lib", "LSAError", "lsa_index", "lsa_block_means", "lsa_select", "lsa_attend",
            "lsa_workspace_clear", "lsa_select_workspace_bytes", "lsa_attend_workspace_bytes",
            "LSA_BF16", "LSA_FP8_E4M3FN", "LSA_F32", "LSA_INDEX_TOKENS", "LSA_INDEX_BLOCKS",
+           "LSA_WS_UNKNOWN", "LSA_WS_CLEAN",
            "IndexDesc", "BlockMeansDesc", "SelectDesc", "AttendDesc", "STATUS"]
 
 HERE = os.path.dirname(os.path.abspath(__file__))
@@ -23,6 +24,7 @@ LIB_PATH = os.path.join(HERE, "liblsa.so")
 
 LSA_BF16, LSA_FP8_E4M3FN, LSA_F32 = 1, 2, 3
 LSA_INDEX_TOKENS, LSA_INDEX_BLOCKS = 0, 1
+LSA_WS_UNKNOWN, LSA_WS_CLEAN = 0, 1
 STATUS = {0: "LSA_OK", -1: "LSA_E_NULL", -2: "LSA_E_SHAPE", -3: "LSA_E_DTYPE", -4: "LSA_E_BUDGET",
           -5: "LSA_E_ALIGN", -6: "LSA_E_UNSUPPORTED", -7: "LSA_E_WORKSPACE", -8: "LSA_E_HIP"}
 
@@ -44,7 +46,7 @@ class SelectDesc(ctypes.Structure):
     _fields_ = [("B", c_int32), ("T", c_int32), ("N", c_int32), ("ctx_len", c_void_p),
                 ("scores", c_void_p), ("n_cols", c_int32), ("kept", c_void_p), ("n_keep", c_int32),
                 ("block_size", c_int32), ("K", c_int32), ("sink", c_int32), ("window", c_int32),
-                ("causal", c_int32), ("idx", c_void_p)]
+                ("causal", c_int32), ("idx", c_void_p), ("workspace_state", c_int32)]
 
 
 class AttendDesc(ctypes.Structure):
@@ -124,21 +126,21 @@ def _kdtype(t):
     raise TypeError(f"unsupported key dtype {t.dtype}")
 
 
-# Workspaces are cached per (device, kind) and grown on demand. The select workspace
-# must be all-zero before first use; it is cleared by the library's fill kernel.
+# Workspaces are cached per (device, kind, shape key) and grown on demand. A select
+# workspace is "clean" after a successful lsa_select with the same shape key (the
+# library leaves its histogram/counters zeroed), which lets the next call skip its
+# clearing kernel.
 _ws = {}
 
 
-def _workspace(kind: str, nbytes: int, device, stream):
+def _workspace(kind: str, nbytes: int, device, shape_key=()):
     import torch
-    key = (kind, str(device))
-    buf = _ws.get(key)
-    if buf is None or buf.numel() < nbytes:
-        buf = torch.empty(max(nbytes, 256), dtype=torch.uint8, device=device)
-        if kind == "select":
-            _check("lsa_workspace_clear", lib().lsa_workspace_clear(buf.data_ptr(), buf.numel(), stream))
-        _ws[key] = buf
-    return buf
+    key = (kind, str(device), shape_key)
+    ent = _ws.get(key)
+    if ent is None or ent[0].numel() < nbytes:
+        ent = [torch.empty(max(nbytes, 256), dtype=torch.uint8, device=device), False]
+        _ws[key] = ent
+    return ent
 
 
 def lsa_workspace_clear(buf, stream=None):
@@ -204,8 +206,15 @@ def lsa_select(scores, K, sink=0, window=0, *, N=None, ctx_len=None, kept=None, 
     d = _select_desc(scores, K, sink, window, N, ctx_len, kept, block_size, causal, idx)
     s = _stream(stream)
     need = lib().lsa_select_workspace_bytes(ctypes.byref(d))
-    ws = workspace if workspace is not None else _workspace("select", need, scores.device, s)
+    if workspace is not None:
+        ws, ent = workspace, None
+    else:
+        ent = _workspace("select", need, scores.device, (B, T, n_cols))
+        ws = ent[0]
+        d.workspace_state = 1 if ent[1] else 0
     _check("lsa_select", lib().lsa_select(ctypes.byref(d), ws.data_ptr(), ws.numel() * ws.element_size(), s))
+    if ent is not None:
+        ent[1] = True
     return idx
 
 
@@ -245,6 +254,6 @@ def lsa_attend(q, k, v, idx, softmax_scale, *, out=None, lse=None, out_dtype=Non
     d = _attend_desc(q, k, v, idx, softmax_scale, out, lse, mla, n_splits)
     s = _stream(stream)
     need = lib().lsa_attend_workspace_bytes(ctypes.byref(d))
-    ws = workspace if workspace is not None else (_workspace("attend", need, q.device, s) if need else None)
+    ws = workspace if workspace is not None else (_workspace("attend", need, q.device)[0] if need else None)
     _check("lsa_attend", lib().lsa_attend(ctypes.byref(d), _ptr(ws), 0 if ws is None else ws.numel(), s))
     return out, lse

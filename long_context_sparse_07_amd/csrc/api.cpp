@@ -164,6 +164,8 @@ static int32_t select_check(const lsa_select_desc *d, lsa::SelectArgs &a) {
         return fail(LSA_E_BUDGET, "lsa_select: need K >= 1 and 0 <= sink + window <= K (K=%d sink=%d window=%d)", d->K,
                     d->sink, d->window);
     if (d->K > 4096) return fail(LSA_E_UNSUPPORTED, "lsa_select: K=%d above 4096", d->K);
+    if (d->workspace_state != LSA_WS_UNKNOWN && d->workspace_state != LSA_WS_CLEAN)
+        return fail(LSA_E_SHAPE, "lsa_select: unknown workspace_state %d", d->workspace_state);
     if (!d->causal && (d->sink || d->window))
         return fail(LSA_E_BUDGET, "lsa_select: sink and window need causal = 1");
     if (d->kept && (d->n_keep < 1 || d->block_size < 1 || (int64_t)d->n_keep * d->block_size < d->n_cols))
@@ -183,6 +185,7 @@ static int32_t select_check(const lsa_select_desc *d, lsa::SelectArgs &a) {
     a.sink = d->sink;
     a.window = d->window;
     a.causal = d->causal != 0;
+    a.ws_clean = d->workspace_state == LSA_WS_CLEAN;
     a.idx = d->idx;
     return LSA_OK;
 }

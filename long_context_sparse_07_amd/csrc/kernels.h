@@ -55,6 +55,7 @@ struct SelectArgs {
     int n_keep, block_size;
     int K, sink, window;
     bool causal;
+    bool ws_clean;          // histogram/counters already zero (left so by a same-shape call)
     int32_t *idx;
 };
 size_t select_workspace_bytes(const SelectArgs &a);

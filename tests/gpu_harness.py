@@ -96,7 +96,7 @@ def check_band(gpu_idx: np.ndarray, pos: np.ndarray, sc: np.ndarray, forced: np.
     assert fill <= set(cand), f"{what}: selected a non-candidate"
     want = min(m, len(cand))
     assert len(fill) == want, f"{what}: fill {len(fill)} != {want}"
-    if len(cand) <= m:
+    if len(cand) <= m or m == 0:
         return 0
     s_sorted = np.sort(sc)[::-1]
     tau = s_sorted[m - 1]
