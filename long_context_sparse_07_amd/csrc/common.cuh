@@ -50,12 +50,18 @@ __device__ __forceinline__ uint32_t hi_halves(uint32_t lo_word, uint32_t hi_word
     return __builtin_amdgcn_perm(hi_word, lo_word, 0x07060302u);
 }
 
-// Four OCP e4m3fn bytes (one dword) -> four bf16 (two dwords), exact.
+typedef __attribute__((__vector_size__(2 * sizeof(__bf16)))) __bf16 bf16x2;
+
+// Four OCP e4m3fn bytes (one dword) -> four bf16 (two dwords), exact (every e4m3 value
+// is a bf16 value): gfx950 v_cvt_scalef32_pk_bf16_fp8 with scale 1.
 __device__ __forceinline__ void fp8x4_to_bf16x4(uint32_t v, uint32_t &o0, uint32_t &o1) {
-    f32x2 a = __builtin_amdgcn_cvt_pk_f32_fp8(v, false);
-    f32x2 b = __builtin_amdgcn_cvt_pk_f32_fp8(v, true);
-    o0 = hi_halves(f2u(a[0]), f2u(a[1]));
-    o1 = hi_halves(f2u(b[0]), f2u(b[1]));
+    o0 = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(v, 1.0f, false));
+    o1 = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(v, 1.0f, true));
+}
+
+// max(x, 0) on the bit pattern: a float with the sign bit set is a negative int32.
+__device__ __forceinline__ float relu_bits(float x) {
+    return __builtin_bit_cast(float, max(__builtin_bit_cast(int32_t, x), 0));
 }
 
 // 16 fp8 bytes -> two bf16x8 fragments (first 8 bytes, last 8 bytes).

@@ -3,7 +3,9 @@
 // index_tokens_kernel: I[t,s] = scale[s] * sum_h w[t,h] * ReLU(q[t,h] . k[s]) (reading R1
 // of the DSA-style indexer that LSA extends, molayo1419.me LongCat-2.0 article, section
 // "The sparse attention problem at 1M tokens"). The key cache is streamed once, HBM
-// coalesced, into an LDS tile; the (query-head rows) x (keys) contraction runs on
+// coalesced, by direct-to-LDS DMA (global_load_lds_dwordx4) into a 4-stage ring of
+// 128-key tiles (three tiles in flight per workgroup); the (query-head rows) x (keys)
+// contraction runs on
 // v_mfma_f32_32x32x16_bf16 with fp8 keys widened exactly to bf16 in registers; the
 // ReLU, head weights, head sum, per-token scale and causal mask are fused into the
 // MFMA epilogue.
@@ -22,6 +24,16 @@ namespace {
 constexpr int kThreads = 256;
 constexpr int kKT = 128;  // keys per LDS tile (4 waves x 32)
 
+typedef __attribute__((address_space(3))) void lds_void_t;
+typedef __attribute__((address_space(1))) void glb_void_t;
+
+// s_waitcnt vmcnt(n) (gfx9 encoding: expcnt and lgkmcnt left at their maxima)
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+    static_assert(N >= 0 && N < 64, "vmcnt range");
+    __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
+}
+
 // Query-row layouts of one MFMA row group.
 enum { ONEQ = 0, Q4 = 4, Q8 = 8, Q16 = 16 };
 
@@ -29,8 +41,14 @@ template <int D, bool FP8>
 struct Tile {
     static constexpr int RB = FP8 ? D : 2 * D;        // bytes per key row
     static constexpr int CPR = RB / 16;               // 16-byte chunks per row
-    static constexpr int NCH = kKT * CPR / kThreads;  // chunks per thread per tile
     static constexpr int BYTES = kKT * RB;
+    static constexpr int KINSTR = BYTES / 1024;       // 64-lane x 16-byte DMA instructions per tile
+    static constexpr int PER_WAVE = KINSTR / 4 + (FP8 ? 1 : 0);  // + one scale DMA per wave
+    static constexpr int SBYTES = FP8 ? kKT * 4 : 0;  // per-token scales of a tile
+    static constexpr int STAGE = BYTES + SBYTES;
+    static constexpr int NST = 4;                     // ring: one tile computed, three in flight
+    static_assert(KINSTR % 4 == 0, "tile must split evenly over 4 waves");
+    static_assert(PER_WAVE * (NST - 2) < 64, "vmcnt budget");
     static constexpr int RPB = CPR >= 16 ? 1 : 16 / CPR;  // rows per 256-byte bank row
     // XOR swizzle of the 16-byte chunks: 16 lanes reading the same logical chunk of
     // 16 consecutive rows land on 16 distinct groups of 4 banks.
@@ -57,9 +75,8 @@ __global__ __launch_bounds__(kThreads) void index_tokens_kernel(IndexTokensArgs 
     using G = Tile<D, FP8>;
     constexpr int KSTEPS = D / 16;
     constexpr int QPG = MODE == ONEQ ? 1 : 32 / MODE;
-    __shared__ __attribute__((aligned(16))) unsigned char tile[G::BYTES];
-    __shared__ float tscale[kKT];
-    __shared__ int tpos[kKT];
+    extern __shared__ __attribute__((aligned(16))) unsigned char ring[];  // NST x (keys, scales)
+    __shared__ int tpos[G::NST][kKT];                                     // HI: position of each row
 
     const int tid = threadIdx.x;
     const int lane = tid & 63, wave = tid >> 6, half = lane >> 5, l32 = lane & 31;
@@ -121,35 +138,38 @@ __global__ __launch_bounds__(kThreads) void index_tokens_kernel(IndexTokensArgs 
     };
 
     const unsigned char *kbase = reinterpret_cast<const unsigned char *>(a.k) + (int64_t)b * N * G::RB;
-    u32x4 pre[G::NCH];
-    float pscale = 0.0f;
-    int ppos = -1;
+    const float *sbase = FP8 ? a.k_scale + (int64_t)b * N : nullptr;
 
-    auto load_tile = [&](int tc0) {
+    // DMA of one tile into ring stage `st`: key instruction n (of KINSTR) fills LDS chunks
+    // [64 n, 64 n + 64) of the stage; lane l fills physical chunk L = 64 n + l, i.e. row
+    // L / CPR, physical chunk pc = L % CPR, which holds logical chunk pc ^ swz(row) (the
+    // XOR swizzle is applied on the global side, so each row is still read as one
+    // contiguous line). Rows without a position read the cache start (masked later).
+    auto issue_tile = [&](int tc0, int st) {
+        unsigned char *stage = ring + st * G::STAGE;
+        const unsigned char *src[G::KINSTR / 4];
 #pragma unroll
-        for (int j = 0; j < G::NCH; ++j) {
-            int id = j * kThreads + tid;
-            int row = id / G::CPR, c = id % G::CPR;
-            int pos = col_pos(tc0 + row);
-            u32x4 v = {0, 0, 0, 0};
-            if (pos >= 0) v = *reinterpret_cast<const u32x4 *>(kbase + (int64_t)pos * G::RB + c * 16);
-            pre[j] = v;
+        for (int j = 0; j < G::KINSTR / 4; ++j) {
+            const int L = 64 * (j * 4 + wave) + lane;
+            const int row = L / G::CPR, pc = L % G::CPR;
+            const int pos = col_pos(tc0 + row);
+            src[j] = kbase + (pos >= 0 ? (int64_t)pos * G::RB + G::swz(row, pc) * 16 : 0);
         }
-        if (tid < kKT) {
-            ppos = col_pos(tc0 + tid);
-            if constexpr (FP8) pscale = ppos >= 0 ? a.k_scale[(int64_t)b * N + ppos] : 0.0f;
-        }
-    };
-    auto store_tile = [&]() {
 #pragma unroll
-        for (int j = 0; j < G::NCH; ++j) {
-            int id = j * kThreads + tid;
-            int row = id / G::CPR, c = id % G::CPR;
-            *reinterpret_cast<u32x4 *>(tile + row * G::RB + G::swz(row, c) * 16) = pre[j];
+        for (int j = 0; j < G::KINSTR / 4; ++j)
+            __builtin_amdgcn_global_load_lds((const glb_void_t *)src[j], (lds_void_t *)(stage + 1024 * (j * 4 + wave)),
+                                             16, 0, 0);
+        if constexpr (FP8) {
+            // wave w loads the scales of rows [32 w, 32 w + 32): 32 active lanes x 4 bytes
+            if (lane < 32) {
+                const int row = 32 * wave + lane;
+                const int pos = col_pos(tc0 + row);
+                __builtin_amdgcn_global_load_lds((const glb_void_t *)(sbase + (pos >= 0 ? pos : 0)),
+                                                 (lds_void_t *)(stage + G::BYTES + 128 * wave), 4, 0, 0);
+            }
         }
-        if (tid < kKT) {
-            tscale[tid] = pscale;
-            tpos[tid] = ppos;
+        if constexpr (HI) {
+            if (tid < kKT) tpos[st][tid] = col_pos(tc0 + tid);
         }
     };
 
@@ -174,14 +194,23 @@ __global__ __launch_bounds__(kThreads) void index_tokens_kernel(IndexTokensArgs 
             if (col < c1 && t < T) write_score(t, col, kNegInf);
         }
     }
-    if (nvis > 0) load_tile(c0);
+#pragma unroll
+    for (int p = 0; p < G::NST - 1; ++p)
+        if (p < nvis) issue_tile(c0 + p * kKT, p);
 
     for (int it = 0; it < nvis; ++it) {
         const int tc0 = c0 + it * kKT;
-        __syncthreads();
-        store_tile();
-        __syncthreads();
-        if (it + 1 < nvis) load_tile(tc0 + kKT);  // next tile in flight during this compute
+        const int st = it % G::NST;
+        // this wave's DMA of tile `it` is complete once at most `ahead` later tiles'
+        // instructions are pending (vector memory operations retire in issue order)
+        const int ahead = min(G::NST - 2, nvis - 1 - it);
+        if (ahead >= 2) wait_vmcnt<2 * G::PER_WAVE>();
+        else if (ahead == 1) wait_vmcnt<G::PER_WAVE>();
+        else wait_vmcnt<0>();
+        __syncthreads();  // every wave's part of tile `it` landed; stage of tile it-1 is free
+        if (it + G::NST - 1 < nvis) issue_tile(tc0 + (G::NST - 1) * kKT, (it + G::NST - 1) % G::NST);
+        const unsigned char *tile = ring + st * G::STAGE;
+        const float *tscale = reinterpret_cast<const float *>(tile + G::BYTES);
 
         if (active) {
             constexpr int NSUB = PRE ? 4 : 1;
@@ -220,14 +249,16 @@ __global__ __launch_bounds__(kThreads) void index_tokens_kernel(IndexTokensArgs 
                 }
                 // ---- epilogue: ReLU, head weights, head sum, scale, causal mask
                 const int col = tc0 + sub * 32 + l32;
-                const int pos = tpos[row];
+                int pos;
+                if constexpr (HI) pos = tpos[st][row];
+                else pos = col < c1 && col < N ? col : -1;
                 const float sc = FP8 ? tscale[row] : 1.0f;
                 if constexpr (MODE == ONEQ) {
                     float s = 0.0f;
 #pragma unroll
                     for (int hb = 0; hb < HB; ++hb)
 #pragma unroll
-                        for (int r = 0; r < 16; ++r) s += wreg[hb][r] * fmaxf(acc[hb][r], 0.0f);
+                        for (int r = 0; r < 16; ++r) s += wreg[hb][r] * relu_bits(acc[hb][r]);
                     s += __shfl_xor(s, 32, 64);
                     const int t = grp;
                     const int p = ctx - T + t;
@@ -235,7 +266,7 @@ __global__ __launch_bounds__(kThreads) void index_tokens_kernel(IndexTokensArgs 
                 } else if constexpr (MODE == Q4) {
                     float part[4] = {0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
-                    for (int r = 0; r < 16; ++r) part[r / 4] += wreg[0][r] * fmaxf(acc[0][r], 0.0f);
+                    for (int r = 0; r < 16; ++r) part[r / 4] += wreg[0][r] * relu_bits(acc[0][r]);
 #pragma unroll
                     for (int j = 0; j < 4; ++j) {
                         const int t = grp * QPG + 2 * j + half;
@@ -247,7 +278,7 @@ __global__ __launch_bounds__(kThreads) void index_tokens_kernel(IndexTokensArgs 
 #pragma unroll
                     for (int j = 0; j < QPG; ++j) part[j] = 0.0f;
 #pragma unroll
-                    for (int r = 0; r < 16; ++r) part[(8 * (r / 4)) / MODE] += wreg[0][r] * fmaxf(acc[0][r], 0.0f);
+                    for (int r = 0; r < 16; ++r) part[(8 * (r / 4)) / MODE] += wreg[0][r] * relu_bits(acc[0][r]);
 #pragma unroll
                     for (int j = 0; j < QPG; ++j) {
                         part[j] += __shfl_xor(part[j], 32, 64);
@@ -350,13 +381,15 @@ hipError_t launch_tokens_t(const IndexTokensArgs &a, hipStream_t s) {
     const int groups = (a.T + QPG - 1) / QPG;
     const int gy = PRE ? (groups + 3) / 4 : groups;
     const int max_chunks = (a.n_out + kKT - 1) / kKT;
-    int want = (2048 + a.B * gy - 1) / (a.B * gy);
+    int want = (512 + a.B * gy - 1) / (a.B * gy);
     int chunks = want < 1 ? 1 : (want > max_chunks ? max_chunks : want);
     int chunk = (a.n_out + chunks - 1) / chunks;
     chunk = (chunk + kKT - 1) / kKT * kKT;
     chunks = (a.n_out + chunk - 1) / chunk;
     dim3 grid(chunks, gy, a.B);
-    hipLaunchKernelGGL((index_tokens_kernel<D, FP8, MODE, HB, HI, PRE>), grid, dim3(kThreads), 0, s, a, groups, chunk);
+    using G = Tile<D, FP8>;
+    const size_t lds = (size_t)G::NST * G::STAGE;
+    hipLaunchKernelGGL((index_tokens_kernel<D, FP8, MODE, HB, HI, PRE>), grid, dim3(kThreads), lds, s, a, groups, chunk);
     return hipGetLastError();
 }
 

@@ -35,14 +35,16 @@ constexpr int kBitmapMax = 1 << 19;  // positions handled by the LDS bitmap
 constexpr int kCtr = 16;             // per-row counters
 
 // ctr[row][*]
-enum { C_NLIST = 0, C_MODE = 4, C_B1 = 5 };
+enum { C_NLIST = 0, C_NSURE = 1, C_MODE = 4, C_B1 = 5, C_ABOVE = 6 };
 
 struct Ws {
     uint32_t *hist1;  // [rows][4096] fine histogram (top 12 key bits)
     uint32_t *hist0;  // [rows][256] coarse histogram (top 8 key bits)
+    uint32_t *hist2;  // [rows][4096] next 12 key bits of the candidates in bin b1
     uint32_t *ctr;    // [rows][16]
-    uint64_t *list;   // [rows][cap]
-    int cap;
+    int32_t *sure;    // [rows][K] positions of candidates above bin b1
+    uint64_t *list;   // [rows][cap] composites of candidates in bin b1
+    int cap, K;
 };
 
 inline size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
@@ -54,25 +56,32 @@ inline int list_cap(int n_cols) {
     return (c + 63) / 64 * 64;
 }
 
-Ws carve(void *base, int rows, int n_cols) {
+size_t zero_region_bytes(int rows) {
+    return 2 * align256((size_t)rows * kBins * 4) + align256((size_t)rows * 256 * 4) + align256((size_t)rows * kCtr * 4);
+}
+
+Ws carve(void *base, int rows, int K, int n_cols) {
     Ws w;
     char *p = reinterpret_cast<char *>(base);
     w.hist1 = reinterpret_cast<uint32_t *>(p);
+    p += align256((size_t)rows * kBins * 4);
+    w.hist2 = reinterpret_cast<uint32_t *>(p);
     p += align256((size_t)rows * kBins * 4);
     w.hist0 = reinterpret_cast<uint32_t *>(p);
     p += align256((size_t)rows * 256 * 4);
     w.ctr = reinterpret_cast<uint32_t *>(p);
     p += align256((size_t)rows * kCtr * 4);
+    w.sure = reinterpret_cast<int32_t *>(p);
+    p += align256((size_t)rows * K * 4);
     w.list = reinterpret_cast<uint64_t *>(p);
     w.cap = list_cap(n_cols);
+    w.K = K;
     return w;
 }
 
-size_t zero_region_bytes(int rows) {
-    return align256((size_t)rows * kBins * 4) + align256((size_t)rows * 256 * 4) + align256((size_t)rows * kCtr * 4);
+size_t ws_bytes(int rows, int K, int n_cols) {
+    return zero_region_bytes(rows) + align256((size_t)rows * K * 4) + align256((size_t)rows * list_cap(n_cols) * 8);
 }
-
-size_t ws_bytes(int rows, int n_cols) { return zero_region_bytes(rows) + align256((size_t)rows * list_cap(n_cols) * 8); }
 
 // Per-row context: query position, forced set, fill size.
 struct Row {
@@ -159,6 +168,7 @@ __device__ uint32_t block_exscan(uint32_t v, uint32_t *lds4, uint32_t *total) {
 struct BinPick {
     int mode;
     int bin;
+    uint32_t above;  // candidates in bins above `bin` (mode 2)
 };
 
 __device__ BinPick pick_bin(const uint32_t *h, uint32_t need, uint32_t *scratch) {
@@ -169,8 +179,8 @@ __device__ BinPick pick_bin(const uint32_t *h, uint32_t need, uint32_t *scratch)
     for (int e = 0; e < 16; ++e) s += h[hi_bin - e];
     uint32_t total;
     const uint32_t ex = block_exscan(s, scratch, &total);
-    if (need == 0) return BinPick{0, kBins};
-    if (total <= need) return BinPick{1, -1};
+    if (need == 0) return BinPick{0, kBins, 0};
+    if (total <= need) return BinPick{1, -1, total};
     if (ex < need && need <= ex + s) {
         uint32_t acc = ex;
         for (int e = 0; e < 16; ++e) {
@@ -183,7 +193,7 @@ __device__ BinPick pick_bin(const uint32_t *h, uint32_t need, uint32_t *scratch)
         }
     }
     __syncthreads();
-    BinPick r{2, (int)scratch[4]};
+    BinPick r{2, (int)scratch[4], 0};
     __syncthreads();
     return r;
 }
@@ -235,8 +245,8 @@ __device__ BinPick pick_bin2(const uint32_t *g0, const uint32_t *g1, uint32_t ne
     const uint32_t v = g0[255 - tid];  // thread tid owns coarse bin 255 - tid (top first)
     uint32_t total;
     const uint32_t ex = block_exscan(v, scratch, &total);
-    if (need == 0) return BinPick{0, kBins};
-    if (total <= need) return BinPick{1, -1};
+    if (need == 0) return BinPick{0, kBins, 0};
+    if (total <= need) return BinPick{1, -1, total};
     if (ex < need && need <= ex + v) {
         scratch[4] = (uint32_t)(255 - tid);
         scratch[5] = ex;
@@ -251,20 +261,23 @@ __device__ BinPick pick_bin2(const uint32_t *g0, const uint32_t *g1, uint32_t ne
         for (int e = 0; e < 16; ++e) {
             if (acc + s16[e] >= need) {
                 scratch[6] = (uint32_t)(16 * cb + 15 - e);
+                scratch[7] = acc;
                 break;
             }
             acc += s16[e];
         }
     }
     __syncthreads();
-    BinPick r{2, (int)scratch[6]};
+    BinPick r{2, (int)scratch[6], scratch[7]};
     __syncthreads();
     return r;
 }
 
 // ----------------------------------------------------------------------------- F2
 __global__ __launch_bounds__(kT) void select_filter_kernel(SelectArgs a, Ws ws, int part_cols) {
-    __shared__ uint64_t lst[kCh];
+    __shared__ int32_t sbuf[kCh];
+    __shared__ uint64_t lbuf[kCh];
+    __shared__ uint32_t h2[kBins];
     __shared__ uint32_t cnt[4];
     __shared__ uint32_t s16[16];
     __shared__ uint32_t scratch[8];
@@ -275,44 +288,94 @@ __global__ __launch_bounds__(kT) void select_filter_kernel(SelectArgs a, Ws ws, 
     const bool vec = (a.n_cols & 3) == 0;
     const Row r = make_row(a, row);
     uint32_t *ctr = ws.ctr + (int64_t)row * kCtr;
+    int32_t *gsure = ws.sure + (int64_t)row * ws.K;
     uint64_t *glist = ws.list + (int64_t)row * ws.cap;
     if (tid < 4) cnt[tid] = 0;
+    for (int i = tid; i < kBins; i += kT) h2[i] = 0;
+    // the first round's scores are loaded before the threshold pick (independent loads)
+    constexpr int PRE = kCh / (4 * kT);
+    float4 pre[PRE];
+    {
+        const int end = min(c1, c0 + kCh);
+#pragma unroll
+        for (int u = 0; u < PRE; ++u) {
+            const int col = c0 + 4 * (tid + u * kT);
+            if (vec && col + 3 < end) pre[u] = *reinterpret_cast<const float4 *>(r.sc + col);
+            else pre[u] = make_float4(kNegInf, kNegInf, kNegInf, kNegInf);
+        }
+    }
     const BinPick bp = pick_bin2(ws.hist0 + (int64_t)row * 256, ws.hist1 + (int64_t)row * kBins,
                                  (uint32_t)max(r.m, 0), s16, scratch);
     if (blockIdx.x == 0 && tid == 0) {
         ctr[C_MODE] = (uint32_t)bp.mode;
         ctr[C_B1] = (uint32_t)bp.bin;
+        ctr[C_ABOVE] = bp.above;
     }
     if (bp.mode == 0) return;
     const int b1 = bp.bin;
-    for (int base = c0; base < c1; base += kCh) {
-        const int end = min(c1, base + kCh);
-        for (int col = base + 4 * tid; col < end; col += 4 * kT) {
-            float xs[4];
-            if (vec && col + 3 < end) {
-                const float4 v = *reinterpret_cast<const float4 *>(r.sc + col);
-                xs[0] = v.x, xs[1] = v.y, xs[2] = v.z, xs[3] = v.w;
-            } else {
-#pragma unroll
-                for (int e = 0; e < 4; ++e) xs[e] = col + e < end ? r.sc[col + e] : kNegInf;
-            }
-#pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                uint64_t comp;
-                if (col + e < end && candidate_x(a, r, col + e, xs[e], comp) &&
-                    (bp.mode == 1 || (int)(comp >> 52) >= b1))
-                    lst[atomicAdd(&cnt[0], 1u)] = comp;
+    bool any_tie = false;
+    auto classify = [&](int col, float x) {
+        uint64_t comp;
+        if (candidate_x(a, r, col, x, comp)) {
+            const int d1 = (int)(comp >> 52);
+            if (bp.mode == 1 || d1 > b1) {
+                sbuf[atomicAdd(&cnt[0], 1u)] = comp_pos(comp);
+            } else if (d1 == b1) {
+                atomicAdd(&h2[(comp >> 40) & (kBins - 1)], 1u);
+                lbuf[atomicAdd(&cnt[1], 1u)] = comp;
             }
         }
+    };
+    auto classify4 = [&](int col, int end, bool have, float4 v) {
+        if (col >= end) return;
+        if (have && col + 3 < end) {
+            classify(col, v.x);
+            classify(col + 1, v.y);
+            classify(col + 2, v.z);
+            classify(col + 3, v.w);
+        } else {
+            for (int e = 0; e < 4 && col + e < end; ++e) classify(col + e, r.sc[col + e]);
+        }
+    };
+    auto flush = [&]() {
         __syncthreads();
-        if (tid == 0) cnt[1] = cnt[0] ? atomicAdd(&ctr[C_NLIST], cnt[0]) : 0;
+        if (tid == 0) {
+            cnt[2] = cnt[0] ? atomicAdd(&ctr[C_NSURE], cnt[0]) : 0;
+            cnt[3] = cnt[1] ? atomicAdd(&ctr[C_NLIST], cnt[1]) : 0;
+        }
         __syncthreads();
-        const uint32_t n = cnt[0], off = cnt[1];
-        for (uint32_t i = tid; i < n; i += kT)
-            if (off + i < (uint32_t)ws.cap) glist[off + i] = lst[i];
+        const uint32_t ns = cnt[0], nl = cnt[1], os = cnt[2], ol = cnt[3];
+        any_tie |= nl > 0;
+        for (uint32_t i = tid; i < ns; i += kT)
+            if (os + i < (uint32_t)ws.K) gsure[os + i] = sbuf[i];
+        for (uint32_t i = tid; i < nl; i += kT)
+            if (ol + i < (uint32_t)ws.cap) glist[ol + i] = lbuf[i];
         __syncthreads();
-        if (tid == 0) cnt[0] = 0;
+        if (tid < 2) cnt[tid] = 0;
         __syncthreads();
+    };
+    {  // first round from the prefetched registers
+        const int end = min(c1, c0 + kCh);
+#pragma unroll
+        for (int u = 0; u < PRE; ++u) {
+            const int col = c0 + 4 * (tid + u * kT);
+            classify4(col, end, vec, pre[u]);
+        }
+        flush();
+    }
+    for (int base = c0 + kCh; base < c1; base += kCh) {
+        const int end = min(c1, base + kCh);
+        for (int col = base + 4 * tid; col < end; col += 4 * kT) {
+            const bool have = vec && col + 3 < end;
+            const float4 v = have ? *reinterpret_cast<const float4 *>(r.sc + col) : make_float4(0.f, 0.f, 0.f, 0.f);
+            classify4(col, end, have, v);
+        }
+        flush();
+    }
+    if (any_tie) {
+        uint32_t *g2 = ws.hist2 + (int64_t)row * kBins;
+        for (int i = tid; i < kBins; i += kT)
+            if (h2[i]) atomicAdd(&g2[i], h2[i]);
     }
 }
 
@@ -404,62 +467,156 @@ __device__ uint64_t radix_kth(const Src &src, uint32_t need, uint32_t *h256, uin
 }
 
 // ----------------------------------------------------------------------------- R
+// Threshold inside bin b1 from the row's second-level histogram (LDS copy h): the bin b2
+// of the r1-th best tie candidate, and how many tie candidates lie above it.
+__device__ void pick_bin_lds(const uint32_t *h, uint32_t need, uint32_t *scratch, int &bin, uint32_t &above) {
+    const int tid = threadIdx.x;
+    const int hi_bin = kBins - 1 - 16 * tid;
+    uint32_t s = 0;
+#pragma unroll
+    for (int e = 0; e < 16; ++e) s += h[hi_bin - e];
+    uint32_t total;
+    const uint32_t ex = block_exscan(s, scratch, &total);
+    if (ex < need && need <= ex + s) {
+        uint32_t acc = ex;
+        for (int e = 0; e < 16; ++e) {
+            const uint32_t c = h[hi_bin - e];
+            if (acc + c >= need) {
+                scratch[4] = (uint32_t)(hi_bin - e);
+                scratch[5] = acc;
+                break;
+            }
+            acc += c;
+        }
+    }
+    __syncthreads();
+    bin = (int)scratch[4];
+    above = scratch[5];
+    __syncthreads();
+}
+
 template <int KPAD>
 __global__ __launch_bounds__(kT) void select_resolve_kernel(SelectArgs a, Ws ws, int bitmap_words) {
     extern __shared__ __attribute__((aligned(16))) unsigned char dyn[];
-    uint64_t *lst = reinterpret_cast<uint64_t *>(dyn);               // list [kLcap]
+    uint64_t *lst = reinterpret_cast<uint64_t *>(dyn);               // tie list [kLcap]
     uint32_t *area = reinterpret_cast<uint32_t *>(dyn + kLcap * 8);  // bitmap or sort buffer
+    __shared__ uint32_t h[kBins];
     __shared__ uint32_t cnt[4];
     __shared__ uint32_t h256[256];
     __shared__ uint32_t scratch[8];
+    __shared__ uint64_t tiny[256];
+    __shared__ int32_t sure_l[KPAD];
     const int row = blockIdx.x;
     const int tid = threadIdx.x;
     const Row r = make_row(a, row);
     uint32_t *ctr = ws.ctr + (int64_t)row * kCtr;
     const uint64_t *glist = ws.list + (int64_t)row * ws.cap;
+    const int32_t *gsure = ws.sure + (int64_t)row * ws.K;
+    uint32_t *g2 = ws.hist2 + (int64_t)row * kBins;
     const int mode = (int)ctr[C_MODE];
-    const uint32_t n_list = mode == 0 ? 0u : ctr[C_NLIST];
+    const int b1 = (int)ctr[C_B1];
+    const uint32_t n_sure = mode == 0 ? 0u : min(ctr[C_NSURE], (uint32_t)ws.K);
+    const uint32_t n_list = mode == 2 ? ctr[C_NLIST] : 0u;
+    const uint32_t need1 = mode == 2 ? (uint32_t)max(r.m, 0) - ctr[C_ABOVE] : 0u;  // wanted from bin b1
     const bool in_lds = n_list <= (uint32_t)kLcap;
     const bool in_glb = n_list <= (uint32_t)ws.cap;
-    if (in_lds) {
-        // all loads of a thread issued before any is used
+    // issue every independent load first: second-level histogram, tie list, sure list
+    {
+        uint32_t hv[kBins / kT];
+#pragma unroll
+        for (int u = 0; u < kBins / kT; ++u) hv[u] = mode == 2 ? g2[tid + u * kT] : 0u;
         constexpr int U = kLcap / kT;
-        uint64_t v[U];
+        uint64_t lv[U];
 #pragma unroll
         for (int u = 0; u < U; ++u) {
             const uint32_t i = tid + u * kT;
-            v[u] = i < n_list ? __builtin_nontemporal_load(&glist[i]) : 0;
+            lv[u] = (in_lds && i < n_list) ? __builtin_nontemporal_load(&glist[i]) : 0;
+        }
+        constexpr int US = KPAD / kT;
+        int32_t sv[US];
+#pragma unroll
+        for (int u = 0; u < US; ++u) {
+            const uint32_t i = tid + u * kT;
+            sv[u] = i < n_sure ? gsure[i] : 0;
         }
 #pragma unroll
-        for (int u = 0; u < U; ++u) lst[tid + u * kT] = v[u];
+        for (int u = 0; u < kBins / kT; ++u) h[tid + u * kT] = hv[u];
+#pragma unroll
+        for (int u = 0; u < U; ++u) lst[tid + u * kT] = lv[u];
+#pragma unroll
+        for (int u = 0; u < US; ++u) sure_l[tid + u * kT] = sv[u];
     }
+    if (tid == 0) cnt[0] = 0;
     __syncthreads();
-    const ArrSrc lsrc{lst, (int)n_list};
-    const ArrSrc gsrc{glist, (int)min(n_list, (uint32_t)ws.cap)};
-    const RowSrc rsrc{&a, &r};
-    // threshold composite: chosen = candidates with comp >= thr
+    // ---- threshold composite thr: the chosen tie candidates are those with comp >= thr
     uint64_t thr = 0;
-    const uint32_t need = (uint32_t)max(r.m, 0);
+    bool from_row = false;  // exact select over the whole row (large tie groups, overflowed list)
     if (mode == 2) {
-        if (in_lds) thr = radix_kth(lsrc, need, h256, scratch);
-        else if (in_glb) thr = radix_kth(gsrc, need, h256, scratch);
-        else thr = radix_kth(rsrc, need, h256, scratch);
+        int b2;
+        uint32_t above2;
+        pick_bin_lds(h, need1, scratch, b2, above2);
+        const uint32_t need2 = need1 - above2;                    // wanted from (b1, b2)
+        const uint64_t p24 = ((uint64_t)b1 << 52) | ((uint64_t)b2 << 40);
+        const uint32_t n2 = h[b2];
+        if (need2 == n2) {
+            thr = p24;              // the whole (b1, b2) group
+            from_row = !in_glb;     // list incomplete: enumerate comp >= thr from the row
+        } else if (n2 <= 256 && in_glb) {
+            // the few (b1, b2) elements into LDS, then exact radix select on their composites
+            auto gather = [&](uint64_t c) {
+                if ((c >> 40) == (p24 >> 40)) {
+                    const uint32_t slot = atomicAdd(&cnt[0], 1u);
+                    if (slot < 256u) tiny[slot] = c;
+                }
+            };
+            if (in_lds) {
+                for (uint32_t i = tid; i < n_list; i += kT) gather(lst[i]);
+            } else {
+                for (uint32_t i = tid; i < n_list; i += kT) gather(glist[i]);
+            }
+            __syncthreads();
+            // rank of each gathered composite (composites are unique): the need2-th largest
+            // is the one with exactly need2 - 1 larger elements
+            const uint32_t nt = min(cnt[0], 256u);
+            if ((uint32_t)tid < nt) {
+                const uint64_t c = tiny[tid];
+                uint32_t rank = 0;
+                for (uint32_t j = 0; j < nt; ++j) rank += tiny[j] > c;
+                if (rank == need2 - 1) {
+                    scratch[0] = (uint32_t)c;
+                    scratch[1] = (uint32_t)(c >> 32);
+                }
+            }
+            __syncthreads();
+            thr = ((uint64_t)scratch[1] << 32) | scratch[0];
+        } else {
+            // many equal keys or an overflowed list: exact select over the whole row
+            const RowSrc rsrc{&a, &r};
+            thr = radix_kth(rsrc, (uint32_t)max(r.m, 0), h256, scratch);
+            from_row = true;
+        }
     }
     int32_t *dst = a.idx + (int64_t)row * a.K;
+    // chosen fill positions: the sure list plus the tie candidates with comp >= thr, or,
+    // when the row had to be scanned, every candidate with comp >= thr
     auto for_chosen = [&](auto &&fn) {
         if (mode == 0) return;
-        if (in_lds) {
-            for (uint32_t i = tid; i < n_list; i += kT)
-                if (lst[i] >= thr) fn(comp_pos(lst[i]));
-        } else if (in_glb) {
-            for (uint32_t i = tid; i < n_list; i += kT) {
-                const uint64_t c = glist[i];
-                if (c >= thr) fn(comp_pos(c));
-            }
-        } else {
+        if (from_row) {
             for (int i = tid; i < a.n_cols; i += kT) {
                 uint64_t c;
                 if (candidate(a, r, i, c) && c >= thr) fn(comp_pos(c));
+            }
+            return;
+        }
+        for (uint32_t i = tid; i < n_sure; i += kT) fn(sure_l[i]);
+        if (mode != 2) return;
+        if (in_lds) {
+            for (uint32_t i = tid; i < n_list; i += kT)
+                if (lst[i] >= thr) fn(comp_pos(lst[i]));
+        } else {
+            for (uint32_t i = tid; i < n_list; i += kT) {
+                const uint64_t c = glist[i];
+                if (c >= thr) fn(comp_pos(c));
             }
         }
     };
@@ -528,7 +685,10 @@ __global__ __launch_bounds__(kT) void select_resolve_kernel(SelectArgs a, Ws ws,
     }
     // ---- leave the row's histograms and counters at zero for the next call
     uint32_t *g = ws.hist1 + (int64_t)row * kBins;
-    for (int i = tid; i < kBins; i += kT) g[i] = 0;
+    for (int i = tid; i < kBins; i += kT) {
+        g[i] = 0;
+        g2[i] = 0;
+    }
     ws.hist0[(int64_t)row * 256 + tid] = 0;
     if (tid < kCtr) ctr[tid] = 0;
 }
@@ -552,11 +712,11 @@ hipError_t launch_resolve(const SelectArgs &a, const Ws &w, int rows, hipStream_
 
 }  // namespace
 
-size_t select_workspace_bytes(const SelectArgs &a) { return ws_bytes(a.B * a.T, a.n_cols); }
+size_t select_workspace_bytes(const SelectArgs &a) { return ws_bytes(a.B * a.T, a.K, a.n_cols); }
 
 hipError_t launch_select(const SelectArgs &a, void *wsp, hipStream_t s) {
     const int rows = a.B * a.T;
-    Ws w = carve(wsp, rows, a.n_cols);
+    Ws w = carve(wsp, rows, a.K, a.n_cols);
     hipError_t e;
     if (!a.ws_clean) {
         e = launch_clear(wsp, zero_region_bytes(rows), s);
