@@ -97,7 +97,9 @@ extern "C" {
  * kept int32 [B][T][n_keep]; scores fp32 [B][T][n_out] with n_out = N (flat),
  * n_keep*block_size (HI fine) or n_blocks (BLOCKS).
  * Supported: TOKENS D in {64,128}, H in {4,8,16,32,64}, k_dtype bf16 or fp8;
- * BLOCKS D in {64,128}, 1 <= H <= 64, k_dtype f32.
+ * BLOCKS D in {64,128}, 1 <= H <= 64, k_dtype f32, window >= block_size - 1 (so the
+ * incomplete block at p always lies inside the window and never needs fine scoring;
+ * LSA_E_UNSUPPORTED otherwise).
  */
 typedef struct lsa_index_desc {
     int32_t mode;            /* LSA_INDEX_TOKENS or LSA_INDEX_BLOCKS */
@@ -162,7 +164,8 @@ int32_t lsa_block_means(const lsa_block_means_desc *desc, void *stream);
  * call leaves that state zeroed; a caller that reuses a workspace for a call with the
  * same B, T and n_cols (or right after lsa_workspace_clear) may pass LSA_WS_CLEAN to
  * skip the clear. Calls that share one workspace must be ordered on one stream.
- * Supported: 1 <= K <= 4096, n_cols >= 1.
+ * Supported: 1 <= K <= 4096, n_cols >= 1; with a kept map and causal = 1,
+ * window >= block_size - 1 (LSA_E_UNSUPPORTED otherwise).
  */
 typedef struct lsa_select_desc {
     int32_t B, T, N;         /* N: cache rows (bounds positions and the kept map) */

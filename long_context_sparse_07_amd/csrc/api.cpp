@@ -106,6 +106,9 @@ int32_t lsa_index(const lsa_index_desc *d, void *stream) {
         if (d->block_size < 1 || d->n_blocks < 1 || (int64_t)d->n_blocks * d->block_size > d->N)
             return fail(LSA_E_SHAPE, "lsa_index: BLOCKS needs block_size >= 1, 1 <= n_blocks <= N / block_size");
         if (d->sink < 0 || d->window < 0) return fail(LSA_E_SHAPE, "lsa_index: sink and window must be >= 0");
+        if (d->window < d->block_size - 1)
+            return fail(LSA_E_UNSUPPORTED, "lsa_index: BLOCKS needs window >= block_size - 1 (window=%d block_size=%d)",
+                        d->window, d->block_size);
         if (d->D != 64 && d->D != 128) return fail(LSA_E_UNSUPPORTED, "lsa_index: BLOCKS needs D in {64,128}");
         if (d->H > 64) return fail(LSA_E_UNSUPPORTED, "lsa_index: BLOCKS needs H <= 64");
         if (d->T > kMaxGridY) return fail(LSA_E_UNSUPPORTED, "lsa_index: T=%d too large", d->T);
@@ -170,6 +173,9 @@ static int32_t select_check(const lsa_select_desc *d, lsa::SelectArgs &a) {
         return fail(LSA_E_BUDGET, "lsa_select: sink and window need causal = 1");
     if (d->kept && (d->n_keep < 1 || d->block_size < 1 || (int64_t)d->n_keep * d->block_size < d->n_cols))
         return fail(LSA_E_SHAPE, "lsa_select: a kept map needs n_keep * block_size >= n_cols");
+    if (d->kept && d->causal && d->window < d->block_size - 1)
+        return fail(LSA_E_UNSUPPORTED, "lsa_select: a kept map needs window >= block_size - 1 (window=%d block_size=%d)",
+                    d->window, d->block_size);
     if ((int64_t)d->B * d->T > kMaxGridY) return fail(LSA_E_UNSUPPORTED, "lsa_select: B*T too large");
     a = lsa::SelectArgs{};
     a.B = d->B;

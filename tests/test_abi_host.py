@@ -98,7 +98,8 @@ def _att(d, ws=FAKE, nbytes=1 << 40):
     (dict(H=12), -6), (dict(D=96), -6),
     (dict(mode=L.LSA_INDEX_BLOCKS, k_dtype=L.LSA_BF16), -3),
     (dict(mode=L.LSA_INDEX_BLOCKS, k_dtype=L.LSA_F32, block_size=64, n_blocks=17), -2),
-    (dict(mode=L.LSA_INDEX_BLOCKS, k_dtype=L.LSA_F32, block_size=64, n_blocks=16, H=65), -6),
+    (dict(mode=L.LSA_INDEX_BLOCKS, k_dtype=L.LSA_F32, block_size=64, n_blocks=16, window=64, H=65), -6),
+    (dict(mode=L.LSA_INDEX_BLOCKS, k_dtype=L.LSA_F32, block_size=64, n_blocks=16, window=62), -6),
     (dict(kept=FAKE, n_keep=0, block_size=64), -2),
 ])
 def test_index_argument_errors(kw, code):
@@ -114,6 +115,7 @@ def test_index_null_desc():
     (dict(K=0, sink=0, window=0), -4), (dict(sink=200, window=100), -4), (dict(sink=-1), -4),
     (dict(causal=0), -4), (dict(K=5000, sink=0, window=0), -6), (dict(n_cols=0), -2),
     (dict(kept=FAKE, n_keep=4, block_size=64), -2), (dict(B=70000), -6),
+    (dict(kept=FAKE, n_keep=16, block_size=128, window=64), -6),
 ])
 def test_select_argument_errors(kw, code):
     assert _sel(_select_desc(**kw)) == code
