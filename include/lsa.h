@@ -68,6 +68,7 @@ extern "C" {
 /* lsa_select workspace states */
 #define LSA_WS_UNKNOWN 0
 #define LSA_WS_CLEAN 1
+#define LSA_WS_PRIMED 2 /* prepared by lsa_index for exactly the scores it wrote */
 
 /* lsa_index modes */
 #define LSA_INDEX_TOKENS 0
@@ -92,6 +93,18 @@ extern "C" {
  *   block_size - 1 <= p) and holds at least one position outside the forced set
  *   sink [0,sink) U window [p-window+1, p]; -inf for every other block (reading R9).
  *
+ * Priming a selection (TOKENS only): with select_ws != NULL, lsa_index also records in
+ *   select_ws what the selection would otherwise compute in a first pass over these
+ *   scores (per query token, the distribution of the candidate scores: finite scores at
+ *   visible positions outside sink [0,sink) and window [p-window+1, p]). The next
+ *   lsa_select must read exactly these scores, with the same B, T, N, ctx_len, kept
+ *   map, sink and window, causal = 1, and workspace_state = LSA_WS_PRIMED; no other call
+ *   may use select_ws in between. select_ws_bytes must be at least the
+ *   lsa_select_workspace_bytes() of that call (256-byte aligned workspace). With
+ *   select_ws_state = LSA_WS_UNKNOWN the workspace is cleared first (one fill kernel);
+ *   LSA_WS_CLEAN skips that (every successful lsa_select leaves its workspace clean).
+ *   With the kept map, window >= block_size - 1 is required, as in lsa_select.
+ *
  * Shapes: q bf16 [B][T][H][D]; w fp32 [B][T][H]; k per k_dtype: bf16 or fp8 [B][N][D]
  * (TOKENS) or fp32 [B][n_blocks][D] (BLOCKS); k_scale fp32 [B][N] (fp8 keys only);
  * kept int32 [B][T][n_keep]; scores fp32 [B][T][n_out] with n_out = N (flat),
@@ -115,8 +128,12 @@ typedef struct lsa_index_desc {
     int32_t n_keep;          /* kept blocks per query token (HI fine stage) */
     int32_t block_size;      /* HI block size (HI fine stage and BLOCKS) */
     int32_t n_blocks;        /* BLOCKS: block-mean rows per sequence */
-    int32_t sink, window;    /* BLOCKS: forced set used for block eligibility */
+    int32_t sink, window;    /* BLOCKS: forced set used for block eligibility;
+                                TOKENS with select_ws: the forced set of the selection */
     float *scores;           /* fp32 [B][T][n_out], written in full */
+    void *select_ws;         /* optional (TOKENS): workspace of the lsa_select that reads scores */
+    size_t select_ws_bytes;
+    int32_t select_ws_state; /* LSA_WS_UNKNOWN or LSA_WS_CLEAN: state of select_ws on entry */
 } lsa_index_desc;
 
 int32_t lsa_index(const lsa_index_desc *desc, void *stream);
@@ -163,7 +180,9 @@ int32_t lsa_block_means(const lsa_block_means_desc *desc, void *stream);
  * needs (one small fill kernel), so no initial contents are needed. Every successful
  * call leaves that state zeroed; a caller that reuses a workspace for a call with the
  * same B, T and n_cols (or right after lsa_workspace_clear) may pass LSA_WS_CLEAN to
- * skip the clear. Calls that share one workspace must be ordered on one stream.
+ * skip the clear. LSA_WS_PRIMED: lsa_index already prepared the workspace for these
+ * scores (see lsa_index), so the selection skips its first pass over them.
+ * Calls that share one workspace must be ordered on one stream.
  * Supported: 1 <= K <= 4096, n_cols >= 1; with a kept map and causal = 1,
  * window >= block_size - 1 (LSA_E_UNSUPPORTED otherwise).
  */
@@ -177,7 +196,7 @@ typedef struct lsa_select_desc {
     int32_t K, sink, window;
     int32_t causal;          /* 1 token selection at p with forced set, 0 plain top-K */
     int32_t *idx;            /* int32 [B][T][K] */
-    int32_t workspace_state; /* LSA_WS_UNKNOWN (0) or LSA_WS_CLEAN (1), see above */
+    int32_t workspace_state; /* LSA_WS_UNKNOWN (0), LSA_WS_CLEAN (1) or LSA_WS_PRIMED (2) */
 } lsa_select_desc;
 
 size_t lsa_select_workspace_bytes(const lsa_select_desc *desc);

@@ -13,10 +13,10 @@ import ctypes
 import os
 from ctypes import POINTER, c_float, c_int32, c_int64, c_size_t, c_void_p
 
-__all__ = ["lib", "LSAError", "lsa_index", "lsa_block_means", "lsa_select", "lsa_attend",
+__all__ = ["lib", "LSAError", "lsa_index", "lsa_block_means", "lsa_select", "lsa_index_select", "lsa_attend",
            "lsa_workspace_clear", "lsa_select_workspace_bytes", "lsa_attend_workspace_bytes",
            "LSA_BF16", "LSA_FP8_E4M3FN", "LSA_F32", "LSA_INDEX_TOKENS", "LSA_INDEX_BLOCKS",
-           "LSA_WS_UNKNOWN", "LSA_WS_CLEAN",
+           "LSA_WS_UNKNOWN", "LSA_WS_CLEAN", "LSA_WS_PRIMED",
            "IndexDesc", "BlockMeansDesc", "SelectDesc", "AttendDesc", "STATUS"]
 
 HERE = os.path.dirname(os.path.abspath(__file__))
@@ -24,7 +24,7 @@ LIB_PATH = os.path.join(HERE, "liblsa.so")
 
 LSA_BF16, LSA_FP8_E4M3FN, LSA_F32 = 1, 2, 3
 LSA_INDEX_TOKENS, LSA_INDEX_BLOCKS = 0, 1
-LSA_WS_UNKNOWN, LSA_WS_CLEAN = 0, 1
+LSA_WS_UNKNOWN, LSA_WS_CLEAN, LSA_WS_PRIMED = 0, 1, 2
 STATUS = {0: "LSA_OK", -1: "LSA_E_NULL", -2: "LSA_E_SHAPE", -3: "LSA_E_DTYPE", -4: "LSA_E_BUDGET",
           -5: "LSA_E_ALIGN", -6: "LSA_E_UNSUPPORTED", -7: "LSA_E_WORKSPACE", -8: "LSA_E_HIP"}
 
@@ -34,7 +34,8 @@ class IndexDesc(ctypes.Structure):
                 ("ctx_len", c_void_p), ("H", c_int32), ("D", c_int32), ("q", c_void_p),
                 ("w", c_void_p), ("k", c_void_p), ("k_dtype", c_int32), ("k_scale", c_void_p),
                 ("kept", c_void_p), ("n_keep", c_int32), ("block_size", c_int32),
-                ("n_blocks", c_int32), ("sink", c_int32), ("window", c_int32), ("scores", c_void_p)]
+                ("n_blocks", c_int32), ("sink", c_int32), ("window", c_int32), ("scores", c_void_p),
+                ("select_ws", c_void_p), ("select_ws_bytes", c_size_t), ("select_ws_state", c_int32)]
 
 
 class BlockMeansDesc(ctypes.Structure):
@@ -148,9 +149,11 @@ def lsa_workspace_clear(buf, stream=None):
 
 
 def lsa_index(q, w, k, *, k_scale=None, ctx_len=None, kept=None, block_size=0, mode=LSA_INDEX_TOKENS,
-              N=None, n_blocks=0, sink=0, window=0, scores=None, stream=None):
+              N=None, n_blocks=0, sink=0, window=0, scores=None, select_ws=None, select_ws_state=LSA_WS_UNKNOWN,
+              stream=None):
     """Indexer scores. q bf16 [B,T,H,D], w fp32 [B,T,H]; k bf16/fp8 [B,N,D] (tokens) or
-    fp32 block means [B,n_blocks,D] (mode=LSA_INDEX_BLOCKS, N = cache rows)."""
+    fp32 block means [B,n_blocks,D] (mode=LSA_INDEX_BLOCKS, N = cache rows). With
+    select_ws (a uint8 tensor), the selection workspace is primed for these scores."""
     import torch
     B, T, H, D = q.shape
     if mode == LSA_INDEX_TOKENS:
@@ -165,7 +168,9 @@ def lsa_index(q, w, k, *, k_scale=None, ctx_len=None, kept=None, block_size=0, m
         scores = torch.empty((B, T, n_out), dtype=torch.float32, device=q.device)
     d = IndexDesc(mode=mode, B=B, T=T, N=N, ctx_len=_ptr(ctx_len), H=H, D=D, q=_ptr(q), w=_ptr(w), k=_ptr(k),
                   k_dtype=_kdtype(k), k_scale=_ptr(k_scale), kept=_ptr(kept), n_keep=n_keep,
-                  block_size=block_size, n_blocks=n_blocks, sink=sink, window=window, scores=_ptr(scores))
+                  block_size=block_size, n_blocks=n_blocks, sink=sink, window=window, scores=_ptr(scores),
+                  select_ws=_ptr(select_ws), select_ws_bytes=0 if select_ws is None else select_ws.numel(),
+                  select_ws_state=select_ws_state)
     _check("lsa_index", lib().lsa_index(ctypes.byref(d), _stream(stream)))
     return scores
 
@@ -216,6 +221,33 @@ def lsa_select(scores, K, sink=0, window=0, *, N=None, ctx_len=None, kept=None, 
     if ent is not None:
         ent[1] = True
     return idx
+
+
+def lsa_index_select(q, w, k, K, sink, window, *, k_scale=None, ctx_len=None, kept=None, block_size=0,
+                     scores=None, idx=None, stream=None):
+    """lsa_index with a primed selection workspace, then lsa_select on its scores
+    (causal token selection): the same result as the two calls made separately, without
+    the selection's first pass over the scores. Returns (scores, idx)."""
+    import torch
+    B, T = q.shape[0], q.shape[1]
+    N = k.shape[1]
+    n_cols = kept.shape[-1] * block_size if kept is not None else N
+    if scores is None:
+        scores = torch.empty((B, T, n_cols), dtype=torch.float32, device=q.device)
+    if idx is None:
+        idx = torch.empty((B, T, K), dtype=torch.int32, device=q.device)
+    d = _select_desc(scores, K, sink, window, N, ctx_len, kept, block_size, True, idx)
+    need = lib().lsa_select_workspace_bytes(ctypes.byref(d))
+    ent = _workspace("select", need, q.device, (B, T, n_cols))
+    ws = ent[0]
+    lsa_index(q, w, k, k_scale=k_scale, ctx_len=ctx_len, kept=kept, block_size=block_size, N=N, sink=sink,
+              window=window, scores=scores, select_ws=ws, select_ws_state=LSA_WS_CLEAN if ent[1] else LSA_WS_UNKNOWN,
+              stream=stream)
+    ent[1] = False
+    d.workspace_state = LSA_WS_PRIMED
+    _check("lsa_select", lib().lsa_select(ctypes.byref(d), ws.data_ptr(), ws.numel(), _stream(stream)))
+    ent[1] = True
+    return scores, idx
 
 
 def _attend_desc(q, k, v, idx, softmax_scale, out, lse, mla, n_splits):

@@ -82,6 +82,19 @@ int32_t lsa_index(const lsa_index_desc *d, void *stream) {
         }
         if (!lsa::index_tokens_supported(d->H, d->D, hi))
             return fail(LSA_E_UNSUPPORTED, "lsa_index: no token kernel for H=%d D=%d%s", d->H, d->D, hi ? " (HI)" : "");
+        if (d->select_ws) {
+            if (d->sink < 0 || d->window < 0) return fail(LSA_E_SHAPE, "lsa_index: sink and window must be >= 0");
+            if (d->select_ws_state != LSA_WS_UNKNOWN && d->select_ws_state != LSA_WS_CLEAN)
+                return fail(LSA_E_SHAPE, "lsa_index: select_ws_state must be LSA_WS_UNKNOWN or LSA_WS_CLEAN");
+            if ((int64_t)d->B * d->T > kMaxGridY) return fail(LSA_E_UNSUPPORTED, "lsa_index: B*T too large to prime");
+            if (hi && d->window < d->block_size - 1)
+                return fail(LSA_E_UNSUPPORTED, "lsa_index: priming with a kept map needs window >= block_size - 1");
+            const size_t need = lsa::select_workspace_bytes(d->B * d->T, hi ? d->n_keep * d->block_size : d->N, hi);
+            if (d->select_ws_bytes < need)
+                return fail(LSA_E_WORKSPACE, "lsa_index: select_ws of %zu bytes needed, %zu given", need, d->select_ws_bytes);
+            if ((reinterpret_cast<uintptr_t>(d->select_ws) & 255u) != 0)
+                return fail(LSA_E_ALIGN, "lsa_index: select_ws not 256-byte aligned");
+        }
         lsa::IndexTokensArgs a{};
         a.B = d->B;
         a.T = d->T;
@@ -99,7 +112,39 @@ int32_t lsa_index(const lsa_index_desc *d, void *stream) {
         a.block_size = hi ? d->block_size : 0;
         a.scores = d->scores;
         a.n_out = hi ? d->n_keep * d->block_size : d->N;
-        return hip_status(lsa::launch_index_tokens(a, s), "lsa_index");
+        if (!d->select_ws) return hip_status(lsa::launch_index_tokens(a, s), "lsa_index");
+        // priming: the selection histogram, from the indexer epilogue when the kernel has
+        // one query per workgroup, else from the selection's own histogram pass
+        lsa::SelectArgs sa{};
+        sa.B = d->B;
+        sa.T = d->T;
+        sa.N = d->N;
+        sa.ctx_len = d->ctx_len;
+        sa.scores = d->scores;
+        sa.n_cols = a.n_out;
+        sa.kept = d->kept;
+        sa.n_keep = a.n_keep;
+        sa.block_size = hi ? d->block_size : 1;
+        sa.K = 0x3FFFFFFF;  // the histogram counts every candidate
+        sa.sink = d->sink;
+        sa.window = d->window;
+        sa.causal = true;
+        sa.ws_clean = d->select_ws_state == LSA_WS_CLEAN;
+        sa.vec = (a.n_out & 3) == 0;  // scores are 16-byte aligned
+        hipError_t e;
+        if (lsa::index_tokens_fused_hist(d->H, d->T, hi)) {
+            if (!sa.ws_clean) {
+                e = lsa::launch_clear(d->select_ws, lsa::select_zero_bytes(d->B * d->T), s);
+                if (e != hipSuccess) return hip_status(e, "lsa_index");
+            }
+            a.sel_hist = reinterpret_cast<uint32_t *>(d->select_ws);
+            a.sink = d->sink;
+            a.window = d->window;
+            return hip_status(lsa::launch_index_tokens(a, s), "lsa_index");
+        }
+        e = lsa::launch_index_tokens(a, s);
+        if (e != hipSuccess) return hip_status(e, "lsa_index");
+        return hip_status(lsa::launch_select_hist(sa, d->select_ws, s), "lsa_index");
     }
     if (d->mode == LSA_INDEX_BLOCKS) {
         if (d->k_dtype != LSA_F32) return fail(LSA_E_DTYPE, "lsa_index: BLOCKS mode reads fp32 block means");
@@ -167,8 +212,11 @@ static int32_t select_check(const lsa_select_desc *d, lsa::SelectArgs &a) {
         return fail(LSA_E_BUDGET, "lsa_select: need K >= 1 and 0 <= sink + window <= K (K=%d sink=%d window=%d)", d->K,
                     d->sink, d->window);
     if (d->K > 4096) return fail(LSA_E_UNSUPPORTED, "lsa_select: K=%d above 4096", d->K);
-    if (d->workspace_state != LSA_WS_UNKNOWN && d->workspace_state != LSA_WS_CLEAN)
+    if (d->workspace_state != LSA_WS_UNKNOWN && d->workspace_state != LSA_WS_CLEAN &&
+        d->workspace_state != LSA_WS_PRIMED)
         return fail(LSA_E_SHAPE, "lsa_select: unknown workspace_state %d", d->workspace_state);
+    if (d->workspace_state == LSA_WS_PRIMED && !d->causal)
+        return fail(LSA_E_SHAPE, "lsa_select: a primed workspace needs causal = 1");
     if (!d->causal && (d->sink || d->window))
         return fail(LSA_E_BUDGET, "lsa_select: sink and window need causal = 1");
     if (d->kept && (d->n_keep < 1 || d->block_size < 1 || (int64_t)d->n_keep * d->block_size < d->n_cols))
@@ -192,6 +240,8 @@ static int32_t select_check(const lsa_select_desc *d, lsa::SelectArgs &a) {
     a.window = d->window;
     a.causal = d->causal != 0;
     a.ws_clean = d->workspace_state == LSA_WS_CLEAN;
+    a.primed = d->workspace_state == LSA_WS_PRIMED;
+    a.vec = (d->n_cols & 3) == 0 && aligned16(d->scores);
     a.idx = d->idx;
     return LSA_OK;
 }
@@ -199,7 +249,7 @@ static int32_t select_check(const lsa_select_desc *d, lsa::SelectArgs &a) {
 size_t lsa_select_workspace_bytes(const lsa_select_desc *d) {
     lsa::SelectArgs a;
     if (select_check(d, a) != LSA_OK) return 0;
-    return lsa::select_workspace_bytes(a);
+    return lsa::select_workspace_bytes(a.B * a.T, a.n_cols, a.kept != nullptr);
 }
 
 int32_t lsa_select(const lsa_select_desc *d, void *ws, size_t ws_bytes, void *stream) {
@@ -208,7 +258,7 @@ int32_t lsa_select(const lsa_select_desc *d, void *ws, size_t ws_bytes, void *st
     if (rc != LSA_OK) return rc;
     if (!d->scores || !d->idx) return fail(LSA_E_NULL, "lsa_select: scores and idx are required");
     if (!aligned4(d->scores) || !aligned4(d->idx)) return fail(LSA_E_ALIGN, "lsa_select: misaligned scores or idx");
-    const size_t need = lsa::select_workspace_bytes(a);
+    const size_t need = lsa::select_workspace_bytes(a.B * a.T, a.n_cols, a.kept != nullptr);
     if (!ws || ws_bytes < need)
         return fail(LSA_E_WORKSPACE, "lsa_select: workspace of %zu bytes needed, %zu given", need, ws_bytes);
     if ((reinterpret_cast<uintptr_t>(ws) & 255u) != 0) return fail(LSA_E_ALIGN, "lsa_select: workspace not 256-byte aligned");

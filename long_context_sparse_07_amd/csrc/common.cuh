@@ -84,7 +84,33 @@ __device__ __forceinline__ uint32_t order_key(float x) {
     return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
 }
 
+// ---- SI forced set at query position p: sink [0, sink_end) and window [win_lo, p]
+// (empty when win_lo > p); where the two overlap the window starts after the sink.
+__device__ __forceinline__ void forced_bounds(int p, int sink, int window, int &sink_end, int &win_lo) {
+    const int pe = max(p + 1, 0);
+    sink_end = min(sink, pe);
+    win_lo = window > 0 ? max(sink_end, p - window + 1) : pe;
+    win_lo = max(win_lo, 0);
+}
+
+// First-level selection histogram: candidates counted per bin order_key(score) >> 21
+// (sign, exponent and two mantissa bits). Written by the selection's histogram pass or
+// by the indexer epilogue, read by the selection's row pass.
+constexpr int kSelBins = 2048;
+constexpr int kSelShift = 21;
+
 // ---- wave reductions (wave64)
+
+// v[l] + v[l ^ 32] in every lane. v_permlane32_swap exchanges the upper half-wave of
+// its first operand with the lower half-wave of its second; with both operands holding
+// v, the two results hold v[l] and v[l ^ 32] between them. Written as inline asm with
+// both operands read-write: this compiler's builtin for the instruction returns the
+// first result for both. The s_nop pads cover the VALU-write -> permlane-read hazard.
+__device__ __forceinline__ float half_pair_sum(float v) {
+    uint32_t x = __builtin_bit_cast(uint32_t, v), y = x;
+    asm volatile("s_nop 1\n\tv_permlane32_swap_b32 %0, %1\n\ts_nop 1" : "+v"(x), "+v"(y));
+    return __builtin_bit_cast(float, x) + __builtin_bit_cast(float, y);
+}
 __device__ __forceinline__ float wave_xor_f(float v, int mask) { return __shfl_xor(v, mask, 64); }
 
 template <typename T>

@@ -70,13 +70,18 @@ __device__ __forceinline__ void row_to_th(int grp, int i, int H, int T, int &t, 
     }
 }
 
-template <int D, bool FP8, int MODE, int HB, bool HI, bool PRE>
+// HIST (one query per workgroup): the epilogue also counts the selection candidates of
+// its columns per first-level bin of the selection histogram (finite scores at visible
+// positions outside the sink and the window) and adds the counts to sel_hist.
+template <int D, bool FP8, int MODE, int HB, bool HI, bool PRE, bool HIST>
 __global__ __launch_bounds__(kThreads) void index_tokens_kernel(IndexTokensArgs a, int groups, int chunk) {
     using G = Tile<D, FP8>;
     constexpr int KSTEPS = D / 16;
     constexpr int QPG = MODE == ONEQ ? 1 : 32 / MODE;
     extern __shared__ __attribute__((aligned(16))) unsigned char ring[];  // NST x (keys, scales)
     __shared__ int tpos[G::NST][kKT];                                     // HI: position of each row
+    __shared__ uint32_t shist[HIST ? kSelBins : 1];                      // HIST: candidate counts
+    static_assert(!HIST || (MODE == ONEQ && !PRE), "the histogram needs one query per workgroup");
 
     const int tid = threadIdx.x;
     const int lane = tid & 63, wave = tid >> 6, half = lane >> 5, l32 = lane & 31;
@@ -88,8 +93,15 @@ __global__ __launch_bounds__(kThreads) void index_tokens_kernel(IndexTokensArgs 
     int ctx = a.ctx_len ? a.ctx_len[b] : N;
     ctx = min(max(ctx, 0), N);
 
+    constexpr bool OWN = !PRE;
     const int grp = PRE ? blockIdx.y * 4 + wave : blockIdx.y;
     const bool active = grp < groups;
+    int f_se = 0, f_wl = 0;  // HIST: forced set of the workgroup's query
+    if constexpr (HIST) {
+        for (int i = tid; i < kSelBins; i += kThreads) shist[i] = 0;
+        forced_bounds(ctx - T + grp, a.sink, a.window, f_se, f_wl);
+        __syncthreads();
+    }
 
     // ---- query fragments (A operand, rows = query heads) and head weights
     bf16x8 aq[HB][KSTEPS];
@@ -145,31 +157,52 @@ __global__ __launch_bounds__(kThreads) void index_tokens_kernel(IndexTokensArgs 
     // L / CPR, physical chunk pc = L % CPR, which holds logical chunk pc ^ swz(row) (the
     // XOR swizzle is applied on the global side, so each row is still read as one
     // contiguous line). Rows without a position read the cache start (masked later).
+    // OWN (one query group per workgroup): wave w loads exactly the 32 rows it computes,
+    // so the waves stream independently and never wait for each other. Otherwise (four
+    // query groups share each tile) the waves split every tile and meet at a barrier.
+    auto instr = [&](int j) { return OWN ? wave * (G::KINSTR / 4) + j : j * 4 + wave; };
+    // Flat mode: a lane's byte offset from the tile's first row is the same for every
+    // tile, so a tile whose rows all exist only adds the tile offset.
+    int roff[G::KINSTR / 4];
+#pragma unroll
+    for (int j = 0; j < G::KINSTR / 4; ++j) {
+        const int L = 64 * instr(j) + lane;
+        const int row = L / G::CPR, pc = L % G::CPR;
+        roff[j] = row * G::RB + G::swz(row, pc) * 16;
+    }
+    const int full_end = min(c1, N);  // flat: tiles ending at or before it need no masking
     auto issue_tile = [&](int tc0, int st) {
         unsigned char *stage = ring + st * G::STAGE;
+        const bool full = !HI && tc0 + kKT <= full_end;
         const unsigned char *src[G::KINSTR / 4];
+        if (full) {
+            const unsigned char *tb = kbase + (int64_t)tc0 * G::RB;
 #pragma unroll
-        for (int j = 0; j < G::KINSTR / 4; ++j) {
-            const int L = 64 * (j * 4 + wave) + lane;
-            const int row = L / G::CPR, pc = L % G::CPR;
-            const int pos = col_pos(tc0 + row);
-            src[j] = kbase + (pos >= 0 ? (int64_t)pos * G::RB + G::swz(row, pc) * 16 : 0);
+            for (int j = 0; j < G::KINSTR / 4; ++j) src[j] = tb + roff[j];
+        } else {
+#pragma unroll
+            for (int j = 0; j < G::KINSTR / 4; ++j) {
+                const int L = 64 * instr(j) + lane;
+                const int row = L / G::CPR, pc = L % G::CPR;
+                const int pos = col_pos(tc0 + row);
+                src[j] = kbase + (pos >= 0 ? (int64_t)pos * G::RB + G::swz(row, pc) * 16 : 0);
+            }
         }
 #pragma unroll
         for (int j = 0; j < G::KINSTR / 4; ++j)
-            __builtin_amdgcn_global_load_lds((const glb_void_t *)src[j], (lds_void_t *)(stage + 1024 * (j * 4 + wave)),
-                                             16, 0, 0);
+            __builtin_amdgcn_global_load_lds((const glb_void_t *)src[j], (lds_void_t *)(stage + 1024 * instr(j)), 16,
+                                             0, 0);
         if constexpr (FP8) {
             // wave w loads the scales of rows [32 w, 32 w + 32): 32 active lanes x 4 bytes
             if (lane < 32) {
                 const int row = 32 * wave + lane;
-                const int pos = col_pos(tc0 + row);
+                const int pos = full ? tc0 + row : col_pos(tc0 + row);
                 __builtin_amdgcn_global_load_lds((const glb_void_t *)(sbase + (pos >= 0 ? pos : 0)),
                                                  (lds_void_t *)(stage + G::BYTES + 128 * wave), 4, 0, 0);
             }
         }
-        if constexpr (HI) {
-            if (tid < kKT) tpos[st][tid] = col_pos(tc0 + tid);
+        if constexpr (HI) {  // positions of this wave's rows (read back by this wave only)
+            if (lane < 32) tpos[st][32 * wave + lane] = col_pos(tc0 + 32 * wave + lane);
         }
     };
 
@@ -207,7 +240,10 @@ __global__ __launch_bounds__(kThreads) void index_tokens_kernel(IndexTokensArgs 
         if (ahead >= 2) wait_vmcnt<2 * G::PER_WAVE>();
         else if (ahead == 1) wait_vmcnt<G::PER_WAVE>();
         else wait_vmcnt<0>();
-        __syncthreads();  // every wave's part of tile `it` landed; stage of tile it-1 is free
+        // OWN: this wave's rows of tile `it` landed and it has finished reading its rows of
+        // tile it-1 (the stage refilled next). Shared tiles: every wave's part landed and
+        // every wave is done with tile it-1.
+        if constexpr (!OWN) __syncthreads();
         if (it + G::NST - 1 < nvis) issue_tile(tc0 + (G::NST - 1) * kKT, (it + G::NST - 1) % G::NST);
         const unsigned char *tile = ring + st * G::STAGE;
         const float *tscale = reinterpret_cast<const float *>(tile + G::BYTES);
@@ -224,13 +260,17 @@ __global__ __launch_bounds__(kThreads) void index_tokens_kernel(IndexTokensArgs 
                 for (int hb = 0; hb < HB; ++hb)
 #pragma unroll
                     for (int r = 0; r < 16; ++r) acc[hb][r] = 0.0f;
+                // every LDS operand of the sub-tile is requested before the first MFMA
+                const float sc = FP8 ? tscale[row] : 1.0f;
                 if constexpr (FP8) {
+                    u32x4 kv[KSTEPS / 2];
+#pragma unroll
+                    for (int kk = 0; kk < KSTEPS / 2; ++kk)
+                        kv[kk] = *reinterpret_cast<const u32x4 *>(trow + G::swz(row, (D / 32) * half + kk) * 16);
 #pragma unroll
                     for (int kk = 0; kk < KSTEPS / 2; ++kk) {
-                        int c = (D / 32) * half + kk;
-                        u32x4 v = *reinterpret_cast<const u32x4 *>(trow + G::swz(row, c) * 16);
                         bf16x8 f0, f1;
-                        fp8x16_to_frags(v, f0, f1);
+                        fp8x16_to_frags(kv[kk], f0, f1);
 #pragma unroll
                         for (int hb = 0; hb < HB; ++hb) {
                             acc[hb] = mfma32(aq[hb][2 * kk], f0, acc[hb]);
@@ -238,11 +278,13 @@ __global__ __launch_bounds__(kThreads) void index_tokens_kernel(IndexTokensArgs 
                         }
                     }
                 } else {
+                    u32x4 kv[KSTEPS];
+#pragma unroll
+                    for (int ks = 0; ks < KSTEPS; ++ks)  // bytes D*half + 16*ks
+                        kv[ks] = *reinterpret_cast<const u32x4 *>(trow + G::swz(row, (D / 16) * half + ks) * 16);
 #pragma unroll
                     for (int ks = 0; ks < KSTEPS; ++ks) {
-                        int c = (D / 16) * half + ks;  // bytes D*half + 16*ks
-                        u32x4 v = *reinterpret_cast<const u32x4 *>(trow + G::swz(row, c) * 16);
-                        bf16x8 f = __builtin_bit_cast(bf16x8, v);
+                        const bf16x8 f = __builtin_bit_cast(bf16x8, kv[ks]);
 #pragma unroll
                         for (int hb = 0; hb < HB; ++hb) acc[hb] = mfma32(aq[hb][ks], f, acc[hb]);
                     }
@@ -252,17 +294,24 @@ __global__ __launch_bounds__(kThreads) void index_tokens_kernel(IndexTokensArgs 
                 int pos;
                 if constexpr (HI) pos = tpos[st][row];
                 else pos = col < c1 && col < N ? col : -1;
-                const float sc = FP8 ? tscale[row] : 1.0f;
                 if constexpr (MODE == ONEQ) {
-                    float s = 0.0f;
+                    // head sum in four independent chains, then the other half-wave's heads
+                    float s4[4] = {0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
                     for (int hb = 0; hb < HB; ++hb)
 #pragma unroll
-                        for (int r = 0; r < 16; ++r) s += wreg[hb][r] * relu_bits(acc[hb][r]);
-                    s += __shfl_xor(s, 32, 64);
+                        for (int r = 0; r < 16; ++r) s4[r & 3] += wreg[hb][r] * relu_bits(acc[hb][r]);
+                    const float s = half_pair_sum((s4[0] + s4[1]) + (s4[2] + s4[3]));
                     const int t = grp;
                     const int p = ctx - T + t;
-                    if (half == 0 && col < c1) write_score(t, col, (pos >= 0 && pos <= p) ? s * sc : kNegInf);
+                    if (half == 0 && col < c1) {
+                        const bool vis = pos >= 0 && pos <= p;
+                        const float v = vis ? s * sc : kNegInf;
+                        write_score(t, col, v);
+                        if constexpr (HIST)
+                            if (vis && pos >= f_se && pos < f_wl && v > kNegInf)
+                                atomicAdd(&shist[order_key(v) >> kSelShift], 1u);
+                    }
                 } else if constexpr (MODE == Q4) {
                     float part[4] = {0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
@@ -288,6 +337,16 @@ __global__ __launch_bounds__(kThreads) void index_tokens_kernel(IndexTokensArgs 
                             write_score(t, col, (pos >= 0 && pos <= p) ? part[j] * sc : kNegInf);
                     }
                 }
+            }
+        }
+    }
+    if constexpr (HIST) {
+        __syncthreads();
+        if (active) {
+            uint32_t *g = a.sel_hist + (int64_t)(b * T + grp) * kSelBins;
+            for (int i = tid; i < kSelBins; i += kThreads) {
+                const uint32_t v = shist[i];
+                if (v) atomicAdd(&g[i], v);
             }
         }
     }
@@ -375,7 +434,7 @@ __global__ __launch_bounds__(128) void block_means_kernel(BlockMeansArgs a) {
     a.kbar[((int64_t)b * a.n_blocks + j) * D + d] = acc / (float)Bs;
 }
 
-template <int D, bool FP8, int MODE, int HB, bool HI, bool PRE>
+template <int D, bool FP8, int MODE, int HB, bool HI, bool PRE, bool HIST = false>
 hipError_t launch_tokens_t(const IndexTokensArgs &a, hipStream_t s) {
     const int QPG = MODE == ONEQ ? 1 : 32 / MODE;
     const int groups = (a.T + QPG - 1) / QPG;
@@ -389,13 +448,22 @@ hipError_t launch_tokens_t(const IndexTokensArgs &a, hipStream_t s) {
     dim3 grid(chunks, gy, a.B);
     using G = Tile<D, FP8>;
     const size_t lds = (size_t)G::NST * G::STAGE;
-    hipLaunchKernelGGL((index_tokens_kernel<D, FP8, MODE, HB, HI, PRE>), grid, dim3(kThreads), lds, s, a, groups, chunk);
+    hipLaunchKernelGGL((index_tokens_kernel<D, FP8, MODE, HB, HI, PRE, HIST>), grid, dim3(kThreads), lds, s, a, groups,
+                       chunk);
     return hipGetLastError();
 }
 
 template <int D, bool FP8>
 hipError_t launch_tokens_d(const IndexTokensArgs &a, hipStream_t s) {
     const bool hi = a.kept != nullptr;
+    if (a.sel_hist) {  // one query per workgroup: the epilogue builds the selection histogram
+        if (hi) {
+            if (a.H <= 32) return launch_tokens_t<D, FP8, ONEQ, 1, true, false, true>(a, s);
+            return launch_tokens_t<D, FP8, ONEQ, 2, true, false, true>(a, s);
+        }
+        if (a.H == 32) return launch_tokens_t<D, FP8, ONEQ, 1, false, false, true>(a, s);
+        return launch_tokens_t<D, FP8, ONEQ, 2, false, false, true>(a, s);
+    }
     if (hi) {
         if (a.H <= 32) return launch_tokens_t<D, FP8, ONEQ, 1, true, false>(a, s);
         return launch_tokens_t<D, FP8, ONEQ, 2, true, false>(a, s);
@@ -414,6 +482,11 @@ hipError_t launch_tokens_d(const IndexTokensArgs &a, hipStream_t s) {
 }
 
 }  // namespace
+
+bool index_tokens_fused_hist(int H, int T, bool hi) {
+    if (hi) return true;
+    return (H == 32 || H == 64) && T < 64;
+}
 
 bool index_tokens_supported(int H, int D, bool hi) {
     if (D != 64 && D != 128) return false;

@@ -21,9 +21,14 @@ struct IndexTokensArgs {
     int n_keep, block_size;
     float *scores;          // [B][T][n_out]
     int n_out;
+    uint32_t *sel_hist;     // optional: selection histogram [B*T][kSelBins] to add candidates to
+    int sink, window;       // forced set excluded from sel_hist
 };
 hipError_t launch_index_tokens(const IndexTokensArgs &a, hipStream_t s);
 bool index_tokens_supported(int H, int D, bool hi);
+// true when the token kernel for (H, T, hi) builds sel_hist in its epilogue (one query
+// per workgroup); otherwise sel_hist must be built by launch_select_hist.
+bool index_tokens_fused_hist(int H, int T, bool hi);
 
 struct IndexBlocksArgs {
     int B, T, N, H, D;
@@ -55,11 +60,17 @@ struct SelectArgs {
     int n_keep, block_size;
     int K, sink, window;
     bool causal;
-    bool ws_clean;          // histogram/counters already zero (left so by a same-shape call)
+    bool ws_clean;          // histogram already zero (left so by a same-shape call)
+    bool primed;            // histogram already built for these scores (by the indexer)
+    bool vec;               // rows 16-byte aligned (n_cols % 4 == 0 and aligned scores)
     int32_t *idx;
 };
-size_t select_workspace_bytes(const SelectArgs &a);
+size_t select_workspace_bytes(int rows, int n_cols, bool kept);
+size_t select_zero_bytes(int rows);  // the part of the workspace kept at zero between calls
 hipError_t launch_select(const SelectArgs &a, void *ws, hipStream_t s);
+// Histogram pass alone (the selection's first pass), for an index call that primes a
+// selection workspace with a kernel that cannot build it in its epilogue.
+hipError_t launch_select_hist(const SelectArgs &a, void *ws, hipStream_t s);
 
 struct AttendArgs {
     int B, T, N, Hq, Hkv, d_qk, d_v;

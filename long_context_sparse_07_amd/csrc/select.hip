@@ -3,84 +3,87 @@
 // (LongCat-Flash-Lite-Sparse summary, "Good to know" and "Technical features", first
 // bullet: the selection budget is split into a fixed sink and a local window).
 //
-// Exact multi-workgroup selection on a 64-bit composite key
+// Exact selection on a 64-bit composite key
 //     comp = order_key(score) << 32 | ~position
-// (larger comp = better: higher score, then lower position; composites are unique).
-//   F1 hist:    every workgroup histograms the top 12 key bits of its column range in
-//               LDS and adds it to the row's fine (4096-bin) and coarse (256-bin)
-//               histograms with integer atomics.
-//   F2 filter:  every workgroup finds the threshold bin b1 (the bin of the m-th best
-//               candidate) from the coarse histogram and the 16 fine bins under it,
-//               then appends the composites of its candidates in bins >= b1 to the
-//               row's list (one atomic reservation per round).
-//   R resolve:  one workgroup per row loads the list into LDS, finds the m-th largest
-//               composite by 8-bit radix passes, marks the forced and chosen positions
-//               in an LDS bitmap and writes them in ascending order (a bitonic sort
-//               instead when positions exceed 2^19); it then zeroes its row's
-//               histograms and counters for the next call.
-// Kernel boundaries are the only cross-workgroup synchronisation (no device-scope
-// fences). Membership is defined by the total order on composites and the output is
-// sorted, so the result does not depend on the order in which atomics land.
+// (larger comp = better: higher score, then lower position; composites are unique), so
+// the chosen set is the set of the m largest composites among the candidates.
+//   hist:     many workgroups per row count the candidates per first-level bin (top 11
+//             bits of the order key) in LDS and add the counts to the row's histogram
+//             with integer atomics. The indexer can build the same histogram in its
+//             epilogue; then this pass is skipped.
+//   filter:   many workgroups per row find the threshold bin b1 from the histogram and
+//             classify their columns: candidates above b1 are set in the row's column
+//             bitmap (each workgroup writes whole words of its own column range), the
+//             candidates in b1 are appended to the row's tie list.
+//   resolve:  one workgroup per row ranks the tie list in LDS (second-level histogram
+//             of the next 12 key bits, then direct ranking of the few candidates that
+//             share 23 key bits, or radix passes when many are equal), sets the chosen
+//             ties in the bitmap, and compacts the bitmap into ascending positions
+//             between the sink and the window. It leaves the row's histogram and
+//             counters at zero for the next call.
+// Kernel boundaries are the only cross-workgroup synchronisation. Membership is
+// defined by the total order on composites and the output is sorted, so the result
+// does not depend on the order in which atomics land.
 #include "common.cuh"
 #include "kernels.h"
 
 namespace lsa {
 namespace {
 
-constexpr int kT = 256;
-constexpr int kBins = 4096;          // 12-bit first-level digit
-constexpr int kCh = 1024;            // F2 staging round (columns)
-constexpr int kLcap = 4096;          // list entries resolved in LDS
-constexpr int kBitmapMax = 1 << 19;  // positions handled by the LDS bitmap
-constexpr int kCtr = 16;             // per-row counters
-
-// ctr[row][*]
-enum { C_NLIST = 0, C_NSURE = 1, C_MODE = 4, C_B1 = 5, C_ABOVE = 6 };
-
-struct Ws {
-    uint32_t *hist1;  // [rows][4096] fine histogram (top 12 key bits)
-    uint32_t *hist0;  // [rows][256] coarse histogram (top 8 key bits)
-    uint32_t *hist2;  // [rows][4096] next 12 key bits of the candidates in bin b1
-    uint32_t *ctr;    // [rows][16]
-    int32_t *sure;    // [rows][K] positions of candidates above bin b1
-    uint64_t *list;   // [rows][cap] composites of candidates in bin b1
-    int cap, K;
-};
+constexpr int kHT = 256;             // histogram and filter threads
+constexpr int kRT = 1024;            // resolve threads (16 waves)
+constexpr int kFC = 2048;            // filter round: 8 columns per thread
+constexpr int kB2 = 4096;            // second-level bins: the next 12 key bits
+constexpr int kL2Shift = kSelShift - 12;
+constexpr int kGrpShift = 32 + kL2Shift;  // composite bits above it: the 23 key bits of (b1, b2)
+constexpr int kB1Shift = 32 + kSelShift;  // composite bits above it: the 11 key bits of b1
+constexpr int kTieMax = 8192;        // tie list capacity (LDS of the resolve)
+constexpr int kTiny = 1024;          // a final group up to this size is ranked directly
+constexpr int kCtr = 16;             // per-row counters: [0] tie count
 
 inline size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 
-inline int list_cap(int n_cols) {
-    int c = n_cols / 8;
-    if (c < 8192) c = 8192;
-    if (c > n_cols) c = n_cols;
-    return (c + 63) / 64 * 64;
+inline int tie_cap(int n_cols) {
+    int c = (n_cols / 16 + 63) / 64 * 64;
+    return c < 2048 ? 2048 : (c > kTieMax ? kTieMax : c);
 }
+inline int bit_words(int n_cols) { return (n_cols + 31) / 32; }
 
-size_t zero_region_bytes(int rows) {
-    return 2 * align256((size_t)rows * kBins * 4) + align256((size_t)rows * 256 * 4) + align256((size_t)rows * kCtr * 4);
-}
+// Workspace: per row the first-level histogram and counters (kept at zero between
+// calls), the tie list (composites, and columns when a kept map is used) and the column
+// bitmap (rewritten by every call).
+struct Ws {
+    uint32_t *hist;   // [rows][kSelBins]
+    uint32_t *ctr;    // [rows][kCtr]
+    uint64_t *ties;   // [rows][cap]
+    uint32_t *tcols;  // [rows][cap] (kept map only)
+    uint32_t *bits;   // [rows][words]
+    int cap, words;
+};
 
-Ws carve(void *base, int rows, int K, int n_cols) {
+size_t zero_bytes(int rows) { return align256((size_t)rows * kSelBins * 4) + align256((size_t)rows * kCtr * 4); }
+
+Ws carve(void *base, int rows, int n_cols, bool kept) {
     Ws w;
     char *p = reinterpret_cast<char *>(base);
-    w.hist1 = reinterpret_cast<uint32_t *>(p);
-    p += align256((size_t)rows * kBins * 4);
-    w.hist2 = reinterpret_cast<uint32_t *>(p);
-    p += align256((size_t)rows * kBins * 4);
-    w.hist0 = reinterpret_cast<uint32_t *>(p);
-    p += align256((size_t)rows * 256 * 4);
+    w.cap = tie_cap(n_cols);
+    w.words = bit_words(n_cols);
+    w.hist = reinterpret_cast<uint32_t *>(p);
+    p += align256((size_t)rows * kSelBins * 4);
     w.ctr = reinterpret_cast<uint32_t *>(p);
     p += align256((size_t)rows * kCtr * 4);
-    w.sure = reinterpret_cast<int32_t *>(p);
-    p += align256((size_t)rows * K * 4);
-    w.list = reinterpret_cast<uint64_t *>(p);
-    w.cap = list_cap(n_cols);
-    w.K = K;
+    w.ties = reinterpret_cast<uint64_t *>(p);
+    p += align256((size_t)rows * w.cap * 8);
+    w.tcols = kept ? reinterpret_cast<uint32_t *>(p) : nullptr;
+    if (kept) p += align256((size_t)rows * w.cap * 4);
+    w.bits = reinterpret_cast<uint32_t *>(p);
     return w;
 }
 
-size_t ws_bytes(int rows, int K, int n_cols) {
-    return zero_region_bytes(rows) + align256((size_t)rows * K * 4) + align256((size_t)rows * list_cap(n_cols) * 8);
+size_t ws_total(int rows, int n_cols, bool kept) {
+    const int cap = tie_cap(n_cols);
+    return zero_bytes(rows) + align256((size_t)rows * cap * 8) + (kept ? align256((size_t)rows * cap * 4) : 0) +
+           align256((size_t)rows * bit_words(n_cols) * 4);
 }
 
 // Per-row context: query position, forced set, fill size.
@@ -102,10 +105,7 @@ __device__ __forceinline__ Row make_row(const SelectArgs &a, int row) {
     ctx = min(max(ctx, 0), a.N);
     r.p = ctx - a.T + r.t;
     if (a.causal) {
-        const int pe = max(r.p + 1, 0);
-        r.f_sink_end = min(a.sink, pe);
-        r.f_win_lo = a.window > 0 ? max(r.f_sink_end, r.p - a.window + 1) : pe;
-        r.f_win_lo = max(r.f_win_lo, 0);
+        forced_bounds(r.p, a.sink, a.window, r.f_sink_end, r.f_win_lo);
         r.m = a.K - (r.f_sink_end + max(0, r.p - r.f_win_lo + 1));
     } else {
         r.f_sink_end = 0;
@@ -133,27 +133,28 @@ __device__ __forceinline__ bool candidate_x(const SelectArgs &a, const Row &r, i
     return true;
 }
 
-__device__ __forceinline__ bool candidate(const SelectArgs &a, const Row &r, int col, uint64_t &comp) {
-    return candidate_x(a, r, col, r.sc[col], comp);
-}
-
 __device__ __forceinline__ int comp_pos(uint64_t c) { return (int)(~(uint32_t)c); }
 
-// Block-wide exclusive scan of one value per thread (256 threads, wave64).
-__device__ uint32_t block_exscan(uint32_t v, uint32_t *lds4, uint32_t *total) {
+__device__ __forceinline__ uint32_t lane_rank(uint64_t mask) {  // set lanes of mask below this lane
+    return __builtin_amdgcn_mbcnt_hi((uint32_t)(mask >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)mask, 0u));
+}
+
+// Block-wide exclusive scan of one value per thread (NT threads, wave64); lds >= NT/64 words.
+template <int NT>
+__device__ uint32_t block_exscan(uint32_t v, uint32_t *lds, uint32_t *total) {
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     uint32_t x = v;
 #pragma unroll
     for (int o = 1; o < 64; o <<= 1) {
-        uint32_t y = __shfl_up(x, o, 64);
+        const uint32_t y = __shfl_up(x, o, 64);
         if (lane >= o) x += y;
     }
-    if (lane == 63) lds4[wave] = x;
+    if (lane == 63) lds[wave] = x;
     __syncthreads();
     uint32_t base = 0, tot = 0;
 #pragma unroll
-    for (int w = 0; w < 4; ++w) {
-        uint32_t s = lds4[w];
+    for (int w = 0; w < NT / 64; ++w) {
+        const uint32_t s = lds[w];
         if (w < wave) base += s;
         tot += s;
     }
@@ -162,56 +163,57 @@ __device__ uint32_t block_exscan(uint32_t v, uint32_t *lds4, uint32_t *total) {
     return base + x - v;
 }
 
-// Threshold bin of the 4096-bin histogram h (LDS), counted from the top: the bin b with
-// above(b) < need <= above(b) + h[b]. mode 0: need == 0; 1: total <= need (take all);
-// 2: threshold bin found.
+// Threshold bin of an NB-bin LDS histogram counted from the top bin: the bin b with
+// above(b) < need <= above(b) + h[b]. mode 0: need == 0 (nothing); 1: total <= need
+// (take everything); 2: threshold bin found. scr >= 24 words.
 struct BinPick {
     int mode;
     int bin;
-    uint32_t above;  // candidates in bins above `bin` (mode 2)
+    uint32_t above;  // elements in bins above `bin` (mode 2), or the total (mode 1)
 };
 
-__device__ BinPick pick_bin(const uint32_t *h, uint32_t need, uint32_t *scratch) {
-    const int tid = threadIdx.x;
-    const int hi_bin = kBins - 1 - 16 * tid;  // thread tid owns 16 bins, walked from the top
+// v[e] is bin NB - 1 - PER * threadIdx.x - e of an NB = NT * PER bin histogram.
+template <int NT, int PER>
+__device__ BinPick pick_bin(const uint32_t (&v)[PER], uint32_t need, uint32_t *scr) {
+    constexpr int NB = NT * PER;
+    const int top = NB - 1 - PER * (int)threadIdx.x;
     uint32_t s = 0;
 #pragma unroll
-    for (int e = 0; e < 16; ++e) s += h[hi_bin - e];
+    for (int e = 0; e < PER; ++e) s += v[e];
     uint32_t total;
-    const uint32_t ex = block_exscan(s, scratch, &total);
-    if (need == 0) return BinPick{0, kBins, 0};
+    const uint32_t ex = block_exscan<NT>(s, scr, &total);
+    if (need == 0) return BinPick{0, NB, 0};
     if (total <= need) return BinPick{1, -1, total};
     if (ex < need && need <= ex + s) {
         uint32_t acc = ex;
-        for (int e = 0; e < 16; ++e) {
-            const uint32_t c = h[hi_bin - e];
-            if (acc + c >= need) {
-                scratch[4] = (uint32_t)(hi_bin - e);
-                break;
+#pragma unroll
+        for (int e = 0; e < PER; ++e) {
+            if (acc < need && need <= acc + v[e]) {
+                scr[16] = (uint32_t)(top - e);
+                scr[17] = acc;
             }
-            acc += c;
+            acc += v[e];
         }
     }
     __syncthreads();
-    BinPick r{2, (int)scratch[4], 0};
+    const BinPick r{2, (int)scr[16], scr[17]};
     __syncthreads();
     return r;
 }
 
-// ----------------------------------------------------------------------------- F1
-__global__ __launch_bounds__(kT) void select_hist_kernel(SelectArgs a, Ws ws, int part_cols) {
-    __shared__ uint32_t h[kBins];
+// ----------------------------------------------------------------------------- hist
+__global__ __launch_bounds__(kHT) void select_hist_kernel(SelectArgs a, uint32_t *hist, int part_cols) {
+    __shared__ uint32_t h[kSelBins];
     const int row = blockIdx.y;
     const int c0 = blockIdx.x * part_cols;
     const int c1 = min(a.n_cols, c0 + part_cols);
-    const bool vec = (a.n_cols & 3) == 0;
-    for (int i = threadIdx.x; i < kBins; i += kT) h[i] = 0;
+    for (int i = threadIdx.x; i < kSelBins; i += kHT) h[i] = 0;
     __syncthreads();
     const Row r = make_row(a, row);
     if (r.m > 0) {
-        for (int col = c0 + 4 * threadIdx.x; col < c1; col += 4 * kT) {
+        for (int col = c0 + 4 * threadIdx.x; col < c1; col += 4 * kHT) {
             float xs[4];
-            if (vec && col + 3 < c1) {
+            if (a.vec && col + 3 < c1) {
                 const float4 v = *reinterpret_cast<const float4 *>(r.sc + col);
                 xs[0] = v.x, xs[1] = v.y, xs[2] = v.z, xs[3] = v.w;
             } else {
@@ -221,166 +223,17 @@ __global__ __launch_bounds__(kT) void select_hist_kernel(SelectArgs a, Ws ws, in
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
                 uint64_t comp;
-                if (col + e < c1 && candidate_x(a, r, col + e, xs[e], comp)) atomicAdd(&h[comp >> 52], 1u);
+                if (col + e < c1 && candidate_x(a, r, col + e, xs[e], comp)) atomicAdd(&h[(uint32_t)(comp >> 32) >> kSelShift], 1u);
             }
         }
     }
     __syncthreads();
-    uint32_t *g = ws.hist1 + (int64_t)row * kBins;
-    uint32_t *g0 = ws.hist0 + (int64_t)row * 256;
-    for (int i = threadIdx.x; i < kBins; i += kT)
+    uint32_t *g = hist + (int64_t)row * kSelBins;
+    for (int i = threadIdx.x; i < kSelBins; i += kHT)
         if (h[i]) atomicAdd(&g[i], h[i]);
-    // coarse histogram of the top 8 bits: thread i sums fine bins [16 i, 16 i + 16)
-    uint32_t s = 0;
-#pragma unroll
-    for (int e = 0; e < 16; ++e) s += h[16 * threadIdx.x + e];
-    if (s) atomicAdd(&g0[threadIdx.x], s);
 }
 
-// Threshold bin b1 from the coarse (256) and fine (4096) row histograms: one coarse
-// scan, then the 16 fine bins under the chosen coarse bin.
-__device__ BinPick pick_bin2(const uint32_t *g0, const uint32_t *g1, uint32_t need, uint32_t *s16,
-                             uint32_t *scratch) {
-    const int tid = threadIdx.x;
-    const uint32_t v = g0[255 - tid];  // thread tid owns coarse bin 255 - tid (top first)
-    uint32_t total;
-    const uint32_t ex = block_exscan(v, scratch, &total);
-    if (need == 0) return BinPick{0, kBins, 0};
-    if (total <= need) return BinPick{1, -1, total};
-    if (ex < need && need <= ex + v) {
-        scratch[4] = (uint32_t)(255 - tid);
-        scratch[5] = ex;
-    }
-    __syncthreads();
-    const int cb = (int)scratch[4];
-    const uint32_t above = scratch[5];
-    if (tid < 16) s16[tid] = g1[16 * cb + 15 - tid];  // fine bins of cb, top first
-    __syncthreads();
-    if (tid == 0) {
-        uint32_t acc = above;
-        for (int e = 0; e < 16; ++e) {
-            if (acc + s16[e] >= need) {
-                scratch[6] = (uint32_t)(16 * cb + 15 - e);
-                scratch[7] = acc;
-                break;
-            }
-            acc += s16[e];
-        }
-    }
-    __syncthreads();
-    BinPick r{2, (int)scratch[6], scratch[7]};
-    __syncthreads();
-    return r;
-}
-
-// ----------------------------------------------------------------------------- F2
-__global__ __launch_bounds__(kT) void select_filter_kernel(SelectArgs a, Ws ws, int part_cols) {
-    __shared__ int32_t sbuf[kCh];
-    __shared__ uint64_t lbuf[kCh];
-    __shared__ uint32_t h2[kBins];
-    __shared__ uint32_t cnt[4];
-    __shared__ uint32_t s16[16];
-    __shared__ uint32_t scratch[8];
-    const int row = blockIdx.y;
-    const int tid = threadIdx.x;
-    const int c0 = blockIdx.x * part_cols;
-    const int c1 = min(a.n_cols, c0 + part_cols);
-    const bool vec = (a.n_cols & 3) == 0;
-    const Row r = make_row(a, row);
-    uint32_t *ctr = ws.ctr + (int64_t)row * kCtr;
-    int32_t *gsure = ws.sure + (int64_t)row * ws.K;
-    uint64_t *glist = ws.list + (int64_t)row * ws.cap;
-    if (tid < 4) cnt[tid] = 0;
-    for (int i = tid; i < kBins; i += kT) h2[i] = 0;
-    // the first round's scores are loaded before the threshold pick (independent loads)
-    constexpr int PRE = kCh / (4 * kT);
-    float4 pre[PRE];
-    {
-        const int end = min(c1, c0 + kCh);
-#pragma unroll
-        for (int u = 0; u < PRE; ++u) {
-            const int col = c0 + 4 * (tid + u * kT);
-            if (vec && col + 3 < end) pre[u] = *reinterpret_cast<const float4 *>(r.sc + col);
-            else pre[u] = make_float4(kNegInf, kNegInf, kNegInf, kNegInf);
-        }
-    }
-    const BinPick bp = pick_bin2(ws.hist0 + (int64_t)row * 256, ws.hist1 + (int64_t)row * kBins,
-                                 (uint32_t)max(r.m, 0), s16, scratch);
-    if (blockIdx.x == 0 && tid == 0) {
-        ctr[C_MODE] = (uint32_t)bp.mode;
-        ctr[C_B1] = (uint32_t)bp.bin;
-        ctr[C_ABOVE] = bp.above;
-    }
-    if (bp.mode == 0) return;
-    const int b1 = bp.bin;
-    bool any_tie = false;
-    auto classify = [&](int col, float x) {
-        uint64_t comp;
-        if (candidate_x(a, r, col, x, comp)) {
-            const int d1 = (int)(comp >> 52);
-            if (bp.mode == 1 || d1 > b1) {
-                sbuf[atomicAdd(&cnt[0], 1u)] = comp_pos(comp);
-            } else if (d1 == b1) {
-                atomicAdd(&h2[(comp >> 40) & (kBins - 1)], 1u);
-                lbuf[atomicAdd(&cnt[1], 1u)] = comp;
-            }
-        }
-    };
-    auto classify4 = [&](int col, int end, bool have, float4 v) {
-        if (col >= end) return;
-        if (have && col + 3 < end) {
-            classify(col, v.x);
-            classify(col + 1, v.y);
-            classify(col + 2, v.z);
-            classify(col + 3, v.w);
-        } else {
-            for (int e = 0; e < 4 && col + e < end; ++e) classify(col + e, r.sc[col + e]);
-        }
-    };
-    auto flush = [&]() {
-        __syncthreads();
-        if (tid == 0) {
-            cnt[2] = cnt[0] ? atomicAdd(&ctr[C_NSURE], cnt[0]) : 0;
-            cnt[3] = cnt[1] ? atomicAdd(&ctr[C_NLIST], cnt[1]) : 0;
-        }
-        __syncthreads();
-        const uint32_t ns = cnt[0], nl = cnt[1], os = cnt[2], ol = cnt[3];
-        any_tie |= nl > 0;
-        for (uint32_t i = tid; i < ns; i += kT)
-            if (os + i < (uint32_t)ws.K) gsure[os + i] = sbuf[i];
-        for (uint32_t i = tid; i < nl; i += kT)
-            if (ol + i < (uint32_t)ws.cap) glist[ol + i] = lbuf[i];
-        __syncthreads();
-        if (tid < 2) cnt[tid] = 0;
-        __syncthreads();
-    };
-    {  // first round from the prefetched registers
-        const int end = min(c1, c0 + kCh);
-#pragma unroll
-        for (int u = 0; u < PRE; ++u) {
-            const int col = c0 + 4 * (tid + u * kT);
-            classify4(col, end, vec, pre[u]);
-        }
-        flush();
-    }
-    for (int base = c0 + kCh; base < c1; base += kCh) {
-        const int end = min(c1, base + kCh);
-        for (int col = base + 4 * tid; col < end; col += 4 * kT) {
-            const bool have = vec && col + 3 < end;
-            const float4 v = have ? *reinterpret_cast<const float4 *>(r.sc + col) : make_float4(0.f, 0.f, 0.f, 0.f);
-            classify4(col, end, have, v);
-        }
-        flush();
-    }
-    if (any_tie) {
-        uint32_t *g2 = ws.hist2 + (int64_t)row * kBins;
-        for (int i = tid; i < kBins; i += kT)
-            if (h2[i]) atomicAdd(&g2[i], h2[i]);
-    }
-}
-
-// ----------------------------------------------------------------------------- R resolve helpers
-
+// ----------------------------------------------------------------------------- radix
 struct ArrSrc {
     const uint64_t *p;
     int n;
@@ -394,7 +247,7 @@ struct RowSrc {
     const SelectArgs *a;
     const Row *r;
     __device__ int size() const { return a->n_cols; }
-    __device__ bool get(int i, uint64_t &c) const { return candidate(*a, *r, i, c); }
+    __device__ bool get(int i, uint64_t &c) const { return candidate_x(*a, *r, i, r->sc[i], c); }
 };
 
 // LDS histogram increment for digit d (-1: none) with same-digit lanes of the wave
@@ -409,31 +262,34 @@ __device__ __forceinline__ void wave_hist_add(uint32_t *h, int d) {
     }
 }
 
-__device__ __forceinline__ bool hi_match(uint64_t c, uint64_t pref, int bits) {
-    return bits >= 64 ? true : (c >> bits) == (pref >> bits);
-}
-
-// need-th largest composite of the source (1 <= need <= size), by 8-bit radix passes
-// from the top bit; returns the smallest composite that still belongs to the top
-// `need` (every element >= it is selected, exactly `need` of them).
+// need-th largest composite (1 <= need <= group size) of the group of source elements
+// whose bits at and above bit `lo_bits` equal those of pref; radix passes of up to 8
+// bits over the low lo_bits bits (0 < lo_bits < 64). Returns the smallest composite
+// that still belongs to the group's top `need`: those are exactly the group elements
+// >= it.
 template <class Src>
-__device__ uint64_t radix_kth(const Src &src, uint32_t need, uint32_t *h256, uint32_t *scratch) {
-    uint64_t pref = 0;
-    for (int sh = 56; sh >= 0; sh -= 8) {
-        for (int i = threadIdx.x; i < 256; i += kT) h256[i] = 0;
+__device__ uint64_t radix_kth(const Src &src, uint32_t need, uint64_t pref, int lo_bits, uint32_t *h256,
+                              uint32_t *scr) {
+    int hi = lo_bits;
+    pref = pref >> hi << hi;
+    while (hi > 0) {
+        const int w = hi < 8 ? hi : 8;
+        const int sh = hi - w;
+        const uint32_t dmask = (1u << w) - 1;
+        for (int i = threadIdx.x; i < 256; i += kRT) h256[i] = 0;
         __syncthreads();
         const int n = src.size();
-        const int nr = (n + kT - 1) / kT * kT;  // every lane takes part in the wave merge
-        for (int i = threadIdx.x; i < nr; i += kT) {
+        const int nr = (n + kRT - 1) / kRT * kRT;  // every lane takes part in the wave merge
+        for (int i = threadIdx.x; i < nr; i += kRT) {
             uint64_t c = 0;
-            const bool ok = i < n && src.get(i, c) && hi_match(c, pref, sh + 8);
-            wave_hist_add(h256, ok ? (int)((c >> sh) & 255) : -1);
+            const bool ok = i < n && src.get(i, c) && (c >> hi) == (pref >> hi);
+            wave_hist_add(h256, ok ? (int)((c >> sh) & dmask) : -1);
         }
         __syncthreads();
         if (threadIdx.x < 64) {
             const int lane = threadIdx.x;
-            const int hi = 255 - 4 * lane;  // lane owns 4 digits, scanned from the top
-            const uint32_t s = h256[hi] + h256[hi - 1] + h256[hi - 2] + h256[hi - 3];
+            const int top = 255 - 4 * lane;  // lane owns 4 digits, scanned from the top
+            const uint32_t s = h256[top] + h256[top - 1] + h256[top - 2] + h256[top - 3];
             uint32_t x = s;
 #pragma unroll
             for (int o = 1; o < 64; o <<= 1) {
@@ -444,11 +300,11 @@ __device__ uint64_t radix_kth(const Src &src, uint32_t need, uint32_t *h256, uin
             if (ex < need && need <= x) {
                 uint32_t acc = ex;
                 for (int e = 0; e < 4; ++e) {
-                    const uint32_t c = h256[hi - e];
+                    const uint32_t c = h256[top - e];
                     if (acc + c >= need) {
-                        scratch[0] = (uint32_t)(hi - e);
-                        scratch[1] = need - acc;
-                        scratch[2] = (c == need - acc);
+                        scr[0] = (uint32_t)(top - e);
+                        scr[1] = need - acc;
+                        scr[2] = (c == need - acc);
                         break;
                     }
                     acc += c;
@@ -456,241 +312,295 @@ __device__ uint64_t radix_kth(const Src &src, uint32_t need, uint32_t *h256, uin
             }
         }
         __syncthreads();
-        const uint32_t d = scratch[0];
-        need = scratch[1];
-        const bool whole = scratch[2] != 0;
+        const uint32_t d = scr[0];
+        need = scr[1];
+        const bool whole = scr[2] != 0;
         __syncthreads();
         pref |= (uint64_t)d << sh;
-        if (whole) return pref;  // lower bits zero: every element with this prefix
+        hi = sh;
+        if (whole) return pref;  // lower bits zero: every group element with this prefix
     }
     return pref;
 }
 
-// ----------------------------------------------------------------------------- R
-// Threshold inside bin b1 from the row's second-level histogram (LDS copy h): the bin b2
-// of the r1-th best tie candidate, and how many tie candidates lie above it.
-__device__ void pick_bin_lds(const uint32_t *h, uint32_t need, uint32_t *scratch, int &bin, uint32_t &above) {
-    const int tid = threadIdx.x;
-    const int hi_bin = kBins - 1 - 16 * tid;
-    uint32_t s = 0;
-#pragma unroll
-    for (int e = 0; e < 16; ++e) s += h[hi_bin - e];
-    uint32_t total;
-    const uint32_t ex = block_exscan(s, scratch, &total);
-    if (ex < need && need <= ex + s) {
-        uint32_t acc = ex;
-        for (int e = 0; e < 16; ++e) {
-            const uint32_t c = h[hi_bin - e];
-            if (acc + c >= need) {
-                scratch[4] = (uint32_t)(hi_bin - e);
-                scratch[5] = acc;
-                break;
-            }
-            acc += c;
-        }
+// ----------------------------------------------------------------------------- filter
+// grid (parts, rows); part_cols is a multiple of 32, so each workgroup owns whole words
+// of the row's column bitmap.
+__global__ __launch_bounds__(kHT) void select_filter_kernel(SelectArgs a, Ws w, int part_cols) {
+    __shared__ uint32_t wbits[kFC / 32];
+    __shared__ uint64_t tbuf[kFC];
+    __shared__ uint32_t tcbuf[kFC];
+    __shared__ uint32_t scr[24];
+    __shared__ uint32_t tcnt, tbase;
+    const int row = blockIdx.y;
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int c0 = blockIdx.x * part_cols;
+    const int c1 = min(a.n_cols, c0 + part_cols);
+    const Row r = make_row(a, row);
+    const uint32_t m = (uint32_t)max(r.m, 0);
+
+    // first round's scores are requested before the histogram (independent loads)
+    auto load4 = [&](int col, int end) -> float4 {
+        if (a.vec && col + 3 < end) return *reinterpret_cast<const float4 *>(r.sc + col);
+        float4 v;
+        v.x = col < end ? r.sc[col] : kNegInf;
+        v.y = col + 1 < end ? r.sc[col + 1] : kNegInf;
+        v.z = col + 2 < end ? r.sc[col + 2] : kNegInf;
+        v.w = col + 3 < end ? r.sc[col + 3] : kNegInf;
+        return v;
+    };
+    float4 va, vb;
+    {
+        const int end = min(c1, c0 + kFC);
+        va = load4(c0 + 4 * tid, end);
+        vb = load4(c0 + kFC / 2 + 4 * tid, end);
     }
-    __syncthreads();
-    bin = (int)scratch[4];
-    above = scratch[5];
-    __syncthreads();
+    uint32_t hv[kSelBins / kHT];  // thread t: bins from the top, 8 per thread
+    {
+        const uint32_t *g = w.hist + (int64_t)row * kSelBins + kSelBins - kSelBins / kHT * (tid + 1);
+        const uint4 lo = *reinterpret_cast<const uint4 *>(g), hi = *reinterpret_cast<const uint4 *>(g + 4);
+        hv[0] = hi.w, hv[1] = hi.z, hv[2] = hi.y, hv[3] = hi.x, hv[4] = lo.w, hv[5] = lo.z, hv[6] = lo.y, hv[7] = lo.x;
+    }
+    const BinPick bp = pick_bin<kHT, kSelBins / kHT>(hv, m, scr);
+    if (bp.mode == 0) return;
+    const int b1 = bp.bin;
+    uint32_t *gctr = w.ctr + (int64_t)row * kCtr;
+    uint64_t *gties = w.ties + (int64_t)row * w.cap;
+    uint32_t *gtcols = w.tcols ? w.tcols + (int64_t)row * w.cap : nullptr;
+    uint32_t *gbits = w.bits + (int64_t)row * w.words;
+
+    for (int base = c0; base < c1; base += kFC) {
+        const int end = min(c1, base + kFC);
+        if (tid < kFC / 32) wbits[tid] = 0;
+        if (tid == 0) tcnt = 0;
+        __syncthreads();
+        if (base != c0) {
+            va = load4(base + 4 * tid, end);
+            vb = load4(base + kFC / 2 + 4 * tid, end);
+        }
+        // one element per lane, every lane of the wave present (the tie append is merged per wave)
+        auto classify = [&](int col, float x) {
+            uint64_t comp = 0;
+            const bool cand = col < end && candidate_x(a, r, col, x, comp);
+            const int d1 = (int)(comp >> kB1Shift);
+            if (cand && (bp.mode == 1 || d1 > b1)) atomicOr(&wbits[(col - base) >> 5], 1u << (col & 31));
+            const bool tie = cand && bp.mode == 2 && d1 == b1;
+            const uint64_t bal = __ballot(tie);
+            if (bal) {
+                uint32_t sb = 0;
+                if (lane == 0) sb = atomicAdd(&tcnt, (uint32_t)__popcll(bal));
+                sb = __builtin_amdgcn_readfirstlane(sb);
+                if (tie) {
+                    const uint32_t slot = sb + lane_rank(bal);
+                    tbuf[slot] = comp;
+                    tcbuf[slot] = (uint32_t)col;
+                }
+            }
+        };
+        const int ca = base + 4 * tid, cb = base + kFC / 2 + 4 * tid;
+        classify(ca, va.x);
+        classify(ca + 1, va.y);
+        classify(ca + 2, va.z);
+        classify(ca + 3, va.w);
+        classify(cb, vb.x);
+        classify(cb + 1, vb.y);
+        classify(cb + 2, vb.z);
+        classify(cb + 3, vb.w);
+        __syncthreads();
+        const int nw = (end - base + 31) >> 5;
+        if (tid < nw) gbits[(base >> 5) + tid] = wbits[tid];
+        const uint32_t nt = tcnt;
+        if (nt) {
+            if (tid == 0) tbase = atomicAdd(&gctr[0], nt);
+            __syncthreads();
+            const uint32_t tb = tbase;
+            for (uint32_t i = tid; i < nt; i += kHT) {
+                if (tb + i < (uint32_t)w.cap) {
+                    gties[tb + i] = tbuf[i];
+                    if (gtcols) gtcols[tb + i] = tcbuf[i];
+                }
+            }
+        }
+        __syncthreads();  // LDS buffers are reused by the next round
+    }
 }
 
-template <int KPAD>
-__global__ __launch_bounds__(kT) void select_resolve_kernel(SelectArgs a, Ws ws, int bitmap_words) {
+// ----------------------------------------------------------------------------- resolve
+// One workgroup per row. KEPT: columns map to positions through the kept map, so the
+// chosen positions are sorted (bitonic, KPAD entries) before they are written.
+template <bool KEPT, int KPAD>
+__global__ __launch_bounds__(kRT) void select_resolve_kernel(SelectArgs a, Ws w) {
     extern __shared__ __attribute__((aligned(16))) unsigned char dyn[];
-    uint64_t *lst = reinterpret_cast<uint64_t *>(dyn);               // tie list [kLcap]
-    uint32_t *area = reinterpret_cast<uint32_t *>(dyn + kLcap * 8);  // bitmap or sort buffer
-    __shared__ uint32_t h[kBins];
-    __shared__ uint32_t cnt[4];
+    uint64_t *ties = reinterpret_cast<uint64_t *>(dyn);                        // [cap]
+    uint32_t *tcols = reinterpret_cast<uint32_t *>(dyn + (size_t)w.cap * 8);  // [cap] (KEPT)
+    __shared__ __attribute__((aligned(16))) uint32_t h[kB2];  // second-level histogram, then the final group
     __shared__ uint32_t h256[256];
-    __shared__ uint32_t scratch[8];
-    __shared__ uint64_t tiny[256];
-    __shared__ int32_t sure_l[KPAD];
+    __shared__ uint32_t scr[32];
+    __shared__ uint32_t cnt[4];
+    __shared__ int32_t fill[KEPT ? KPAD : 1];
     const int row = blockIdx.x;
     const int tid = threadIdx.x;
     const Row r = make_row(a, row);
-    uint32_t *ctr = ws.ctr + (int64_t)row * kCtr;
-    const uint64_t *glist = ws.list + (int64_t)row * ws.cap;
-    const int32_t *gsure = ws.sure + (int64_t)row * ws.K;
-    uint32_t *g2 = ws.hist2 + (int64_t)row * kBins;
-    const int mode = (int)ctr[C_MODE];
-    const int b1 = (int)ctr[C_B1];
-    const uint32_t n_sure = mode == 0 ? 0u : min(ctr[C_NSURE], (uint32_t)ws.K);
-    const uint32_t n_list = mode == 2 ? ctr[C_NLIST] : 0u;
-    const uint32_t need1 = mode == 2 ? (uint32_t)max(r.m, 0) - ctr[C_ABOVE] : 0u;  // wanted from bin b1
-    const bool in_lds = n_list <= (uint32_t)kLcap;
-    const bool in_glb = n_list <= (uint32_t)ws.cap;
-    // issue every independent load first: second-level histogram, tie list, sure list
-    {
-        uint32_t hv[kBins / kT];
-#pragma unroll
-        for (int u = 0; u < kBins / kT; ++u) hv[u] = mode == 2 ? g2[tid + u * kT] : 0u;
-        constexpr int U = kLcap / kT;
-        uint64_t lv[U];
-#pragma unroll
-        for (int u = 0; u < U; ++u) {
-            const uint32_t i = tid + u * kT;
-            lv[u] = (in_lds && i < n_list) ? __builtin_nontemporal_load(&glist[i]) : 0;
-        }
-        constexpr int US = KPAD / kT;
-        int32_t sv[US];
-#pragma unroll
-        for (int u = 0; u < US; ++u) {
-            const uint32_t i = tid + u * kT;
-            sv[u] = i < n_sure ? gsure[i] : 0;
-        }
-#pragma unroll
-        for (int u = 0; u < kBins / kT; ++u) h[tid + u * kT] = hv[u];
-#pragma unroll
-        for (int u = 0; u < U; ++u) lst[tid + u * kT] = lv[u];
-#pragma unroll
-        for (int u = 0; u < US; ++u) sure_l[tid + u * kT] = sv[u];
+    const uint32_t m = (uint32_t)max(r.m, 0);
+    uint32_t *g1 = w.hist + (int64_t)row * kSelBins;
+    uint32_t *gctr = w.ctr + (int64_t)row * kCtr;
+    const uint64_t *gties = w.ties + (int64_t)row * w.cap;
+    const uint32_t *gtcols = KEPT ? w.tcols + (int64_t)row * w.cap : nullptr;
+    uint32_t *gbits = w.bits + (int64_t)row * w.words;
+
+    // ---- histogram (2 bins per thread from the top), tie count, the first tie entries;
+    // the histogram and the counters are left at zero
+    uint32_t hv[2];
+    hv[0] = g1[kSelBins - 1 - 2 * tid];
+    hv[1] = g1[kSelBins - 2 - 2 * tid];
+    const uint32_t ntie = gctr[0];
+    uint64_t t0 = 0, t1 = 0;
+    uint32_t tc0 = 0, tc1 = 0;
+    if (tid < w.cap) t0 = gties[tid];
+    if (tid + kRT < w.cap) t1 = gties[tid + kRT];
+    if (KEPT) {
+        if (tid < w.cap) tc0 = gtcols[tid];
+        if (tid + kRT < w.cap) tc1 = gtcols[tid + kRT];
     }
-    if (tid == 0) cnt[0] = 0;
-    __syncthreads();
-    // ---- threshold composite thr: the chosen tie candidates are those with comp >= thr
-    uint64_t thr = 0;
-    bool from_row = false;  // exact select over the whole row (large tie groups, overflowed list)
-    if (mode == 2) {
-        int b2;
-        uint32_t above2;
-        pick_bin_lds(h, need1, scratch, b2, above2);
-        const uint32_t need2 = need1 - above2;                    // wanted from (b1, b2)
-        const uint64_t p24 = ((uint64_t)b1 << 52) | ((uint64_t)b2 << 40);
-        const uint32_t n2 = h[b2];
-        if (need2 == n2) {
-            thr = p24;              // the whole (b1, b2) group
-            from_row = !in_glb;     // list incomplete: enumerate comp >= thr from the row
-        } else if (n2 <= 256 && in_glb) {
-            // the few (b1, b2) elements into LDS, then exact radix select on their composites
-            auto gather = [&](uint64_t c) {
-                if ((c >> 40) == (p24 >> 40)) {
-                    const uint32_t slot = atomicAdd(&cnt[0], 1u);
-                    if (slot < 256u) tiny[slot] = c;
-                }
-            };
-            if (in_lds) {
-                for (uint32_t i = tid; i < n_list; i += kT) gather(lst[i]);
-            } else {
-                for (uint32_t i = tid; i < n_list; i += kT) gather(glist[i]);
+    const BinPick bp = pick_bin<kRT, 2>(hv, m, scr);  // its barriers follow every thread's reads
+    g1[kSelBins - 1 - 2 * tid] = 0;
+    g1[kSelBins - 2 - 2 * tid] = 0;
+    if (tid < kCtr) gctr[tid] = 0;
+    const int b1 = bp.bin;
+
+    auto mark = [&](int col) { atomicOr(&gbits[col >> 5], 1u << (col & 31)); };
+    if (bp.mode == 2) {
+        const bool overflow = ntie > (uint32_t)w.cap;
+        const uint32_t nl = min(ntie, (uint32_t)w.cap);
+        const uint32_t need1 = m > bp.above ? m - bp.above : 0u;
+        uint64_t thr = ~(uint64_t)0;
+        if (!overflow) {
+            if ((uint32_t)tid < nl) ties[tid] = t0;
+            if ((uint32_t)tid + kRT < nl) ties[tid + kRT] = t1;
+            for (uint32_t i = tid + 2 * kRT; i < nl; i += kRT) ties[i] = gties[i];
+            if (KEPT) {
+                if ((uint32_t)tid < nl) tcols[tid] = tc0;
+                if ((uint32_t)tid + kRT < nl) tcols[tid + kRT] = tc1;
+                for (uint32_t i = tid + 2 * kRT; i < nl; i += kRT) tcols[i] = gtcols[i];
             }
+            for (int i = tid; i < kB2; i += kRT) h[i] = 0;
+            if (tid < 4) cnt[tid] = 0;
             __syncthreads();
-            // rank of each gathered composite (composites are unique): the need2-th largest
-            // is the one with exactly need2 - 1 larger elements
-            const uint32_t nt = min(cnt[0], 256u);
-            if ((uint32_t)tid < nt) {
-                const uint64_t c = tiny[tid];
-                uint32_t rank = 0;
-                for (uint32_t j = 0; j < nt; ++j) rank += tiny[j] > c;
-                if (rank == need2 - 1) {
-                    scratch[0] = (uint32_t)c;
-                    scratch[1] = (uint32_t)(c >> 32);
+            for (uint32_t i = tid; i < nl; i += kRT)
+                atomicAdd(&h[((uint32_t)(ties[i] >> 32) >> kL2Shift) & (kB2 - 1)], 1u);
+            __syncthreads();
+            uint32_t v2[4];
+#pragma unroll
+            for (int e = 0; e < 4; ++e) v2[e] = h[kB2 - 1 - 4 * tid - e];
+            const BinPick p2 = pick_bin<kRT, 4>(v2, need1, scr);
+            if (p2.mode == 1) {
+                thr = 0;  // every tie
+            } else if (p2.mode == 2) {
+                const int b2 = p2.bin;
+                const uint32_t n2 = h[b2];
+                const uint32_t need2 = need1 - p2.above;  // wanted from the (b1, b2) group
+                const uint64_t pre = (uint64_t)(((uint32_t)b1 << kSelShift) | ((uint32_t)b2 << kL2Shift)) << 32;
+                __syncthreads();  // h is reused below
+                if (need2 == n2) {
+                    thr = pre;  // the whole group
+                } else if (n2 <= (uint32_t)kTiny) {
+                    uint64_t *tiny = reinterpret_cast<uint64_t *>(h);
+                    for (uint32_t i = tid; i < nl; i += kRT) {
+                        const uint64_t c = ties[i];
+                        if ((c >> kGrpShift) == (pre >> kGrpShift)) {
+                            const uint32_t slot = atomicAdd(&cnt[2], 1u);
+                            if (slot < (uint32_t)kTiny) tiny[slot] = c;
+                        }
+                    }
+                    __syncthreads();
+                    const uint32_t nt = min(cnt[2], (uint32_t)kTiny);
+                    if ((uint32_t)tid < nt) {
+                        const uint64_t c = tiny[tid];
+                        uint32_t rank = 0;  // composites are unique
+                        for (uint32_t j = 0; j < nt; ++j) rank += tiny[j] > c;
+                        if (rank == need2 - 1) {
+                            scr[20] = (uint32_t)c;
+                            scr[21] = (uint32_t)(c >> 32);
+                        }
+                    }
+                    __syncthreads();
+                    thr = ((uint64_t)scr[21] << 32) | scr[20];
+                } else {
+                    thr = radix_kth(ArrSrc{ties, (int)nl}, need2, pre, kGrpShift, h256, scr);
                 }
             }
-            __syncthreads();
-            thr = ((uint64_t)scratch[1] << 32) | scratch[0];
+            for (uint32_t i = tid; i < nl; i += kRT)
+                if (ties[i] >= thr) mark(KEPT ? (int)tcols[i] : comp_pos(ties[i]));
         } else {
-            // many equal keys or an overflowed list: exact select over the whole row
-            const RowSrc rsrc{&a, &r};
-            thr = radix_kth(rsrc, (uint32_t)max(r.m, 0), h256, scratch);
-            from_row = true;
-        }
-    }
-    int32_t *dst = a.idx + (int64_t)row * a.K;
-    // chosen fill positions: the sure list plus the tie candidates with comp >= thr, or,
-    // when the row had to be scanned, every candidate with comp >= thr
-    auto for_chosen = [&](auto &&fn) {
-        if (mode == 0) return;
-        if (from_row) {
-            for (int i = tid; i < a.n_cols; i += kT) {
+            // the tie list overflowed: exact select inside bin b1 over the whole row
+            const RowSrc rs{&a, &r};
+            const uint64_t pre = (uint64_t)b1 << kB1Shift;
+            thr = radix_kth(rs, need1, pre, kB1Shift, h256, scr);
+            for (int col = tid; col < a.n_cols; col += kRT) {
                 uint64_t c;
-                if (candidate(a, r, i, c) && c >= thr) fn(comp_pos(c));
-            }
-            return;
-        }
-        for (uint32_t i = tid; i < n_sure; i += kT) fn(sure_l[i]);
-        if (mode != 2) return;
-        if (in_lds) {
-            for (uint32_t i = tid; i < n_list; i += kT)
-                if (lst[i] >= thr) fn(comp_pos(lst[i]));
-        } else {
-            for (uint32_t i = tid; i < n_list; i += kT) {
-                const uint64_t c = glist[i];
-                if (c >= thr) fn(comp_pos(c));
+                if (candidate_x(a, r, col, r.sc[col], c) && (c >> kB1Shift) == (uint64_t)b1 && c >= thr) mark(col);
             }
         }
-    };
-    // ---- ascending output: sink [0, f_sink_end), then the fill (all strictly between
-    // sink and window), then the window [f_win_lo, p]
-    if (bitmap_words > 0) {
-        for (int i = tid; i < bitmap_words; i += kT) area[i] = 0;
-        __syncthreads();
-        for_chosen([&](int pos) { atomicOr(&area[pos >> 5], 1u << (pos & 31)); });
-        __syncthreads();
-        const int per = (bitmap_words + kT - 1) / kT;
-        const int w0 = min(bitmap_words, tid * per), w1 = min(bitmap_words, w0 + per);
+    }
+    __syncthreads();
+
+    // ---- ascending output: sink [0, f_sink_end), the fill (strictly between sink and
+    // window), the window [f_win_lo, p], then -1
+    int32_t *dst = a.idx + (int64_t)row * a.K;
+    const int nsink = a.causal ? r.f_sink_end : 0;
+    const int nwin = a.causal ? max(0, r.p - r.f_win_lo + 1) : 0;
+    uint32_t nfill = 0;
+    if (bp.mode != 0) {
+        const int per = (w.words + kRT - 1) / kRT;
+        const int w0 = min(w.words, tid * per), w1 = min(w.words, w0 + per);
         uint32_t c = 0;
-        for (int i = w0; i < w1; ++i) c += __popc(area[i]);
-        uint32_t nfill;
-        const int nsink = a.causal ? r.f_sink_end : 0;
-        const int nwin = a.causal ? max(0, r.p - r.f_win_lo + 1) : 0;
-        uint32_t off = nsink + block_exscan(c, scratch, &nfill);
+        for (int i = w0; i < w1; ++i) c += __popc(__hip_atomic_load(&gbits[i], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT));
+        uint32_t off = block_exscan<kRT>(c, scr, &nfill);
         for (int i = w0; i < w1; ++i) {
-            uint32_t bits = area[i];
+            uint32_t bits = __hip_atomic_load(&gbits[i], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
             while (bits) {
-                const int bpos = __ffs(bits) - 1;
+                const int col = i * 32 + __ffs(bits) - 1;
                 bits &= bits - 1;
-                if (off < (uint32_t)a.K) dst[off] = i * 32 + bpos;
+                if constexpr (KEPT) {
+                    const int blk = col / a.block_size;
+                    if (off < (uint32_t)KPAD) fill[off] = r.kept[blk] * a.block_size + (col - blk * a.block_size);
+                } else {
+                    if (nsink + off < (uint32_t)a.K) dst[nsink + off] = col;
+                }
                 ++off;
             }
         }
-        for (int s2 = tid; s2 < nsink; s2 += kT) dst[s2] = s2;
-        const int wbase = nsink + (int)nfill;
-        for (int j = tid; j < nwin; j += kT)
-            if (wbase + j < a.K) dst[wbase + j] = r.f_win_lo + j;
-        for (int i = wbase + nwin + tid; i < a.K; i += kT) dst[i] = -1;
-    } else {
-        int32_t *out = reinterpret_cast<int32_t *>(area);
-        for (int i = tid; i < KPAD; i += kT) out[i] = 0x7FFFFFFF;
-        if (tid == 0) cnt[2] = 0;
-        __syncthreads();
-        auto emit = [&](int pos) {
-            const uint32_t slot = atomicAdd(&cnt[2], 1u);
-            if (slot < (uint32_t)KPAD) out[slot] = pos;
-        };
-        if (a.causal) {
-            for (int s = tid; s < r.f_sink_end; s += kT) emit(s);
-            for (int s = r.f_win_lo + tid; s <= r.p; s += kT) emit(s);
-        }
-        for_chosen(emit);
-        __syncthreads();
-        const uint32_t count = min(cnt[2], (uint32_t)KPAD);
-        for (int k = 2; k <= KPAD; k <<= 1) {
-            for (int j = k >> 1; j > 0; j >>= 1) {
-                for (int i = tid; i < KPAD; i += kT) {
-                    const int ixj = i ^ j;
-                    if (ixj > i) {
-                        const int x = out[i], y = out[ixj];
-                        const bool up = (i & k) == 0;
-                        if ((x > y) == up) {
-                            out[i] = y;
-                            out[ixj] = x;
+        if constexpr (KEPT) {
+            nfill = min(nfill, (uint32_t)KPAD);
+            __syncthreads();
+            for (int i = tid; i < KPAD; i += kRT)
+                if ((uint32_t)i >= nfill) fill[i] = 0x7FFFFFFF;
+            __syncthreads();
+            for (int k = 2; k <= KPAD; k <<= 1) {
+                for (int j = k >> 1; j > 0; j >>= 1) {
+                    for (int i = tid; i < KPAD; i += kRT) {
+                        const int ixj = i ^ j;
+                        if (ixj > i) {
+                            const int x = fill[i], y = fill[ixj];
+                            const bool up = (i & k) == 0;
+                            if ((x > y) == up) {
+                                fill[i] = y;
+                                fill[ixj] = x;
+                            }
                         }
                     }
+                    __syncthreads();
                 }
-                __syncthreads();
             }
+            for (uint32_t i = tid; i < nfill; i += kRT)
+                if (nsink + i < (uint32_t)a.K) dst[nsink + i] = fill[i];
         }
-        for (int i = tid; i < a.K; i += kT) dst[i] = (uint32_t)i < count ? out[i] : -1;
     }
-    // ---- leave the row's histograms and counters at zero for the next call
-    uint32_t *g = ws.hist1 + (int64_t)row * kBins;
-    for (int i = tid; i < kBins; i += kT) {
-        g[i] = 0;
-        g2[i] = 0;
-    }
-    ws.hist0[(int64_t)row * 256 + tid] = 0;
-    if (tid < kCtr) ctr[tid] = 0;
+    for (int s = tid; s < nsink; s += kRT) dst[s] = s;
+    const int wbase = nsink + (int)nfill;
+    for (int j = tid; j < nwin; j += kRT)
+        if (wbase + j < a.K) dst[wbase + j] = r.f_win_lo + j;
+    for (int i = wbase + nwin + tid; i < a.K; i += kRT) dst[i] = -1;
 }
 
 __global__ void clear_kernel(uint4 *p, size_t n16, uint8_t *tail, size_t ntail) {
@@ -700,46 +610,66 @@ __global__ void clear_kernel(uint4 *p, size_t n16, uint8_t *tail, size_t ntail) 
     if (i < ntail) tail[i] = 0;
 }
 
-template <int KPAD>
-hipError_t launch_resolve(const SelectArgs &a, const Ws &w, int rows, hipStream_t s) {
-    const int64_t npos = (a.causal || a.kept) ? (int64_t)a.N : (int64_t)a.n_cols;  // positions bound
-    const int words = npos <= kBitmapMax ? (int)((npos + 31) / 32) : 0;
-    const size_t area = words ? (size_t)words * 4 : (size_t)KPAD * 4;
-    const size_t lds = (size_t)kLcap * 8 + area;
-    hipLaunchKernelGGL((select_resolve_kernel<KPAD>), dim3(rows), dim3(kT), lds, s, a, w, words);
+template <bool KEPT, int KPAD>
+hipError_t launch_resolve_t(const SelectArgs &a, const Ws &w, hipStream_t s) {
+    const size_t lds = (size_t)w.cap * (KEPT ? 12 : 8);
+    hipLaunchKernelGGL((select_resolve_kernel<KEPT, KPAD>), dim3(a.B * a.T), dim3(kRT), lds, s, a, w);
     return hipGetLastError();
+}
+
+hipError_t launch_resolve(const SelectArgs &a, const Ws &w, hipStream_t s) {
+    if (!a.kept) return launch_resolve_t<false, 1>(a, w, s);
+    if (a.K <= 1024) return launch_resolve_t<true, 1024>(a, w, s);
+    if (a.K <= 2048) return launch_resolve_t<true, 2048>(a, w, s);
+    return launch_resolve_t<true, 4096>(a, w, s);
+}
+
+// Columns per filter (and histogram) workgroup: about 1024 workgroups in all, at least
+// 2048 columns each, a multiple of 32.
+int part_columns(int rows, int n_cols, int &parts) {
+    int p = (1024 + rows - 1) / rows;
+    const int max_parts = (n_cols + 2047) / 2048;
+    if (p > max_parts) p = max_parts;
+    if (p < 1) p = 1;
+    int pc = (n_cols + p - 1) / p;
+    pc = (pc + 31) / 32 * 32;
+    parts = (n_cols + pc - 1) / pc;
+    return pc;
 }
 
 }  // namespace
 
-size_t select_workspace_bytes(const SelectArgs &a) { return ws_bytes(a.B * a.T, a.K, a.n_cols); }
+size_t select_workspace_bytes(int rows, int n_cols, bool kept) { return ws_total(rows, n_cols, kept); }
+
+size_t select_zero_bytes(int rows) { return zero_bytes(rows); }
+
+hipError_t launch_select_hist(const SelectArgs &a, void *wsp, hipStream_t s) {
+    const int rows = a.B * a.T;
+    if (!a.ws_clean) {
+        const hipError_t e = launch_clear(wsp, zero_bytes(rows), s);
+        if (e != hipSuccess) return e;
+    }
+    int parts;
+    const int pc = part_columns(rows, a.n_cols, parts);
+    const Ws w = carve(wsp, rows, a.n_cols, a.kept != nullptr);
+    hipLaunchKernelGGL(select_hist_kernel, dim3(parts, rows), dim3(kHT), 0, s, a, w.hist, pc);
+    return hipGetLastError();
+}
 
 hipError_t launch_select(const SelectArgs &a, void *wsp, hipStream_t s) {
     const int rows = a.B * a.T;
-    Ws w = carve(wsp, rows, a.K, a.n_cols);
     hipError_t e;
-    if (!a.ws_clean) {
-        e = launch_clear(wsp, zero_region_bytes(rows), s);
+    if (!a.primed) {
+        e = launch_select_hist(a, wsp, s);
         if (e != hipSuccess) return e;
     }
-    int parts = (1024 + rows - 1) / rows;
-    const int max_parts = (a.n_cols + 2047) / 2048;
-    if (parts > max_parts) parts = max_parts;
-    if (parts < 1) parts = 1;
-    int part_cols = (a.n_cols + parts - 1) / parts;
-    part_cols = (part_cols + 3) / 4 * 4;
-    parts = (a.n_cols + part_cols - 1) / part_cols;
-    dim3 grid(parts, rows);
-    hipLaunchKernelGGL(select_hist_kernel, grid, dim3(kT), 0, s, a, w, part_cols);
+    const Ws w = carve(wsp, rows, a.n_cols, a.kept != nullptr);
+    int parts;
+    const int pc = part_columns(rows, a.n_cols, parts);
+    hipLaunchKernelGGL(select_filter_kernel, dim3(parts, rows), dim3(kHT), 0, s, a, w, pc);
     e = hipGetLastError();
     if (e != hipSuccess) return e;
-    hipLaunchKernelGGL(select_filter_kernel, grid, dim3(kT), 0, s, a, w, part_cols);
-    e = hipGetLastError();
-    if (e != hipSuccess) return e;
-    if (a.K <= 512) return launch_resolve<512>(a, w, rows, s);
-    if (a.K <= 1024) return launch_resolve<1024>(a, w, rows, s);
-    if (a.K <= 2048) return launch_resolve<2048>(a, w, rows, s);
-    return launch_resolve<4096>(a, w, rows, s);
+    return launch_resolve(a, w, s);
 }
 
 hipError_t launch_clear(void *p, size_t bytes, hipStream_t s) {

@@ -107,6 +107,17 @@ def test_index_argument_errors(kw, code):
     assert L.lib().lsa_last_error()
 
 
+@pytest.mark.parametrize("kw,code", [
+    (dict(select_ws=FAKE + 16, select_ws_bytes=1 << 30), -5),
+    (dict(select_ws=FAKE, select_ws_bytes=100), -7),
+    (dict(select_ws=FAKE, select_ws_bytes=1 << 30, select_ws_state=2), -2),
+    (dict(select_ws=FAKE, select_ws_bytes=1 << 30, sink=-1), -2),
+    (dict(select_ws=FAKE, select_ws_bytes=1 << 30, kept=FAKE, n_keep=16, block_size=64, window=32), -6),
+])
+def test_index_priming_errors(kw, code):
+    assert _idx(_index_desc(**kw)) == code
+
+
 def test_index_null_desc():
     assert L.lib().lsa_index(None, None) == -1
 
@@ -119,6 +130,11 @@ def test_index_null_desc():
 ])
 def test_select_argument_errors(kw, code):
     assert _sel(_select_desc(**kw)) == code
+
+
+def test_select_workspace_state_errors():
+    assert _sel(_select_desc(workspace_state=3)) == -2
+    assert _sel(_select_desc(workspace_state=L.LSA_WS_PRIMED, causal=0, sink=0, window=0)) == -2
 
 
 def test_select_workspace_and_pointer_errors():
