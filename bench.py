@@ -11,8 +11,9 @@ B=8 sequences, N=131072 cached tokens each, one query token, indexer 64 heads x 
 Inputs are synthetic (seeded, see synth/) and resident in HBM before timing starts.
 R input replicas (default 4, 5.4 GB) are rotated step by step so that every step
 reads cold data (the 256 MB MALL cannot hold them). The headline runs the step as a
-captured HIP graph (one graph per replica); the plain stream-launch rate is reported
-beside it. Prints one JSON line.
+captured HIP graph (one graph per replica) and as plain stream launches; the headline
+is the faster of the two (named in config.launch), both rates are reported. Prints one
+JSON line.
 """
 from __future__ import annotations
 
@@ -225,7 +226,9 @@ def main():
         torch.cuda.synchronize()
         ms_graph = timed(lambda r: graphs[r].replay(), args.steps, args.warmup)
 
-    ms = ms_graph if ms_graph is not None else ms_plain
+    # headline: the faster of the two ways of launching the same step (both are reported)
+    use_graph = ms_graph is not None and ms_graph < ms_plain
+    ms = ms_graph if use_graph else ms_plain
     idx_b, gat_b, small_b = algorithmic_bytes(cfg)
     step_bytes = idx_b + gat_b + small_b
     achieved_index = idx_b / (ms_index * 1e-3) / 1e9
@@ -246,7 +249,7 @@ def main():
         "config": {"workload": "c2 LSA decode: B=8, 128K context, T=1, indexer 64x128 fp8-e4m3 + fp32 scale, "
                                "MLA 64 heads 576/512 bf16, K=2048 (sink 64, window 512)",
                    "batch": B, "context": N, "query_tokens": T, "topk": cfg.K,
-                   "launch": "hip graph replay" if ms_graph is not None else "stream launches",
+                   "launch": "hip graph replay" if use_graph else "stream launches",
                    "input_replicas": R},
         "roofline": {"bound": "hbm", "kernel": "index_tokens_kernel (lsa_index, fp8 keys)",
                      "achieved": achieved_index, "peak": PEAK_HBM_GBS, "unit": "GB/s",

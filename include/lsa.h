@@ -220,11 +220,12 @@ int32_t lsa_select(const lsa_select_desc *desc, void *workspace, size_t workspac
  * q bf16 [n_layers][B][T][Hq][d_qk] (layer stride layer_stride_q); out [n_layers][B][T]
  * [Hq][d_v] (layer_stride_out); lse fp32 [n_layers][B][T][Hq] (layer_stride_lse) or NULL.
  * n_splits: how many parts the K rows of one query are split into (0 = library
- * choice); partial results are merged in a fixed order.
+ * choice; clamped to [ceil(K/2048), min(ceil(K/32), 128)]); partial results are merged
+ * in a fixed order.
  * Workspace: lsa_attend_workspace_bytes(desc) bytes (may be 0), 256-byte aligned;
  * no initial contents needed.
  * Supported: (d_qk, d_v) in {(128,128), (576,512)}, Hq % Hkv == 0, Hq/Hkv <= 64,
- * K >= 1, strides multiples of 8 elements.
+ * 1 <= K <= 262144, strides multiples of 8 elements.
  */
 typedef struct lsa_attend_desc {
     int32_t B, T, N;

@@ -321,8 +321,11 @@ static int32_t attend_check(const lsa_attend_desc *d, lsa::AttendArgs &a) {
     a.n_splits = 1;
     int sp = d->n_splits > 0 ? d->n_splits : lsa::attend_default_splits(a);
     const int smin = (d->K + 2047) / 2048;
+    if (smin > lsa::kAttendMaxSplits)
+        return fail(LSA_E_UNSUPPORTED, "lsa_attend: K=%d above %d", d->K, 2048 * lsa::kAttendMaxSplits);
     if (sp < smin) sp = smin;
     if (sp > (d->K + 31) / 32) sp = (d->K + 31) / 32;
+    if (sp > lsa::kAttendMaxSplits) sp = lsa::kAttendMaxSplits;
     a.n_splits = sp;
     return LSA_OK;
 }

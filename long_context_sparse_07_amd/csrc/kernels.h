@@ -89,6 +89,7 @@ struct AttendArgs {
     int64_t lsq, lsk, lsv, lso, lsl;
     int n_splits;           // resolved (>= 1)
 };
+constexpr int kAttendMaxSplits = 128;  // split partials merged by one combine workgroup
 int attend_default_splits(const AttendArgs &a);
 size_t attend_workspace_bytes(const AttendArgs &a);
 bool attend_supported(int d_qk, int d_v, int g);

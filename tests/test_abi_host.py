@@ -156,6 +156,7 @@ def test_select_workspace_and_pointer_errors():
     (dict(d_qk=64, d_v=64), -6), (dict(Hq=48), -6), (dict(out_dtype=5), -3),
     (dict(k_stride_n=577, v_stride_n=577), -5), (dict(v=FAKE + 256), -6),
     (dict(q=FAKE + 8), -5), (dict(n_layers=0), -2), (dict(n_splits=-1), -2),
+    (dict(K=2048 * 128 + 1), -6),
 ])
 def test_attend_argument_errors(kw, code):
     assert _att(_attend_desc(**kw)) == code
@@ -164,7 +165,8 @@ def test_attend_argument_errors(kw, code):
 def test_attend_workspace_rules():
     d = _attend_desc(n_splits=4)
     need = L.lib().lsa_attend_workspace_bytes(ctypes.byref(d))
-    assert need == 2 * 4 * 64 * (512 + 2) * 4
+    # bf16 partial rows (256-byte aligned), then fp32 (m, l) per head and split
+    assert need == 2 * 4 * 64 * 512 * 2 + 2 * 4 * 64 * 2 * 4
     assert _att(d, FAKE, need - 4) == -7
     assert _att(d, None, 0) == -7
     one = _attend_desc(n_splits=1)
