@@ -37,15 +37,21 @@ constexpr int kB2 = 4096;            // second-level bins: the next 12 key bits
 constexpr int kL2Shift = kSelShift - 12;
 constexpr int kGrpShift = 32 + kL2Shift;  // composite bits above it: the 23 key bits of (b1, b2)
 constexpr int kB1Shift = 32 + kSelShift;  // composite bits above it: the 11 key bits of b1
-constexpr int kTieMax = 8192;        // tie list capacity (LDS of the resolve)
+constexpr int kTieLds = 8192;        // tie entries the resolve keeps in LDS
+constexpr int kBitsLds = 8192;       // bitmap words the resolve keeps in LDS
 constexpr int kTiny = 1024;          // a final group up to this size is ranked directly
 constexpr int kCtr = 16;             // per-row counters: [0] tie count
 
 inline size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 
-inline int tie_cap(int n_cols) {
-    int c = (n_cols / 16 + 63) / 64 * 64;
-    return c < 2048 ? 2048 : (c > kTieMax ? kTieMax : c);
+// Tie list capacity per row: every column when the rows together stay within 2^24
+// entries, else 2^24 / rows (at least 8192); a longer threshold bin is resolved by
+// rescanning the row.
+inline int tie_cap(int rows, int n_cols) {
+    const int64_t all = ((int64_t)n_cols + 63) / 64 * 64;
+    int64_t c = ((int64_t)(1 << 24) / rows + 63) / 64 * 64;
+    if (c < kTieLds) c = kTieLds;
+    return (int)(all < c ? all : c);
 }
 inline int bit_words(int n_cols) { return (n_cols + 31) / 32; }
 
@@ -66,7 +72,7 @@ size_t zero_bytes(int rows) { return align256((size_t)rows * kSelBins * 4) + ali
 Ws carve(void *base, int rows, int n_cols, bool kept) {
     Ws w;
     char *p = reinterpret_cast<char *>(base);
-    w.cap = tie_cap(n_cols);
+    w.cap = tie_cap(rows, n_cols);
     w.words = bit_words(n_cols);
     w.hist = reinterpret_cast<uint32_t *>(p);
     p += align256((size_t)rows * kSelBins * 4);
@@ -81,7 +87,7 @@ Ws carve(void *base, int rows, int n_cols, bool kept) {
 }
 
 size_t ws_total(int rows, int n_cols, bool kept) {
-    const int cap = tie_cap(n_cols);
+    const int cap = tie_cap(rows, n_cols);
     return zero_bytes(rows) + align256((size_t)rows * cap * 8) + (kept ? align256((size_t)rows * cap * 4) : 0) +
            align256((size_t)rows * bit_words(n_cols) * 4);
 }
@@ -426,13 +432,19 @@ __global__ __launch_bounds__(kHT) void select_filter_kernel(SelectArgs a, Ws w, 
 }
 
 // ----------------------------------------------------------------------------- resolve
-// One workgroup per row. KEPT: columns map to positions through the kept map, so the
-// chosen positions are sorted (bitonic, KPAD entries) before they are written.
+// One workgroup per row. Ties are ranked from LDS when they fit (kTieLds), else read
+// from the workspace list. LWORDS > 0: the row's bitmap (LWORDS words) is loaded into LDS
+// with the first loads, the chosen ties are set there and the compaction reads it back;
+// else the bitmap stays in the workspace (global atomics, then coherent reads). KEPT:
+// columns map to positions through the kept map, so the chosen positions are sorted
+// (bitonic, KPAD entries) before they are written.
 template <bool KEPT, int KPAD>
-__global__ __launch_bounds__(kRT) void select_resolve_kernel(SelectArgs a, Ws w) {
+__global__ __launch_bounds__(kRT) void select_resolve_kernel(SelectArgs a, Ws w, int lwords) {
     extern __shared__ __attribute__((aligned(16))) unsigned char dyn[];
-    uint64_t *ties = reinterpret_cast<uint64_t *>(dyn);                        // [cap]
-    uint32_t *tcols = reinterpret_cast<uint32_t *>(dyn + (size_t)w.cap * 8);  // [cap] (KEPT)
+    const int tcap = min(w.cap, kTieLds);                                        // ties held in LDS
+    uint64_t *lties = reinterpret_cast<uint64_t *>(dyn);                         // [tcap]
+    uint32_t *ltcols = reinterpret_cast<uint32_t *>(dyn + (size_t)tcap * 8);     // [tcap] (KEPT)
+    uint32_t *lbits = reinterpret_cast<uint32_t *>(dyn + (size_t)tcap * (KEPT ? 12 : 8));  // [lwords]
     __shared__ __attribute__((aligned(16))) uint32_t h[kB2];  // second-level histogram, then the final group
     __shared__ uint32_t h256[256];
     __shared__ uint32_t scr[32];
@@ -448,46 +460,55 @@ __global__ __launch_bounds__(kRT) void select_resolve_kernel(SelectArgs a, Ws w)
     const uint32_t *gtcols = KEPT ? w.tcols + (int64_t)row * w.cap : nullptr;
     uint32_t *gbits = w.bits + (int64_t)row * w.words;
 
-    // ---- histogram (2 bins per thread from the top), tie count, the first tie entries;
-    // the histogram and the counters are left at zero
+    // ---- first loads: histogram (2 bins per thread from the top), tie count, the first
+    // tie entries, the bitmap; the histogram and the counters are left at zero
     uint32_t hv[2];
     hv[0] = g1[kSelBins - 1 - 2 * tid];
     hv[1] = g1[kSelBins - 2 - 2 * tid];
     const uint32_t ntie = gctr[0];
     uint64_t t0 = 0, t1 = 0;
     uint32_t tc0 = 0, tc1 = 0;
-    if (tid < w.cap) t0 = gties[tid];
-    if (tid + kRT < w.cap) t1 = gties[tid + kRT];
+    if (tid < tcap) t0 = gties[tid];
+    if (tid + kRT < tcap) t1 = gties[tid + kRT];
     if (KEPT) {
-        if (tid < w.cap) tc0 = gtcols[tid];
-        if (tid + kRT < w.cap) tc1 = gtcols[tid + kRT];
+        if (tid < tcap) tc0 = gtcols[tid];
+        if (tid + kRT < tcap) tc1 = gtcols[tid + kRT];
     }
+    for (int i = tid; i < lwords; i += kRT) lbits[i] = gbits[i];
     const BinPick bp = pick_bin<kRT, 2>(hv, m, scr);  // its barriers follow every thread's reads
     g1[kSelBins - 1 - 2 * tid] = 0;
     g1[kSelBins - 2 - 2 * tid] = 0;
     if (tid < kCtr) gctr[tid] = 0;
     const int b1 = bp.bin;
 
-    auto mark = [&](int col) { atomicOr(&gbits[col >> 5], 1u << (col & 31)); };
+    auto mark = [&](int col) {
+        if (lwords) atomicOr(&lbits[col >> 5], 1u << (col & 31));
+        else atomicOr(&gbits[col >> 5], 1u << (col & 31));
+    };
     if (bp.mode == 2) {
-        const bool overflow = ntie > (uint32_t)w.cap;
+        const bool overflow = ntie > (uint32_t)w.cap;  // the list is incomplete
         const uint32_t nl = min(ntie, (uint32_t)w.cap);
+        const bool inlds = nl <= (uint32_t)tcap;
+        const uint64_t *tl = inlds ? lties : gties;            // the tie list being ranked
+        const uint32_t *tcl = inlds ? ltcols : gtcols;
         const uint32_t need1 = m > bp.above ? m - bp.above : 0u;
         uint64_t thr = ~(uint64_t)0;
         if (!overflow) {
-            if ((uint32_t)tid < nl) ties[tid] = t0;
-            if ((uint32_t)tid + kRT < nl) ties[tid + kRT] = t1;
-            for (uint32_t i = tid + 2 * kRT; i < nl; i += kRT) ties[i] = gties[i];
-            if (KEPT) {
-                if ((uint32_t)tid < nl) tcols[tid] = tc0;
-                if ((uint32_t)tid + kRT < nl) tcols[tid + kRT] = tc1;
-                for (uint32_t i = tid + 2 * kRT; i < nl; i += kRT) tcols[i] = gtcols[i];
+            if (inlds) {
+                if ((uint32_t)tid < nl) lties[tid] = t0;
+                if ((uint32_t)tid + kRT < nl) lties[tid + kRT] = t1;
+                for (uint32_t i = tid + 2 * kRT; i < nl; i += kRT) lties[i] = gties[i];
+                if (KEPT) {
+                    if ((uint32_t)tid < nl) ltcols[tid] = tc0;
+                    if ((uint32_t)tid + kRT < nl) ltcols[tid + kRT] = tc1;
+                    for (uint32_t i = tid + 2 * kRT; i < nl; i += kRT) ltcols[i] = gtcols[i];
+                }
             }
             for (int i = tid; i < kB2; i += kRT) h[i] = 0;
             if (tid < 4) cnt[tid] = 0;
             __syncthreads();
             for (uint32_t i = tid; i < nl; i += kRT)
-                atomicAdd(&h[((uint32_t)(ties[i] >> 32) >> kL2Shift) & (kB2 - 1)], 1u);
+                atomicAdd(&h[((uint32_t)(tl[i] >> 32) >> kL2Shift) & (kB2 - 1)], 1u);
             __syncthreads();
             uint32_t v2[4];
 #pragma unroll
@@ -506,7 +527,7 @@ __global__ __launch_bounds__(kRT) void select_resolve_kernel(SelectArgs a, Ws w)
                 } else if (n2 <= (uint32_t)kTiny) {
                     uint64_t *tiny = reinterpret_cast<uint64_t *>(h);
                     for (uint32_t i = tid; i < nl; i += kRT) {
-                        const uint64_t c = ties[i];
+                        const uint64_t c = tl[i];
                         if ((c >> kGrpShift) == (pre >> kGrpShift)) {
                             const uint32_t slot = atomicAdd(&cnt[2], 1u);
                             if (slot < (uint32_t)kTiny) tiny[slot] = c;
@@ -526,11 +547,11 @@ __global__ __launch_bounds__(kRT) void select_resolve_kernel(SelectArgs a, Ws w)
                     __syncthreads();
                     thr = ((uint64_t)scr[21] << 32) | scr[20];
                 } else {
-                    thr = radix_kth(ArrSrc{ties, (int)nl}, need2, pre, kGrpShift, h256, scr);
+                    thr = radix_kth(ArrSrc{tl, (int)nl}, need2, pre, kGrpShift, h256, scr);
                 }
             }
             for (uint32_t i = tid; i < nl; i += kRT)
-                if (ties[i] >= thr) mark(KEPT ? (int)tcols[i] : comp_pos(ties[i]));
+                if (tl[i] >= thr) mark(KEPT ? (int)tcl[i] : comp_pos(tl[i]));
         } else {
             // the tie list overflowed: exact select inside bin b1 over the whole row
             const RowSrc rs{&a, &r};
@@ -551,13 +572,16 @@ __global__ __launch_bounds__(kRT) void select_resolve_kernel(SelectArgs a, Ws w)
     const int nwin = a.causal ? max(0, r.p - r.f_win_lo + 1) : 0;
     uint32_t nfill = 0;
     if (bp.mode != 0) {
+        auto word = [&](int i) -> uint32_t {
+            return lwords ? lbits[i] : __hip_atomic_load(&gbits[i], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        };
         const int per = (w.words + kRT - 1) / kRT;
         const int w0 = min(w.words, tid * per), w1 = min(w.words, w0 + per);
         uint32_t c = 0;
-        for (int i = w0; i < w1; ++i) c += __popc(__hip_atomic_load(&gbits[i], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT));
+        for (int i = w0; i < w1; ++i) c += __popc(word(i));
         uint32_t off = block_exscan<kRT>(c, scr, &nfill);
         for (int i = w0; i < w1; ++i) {
-            uint32_t bits = __hip_atomic_load(&gbits[i], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            uint32_t bits = word(i);
             while (bits) {
                 const int col = i * 32 + __ffs(bits) - 1;
                 bits &= bits - 1;
@@ -612,8 +636,12 @@ __global__ void clear_kernel(uint4 *p, size_t n16, uint8_t *tail, size_t ntail) 
 
 template <bool KEPT, int KPAD>
 hipError_t launch_resolve_t(const SelectArgs &a, const Ws &w, hipStream_t s) {
-    const size_t lds = (size_t)w.cap * (KEPT ? 12 : 8);
-    hipLaunchKernelGGL((select_resolve_kernel<KEPT, KPAD>), dim3(a.B * a.T), dim3(kRT), lds, s, a, w);
+    const int tcap = w.cap < kTieLds ? w.cap : kTieLds;
+    const size_t tie_lds = (size_t)tcap * (KEPT ? 12 : 8);
+    // the bitmap goes to LDS when it fits beside the ties and the static arrays (<= 34 KB)
+    const int lwords = (w.words <= kBitsLds && tie_lds + (size_t)w.words * 4 <= 126 * 1024) ? w.words : 0;
+    const size_t lds = tie_lds + (size_t)lwords * 4;
+    hipLaunchKernelGGL((select_resolve_kernel<KEPT, KPAD>), dim3(a.B * a.T), dim3(kRT), lds, s, a, w, lwords);
     return hipGetLastError();
 }
 

@@ -4,9 +4,10 @@ against the oracle's selection of the same fp32 values, and the primed selection
 
 The designed rows exercise every path of the selection's row pass: the position bitmap
 (N <= 2^18) and the sorted list (N > 2^18); rows whose length is not a multiple of 4;
-threshold groups ranked directly, by radix passes over the LDS tie list (more than 1024
-equal scores) and by rescanning the row (more than 8192 equal scores); -0.0 next to
-+0.0; -inf entries (never candidates); fewer candidates than the fill.
+threshold groups ranked directly, by radix passes over the tie list (more than 1024
+equal scores), from the workspace copy of the tie list (more ties than the resolve holds
+in LDS), and by rescanning the row (more ties than the list holds); -0.0 next to +0.0;
+-inf entries (never candidates); fewer candidates than the fill.
 """
 import numpy as np
 import pytest
@@ -71,8 +72,9 @@ def test_many_equal_scores_in_threshold_group():
     _check_rows(row[None], 2048, 16, 64)
 
 
-def test_equal_scores_overflow_tie_list():
-    # 10000 scores exactly 2.0 (more than the LDS tie list holds) with part of them needed
+def test_equal_scores_beyond_lds_tie_list():
+    # 10000 scores exactly 2.0 (more than the resolve keeps in LDS: ranked from the
+    # workspace list) with part of them needed
     rng = np.random.default_rng(14)
     N = 40000
     row = (rng.standard_normal(N) * 0.01 - 5.0).astype(np.float32)
@@ -80,6 +82,23 @@ def test_equal_scores_overflow_tie_list():
     row[pos[:500]] = 3.0 + rng.random(500).astype(np.float32)
     row[pos[500:10500]] = 2.0
     _check_rows(row[None], 2048, 16, 64)
+
+
+def test_tie_list_overflow_rescans_row():
+    # 2048 rows x 16384 columns: the per-row tie list holds 8192 entries, so a row whose
+    # threshold bin holds 10000 equal scores is resolved by rescanning the row
+    rng = np.random.default_rng(17)
+    R, N = 2048, 16384
+    rows = rng.standard_normal((R, N)).astype(np.float32)
+    hot = 7
+    rows[hot] = (rng.standard_normal(N) * 0.01 - 5.0).astype(np.float32)
+    pos = rng.permutation(np.arange(16, N - 64))
+    rows[hot, pos[:500]] = 3.0 + rng.random(500).astype(np.float32)
+    rows[hot, pos[500:10500]] = 2.0
+    got = _gpu_select(rows, 2048, 16, 64)
+    for i in (hot, 0, 1234, R - 1):
+        want = _oracle_select(rows[i], 2048, 16, 64)
+        assert np.array_equal(got[i], want), f"row {i}"
 
 
 def test_signed_zeros_and_masked_entries():
