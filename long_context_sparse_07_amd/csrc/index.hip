@@ -34,6 +34,15 @@ __device__ __forceinline__ void wait_vmcnt() {
     __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
 }
 
+// LDS add without return, issued as inline asm. Written as a plain atomic, the compiler
+// orders it after every outstanding direct-to-LDS DMA (s_waitcnt vmcnt(0)), which would
+// drain the key ring on every tile. The histogram and the ring never overlap.
+__device__ __forceinline__ void lds_add_u32(uint32_t *p, uint32_t v) {
+    const uint32_t la = (uint32_t)(uintptr_t)((__attribute__((address_space(3))) uint32_t *)p);
+    asm volatile("ds_add_u32 %0, %1" ::"v"(la), "v"(v) : "memory");
+}
+__device__ __forceinline__ void lds_wait_all() { asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory"); }
+
 // Query-row layouts of one MFMA row group.
 enum { ONEQ = 0, Q4 = 4, Q8 = 8, Q16 = 16 };
 
@@ -215,7 +224,170 @@ __global__ __launch_bounds__(kThreads) void index_tokens_kernel(IndexTokensArgs 
     // position; visibility only shrinks with the column, so skipped tiles form a suffix.
     int nvis = ntiles;
     if constexpr (!HI) nvis = maxp < c0 ? 0 : min(ntiles, (maxp - c0) / kKT + 1);
-    {
+#pragma unroll
+    for (int p = 0; p < G::NST - 1; ++p)
+        if (p < nvis) issue_tile(c0 + p * kKT, p);
+    // the query and weight loads were issued before the ring DMA and so have landed once
+    // at most the DMA instructions are pending; waiting here (no store is pending yet, so
+    // the count is exact) lets the loop use them without a full drain of the ring
+    if (nvis >= 3) wait_vmcnt<3 * G::PER_WAVE>();
+    else if (nvis == 2) wait_vmcnt<2 * G::PER_WAVE>();
+    else if (nvis == 1) wait_vmcnt<G::PER_WAVE>();
+    else wait_vmcnt<0>();
+
+    // ---- one sub-tile of 32 rows: LDS operands -> MFMA accumulators
+    auto mfma_tile = [&](const unsigned char *tile, int row, f32x16(&acc)[HB]) {
+        const unsigned char *trow = tile + row * G::RB;
+#pragma unroll
+        for (int hb = 0; hb < HB; ++hb)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) acc[hb][r] = 0.0f;
+        // every LDS operand of the sub-tile is requested before the first MFMA
+        if constexpr (FP8) {
+            u32x4 kv[KSTEPS / 2];
+#pragma unroll
+            for (int kk = 0; kk < KSTEPS / 2; ++kk)
+                kv[kk] = *reinterpret_cast<const u32x4 *>(trow + G::swz(row, (D / 32) * half + kk) * 16);
+#pragma unroll
+            for (int kk = 0; kk < KSTEPS / 2; ++kk) {
+                bf16x8 f0, f1;
+                fp8x16_to_frags(kv[kk], f0, f1);
+#pragma unroll
+                for (int hb = 0; hb < HB; ++hb) {
+                    acc[hb] = mfma32(aq[hb][2 * kk], f0, acc[hb]);
+                    acc[hb] = mfma32(aq[hb][2 * kk + 1], f1, acc[hb]);
+                }
+            }
+        } else {
+            u32x4 kv[KSTEPS];
+#pragma unroll
+            for (int ks = 0; ks < KSTEPS; ++ks)  // bytes D*half + 16*ks
+                kv[ks] = *reinterpret_cast<const u32x4 *>(trow + G::swz(row, (D / 16) * half + ks) * 16);
+#pragma unroll
+            for (int ks = 0; ks < KSTEPS; ++ks) {
+                const bf16x8 f = __builtin_bit_cast(bf16x8, kv[ks]);
+#pragma unroll
+                for (int hb = 0; hb < HB; ++hb) acc[hb] = mfma32(aq[hb][ks], f, acc[hb]);
+            }
+        }
+    };
+
+    // ---- epilogue of one sub-tile: ReLU, head weights, head sum, scale, causal mask
+    // (col: the lane's column; pos: its cache position or -1; sc: its per-token scale)
+    auto epilogue = [&](const f32x16(&acc)[HB], int col, int pos, float sc) {
+        if constexpr (MODE == ONEQ) {
+            // head sum in four independent chains, then the other half-wave's heads
+            float s4[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+            for (int hb = 0; hb < HB; ++hb)
+#pragma unroll
+                for (int r = 0; r < 16; ++r) s4[r & 3] += wreg[hb][r] * relu_bits(acc[hb][r]);
+            const float s = half_pair_sum((s4[0] + s4[1]) + (s4[2] + s4[3]));
+            const int t = grp;
+            const int p = ctx - T + t;
+            if (half == 0 && col < c1) {
+                const bool vis = pos >= 0 && pos <= p;
+                const float v = vis ? s * sc : kNegInf;
+                write_score(t, col, v);
+                if constexpr (HIST)
+                    if (vis && pos >= f_se && pos < f_wl && v > kNegInf) lds_add_u32(&shist[order_key(v) >> kSelShift], 1u);
+            }
+        } else if constexpr (MODE == Q4) {
+            float part[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+            for (int r = 0; r < 16; ++r) part[r / 4] += wreg[0][r] * relu_bits(acc[0][r]);
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                const int t = grp * QPG + 2 * j + half;
+                const int p = ctx - T + t;
+                if (t < T && col < c1) write_score(t, col, (pos >= 0 && pos <= p) ? part[j] * sc : kNegInf);
+            }
+        } else {
+            float part[QPG];
+#pragma unroll
+            for (int j = 0; j < QPG; ++j) part[j] = 0.0f;
+#pragma unroll
+            for (int r = 0; r < 16; ++r) part[(8 * (r / 4)) / MODE] += wreg[0][r] * relu_bits(acc[0][r]);
+#pragma unroll
+            for (int j = 0; j < QPG; ++j) {
+                part[j] += __shfl_xor(part[j], 32, 64);
+                const int t = grp * QPG + j;
+                const int p = ctx - T + t;
+                if (half == 0 && t < T && col < c1) write_score(t, col, (pos >= 0 && pos <= p) ? part[j] * sc : kNegInf);
+            }
+        }
+    };
+
+    // ---- ring wait + refill at the top of iteration `it`
+    auto advance = [&](int it) {
+        // this wave's DMA of tile `it` is complete once at most `ahead` later tiles'
+        // instructions are pending (vector memory operations retire in issue order)
+        const int ahead = min(G::NST - 2, nvis - 1 - it);
+        if (ahead >= 2) wait_vmcnt<2 * G::PER_WAVE>();
+        else if (ahead == 1) wait_vmcnt<G::PER_WAVE>();
+        else wait_vmcnt<0>();
+        // OWN: this wave's rows of tile `it` landed and it has finished reading its rows of
+        // tile it-1 (the stage refilled next). Shared tiles: every wave's part landed and
+        // every wave is done with tile it-1.
+        if constexpr (!OWN) __syncthreads();
+        if (it + G::NST - 1 < nvis)
+            issue_tile(c0 + (it + G::NST - 1) * kKT, (it + G::NST - 1) % G::NST);
+    };
+
+    if constexpr (PRE) {
+        // four query groups share each tile: every wave computes all four sub-tiles
+        for (int it = 0; it < nvis; ++it) {
+            advance(it);
+            const int st = it % G::NST;
+            const unsigned char *tile = ring + st * G::STAGE;
+            const float *tscale = reinterpret_cast<const float *>(tile + G::BYTES);
+            if (active) {
+#pragma unroll
+                for (int sb = 0; sb < 4; ++sb) {
+                    const int row = sb * 32 + l32;
+                    f32x16 acc[HB];
+                    mfma_tile(tile, row, acc);
+                    const int col = c0 + it * kKT + row;
+                    epilogue(acc, col, col < c1 && col < N ? col : -1, FP8 ? tscale[row] : 1.0f);
+                }
+            }
+        }
+    } else {
+        // (one query group per workgroup: every wave is active)
+        // Software pipeline over this wave's 32 rows of each tile: the MFMAs of tile `it`
+        // are issued before the epilogue of tile it-1 (accumulators alternate), so the
+        // matrix core and the VALU work on different tiles at the same time. The scale
+        // and position of a tile are read while its stage is current (the refill at the
+        // top of the next iteration overwrites that stage).
+        const int row = wave * 32 + l32;
+        f32x16 acc0[HB], acc1[HB];
+        int pcol = 0, ppos = -1;
+        float psc = 0.0f;
+        auto step = [&](int it, f32x16(&cur)[HB], const f32x16(&prev)[HB]) {
+            advance(it);
+            const int st = it % G::NST;
+            const unsigned char *tile = ring + st * G::STAGE;
+            const float sc = FP8 ? reinterpret_cast<const float *>(tile + G::BYTES)[row] : 1.0f;
+            const int col = c0 + it * kKT + row;
+            int pos;
+            if constexpr (HI) pos = tpos[st][row];
+            else pos = col < c1 && col < N ? col : -1;
+            mfma_tile(tile, row, cur);
+            if (it > 0) epilogue(prev, pcol, ppos, psc);
+            pcol = col;
+            ppos = pos;
+            psc = sc;
+        };
+        for (int it = 0; it < nvis; it += 2) {
+            step(it, acc0, acc1);
+            if (it + 1 < nvis) step(it + 1, acc1, acc0);
+        }
+        if (nvis > 0) {
+            if (nvis & 1) epilogue(acc0, pcol, ppos, psc);
+            else epilogue(acc1, pcol, ppos, psc);
+        }
+    }
+    {  // tiles past every query's position: -inf
         constexpr int NQ = PRE ? 4 : QPG;
         for (int e = nvis * kKT + tid; e < ntiles * kKT * NQ; e += kThreads) {
             // e runs over (query q, column offset) of the skipped tiles
@@ -227,120 +399,8 @@ __global__ __launch_bounds__(kThreads) void index_tokens_kernel(IndexTokensArgs 
             if (col < c1 && t < T) write_score(t, col, kNegInf);
         }
     }
-#pragma unroll
-    for (int p = 0; p < G::NST - 1; ++p)
-        if (p < nvis) issue_tile(c0 + p * kKT, p);
-
-    for (int it = 0; it < nvis; ++it) {
-        const int tc0 = c0 + it * kKT;
-        const int st = it % G::NST;
-        // this wave's DMA of tile `it` is complete once at most `ahead` later tiles'
-        // instructions are pending (vector memory operations retire in issue order)
-        const int ahead = min(G::NST - 2, nvis - 1 - it);
-        if (ahead >= 2) wait_vmcnt<2 * G::PER_WAVE>();
-        else if (ahead == 1) wait_vmcnt<G::PER_WAVE>();
-        else wait_vmcnt<0>();
-        // OWN: this wave's rows of tile `it` landed and it has finished reading its rows of
-        // tile it-1 (the stage refilled next). Shared tiles: every wave's part landed and
-        // every wave is done with tile it-1.
-        if constexpr (!OWN) __syncthreads();
-        if (it + G::NST - 1 < nvis) issue_tile(tc0 + (G::NST - 1) * kKT, (it + G::NST - 1) % G::NST);
-        const unsigned char *tile = ring + st * G::STAGE;
-        const float *tscale = reinterpret_cast<const float *>(tile + G::BYTES);
-
-        if (active) {
-            constexpr int NSUB = PRE ? 4 : 1;
-#pragma unroll
-            for (int sb = 0; sb < NSUB; ++sb) {
-                const int sub = PRE ? sb : wave;
-                const int row = sub * 32 + l32;
-                const unsigned char *trow = tile + row * G::RB;
-                f32x16 acc[HB];
-#pragma unroll
-                for (int hb = 0; hb < HB; ++hb)
-#pragma unroll
-                    for (int r = 0; r < 16; ++r) acc[hb][r] = 0.0f;
-                // every LDS operand of the sub-tile is requested before the first MFMA
-                const float sc = FP8 ? tscale[row] : 1.0f;
-                if constexpr (FP8) {
-                    u32x4 kv[KSTEPS / 2];
-#pragma unroll
-                    for (int kk = 0; kk < KSTEPS / 2; ++kk)
-                        kv[kk] = *reinterpret_cast<const u32x4 *>(trow + G::swz(row, (D / 32) * half + kk) * 16);
-#pragma unroll
-                    for (int kk = 0; kk < KSTEPS / 2; ++kk) {
-                        bf16x8 f0, f1;
-                        fp8x16_to_frags(kv[kk], f0, f1);
-#pragma unroll
-                        for (int hb = 0; hb < HB; ++hb) {
-                            acc[hb] = mfma32(aq[hb][2 * kk], f0, acc[hb]);
-                            acc[hb] = mfma32(aq[hb][2 * kk + 1], f1, acc[hb]);
-                        }
-                    }
-                } else {
-                    u32x4 kv[KSTEPS];
-#pragma unroll
-                    for (int ks = 0; ks < KSTEPS; ++ks)  // bytes D*half + 16*ks
-                        kv[ks] = *reinterpret_cast<const u32x4 *>(trow + G::swz(row, (D / 16) * half + ks) * 16);
-#pragma unroll
-                    for (int ks = 0; ks < KSTEPS; ++ks) {
-                        const bf16x8 f = __builtin_bit_cast(bf16x8, kv[ks]);
-#pragma unroll
-                        for (int hb = 0; hb < HB; ++hb) acc[hb] = mfma32(aq[hb][ks], f, acc[hb]);
-                    }
-                }
-                // ---- epilogue: ReLU, head weights, head sum, scale, causal mask
-                const int col = tc0 + sub * 32 + l32;
-                int pos;
-                if constexpr (HI) pos = tpos[st][row];
-                else pos = col < c1 && col < N ? col : -1;
-                if constexpr (MODE == ONEQ) {
-                    // head sum in four independent chains, then the other half-wave's heads
-                    float s4[4] = {0.0f, 0.0f, 0.0f, 0.0f};
-#pragma unroll
-                    for (int hb = 0; hb < HB; ++hb)
-#pragma unroll
-                        for (int r = 0; r < 16; ++r) s4[r & 3] += wreg[hb][r] * relu_bits(acc[hb][r]);
-                    const float s = half_pair_sum((s4[0] + s4[1]) + (s4[2] + s4[3]));
-                    const int t = grp;
-                    const int p = ctx - T + t;
-                    if (half == 0 && col < c1) {
-                        const bool vis = pos >= 0 && pos <= p;
-                        const float v = vis ? s * sc : kNegInf;
-                        write_score(t, col, v);
-                        if constexpr (HIST)
-                            if (vis && pos >= f_se && pos < f_wl && v > kNegInf)
-                                atomicAdd(&shist[order_key(v) >> kSelShift], 1u);
-                    }
-                } else if constexpr (MODE == Q4) {
-                    float part[4] = {0.0f, 0.0f, 0.0f, 0.0f};
-#pragma unroll
-                    for (int r = 0; r < 16; ++r) part[r / 4] += wreg[0][r] * relu_bits(acc[0][r]);
-#pragma unroll
-                    for (int j = 0; j < 4; ++j) {
-                        const int t = grp * QPG + 2 * j + half;
-                        const int p = ctx - T + t;
-                        if (t < T && col < c1) write_score(t, col, (pos >= 0 && pos <= p) ? part[j] * sc : kNegInf);
-                    }
-                } else {
-                    float part[QPG];
-#pragma unroll
-                    for (int j = 0; j < QPG; ++j) part[j] = 0.0f;
-#pragma unroll
-                    for (int r = 0; r < 16; ++r) part[(8 * (r / 4)) / MODE] += wreg[0][r] * relu_bits(acc[0][r]);
-#pragma unroll
-                    for (int j = 0; j < QPG; ++j) {
-                        part[j] += __shfl_xor(part[j], 32, 64);
-                        const int t = grp * QPG + j;
-                        const int p = ctx - T + t;
-                        if (half == 0 && t < T && col < c1)
-                            write_score(t, col, (pos >= 0 && pos <= p) ? part[j] * sc : kNegInf);
-                    }
-                }
-            }
-        }
-    }
     if constexpr (HIST) {
+        lds_wait_all();  // the histogram adds above are inline asm: not tracked by the compiler
         __syncthreads();
         if (active) {
             uint32_t *g = a.sel_hist + (int64_t)(b * T + grp) * kSelBins;
