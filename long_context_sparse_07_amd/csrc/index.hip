@@ -43,10 +43,16 @@ __device__ __forceinline__ void lds_add_u32(uint32_t *p, uint32_t v) {
 }
 __device__ __forceinline__ void lds_wait_all() { asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory"); }
 
+// Workgroup barrier for the key ring: this wave's LDS operations complete first, its
+// outstanding vector memory operations do not (a workgroup fence would also wait for the
+// direct-to-LDS DMA still in flight, i.e. drain the ring). The memory clobber keeps the
+// compiler from moving memory accesses across it.
+__device__ __forceinline__ void lds_barrier() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
+
 // Query-row layouts of one MFMA row group.
 enum { ONEQ = 0, Q4 = 4, Q8 = 8, Q16 = 16 };
 
-template <int D, bool FP8>
+template <int D, bool FP8, int NST_>
 struct Tile {
     static constexpr int RB = FP8 ? D : 2 * D;        // bytes per key row
     static constexpr int CPR = RB / 16;               // 16-byte chunks per row
@@ -55,7 +61,7 @@ struct Tile {
     static constexpr int PER_WAVE = KINSTR / 4 + (FP8 ? 1 : 0);  // + one scale DMA per wave
     static constexpr int SBYTES = FP8 ? kKT * 4 : 0;  // per-token scales of a tile
     static constexpr int STAGE = BYTES + SBYTES;
-    static constexpr int NST = 4;                     // ring: one tile computed, three in flight
+    static constexpr int NST = NST_;                  // ring: one tile computed, NST-1 in flight
     static_assert(KINSTR % 4 == 0, "tile must split evenly over 4 waves");
     static_assert(PER_WAVE * (NST - 2) < 64, "vmcnt budget");
     static constexpr int RPB = CPR >= 16 ? 1 : 16 / CPR;  // rows per 256-byte bank row
@@ -63,6 +69,20 @@ struct Tile {
     // 16 consecutive rows land on 16 distinct groups of 4 banks.
     __device__ static __forceinline__ int swz(int row, int c) { return c ^ ((row / RPB) & (CPR - 1)); }
 };
+
+// Wait until at most n tiles' DMA instructions (PW per tile, n <= MAXN) are pending.
+template <int PW, int MAXN>
+__device__ __forceinline__ void wait_tiles(int n) {
+    if constexpr (MAXN > 0) {
+        if (n >= MAXN) {
+            wait_vmcnt<MAXN * PW>();
+            return;
+        }
+        wait_tiles<PW, MAXN - 1>(n);
+    } else {
+        wait_vmcnt<0>();
+    }
+}
 
 // Row i of the (query, head) row space of group `grp` -> (t, h); ok = a real row.
 template <int MODE>
@@ -82,18 +102,27 @@ __device__ __forceinline__ void row_to_th(int grp, int i, int H, int T, int &t, 
 // HIST (one query per workgroup): the epilogue also counts the selection candidates of
 // its columns per first-level bin of the selection histogram (finite scores at visible
 // positions outside the sink and the window) and adds the counts to sel_hist.
-template <int D, bool FP8, int MODE, int HB, bool HI, bool PRE, bool HIST>
-__global__ __launch_bounds__(kThreads) void index_tokens_kernel(IndexTokensArgs a, int groups, int chunk) {
-    using G = Tile<D, FP8>;
+template <int D, bool FP8, int MODE, int HB, bool HI, bool PRE, bool HIST, int NST>
+__global__ __launch_bounds__(PRE ? kThreads : 2 * kThreads) void index_tokens_kernel(IndexTokensArgs a, int groups,
+                                                                                      int chunk) {
+    using G = Tile<D, FP8, NST>;
+    // SPLIT (one query group per workgroup): waves 0-3 compute, waves 4-7 only stream the
+    // key tiles into the LDS ring, so a DMA issue that stalls on a full memory queue
+    // never holds up the MFMA and VALU work. Otherwise (four query groups share each
+    // tile, 4 waves) every wave does both.
+    constexpr bool SPLIT = !PRE;
+    constexpr int NT = SPLIT ? 2 * kThreads : kThreads;
     constexpr int KSTEPS = D / 16;
     constexpr int QPG = MODE == ONEQ ? 1 : 32 / MODE;
     extern __shared__ __attribute__((aligned(16))) unsigned char ring[];  // NST x (keys, scales)
-    __shared__ int tpos[G::NST][kKT];                                     // HI: position of each row
+    __shared__ int tpos[HI ? G::NST : 1][kKT];                            // HI: position of each row
     __shared__ uint32_t shist[HIST ? kSelBins : 1];                      // HIST: candidate counts
     static_assert(!HIST || (MODE == ONEQ && !PRE), "the histogram needs one query per workgroup");
 
     const int tid = threadIdx.x;
-    const int lane = tid & 63, wave = tid >> 6, half = lane >> 5, l32 = lane & 31;
+    const int lane = tid & 63, half = lane >> 5, l32 = lane & 31;
+    const int wave = (tid >> 6) & 3;               // compute wave, or the producer of its rows
+    const bool producer = SPLIT && (tid >> 6) >= 4;
     const int b = blockIdx.z;
     const int c0 = blockIdx.x * chunk;
     if (c0 >= a.n_out) return;
@@ -107,12 +136,12 @@ __global__ __launch_bounds__(kThreads) void index_tokens_kernel(IndexTokensArgs 
     const bool active = grp < groups;
     int f_se = 0, f_wl = 0;  // HIST: forced set of the workgroup's query
     if constexpr (HIST) {
-        for (int i = tid; i < kSelBins; i += kThreads) shist[i] = 0;
+        for (int i = tid; i < kSelBins; i += NT) shist[i] = 0;
         forced_bounds(ctx - T + grp, a.sink, a.window, f_se, f_wl);
-        __syncthreads();
     }
+    if constexpr (HIST) __syncthreads();
 
-    // ---- query fragments (A operand, rows = query heads) and head weights
+    // ---- query fragments (A operand, rows = query heads) and head weights (compute waves)
     bf16x8 aq[HB][KSTEPS];
     float wreg[HB][16];
 #pragma unroll
@@ -120,7 +149,7 @@ __global__ __launch_bounds__(kThreads) void index_tokens_kernel(IndexTokensArgs 
         int t, h;
         bool ok;
         row_to_th<MODE>(grp, 32 * hb + l32, H, T, t, h, ok);
-        ok = ok && active;
+        ok = ok && active && !producer;
         const uint16_t *qrow = a.q + ((int64_t)(b * T + t) * H + h) * D + (D / 2) * half;
 #pragma unroll
         for (int ks = 0; ks < KSTEPS; ++ks) {
@@ -132,9 +161,13 @@ __global__ __launch_bounds__(kThreads) void index_tokens_kernel(IndexTokensArgs 
         for (int r = 0; r < 16; ++r) {
             int i = 32 * hb + 8 * (r / 4) + 4 * half + (r % 4);
             row_to_th<MODE>(grp, i, H, T, t, h, ok);
-            wreg[hb][r] = (ok && active) ? a.w[(int64_t)(b * T + t) * H + h] : 0.0f;
+            wreg[hb][r] = (ok && active && !producer) ? a.w[(int64_t)(b * T + t) * H + h] : 0.0f;
         }
     }
+    // SPLIT: the compute waves wait for their query and weight loads here, before any
+    // score store is pending (the compiler then knows them complete inside the loop);
+    // the producers have nothing outstanding yet
+    if constexpr (SPLIT) wait_vmcnt<0>();
 
     // Last visible position over every query of this workgroup (flat mode skips tiles past it).
     int last_t;
@@ -166,9 +199,8 @@ __global__ __launch_bounds__(kThreads) void index_tokens_kernel(IndexTokensArgs 
     // L / CPR, physical chunk pc = L % CPR, which holds logical chunk pc ^ swz(row) (the
     // XOR swizzle is applied on the global side, so each row is still read as one
     // contiguous line). Rows without a position read the cache start (masked later).
-    // OWN (one query group per workgroup): wave w loads exactly the 32 rows it computes,
-    // so the waves stream independently and never wait for each other. Otherwise (four
-    // query groups share each tile) the waves split every tile and meet at a barrier.
+    // SPLIT: producer w loads exactly the 32 rows compute wave w uses. Otherwise (four
+    // query groups share each tile) the waves split every tile.
     auto instr = [&](int j) { return OWN ? wave * (G::KINSTR / 4) + j : j * 4 + wave; };
     // Flat mode: a lane's byte offset from the tile's first row is the same for every
     // tile, so a tile whose rows all exist only adds the tile offset.
@@ -210,7 +242,7 @@ __global__ __launch_bounds__(kThreads) void index_tokens_kernel(IndexTokensArgs 
                                                  (lds_void_t *)(stage + G::BYTES + 128 * wave), 4, 0, 0);
             }
         }
-        if constexpr (HI) {  // positions of this wave's rows (read back by this wave only)
+        if constexpr (HI) {  // positions of these rows (read back by the wave that computes them)
             if (lane < 32) tpos[st][32 * wave + lane] = col_pos(tc0 + 32 * wave + lane);
         }
     };
@@ -224,34 +256,37 @@ __global__ __launch_bounds__(kThreads) void index_tokens_kernel(IndexTokensArgs 
     // position; visibility only shrinks with the column, so skipped tiles form a suffix.
     int nvis = ntiles;
     if constexpr (!HI) nvis = maxp < c0 ? 0 : min(ntiles, (maxp - c0) / kKT + 1);
+    if (!SPLIT || producer) {
 #pragma unroll
-    for (int p = 0; p < G::NST - 1; ++p)
-        if (p < nvis) issue_tile(c0 + p * kKT, p);
+        for (int p = 0; p < G::NST - 1; ++p)
+            if (p < nvis) issue_tile(c0 + p * kKT, p);
+    }
     // the query and weight loads were issued before the ring DMA and so have landed once
     // at most the DMA instructions are pending; waiting here (no store is pending yet, so
     // the count is exact) lets the loop use them without a full drain of the ring
-    if (nvis >= 3) wait_vmcnt<3 * G::PER_WAVE>();
-    else if (nvis == 2) wait_vmcnt<2 * G::PER_WAVE>();
-    else if (nvis == 1) wait_vmcnt<G::PER_WAVE>();
-    else wait_vmcnt<0>();
+    if (!SPLIT) wait_tiles<G::PER_WAVE, G::NST - 1>(min(nvis, G::NST - 1));
 
-    // ---- one sub-tile of 32 rows: LDS operands -> MFMA accumulators
-    auto mfma_tile = [&](const unsigned char *tile, int row, f32x16(&acc)[HB]) {
+    // ---- one sub-tile of 32 rows: LDS operands (load_k), then MFMA accumulators (mma)
+    constexpr int NKV = FP8 ? KSTEPS / 2 : KSTEPS;  // 16-byte key fragments per lane
+    struct KFrag {
+        u32x4 v[NKV];
+    };
+    auto load_k = [&](const unsigned char *tile, int row, KFrag &kf) {
         const unsigned char *trow = tile + row * G::RB;
+#pragma unroll
+        for (int j = 0; j < NKV; ++j)  // bytes (D / 2 or D) * half + 16 j of the row
+            kf.v[j] = *reinterpret_cast<const u32x4 *>(trow + G::swz(row, NKV * half + j) * 16);
+    };
+    auto mma = [&](const KFrag &kf, f32x16(&acc)[HB]) {
 #pragma unroll
         for (int hb = 0; hb < HB; ++hb)
 #pragma unroll
             for (int r = 0; r < 16; ++r) acc[hb][r] = 0.0f;
-        // every LDS operand of the sub-tile is requested before the first MFMA
         if constexpr (FP8) {
-            u32x4 kv[KSTEPS / 2];
 #pragma unroll
-            for (int kk = 0; kk < KSTEPS / 2; ++kk)
-                kv[kk] = *reinterpret_cast<const u32x4 *>(trow + G::swz(row, (D / 32) * half + kk) * 16);
-#pragma unroll
-            for (int kk = 0; kk < KSTEPS / 2; ++kk) {
+            for (int kk = 0; kk < NKV; ++kk) {
                 bf16x8 f0, f1;
-                fp8x16_to_frags(kv[kk], f0, f1);
+                fp8x16_to_frags(kf.v[kk], f0, f1);
 #pragma unroll
                 for (int hb = 0; hb < HB; ++hb) {
                     acc[hb] = mfma32(aq[hb][2 * kk], f0, acc[hb]);
@@ -259,17 +294,18 @@ __global__ __launch_bounds__(kThreads) void index_tokens_kernel(IndexTokensArgs 
                 }
             }
         } else {
-            u32x4 kv[KSTEPS];
 #pragma unroll
-            for (int ks = 0; ks < KSTEPS; ++ks)  // bytes D*half + 16*ks
-                kv[ks] = *reinterpret_cast<const u32x4 *>(trow + G::swz(row, (D / 16) * half + ks) * 16);
-#pragma unroll
-            for (int ks = 0; ks < KSTEPS; ++ks) {
-                const bf16x8 f = __builtin_bit_cast(bf16x8, kv[ks]);
+            for (int ks = 0; ks < NKV; ++ks) {
+                const bf16x8 f = __builtin_bit_cast(bf16x8, kf.v[ks]);
 #pragma unroll
                 for (int hb = 0; hb < HB; ++hb) acc[hb] = mfma32(aq[hb][ks], f, acc[hb]);
             }
         }
+    };
+    auto mfma_tile = [&](const unsigned char *tile, int row, f32x16(&acc)[HB]) {
+        KFrag kf;
+        load_k(tile, row, kf);  // every LDS operand of the sub-tile is requested before the first MFMA
+        mma(kf, acc);
     };
 
     // ---- epilogue of one sub-tile: ReLU, head weights, head sum, scale, causal mask
@@ -322,15 +358,22 @@ __global__ __launch_bounds__(kThreads) void index_tokens_kernel(IndexTokensArgs 
     auto advance = [&](int it) {
         // this wave's DMA of tile `it` is complete once at most `ahead` later tiles'
         // instructions are pending (vector memory operations retire in issue order)
-        const int ahead = min(G::NST - 2, nvis - 1 - it);
-        if (ahead >= 2) wait_vmcnt<2 * G::PER_WAVE>();
-        else if (ahead == 1) wait_vmcnt<G::PER_WAVE>();
-        else wait_vmcnt<0>();
+        wait_tiles<G::PER_WAVE, G::NST - 2>(min(G::NST - 2, nvis - 1 - it));
         // OWN: this wave's rows of tile `it` landed and it has finished reading its rows of
         // tile it-1 (the stage refilled next). Shared tiles: every wave's part landed and
         // every wave is done with tile it-1.
         if constexpr (!OWN) __syncthreads();
         if (it + G::NST - 1 < nvis)
+            issue_tile(c0 + (it + G::NST - 1) * kKT, (it + G::NST - 1) % G::NST);
+    };
+
+    // SPLIT: tile `it` is in the ring once every producer's DMA of it landed (each waits
+    // for its own), and its stage may be refilled once every compute wave is done with
+    // tile it-1: one workgroup barrier (LDS ordering only) per tile covers both.
+    auto sync_tile = [&](int it) {
+        if (producer) wait_tiles<G::PER_WAVE, G::NST - 2>(min(G::NST - 2, nvis - 1 - it));
+        lds_barrier();
+        if (producer && it + G::NST - 1 < nvis)
             issue_tile(c0 + (it + G::NST - 1) * kKT, (it + G::NST - 1) % G::NST);
     };
 
@@ -353,18 +396,17 @@ __global__ __launch_bounds__(kThreads) void index_tokens_kernel(IndexTokensArgs 
             }
         }
     } else {
-        // (one query group per workgroup: every wave is active)
+        // (one query group per workgroup: every compute wave is active)
         // Software pipeline over this wave's 32 rows of each tile: the MFMAs of tile `it`
         // are issued before the epilogue of tile it-1 (accumulators alternate), so the
         // matrix core and the VALU work on different tiles at the same time. The scale
-        // and position of a tile are read while its stage is current (the refill at the
-        // top of the next iteration overwrites that stage).
+        // and position of a tile are read while its stage is current (the producers
+        // refill that stage after the next barrier).
         const int row = wave * 32 + l32;
         f32x16 acc0[HB], acc1[HB];
         int pcol = 0, ppos = -1;
         float psc = 0.0f;
         auto step = [&](int it, f32x16(&cur)[HB], const f32x16(&prev)[HB]) {
-            advance(it);
             const int st = it % G::NST;
             const unsigned char *tile = ring + st * G::STAGE;
             const float sc = FP8 ? reinterpret_cast<const float *>(tile + G::BYTES)[row] : 1.0f;
@@ -379,17 +421,21 @@ __global__ __launch_bounds__(kThreads) void index_tokens_kernel(IndexTokensArgs 
             psc = sc;
         };
         for (int it = 0; it < nvis; it += 2) {
-            step(it, acc0, acc1);
-            if (it + 1 < nvis) step(it + 1, acc1, acc0);
+            sync_tile(it);
+            if (!producer) step(it, acc0, acc1);
+            if (it + 1 < nvis) {
+                sync_tile(it + 1);
+                if (!producer) step(it + 1, acc1, acc0);
+            }
         }
-        if (nvis > 0) {
+        if (!producer && nvis > 0) {
             if (nvis & 1) epilogue(acc0, pcol, ppos, psc);
             else epilogue(acc1, pcol, ppos, psc);
         }
     }
     {  // tiles past every query's position: -inf
         constexpr int NQ = PRE ? 4 : QPG;
-        for (int e = nvis * kKT + tid; e < ntiles * kKT * NQ; e += kThreads) {
+        for (int e = nvis * kKT + tid; e < ntiles * kKT * NQ; e += NT) {
             // e runs over (query q, column offset) of the skipped tiles
             int q = e / (ntiles * kKT);
             int off = e % (ntiles * kKT);
@@ -404,7 +450,7 @@ __global__ __launch_bounds__(kThreads) void index_tokens_kernel(IndexTokensArgs 
         __syncthreads();
         if (active) {
             uint32_t *g = a.sel_hist + (int64_t)(b * T + grp) * kSelBins;
-            for (int i = tid; i < kSelBins; i += kThreads) {
+            for (int i = tid; i < kSelBins; i += NT) {
                 const uint32_t v = shist[i];
                 if (v) atomicAdd(&g[i], v);
             }
@@ -494,22 +540,34 @@ __global__ __launch_bounds__(128) void block_means_kernel(BlockMeansArgs a) {
     a.kbar[((int64_t)b * a.n_blocks + j) * D + d] = acc / (float)Bs;
 }
 
+int compute_units() {
+    int dev = 0, n = 0;
+    if (hipGetDevice(&dev) != hipSuccess || hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n < 1)
+        n = 256;
+    return n;
+}
+
 template <int D, bool FP8, int MODE, int HB, bool HI, bool PRE, bool HIST = false>
 hipError_t launch_tokens_t(const IndexTokensArgs &a, hipStream_t s) {
+    constexpr int NST = 4;  // one tile computed, three in flight (deeper rings measured no faster)
+    using G = Tile<D, FP8, NST>;
     const int QPG = MODE == ONEQ ? 1 : 32 / MODE;
     const int groups = (a.T + QPG - 1) / QPG;
     const int gy = PRE ? (groups + 3) / 4 : groups;
     const int max_chunks = (a.n_out + kKT - 1) / kKT;
-    int want = (512 + a.B * gy - 1) / (a.B * gy);
+    // SPLIT kernels (8 waves, 2 per SIMD): one workgroup per CU, every wave of a CU the
+    // same age, so no workgroup is starved by the oldest-first issue arbitration of an
+    // older one on the same CU; shared tiles (4 waves): two per CU
+    const int target = PRE ? 512 : compute_units();
+    int want = (target + a.B * gy - 1) / (a.B * gy);
     int chunks = want < 1 ? 1 : (want > max_chunks ? max_chunks : want);
     int chunk = (a.n_out + chunks - 1) / chunks;
     chunk = (chunk + kKT - 1) / kKT * kKT;
     chunks = (a.n_out + chunk - 1) / chunk;
     dim3 grid(chunks, gy, a.B);
-    using G = Tile<D, FP8>;
     const size_t lds = (size_t)G::NST * G::STAGE;
-    hipLaunchKernelGGL((index_tokens_kernel<D, FP8, MODE, HB, HI, PRE, HIST>), grid, dim3(kThreads), lds, s, a, groups,
-                       chunk);
+    hipLaunchKernelGGL((index_tokens_kernel<D, FP8, MODE, HB, HI, PRE, HIST, NST>), grid, dim3(PRE ? kThreads : 2 * kThreads), lds, s, a,
+                       groups, chunk);
     return hipGetLastError();
 }
 
