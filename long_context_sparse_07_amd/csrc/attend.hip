@@ -485,7 +485,7 @@ int attend_default_splits(const AttendArgs &a) {
     const int g = a.Hq / a.Hkv;
     const int HW = (g + 15) / 16;
     const long units = (long)a.L * a.B * a.T * a.Hkv;
-    const long target = HW == 4 ? 128 : 1024;
+    const long target = HW == 4 ? 256 : 1024;
     long s = (target + units - 1) / units;
     const long smax = (a.K + kRows - 1) / kRows;
     const long smin = (a.K + kMaxR - 1) / kMaxR;

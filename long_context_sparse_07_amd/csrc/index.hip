@@ -446,8 +446,9 @@ __global__ __launch_bounds__(PRE ? kThreads : 2 * kThreads) void index_tokens_ke
         }
     }
     if constexpr (HIST) {
-        lds_wait_all();  // the histogram adds above are inline asm: not tracked by the compiler
-        __syncthreads();
+        // the histogram adds above are inline asm (not tracked by the compiler); the LDS-only
+        // barrier does not wait for the score stores still in flight
+        lds_barrier();
         if (active) {
             uint32_t *g = a.sel_hist + (int64_t)(b * T + grp) * kSelBins;
             for (int i = tid; i < kSelBins; i += NT) {

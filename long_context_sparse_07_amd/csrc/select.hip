@@ -273,7 +273,7 @@ __device__ __forceinline__ void wave_hist_add(uint32_t *h, int d) {
 // bits over the low lo_bits bits (0 < lo_bits < 64). Returns the smallest composite
 // that still belongs to the group's top `need`: those are exactly the group elements
 // >= it.
-template <class Src>
+template <int NT, class Src>
 __device__ uint64_t radix_kth(const Src &src, uint32_t need, uint64_t pref, int lo_bits, uint32_t *h256,
                               uint32_t *scr) {
     int hi = lo_bits;
@@ -282,11 +282,11 @@ __device__ uint64_t radix_kth(const Src &src, uint32_t need, uint64_t pref, int 
         const int w = hi < 8 ? hi : 8;
         const int sh = hi - w;
         const uint32_t dmask = (1u << w) - 1;
-        for (int i = threadIdx.x; i < 256; i += kRT) h256[i] = 0;
+        for (int i = threadIdx.x; i < 256; i += NT) h256[i] = 0;
         __syncthreads();
         const int n = src.size();
-        const int nr = (n + kRT - 1) / kRT * kRT;  // every lane takes part in the wave merge
-        for (int i = threadIdx.x; i < nr; i += kRT) {
+        const int nr = (n + NT - 1) / NT * NT;  // every lane takes part in the wave merge
+        for (int i = threadIdx.x; i < nr; i += NT) {
             uint64_t c = 0;
             const bool ok = i < n && src.get(i, c) && (c >> hi) == (pref >> hi);
             wave_hist_add(h256, ok ? (int)((c >> sh) & dmask) : -1);
@@ -431,6 +431,42 @@ __global__ __launch_bounds__(kHT) void select_filter_kernel(SelectArgs a, Ws w, 
     }
 }
 
+// Copy n 32-bit words global -> LDS with several loads per thread in flight (a plain
+// element loop would wait for each load before its LDS store): U 16-byte loads when
+// both pointers are 16-byte aligned, else 4 U word loads. (Native vector types: arrays
+// of the HIP vector classes end up in scratch memory.)
+template <int NT, int U>
+__device__ void copy_words_to_lds(const uint32_t *src, uint32_t *dst, int n) {
+    const int tid = (int)threadIdx.x;
+    if ((((uintptr_t)src | (uintptr_t)dst) & 15) == 0) {
+        const int n4 = n >> 2;
+        const u32x4 *s4 = reinterpret_cast<const u32x4 *>(src);
+        u32x4 *d4 = reinterpret_cast<u32x4 *>(dst);
+        for (int base = 0; base < n4; base += NT * U) {
+            u32x4 v[U];
+#pragma unroll
+            for (int u = 0; u < U; ++u) {
+                const int i = min(base + u * NT + tid, n4 - 1);
+                v[u] = s4[i];
+            }
+#pragma unroll
+            for (int u = 0; u < U; ++u)
+                if (base + u * NT + tid < n4) d4[base + u * NT + tid] = v[u];
+        }
+        for (int i = 4 * n4 + tid; i < n; i += NT) dst[i] = src[i];
+    } else {
+        constexpr int V = 4 * U;
+        for (int base = 0; base < n; base += NT * V) {
+            uint32_t v[V];
+#pragma unroll
+            for (int u = 0; u < V; ++u) v[u] = src[min(base + u * NT + tid, n - 1)];
+#pragma unroll
+            for (int u = 0; u < V; ++u)
+                if (base + u * NT + tid < n) dst[base + u * NT + tid] = v[u];
+        }
+    }
+}
+
 // ----------------------------------------------------------------------------- resolve
 // One workgroup per row. Ties are ranked from LDS when they fit (kTieLds), else read
 // from the workspace list. LWORDS > 0: the row's bitmap (LWORDS words) is loaded into LDS
@@ -474,11 +510,8 @@ __global__ __launch_bounds__(kRT) void select_resolve_kernel(SelectArgs a, Ws w,
         if (tid < tcap) tc0 = gtcols[tid];
         if (tid + kRT < tcap) tc1 = gtcols[tid + kRT];
     }
-    for (int i = tid; i < lwords; i += kRT) lbits[i] = gbits[i];
+    if (lwords) copy_words_to_lds<kRT, 2>(gbits, lbits, lwords);
     const BinPick bp = pick_bin<kRT, 2>(hv, m, scr);  // its barriers follow every thread's reads
-    g1[kSelBins - 1 - 2 * tid] = 0;
-    g1[kSelBins - 2 - 2 * tid] = 0;
-    if (tid < kCtr) gctr[tid] = 0;
     const int b1 = bp.bin;
 
     auto mark = [&](int col) {
@@ -547,7 +580,7 @@ __global__ __launch_bounds__(kRT) void select_resolve_kernel(SelectArgs a, Ws w,
                     __syncthreads();
                     thr = ((uint64_t)scr[21] << 32) | scr[20];
                 } else {
-                    thr = radix_kth(ArrSrc{tl, (int)nl}, need2, pre, kGrpShift, h256, scr);
+                    thr = radix_kth<kRT>(ArrSrc{tl, (int)nl}, need2, pre, kGrpShift, h256, scr);
                 }
             }
             for (uint32_t i = tid; i < nl; i += kRT)
@@ -556,7 +589,7 @@ __global__ __launch_bounds__(kRT) void select_resolve_kernel(SelectArgs a, Ws w,
             // the tie list overflowed: exact select inside bin b1 over the whole row
             const RowSrc rs{&a, &r};
             const uint64_t pre = (uint64_t)b1 << kB1Shift;
-            thr = radix_kth(rs, need1, pre, kB1Shift, h256, scr);
+            thr = radix_kth<kRT>(rs, need1, pre, kB1Shift, h256, scr);
             for (int col = tid; col < a.n_cols; col += kRT) {
                 uint64_t c;
                 if (candidate_x(a, r, col, r.sc[col], c) && (c >> kB1Shift) == (uint64_t)b1 && c >= thr) mark(col);
@@ -625,6 +658,10 @@ __global__ __launch_bounds__(kRT) void select_resolve_kernel(SelectArgs a, Ws w,
     for (int j = tid; j < nwin; j += kRT)
         if (wbase + j < a.K) dst[wbase + j] = r.f_win_lo + j;
     for (int i = wbase + nwin + tid; i < a.K; i += kRT) dst[i] = -1;
+    // the histogram and the counters are left at zero (last: a barrier would wait for these stores)
+    g1[kSelBins - 1 - 2 * tid] = 0;
+    g1[kSelBins - 2 - 2 * tid] = 0;
+    if (tid < kCtr) gctr[tid] = 0;
 }
 
 __global__ void clear_kernel(uint4 *p, size_t n16, uint8_t *tail, size_t ntail) {
