@@ -41,6 +41,8 @@ def parse():
     ap.add_argument("--no-graph", action="store_true", help="headline from plain stream launches")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--profile-only", action="store_true", help="few plain steps, no graphs (for rocprofv3)")
+    ap.add_argument("--no-workloads", action="store_true",
+                    help="skip the other configurations' step times (extra.workloads)")
     ap.add_argument("--calib-copy", action="store_true",
                     help="with --profile-only: also run one elementwise add of known traffic (counter calibration)")
     return ap.parse_args()
@@ -91,6 +93,152 @@ def pmc_traffic(index_bytes_per_launch):
         return rec["traffic_bytes_per_launch"]
     except Exception:
         return None
+
+
+def measure_workloads(steps=50):
+    """Step times of the other configurations (each the parity workload of its name),
+    reported beside the headline: HIP-graph replay of one captured step, inputs resident.
+      c1 tiny decode: us/step.  c3 hierarchical 1M decode: us/step, and the flat path
+      (index + select over all 1M keys) on the same inputs for the HI/flat ratios.
+      c4 chunked prefill: tokens/s, and the indexer's MFMA utilisation (bf16 peak).
+      c5 cross-layer decode (4 layers, one selection): us/step, and the same work with
+      the selection recomputed for every layer."""
+    import numpy as np
+    import torch
+    import long_context_sparse_07_amd as L
+    from synth import config, make_inputs
+
+    def bf16(a):
+        return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).view(torch.bfloat16).cuda()
+
+    def upload(inp, cfg):
+        d = {"qI": bf16(inp["qI"]), "w": torch.from_numpy(inp["w"]).cuda(),
+             "ctx": torch.from_numpy(inp["ctx_len"]).cuda(), "q": bf16(inp["q"]), "k": bf16(inp["k"]),
+             "v": bf16(inp["v"]) if inp["v"] is not None else None}
+        if cfg.k_fp8:
+            d["kI"] = torch.from_numpy(inp["kI"]).cuda().view(torch.float8_e4m3fn)
+            d["ks"] = torch.from_numpy(inp["kI_scale"]).cuda()
+        else:
+            d["kI"], d["ks"] = bf16(inp["kI"]), None
+        return d
+
+    def graph_us(fn):
+        fn()  # allocates and caches workspaces, leaves them clean
+        torch.cuda.synchronize()
+        side = torch.cuda.Stream()
+        side.wait_stream(torch.cuda.current_stream())
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.stream(side):
+            fn()
+            torch.cuda.synchronize()
+            with torch.cuda.graph(g, stream=side):
+                fn()
+        torch.cuda.current_stream().wait_stream(side)
+        torch.cuda.synchronize()
+        for _ in range(5):
+            g.replay()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(steps):
+            g.replay()
+        e1.record()
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / steps * 1e3
+
+    res = {}
+
+    def run(name, body):
+        try:
+            res[name] = body()
+        except Exception as e:  # a secondary workload never hides the headline
+            res[name] = {"error": f"{type(e).__name__}: {e}"}
+        torch.cuda.empty_cache()
+
+    def flat_step(cfg, d, sc, idx, out, lse, layers_out=None):
+        def fn():
+            L.lsa_index_select(d["qI"], d["w"], d["kI"], cfg.K, cfg.S, cfg.W, k_scale=d["ks"], ctx_len=d["ctx"],
+                               scores=sc, idx=idx)
+            L.lsa_attend(d["q"], d["k"], d["v"], idx, cfg.tau, out=out, lse=lse)
+        return fn
+
+    def c_flat(cid):
+        cfg = config(cid)
+        d = upload(make_inputs(cfg), cfg)
+        B, T = cfg.B, cfg.T
+        sc = torch.empty((B, T, cfg.N), dtype=torch.float32, device="cuda")
+        idx = torch.empty((B, T, cfg.K), dtype=torch.int32, device="cuda")
+        out = torch.empty((cfg.layers, B, T, cfg.Hq, cfg.d_v), dtype=torch.bfloat16, device="cuda")
+        lse = torch.empty((cfg.layers, B, T, cfg.Hq), dtype=torch.float32, device="cuda")
+        return cfg, d, sc, idx, out, lse
+
+    def w1():
+        cfg, d, sc, idx, out, lse = c_flat(1)
+        return {"workload": "c1 tiny decode (B=1, N=4096, T=8, 4x64 bf16 indexer, 16 heads MQA d=128, K=512)",
+                "us_per_step": graph_us(flat_step(cfg, d, sc, idx, out, lse))}
+
+    def w4():
+        cfg, d, sc, idx, out, lse = c_flat(4)
+        us = graph_us(flat_step(cfg, d, sc, idx, out, lse))
+        us_index = graph_us(lambda: L.lsa_index(d["qI"], d["w"], d["kI"], k_scale=d["ks"], ctx_len=d["ctx"], scores=sc))
+        p0 = cfg.N - cfg.T
+        pairs = sum(p0 + t + 1 for t in range(cfg.T))
+        flops = 2.0 * pairs * cfg.H_I * cfg.D_I
+        return {"workload": "c4 chunked prefill (4096 queries after 256K, 64x128 fp8 indexer, GQA 64/8 d=128, K=2048)",
+                "us_per_step": us, "prefill_tokens_per_s": cfg.B * cfg.T / (us * 1e-6), "us_index": us_index,
+                "index_tflops": flops / (us_index * 1e-6) / 1e12,
+                "index_mfma_frac_of_bf16_peak": flops / (us_index * 1e-6) / 2.5e15}
+
+    def w5():
+        cfg, d, sc, idx, out, lse = c_flat(5)
+        us = graph_us(flat_step(cfg, d, sc, idx, out, lse))
+        out1 = torch.empty((1,) + tuple(out.shape[1:]), dtype=out.dtype, device="cuda")
+        lse1 = torch.empty((1,) + tuple(lse.shape[1:]), dtype=lse.dtype, device="cuda")
+
+        def recompute():
+            for l in range(cfg.layers):
+                L.lsa_index_select(d["qI"], d["w"], d["kI"], cfg.K, cfg.S, cfg.W, k_scale=d["ks"], ctx_len=d["ctx"],
+                                   scores=sc, idx=idx)
+                L.lsa_attend(d["q"][l:l + 1], d["k"][l:l + 1], d["v"][l:l + 1], idx, cfg.tau, out=out1, lse=lse1)
+        us_rec = graph_us(recompute)
+        return {"workload": "c5 cross-layer decode (B=16, N=64K, 4 layers sharing one selection, 32x128 fp8 indexer, "
+                            "GQA 32/4 d=128, K=2048)",
+                "us_per_step": us, "us_per_step_selection_per_layer": us_rec, "cli_speedup": us_rec / us}
+
+    def w3():
+        cfg = config(3)
+        d = upload(make_inputs(cfg), cfg)
+        B, T = cfg.B, cfg.T
+        nb = cfg.N // cfg.Bs
+        kbar = L.lsa_block_means(d["kI"], cfg.Bs, k_scale=d["ks"])  # maintained once per block, not per step
+        cs = torch.empty((B, T, nb), dtype=torch.float32, device="cuda")
+        kept = torch.empty((B, T, cfg.n_keep), dtype=torch.int32, device="cuda")
+        fs = torch.empty((B, T, cfg.n_keep * cfg.Bs), dtype=torch.float32, device="cuda")
+        idx = torch.empty((B, T, cfg.K), dtype=torch.int32, device="cuda")
+        out = torch.empty((1, B, T, cfg.Hq, cfg.d_v), dtype=torch.bfloat16, device="cuda")
+        lse = torch.empty((1, B, T, cfg.Hq), dtype=torch.float32, device="cuda")
+
+        def hi():
+            L.lsa_index(d["qI"], d["w"], kbar, mode=L.LSA_INDEX_BLOCKS, N=cfg.N, ctx_len=d["ctx"],
+                        block_size=cfg.Bs, sink=cfg.S, window=cfg.W, scores=cs)
+            L.lsa_select(cs, cfg.n_keep, 0, 0, causal=False, idx=kept)
+            L.lsa_index_select(d["qI"], d["w"], d["kI"], cfg.K, cfg.S, cfg.W, k_scale=d["ks"], ctx_len=d["ctx"],
+                               kept=kept, block_size=cfg.Bs, scores=fs, idx=idx)
+            L.lsa_attend(d["q"], d["k"], d["v"], idx, cfg.tau, out=out, lse=lse)
+        us = graph_us(hi)
+        sc = torch.empty((B, T, cfg.N), dtype=torch.float32, device="cuda")
+        us_flat = graph_us(flat_step(cfg, d, sc, idx, out, lse))
+        kb = 2  # bf16 indexer keys
+        hi_bytes = B * nb * cfg.D_I * 4 + B * T * cfg.n_keep * cfg.Bs * cfg.D_I * kb + B * T * cfg.K * cfg.d_qk * 2
+        flat_bytes = B * cfg.N * cfg.D_I * kb + B * T * cfg.K * cfg.d_qk * 2
+        return {"workload": "c3 hierarchical decode (B=1, N=1M, T=4, 4x64 bf16 indexer, blocks of 64, keep 256, K=2048)",
+                "us_per_step": us, "steps_per_s": 1e6 / us, "us_per_step_flat": us_flat,
+                "hi_over_flat_time": us / us_flat, "hi_over_flat_bytes": hi_bytes / flat_bytes}
+
+    for name, body in (("c1", w1), ("c3", w3), ("c4", w4), ("c5", w5)):
+        run(name, body)
+        print(f"[bench] workload {name}: {res[name]}", file=sys.stderr, flush=True)
+    return res
 
 
 def main():
@@ -260,6 +408,8 @@ def main():
                   "ms_index": ms_index, "ms_select": ms_select, "ms_attend": ms_attend,
                   "index_bytes_per_launch": idx_b, "gather_bytes": gat_b},
     }
+    if not args.no_workloads:
+        res["extra"]["workloads"] = measure_workloads()
     if not args.no_cpu_baseline:
         res["cpu_baseline"] = cpu_baseline(inp, cfg)
     print(json.dumps(res))
