@@ -3,7 +3,8 @@
 One step = the whole hot path on one batch: lsa_index (indexer sweep over the fp8
 key cache, which also primes the selection workspace) -> lsa_select (sink + window +
 top-k fill) -> lsa_attend (MLA sparse attention over the 2048 selected rows), for the
-128K-context decode workload:
+128K-context decode workload (the last two also as the one chained call
+lsa_select_attend, whose attention kernel finishes the selection; both are timed):
 B=8 sequences, N=131072 cached tokens each, one query token, indexer 64 heads x 128
 (fp8-e4m3 keys + per-token fp32 scale), MLA 64 heads over 576-wide latent rows
 (V = first 512 columns), K=2048 with sink 64 and window 512.
@@ -41,6 +42,7 @@ def parse():
     ap.add_argument("--no-graph", action="store_true", help="headline from plain stream launches")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--profile-only", action="store_true", help="few plain steps, no graphs (for rocprofv3)")
+    ap.add_argument("--fused", action="store_true", help="with --profile-only: the lsa_select_attend chain")
     ap.add_argument("--no-workloads", action="store_true",
                     help="skip the other configurations' step times (extra.workloads)")
     ap.add_argument("--calib-copy", action="store_true",
@@ -306,10 +308,19 @@ def main():
     def c_attend(r):
         L._check("lsa_attend", lib.lsa_attend(ctypes.byref(descs[r][2]), ws_att.data_ptr(), ws_att.numel(), sptr))
 
+    def c_fused(r):
+        L._check("lsa_select_attend", lib.lsa_select_attend(ctypes.byref(descs[r][1]), ctypes.byref(descs[r][2]),
+                                                            ws_sel.data_ptr(), ws_sel.numel(), ws_att.data_ptr(),
+                                                            ws_att.numel(), sptr))
+
     def step(r):
         c_index(r)
         c_select(r)
         c_attend(r)
+
+    def step_fused(r):
+        c_index(r)
+        c_fused(r)
 
     # the first call clears the select workspace; every later call (same shape) finds it
     # clean, since each selection leaves it so
@@ -331,7 +342,7 @@ def main():
         return e0.elapsed_time(e1) / n
 
     if args.profile_only:
-        ms = timed(step, args.steps, args.warmup)
+        ms = timed(step_fused if args.fused else step, args.steps, args.warmup)
         if args.calib_copy:
             # a plain elementwise kernel of known traffic: c = a + b reads 2 GiB, writes 1 GiB
             # (the inputs are 8x the MALL, so they come from HBM)
@@ -346,6 +357,7 @@ def main():
 
     # plain stream launches
     ms_plain = timed(step, args.steps, args.warmup)
+    ms_plain_fused = timed(step_fused, args.steps, args.warmup)
     # per-call times (live, same stream, same replica rotation). A primed selection
     # consumes what the indexer left, so it is timed as (index + select) - index; the
     # workspace is cleared after the indexer-only loop, which leaves it unbalanced.
@@ -354,29 +366,40 @@ def main():
     ms_index_select = timed(lambda r: (c_index(r), c_select(r)), args.steps, args.warmup)
     ms_select = ms_index_select - ms_index
     ms_attend = timed(c_attend, args.steps, args.warmup)
+    ms_select_attend = timed(step_fused, args.steps, args.warmup) - ms_index
 
     # HIP graphs: one captured step per replica
-    ms_graph = None
+    ms_graph = ms_graph_fused = None
     if not args.no_graph:
-        graphs = []
+        graphs, graphs_fused = [], []
         side = torch.cuda.Stream()
         side.wait_stream(stream)
         with torch.cuda.stream(side):
+            gptr = ctypes.c_void_p(side.cuda_stream)
             for r in range(R):
                 g = torch.cuda.CUDAGraph()
-                gptr = ctypes.c_void_p(side.cuda_stream)
                 with torch.cuda.graph(g, stream=side):
                     lib.lsa_index(ctypes.byref(descs[r][0]), gptr)
                     lib.lsa_select(ctypes.byref(descs[r][1]), ws_sel.data_ptr(), ws_sel.numel(), gptr)
                     lib.lsa_attend(ctypes.byref(descs[r][2]), ws_att.data_ptr(), ws_att.numel(), gptr)
                 graphs.append(g)
+                g = torch.cuda.CUDAGraph()
+                with torch.cuda.graph(g, stream=side):
+                    lib.lsa_index(ctypes.byref(descs[r][0]), gptr)
+                    lib.lsa_select_attend(ctypes.byref(descs[r][1]), ctypes.byref(descs[r][2]), ws_sel.data_ptr(),
+                                          ws_sel.numel(), ws_att.data_ptr(), ws_att.numel(), gptr)
+                graphs_fused.append(g)
         stream.wait_stream(side)
         torch.cuda.synchronize()
         ms_graph = timed(lambda r: graphs[r].replay(), args.steps, args.warmup)
+        ms_graph_fused = timed(lambda r: graphs_fused[r].replay(), args.steps, args.warmup)
 
-    # headline: the faster of the two ways of launching the same step (both are reported)
-    use_graph = ms_graph is not None and ms_graph < ms_plain
-    ms = ms_graph if use_graph else ms_plain
+    # headline: the fastest of the ways of running the same step (all are reported)
+    ways = {("stream launches", "separate"): ms_plain, ("stream launches", "fused"): ms_plain_fused}
+    if ms_graph is not None:
+        ways[("hip graph replay", "separate")] = ms_graph
+        ways[("hip graph replay", "fused")] = ms_graph_fused
+    (launch, path), ms = min(ways.items(), key=lambda kv: kv[1])
     idx_b, gat_b, small_b = algorithmic_bytes(cfg)
     step_bytes = idx_b + gat_b + small_b
     achieved_index = idx_b / (ms_index * 1e-3) / 1e9
@@ -397,7 +420,8 @@ def main():
         "config": {"workload": "c2 LSA decode: B=8, 128K context, T=1, indexer 64x128 fp8-e4m3 + fp32 scale, "
                                "MLA 64 heads 576/512 bf16, K=2048 (sink 64, window 512)",
                    "batch": B, "context": N, "query_tokens": T, "topk": cfg.K,
-                   "launch": "hip graph replay" if use_graph else "stream launches",
+                   "launch": launch,
+                   "calls": "lsa_index, lsa_select_attend" if path == "fused" else "lsa_index, lsa_select, lsa_attend",
                    "input_replicas": R},
         "roofline": {"bound": "hbm", "kernel": "index_tokens_kernel (lsa_index, fp8 keys)",
                      "achieved": achieved_index, "peak": PEAK_HBM_GBS, "unit": "GB/s",
@@ -405,7 +429,9 @@ def main():
         "extra": {"step_algorithmic_bytes": step_bytes, "step_hbm_gbs": step_bytes / (ms * 1e-3) / 1e9,
                   "step_frac_of_peak": step_bytes / (ms * 1e-3) / 1e9 / PEAK_HBM_GBS,
                   "ms_per_step_plain": ms_plain, "ms_per_step_graph": ms_graph,
+                  "ms_per_step_plain_fused": ms_plain_fused, "ms_per_step_graph_fused": ms_graph_fused,
                   "ms_index": ms_index, "ms_select": ms_select, "ms_attend": ms_attend,
+                  "ms_select_attend_fused": ms_select_attend,
                   "index_bytes_per_launch": idx_b, "gather_bytes": gat_b},
     }
     if not args.no_workloads:

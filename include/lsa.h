@@ -249,6 +249,26 @@ typedef struct lsa_attend_desc {
 size_t lsa_attend_workspace_bytes(const lsa_attend_desc *desc);
 int32_t lsa_attend(const lsa_attend_desc *desc, void *workspace, size_t workspace_bytes, void *stream);
 
+/*
+ * lsa_select_attend — lsa_select(sel) followed by lsa_attend(att) on the positions it
+ * selects, as one chain: the attention workgroups finish the selection themselves
+ * (each the part of the index list it attends over), so the index list does not make
+ * a round trip through memory between the two. Same pages as lsa_select and
+ * lsa_attend (SI budget of sink, window and top-k fill; attention over the selected
+ * tokens only).
+ * Results: sel->idx and att->out / att->lse are bit-identical to those of the two
+ * calls made separately with the same descriptors (and the same n_splits).
+ * Requirements: everything lsa_select and lsa_attend require, and: no kept map
+ * (sel->kept == NULL); sel and att agree on B, T, N and K; att->idx is NULL or
+ * equal to sel->idx (it is ignored: the positions come from the selection).
+ * Workspaces: select_ws as for lsa_select (workspace_state applies as there) and
+ * attend_ws as for lsa_attend, with their own *_workspace_bytes() sizes; after a
+ * successful call select_ws is clean, as after lsa_select.
+ * Errors as for the two calls; LSA_E_UNSUPPORTED for a kept map.
+ */
+int32_t lsa_select_attend(const lsa_select_desc *sel, const lsa_attend_desc *att, void *select_ws,
+                          size_t select_ws_bytes, void *attend_ws, size_t attend_ws_bytes, void *stream);
+
 /* Zero-fill `bytes` of device memory at `ptr` with a fill kernel (for workspaces). */
 int32_t lsa_workspace_clear(void *ptr, size_t bytes, void *stream);
 

@@ -84,6 +84,9 @@ def lib():
         L.lsa_select.restype = c_int32
         L.lsa_attend.argtypes = [POINTER(AttendDesc), c_void_p, c_size_t, c_void_p]
         L.lsa_attend.restype = c_int32
+        L.lsa_select_attend.argtypes = [POINTER(SelectDesc), POINTER(AttendDesc), c_void_p, c_size_t, c_void_p,
+                                        c_size_t, c_void_p]
+        L.lsa_select_attend.restype = c_int32
         L.lsa_select_workspace_bytes.argtypes = [POINTER(SelectDesc)]
         L.lsa_select_workspace_bytes.restype = c_size_t
         L.lsa_attend_workspace_bytes.argtypes = [POINTER(AttendDesc)]
@@ -289,3 +292,66 @@ def lsa_attend(q, k, v, idx, softmax_scale, *, out=None, lse=None, out_dtype=Non
     ws = workspace if workspace is not None else (_workspace("attend", need, q.device)[0] if need else None)
     _check("lsa_attend", lib().lsa_attend(ctypes.byref(d), _ptr(ws), 0 if ws is None else ws.numel(), s))
     return out, lse
+
+
+def _attend_outputs(q, v, out, lse, out_dtype, with_lse):
+    import torch
+    L, B, T, Hq, dqk = q.shape
+    dv = 512 if v is None else v.shape[-1]
+    if out is None:
+        out = torch.empty((L, B, T, Hq, dv), dtype=out_dtype or torch.bfloat16, device=q.device)
+    if lse is None and with_lse:
+        lse = torch.empty((L, B, T, Hq), dtype=torch.float32, device=q.device)
+    return out, lse
+
+
+def _select_attend_call(ds, da, sel_ent, q, stream):
+    need_a = lib().lsa_attend_workspace_bytes(ctypes.byref(da))
+    wa = _workspace("attend", need_a, q.device)[0] if need_a else None
+    ws = sel_ent[0]
+    _check("lsa_select_attend", lib().lsa_select_attend(ctypes.byref(ds), ctypes.byref(da), ws.data_ptr(), ws.numel(),
+                                                        _ptr(wa), 0 if wa is None else wa.numel(), _stream(stream)))
+    sel_ent[1] = True
+
+
+def lsa_select_attend(scores, K, sink, window, q, k, v, softmax_scale, *, N=None, ctx_len=None, causal=True,
+                      idx=None, out=None, lse=None, out_dtype=None, with_lse=True, n_splits=0, stream=None):
+    """lsa_select on scores, then lsa_attend on the positions it selects, as one chain
+    (the attention kernel finishes the selection). Same arguments and results as the
+    two calls; no kept map. Returns (idx, out, lse)."""
+    import torch
+    B, T, n_cols = scores.shape
+    N = n_cols if N is None else N
+    if idx is None:
+        idx = torch.empty((B, T, K), dtype=torch.int32, device=scores.device)
+    out, lse = _attend_outputs(q, v, out, lse, out_dtype, with_lse)
+    ds = _select_desc(scores, K, sink, window, N, ctx_len, None, 0, causal, idx)
+    da = _attend_desc(q, k, v, idx, softmax_scale, out, lse, v is None, n_splits)
+    ent = _workspace("select", lib().lsa_select_workspace_bytes(ctypes.byref(ds)), scores.device, (B, T, n_cols))
+    ds.workspace_state = LSA_WS_CLEAN if ent[1] else LSA_WS_UNKNOWN
+    _select_attend_call(ds, da, ent, q, stream)
+    return idx, out, lse
+
+
+def lsa_index_select_attend(qI, w, kI, K, sink, window, q, k, v, softmax_scale, *, k_scale=None, ctx_len=None,
+                            scores=None, idx=None, out=None, lse=None, out_dtype=None, with_lse=True, n_splits=0,
+                            stream=None):
+    """The whole flat decode path: lsa_index (priming the selection workspace), then
+    lsa_select_attend on its scores. Returns (scores, idx, out, lse)."""
+    import torch
+    B, T = qI.shape[0], qI.shape[1]
+    N = kI.shape[1]
+    if scores is None:
+        scores = torch.empty((B, T, N), dtype=torch.float32, device=qI.device)
+    if idx is None:
+        idx = torch.empty((B, T, K), dtype=torch.int32, device=qI.device)
+    out, lse = _attend_outputs(q, v, out, lse, out_dtype, with_lse)
+    ds = _select_desc(scores, K, sink, window, N, ctx_len, None, 0, True, idx)
+    da = _attend_desc(q, k, v, idx, softmax_scale, out, lse, v is None, n_splits)
+    ent = _workspace("select", lib().lsa_select_workspace_bytes(ctypes.byref(ds)), qI.device, (B, T, N))
+    lsa_index(qI, w, kI, k_scale=k_scale, ctx_len=ctx_len, N=N, sink=sink, window=window, scores=scores,
+              select_ws=ent[0], select_ws_state=LSA_WS_CLEAN if ent[1] else LSA_WS_UNKNOWN, stream=stream)
+    ent[1] = False
+    ds.workspace_state = LSA_WS_PRIMED
+    _select_attend_call(ds, da, ent, q, stream)
+    return scores, idx, out, lse

@@ -352,6 +352,37 @@ int32_t lsa_attend(const lsa_attend_desc *d, void *ws, size_t ws_bytes, void *st
     return hip_status(lsa::launch_attend(a, ws, reinterpret_cast<hipStream_t>(stream)), "lsa_attend");
 }
 
+int32_t lsa_select_attend(const lsa_select_desc *sd, const lsa_attend_desc *ad, void *sel_ws, size_t sel_ws_bytes,
+                          void *att_ws, size_t att_ws_bytes, void *stream) {
+    lsa::SelectArgs sa;
+    int32_t rc = select_check(sd, sa);
+    if (rc != LSA_OK) return rc;
+    lsa::AttendArgs a;
+    rc = attend_check(ad, a);
+    if (rc != LSA_OK) return rc;
+    if (sd->kept) return fail(LSA_E_UNSUPPORTED, "lsa_select_attend: no kept map (call lsa_select, then lsa_attend)");
+    if (sd->B != ad->B || sd->T != ad->T || sd->N != ad->N || sd->K != ad->K)
+        return fail(LSA_E_SHAPE, "lsa_select_attend: selection and attention disagree on B, T, N or K");
+    if (ad->idx && ad->idx != sd->idx) return fail(LSA_E_SHAPE, "lsa_select_attend: att->idx must be NULL or sel->idx");
+    if (!sd->scores || !sd->idx || !ad->q || !ad->k || !ad->v || !ad->out)
+        return fail(LSA_E_NULL, "lsa_select_attend: scores, idx, q, k, v, out are required");
+    if (!aligned4(sd->scores) || !aligned4(sd->idx) || !aligned16(ad->q) || !aligned16(ad->k) || !aligned16(ad->v) ||
+        !aligned16(ad->out) || (ad->lse && !aligned4(ad->lse)))
+        return fail(LSA_E_ALIGN, "lsa_select_attend: misaligned scores, idx, q, k, v, out or lse");
+    const size_t sneed = lsa::select_workspace_bytes(sa.B * sa.T, sa.n_cols, false);
+    if (!sel_ws || sel_ws_bytes < sneed)
+        return fail(LSA_E_WORKSPACE, "lsa_select_attend: selection workspace of %zu bytes needed, %zu given", sneed,
+                    sel_ws_bytes);
+    const size_t aneed = lsa::attend_workspace_bytes(a);
+    if (aneed && (!att_ws || att_ws_bytes < aneed))
+        return fail(LSA_E_WORKSPACE, "lsa_select_attend: attention workspace of %zu bytes needed, %zu given", aneed,
+                    att_ws_bytes);
+    if ((reinterpret_cast<uintptr_t>(sel_ws) & 255u) != 0 || (aneed && (reinterpret_cast<uintptr_t>(att_ws) & 255u) != 0))
+        return fail(LSA_E_ALIGN, "lsa_select_attend: workspaces must be 256-byte aligned");
+    return hip_status(lsa::launch_select_attend(sa, sel_ws, a, att_ws, reinterpret_cast<hipStream_t>(stream)),
+                      "lsa_select_attend");
+}
+
 int32_t lsa_workspace_clear(void *ptr, size_t bytes, void *stream) {
     if (bytes == 0) return LSA_OK;
     if (!ptr) return fail(LSA_E_NULL, "lsa_workspace_clear: ptr is NULL");

@@ -18,8 +18,13 @@
 //     transpose reads (ds_read_b64_tr_b16).
 // Splits write partials (o / l as bf16 rows, m and l in fp32) that a second kernel
 // merges in split order.
-#include "common.cuh"
-#include "kernels.h"
+//
+// Fused selection: a workgroup can also resolve its own split of the selection (the
+// selection's last pass, for flat rows) before it gathers: the LDS tile ring is free
+// then and holds the pass's working set, and the positions land straight in the LDS
+// position list, with no kernel boundary and no round trip of the index list through
+// memory in between.
+#include "select_core.cuh"
 
 namespace lsa {
 namespace {
@@ -48,6 +53,16 @@ __device__ __forceinline__ void wait_vmcnt() {
 // Physical chunk slot (0..3) of logical chunk j of row r inside a block.
 __device__ __forceinline__ int slot(int j, int r) { return j ^ ((r >> 2) & 3); }
 
+// Fused selection resolve: the selection's arguments and workspace, and the share of the
+// tile ring its working set takes (tie entries held in LDS, the row bitmap in LDS or not).
+struct FuseArgs {
+    SelectArgs sa;
+    sel::Ws w;
+    int tl;
+    int pw_log;
+    int bits_lds;
+};
+
 template <int DQK, int DV, int HW, bool MLA, bool OUTF32>
 struct AttTile {
     static constexpr int NT = 64 * HW;
@@ -68,8 +83,8 @@ struct AttTile {
     static_assert(!MLA || DV == 512, "MLA values are the first 512 columns (16 blocks)");
 };
 
-template <int DQK, int DV, int HW, bool MLA, bool OUTF32>
-__global__ __launch_bounds__(64 * HW) void attend_kernel(AttendArgs a, uint16_t *po, float *pml, int R) {
+template <int DQK, int DV, int HW, bool MLA, bool OUTF32, bool FUSED>
+__global__ __launch_bounds__(64 * HW) void attend_kernel(AttendArgs a, uint16_t *po, float *pml, int R, FuseArgs f) {
     using G = AttTile<DQK, DV, HW, MLA, OUTF32>;
     constexpr int NT = G::NT;
     constexpr int KSQ = DQK / 32;
@@ -93,7 +108,33 @@ __global__ __launch_bounds__(64 * HW) void attend_kernel(AttendArgs a, uint16_t 
     const int nsplit = gridDim.x;
     const int ntile = (nrows + kRows - 1) / kRows;
 
-    const int32_t *idxrow = a.idx + ((int64_t)b * T + t) * K + r0;
+    const int64_t selrow = (int64_t)b * T + t;
+    // the workgroups sharing a selection row: splits x KV heads x layers
+    const int nslices = nsplit * Hkv * a.L, slice = split + nsplit * (kvh + Hkv * layer);
+    if constexpr (FUSED) {
+        // resolve rows r0 .. r0 + nrows - 1 of the selection into the position list;
+        // its working set lives in the tile ring (ties, histograms, scratch, bitmap)
+        sel::SliceLds S;
+        unsigned char *p = lds;
+        S.ties = reinterpret_cast<uint64_t *>(p);
+        p += (size_t)f.tl * 8;
+        S.h = reinterpret_cast<uint32_t *>(p);
+        p += sel::kB2 * 4;
+        S.h256 = reinterpret_cast<uint32_t *>(p);
+        p += 256 * 4;
+        S.scr = reinterpret_cast<uint32_t *>(p);
+        p += 32 * 4;
+        S.bits = reinterpret_cast<uint32_t *>(p);
+        S.tl = f.tl;
+        S.pw_log = f.pw_log;
+        S.bits_lds = f.bits_lds != 0;
+        sel::resolve_slice<NT>(f.sa, f.w, (int)selrow, r0, r0 + nrows, S, posbuf);  // ends with a barrier
+        if (kvh == 0 && layer == 0) {
+            int32_t *dst = f.sa.idx + selrow * K + r0;
+            for (int i = tid; i < nrows; i += NT) dst[i] = posbuf[i];
+        }
+    }
+    const int32_t *idxrow = FUSED ? nullptr : a.idx + selrow * K + r0;
     const uint16_t *kbase = a.k + layer * a.lsk + b * a.ksb + kvh * a.ksh;
     const uint16_t *vbase = MLA ? kbase : a.v + layer * a.lsv + b * a.vsb + kvh * a.vsh;
 
@@ -125,7 +166,8 @@ __global__ __launch_bounds__(64 * HW) void attend_kernel(AttendArgs a, uint16_t 
     // 1 .. NST-2. The position list is written to LDS last, ready by the loop's first
     // barrier.
     auto rowpos = [&](int i) {  // position of selected row i of the split, -1 if none
-        const int s = i < nrows ? idxrow[i] : -1;
+        int s = -1;
+        if (i < nrows) s = FUSED ? posbuf[i] : idxrow[i];
         return (s >= 0 && s < a.N) ? s : -1;
     };
     const int lpos0 = rowpos(tid);  // this thread's first entry of the LDS position list
@@ -151,6 +193,8 @@ __global__ __launch_bounds__(64 * HW) void attend_kernel(AttendArgs a, uint16_t 
 #pragma unroll
     for (int p = 1; p < G::NST - 1; ++p)
         if (p < ntile) issue_tile(p, max(dpos[p][0], 0), max(dpos[p][1], 0));
+    // (FUSED: entries are rewritten in place, each by the thread that reads it; the DMA
+    // positions read above take max(., 0) and so agree with either value)
     for (int i = tid; i < ntile * kRows; i += NT) {
         const int ps = i == tid ? lpos0 : rowpos(i);
         posbuf[i] = max(ps, 0);
@@ -303,6 +347,7 @@ __global__ __launch_bounds__(64 * HW) void attend_kernel(AttendArgs a, uint16_t 
             if (a.lse && lane < 16)
                 a.lse[layer * a.lsl + ohead] = l_tot > 0.0f ? (m_run + __builtin_log2f(l_tot)) * kLn2 : kNegInf;
         }
+        if constexpr (FUSED) sel::release_slice<NT>(f.w, (int)selrow, nslices, slice);
         return;
     }
     // bf16 rows o / l (the output, or a split's normalised partial) staged per wave in
@@ -345,6 +390,7 @@ __global__ __launch_bounds__(64 * HW) void attend_kernel(AttendArgs a, uint16_t 
             pml[2 * pidx + 1] = l_tot;
         }
     }
+    if constexpr (FUSED) sel::release_slice<NT>(f.w, (int)selrow, nslices, slice);
 }
 
 // Merge the split partials of HPW heads of one (layer, b, t) in split order. Lane l of
@@ -442,7 +488,7 @@ size_t partial_rows_bytes(const AttendArgs &a, int S) {
 }
 
 template <int DQK, int DV, int HW, bool MLA, bool OUTF32>
-hipError_t launch_t(const AttendArgs &a, void *ws, hipStream_t s) {
+hipError_t launch_t(const AttendArgs &a, void *ws, hipStream_t s, const FuseArgs *fuse) {
     const int R = rows_per_split(a);
     const int S = (a.K + R - 1) / R;
     uint16_t *po = reinterpret_cast<uint16_t *>(ws);
@@ -450,7 +496,22 @@ hipError_t launch_t(const AttendArgs &a, void *ws, hipStream_t s) {
     dim3 grid(S, a.T * a.Hkv, a.B * a.L);
     using G = AttTile<DQK, DV, HW, MLA, OUTF32>;
     const size_t lds = (size_t)G::NST * G::STAGE + (size_t)kMaxR * sizeof(int) + (size_t)(kMaxR / 32) * sizeof(uint32_t);
-    hipLaunchKernelGGL((attend_kernel<DQK, DV, HW, MLA, OUTF32>), grid, dim3(64 * HW), lds, s, a, po, pml, R);
+    if (fuse) {
+        // the resolve's working set in the tile ring: histograms and scratch, the row
+        // bitmap when it fits beside the first tie entries, the rest for ties
+        FuseArgs f = *fuse;
+        constexpr size_t ring = (size_t)G::NST * G::STAGE;
+        constexpr size_t fixed = sel::kB2 * 4 + 256 * 4 + 32 * 4;
+        f.pw_log = sel::slice_pw_log(f.w.words, G::NT);
+        const size_t bb = ((size_t)G::NT << f.pw_log) * 4;  // transposed bitmap
+        static_assert(ring >= fixed + sel::kSliceTiesFirst * 8, "tile ring too small for the resolve");
+        f.bits_lds = ring >= fixed + bb + (size_t)sel::kSliceTiesFirst * 8;
+        f.tl = (int)(((ring - fixed - (f.bits_lds ? bb : 0)) / 8) & ~(size_t)1);
+        hipLaunchKernelGGL((attend_kernel<DQK, DV, HW, MLA, OUTF32, true>), grid, dim3(64 * HW), lds, s, a, po, pml, R, f);
+    } else {
+        hipLaunchKernelGGL((attend_kernel<DQK, DV, HW, MLA, OUTF32, false>), grid, dim3(64 * HW), lds, s, a, po, pml, R,
+                           FuseArgs{});
+    }
     hipError_t e = hipGetLastError();
     if (e != hipSuccess || S == 1) return e;
     constexpr int HPW = kCombT / (DV / 8);
@@ -460,17 +521,17 @@ hipError_t launch_t(const AttendArgs &a, void *ws, hipStream_t s) {
 }
 
 template <int DQK, int DV, bool MLA>
-hipError_t launch_d(const AttendArgs &a, void *ws, hipStream_t s) {
+hipError_t launch_d(const AttendArgs &a, void *ws, hipStream_t s, const FuseArgs *fuse) {
     const int g = a.Hq / a.Hkv;
     const int HW = (g + 15) / 16;
     if (a.out_f32) {
-        if (HW == 1) return launch_t<DQK, DV, 1, MLA, true>(a, ws, s);
-        if (HW == 2) return launch_t<DQK, DV, 2, MLA, true>(a, ws, s);
-        return launch_t<DQK, DV, 4, MLA, true>(a, ws, s);
+        if (HW == 1) return launch_t<DQK, DV, 1, MLA, true>(a, ws, s, fuse);
+        if (HW == 2) return launch_t<DQK, DV, 2, MLA, true>(a, ws, s, fuse);
+        return launch_t<DQK, DV, 4, MLA, true>(a, ws, s, fuse);
     }
-    if (HW == 1) return launch_t<DQK, DV, 1, MLA, false>(a, ws, s);
-    if (HW == 2) return launch_t<DQK, DV, 2, MLA, false>(a, ws, s);
-    return launch_t<DQK, DV, 4, MLA, false>(a, ws, s);
+    if (HW == 1) return launch_t<DQK, DV, 1, MLA, false>(a, ws, s, fuse);
+    if (HW == 2) return launch_t<DQK, DV, 2, MLA, false>(a, ws, s, fuse);
+    return launch_t<DQK, DV, 4, MLA, false>(a, ws, s, fuse);
 }
 
 }  // namespace
@@ -504,8 +565,18 @@ size_t attend_workspace_bytes(const AttendArgs &a) {
 
 hipError_t launch_attend(const AttendArgs &a, void *ws, hipStream_t s) {
     const bool mla = a.d_qk == 576;
-    if (mla) return launch_d<576, 512, true>(a, ws, s);
-    return launch_d<128, 128, false>(a, ws, s);
+    if (mla) return launch_d<576, 512, true>(a, ws, s, nullptr);
+    return launch_d<128, 128, false>(a, ws, s, nullptr);
+}
+
+hipError_t launch_select_attend(const SelectArgs &sa, void *sel_ws, const AttendArgs &a, void *ws, hipStream_t s) {
+    const hipError_t e = launch_select_front(sa, sel_ws, s);
+    if (e != hipSuccess) return e;
+    FuseArgs f{};
+    f.sa = sa;
+    f.w = sel::carve(sel_ws, sa.B * sa.T, sa.n_cols, false);
+    if (a.d_qk == 576) return launch_d<576, 512, true>(a, ws, s, &f);
+    return launch_d<128, 128, false>(a, ws, s, &f);
 }
 
 }  // namespace lsa

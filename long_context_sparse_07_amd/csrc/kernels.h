@@ -71,6 +71,9 @@ hipError_t launch_select(const SelectArgs &a, void *ws, hipStream_t s);
 // Histogram pass alone (the selection's first pass), for an index call that primes a
 // selection workspace with a kernel that cannot build it in its epilogue.
 hipError_t launch_select_hist(const SelectArgs &a, void *ws, hipStream_t s);
+// The selection up to its last pass (the histogram pass unless primed, then the filter
+// pass), for an attention launch that resolves the selection itself.
+hipError_t launch_select_front(const SelectArgs &a, void *ws, hipStream_t s);
 
 struct AttendArgs {
     int B, T, N, Hq, Hkv, d_qk, d_v;
@@ -94,6 +97,10 @@ int attend_default_splits(const AttendArgs &a);
 size_t attend_workspace_bytes(const AttendArgs &a);
 bool attend_supported(int d_qk, int d_v, int g);
 hipError_t launch_attend(const AttendArgs &a, void *ws, hipStream_t s);
+// Selection (flat rows, no kept map) and attention on its output in one chain: the
+// attention workgroups resolve their own slices of the selection (sa.idx written too).
+// a.idx is ignored; sa and a describe the same B, T, N, K.
+hipError_t launch_select_attend(const SelectArgs &sa, void *sel_ws, const AttendArgs &a, void *ws, hipStream_t s);
 
 hipError_t launch_clear(void *p, size_t bytes, hipStream_t s);
 

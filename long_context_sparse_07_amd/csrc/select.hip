@@ -20,193 +20,22 @@
 //             share 23 key bits, or radix passes when many are equal), sets the chosen
 //             ties in the bitmap, and compacts the bitmap into ascending positions
 //             between the sink and the window. It leaves the row's histogram and
-//             counters at zero for the next call.
-// Kernel boundaries are the only cross-workgroup synchronisation. Membership is
+//             counters at zero for the next call. (A fused selection + attention
+//             launch replaces this pass: each attention workgroup resolves the slice
+//             of the row it attends over; the filter records its pick for them.)
+// Kernel boundaries are the only cross-workgroup synchronisation, apart from the
+// counter that tells the last of a row's sliced resolves to clear the row's counters. Membership is
 // defined by the total order on composites and the output is sorted, so the result
 // does not depend on the order in which atomics land.
-#include "common.cuh"
-#include "kernels.h"
+#include "select_core.cuh"
 
 namespace lsa {
 namespace {
+using namespace sel;
 
 constexpr int kHT = 256;             // histogram and filter threads
 constexpr int kRT = 1024;            // resolve threads (16 waves)
 constexpr int kFC = 2048;            // filter round: 8 columns per thread
-constexpr int kB2 = 4096;            // second-level bins: the next 12 key bits
-constexpr int kL2Shift = kSelShift - 12;
-constexpr int kGrpShift = 32 + kL2Shift;  // composite bits above it: the 23 key bits of (b1, b2)
-constexpr int kB1Shift = 32 + kSelShift;  // composite bits above it: the 11 key bits of b1
-constexpr int kTieLds = 8192;        // tie entries the resolve keeps in LDS
-constexpr int kBitsLds = 8192;       // bitmap words the resolve keeps in LDS
-constexpr int kTiny = 1024;          // a final group up to this size is ranked directly
-constexpr int kCtr = 16;             // per-row counters: [0] tie count
-
-inline size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
-
-// Tie list capacity per row: every column when the rows together stay within 2^24
-// entries, else 2^24 / rows (at least 8192); a longer threshold bin is resolved by
-// rescanning the row.
-inline int tie_cap(int rows, int n_cols) {
-    const int64_t all = ((int64_t)n_cols + 63) / 64 * 64;
-    int64_t c = ((int64_t)(1 << 24) / rows + 63) / 64 * 64;
-    if (c < kTieLds) c = kTieLds;
-    return (int)(all < c ? all : c);
-}
-inline int bit_words(int n_cols) { return (n_cols + 31) / 32; }
-
-// Workspace: per row the first-level histogram and counters (kept at zero between
-// calls), the tie list (composites, and columns when a kept map is used) and the column
-// bitmap (rewritten by every call).
-struct Ws {
-    uint32_t *hist;   // [rows][kSelBins]
-    uint32_t *ctr;    // [rows][kCtr]
-    uint64_t *ties;   // [rows][cap]
-    uint32_t *tcols;  // [rows][cap] (kept map only)
-    uint32_t *bits;   // [rows][words]
-    int cap, words;
-};
-
-size_t zero_bytes(int rows) { return align256((size_t)rows * kSelBins * 4) + align256((size_t)rows * kCtr * 4); }
-
-Ws carve(void *base, int rows, int n_cols, bool kept) {
-    Ws w;
-    char *p = reinterpret_cast<char *>(base);
-    w.cap = tie_cap(rows, n_cols);
-    w.words = bit_words(n_cols);
-    w.hist = reinterpret_cast<uint32_t *>(p);
-    p += align256((size_t)rows * kSelBins * 4);
-    w.ctr = reinterpret_cast<uint32_t *>(p);
-    p += align256((size_t)rows * kCtr * 4);
-    w.ties = reinterpret_cast<uint64_t *>(p);
-    p += align256((size_t)rows * w.cap * 8);
-    w.tcols = kept ? reinterpret_cast<uint32_t *>(p) : nullptr;
-    if (kept) p += align256((size_t)rows * w.cap * 4);
-    w.bits = reinterpret_cast<uint32_t *>(p);
-    return w;
-}
-
-size_t ws_total(int rows, int n_cols, bool kept) {
-    const int cap = tie_cap(rows, n_cols);
-    return zero_bytes(rows) + align256((size_t)rows * cap * 8) + (kept ? align256((size_t)rows * cap * 4) : 0) +
-           align256((size_t)rows * bit_words(n_cols) * 4);
-}
-
-// Per-row context: query position, forced set, fill size.
-struct Row {
-    int b, t, p;
-    int f_sink_end;  // sink = [0, f_sink_end)
-    int f_win_lo;    // window = [f_win_lo, p] (empty when f_win_lo > p)
-    int m;           // fill size
-    const float *sc;
-    const int32_t *kept;
-    int nblk;
-};
-
-__device__ __forceinline__ Row make_row(const SelectArgs &a, int row) {
-    Row r;
-    r.b = row / a.T;
-    r.t = row % a.T;
-    int ctx = a.ctx_len ? a.ctx_len[r.b] : a.N;
-    ctx = min(max(ctx, 0), a.N);
-    r.p = ctx - a.T + r.t;
-    if (a.causal) {
-        forced_bounds(r.p, a.sink, a.window, r.f_sink_end, r.f_win_lo);
-        r.m = a.K - (r.f_sink_end + max(0, r.p - r.f_win_lo + 1));
-    } else {
-        r.f_sink_end = 0;
-        r.f_win_lo = 0x7FFFFFFF;
-        r.m = a.K;
-    }
-    r.sc = a.scores + (int64_t)row * a.n_cols;
-    r.kept = a.kept ? a.kept + (int64_t)row * a.n_keep : nullptr;
-    r.nblk = a.kept ? a.N / a.block_size : 0;
-    return r;
-}
-
-__device__ __forceinline__ bool candidate_x(const SelectArgs &a, const Row &r, int col, float x, uint64_t &comp) {
-    if (!(x > kNegInf)) return false;  // -inf and NaN are never selected
-    int pos = col;
-    if (r.kept) {
-        const int blk = col / a.block_size;
-        if (blk >= a.n_keep) return false;
-        const int kb = r.kept[blk];
-        if (kb < 0 || kb >= r.nblk) return false;
-        pos = kb * a.block_size + (col - blk * a.block_size);
-    }
-    if (a.causal && (pos > r.p || pos < r.f_sink_end || pos >= r.f_win_lo)) return false;
-    comp = ((uint64_t)order_key(x) << 32) | (uint32_t)(~(uint32_t)pos);
-    return true;
-}
-
-__device__ __forceinline__ int comp_pos(uint64_t c) { return (int)(~(uint32_t)c); }
-
-__device__ __forceinline__ uint32_t lane_rank(uint64_t mask) {  // set lanes of mask below this lane
-    return __builtin_amdgcn_mbcnt_hi((uint32_t)(mask >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)mask, 0u));
-}
-
-// Block-wide exclusive scan of one value per thread (NT threads, wave64); lds >= NT/64 words.
-template <int NT>
-__device__ uint32_t block_exscan(uint32_t v, uint32_t *lds, uint32_t *total) {
-    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-    uint32_t x = v;
-#pragma unroll
-    for (int o = 1; o < 64; o <<= 1) {
-        const uint32_t y = __shfl_up(x, o, 64);
-        if (lane >= o) x += y;
-    }
-    if (lane == 63) lds[wave] = x;
-    __syncthreads();
-    uint32_t base = 0, tot = 0;
-#pragma unroll
-    for (int w = 0; w < NT / 64; ++w) {
-        const uint32_t s = lds[w];
-        if (w < wave) base += s;
-        tot += s;
-    }
-    __syncthreads();
-    *total = tot;
-    return base + x - v;
-}
-
-// Threshold bin of an NB-bin LDS histogram counted from the top bin: the bin b with
-// above(b) < need <= above(b) + h[b]. mode 0: need == 0 (nothing); 1: total <= need
-// (take everything); 2: threshold bin found. scr >= 24 words.
-struct BinPick {
-    int mode;
-    int bin;
-    uint32_t above;  // elements in bins above `bin` (mode 2), or the total (mode 1)
-};
-
-// v[e] is bin NB - 1 - PER * threadIdx.x - e of an NB = NT * PER bin histogram.
-template <int NT, int PER>
-__device__ BinPick pick_bin(const uint32_t (&v)[PER], uint32_t need, uint32_t *scr) {
-    constexpr int NB = NT * PER;
-    const int top = NB - 1 - PER * (int)threadIdx.x;
-    uint32_t s = 0;
-#pragma unroll
-    for (int e = 0; e < PER; ++e) s += v[e];
-    uint32_t total;
-    const uint32_t ex = block_exscan<NT>(s, scr, &total);
-    if (need == 0) return BinPick{0, NB, 0};
-    if (total <= need) return BinPick{1, -1, total};
-    if (ex < need && need <= ex + s) {
-        uint32_t acc = ex;
-#pragma unroll
-        for (int e = 0; e < PER; ++e) {
-            if (acc < need && need <= acc + v[e]) {
-                scr[16] = (uint32_t)(top - e);
-                scr[17] = acc;
-            }
-            acc += v[e];
-        }
-    }
-    __syncthreads();
-    const BinPick r{2, (int)scr[16], scr[17]};
-    __syncthreads();
-    return r;
-}
-
 // ----------------------------------------------------------------------------- hist
 __global__ __launch_bounds__(kHT) void select_hist_kernel(SelectArgs a, uint32_t *hist, int part_cols) {
     __shared__ uint32_t h[kSelBins];
@@ -237,96 +66,6 @@ __global__ __launch_bounds__(kHT) void select_hist_kernel(SelectArgs a, uint32_t
     uint32_t *g = hist + (int64_t)row * kSelBins;
     for (int i = threadIdx.x; i < kSelBins; i += kHT)
         if (h[i]) atomicAdd(&g[i], h[i]);
-}
-
-// ----------------------------------------------------------------------------- radix
-struct ArrSrc {
-    const uint64_t *p;
-    int n;
-    __device__ int size() const { return n; }
-    __device__ bool get(int i, uint64_t &c) const {
-        c = p[i];
-        return true;
-    }
-};
-struct RowSrc {
-    const SelectArgs *a;
-    const Row *r;
-    __device__ int size() const { return a->n_cols; }
-    __device__ bool get(int i, uint64_t &c) const { return candidate_x(*a, *r, i, r->sc[i], c); }
-};
-
-// LDS histogram increment for digit d (-1: none) with same-digit lanes of the wave
-// merged into one atomic (radix digits of nearly sorted keys are mostly equal).
-__device__ __forceinline__ void wave_hist_add(uint32_t *h, int d) {
-    const int d0 = __builtin_amdgcn_readfirstlane(d);
-    const uint64_t same = __ballot(d == d0);
-    if (d == d0) {
-        if (d0 >= 0 && (int)__lane_id() == __ffsll((unsigned long long)same) - 1) atomicAdd(&h[d0], (uint32_t)__popcll(same));
-    } else if (d >= 0) {
-        atomicAdd(&h[d], 1u);
-    }
-}
-
-// need-th largest composite (1 <= need <= group size) of the group of source elements
-// whose bits at and above bit `lo_bits` equal those of pref; radix passes of up to 8
-// bits over the low lo_bits bits (0 < lo_bits < 64). Returns the smallest composite
-// that still belongs to the group's top `need`: those are exactly the group elements
-// >= it.
-template <int NT, class Src>
-__device__ uint64_t radix_kth(const Src &src, uint32_t need, uint64_t pref, int lo_bits, uint32_t *h256,
-                              uint32_t *scr) {
-    int hi = lo_bits;
-    pref = pref >> hi << hi;
-    while (hi > 0) {
-        const int w = hi < 8 ? hi : 8;
-        const int sh = hi - w;
-        const uint32_t dmask = (1u << w) - 1;
-        for (int i = threadIdx.x; i < 256; i += NT) h256[i] = 0;
-        __syncthreads();
-        const int n = src.size();
-        const int nr = (n + NT - 1) / NT * NT;  // every lane takes part in the wave merge
-        for (int i = threadIdx.x; i < nr; i += NT) {
-            uint64_t c = 0;
-            const bool ok = i < n && src.get(i, c) && (c >> hi) == (pref >> hi);
-            wave_hist_add(h256, ok ? (int)((c >> sh) & dmask) : -1);
-        }
-        __syncthreads();
-        if (threadIdx.x < 64) {
-            const int lane = threadIdx.x;
-            const int top = 255 - 4 * lane;  // lane owns 4 digits, scanned from the top
-            const uint32_t s = h256[top] + h256[top - 1] + h256[top - 2] + h256[top - 3];
-            uint32_t x = s;
-#pragma unroll
-            for (int o = 1; o < 64; o <<= 1) {
-                const uint32_t y = __shfl_up(x, o, 64);
-                if (lane >= o) x += y;
-            }
-            const uint32_t ex = x - s;
-            if (ex < need && need <= x) {
-                uint32_t acc = ex;
-                for (int e = 0; e < 4; ++e) {
-                    const uint32_t c = h256[top - e];
-                    if (acc + c >= need) {
-                        scr[0] = (uint32_t)(top - e);
-                        scr[1] = need - acc;
-                        scr[2] = (c == need - acc);
-                        break;
-                    }
-                    acc += c;
-                }
-            }
-        }
-        __syncthreads();
-        const uint32_t d = scr[0];
-        need = scr[1];
-        const bool whole = scr[2] != 0;
-        __syncthreads();
-        pref |= (uint64_t)d << sh;
-        hi = sh;
-        if (whole) return pref;  // lower bits zero: every group element with this prefix
-    }
-    return pref;
 }
 
 // ----------------------------------------------------------------------------- filter
@@ -368,9 +107,14 @@ __global__ __launch_bounds__(kHT) void select_filter_kernel(SelectArgs a, Ws w, 
         hv[0] = hi.w, hv[1] = hi.z, hv[2] = hi.y, hv[3] = hi.x, hv[4] = lo.w, hv[5] = lo.z, hv[6] = lo.y, hv[7] = lo.x;
     }
     const BinPick bp = pick_bin<kHT, kSelBins / kHT>(hv, m, scr);
+    uint32_t *gctr = w.ctr + (int64_t)row * kCtr;
+    if (blockIdx.x == 0 && tid == 0) {  // every workgroup of the row picks the same; one records it
+        gctr[1] = (uint32_t)bp.mode;
+        gctr[2] = (uint32_t)bp.bin;
+        gctr[3] = bp.above;
+    }
     if (bp.mode == 0) return;
     const int b1 = bp.bin;
-    uint32_t *gctr = w.ctr + (int64_t)row * kCtr;
     uint64_t *gties = w.ties + (int64_t)row * w.cap;
     uint32_t *gtcols = w.tcols ? w.tcols + (int64_t)row * w.cap : nullptr;
     uint32_t *gbits = w.bits + (int64_t)row * w.words;
@@ -428,42 +172,6 @@ __global__ __launch_bounds__(kHT) void select_filter_kernel(SelectArgs a, Ws w, 
             }
         }
         __syncthreads();  // LDS buffers are reused by the next round
-    }
-}
-
-// Copy n 32-bit words global -> LDS with several loads per thread in flight (a plain
-// element loop would wait for each load before its LDS store): U 16-byte loads when
-// both pointers are 16-byte aligned, else 4 U word loads. (Native vector types: arrays
-// of the HIP vector classes end up in scratch memory.)
-template <int NT, int U>
-__device__ void copy_words_to_lds(const uint32_t *src, uint32_t *dst, int n) {
-    const int tid = (int)threadIdx.x;
-    if ((((uintptr_t)src | (uintptr_t)dst) & 15) == 0) {
-        const int n4 = n >> 2;
-        const u32x4 *s4 = reinterpret_cast<const u32x4 *>(src);
-        u32x4 *d4 = reinterpret_cast<u32x4 *>(dst);
-        for (int base = 0; base < n4; base += NT * U) {
-            u32x4 v[U];
-#pragma unroll
-            for (int u = 0; u < U; ++u) {
-                const int i = min(base + u * NT + tid, n4 - 1);
-                v[u] = s4[i];
-            }
-#pragma unroll
-            for (int u = 0; u < U; ++u)
-                if (base + u * NT + tid < n4) d4[base + u * NT + tid] = v[u];
-        }
-        for (int i = 4 * n4 + tid; i < n; i += NT) dst[i] = src[i];
-    } else {
-        constexpr int V = 4 * U;
-        for (int base = 0; base < n; base += NT * V) {
-            uint32_t v[V];
-#pragma unroll
-            for (int u = 0; u < V; ++u) v[u] = src[min(base + u * NT + tid, n - 1)];
-#pragma unroll
-            for (int u = 0; u < V; ++u)
-                if (base + u * NT + tid < n) dst[base + u * NT + tid] = v[u];
-        }
     }
 }
 
@@ -721,20 +429,23 @@ hipError_t launch_select_hist(const SelectArgs &a, void *wsp, hipStream_t s) {
     return hipGetLastError();
 }
 
-hipError_t launch_select(const SelectArgs &a, void *wsp, hipStream_t s) {
+hipError_t launch_select_front(const SelectArgs &a, void *wsp, hipStream_t s) {
     const int rows = a.B * a.T;
-    hipError_t e;
     if (!a.primed) {
-        e = launch_select_hist(a, wsp, s);
+        const hipError_t e = launch_select_hist(a, wsp, s);
         if (e != hipSuccess) return e;
     }
     const Ws w = carve(wsp, rows, a.n_cols, a.kept != nullptr);
     int parts;
     const int pc = part_columns(rows, a.n_cols, parts);
     hipLaunchKernelGGL(select_filter_kernel, dim3(parts, rows), dim3(kHT), 0, s, a, w, pc);
-    e = hipGetLastError();
+    return hipGetLastError();
+}
+
+hipError_t launch_select(const SelectArgs &a, void *wsp, hipStream_t s) {
+    const hipError_t e = launch_select_front(a, wsp, s);
     if (e != hipSuccess) return e;
-    return launch_resolve(a, w, s);
+    return launch_resolve(a, carve(wsp, a.B * a.T, a.n_cols, a.kept != nullptr), s);
 }
 
 hipError_t launch_clear(void *p, size_t bytes, hipStream_t s) {

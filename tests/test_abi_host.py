@@ -26,7 +26,7 @@ def test_library_exports_every_declared_function():
     names = declared_functions()
     assert {"lsa_index", "lsa_block_means", "lsa_select", "lsa_attend", "lsa_select_workspace_bytes",
             "lsa_attend_workspace_bytes", "lsa_workspace_clear", "lsa_status_str", "lsa_last_error",
-            "lsa_version"} <= set(names)
+            "lsa_version", "lsa_select_attend"} <= set(names)
     for n in names:
         assert hasattr(lib, n), f"{n} declared in lsa.h but not exported"
     assert lib.lsa_version() == 1
@@ -171,6 +171,37 @@ def test_attend_workspace_rules():
     assert _att(d, None, 0) == -7
     one = _attend_desc(n_splits=1)
     assert L.lib().lsa_attend_workspace_bytes(ctypes.byref(one)) == 0
+
+
+def _sel_att(ds, da, ws=FAKE, nbytes=1 << 40, wa=FAKE, na=1 << 40):
+    return L.lib().lsa_select_attend(ctypes.byref(ds), ctypes.byref(da), ws, nbytes, wa, na, None)
+
+
+@pytest.mark.parametrize("skw,akw,code", [
+    (dict(), dict(B=3), -2), (dict(), dict(K=512), -2), (dict(), dict(N=2048), -2),
+    (dict(), dict(idx=FAKE + 4096), -2),
+    (dict(kept=FAKE, n_keep=16, block_size=64), dict(), -6),
+    (dict(scores=None), dict(), -1), (dict(), dict(q=None), -1), (dict(), dict(out=None), -1),
+    (dict(K=0, sink=0, window=0), dict(), -4), (dict(), dict(Hq=48), -6),
+    (dict(), dict(q=FAKE + 8), -5), (dict(idx=FAKE + 2), dict(idx=None), -5),
+])
+def test_select_attend_argument_errors(skw, akw, code):
+    assert _sel_att(_select_desc(**skw), _attend_desc(**akw)) == code
+    assert L.lib().lsa_last_error()
+
+
+def test_select_attend_workspace_errors():
+    ds, da = _select_desc(), _attend_desc(n_splits=4)
+    sneed = L.lib().lsa_select_workspace_bytes(ctypes.byref(ds))
+    aneed = L.lib().lsa_attend_workspace_bytes(ctypes.byref(da))
+    assert _sel_att(ds, da, FAKE, sneed - 1) == -7
+    assert _sel_att(ds, da, None, sneed) == -7
+    assert _sel_att(ds, da, FAKE, sneed, FAKE, aneed - 4) == -7
+    assert _sel_att(ds, da, FAKE, sneed, None, aneed) == -7
+    assert _sel_att(ds, da, FAKE + 16, sneed) == -5
+    assert _sel_att(ds, da, FAKE, sneed, FAKE + 16, aneed) == -5
+    assert L.lib().lsa_select_attend(None, ctypes.byref(da), FAKE, sneed, FAKE, aneed, None) == -1
+    assert L.lib().lsa_select_attend(ctypes.byref(ds), None, FAKE, sneed, FAKE, aneed, None) == -1
 
 
 def test_status_strings():
