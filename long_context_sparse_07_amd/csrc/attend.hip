@@ -108,6 +108,19 @@ __global__ __launch_bounds__(64 * HW) void attend_kernel(AttendArgs a, uint16_t 
     const int nsplit = gridDim.x;
     const int ntile = (nrows + kRows - 1) / kRows;
 
+    // Q as the B operand of S^T = K Q^T: lane holds head hl, dims 32 ks + 8 q4 .. +8
+    bf16x8 bq[KSQ];
+    auto load_q = [&]() __attribute__((always_inline)) {
+        const uint16_t *qp = a.q + layer * a.lsq + (((int64_t)b * T + t) * Hq + hq) * DQK + 8 * q4;
+#pragma unroll
+        for (int ks = 0; ks < KSQ; ++ks) {
+            u32x4 v = {0, 0, 0, 0};
+            if (hvalid) v = *reinterpret_cast<const u32x4 *>(qp + 32 * ks);
+            bq[ks] = __builtin_bit_cast(bf16x8, v);
+        }
+    };
+    // FUSED: Q is requested first, its latency hidden under the selection's
+    if constexpr (FUSED) load_q();
     const int64_t selrow = (int64_t)b * T + t;
     // the workgroups sharing a selection row: splits x KV heads x layers
     const int nslices = nsplit * Hkv * a.L, slice = split + nsplit * (kvh + Hkv * layer);
@@ -179,17 +192,7 @@ __global__ __launch_bounds__(64 * HW) void attend_kernel(AttendArgs a, uint16_t 
     }
     // invalid rows read row 0 (finite values; zero probability)
     if (ntile > 0) issue_tile(0, max(dpos[0][0], 0), max(dpos[0][1], 0));
-    // Q as the B operand of S^T = K Q^T: lane holds head hl, dims 32 ks + 8 q4 .. +8
-    bf16x8 bq[KSQ];
-    {
-        const uint16_t *qp = a.q + layer * a.lsq + (((int64_t)b * T + t) * Hq + hq) * DQK + 8 * q4;
-#pragma unroll
-        for (int ks = 0; ks < KSQ; ++ks) {
-            u32x4 v = {0, 0, 0, 0};
-            if (hvalid) v = *reinterpret_cast<const u32x4 *>(qp + 32 * ks);
-            bq[ks] = __builtin_bit_cast(bf16x8, v);
-        }
-    }
+    if constexpr (!FUSED) load_q();
 #pragma unroll
     for (int p = 1; p < G::NST - 1; ++p)
         if (p < ntile) issue_tile(p, max(dpos[p][0], 0), max(dpos[p][1], 0));

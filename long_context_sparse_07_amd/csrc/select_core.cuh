@@ -423,6 +423,8 @@ __device__ void resolve_slice(const SelectArgs &a, const Ws &w, int row, int k0,
     const int pwl = S.pw_log;
     if (S.bits_lds) copy_bits_transposed<NT>(gbits, S.bits, w.words, pwl);
     copy_words_to_lds<NT, 4>(reinterpret_cast<const uint32_t *>(gties), reinterpret_cast<uint32_t *>(S.ties), 2 * tfirst);
+    for (int i = tid; i < kB2; i += NT) S.h[i] = 0;  // the second-level histogram
+    if (tid == 0) scr[24] = 0;
     __syncthreads();
     const uint32_t ntie = scr[28], mode = scr[29], b1 = scr[30], above = scr[31];
     const uint32_t nfill = mode == 0 ? 0u : (mode == 1 ? min(above, m) : m);
@@ -452,17 +454,16 @@ __device__ void resolve_slice(const SelectArgs &a, const Ws &w, int row, int k0,
     };
     if (f0 < f1 && mode == 2) {
         const uint32_t need1 = m > above ? m - above : 0u;
-        if (!overflow && ties_lds && nl > (uint32_t)tfirst)
+        if (!overflow && ties_lds && nl > (uint32_t)tfirst) {  // uniform
             copy_words_to_lds<NT, 4>(reinterpret_cast<const uint32_t *>(gties + tfirst),
                                      reinterpret_cast<uint32_t *>(S.ties + tfirst), 2 * ((int)nl - tfirst));
+            __syncthreads();
+        }
         // rank the tie list where it lives (inlined at each call, so that the LDS copy is
         // read with LDS instructions)
         auto rank_and_mark = [&](const uint64_t *tl) __attribute__((always_inline)) {
             uint64_t thr = ~(uint64_t)0;
-            uint32_t *h = S.h;
-            for (int i = tid; i < kB2; i += NT) h[i] = 0;
-            if (tid == 0) scr[24] = 0;
-            __syncthreads();
+            uint32_t *h = S.h;  // zeroed with the first loads
             for (uint32_t i = tid; i < nl; i += NT)
                 atomicAdd(&h[hslot((int)(((uint32_t)(tl[i] >> 32) >> kL2Shift) & (kB2 - 1)))], 1u);
             __syncthreads();
