@@ -71,8 +71,8 @@ __global__ __launch_bounds__(kHT) void select_hist_kernel(SelectArgs a, uint32_t
 // ----------------------------------------------------------------------------- filter
 // grid (parts, rows); part_cols is a multiple of 32, so each workgroup owns whole words
 // of the row's column bitmap.
+template <bool KEPT>
 __global__ __launch_bounds__(kHT) void select_filter_kernel(SelectArgs a, Ws w, int part_cols) {
-    __shared__ uint32_t wbits[kFC / 32];
     __shared__ uint64_t tbuf[kFC];
     __shared__ uint32_t tcbuf[kFC];
     __shared__ uint32_t scr[24];
@@ -94,12 +94,20 @@ __global__ __launch_bounds__(kHT) void select_filter_kernel(SelectArgs a, Ws w, 
         v.w = col + 3 < end ? r.sc[col + 3] : kNegInf;
         return v;
     };
+    // both halves of a round's columns; a whole aligned round takes plain vector loads
+    // (a workgroup-uniform choice: no divergent paths writing the same registers)
     float4 va, vb;
-    {
-        const int end = min(c1, c0 + kFC);
-        va = load4(c0 + 4 * tid, end);
-        vb = load4(c0 + kFC / 2 + 4 * tid, end);
-    }
+    auto load_round = [&](int base) __attribute__((always_inline)) {
+        const int end = min(c1, base + kFC);
+        if (a.vec && base + kFC <= c1) {
+            va = *reinterpret_cast<const float4 *>(r.sc + base + 4 * tid);
+            vb = *reinterpret_cast<const float4 *>(r.sc + base + kFC / 2 + 4 * tid);
+        } else {
+            va = load4(base + 4 * tid, end);
+            vb = load4(base + kFC / 2 + 4 * tid, end);
+        }
+    };
+    load_round(c0);
     uint32_t hv[kSelBins / kHT];  // thread t: bins from the top, 8 per thread
     {
         const uint32_t *g = w.hist + (int64_t)row * kSelBins + kSelBins - kSelBins / kHT * (tid + 1);
@@ -121,44 +129,72 @@ __global__ __launch_bounds__(kHT) void select_filter_kernel(SelectArgs a, Ws w, 
 
     for (int base = c0; base < c1; base += kFC) {
         const int end = min(c1, base + kFC);
-        if (tid < kFC / 32) wbits[tid] = 0;
         if (tid == 0) tcnt = 0;
         __syncthreads();
-        if (base != c0) {
-            va = load4(base + 4 * tid, end);
-            vb = load4(base + kFC / 2 + 4 * tid, end);
-        }
-        // one element per lane, every lane of the wave present (the tie append is merged per wave)
-        auto classify = [&](int col, float x) {
-            uint64_t comp = 0;
-            const bool cand = col < end && candidate_x(a, r, col, x, comp);
-            const int d1 = (int)(comp >> kB1Shift);
-            if (cand && (bp.mode == 1 || d1 > b1)) atomicOr(&wbits[(col - base) >> 5], 1u << (col & 31));
-            const bool tie = cand && bp.mode == 2 && d1 == b1;
-            const uint64_t bal = __ballot(tie);
-            if (bal) {
-                uint32_t sb = 0;
-                if (lane == 0) sb = atomicAdd(&tcnt, (uint32_t)__popcll(bal));
-                sb = __builtin_amdgcn_readfirstlane(sb);
-                if (tie) {
-                    const uint32_t slot = sb + lane_rank(bal);
-                    tbuf[slot] = comp;
-                    tcbuf[slot] = (uint32_t)col;
-                }
-            }
-        };
+        if (base != c0) load_round(base);
+        // Lane l of wave w holds columns base + 256 w + 4 l + e (va) and base + 1024 +
+        // 256 w + 4 l + e (vb), e = 0..3. Per column slot i (0..7) one ballot of the columns
+        // above the threshold bin and one of the ties: bitmap word k of a half-row slice
+        // is interleaved from the four ballots of that half (lanes 8k .. 8k+7, bit 4 j + e
+        // for lane 8k + j), and the ties take one LDS append per wave.
         const int ca = base + 4 * tid, cb = base + kFC / 2 + 4 * tid;
-        classify(ca, va.x);
-        classify(ca + 1, va.y);
-        classify(ca + 2, va.z);
-        classify(ca + 3, va.w);
-        classify(cb, vb.x);
-        classify(cb + 1, vb.y);
-        classify(cb + 2, vb.z);
-        classify(cb + 3, vb.w);
+        uint64_t selb[8], tieb[8], comps[8];
+        // flat rows: branch-free (the column is the position); a kept map needs its load
+        const int lo = a.causal ? r.f_sink_end : 0;
+        const int hi = a.causal ? min(r.p + 1, r.f_win_lo) : end;  // candidates: lo <= col < hi
+        auto classify = [&](int i, int col, float x) {
+            uint64_t comp = 0;
+            bool cand;
+            if constexpr (KEPT) {
+                cand = col < end && candidate_x(a, r, col, x, comp);
+            } else {
+                cand = x > kNegInf && col < end && col >= lo && col < hi;
+                comp = ((uint64_t)order_key(x) << 32) | (uint32_t)~(uint32_t)col;
+            }
+            const int d1 = (int)(comp >> kB1Shift);
+            selb[i] = __ballot(cand && (bp.mode == 1 || d1 > b1));
+            tieb[i] = __ballot(cand && bp.mode == 2 && d1 == b1);
+            comps[i] = comp;
+        };
+        classify(0, ca, va.x);
+        classify(1, ca + 1, va.y);
+        classify(2, ca + 2, va.z);
+        classify(3, ca + 3, va.w);
+        classify(4, cb, vb.x);
+        classify(5, cb + 1, vb.y);
+        classify(6, cb + 2, vb.z);
+        classify(7, cb + 3, vb.w);
+        // lanes 0..15: word (lane & 7) of half (lane >> 3) of this wave's slice (both
+        // halves computed, one kept: no dynamic index into the ballot array)
+        const int half = (lane >> 3) & 1, wk = lane & 7;
+        const int wi = half * (kFC / 64) + 8 * (tid >> 6) + wk;  // word index from base
+        auto spread = [&](uint64_t bsel) {  // bit j of lane 8 wk + j's byte -> bit 4 j
+            uint32_t x = (uint32_t)(bsel >> (8 * wk)) & 0xFFu;
+            x = (x | (x << 12)) & 0x000F000Fu;
+            x = (x | (x << 6)) & 0x03030303u;
+            return (x | (x << 3)) & 0x11111111u;
+        };
+        const uint32_t wlo = spread(selb[0]) | spread(selb[1]) << 1 | spread(selb[2]) << 2 | spread(selb[3]) << 3;
+        const uint32_t whi = spread(selb[4]) | spread(selb[5]) << 1 | spread(selb[6]) << 2 | spread(selb[7]) << 3;
+        const uint32_t word = half ? whi : wlo;
+        uint32_t ntw = 0;
+#pragma unroll
+        for (int i = 0; i < 8; ++i) ntw += (uint32_t)__popcll(tieb[i]);
+        if (ntw) {  // uniform per wave
+            uint32_t sb = 0;
+            if (lane == 0) sb = atomicAdd(&tcnt, ntw);
+            sb = __builtin_amdgcn_readfirstlane(sb);
+#pragma unroll
+            for (int i = 0; i < 8; ++i) {
+                if ((tieb[i] >> lane) & 1ull) {
+                    const uint32_t slot = sb + lane_rank(tieb[i]);
+                    tbuf[slot] = comps[i];
+                    tcbuf[slot] = (uint32_t)((i < 4 ? ca : cb) + (i & 3));
+                }
+                sb += (uint32_t)__popcll(tieb[i]);
+            }
+        }
         __syncthreads();
-        const int nw = (end - base + 31) >> 5;
-        if (tid < nw) gbits[(base >> 5) + tid] = wbits[tid];
         const uint32_t nt = tcnt;
         if (nt) {
             if (tid == 0) tbase = atomicAdd(&gctr[0], nt);
@@ -171,7 +207,9 @@ __global__ __launch_bounds__(kHT) void select_filter_kernel(SelectArgs a, Ws w, 
                 }
             }
         }
-        __syncthreads();  // LDS buffers are reused by the next round
+        // bitmap words last (a barrier would wait for these stores)
+        if (lane < 16 && base + 32 * wi < end) gbits[(base >> 5) + wi] = word;
+        if (base + kFC < c1) __syncthreads();  // LDS buffers are reused by the next round
     }
 }
 
@@ -438,7 +476,8 @@ hipError_t launch_select_front(const SelectArgs &a, void *wsp, hipStream_t s) {
     const Ws w = carve(wsp, rows, a.n_cols, a.kept != nullptr);
     int parts;
     const int pc = part_columns(rows, a.n_cols, parts);
-    hipLaunchKernelGGL(select_filter_kernel, dim3(parts, rows), dim3(kHT), 0, s, a, w, pc);
+    if (a.kept) hipLaunchKernelGGL(select_filter_kernel<true>, dim3(parts, rows), dim3(kHT), 0, s, a, w, pc);
+    else hipLaunchKernelGGL(select_filter_kernel<false>, dim3(parts, rows), dim3(kHT), 0, s, a, w, pc);
     return hipGetLastError();
 }
 
