@@ -32,6 +32,10 @@ Readings where the pages are silent (the pages give no formula at all):
   R2/R16 one selection per query token shared by all heads; query head hq reads
       KV head hq // (Hq/Hkv).
   R15 MLA: one latent row per token; K = the whole row, V = its first d_v columns.
+  R12 fp8 keys: per token scale = max(max|k|, 1e-12)/448, bytes = e4m3fn(clamp(k/scale)),
+      round to nearest even, float32 arithmetic.
+  R22 cache append: new tokens go to positions pos0 + t; a block's HI summary is the mean
+      of its dequantised keys, brought up to date when the block's last row is written.
 """
 from __future__ import annotations
 
@@ -70,6 +74,70 @@ def index_keys_f64(kI: np.ndarray, kI_scale) -> np.ndarray:
     if kI_scale is None:
         return decode_bf16(kI)
     return decode_e4m3fn(kI) * np.asarray(kI_scale, dtype=np.float64)[..., None]
+
+
+# ----------------------------------------------------------------------------- cache append
+# The write side of a decode step. SI's window ends at the current token (reading R4), so a
+# step's new rows are in the caches before it runs; HI's coarse pass reads one summary per
+# block [P5 "technical features", third bullet], kept current as blocks fill (reading R22:
+# a block's summary is the mean of its dequantised keys, written when its last row is).
+
+def encode_e4m3fn(x: np.ndarray) -> np.ndarray:
+    """Values -> OCP e4m3fn bytes: the nearest finite value of the format (magnitudes above
+    448 take 448), ties to the code with an even mantissa; the sign bit follows the sign of
+    x (-0.0 included). From the format definition: the candidates are the decoded
+    non-negative finite codes 0x00..0x7E, which increase with the code."""
+    x = np.asarray(x, dtype=np.float64)
+    table = decode_e4m3fn(np.arange(0x7F, dtype=np.uint8))
+    a = np.minimum(np.abs(x), table[-1])
+    hi = np.clip(np.searchsorted(table, a, side="left"), 0, 0x7E)  # first value >= a
+    lo = np.maximum(hi - 1, 0)
+    d_lo, d_hi = a - table[lo], table[hi] - a
+    pick_hi = (d_hi < d_lo) | ((d_hi == d_lo) & (hi % 2 == 0))
+    code = np.where(pick_hi, hi, lo).astype(np.uint8)
+    return code | (np.signbit(x).astype(np.uint8) << np.uint8(7))
+
+
+def quantize_key_rows(k32: np.ndarray):
+    """Reading R12 for one row per token, in float32 arithmetic (the precision the pages'
+    fp8 caches are written in): scale = max(max|k|, 1e-12) / 448, bytes =
+    e4m3fn(clamp(k / scale, +-448)). Returns (bytes uint8 [n, D], scale float32 [n])."""
+    k32 = np.asarray(k32, dtype=np.float32)
+    amax = np.max(np.abs(k32), axis=-1)
+    scale = np.maximum(amax, np.float32(1e-12)) / np.float32(448.0)
+    y = np.clip(k32 / scale[..., None], np.float32(-448.0), np.float32(448.0))
+    return encode_e4m3fn(y), scale.astype(np.float32)
+
+
+def cache_append(caches: dict, k_new32: np.ndarray, rows_new: list, pos0: np.ndarray, fp8: bool):
+    """Write T new tokens per sequence at positions pos0[b] + t (positions outside [0, N)
+    are skipped). caches: 'k' (uint8 fp8 codes or uint16 bf16 bits [B, N, D]), 'scale'
+    (float32 [B, N], fp8 only), 'rows' (list of uint16 arrays [B, N, E]). k_new32: the new
+    keys as float32 [B, T, D] (bf16 values); rows_new: uint16 [B, T, E] per row set.
+    Returns the list of (b, position) written."""
+    B, T, _ = k_new32.shape
+    N = caches["k"].shape[1]
+    written = []
+    for b in range(B):
+        for t in range(T):
+            s = int(pos0[b]) + t
+            if not 0 <= s < N:
+                continue
+            if fp8:
+                code, sc = quantize_key_rows(k_new32[b, t][None])
+                caches["k"][b, s] = code[0]
+                caches["scale"][b, s] = sc[0]
+            else:
+                caches["k"][b, s] = (np.asarray(k_new32[b, t], np.float32).view(np.uint32) >> 16).astype(np.uint16)
+            for rc, rn in zip(caches["rows"], rows_new):
+                rc[b, s] = rn[b, t]
+            written.append((b, s))
+    return written
+
+
+def completed_blocks(written, Bs: int, n_blocks: int):
+    """Blocks whose last row was written: (b, j) with (s + 1) % Bs == 0, j = s // Bs < n_blocks."""
+    return sorted({(b, s // Bs) for b, s in written if (s + 1) % Bs == 0 and s // Bs < n_blocks})
 
 
 # ----------------------------------------------------------------------------- O2 positions

@@ -365,3 +365,82 @@ def test_reference_step_small_c1_shape_consistency():
     chosen = set(res["idx"][(0, 0)].tolist())
     chance = (cfg.K - cfg.S - cfg.W) / (cfg.N - cfg.T - cfg.S - cfg.W)
     assert len(sal & chosen) / len(sal) > 4 * chance
+
+
+# ----------------------------------------------------------------------------- cache append (R12, R22)
+
+def test_e4m3fn_encode_round_trips_every_finite_code():
+    codes = np.arange(256, dtype=np.uint8)
+    vals = O.decode_e4m3fn(codes)
+    fin = np.isfinite(vals)
+    assert np.array_equal(O.encode_e4m3fn(vals[fin]), codes[fin])  # -0.0 -> 0x80 included
+
+
+def test_e4m3fn_encode_ties_to_even_and_saturation():
+    # midpoints between neighbours go to the even code (mantissa LSB 0)
+    cases = {
+        1.0625: 0x38,            # between 1.0 (0x38) and 1.125 (0x39)
+        1.1875: 0x3A,            # between 1.125 (0x39) and 1.25 (0x3A)
+        2.0 ** -10: 0x00,        # between 0 and the smallest subnormal 2^-9 (0x01)
+        1.5 * 2.0 ** -9: 0x02,   # between 2^-9 (0x01) and 2^-8 (0x02)
+        2.0 ** -6 - 2.0 ** -10: 0x08,  # between the largest subnormal 7*2^-9 (0x07) and 2^-6 (0x08)
+        432.0: 0x7E,             # between 416 (0x7D) and 448 (0x7E)
+        1.0e6: 0x7E,             # beyond the range: the largest finite value
+        -1.0625: 0xB8,
+        -1.0e-30: 0x80,          # rounds to -0
+    }
+    x = np.array(list(cases), dtype=np.float64)
+    assert np.array_equal(O.encode_e4m3fn(x), np.array(list(cases.values()), dtype=np.uint8))
+    # just off a midpoint: to the nearer side
+    assert O.encode_e4m3fn(np.array([1.0625 + 1e-9, 1.1875 - 1e-9])).tolist() == [0x39, 0x39]
+
+
+def test_e4m3fn_encode_matches_torch_cast():
+    # a library routine on the special case of in-range float32 values, subnormals included
+    rng = np.random.default_rng(7)
+    x = np.concatenate([rng.uniform(-448, 448, 20000), rng.standard_normal(20000) * 1e-2,
+                        rng.standard_normal(5000) * 3e-3]).astype(np.float32)
+    ref = torch.from_numpy(x).to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+    assert np.array_equal(O.encode_e4m3fn(x), ref)
+
+
+def test_quantize_key_rows_scale_and_extremes():
+    rng = np.random.default_rng(8)
+    k = (rng.standard_normal((64, 128)) / np.sqrt(128)).astype(np.float32)
+    k[3] = 0.0
+    codes, scale = O.quantize_key_rows(k)
+    amax = np.abs(k).max(axis=1)
+    assert scale.dtype == np.float32
+    assert scale[3] == np.float32(np.float32(1e-12) / np.float32(448.0)) and not codes[3].any()
+    rows = np.arange(64) != 3
+    # the largest magnitude of each row lands on +-448 (0x7E / 0xFE)
+    j = np.abs(k).argmax(axis=1)
+    assert np.all((codes[rows, j[rows]] & 0x7F) == 0x7E)
+    # dequantised keys within half a step of 3 mantissa bits (relative 2^-4), or of the
+    # subnormal spacing 2^-9 * scale near zero
+    deq = O.decode_e4m3fn(codes) * scale[:, None].astype(np.float64)
+    err = np.abs(deq - k)
+    bound = np.maximum(np.abs(k) * 2.0 ** -4, 2.0 ** -10 * scale[:, None]) * (1 + 1e-6)
+    assert np.all(err[rows] <= bound[rows])
+    # agrees with the generator's reading of the same quantisation (torch's cast)
+    y = np.clip(k / scale[:, None], -448, 448).astype(np.float32)
+    assert np.array_equal(codes, torch.from_numpy(y).to(torch.float8_e4m3fn).view(torch.uint8).numpy())
+
+
+def test_cache_append_positions_rows_and_completed_blocks():
+    rng = np.random.default_rng(9)
+    B, N, D, T, E = 3, 256, 8, 5, 6
+    caches = {"k": np.zeros((B, N, D), np.uint8), "scale": np.zeros((B, N), np.float32),
+              "rows": [np.zeros((B, N, E), np.uint16)]}
+    k_new = rng.standard_normal((B, T, D)).astype(np.float32)
+    rows_new = [rng.integers(0, 65535, (B, T, E), dtype=np.uint16)]
+    pos0 = np.array([0, 60, 253])  # sequence 2: the last two new tokens fall past N
+    written = O.cache_append(caches, k_new, rows_new, pos0, fp8=True)
+    assert written == [(0, s) for s in range(5)] + [(1, s) for s in range(60, 65)] + [(2, 253), (2, 254), (2, 255)]
+    assert np.array_equal(caches["rows"][0][1, 60:65], rows_new[0][1])
+    assert not caches["rows"][0][1, 65:].any() and not caches["rows"][0][1, :60].any()
+    codes, sc = O.quantize_key_rows(k_new[2, :3])
+    assert np.array_equal(caches["k"][2, 253:256], codes) and np.array_equal(caches["scale"][2, 253:256], sc)
+    # blocks of 64: sequence 1 completes block 0 (row 63), sequence 2 completes block 3 (row 255)
+    assert O.completed_blocks(written, 64, 4) == [(1, 0), (2, 3)]
+    assert O.completed_blocks(written, 64, 3) == [(1, 0)]
