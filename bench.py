@@ -99,12 +99,14 @@ def pmc_traffic(index_bytes_per_launch):
 
 def measure_workloads(steps=50):
     """Step times of the other configurations (each the parity workload of its name),
-    reported beside the headline: HIP-graph replay of one captured step, inputs resident.
+    reported beside the headline: HIP-graph replay of several captured steps (the replay
+    cost shared by them), inputs resident.
       c1 tiny decode: us/step.  c3 hierarchical 1M decode: us/step, and the flat path
       (index + select over all 1M keys) on the same inputs for the HI/flat ratios.
       c4 chunked prefill: tokens/s, and the indexer's MFMA utilisation (bf16 peak).
       c5 cross-layer decode (4 layers, one selection): us/step, and the same work with
-      the selection recomputed for every layer."""
+      the selection recomputed for every layer.
+      cache append (the step's write side): us per call for the c2 and c3 cache shapes."""
     import numpy as np
     import torch
     import long_context_sparse_07_amd as L
@@ -124,7 +126,9 @@ def measure_workloads(steps=50):
             d["kI"], d["ks"] = bf16(inp["kI"]), None
         return d
 
-    def graph_us(fn):
+    def graph_us(fn, reps=1):
+        # one graph holds `reps` consecutive steps, so that the replay's own launch cost
+        # (≈14 µs here, comparable to a tiny step) is shared by them
         fn()  # allocates and caches workspaces, leaves them clean
         torch.cuda.synchronize()
         side = torch.cuda.Stream()
@@ -134,7 +138,8 @@ def measure_workloads(steps=50):
             fn()
             torch.cuda.synchronize()
             with torch.cuda.graph(g, stream=side):
-                fn()
+                for _ in range(reps):
+                    fn()
         torch.cuda.current_stream().wait_stream(side)
         torch.cuda.synchronize()
         for _ in range(5):
@@ -146,7 +151,7 @@ def measure_workloads(steps=50):
             g.replay()
         e1.record()
         torch.cuda.synchronize()
-        return e0.elapsed_time(e1) / steps * 1e3
+        return e0.elapsed_time(e1) / steps / reps * 1e3
 
     res = {}
 
@@ -177,7 +182,7 @@ def measure_workloads(steps=50):
     def w1():
         cfg, d, sc, idx, out, lse = c_flat(1)
         return {"workload": "c1 tiny decode (B=1, N=4096, T=8, 4x64 bf16 indexer, 16 heads MQA d=128, K=512)",
-                "us_per_step": graph_us(flat_step(cfg, d, sc, idx, out, lse))}
+                "us_per_step": graph_us(flat_step(cfg, d, sc, idx, out, lse), reps=20)}
 
     def w4():
         cfg, d, sc, idx, out, lse = c_flat(4)
@@ -193,7 +198,7 @@ def measure_workloads(steps=50):
 
     def w5():
         cfg, d, sc, idx, out, lse = c_flat(5)
-        us = graph_us(flat_step(cfg, d, sc, idx, out, lse))
+        us = graph_us(flat_step(cfg, d, sc, idx, out, lse), reps=10)
         out1 = torch.empty((1,) + tuple(out.shape[1:]), dtype=out.dtype, device="cuda")
         lse1 = torch.empty((1,) + tuple(lse.shape[1:]), dtype=lse.dtype, device="cuda")
 
@@ -202,7 +207,7 @@ def measure_workloads(steps=50):
                 L.lsa_index_select(d["qI"], d["w"], d["kI"], cfg.K, cfg.S, cfg.W, k_scale=d["ks"], ctx_len=d["ctx"],
                                    scores=sc, idx=idx)
                 L.lsa_attend(d["q"][l:l + 1], d["k"][l:l + 1], d["v"][l:l + 1], idx, cfg.tau, out=out1, lse=lse1)
-        us_rec = graph_us(recompute)
+        us_rec = graph_us(recompute, reps=10)
         return {"workload": "c5 cross-layer decode (B=16, N=64K, 4 layers sharing one selection, 32x128 fp8 indexer, "
                             "GQA 32/4 d=128, K=2048)",
                 "us_per_step": us, "us_per_step_selection_per_layer": us_rec, "cli_speedup": us_rec / us}
@@ -227,9 +232,9 @@ def measure_workloads(steps=50):
             L.lsa_index_select(d["qI"], d["w"], d["kI"], cfg.K, cfg.S, cfg.W, k_scale=d["ks"], ctx_len=d["ctx"],
                                kept=kept, block_size=cfg.Bs, scores=fs, idx=idx)
             L.lsa_attend(d["q"], d["k"], d["v"], idx, cfg.tau, out=out, lse=lse)
-        us = graph_us(hi)
+        us = graph_us(hi, reps=10)
         sc = torch.empty((B, T, cfg.N), dtype=torch.float32, device="cuda")
-        us_flat = graph_us(flat_step(cfg, d, sc, idx, out, lse))
+        us_flat = graph_us(flat_step(cfg, d, sc, idx, out, lse), reps=10)
         kb = 2  # bf16 indexer keys
         hi_bytes = B * nb * cfg.D_I * 4 + B * T * cfg.n_keep * cfg.Bs * cfg.D_I * kb + B * T * cfg.K * cfg.d_qk * 2
         flat_bytes = B * cfg.N * cfg.D_I * kb + B * T * cfg.K * cfg.d_qk * 2
@@ -237,7 +242,31 @@ def measure_workloads(steps=50):
                 "us_per_step": us, "steps_per_s": 1e6 / us, "us_per_step_flat": us_flat,
                 "hi_over_flat_time": us / us_flat, "hi_over_flat_bytes": hi_bytes / flat_bytes}
 
-    for name, body in (("c1", w1), ("c3", w3), ("c4", w4), ("c5", w5)):
+    def w_append():
+        # the decode step's write side for the c2 cache (8 sequences, one token each: an fp8
+        # indexer key of 128 and a 576-wide MLA row), and the c3 cache with HI summaries (one
+        # bf16 key of 64 per token; every 64th append completes a block)
+        out = {"workload": "cache append: c2 shape (B=8, T=1, fp8 key 128 + MLA row 576) and c3 shape "
+                           "(B=1, T=4, bf16 key 64, blocks of 64, summary of the completed block)"}
+        for tag, (B, N, D, fp8, row, Bs) in (("c2", (8, 131072, 128, True, 576, 0)),
+                                             ("c3", (1, 1048576, 64, False, 128, 64))):
+            T = 1 if tag == "c2" else 4
+            kc = torch.zeros((B, N, D), dtype=torch.uint8 if fp8 else torch.int16, device="cuda")
+            kc = kc.view(torch.float8_e4m3fn) if fp8 else kc.view(torch.bfloat16)
+            ks = torch.zeros((B, N), dtype=torch.float32, device="cuda") if fp8 else None
+            rc = torch.zeros((B, N, row), dtype=torch.bfloat16, device="cuda")
+            kn = torch.randn((B, T, D), device="cuda").to(torch.bfloat16)
+            rn = torch.randn((B, T, row), device="cuda").to(torch.bfloat16)
+            kbar = torch.zeros((B, N // Bs, D), dtype=torch.float32, device="cuda") if Bs else None
+            # positions whose appends complete a block (c3) or land anywhere (c2)
+            p0 = torch.full((B,), (N // 2 // 64) * 64 + 64 - T, dtype=torch.int32, device="cuda")
+            us = graph_us(lambda: L.lsa_cache_append(kn, kc, k_scale=ks, rows=[(rn, rc)], pos0=p0, kbar=kbar,
+                                                     block_size=Bs), reps=50)
+            out[f"us_{tag}"] = us
+            del kc, ks, rc, kbar
+        return out
+
+    for name, body in (("c1", w1), ("c3", w3), ("c4", w4), ("c5", w5), ("append", w_append)):
         run(name, body)
         print(f"[bench] workload {name}: {res[name]}", file=sys.stderr, flush=True)
     return res

@@ -269,6 +269,49 @@ int32_t lsa_attend(const lsa_attend_desc *desc, void *workspace, size_t workspac
 int32_t lsa_select_attend(const lsa_select_desc *sel, const lsa_attend_desc *att, void *select_ws,
                           size_t select_ws_bytes, void *attend_ws, size_t attend_ws_bytes, void *stream);
 
+/*
+ * lsa_cache_append — the write side of a decode step: T new tokens per sequence enter the
+ * caches that lsa_index and lsa_attend read. SI's local window ends at the current token
+ * (reading R4), so a step's rows are appended before the step; HI's coarse pass reads one
+ * summary per key block ("LongCat-Flash-Lite-Sparse" summary, "Technical features",
+ * first and third bullets), brought up to date here when a block's last row is written
+ * (reading R22).
+ *
+ * New token t of sequence b goes to position s = pos0[b] + t (pos0: device int32 [B],
+ * the rows already cached; NULL means N - T, i.e. the last T rows). Positions outside
+ * [0, N) are skipped (nothing is written for them).
+ *   Indexer key, k_new bf16 [B][T][D] (finite values):
+ *     k_dtype LSA_FP8_E4M3FN: k_scale[b][s] = max(max_d |k|, 1e-12) / 448 and
+ *       k_cache[b][s][d] = e4m3fn(clamp(k[d] / k_scale[b][s], -448, 448)), fp32 with
+ *       correctly rounded divisions, round to nearest even (reading R12, the same
+ *       quantisation as the fp8 key caches lsa_index reads);
+ *     k_dtype LSA_BF16: k_cache[b][s] = k_new[b][t] (copied).
+ *   Row sets (n_rows = 0, 1 or 2; e.g. one MLA latent row, or K and V): row_elems bf16
+ *     elements of rows_new[i] [B][T][row_elems] are copied to rows_cache[i] +
+ *     b*rows_stride_b[i] + s*rows_stride_n[i] (elements).
+ *   kbar (optional, fp32 [B][n_blocks][D]): for every block j = s / block_size whose last
+ *     row s ((s + 1) % block_size == 0, j < n_blocks) this call writes, kbar[b][j] is
+ *     recomputed from the cache exactly as lsa_block_means computes it (same bytes).
+ * Shapes: D in {64, 128}; row_elems, strides multiples of 8; k_new, k_cache, rows
+ * 16-byte aligned. Errors as for the other calls (LSA_E_UNSUPPORTED for other D).
+ */
+typedef struct lsa_cache_append_desc {
+    int32_t B, T, N, D;
+    const int32_t *pos0;        /* [B] rows already cached, or NULL (= N - T) */
+    const void *k_new;          /* bf16 [B][T][D] */
+    void *k_cache;              /* fp8 or bf16 [B][N][D] */
+    int32_t k_dtype;            /* LSA_FP8_E4M3FN or LSA_BF16 */
+    float *k_scale;             /* fp32 [B][N] (fp8 keys), else NULL */
+    int32_t n_rows;             /* 0, 1 or 2 */
+    const void *rows_new[2];    /* bf16 [B][T][row_elems[i]] */
+    void *rows_cache[2];        /* bf16 cache rows, strided */
+    int64_t row_elems[2], rows_stride_b[2], rows_stride_n[2];
+    float *kbar;                /* optional fp32 [B][n_blocks][D] */
+    int32_t block_size, n_blocks;
+} lsa_cache_append_desc;
+
+int32_t lsa_cache_append(const lsa_cache_append_desc *desc, void *stream);
+
 /* Zero-fill `bytes` of device memory at `ptr` with a fill kernel (for workspaces). */
 int32_t lsa_workspace_clear(void *ptr, size_t bytes, void *stream);
 

@@ -16,8 +16,9 @@ from ctypes import POINTER, c_float, c_int32, c_int64, c_size_t, c_void_p
 __all__ = ["lib", "LSAError", "lsa_index", "lsa_block_means", "lsa_select", "lsa_index_select", "lsa_attend",
            "lsa_workspace_clear", "lsa_select_workspace_bytes", "lsa_attend_workspace_bytes",
            "LSA_BF16", "LSA_FP8_E4M3FN", "LSA_F32", "LSA_INDEX_TOKENS", "LSA_INDEX_BLOCKS",
-           "LSA_WS_UNKNOWN", "LSA_WS_CLEAN", "LSA_WS_PRIMED",
-           "IndexDesc", "BlockMeansDesc", "SelectDesc", "AttendDesc", "STATUS"]
+           "LSA_WS_UNKNOWN", "LSA_WS_CLEAN", "LSA_WS_PRIMED", "lsa_select_attend", "lsa_index_select_attend",
+           "lsa_cache_append", "IndexDesc", "BlockMeansDesc", "SelectDesc", "AttendDesc", "CacheAppendDesc",
+           "STATUS"]
 
 HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(HERE, "liblsa.so")
@@ -50,6 +51,14 @@ class SelectDesc(ctypes.Structure):
                 ("causal", c_int32), ("idx", c_void_p), ("workspace_state", c_int32)]
 
 
+class CacheAppendDesc(ctypes.Structure):
+    _fields_ = [("B", c_int32), ("T", c_int32), ("N", c_int32), ("D", c_int32), ("pos0", c_void_p),
+                ("k_new", c_void_p), ("k_cache", c_void_p), ("k_dtype", c_int32), ("k_scale", c_void_p),
+                ("n_rows", c_int32), ("rows_new", c_void_p * 2), ("rows_cache", c_void_p * 2),
+                ("row_elems", c_int64 * 2), ("rows_stride_b", c_int64 * 2), ("rows_stride_n", c_int64 * 2),
+                ("kbar", c_void_p), ("block_size", c_int32), ("n_blocks", c_int32)]
+
+
 class AttendDesc(ctypes.Structure):
     _fields_ = [("B", c_int32), ("T", c_int32), ("N", c_int32), ("Hq", c_int32), ("Hkv", c_int32),
                 ("d_qk", c_int32), ("d_v", c_int32), ("q", c_void_p), ("k", c_void_p),
@@ -77,7 +86,8 @@ def lib():
         if not os.path.exists(LIB_PATH):
             raise RuntimeError(f"{LIB_PATH} is missing: build it with `python -m long_context_sparse_07_amd.build`")
         L = ctypes.CDLL(LIB_PATH)
-        for name, desc in (("lsa_index", IndexDesc), ("lsa_block_means", BlockMeansDesc)):
+        for name, desc in (("lsa_index", IndexDesc), ("lsa_block_means", BlockMeansDesc),
+                           ("lsa_cache_append", CacheAppendDesc)):
             getattr(L, name).argtypes = [POINTER(desc), c_void_p]
             getattr(L, name).restype = c_int32
         L.lsa_select.argtypes = [POINTER(SelectDesc), c_void_p, c_size_t, c_void_p]
@@ -355,3 +365,23 @@ def lsa_index_select_attend(qI, w, kI, K, sink, window, q, k, v, softmax_scale, 
     ds.workspace_state = LSA_WS_PRIMED
     _select_attend_call(ds, da, ent, q, stream)
     return scores, idx, out, lse
+
+
+def lsa_cache_append(k_new, k_cache, *, k_scale=None, rows=(), pos0=None, kbar=None, block_size=0, stream=None):
+    """Append T new tokens per sequence. k_new bf16 [B,T,D]; k_cache fp8 (with k_scale fp32
+    [B,N]) or bf16 [B,N,D]; rows: up to two (new [B,T,...] bf16 contiguous, cache
+    [B,N,...] bf16) pairs; pos0 int32 [B] (rows already cached; None = N - T); kbar fp32
+    [B,n_blocks,D] updated for the blocks this append completes."""
+    B, T, D = k_new.shape
+    N = k_cache.shape[1]
+    d = CacheAppendDesc(B=B, T=T, N=N, D=D, pos0=_ptr(pos0), k_new=_ptr(k_new), k_cache=_ptr(k_cache),
+                        k_dtype=_kdtype(k_cache), k_scale=_ptr(k_scale), n_rows=len(rows), kbar=_ptr(kbar),
+                        block_size=block_size if kbar is not None else 0,
+                        n_blocks=kbar.shape[1] if kbar is not None else 0)
+    for i, (rn, rc) in enumerate(rows):
+        d.rows_new[i] = rn.data_ptr()
+        d.rows_cache[i] = rc.data_ptr()
+        d.row_elems[i] = rn[0, 0].numel()
+        d.rows_stride_b[i] = rc.stride(0)
+        d.rows_stride_n[i] = rc.stride(1)
+    _check("lsa_cache_append", lib().lsa_cache_append(ctypes.byref(d), _stream(stream)))

@@ -383,6 +383,58 @@ int32_t lsa_select_attend(const lsa_select_desc *sd, const lsa_attend_desc *ad, 
                       "lsa_select_attend");
 }
 
+int32_t lsa_cache_append(const lsa_cache_append_desc *d, void *stream) {
+    if (!d) return fail(LSA_E_NULL, "lsa_cache_append: desc is NULL");
+    if (!d->k_new || !d->k_cache) return fail(LSA_E_NULL, "lsa_cache_append: k_new and k_cache are required");
+    if (d->B < 1 || d->T < 1 || d->N < 1) return fail(LSA_E_SHAPE, "lsa_cache_append: B, T, N must be >= 1");
+    if (d->k_dtype != LSA_FP8_E4M3FN && d->k_dtype != LSA_BF16)
+        return fail(LSA_E_DTYPE, "lsa_cache_append: the key cache must be fp8-e4m3fn or bf16");
+    const bool fp8 = d->k_dtype == LSA_FP8_E4M3FN;
+    if (fp8 && !d->k_scale) return fail(LSA_E_NULL, "lsa_cache_append: fp8 keys need k_scale");
+    if (d->D != 64 && d->D != 128) return fail(LSA_E_UNSUPPORTED, "lsa_cache_append: D must be 64 or 128");
+    if (d->n_rows < 0 || d->n_rows > 2) return fail(LSA_E_SHAPE, "lsa_cache_append: n_rows must be 0, 1 or 2");
+    if (d->B > kMaxGridY) return fail(LSA_E_UNSUPPORTED, "lsa_cache_append: B too large");
+    if (!aligned16(d->k_new) || !aligned16(d->k_cache) || (fp8 && !aligned4(d->k_scale)))
+        return fail(LSA_E_ALIGN, "lsa_cache_append: k_new and k_cache must be 16-byte aligned");
+    for (int i = 0; i < d->n_rows; ++i) {
+        if (!d->rows_new[i] || !d->rows_cache[i]) return fail(LSA_E_NULL, "lsa_cache_append: row set %d is NULL", i);
+        if (d->row_elems[i] < 8 || d->row_elems[i] % 8 || d->rows_stride_b[i] < 0 || d->rows_stride_b[i] % 8 ||
+            d->rows_stride_n[i] < d->row_elems[i] || d->rows_stride_n[i] % 8)
+            return fail(LSA_E_SHAPE, "lsa_cache_append: row set %d needs row_elems and strides multiples of 8 "
+                        "(row stride >= row_elems)", i);
+        if (!aligned16(d->rows_new[i]) || !aligned16(d->rows_cache[i]))
+            return fail(LSA_E_ALIGN, "lsa_cache_append: row set %d must be 16-byte aligned", i);
+    }
+    if (d->kbar) {
+        if (d->block_size < 1 || d->n_blocks < 1 || (int64_t)d->n_blocks * d->block_size > d->N)
+            return fail(LSA_E_SHAPE, "lsa_cache_append: kbar needs block_size >= 1, 1 <= n_blocks <= N / block_size");
+        if (!aligned4(d->kbar)) return fail(LSA_E_ALIGN, "lsa_cache_append: misaligned kbar");
+        if ((int64_t)d->T / d->block_size + 1 > 0x7FFFFFFF) return fail(LSA_E_UNSUPPORTED, "lsa_cache_append: T too large");
+    }
+    lsa::CacheAppendArgs a{};
+    a.B = d->B;
+    a.T = d->T;
+    a.N = d->N;
+    a.D = d->D;
+    a.pos0 = d->pos0;
+    a.k_new = reinterpret_cast<const uint16_t *>(d->k_new);
+    a.k_cache = d->k_cache;
+    a.fp8 = fp8;
+    a.k_scale = fp8 ? d->k_scale : nullptr;
+    a.n_rows = d->n_rows;
+    for (int i = 0; i < d->n_rows; ++i) {
+        a.rows_new[i] = reinterpret_cast<const uint16_t *>(d->rows_new[i]);
+        a.rows_cache[i] = reinterpret_cast<uint16_t *>(d->rows_cache[i]);
+        a.row_elems[i] = d->row_elems[i];
+        a.stride_b[i] = d->rows_stride_b[i];
+        a.stride_n[i] = d->rows_stride_n[i];
+    }
+    a.kbar = d->kbar;
+    a.block_size = d->kbar ? d->block_size : 1;
+    a.n_blocks = d->kbar ? d->n_blocks : 0;
+    return hip_status(lsa::launch_cache_append(a, reinterpret_cast<hipStream_t>(stream)), "lsa_cache_append");
+}
+
 int32_t lsa_workspace_clear(void *ptr, size_t bytes, void *stream) {
     if (bytes == 0) return LSA_OK;
     if (!ptr) return fail(LSA_E_NULL, "lsa_workspace_clear: ptr is NULL");

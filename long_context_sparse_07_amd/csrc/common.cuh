@@ -84,6 +84,45 @@ __device__ __forceinline__ uint32_t order_key(float x) {
     return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
 }
 
+// ---- HI block summary: element d of the mean dequantised key of the Bs rows starting at
+// row0 (fp8 bytes times the per-token scale, or bf16), summed in row order in fp32. The
+// summary kernel and the cache append both use this, so their results agree bit for bit.
+// Loads go 64 rows at a time (clamped to the block; one memory round trip for a block of
+// 64, the key type chosen outside the unrolled loads); the sum stays in row order, one
+// fused multiply-add per fp8 row.
+__device__ __forceinline__ float block_mean_d(const void *k, bool fp8, const float *k_scale, int64_t row0, int Bs,
+                                              int D, int d) {
+    constexpr int R = 64;
+    float acc = 0.0f;
+    if (fp8) {
+        const uint8_t *k8 = reinterpret_cast<const uint8_t *>(k);
+        for (int s0 = 0; s0 < Bs; s0 += R) {
+            uint32_t byte[R];
+            float sc[R];
+#pragma unroll
+            for (int u = 0; u < R; ++u) {
+                const int64_t r = row0 + min(s0 + u, Bs - 1);
+                byte[u] = k8[r * D + d];
+                sc[u] = k_scale[r];
+            }
+#pragma unroll
+            for (int u = 0; u < R; ++u)
+                if (s0 + u < Bs) acc = __builtin_fmaf(sc[u], __builtin_amdgcn_cvt_pk_f32_fp8(byte[u], false)[0], acc);
+        }
+    } else {
+        const uint16_t *k16 = reinterpret_cast<const uint16_t *>(k);
+        for (int s0 = 0; s0 < Bs; s0 += R) {
+            uint32_t h[R];
+#pragma unroll
+            for (int u = 0; u < R; ++u) h[u] = k16[(row0 + min(s0 + u, Bs - 1)) * D + d];
+#pragma unroll
+            for (int u = 0; u < R; ++u)
+                if (s0 + u < Bs) acc += u2f(h[u] << 16);
+        }
+    }
+    return acc / (float)Bs;
+}
+
 // ---- SI forced set at query position p: sink [0, sink_end) and window [win_lo, p]
 // (empty when win_lo > p); where the two overlap the window starts after the sink.
 __device__ __forceinline__ void forced_bounds(int p, int sink, int window, int &sink_end, int &win_lo) {

@@ -526,19 +526,7 @@ __global__ __launch_bounds__(128) void block_means_kernel(BlockMeansArgs a) {
     if (d >= a.D) return;
     const int Bs = a.block_size, D = a.D;
     const int64_t row0 = (int64_t)b * a.N + (int64_t)j * Bs;
-    float acc = 0.0f;
-    if (a.fp8) {
-        const uint8_t *k = reinterpret_cast<const uint8_t *>(a.k);
-        for (int s = 0; s < Bs; ++s) {
-            uint32_t byte = k[(row0 + s) * D + d];
-            float v = __builtin_amdgcn_cvt_pk_f32_fp8(byte, false)[0];
-            acc += a.k_scale[row0 + s] * v;
-        }
-    } else {
-        const uint16_t *k = reinterpret_cast<const uint16_t *>(a.k);
-        for (int s = 0; s < Bs; ++s) acc += u2f((uint32_t)k[(row0 + s) * D + d] << 16);
-    }
-    a.kbar[((int64_t)b * a.n_blocks + j) * D + d] = acc / (float)Bs;
+    a.kbar[((int64_t)b * a.n_blocks + j) * D + d] = block_mean_d(a.k, a.fp8, a.k_scale, row0, Bs, D, d);
 }
 
 int compute_units() {

@@ -51,6 +51,24 @@ struct BlockMeansArgs {
 };
 hipError_t launch_block_means(const BlockMeansArgs &a, hipStream_t s);
 
+// Cache append (the decode step's write side): new token t of sequence b goes to
+// position pos0[b] + t (pos0 NULL: N - T); positions outside [0, N) are skipped.
+struct CacheAppendArgs {
+    int B, T, N, D;
+    const int32_t *pos0;
+    const uint16_t *k_new;        // bf16 [B][T][D]
+    void *k_cache;                // fp8 or bf16 [B][N][D]
+    bool fp8;
+    float *k_scale;               // [B][N] (fp8)
+    int n_rows;                   // row sets copied (0..2)
+    const uint16_t *rows_new[2];  // bf16 [B][T][row_elems]
+    uint16_t *rows_cache[2];      // bf16, element (b, s, e) at b*stride_b + s*stride_n + e
+    int64_t row_elems[2], stride_b[2], stride_n[2];
+    float *kbar;                  // optional [B][n_blocks][D]
+    int block_size, n_blocks;
+};
+hipError_t launch_cache_append(const CacheAppendArgs &a, hipStream_t s);
+
 struct SelectArgs {
     int B, T, N;
     const int32_t *ctx_len;

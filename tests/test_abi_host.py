@@ -26,7 +26,7 @@ def test_library_exports_every_declared_function():
     names = declared_functions()
     assert {"lsa_index", "lsa_block_means", "lsa_select", "lsa_attend", "lsa_select_workspace_bytes",
             "lsa_attend_workspace_bytes", "lsa_workspace_clear", "lsa_status_str", "lsa_last_error",
-            "lsa_version", "lsa_select_attend"} <= set(names)
+            "lsa_version", "lsa_select_attend", "lsa_cache_append"} <= set(names)
     for n in names:
         assert hasattr(lib, n), f"{n} declared in lsa.h but not exported"
     assert lib.lsa_version() == 1
@@ -34,7 +34,8 @@ def test_library_exports_every_declared_function():
 
 def test_descriptor_layout_matches_c(tmp_path):
     structs = {"lsa_index_desc": L.IndexDesc, "lsa_block_means_desc": L.BlockMeansDesc,
-               "lsa_select_desc": L.SelectDesc, "lsa_attend_desc": L.AttendDesc}
+               "lsa_select_desc": L.SelectDesc, "lsa_attend_desc": L.AttendDesc,
+               "lsa_cache_append_desc": L.CacheAppendDesc}
     lines = ['#include <stdio.h>', '#include <stddef.h>', f'#include "{HEADER}"', "int main(void){"]
     for cname, py in structs.items():
         lines.append(f'printf("{cname} size %zu\\n", sizeof({cname}));')
@@ -202,6 +203,50 @@ def test_select_attend_workspace_errors():
     assert _sel_att(ds, da, FAKE, sneed, FAKE + 16, aneed) == -5
     assert L.lib().lsa_select_attend(None, ctypes.byref(da), FAKE, sneed, FAKE, aneed, None) == -1
     assert L.lib().lsa_select_attend(ctypes.byref(ds), None, FAKE, sneed, FAKE, aneed, None) == -1
+
+
+def _append_desc(rows=1, **kw):
+    d = L.CacheAppendDesc(B=2, T=1, N=1024, D=128, k_new=FAKE, k_cache=FAKE, k_dtype=L.LSA_FP8_E4M3FN,
+                          k_scale=FAKE, n_rows=rows)
+    for i in range(rows):
+        d.rows_new[i] = FAKE
+        d.rows_cache[i] = FAKE
+        d.row_elems[i] = 576
+        d.rows_stride_b[i] = 1024 * 576
+        d.rows_stride_n[i] = 576
+    for k, v in kw.items():
+        setattr(d, k, v)
+    return d
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(k_new=None), -1), (dict(k_cache=None), -1), (dict(k_scale=None), -1),
+    (dict(B=0), -2), (dict(T=0), -2), (dict(n_rows=3), -2),
+    (dict(k_dtype=L.LSA_F32), -3), (dict(D=96), -6), (dict(B=70000), -6),
+    (dict(k_new=FAKE + 8), -5), (dict(k_cache=FAKE + 4), -5),
+    (dict(kbar=FAKE, block_size=64, n_blocks=17), -2), (dict(kbar=FAKE, block_size=0, n_blocks=1), -2),
+    (dict(kbar=FAKE + 2, block_size=64, n_blocks=16), -5),
+])
+def test_cache_append_argument_errors(kw, code):
+    assert L.lib().lsa_cache_append(ctypes.byref(_append_desc(**kw)), None) == code
+    assert L.lib().lsa_last_error()
+
+
+def test_cache_append_row_set_errors():
+    lib = L.lib()
+    d = _append_desc()
+    d.row_elems[0] = 570
+    assert lib.lsa_cache_append(ctypes.byref(d), None) == -2
+    d = _append_desc()
+    d.rows_stride_n[0] = 500
+    assert lib.lsa_cache_append(ctypes.byref(d), None) == -2
+    d = _append_desc()
+    d.rows_cache[0] = FAKE + 8
+    assert lib.lsa_cache_append(ctypes.byref(d), None) == -5
+    d = _append_desc()
+    d.rows_new[0] = None
+    assert lib.lsa_cache_append(ctypes.byref(d), None) == -1
+    assert lib.lsa_cache_append(None, None) == -1
 
 
 def test_status_strings():
