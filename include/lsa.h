@@ -275,7 +275,7 @@ int32_t lsa_select_attend(const lsa_select_desc *sel, const lsa_attend_desc *att
  * (reading R4), so a step's rows are appended before the step; HI's coarse pass reads one
  * summary per key block ("LongCat-Flash-Lite-Sparse" summary, "Technical features",
  * first and third bullets), brought up to date here when a block's last row is written
- * (reading R22).
+ * (reading R25).
  *
  * New token t of sequence b goes to position s = pos0[b] + t (pos0: device int32 [B],
  * the rows already cached; NULL means N - T, i.e. the last T rows). Positions outside

@@ -34,7 +34,7 @@ Readings where the pages are silent (the pages give no formula at all):
   R15 MLA: one latent row per token; K = the whole row, V = its first d_v columns.
   R12 fp8 keys: per token scale = max(max|k|, 1e-12)/448, bytes = e4m3fn(clamp(k/scale)),
       round to nearest even, float32 arithmetic.
-  R22 cache append: new tokens go to positions pos0 + t; a block's HI summary is the mean
+  R25 cache append: new tokens go to positions pos0 + t; a block's HI summary is the mean
       of its dequantised keys, brought up to date when the block's last row is written.
 """
 from __future__ import annotations
@@ -79,7 +79,7 @@ def index_keys_f64(kI: np.ndarray, kI_scale) -> np.ndarray:
 # ----------------------------------------------------------------------------- cache append
 # The write side of a decode step. SI's window ends at the current token (reading R4), so a
 # step's new rows are in the caches before it runs; HI's coarse pass reads one summary per
-# block [P5 "technical features", third bullet], kept current as blocks fill (reading R22:
+# block [P5 "technical features", third bullet], kept current as blocks fill (reading R25:
 # a block's summary is the mean of its dequantised keys, written when its last row is).
 
 def encode_e4m3fn(x: np.ndarray) -> np.ndarray:

@@ -1,5 +1,5 @@
 """lsa_cache_append on the GPU against the oracle's cache append (reading R12 quantisation,
-reading R22 positions and block summaries).
+reading R25 positions and block summaries).
 
 Bit-exact: the fp8 key bytes and per-token scales (both sides quantise in fp32 with
 correctly rounded divisions and round-to-nearest-even), the copied bf16 rows, and the

@@ -367,7 +367,7 @@ def test_reference_step_small_c1_shape_consistency():
     assert len(sal & chosen) / len(sal) > 4 * chance
 
 
-# ----------------------------------------------------------------------------- cache append (R12, R22)
+# ----------------------------------------------------------------------------- cache append (R12, R25)
 
 def test_e4m3fn_encode_round_trips_every_finite_code():
     codes = np.arange(256, dtype=np.uint8)
