@@ -106,7 +106,9 @@ def measure_workloads(steps=50):
       c4 chunked prefill: tokens/s, and the indexer's MFMA utilisation (bf16 peak).
       c5 cross-layer decode (4 layers, one selection): us/step, and the same work with
       the selection recomputed for every layer.
-      cache append (the step's write side): us per call for the c2 and c3 cache shapes."""
+      cache append (the step's write side): us per call for the c2 and c3 cache shapes.
+      paged KV: the c2 attention over a fixed selection from the contiguous cache and
+      from page pools (pages in random order, block table lookups), us per call."""
     import numpy as np
     import torch
     import long_context_sparse_07_amd as L
@@ -266,7 +268,32 @@ def measure_workloads(steps=50):
             del kc, ks, rc, kbar
         return out
 
-    for name, body in (("c1", w1), ("c3", w3), ("c4", w4), ("c5", w5), ("append", w_append)):
+    def w_paged():
+        # c2 attention (8 sequences of 128K, MLA 64 heads, 2048 selected rows each) over the
+        # contiguous cache and over page pools of 64- and 16-row pages in random order
+        B, N, K, Hq = 8, 131072, 2048, 64
+        g = torch.Generator(device="cuda").manual_seed(7)
+        q = (torch.randn((1, B, 1, Hq, 576), device="cuda", generator=g) * 576 ** -0.5).to(torch.bfloat16)
+        k = torch.randn((1, B, N, 1, 576), device="cuda", generator=g).to(torch.bfloat16)
+        idx = torch.rand((B, N), device="cuda", generator=g).topk(K, dim=1).indices.sort(dim=1).values
+        idx = idx.to(torch.int32).view(B, 1, K).contiguous()
+        out = torch.empty((1, B, 1, Hq, 512), dtype=torch.bfloat16, device="cuda")
+        lse = torch.empty((1, B, 1, Hq), dtype=torch.float32, device="cuda")
+        res_p = {"workload": "paged KV: c2 attention (B=8, 128K, MLA 64 heads 576/512, K=2048) over a contiguous "
+                             "cache and over page pools in random page order",
+                 "us_contiguous": graph_us(lambda: L.lsa_attend(q, k, None, idx, 576 ** -0.5, out=out, lse=lse),
+                                           reps=20)}
+        for ps in (64, 16):
+            mp = N // ps
+            bt = torch.randperm(B * mp, device="cuda", generator=g).to(torch.int32).view(B, mp)
+            pool = torch.empty((1, B * mp, ps, 1, 576), dtype=torch.bfloat16, device="cuda")
+            pool[0, bt.flatten().long()] = k[0].reshape(B * mp, ps, 1, 576)
+            res_p[f"us_paged_{ps}"] = graph_us(lambda: L.lsa_attend(q, pool, None, idx, 576 ** -0.5, out=out,
+                                                                    lse=lse, block_table=bt, N=N), reps=20)
+            del pool
+        return res_p
+
+    for name, body in (("c1", w1), ("c3", w3), ("c4", w4), ("c5", w5), ("append", w_append), ("paged", w_paged)):
         run(name, body)
         print(f"[bench] workload {name}: {res[name]}", file=sys.stderr, flush=True)
     return res

@@ -226,6 +226,19 @@ int32_t lsa_select(const lsa_select_desc *desc, void *workspace, size_t workspac
  * no initial contents needed.
  * Supported: (d_qk, d_v) in {(128,128), (576,512)}, Hq % Hkv == 0, Hq/Hkv <= 64,
  * 1 <= K <= 262144, strides multiples of 8 elements.
+ * Paged caches (block_table != NULL; reading R26: the "LongCat-Flash-Lite-Sparse"
+ * summary, "Good to know", deployment bullet, has the model served by an existing engine
+ * whose launcher sets the KV cache dtype and memory split; such engines keep KV in pages
+ * named by a per-sequence table): K and V of a
+ * layer are one pool of num_pages pages of page_size rows, and position s of sequence
+ * b lives in pool row r = block_table[b][s / page_size] * page_size + s % page_size,
+ * i.e. K element (b,s,h,d) is at k[l*layer_stride_k + r*k_stride_n + h*k_stride_h + d]
+ * (k_stride_b, v_stride_b unused). block_table: device int32 [B][max_pages], owned by
+ * the caller, read only. A position whose page index is >= max_pages or whose entry is
+ * outside [0, num_pages) is skipped like an invalid idx entry. Results equal those of
+ * the contiguous layout holding the same rows, bit for bit. Errors: LSA_E_SHAPE for
+ * page_size, max_pages or num_pages < 1, or a pool above 2^31 - 1 rows.
+ * With block_table == NULL the three sizes are ignored.
  */
 typedef struct lsa_attend_desc {
     int32_t B, T, N;
@@ -244,6 +257,8 @@ typedef struct lsa_attend_desc {
     int32_t n_layers;        /* >= 1 */
     int64_t layer_stride_q, layer_stride_k, layer_stride_v, layer_stride_out, layer_stride_lse;
     int32_t n_splits;
+    const int32_t *block_table; /* paged caches: int32 [B][max_pages], or NULL (contiguous) */
+    int32_t page_size, max_pages, num_pages;
 } lsa_attend_desc;
 
 size_t lsa_attend_workspace_bytes(const lsa_attend_desc *desc);

@@ -67,7 +67,8 @@ class AttendDesc(ctypes.Structure):
                 ("idx", c_void_p), ("K", c_int32), ("softmax_scale", c_float), ("out", c_void_p),
                 ("out_dtype", c_int32), ("lse", c_void_p), ("n_layers", c_int32),
                 ("layer_stride_q", c_int64), ("layer_stride_k", c_int64), ("layer_stride_v", c_int64),
-                ("layer_stride_out", c_int64), ("layer_stride_lse", c_int64), ("n_splits", c_int32)]
+                ("layer_stride_out", c_int64), ("layer_stride_lse", c_int64), ("n_splits", c_int32),
+                ("block_table", c_void_p), ("page_size", c_int32), ("max_pages", c_int32), ("num_pages", c_int32)]
 
 
 class LSAError(RuntimeError):
@@ -263,30 +264,49 @@ def lsa_index_select(q, w, k, K, sink, window, *, k_scale=None, ctx_len=None, ke
     return scores, idx
 
 
-def _attend_desc(q, k, v, idx, softmax_scale, out, lse, mla, n_splits):
-    """q [L,B,T,Hq,dqk]; k,v [L,B,N,Hkv,d] (contiguous per layer). MLA: k [L,B,N,1,576], v=None."""
+def _attend_desc(q, k, v, idx, softmax_scale, out, lse, mla, n_splits, block_table=None, N=None):
+    """q [L,B,T,Hq,dqk]; k,v [L,B,N,Hkv,d] (contiguous per layer). MLA: k [L,B,N,1,576], v=None.
+    Paged (block_table int32 [B,max_pages]): k, v are page pools [L,num_pages,page_size,Hkv,d]
+    and N (default max_pages * page_size) bounds the positions."""
     L, B, T, Hq, dqk = q.shape
-    N, Hkv = k.shape[2], k.shape[3]
     if mla:
         v = k
         dv = 512
     else:
         dv = v.shape[-1]
     K = idx.shape[-1]
+    paged = {}
+    if block_table is not None:
+        num_pages, page_size, Hkv = k.shape[1], k.shape[2], k.shape[3]
+        for t in (k, v):
+            if t.shape[1:3] != k.shape[1:3] or t.stride(1) != page_size * t.stride(2):
+                raise ValueError("paged k, v: pools [L, num_pages, page_size, Hkv, d] with whole pages")
+        if str(block_table.dtype) != "torch.int32" or block_table.shape[0] != B or not block_table.is_contiguous():
+            raise ValueError("block_table: contiguous int32 [B, max_pages]")
+        max_pages = block_table.shape[1]
+        N = max_pages * page_size if N is None else N
+        paged = dict(block_table=_ptr(block_table), page_size=page_size, max_pages=max_pages, num_pages=num_pages)
+        strides_k = (0, k.stride(2), k.stride(3))
+        strides_v = (0, v.stride(2), v.stride(3))
+    else:
+        N, Hkv = k.shape[2], k.shape[3]
+        strides_k = (k.stride(1), k.stride(2), k.stride(3))
+        strides_v = (v.stride(1), v.stride(2), v.stride(3))
     return AttendDesc(B=B, T=T, N=N, Hq=Hq, Hkv=Hkv, d_qk=dqk, d_v=dv, q=_ptr(q), k=_ptr(k),
-                      k_stride_b=k.stride(1), k_stride_n=k.stride(2), k_stride_h=k.stride(3),
-                      v=_ptr(v), v_stride_b=v.stride(1), v_stride_n=v.stride(2), v_stride_h=v.stride(3),
+                      k_stride_b=strides_k[0], k_stride_n=strides_k[1], k_stride_h=strides_k[2],
+                      v=_ptr(v), v_stride_b=strides_v[0], v_stride_n=strides_v[1], v_stride_h=strides_v[2],
                       idx=_ptr(idx), K=K, softmax_scale=softmax_scale, out=_ptr(out),
                       out_dtype=LSA_F32 if out is not None and out.dtype.is_floating_point and out.element_size() == 4 else LSA_BF16,
                       lse=_ptr(lse), n_layers=L, layer_stride_q=q.stride(0), layer_stride_k=k.stride(0),
                       layer_stride_v=v.stride(0), layer_stride_out=out.stride(0) if out is not None else 0,
-                      layer_stride_lse=lse.stride(0) if lse is not None else 0, n_splits=n_splits)
+                      layer_stride_lse=lse.stride(0) if lse is not None else 0, n_splits=n_splits, **paged)
 
 
 def lsa_attend(q, k, v, idx, softmax_scale, *, out=None, lse=None, out_dtype=None, with_lse=True,
-               n_splits=0, workspace=None, stream=None):
+               n_splits=0, workspace=None, block_table=None, N=None, stream=None):
     """Sparse attention for L layers sharing idx. q bf16 [L,B,T,Hq,dqk]; k, v bf16
     [L,B,N,Hkv,d] (v=None: MLA latent rows, V = k[..., :512]); idx int32 [B,T,K].
+    With block_table (int32 [B,max_pages]) k, v are page pools [L,num_pages,page_size,Hkv,d].
     Returns (out [L,B,T,Hq,dv], lse fp32 [L,B,T,Hq] or None)."""
     import torch
     L, B, T, Hq, dqk = q.shape
@@ -296,7 +316,7 @@ def lsa_attend(q, k, v, idx, softmax_scale, *, out=None, lse=None, out_dtype=Non
         out = torch.empty((L, B, T, Hq, dv), dtype=out_dtype or torch.bfloat16, device=q.device)
     if lse is None and with_lse:
         lse = torch.empty((L, B, T, Hq), dtype=torch.float32, device=q.device)
-    d = _attend_desc(q, k, v, idx, softmax_scale, out, lse, mla, n_splits)
+    d = _attend_desc(q, k, v, idx, softmax_scale, out, lse, mla, n_splits, block_table, N)
     s = _stream(stream)
     need = lib().lsa_attend_workspace_bytes(ctypes.byref(d))
     ws = workspace if workspace is not None else (_workspace("attend", need, q.device)[0] if need else None)
@@ -325,10 +345,11 @@ def _select_attend_call(ds, da, sel_ent, q, stream):
 
 
 def lsa_select_attend(scores, K, sink, window, q, k, v, softmax_scale, *, N=None, ctx_len=None, causal=True,
-                      idx=None, out=None, lse=None, out_dtype=None, with_lse=True, n_splits=0, stream=None):
+                      idx=None, out=None, lse=None, out_dtype=None, with_lse=True, n_splits=0, block_table=None,
+                      stream=None):
     """lsa_select on scores, then lsa_attend on the positions it selects, as one chain
     (the attention kernel finishes the selection). Same arguments and results as the
-    two calls; no kept map. Returns (idx, out, lse)."""
+    two calls (block_table: paged k, v as in lsa_attend); no kept map. Returns (idx, out, lse)."""
     import torch
     B, T, n_cols = scores.shape
     N = n_cols if N is None else N
@@ -336,7 +357,7 @@ def lsa_select_attend(scores, K, sink, window, q, k, v, softmax_scale, *, N=None
         idx = torch.empty((B, T, K), dtype=torch.int32, device=scores.device)
     out, lse = _attend_outputs(q, v, out, lse, out_dtype, with_lse)
     ds = _select_desc(scores, K, sink, window, N, ctx_len, None, 0, causal, idx)
-    da = _attend_desc(q, k, v, idx, softmax_scale, out, lse, v is None, n_splits)
+    da = _attend_desc(q, k, v, idx, softmax_scale, out, lse, v is None, n_splits, block_table, N)
     ent = _workspace("select", lib().lsa_select_workspace_bytes(ctypes.byref(ds)), scores.device, (B, T, n_cols))
     ds.workspace_state = LSA_WS_CLEAN if ent[1] else LSA_WS_UNKNOWN
     _select_attend_call(ds, da, ent, q, stream)
@@ -345,7 +366,7 @@ def lsa_select_attend(scores, K, sink, window, q, k, v, softmax_scale, *, N=None
 
 def lsa_index_select_attend(qI, w, kI, K, sink, window, q, k, v, softmax_scale, *, k_scale=None, ctx_len=None,
                             scores=None, idx=None, out=None, lse=None, out_dtype=None, with_lse=True, n_splits=0,
-                            stream=None):
+                            block_table=None, stream=None):
     """The whole flat decode path: lsa_index (priming the selection workspace), then
     lsa_select_attend on its scores. Returns (scores, idx, out, lse)."""
     import torch
@@ -357,7 +378,7 @@ def lsa_index_select_attend(qI, w, kI, K, sink, window, q, k, v, softmax_scale, 
         idx = torch.empty((B, T, K), dtype=torch.int32, device=qI.device)
     out, lse = _attend_outputs(q, v, out, lse, out_dtype, with_lse)
     ds = _select_desc(scores, K, sink, window, N, ctx_len, None, 0, True, idx)
-    da = _attend_desc(q, k, v, idx, softmax_scale, out, lse, v is None, n_splits)
+    da = _attend_desc(q, k, v, idx, softmax_scale, out, lse, v is None, n_splits, block_table, N)
     ent = _workspace("select", lib().lsa_select_workspace_bytes(ctypes.byref(ds)), qI.device, (B, T, N))
     lsa_index(qI, w, kI, k_scale=k_scale, ctx_len=ctx_len, N=N, sink=sink, window=window, scores=scores,
               select_ws=ent[0], select_ws_state=LSA_WS_CLEAN if ent[1] else LSA_WS_UNKNOWN, stream=stream)

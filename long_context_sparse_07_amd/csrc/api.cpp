@@ -289,6 +289,13 @@ static int32_t attend_check(const lsa_attend_desc *d, lsa::AttendArgs &a) {
     if ((int64_t)d->T * d->Hkv > kMaxGridY || (int64_t)d->B * d->n_layers > kMaxGridY)
         return fail(LSA_E_UNSUPPORTED, "lsa_attend: grid too large");
     if (d->n_splits < 0) return fail(LSA_E_SHAPE, "lsa_attend: n_splits must be >= 0");
+    if (d->block_table) {
+        if (d->page_size < 1 || d->max_pages < 1 || d->num_pages < 1)
+            return fail(LSA_E_SHAPE, "lsa_attend: paged caches need page_size, max_pages, num_pages >= 1");
+        if ((int64_t)d->num_pages * d->page_size > INT32_MAX)
+            return fail(LSA_E_SHAPE, "lsa_attend: page pool of %lld rows above 2^31 - 1",
+                        (long long)d->num_pages * d->page_size);
+    }
     a = lsa::AttendArgs{};
     a.B = d->B;
     a.T = d->T;
@@ -318,6 +325,10 @@ static int32_t attend_check(const lsa_attend_desc *d, lsa::AttendArgs &a) {
     a.lsv = d->layer_stride_v;
     a.lso = d->layer_stride_out;
     a.lsl = d->layer_stride_lse;
+    a.bt = d->block_table;
+    a.page_size = d->block_table ? d->page_size : 1;
+    a.max_pages = d->block_table ? d->max_pages : 0;
+    a.num_pages = d->block_table ? d->num_pages : 0;
     a.n_splits = 1;
     int sp = d->n_splits > 0 ? d->n_splits : lsa::attend_default_splits(a);
     const int smin = (d->K + 2047) / 2048;

@@ -122,6 +122,16 @@ __global__ __launch_bounds__(64 * HW) void attend_kernel(AttendArgs a, uint16_t 
     // FUSED: Q is requested first, its latency hidden under the selection's
     if constexpr (FUSED) load_q();
     const int64_t selrow = (int64_t)b * T + t;
+    // paged caches: one row pool per layer (no per-sequence offset), position s of
+    // sequence b at row bt[b][s / page_size] * page_size + s % page_size
+    const int64_t bofs_k = a.bt ? 0 : b * a.ksb, bofs_v = a.bt ? 0 : b * a.vsb;
+    auto phys = [&](int s) -> int {  // cache row of position s in [0, N), -1 if its page is unmapped
+        if (!a.bt) return s;
+        const int pg = s / a.page_size;
+        if (pg >= a.max_pages) return -1;
+        const int pp = a.bt[(int64_t)b * a.max_pages + pg];
+        return (pp >= 0 && pp < a.num_pages) ? pp * a.page_size + (s - pg * a.page_size) : -1;
+    };
     // the workgroups sharing a selection row: splits x KV heads x layers
     const int nslices = nsplit * Hkv * a.L, slice = split + nsplit * (kvh + Hkv * layer);
     if constexpr (FUSED) {
@@ -146,10 +156,17 @@ __global__ __launch_bounds__(64 * HW) void attend_kernel(AttendArgs a, uint16_t 
             int32_t *dst = f.sa.idx + selrow * K + r0;
             for (int i = tid; i < nrows; i += NT) dst[i] = posbuf[i];
         }
+        if (a.bt) {  // positions -> cache rows (or -1), each thread its own entries
+            for (int i = tid; i < nrows; i += NT) {
+                const int ps = posbuf[i];
+                posbuf[i] = (ps >= 0 && ps < a.N) ? phys(ps) : -1;
+            }
+            __syncthreads();
+        }
     }
     const int32_t *idxrow = FUSED ? nullptr : a.idx + selrow * K + r0;
-    const uint16_t *kbase = a.k + layer * a.lsk + b * a.ksb + kvh * a.ksh;
-    const uint16_t *vbase = MLA ? kbase : a.v + layer * a.lsv + b * a.vsb + kvh * a.vsh;
+    const uint16_t *kbase = a.k + layer * a.lsk + bofs_k + kvh * a.ksh;
+    const uint16_t *vbase = MLA ? kbase : a.v + layer * a.lsv + bofs_v + kvh * a.vsh;
 
     // ---- DMA: instruction n of a tile fills block n / 2 (K blocks, then V blocks) for
     // rows 16 (n & 1) .. +15; lane l writes 16 bytes at 16 l: row 16 (n & 1) + l / 4,
@@ -178,10 +195,14 @@ __global__ __launch_bounds__(64 * HW) void attend_kernel(AttendArgs a, uint16_t 
     // Q, and so for tile 0, but not for the later tiles), then the DMA of tiles
     // 1 .. NST-2. The position list is written to LDS last, ready by the loop's first
     // barrier.
-    auto rowpos = [&](int i) {  // position of selected row i of the split, -1 if none
-        int s = -1;
-        if (i < nrows) s = FUSED ? posbuf[i] : idxrow[i];
-        return (s >= 0 && s < a.N) ? s : -1;
+    auto rowpos = [&](int i) {  // cache row of selected row i of the split, -1 if none
+        if constexpr (FUSED) {  // the position list holds cache rows when paged
+            const int s = i < nrows ? posbuf[i] : -1;
+            return (s >= 0 && (a.bt || s < a.N)) ? s : -1;
+        } else {
+            const int s = i < nrows ? idxrow[i] : -1;
+            return (s >= 0 && s < a.N) ? phys(s) : -1;
+        }
     };
     const int lpos0 = rowpos(tid);  // this thread's first entry of the LDS position list
     int dpos[G::NST - 1][2];

@@ -109,6 +109,8 @@ struct AttendArgs {
     int L;
     int64_t lsq, lsk, lsv, lso, lsl;
     int n_splits;           // resolved (>= 1)
+    const int32_t *bt;      // paged caches: block table [B][max_pages] (pool page of each
+    int page_size, max_pages, num_pages;  // logical page), else null; pool of num_pages pages
 };
 constexpr int kAttendMaxSplits = 128;  // split partials merged by one combine workgroup
 int attend_default_splits(const AttendArgs &a);

@@ -158,6 +158,11 @@ def test_select_workspace_and_pointer_errors():
     (dict(k_stride_n=577, v_stride_n=577), -5), (dict(v=FAKE + 256), -6),
     (dict(q=FAKE + 8), -5), (dict(n_layers=0), -2), (dict(n_splits=-1), -2),
     (dict(K=2048 * 128 + 1), -6),
+    # paged caches: sizes must be >= 1 and the pool's rows must fit int32
+    (dict(block_table=FAKE, page_size=0, max_pages=16, num_pages=32), -2),
+    (dict(block_table=FAKE, page_size=64, max_pages=0, num_pages=32), -2),
+    (dict(block_table=FAKE, page_size=64, max_pages=16, num_pages=0), -2),
+    (dict(block_table=FAKE, page_size=1 << 16, max_pages=16, num_pages=1 << 15), -2),
 ])
 def test_attend_argument_errors(kw, code):
     assert _att(_attend_desc(**kw)) == code

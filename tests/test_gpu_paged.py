@@ -1,0 +1,166 @@
+"""Paged KV caches (block-table indirection) in lsa_attend and the fused chains.
+
+A contiguous cache is scattered page by page into a pool of pages in random order
+(spare pages hold other random values, so a wrong page shows), with a block table
+[B][max_pages] naming the pool page of each logical page. Attention over the pool must
+equal attention over the contiguous cache bit for bit (out and lse): the same rows enter
+the same arithmetic. Unmapped pages (entry -1 or past the pool) and positions at or past
+N are skipped like padding. One case also checks the paged path against the oracle's
+float64 attention directly. Cases: MLA (64 heads) and GQA (4 KV heads, two layers),
+page sizes 1, 16 and 64, one split and many, the fused select+attend and
+index+select+attend chains.
+"""
+import numpy as np
+import pytest
+import torch
+
+import long_context_sparse_07_amd as L
+from oracle import lsa_oracle as O
+from gpu_harness import check_attn
+
+pytestmark = pytest.mark.gpu
+
+
+def _bf16(rng, shape, scale=1.0):
+    return torch.from_numpy((rng.standard_normal(shape) * scale).astype(np.float32)).to(torch.bfloat16).cuda()
+
+
+def _kv(rng, layers, B, N, Hq, Hkv, mla):
+    if mla:
+        return (_bf16(rng, (layers, B, 1, Hq, 576), 576 ** -0.5), _bf16(rng, (layers, B, N, 1, 576)), None,
+                576 ** -0.5)
+    return (_bf16(rng, (layers, B, 1, Hq, 128), 128 ** -0.5), _bf16(rng, (layers, B, N, Hkv, 128)),
+            _bf16(rng, (layers, B, N, Hkv, 128)), 128 ** -0.5)
+
+
+def _pool(rng, cache, bt, page_size, P):
+    """cache [L,B,N,H,d] scattered into a pool [L,P,page_size,H,d] of random values by bt."""
+    Ly, B, N, H, d = cache.shape
+    pool = _bf16(rng, (Ly, P, page_size, H, d), 3.0)
+    for b in range(B):
+        for j in range(bt.shape[1]):
+            n = min(page_size, N - j * page_size)
+            pool[:, bt[b, j], :n] = cache[:, b, j * page_size:j * page_size + n]
+    return pool
+
+
+def _page(rng, k, v, page_size, spare=5):
+    """k, v [L,B,N,H,d] (v None: MLA) -> (k pool, v pool or None, block table int32 [B,max_pages])."""
+    B, N = k.shape[1], k.shape[2]
+    mp = -(-N // page_size)
+    P = B * mp + spare
+    bt = rng.permutation(P)[:B * mp].reshape(B, mp).astype(np.int32)
+    kp = _pool(rng, k, bt, page_size, P)
+    vp = None if v is None else _pool(rng, v, bt, page_size, P)
+    return kp, vp, torch.from_numpy(bt).cuda()
+
+
+def _idx(rng, B, N, K):
+    """Sorted distinct positions with -1 padding and a few entries past N."""
+    idx = np.full((B, 1, K), -1, np.int32)
+    for b in range(B):
+        n = min(N, K - 8 - 3 * b)
+        idx[b, 0, :n] = np.sort(rng.choice(N, n, replace=False))
+        idx[b, 0, n:n + 3] = N + b
+    return torch.from_numpy(idx).cuda()
+
+
+def _same(o1, l1, o0, l0):
+    assert torch.equal(o1.view(torch.int16), o0.view(torch.int16)), f"{int((o1 != o0).sum())} outputs differ"
+    assert torch.equal(l1, l0)
+
+
+@pytest.mark.parametrize("mla,page_size,splits", [(True, 64, 0), (True, 16, 1), (True, 1, 5), (False, 64, 0),
+                                                  (False, 16, 3)])
+def test_paged_equals_contiguous(mla, page_size, splits):
+    rng = np.random.default_rng(900 + 10 * page_size + mla)
+    B, N, K = 3, 3000 if page_size == 1 else 7001, 1024
+    layers, Hq, Hkv = (1, 64, 1) if mla else (2, 32, 4)
+    q, k, v, scale = _kv(rng, layers, B, N, Hq, Hkv, mla)
+    idx = _idx(rng, B, N, K)
+    o0, l0 = L.lsa_attend(q, k, v, idx, scale, n_splits=splits)
+    kp, vp, bt = _page(rng, k, v, page_size)
+    o1, l1 = L.lsa_attend(q, kp, vp, idx, scale, n_splits=splits, block_table=bt, N=N)
+    torch.cuda.synchronize()
+    _same(o1, l1, o0, l0)
+
+
+def test_unmapped_pages_and_positions_past_n_are_skipped():
+    rng = np.random.default_rng(950)
+    B, N, K, ps = 2, 5000, 1536, 64
+    q, k, _, scale = _kv(rng, 1, B, N, 64, 1, True)
+    kp, _, bt = _page(rng, k, None, ps)
+    btn = bt.cpu().numpy().copy()
+    btn[0, 3] = -1                      # unmapped
+    btn[0, 10] = kp.shape[1]            # past the pool
+    btn[1, btn.shape[1] - 1] = -1       # the last (partial) page
+    bt2 = torch.from_numpy(btn).cuda()
+    idx = _idx(rng, B, N, K)
+    # N' = 4900: positions 4900 .. 4999 exist in the pool but are past N'
+    Np = 4900
+    ref = idx.cpu().numpy().copy()
+    pg = np.where(ref >= 0, ref // ps, -1)
+    dead = (ref >= Np) | ((np.arange(B)[:, None, None] == 0) & ((pg == 3) | (pg == 10))) | \
+           ((np.arange(B)[:, None, None] == 1) & (pg == btn.shape[1] - 1))
+    ref[dead] = -1
+    o0, l0 = L.lsa_attend(q, k, None, torch.from_numpy(ref).cuda(), scale)
+    o1, l1 = L.lsa_attend(q, kp, None, idx, scale, block_table=bt2, N=Np)
+    torch.cuda.synchronize()
+    _same(o1, l1, o0, l0)
+
+
+def test_paged_against_oracle():
+    rng = np.random.default_rng(960)
+    B, N, K, ps = 2, 2500, 512, 16
+    q, k, v, scale = _kv(rng, 1, B, N, 16, 2, False)
+    kp, vp, bt = _page(rng, k, v, ps)
+    idx = _idx(rng, B, N, K)
+    out, lse = L.lsa_attend(q, kp, vp, idx, scale, block_table=bt, N=N)
+    o, ls = out.float().cpu().numpy(), lse.cpu().numpy()
+    qf, kf, vf = q.float().cpu().numpy().astype(np.float64), k.float().cpu().numpy(), v.float().cpu().numpy()
+    ii = idx.cpu().numpy()
+    for b in range(B):
+        sel = ii[b, 0]
+        sel = np.where(sel < N, sel, -1)
+        want, wl = O.attend(qf[0, b, 0], kf[0, b].astype(np.float64), vf[0, b].astype(np.float64), sel, scale)
+        check_attn(o[0, b, 0], want, f"paged b={b}")
+        assert np.allclose(ls[0, b, 0], wl, atol=2e-3)
+
+
+@pytest.mark.parametrize("mla", [True, False])
+def test_paged_fused_chain(mla):
+    rng = np.random.default_rng(970 + mla)
+    B, N, K, S, W, ps = 2, 9000, 512, 32, 128, 64
+    layers, Hq, Hkv = (1, 64, 1) if mla else (2, 32, 2)
+    rows = rng.standard_normal((B, 1, N)).astype(np.float32)
+    sc = torch.from_numpy(rows).cuda()
+    q, k, v, scale = _kv(rng, layers, B, N, Hq, Hkv, mla)
+    kp, vp, bt = _page(rng, k, v, ps)
+    idx0, o0, l0 = L.lsa_select_attend(sc, K, S, W, q, k, v, scale)
+    for _ in range(2):
+        idx1, o1, l1 = L.lsa_select_attend(sc, K, S, W, q, kp, vp, scale, block_table=bt)
+        torch.cuda.synchronize()
+        assert torch.equal(idx1, idx0)
+        _same(o1, l1, o0, l0)
+    # the plain calls agree with both
+    idx2 = L.lsa_select(sc, K, S, W)
+    o2, l2 = L.lsa_attend(q, kp, vp, idx2, scale, block_table=bt, N=N)
+    assert torch.equal(idx2, idx0)
+    _same(o2, l2, o0, l0)
+
+
+def test_paged_primed_chain():
+    from synth import config, make_inputs
+    from gpu_harness import upload
+    cfg = config(2, B=2, N=9000, K=512, S=32, W=128)
+    d = upload(make_inputs(cfg))
+    rng = np.random.default_rng(980)
+    q, k, _, scale = _kv(rng, 1, cfg.B, cfg.N, 64, 1, True)
+    kp, _, bt = _page(rng, k, None, 64)
+    ref = L.lsa_index_select_attend(d["qI"], d["w"], d["kI"], cfg.K, cfg.S, cfg.W, q, k, None, scale,
+                                    k_scale=d["kI_scale"], ctx_len=d["ctx_len"])
+    got = L.lsa_index_select_attend(d["qI"], d["w"], d["kI"], cfg.K, cfg.S, cfg.W, q, kp, None, scale,
+                                    k_scale=d["kI_scale"], ctx_len=d["ctx_len"], block_table=bt)
+    torch.cuda.synchronize()
+    assert torch.equal(got[0], ref[0]) and torch.equal(got[1], ref[1])
+    _same(got[2], got[3], ref[2], ref[3])
