@@ -36,6 +36,9 @@ Readings where the pages are silent (the pages give no formula at all):
       round to nearest even, float32 arithmetic.
   R25 cache append: new tokens go to positions pos0 + t; a block's HI summary is the mean
       of its dequantised keys, brought up to date when the block's last row is written.
+  R27 fp8-query indexer (an option of the token scores, fp8 keys only): each (token,
+      head) query row is quantised as R12 quantises a key row, and the score is R1's
+      with the dequantised rows.
 """
 from __future__ import annotations
 
@@ -67,6 +70,23 @@ def decode_e4m3fn(codes: np.ndarray) -> np.ndarray:
     val = np.where(e == 0, sub, normal)
     val = np.where((e == 15) & (m == 7), np.nan, val)
     return np.where(sign == 1, -val, val)
+
+
+def index_query_f64(qI_bits: np.ndarray, fp8_query: bool = False) -> np.ndarray:
+    """Indexer query rows (bf16 bits [..., D]) -> float64 (R1).
+
+    fp8_query (reading R27; the indexer the pages' LSA extends runs its contraction in
+    fp8, [P3] "The sparse attention problem at 1M tokens"): every row (one token, one
+    head) is quantised by R12's procedure, codes c and scale s_q, and enters the score
+    as s_q * e4m3fn(c). Since ReLU(s x) = s ReLU(x) for s > 0, the score equals
+    scale_k[s] * sum_h (w[h] * s_q[h]) * ReLU(c_h . c_k), the form an fp8 x fp8
+    contraction computes.
+    """
+    q = decode_bf16(qI_bits)
+    if not fp8_query:
+        return q
+    codes, scale = quantize_key_rows(q.astype(np.float32))
+    return decode_e4m3fn(codes) * scale.astype(np.float64)[..., None]
 
 
 def index_keys_f64(kI: np.ndarray, kI_scale) -> np.ndarray:
@@ -341,6 +361,8 @@ def reference_step(inp: dict, rows=None, layers=None, with_attend: bool = True) 
     if rows is None:
         rows = [(b, t) for b in range(B) for t in range(T)]
     L = cfg.layers if layers is None else layers
+    if cfg.hi and getattr(cfg, "q_fp8", False):
+        raise NotImplementedError("R27 covers the token scores; the coarse block pass keeps bf16 queries")
     res = {"idx": {}, "kept": {}, "scores": {}, "cand": {}, "out": {}, "lse": {}}
     by_b = {}
     for b, t in rows:
@@ -351,7 +373,7 @@ def reference_step(inp: dict, rows=None, layers=None, with_attend: bool = True) 
         kv = {}
         for t in ts:
             p = int(P[b, t])
-            qI = decode_bf16(inp["qI"][b, t])
+            qI = index_query_f64(inp["qI"][b, t], getattr(cfg, "q_fp8", False))
             w = np.asarray(inp["w"][b, t], dtype=np.float64)
             if cfg.hi:
                 idx, kept, cand, sc = select_tokens_hi(qI, w, keys, kbar, p, cfg.K, cfg.S,

@@ -63,6 +63,7 @@ class LSAConfig:
     S: int                  # sink
     W: int                  # local window (ends at the query position, inclusive)
     hi: bool = False        # hierarchical (block) pre-selection
+    q_fp8: bool = False     # indexer queries quantised to fp8 per (token, head) row
     Bs: int = 64            # HI block size
     n_keep: int = 256       # HI kept blocks per query token
     layers: int = 1         # consecutive layers sharing one selection (CLI)

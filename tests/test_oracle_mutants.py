@@ -35,7 +35,9 @@ ALL = ["test_golden_hand_worked_flat_and_hi", "test_indexer_single_head_is_relu_
        "test_selection_matches_rank_counting", "test_selection_without_forced_is_lexsort_and_partition",
        "test_hi_matches_brute_force", "test_hi_all_blocks_kept_equals_flat",
        "test_budget_covers_context_equals_dense_causal", "test_attention_closed_forms",
-       "test_attention_permutation_invariant_and_gqa_mapping", "test_e4m3fn_matches_torch_all_codes"]
+       "test_attention_permutation_invariant_and_gqa_mapping", "test_e4m3fn_matches_torch_all_codes",
+       "test_fp8_query_worked_example", "test_fp8_query_exact_for_representable_rows",
+       "test_fp8_query_error_bound_rows_and_scaling", "test_fp8_query_score_is_the_fp8_contraction"]
 
 
 def _no_relu(q, w, keys, p):
@@ -103,6 +105,24 @@ def _e4m3_bias8(codes):
     return np.where((c >> 7) == 1, -val, val)
 
 
+def _query_no_scale(qI_bits, fp8_query=False):
+    q = O.decode_bf16(qI_bits)
+    if not fp8_query:
+        return q
+    codes, _ = O.quantize_key_rows(q.astype(np.float32))
+    return O.decode_e4m3fn(codes)
+
+
+def _query_shared_scale(qI_bits, fp8_query=False):
+    # one scale for the whole query (all heads) instead of one per row
+    q = O.decode_bf16(qI_bits)
+    if not fp8_query:
+        return q
+    s = np.float32(max(np.abs(q).max(), 1e-12)) / np.float32(448.0)
+    y = np.clip(q.astype(np.float32) / s, -448.0, 448.0)
+    return O.decode_e4m3fn(O.encode_e4m3fn(y)) * np.float64(s)
+
+
 MUTANTS = [
     ("indexer_scores", _no_relu),
     ("indexer_scores", _max_heads),
@@ -113,6 +133,8 @@ MUTANTS = [
     ("attend", _attend_no_tau),
     ("attend", _attend_modulo_heads),
     ("decode_e4m3fn", _e4m3_bias8),
+    ("index_query_f64", _query_no_scale),
+    ("index_query_f64", _query_shared_scale),
 ]
 
 

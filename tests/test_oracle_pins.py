@@ -444,3 +444,77 @@ def test_cache_append_positions_rows_and_completed_blocks():
     # blocks of 64: sequence 1 completes block 0 (row 63), sequence 2 completes block 3 (row 255)
     assert O.completed_blocks(written, 64, 4) == [(1, 0), (2, 3)]
     assert O.completed_blocks(written, 64, 3) == [(1, 0)]
+
+
+# ----------------------------------------------------------------------------- fp8-query indexer (R27)
+
+def _bf16_bits(x):
+    x = np.asarray(x, dtype=np.float32)
+    bits = (x.view(np.uint32) >> 16).astype(np.uint16)
+    assert np.array_equal(O.decode_bf16(bits), x.astype(np.float64)), "value not exact in bf16"
+    return bits
+
+
+def test_fp8_query_worked_example():
+    # q = (2, -1, 0.5, 13/128): amax 2, scale s = 2/448 in fp32; q/s = 448, -224, 112,
+    # 22.75 -> codes 448, -224, 112 and 22 (22.75 lies between the grid points 22 and 24)
+    bits = _bf16_bits([2.0, -1.0, 0.5, 0.1015625])
+    s = float(np.float32(2.0) / np.float32(448.0))
+    deq = O.index_query_f64(bits[None], True)[0]
+    assert np.array_equal(deq, np.array([448.0, -224.0, 112.0, 22.0]) * s)
+    assert np.array_equal(O.index_query_f64(bits[None], False)[0], [2.0, -1.0, 0.5, 0.1015625])
+    # one head of weight 0.5 against the key (1, 1, 1, 1): 0.5 * (448 - 224 + 112 + 22) * s
+    sc = O.indexer_scores(deq[None], np.array([0.5]), np.ones((1, 4)), 0)
+    assert sc[0] == 0.5 * 358.0 * s
+
+
+def test_fp8_query_exact_for_representable_rows():
+    # rows that are e4m3 values times 2^-6 with a 448 * 2^-6 entry: scale 2^-6 exactly,
+    # every code reproduces its element, so the quantised query equals the bf16 query
+    rng = np.random.default_rng(27)
+    codes = rng.integers(0, 256, (3, 5, 64)).astype(np.uint8)
+    codes[(codes & 0x7F) == 0x7F] = 0x3C            # no NaN codes
+    codes[..., 7] = 0x7E                             # +448
+    q = O.decode_e4m3fn(codes) * 2.0 ** -6
+    bits = _bf16_bits(q.astype(np.float32))
+    assert np.array_equal(O.index_query_f64(bits, True), O.decode_bf16(bits))
+
+
+def test_fp8_query_error_bound_rows_and_scaling():
+    rng = np.random.default_rng(28)
+    x = rng.standard_normal((4, 8, 128)).astype(np.float32)
+    x *= (2.0 ** rng.integers(-10, 10, (4, 8, 1))).astype(np.float32)   # row magnitudes differ
+    bits = _bf16_bits_round(x)
+    q = O.decode_bf16(bits)
+    deq = O.index_query_f64(bits, True)
+    s = np.maximum(np.abs(q).max(axis=-1, keepdims=True), 1e-12) / 448.0
+    # round to nearest on the e4m3 grid: relative 2^-4 (normal codes), 2^-10 * s (subnormal)
+    assert np.all(np.abs(deq - q) <= np.maximum(2.0 ** -4 * np.abs(q), 2.0 ** -10 * s) * (1 + 1e-6))
+    # each row on its own scale: quantising rows one at a time changes nothing
+    for t in range(4):
+        for h in range(8):
+            assert np.array_equal(O.index_query_f64(bits[t, h][None], True)[0], deq[t, h])
+    # doubling a row (exact in bf16) doubles its dequantised values exactly
+    bits2 = _bf16_bits((q * 2.0).astype(np.float32))
+    assert np.array_equal(O.index_query_f64(bits2, True), 2.0 * deq)
+
+
+def _bf16_bits_round(x):
+    """float32 -> bf16 bits, round to nearest even (torch's cast)."""
+    return torch.from_numpy(np.ascontiguousarray(x, dtype=np.float32)).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+
+
+def test_fp8_query_score_is_the_fp8_contraction():
+    # scale_k * sum_h (w_h * s_q,h) * ReLU(codes_h . codes_k) in exact arithmetic on the
+    # decoded codes (every product of two e4m3 values and their 128-term sums are exact
+    # in float64) equals the score of the dequantised rows
+    rng = np.random.default_rng(29)
+    H, D, n = 16, 128, 40
+    bits = _bf16_bits_round(rng.standard_normal((H, D)).astype(np.float32))
+    w = rng.random(H)
+    kc, ks = O.quantize_key_rows(rng.standard_normal((n, D)).astype(np.float32))
+    qc, qs = O.quantize_key_rows(O.decode_bf16(bits).astype(np.float32))
+    dots = O.decode_e4m3fn(kc) @ O.decode_e4m3fn(qc).T                    # [n, H], exact
+    want = ks.astype(np.float64) * (np.maximum(dots, 0.0) @ (w * qs.astype(np.float64)))
+    got = O.indexer_scores(O.index_query_f64(bits, True), w, O.index_keys_f64(kc, ks), n - 1)
+    assert np.allclose(got, want, rtol=1e-12, atol=0)
