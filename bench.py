@@ -47,7 +47,42 @@ def parse():
                     help="skip the other configurations' step times (extra.workloads)")
     ap.add_argument("--calib-copy", action="store_true",
                     help="with --profile-only: also run one elementwise add of known traffic (counter calibration)")
+    ap.add_argument("--profile-c4-index", action="store_true",
+                    help="only the c4 prefill indexer, bf16 then fp8 queries, `--steps` calls each (for rocprofv3)")
     return ap.parse_args()
+
+
+def profile_c4_index(steps, warmup):
+    """The c4 chunked-prefill indexer (4096 queries after 256K keys, 64x128 fp8 keys), with
+    bf16 queries and with fp8 queries: plain launches, timed with events."""
+    import numpy as np
+    import torch
+    import long_context_sparse_07_amd as L
+    from synth import config, make_inputs
+    cfg = config(4)
+    inp = make_inputs(cfg, with_kv=False)
+    bf = lambda a: torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).view(torch.bfloat16).cuda()
+    qI, w = bf(inp["qI"]), torch.from_numpy(inp["w"]).cuda()
+    kI = torch.from_numpy(inp["kI"]).cuda().view(torch.float8_e4m3fn)
+    ks, ctx = torch.from_numpy(inp["kI_scale"]).cuda(), torch.from_numpy(inp["ctx_len"]).cuda()
+    sc = torch.empty((cfg.B, cfg.T, cfg.N), dtype=torch.float32, device="cuda")
+    flops = 2.0 * sum(cfg.N - cfg.T + t + 1 for t in range(cfg.T)) * cfg.H_I * cfg.D_I
+    res = {"profile_c4_index": True}
+    for q8 in (False, True):
+        f = lambda: L.lsa_index(qI, w, kI, k_scale=ks, ctx_len=ctx, scores=sc, q_fp8=q8)
+        for _ in range(warmup):
+            f()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(steps):
+            f()
+        e1.record()
+        torch.cuda.synchronize()
+        us = e0.elapsed_time(e1) / steps * 1e3
+        res["fp8_query" if q8 else "bf16_query"] = {"us": us, "tflops": flops / us / 1e6}
+        print(f"[bench] c4 index q_fp8={q8}: {us:.0f} us", file=sys.stderr, flush=True)
+    print(json.dumps(res))
 
 
 def algorithmic_bytes(cfg):
@@ -193,10 +228,15 @@ def measure_workloads(steps=50):
         p0 = cfg.N - cfg.T
         pairs = sum(p0 + t + 1 for t in range(cfg.T))
         flops = 2.0 * pairs * cfg.H_I * cfg.D_I
+        # the fp8-query indexer (queries quantised per row, fp8 x fp8 matrix instructions)
+        us_index_q8 = graph_us(lambda: L.lsa_index(d["qI"], d["w"], d["kI"], k_scale=d["ks"], ctx_len=d["ctx"],
+                                                   scores=sc, q_fp8=True))
         return {"workload": "c4 chunked prefill (4096 queries after 256K, 64x128 fp8 indexer, GQA 64/8 d=128, K=2048)",
                 "us_per_step": us, "prefill_tokens_per_s": cfg.B * cfg.T / (us * 1e-6), "us_index": us_index,
                 "index_tflops": flops / (us_index * 1e-6) / 1e12,
-                "index_mfma_frac_of_bf16_peak": flops / (us_index * 1e-6) / 2.5e15}
+                "index_mfma_frac_of_bf16_peak": flops / (us_index * 1e-6) / 2.5e15,
+                "us_index_fp8_query": us_index_q8, "index_fp8_query_tflops": flops / (us_index_q8 * 1e-6) / 1e12,
+                "index_fp8_query_frac_of_fp8_peak": flops / (us_index_q8 * 1e-6) / 5.0e15}
 
     def w5():
         cfg, d, sc, idx, out, lse = c_flat(5)
@@ -305,6 +345,9 @@ def main():
         print(f"bench.py measures one GPU only (got --gpus {args.gpus}); this build has no multi-GPU path.",
               file=sys.stderr)
         sys.exit(2)
+    if args.profile_c4_index:
+        profile_c4_index(args.steps, args.warmup)
+        return
     import ctypes
     import numpy as np
     import torch

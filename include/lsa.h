@@ -82,6 +82,15 @@ extern "C" {
  *   for s <= p, and -inf for s > p. k_scale is NULL for bf16 keys (scale 1).
  *   The contraction runs as bf16 x bf16 products with fp32 accumulation; fp8 keys
  *   are widened exactly to bf16.
+ *   q_dtype = LSA_FP8_E4M3FN (fp8 keys, D = 128, TOKENS only; reading R27: the DSA
+ *   indexer that LSA extends contracts in fp8, molayo1419.me LongCat-2.0 article,
+ *   "The sparse attention problem at 1M tokens"): each query row q[b][t][h] is first
+ *   quantised as the fp8 key rows are, s_q = max(max_d |q|, 1e-12) / 448 and codes
+ *   c = e4m3fn(clamp(q / s_q, -448, 448)) in fp32, round to nearest even, and the score
+ *   uses s_q * c in place of q: k_scale * sum_h (w * s_q) * max(0, c . k), computed as
+ *   fp8 x fp8 products with fp32 accumulation (the matrix unit adds the 64 products of
+ *   one instruction with a truncated alignment: relative error up to about 2^-11 of
+ *   the largest product). q_dtype 0 or LSA_BF16: bf16 queries as above.
  * TOKENS, HI fine stage (kept != NULL): column c of query (b,t) stands for position
  *   s = kept[b][t][c / block_size] * block_size + c % block_size, c < n_keep *
  *   block_size; the score is as above. Columns whose kept entry is -1 or outside
@@ -134,6 +143,7 @@ typedef struct lsa_index_desc {
     void *select_ws;         /* optional (TOKENS): workspace of the lsa_select that reads scores */
     size_t select_ws_bytes;
     int32_t select_ws_state; /* LSA_WS_UNKNOWN or LSA_WS_CLEAN: state of select_ws on entry */
+    int32_t q_dtype;         /* TOKENS: 0 or LSA_BF16 (bf16 contraction), LSA_FP8_E4M3FN (reading R27) */
 } lsa_index_desc;
 
 int32_t lsa_index(const lsa_index_desc *desc, void *stream);

@@ -36,7 +36,8 @@ class IndexDesc(ctypes.Structure):
                 ("w", c_void_p), ("k", c_void_p), ("k_dtype", c_int32), ("k_scale", c_void_p),
                 ("kept", c_void_p), ("n_keep", c_int32), ("block_size", c_int32),
                 ("n_blocks", c_int32), ("sink", c_int32), ("window", c_int32), ("scores", c_void_p),
-                ("select_ws", c_void_p), ("select_ws_bytes", c_size_t), ("select_ws_state", c_int32)]
+                ("select_ws", c_void_p), ("select_ws_bytes", c_size_t), ("select_ws_state", c_int32),
+                ("q_dtype", c_int32)]
 
 
 class BlockMeansDesc(ctypes.Structure):
@@ -164,10 +165,11 @@ def lsa_workspace_clear(buf, stream=None):
 
 def lsa_index(q, w, k, *, k_scale=None, ctx_len=None, kept=None, block_size=0, mode=LSA_INDEX_TOKENS,
               N=None, n_blocks=0, sink=0, window=0, scores=None, select_ws=None, select_ws_state=LSA_WS_UNKNOWN,
-              stream=None):
+              q_fp8=False, stream=None):
     """Indexer scores. q bf16 [B,T,H,D], w fp32 [B,T,H]; k bf16/fp8 [B,N,D] (tokens) or
     fp32 block means [B,n_blocks,D] (mode=LSA_INDEX_BLOCKS, N = cache rows). With
-    select_ws (a uint8 tensor), the selection workspace is primed for these scores."""
+    select_ws (a uint8 tensor), the selection workspace is primed for these scores.
+    q_fp8: quantise each query row to fp8 and contract fp8 x fp8 (fp8 keys, D=128)."""
     import torch
     B, T, H, D = q.shape
     if mode == LSA_INDEX_TOKENS:
@@ -184,7 +186,7 @@ def lsa_index(q, w, k, *, k_scale=None, ctx_len=None, kept=None, block_size=0, m
                   k_dtype=_kdtype(k), k_scale=_ptr(k_scale), kept=_ptr(kept), n_keep=n_keep,
                   block_size=block_size, n_blocks=n_blocks, sink=sink, window=window, scores=_ptr(scores),
                   select_ws=_ptr(select_ws), select_ws_bytes=0 if select_ws is None else select_ws.numel(),
-                  select_ws_state=select_ws_state)
+                  select_ws_state=select_ws_state, q_dtype=LSA_FP8_E4M3FN if q_fp8 else 0)
     _check("lsa_index", lib().lsa_index(ctypes.byref(d), _stream(stream)))
     return scores
 
@@ -238,7 +240,7 @@ def lsa_select(scores, K, sink=0, window=0, *, N=None, ctx_len=None, kept=None, 
 
 
 def lsa_index_select(q, w, k, K, sink, window, *, k_scale=None, ctx_len=None, kept=None, block_size=0,
-                     scores=None, idx=None, stream=None):
+                     scores=None, idx=None, q_fp8=False, stream=None):
     """lsa_index with a primed selection workspace, then lsa_select on its scores
     (causal token selection): the same result as the two calls made separately, without
     the selection's first pass over the scores. Returns (scores, idx)."""
@@ -256,7 +258,7 @@ def lsa_index_select(q, w, k, K, sink, window, *, k_scale=None, ctx_len=None, ke
     ws = ent[0]
     lsa_index(q, w, k, k_scale=k_scale, ctx_len=ctx_len, kept=kept, block_size=block_size, N=N, sink=sink,
               window=window, scores=scores, select_ws=ws, select_ws_state=LSA_WS_CLEAN if ent[1] else LSA_WS_UNKNOWN,
-              stream=stream)
+              q_fp8=q_fp8, stream=stream)
     ent[1] = False
     d.workspace_state = LSA_WS_PRIMED
     _check("lsa_select", lib().lsa_select(ctypes.byref(d), ws.data_ptr(), ws.numel(), _stream(stream)))

@@ -82,6 +82,11 @@ int32_t lsa_index(const lsa_index_desc *d, void *stream) {
         }
         if (!lsa::index_tokens_supported(d->H, d->D, hi))
             return fail(LSA_E_UNSUPPORTED, "lsa_index: no token kernel for H=%d D=%d%s", d->H, d->D, hi ? " (HI)" : "");
+        if (d->q_dtype != 0 && d->q_dtype != LSA_BF16 && d->q_dtype != LSA_FP8_E4M3FN)
+            return fail(LSA_E_DTYPE, "lsa_index: q_dtype must be 0, LSA_BF16 or LSA_FP8_E4M3FN (got %d)", d->q_dtype);
+        const bool qf8 = d->q_dtype == LSA_FP8_E4M3FN;
+        if (qf8 && (!fp8 || d->D != 128))
+            return fail(LSA_E_UNSUPPORTED, "lsa_index: fp8 queries need fp8 keys and D=128");
         if (d->select_ws) {
             if (d->sink < 0 || d->window < 0) return fail(LSA_E_SHAPE, "lsa_index: sink and window must be >= 0");
             if (d->select_ws_state != LSA_WS_UNKNOWN && d->select_ws_state != LSA_WS_CLEAN)
@@ -106,6 +111,7 @@ int32_t lsa_index(const lsa_index_desc *d, void *stream) {
         a.w = d->w;
         a.k = d->k;
         a.fp8 = fp8;
+        a.qf8 = qf8;
         a.k_scale = fp8 ? d->k_scale : nullptr;
         a.kept = d->kept;
         a.n_keep = hi ? d->n_keep : 0;

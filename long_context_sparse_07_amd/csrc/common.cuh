@@ -27,6 +27,15 @@ __device__ __forceinline__ f32x4 mfma16(bf16x8 a, bf16x8 b, f32x4 c) {
 __device__ __forceinline__ f32x16 mfma32(bf16x8 a, bf16x8 b, f32x16 c) {
     return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
 }
+// 32x32 fp32 += (32 x 64 e4m3) x (64 x 32 e4m3), unscaled (v_mfma_f32_32x32x64_f8f6f4):
+// lane l supplies 32 bytes of row (A) / column (B) l % 32; lanes l and l + 32 hold
+// complementary halves of the 64-long contraction, the same for A and B, so any fixed
+// assignment of contraction indices to (lane half, byte) shared by both operands sums
+// every index once
+typedef __attribute__((ext_vector_type(8))) int i32x8;
+__device__ __forceinline__ f32x16 mfma32_fp8(i32x8 a, i32x8 b, f32x16 c) {
+    return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, c, 0, 0, 0, 0, 0, 0);
+}
 
 // ---- bit casts
 __device__ __forceinline__ uint32_t f2u(float x) { return __builtin_bit_cast(uint32_t, x); }

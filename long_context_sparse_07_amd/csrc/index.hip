@@ -8,7 +8,10 @@
 // contraction runs on
 // v_mfma_f32_32x32x16_bf16 with fp8 keys widened exactly to bf16 in registers; the
 // ReLU, head weights, head sum, per-token scale and causal mask are fused into the
-// MFMA epilogue.
+// MFMA epilogue. With fp8 queries (an option for fp8 keys: each query row quantised
+// like a key row, its scale folded into the head weight, since ReLU(s x) = s ReLU(x)
+// for s > 0) the contraction runs on v_mfma_f32_32x32x64_f8f6f4 straight from the fp8
+// key bytes in LDS.
 //
 // index_blocks_kernel: coarse HI block scores max_h w * ReLU(q . kbar) in fp32 (VALU),
 // so that the block means are not rounded to bf16 (LongCat-Flash-Lite-Sparse summary,
@@ -102,10 +105,11 @@ __device__ __forceinline__ void row_to_th(int grp, int i, int H, int T, int &t, 
 // HIST (one query per workgroup): the epilogue also counts the selection candidates of
 // its columns per first-level bin of the selection histogram (finite scores at visible
 // positions outside the sink and the window) and adds the counts to sel_hist.
-template <int D, bool FP8, int MODE, int HB, bool HI, bool PRE, bool HIST, int NST>
+template <int D, bool FP8, bool QF8, int MODE, int HB, bool HI, bool PRE, bool HIST, int NST>
 __global__ __launch_bounds__(PRE ? kThreads : 2 * kThreads) void index_tokens_kernel(IndexTokensArgs a, int groups,
                                                                                       int chunk) {
     using G = Tile<D, FP8, NST>;
+    static_assert(!QF8 || FP8, "fp8 queries need fp8 keys");
     // SPLIT (one query group per workgroup): waves 0-3 compute, waves 4-7 only stream the
     // key tiles into the LDS ring, so a DMA issue that stalls on a full memory queue
     // never holds up the MFMA and VALU work. Otherwise (four query groups share each
@@ -142,7 +146,10 @@ __global__ __launch_bounds__(PRE ? kThreads : 2 * kThreads) void index_tokens_ke
     if constexpr (HIST) __syncthreads();
 
     // ---- query fragments (A operand, rows = query heads) and head weights (compute waves)
-    bf16x8 aq[HB][KSTEPS];
+    // lane (l32, half) holds dims (D / 2) half .. +D/2 of row 32 hb + l32
+    constexpr int KF8 = D / 64;  // fp8 MFMA steps: dims (D / 2) half + 32 kk .. +32
+    bf16x8 aq[HB][QF8 ? 1 : KSTEPS];
+    i32x8 aq8[HB][QF8 ? KF8 : 1];
     float wreg[HB][16];
 #pragma unroll
     for (int hb = 0; hb < HB; ++hb) {
@@ -151,17 +158,44 @@ __global__ __launch_bounds__(PRE ? kThreads : 2 * kThreads) void index_tokens_ke
         row_to_th<MODE>(grp, 32 * hb + l32, H, T, t, h, ok);
         ok = ok && active && !producer;
         const uint16_t *qrow = a.q + ((int64_t)(b * T + t) * H + h) * D + (D / 2) * half;
+        u32x4 qv[KSTEPS];
 #pragma unroll
         for (int ks = 0; ks < KSTEPS; ++ks) {
             u32x4 v = {0, 0, 0, 0};
             if (ok) v = *reinterpret_cast<const u32x4 *>(qrow + 8 * ks);
-            aq[hb][ks] = __builtin_bit_cast(bf16x8, v);
+            qv[ks] = v;
+            if constexpr (!QF8) aq[hb][ks] = __builtin_bit_cast(bf16x8, v);
+        }
+        float qs = 1.0f;  // QF8: the row's scale, max(amax, 1e-12) / 448
+        if constexpr (QF8) {
+            float amax = 0.0f;
+#pragma unroll
+            for (int ks = 0; ks < KSTEPS; ++ks)
+#pragma unroll
+                for (int e = 0; e < 4; ++e)
+                    amax = fmaxf(amax, fmaxf(fabsf(bf16lo(qv[ks][e])), fabsf(bf16hi(qv[ks][e]))));
+            amax = fmaxf(amax, __shfl_xor(amax, 32, 64));  // the row's other half
+            qs = fmaxf(amax, 1e-12f) / 448.0f;
+            auto code = [&](float x) { return fminf(fmaxf(x / qs, -448.0f), 448.0f); };
+#pragma unroll
+            for (int kk = 0; kk < KF8; ++kk)
+#pragma unroll
+                for (int wi = 0; wi < 8; ++wi) {  // bytes 4 wi .. +3: dims 32 kk + 4 wi .. +3
+                    const int dd = 32 * kk + 4 * wi;
+                    const uint32_t lo = qv[dd / 8][(dd % 8) / 2], hi = qv[dd / 8][(dd % 8) / 2 + 1];
+                    uint32_t wv = __builtin_amdgcn_cvt_pk_fp8_f32(code(bf16lo(lo)), code(bf16hi(lo)), 0, false);
+                    wv = __builtin_amdgcn_cvt_pk_fp8_f32(code(bf16lo(hi)), code(bf16hi(hi)), wv, true);
+                    aq8[hb][kk][wi] = (int)wv;
+                }
         }
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
-            int i = 32 * hb + 8 * (r / 4) + 4 * half + (r % 4);
+            const int rb = 8 * (r / 4) + 4 * half + (r % 4);  // C row within the block
+            const int i = 32 * hb + rb;
             row_to_th<MODE>(grp, i, H, T, t, h, ok);
-            wreg[hb][r] = (ok && active && !producer) ? a.w[(int64_t)(b * T + t) * H + h] : 0.0f;
+            float wv = (ok && active && !producer) ? a.w[(int64_t)(b * T + t) * H + h] : 0.0f;
+            if constexpr (QF8) wv *= __shfl(qs, rb, 64);  // lane rb holds row rb's scale
+            wreg[hb][r] = wv;
         }
     }
     // SPLIT: the compute waves wait for their query and weight loads here, before any
@@ -282,7 +316,17 @@ __global__ __launch_bounds__(PRE ? kThreads : 2 * kThreads) void index_tokens_ke
         for (int hb = 0; hb < HB; ++hb)
 #pragma unroll
             for (int r = 0; r < 16; ++r) acc[hb][r] = 0.0f;
-        if constexpr (FP8) {
+        if constexpr (QF8) {
+            // the key bytes (D / 2) half + 32 kk .. +32 of the row, as they sit in LDS
+#pragma unroll
+            for (int kk = 0; kk < KF8; ++kk) {
+                const u32x4 k0 = kf.v[2 * kk], k1 = kf.v[2 * kk + 1];
+                const i32x8 kb = {(int)k0[0], (int)k0[1], (int)k0[2], (int)k0[3],
+                                  (int)k1[0], (int)k1[1], (int)k1[2], (int)k1[3]};
+#pragma unroll
+                for (int hb = 0; hb < HB; ++hb) acc[hb] = mfma32_fp8(aq8[hb][kk], kb, acc[hb]);
+            }
+        } else if constexpr (FP8) {
 #pragma unroll
             for (int kk = 0; kk < NKV; ++kk) {
                 bf16x8 f0, f1;
@@ -536,7 +580,7 @@ int compute_units() {
     return n;
 }
 
-template <int D, bool FP8, int MODE, int HB, bool HI, bool PRE, bool HIST = false>
+template <int D, bool FP8, bool QF8, int MODE, int HB, bool HI, bool PRE, bool HIST = false>
 hipError_t launch_tokens_t(const IndexTokensArgs &a, hipStream_t s) {
     constexpr int NST = 4;  // one tile computed, three in flight (deeper rings measured no faster)
     using G = Tile<D, FP8, NST>;
@@ -555,36 +599,36 @@ hipError_t launch_tokens_t(const IndexTokensArgs &a, hipStream_t s) {
     chunks = (a.n_out + chunk - 1) / chunk;
     dim3 grid(chunks, gy, a.B);
     const size_t lds = (size_t)G::NST * G::STAGE;
-    hipLaunchKernelGGL((index_tokens_kernel<D, FP8, MODE, HB, HI, PRE, HIST, NST>), grid, dim3(PRE ? kThreads : 2 * kThreads), lds, s, a,
+    hipLaunchKernelGGL((index_tokens_kernel<D, FP8, QF8, MODE, HB, HI, PRE, HIST, NST>), grid, dim3(PRE ? kThreads : 2 * kThreads), lds, s, a,
                        groups, chunk);
     return hipGetLastError();
 }
 
-template <int D, bool FP8>
+template <int D, bool FP8, bool QF8 = false>
 hipError_t launch_tokens_d(const IndexTokensArgs &a, hipStream_t s) {
     const bool hi = a.kept != nullptr;
     if (a.sel_hist) {  // one query per workgroup: the epilogue builds the selection histogram
         if (hi) {
-            if (a.H <= 32) return launch_tokens_t<D, FP8, ONEQ, 1, true, false, true>(a, s);
-            return launch_tokens_t<D, FP8, ONEQ, 2, true, false, true>(a, s);
+            if (a.H <= 32) return launch_tokens_t<D, FP8, QF8, ONEQ, 1, true, false, true>(a, s);
+            return launch_tokens_t<D, FP8, QF8, ONEQ, 2, true, false, true>(a, s);
         }
-        if (a.H == 32) return launch_tokens_t<D, FP8, ONEQ, 1, false, false, true>(a, s);
-        return launch_tokens_t<D, FP8, ONEQ, 2, false, false, true>(a, s);
+        if (a.H == 32) return launch_tokens_t<D, FP8, QF8, ONEQ, 1, false, false, true>(a, s);
+        return launch_tokens_t<D, FP8, QF8, ONEQ, 2, false, false, true>(a, s);
     }
     if (hi) {
-        if (a.H <= 32) return launch_tokens_t<D, FP8, ONEQ, 1, true, false>(a, s);
-        return launch_tokens_t<D, FP8, ONEQ, 2, true, false>(a, s);
+        if (a.H <= 32) return launch_tokens_t<D, FP8, QF8, ONEQ, 1, true, false>(a, s);
+        return launch_tokens_t<D, FP8, QF8, ONEQ, 2, true, false>(a, s);
     }
     switch (a.H) {
-        case 4: return launch_tokens_t<D, FP8, Q4, 1, false, false>(a, s);
-        case 8: return launch_tokens_t<D, FP8, Q8, 1, false, false>(a, s);
-        case 16: return launch_tokens_t<D, FP8, Q16, 1, false, false>(a, s);
+        case 4: return launch_tokens_t<D, FP8, QF8, Q4, 1, false, false>(a, s);
+        case 8: return launch_tokens_t<D, FP8, QF8, Q8, 1, false, false>(a, s);
+        case 16: return launch_tokens_t<D, FP8, QF8, Q16, 1, false, false>(a, s);
         case 32:
-            if (a.T >= 64) return launch_tokens_t<D, FP8, ONEQ, 1, false, true>(a, s);
-            return launch_tokens_t<D, FP8, ONEQ, 1, false, false>(a, s);
+            if (a.T >= 64) return launch_tokens_t<D, FP8, QF8, ONEQ, 1, false, true>(a, s);
+            return launch_tokens_t<D, FP8, QF8, ONEQ, 1, false, false>(a, s);
         default:
-            if (a.T >= 64) return launch_tokens_t<D, FP8, ONEQ, 2, false, true>(a, s);
-            return launch_tokens_t<D, FP8, ONEQ, 2, false, false>(a, s);
+            if (a.T >= 64) return launch_tokens_t<D, FP8, QF8, ONEQ, 2, false, true>(a, s);
+            return launch_tokens_t<D, FP8, QF8, ONEQ, 2, false, false>(a, s);
     }
 }
 
@@ -602,6 +646,7 @@ bool index_tokens_supported(int H, int D, bool hi) {
 }
 
 hipError_t launch_index_tokens(const IndexTokensArgs &a, hipStream_t s) {
+    if (a.qf8) return launch_tokens_d<128, true, true>(a, s);  // fp8 keys, D = 128 (checked by the caller)
     if (a.D == 64) return a.fp8 ? launch_tokens_d<64, true>(a, s) : launch_tokens_d<64, false>(a, s);
     return a.fp8 ? launch_tokens_d<128, true>(a, s) : launch_tokens_d<128, false>(a, s);
 }

@@ -16,6 +16,7 @@ struct IndexTokensArgs {
     const float *w;         // [B][T][H]
     const void *k;          // bf16 or fp8 [B][N][D]
     bool fp8;
+    bool qf8;               // fp8 keys only: query rows quantised to fp8, fp8 x fp8 contraction
     const float *k_scale;   // [B][N] or null
     const int32_t *kept;    // HI fine: [B][T][n_keep] or null
     int n_keep, block_size;

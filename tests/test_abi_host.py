@@ -102,6 +102,10 @@ def _att(d, ws=FAKE, nbytes=1 << 40):
     (dict(mode=L.LSA_INDEX_BLOCKS, k_dtype=L.LSA_F32, block_size=64, n_blocks=16, window=64, H=65), -6),
     (dict(mode=L.LSA_INDEX_BLOCKS, k_dtype=L.LSA_F32, block_size=64, n_blocks=16, window=62), -6),
     (dict(kept=FAKE, n_keep=0, block_size=64), -2),
+    # fp8 queries: a known dtype, fp8 keys and D = 128 only
+    (dict(q_dtype=9), -3), (dict(q_dtype=L.LSA_F32), -3),
+    (dict(q_dtype=L.LSA_FP8_E4M3FN, k_dtype=L.LSA_BF16, k_scale=None), -6),
+    (dict(q_dtype=L.LSA_FP8_E4M3FN, D=64), -6),
 ])
 def test_index_argument_errors(kw, code):
     assert _idx(_index_desc(**kw)) == code
