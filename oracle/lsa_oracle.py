@@ -39,6 +39,11 @@ Readings where the pages are silent (the pages give no formula at all):
   R27 fp8-query indexer (an option of the token scores, fp8 keys only): each (token,
       head) query row is quantised as R12 quantises a key row, and the score is R1's
       with the dequantised rows.
+  R28 backward of the sparse attention (training; [P3] describes LSA as trained, and
+      its operators as deterministic): the gradient of the attention of R2/R16 with
+      respect to q, K and V over the selected rows only, the selection held fixed;
+      it takes the forward's output and log-sum-exp as inputs (D = dO . O and
+      P = exp(z - lse)), and gradients of one row from several queries add up.
 """
 from __future__ import annotations
 
@@ -338,6 +343,48 @@ def attend(q: np.ndarray, k_rows: np.ndarray, v_rows: np.ndarray, idx: np.ndarra
         o[kvh * g:(kvh + 1) * g] = (e @ Vs) / den
         lse[kvh * g:(kvh + 1) * g] = (zmax + np.log(den))[:, 0]
     return o, lse
+
+
+def attend_backward(q, k_rows, v_rows, idx, tau, out, lse, dout):
+    """Gradient of attend() for one query token (R28): the selection is a fixed input.
+
+    q [Hq, d_qk], k_rows [N, Hkv, d_qk], v_rows [N, Hkv, d_v], idx [K] (-1 padding), out
+    [Hq, d_v] and lse [Hq] from the forward, dout [Hq, d_v]; float64 throughout. With
+    z_s = tau q . K_s, P_s = exp(z_s - lse), dP_s = dout . V_s, D = dout . out and
+    dS_s = P_s (dP_s - D) (the softmax Jacobian applied to dP):
+      dq = tau sum_s dS_s K_s;  dK_s = tau sum_h dS_s q_h;  dV_s = sum_h P_s dout_h
+    where the KV sums run over the query heads of that KV head.
+    Returns (dq [Hq, d_qk], dK [N, Hkv, d_qk], dV [N, Hkv, d_v]); rows not selected are 0.
+    """
+    sel = np.asarray(idx, dtype=np.int64)
+    sel = sel[sel >= 0]
+    Hq, dqk = q.shape
+    N, Hkv = k_rows.shape[0], k_rows.shape[1]
+    g = Hq // Hkv
+    dq = np.zeros((Hq, dqk))
+    dK = np.zeros((N, Hkv, dqk))
+    dV = np.zeros((N, Hkv, v_rows.shape[2]))
+    if sel.size == 0:
+        return dq, dK, dV
+    for kvh in range(Hkv):
+        hs = slice(kvh * g, (kvh + 1) * g)
+        Ks, Vs = k_rows[sel, kvh, :], v_rows[sel, kvh, :]       # [n, d]
+        P = np.exp(tau * (q[hs] @ Ks.T) - lse[hs, None])         # [g, n]
+        dP = dout[hs] @ Vs.T                                     # [g, n]
+        D = np.sum(dout[hs] * out[hs], axis=1, keepdims=True)    # [g, 1]
+        dS = P * (dP - D)
+        dq[hs] = tau * (dS @ Ks)
+        dK[sel, kvh, :] = tau * (dS.T @ q[hs])
+        dV[sel, kvh, :] = P.T @ dout[hs]
+    return dq, dK, dV
+
+
+def mla_row_grad(dK, dV):
+    """R15 under R28: an MLA latent row is both K and (its first d_v columns) V, so its
+    gradient is dK plus dV on the first d_v columns."""
+    d = dK.copy()
+    d[..., : dV.shape[-1]] += dV
+    return d
 
 
 def mla_kv(rows: np.ndarray, d_v: int):

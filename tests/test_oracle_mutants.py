@@ -37,7 +37,8 @@ ALL = ["test_golden_hand_worked_flat_and_hi", "test_indexer_single_head_is_relu_
        "test_budget_covers_context_equals_dense_causal", "test_attention_closed_forms",
        "test_attention_permutation_invariant_and_gqa_mapping", "test_e4m3fn_matches_torch_all_codes",
        "test_fp8_query_worked_example", "test_fp8_query_exact_for_representable_rows",
-       "test_fp8_query_error_bound_rows_and_scaling", "test_fp8_query_score_is_the_fp8_contraction"]
+       "test_fp8_query_error_bound_rows_and_scaling", "test_fp8_query_score_is_the_fp8_contraction",
+       "test_attention_backward_finite_differences", "test_attention_backward_closed_forms"]
 
 
 def _no_relu(q, w, keys, p):
@@ -123,6 +124,19 @@ def _query_shared_scale(qI_bits, fp8_query=False):
     return O.decode_e4m3fn(O.encode_e4m3fn(y)) * np.float64(s)
 
 
+_real_bwd = O.attend_backward
+
+
+def _bwd_no_delta(q, k_rows, v_rows, idx, tau, out, lse, dout):
+    # the softmax Jacobian without its rank-one term (D = 0)
+    return _real_bwd(q, k_rows, v_rows, idx, tau, np.zeros_like(out), lse, dout)
+
+
+def _bwd_dk_without_tau(q, k_rows, v_rows, idx, tau, out, lse, dout):
+    dq, dK, dV = _real_bwd(q, k_rows, v_rows, idx, tau, out, lse, dout)
+    return dq, dK / tau, dV
+
+
 MUTANTS = [
     ("indexer_scores", _no_relu),
     ("indexer_scores", _max_heads),
@@ -135,6 +149,8 @@ MUTANTS = [
     ("decode_e4m3fn", _e4m3_bias8),
     ("index_query_f64", _query_no_scale),
     ("index_query_f64", _query_shared_scale),
+    ("attend_backward", _bwd_no_delta),
+    ("attend_backward", _bwd_dk_without_tau),
 ]
 
 

@@ -518,3 +518,91 @@ def test_fp8_query_score_is_the_fp8_contraction():
     want = ks.astype(np.float64) * (np.maximum(dots, 0.0) @ (w * qs.astype(np.float64)))
     got = O.indexer_scores(O.index_query_f64(bits, True), w, O.index_keys_f64(kc, ks), n - 1)
     assert np.allclose(got, want, rtol=1e-12, atol=0)
+
+
+# ----------------------------------------------------------------------------- attention backward (R28)
+
+def _torch_sparse_attention(q, k_rows, v_rows, idx, tau):
+    """Sparse attention written with torch ops (gather, softmax), float64, for autograd."""
+    sel = torch.as_tensor(np.asarray(idx)[np.asarray(idx) >= 0], dtype=torch.long)
+    Hq, Hkv = q.shape[0], k_rows.shape[1]
+    g = Hq // Hkv
+    kv_of_head = torch.arange(Hq) // g
+    Ks = k_rows[sel][:, kv_of_head, :].permute(1, 0, 2)        # [Hq, n, dqk]
+    Vs = v_rows[sel][:, kv_of_head, :].permute(1, 0, 2)        # [Hq, n, dv]
+    z = tau * torch.einsum("hd,hnd->hn", q, Ks)
+    return torch.einsum("hn,hnd->hd", torch.softmax(z, dim=1), Vs), torch.logsumexp(z, dim=1)
+
+
+def _bwd_case(rng, Hq, Hkv, dqk, dv, N, K, n_pad=0):
+    q = rng.standard_normal((Hq, dqk)) / np.sqrt(dqk)
+    k = rng.standard_normal((N, Hkv, dqk))
+    v = rng.standard_normal((N, Hkv, dv))
+    idx = np.full(K, -1, np.int64)
+    idx[: K - n_pad] = np.sort(rng.choice(N, K - n_pad, replace=False))
+    dout = rng.standard_normal((Hq, dv))
+    return q, k, v, idx, dout
+
+
+@pytest.mark.parametrize("Hq,Hkv,dqk,dv,mla", [(8, 2, 16, 16, False), (6, 1, 24, 16, True), (4, 4, 8, 12, False)])
+def test_attention_backward_matches_autograd(Hq, Hkv, dqk, dv, mla):
+    rng = np.random.default_rng(31 + Hq)
+    N, K, tau = 40, 12, 0.3
+    q, k, v, idx, dout = _bwd_case(rng, Hq, Hkv, dqk, dv, N, K, n_pad=3)
+    if mla:
+        v = k[..., :dv]
+    out, lse = O.attend(q, k, v, idx, tau)
+    dq, dK, dV = O.attend_backward(q, k, v, idx, tau, out, lse, dout)
+    tq = torch.tensor(q, requires_grad=True)
+    tk = torch.tensor(k, requires_grad=True)
+    tv = tk[..., :dv] if mla else torch.tensor(v, requires_grad=True)
+    to, tl = _torch_sparse_attention(tq, tk, tv, idx, tau)
+    assert np.allclose(to.detach().numpy(), out, atol=1e-12) and np.allclose(tl.detach().numpy(), lse, atol=1e-12)
+    grads = torch.autograd.grad((to * torch.tensor(dout)).sum(), (tq, tk) if mla else (tq, tk, tv))
+    assert np.allclose(dq, grads[0].numpy(), atol=1e-12)
+    if mla:
+        assert np.allclose(O.mla_row_grad(dK, dV), grads[1].numpy(), atol=1e-12)
+    else:
+        assert np.allclose(dK, grads[1].numpy(), atol=1e-12)
+        assert np.allclose(dV, grads[2].numpy(), atol=1e-12)
+
+
+def test_attention_backward_finite_differences():
+    rng = np.random.default_rng(32)
+    q, k, v, idx, dout = _bwd_case(rng, 2, 1, 4, 3, 7, 4, n_pad=1)
+    tau = 0.7
+
+    def loss(q_, k_, v_):
+        o, _ = O.attend(q_, k_, v_, idx, tau)
+        return float(np.sum(o * dout))
+    out, lse = O.attend(q, k, v, idx, tau)
+    dq, dK, dV = O.attend_backward(q, k, v, idx, tau, out, lse, dout)
+    eps = 1e-6
+    for arr, grad, which in ((q, dq, 0), (k, dK, 1), (v, dV, 2)):
+        for pos in np.ndindex(arr.shape):
+            args = [q.copy(), k.copy(), v.copy()]
+            args[which][pos] += eps
+            up = loss(*args)
+            args[which][pos] -= 2 * eps
+            dn = loss(*args)
+            assert abs((up - dn) / (2 * eps) - grad[pos]) < 1e-7, (which, pos)
+
+
+def test_attention_backward_closed_forms():
+    rng = np.random.default_rng(33)
+    q, k, v, _, dout = _bwd_case(rng, 4, 2, 8, 8, 10, 1)
+    # one selected row: the softmax is constant 1, so q and K get no gradient and V's
+    # row receives the sum of its heads' output gradients
+    idx = np.array([6, -1, -1])
+    out, lse = O.attend(q, k, v, idx, 0.5)
+    dq, dK, dV = O.attend_backward(q, k, v, idx, 0.5, out, lse, dout)
+    assert np.allclose(dq, 0, atol=1e-15) and np.allclose(dK, 0, atol=1e-15)
+    assert np.allclose(dV[6, 0], dout[0] + dout[1]) and np.allclose(dV[6, 1], dout[2] + dout[3])
+    assert np.count_nonzero(dV[np.arange(10) != 6]) == 0
+    # nothing selected: every gradient is zero
+    dq0, dK0, dV0 = O.attend_backward(q, k, v, np.full(3, -1), 0.5, np.zeros_like(out), np.full(4, -np.inf), dout)
+    assert not dq0.any() and not dK0.any() and not dV0.any()
+    # zero output gradient: zero everywhere
+    z = O.attend_backward(q, k, v, np.array([1, 4, 9]), 0.5, *O.attend(q, k, v, np.array([1, 4, 9]), 0.5),
+                          np.zeros_like(dout))
+    assert all(not a.any() for a in z)
