@@ -49,7 +49,26 @@ def parse():
                     help="with --profile-only: also run one elementwise add of known traffic (counter calibration)")
     ap.add_argument("--profile-c4-index", action="store_true",
                     help="only the c4 prefill indexer, bf16 then fp8 queries, `--steps` calls each (for rocprofv3)")
+    ap.add_argument("--profile-backward", action="store_true",
+                    help="only lsa_attend_backward on the c2 shape, `--steps` calls (for rocprofv3)")
     return ap.parse_args()
+
+
+def backward_inputs(B, N, K, Hq, seed=11):
+    """Device inputs of one lsa_attend_backward call on an MLA decode shape (one query token
+    per sequence; forward output and lse from lsa_attend); returns the call."""
+    import torch
+    import long_context_sparse_07_amd as L
+    g = torch.Generator(device="cuda").manual_seed(seed)
+    q = (torch.randn((1, B, 1, Hq, 576), device="cuda", generator=g) * 576 ** -0.5).to(torch.bfloat16)
+    k = torch.randn((1, B, N, 1, 576), device="cuda", generator=g).to(torch.bfloat16)
+    idx = torch.rand((B, N), device="cuda", generator=g).topk(K, dim=1).indices.sort(dim=1).values
+    idx = idx.to(torch.int32).view(B, 1, K).contiguous()
+    out, lse = L.lsa_attend(q, k, None, idx, 576 ** -0.5)
+    dout = torch.randn((B, 1, Hq, 512), device="cuda", generator=g).to(torch.bfloat16)
+    dq = torch.empty((B, 1, Hq, 576), dtype=torch.float32, device="cuda")
+    dk = torch.empty((B, N, 1, 576), dtype=torch.float32, device="cuda")
+    return lambda: L.lsa_attend_backward(q[0], k[0], None, idx, 576 ** -0.5, out[0], lse[0], dout, dq=dq, dk=dk)
 
 
 def profile_c4_index(steps, warmup):
@@ -143,7 +162,9 @@ def measure_workloads(steps=50):
       the selection recomputed for every layer.
       cache append (the step's write side): us per call for the c2 and c3 cache shapes.
       paged KV: the c2 attention over a fixed selection from the contiguous cache and
-      from page pools (pages in random order, block table lookups), us per call."""
+      from page pools (pages in random order, block table lookups), us per call.
+      backward: lsa_attend_backward on the c2 shape (one query token per sequence), us
+      per call."""
     import numpy as np
     import torch
     import long_context_sparse_07_amd as L
@@ -333,7 +354,18 @@ def measure_workloads(steps=50):
             del pool
         return res_p
 
-    for name, body in (("c1", w1), ("c3", w3), ("c4", w4), ("c5", w5), ("append", w_append), ("paged", w_paged)):
+    def w_bwd():
+        B, N, K, Hq = 8, 131072, 2048, 64
+        f = backward_inputs(B, N, K, Hq)
+        us = graph_us(f, reps=10)
+        rows_flops = B * Hq * K * 2.0 * (3 * 576 + 2 * 512)
+        dk_bytes = B * N * 576 * 4
+        return {"workload": "backward: c2 shape (B=8, 128K, T=1, MLA 64 heads 576/512, K=2048), dq and the dense "
+                            "fp32 latent-row gradient",
+                "us_per_call": us, "rows_gflop": rows_flops / 1e9, "dk_write_gb": dk_bytes / 1e9}
+
+    for name, body in (("c1", w1), ("c3", w3), ("c4", w4), ("c5", w5), ("append", w_append), ("paged", w_paged),
+                       ("backward", w_bwd)):
         run(name, body)
         print(f"[bench] workload {name}: {res[name]}", file=sys.stderr, flush=True)
     return res
@@ -347,6 +379,20 @@ def main():
         sys.exit(2)
     if args.profile_c4_index:
         profile_c4_index(args.steps, args.warmup)
+        return
+    if args.profile_backward:
+        import torch
+        f = backward_inputs(8, 131072, 2048, 64)
+        for _ in range(args.warmup):
+            f()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(args.steps):
+            f()
+        e1.record()
+        torch.cuda.synchronize()
+        print(json.dumps({"profile_backward": True, "us_per_call": e0.elapsed_time(e1) / args.steps * 1e3}))
         return
     import ctypes
     import numpy as np

@@ -295,6 +295,52 @@ int32_t lsa_select_attend(const lsa_select_desc *sel, const lsa_attend_desc *att
                           size_t select_ws_bytes, void *attend_ws, size_t attend_ws_bytes, void *stream);
 
 /*
+ * lsa_attend_backward — gradients of lsa_attend (one layer, n_layers = 1) with respect to
+ * q, K and V, the selection held fixed (reading R28: the pages' LSA is trained with its
+ * sparse operators, and those operators are deterministic: molayo1419.me LongCat-2.0
+ * article, "The sparse attention problem at 1M tokens" and "Training on 50,000 Chinese
+ * ASICs"). With z_s = softmax_scale q . K_s over the valid entries s of idx[b][t],
+ * P_s = exp(z_s - lse), dP_s = dout . V_s, D = dout . out and dS_s = P_s (dP_s - D):
+ *   dq[b][t][hq]    = softmax_scale sum_s dS_s K[b][s][kvh]
+ *   dk[b][s][kvh]   = softmax_scale sum over (t, hq of kvh) selecting s of dS_s q[b][t][hq]
+ *   dv[b][s][kvh]   = sum over (t, hq of kvh) selecting s of P_s dout[b][t][hq]
+ * fp32 arithmetic from the bf16 inputs; out and lse are the forward's (lsa_attend with
+ * the same idx). Every sum runs in a fixed order (query tokens ascending), so results are
+ * reproducible bit for bit; no atomics.
+ * Layouts: q, out, dout bf16 [B][T][Hq][d]; lse fp32 [B][T][Hq]; k, v as in lsa_attend
+ * (strides in elements); idx int32 [B][T][K] as lsa_select writes it (valid entries
+ * strictly ascending, then -1; entries outside [0, N) skipped). Outputs fp32, written in
+ * full: dq [B][T][Hq][d_qk]; dk [B][N][Hkv][d_qk] and dv [B][N][Hkv][d_v] (zero at
+ * positions no query selected). MLA (d_qk = 576, d_v = 512, v aliasing k, reading R15):
+ * dk is the latent row's gradient, dK plus dV on its first 512 columns, and dv is NULL.
+ * Workspace: lsa_attend_backward_workspace_bytes(desc), 256-byte aligned, no initial
+ * contents: per (query token, KV head, selected row) one row of fp32 contributions
+ * (d_qk + d_v floats, MLA d_qk) plus per-tile parts of dq (32 rows a tile).
+ * Supported: (d_qk, d_v) in {(128, 128), (576, 512)}, Hq % Hkv == 0, Hq / Hkv <= 64,
+ * B * T <= 65535, strides multiples of 8 elements; q, k, v, out, dout, dk, dv 16-byte
+ * aligned. Errors as for lsa_attend.
+ */
+typedef struct lsa_attend_bwd_desc {
+    int32_t B, T, N;
+    int32_t Hq, Hkv, d_qk, d_v;
+    const void *q;
+    const void *k;
+    int64_t k_stride_b, k_stride_n, k_stride_h;
+    const void *v;
+    int64_t v_stride_b, v_stride_n, v_stride_h;
+    const int32_t *idx;
+    int32_t K;
+    float softmax_scale;
+    const void *out;
+    const float *lse;
+    const void *dout;
+    float *dq, *dk, *dv;
+} lsa_attend_bwd_desc;
+
+size_t lsa_attend_backward_workspace_bytes(const lsa_attend_bwd_desc *desc);
+int32_t lsa_attend_backward(const lsa_attend_bwd_desc *desc, void *workspace, size_t workspace_bytes, void *stream);
+
+/*
  * lsa_cache_append — the write side of a decode step: T new tokens per sequence enter the
  * caches that lsa_index and lsa_attend read. SI's local window ends at the current token
  * (reading R4), so a step's rows are appended before the step; HI's coarse pass reads one

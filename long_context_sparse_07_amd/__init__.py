@@ -17,8 +17,8 @@ __all__ = ["lib", "LSAError", "lsa_index", "lsa_block_means", "lsa_select", "lsa
            "lsa_workspace_clear", "lsa_select_workspace_bytes", "lsa_attend_workspace_bytes",
            "LSA_BF16", "LSA_FP8_E4M3FN", "LSA_F32", "LSA_INDEX_TOKENS", "LSA_INDEX_BLOCKS",
            "LSA_WS_UNKNOWN", "LSA_WS_CLEAN", "LSA_WS_PRIMED", "lsa_select_attend", "lsa_index_select_attend",
-           "lsa_cache_append", "IndexDesc", "BlockMeansDesc", "SelectDesc", "AttendDesc", "CacheAppendDesc",
-           "STATUS"]
+           "lsa_cache_append", "lsa_attend_backward", "IndexDesc", "BlockMeansDesc", "SelectDesc", "AttendDesc",
+           "AttendBwdDesc", "CacheAppendDesc", "STATUS"]
 
 HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(HERE, "liblsa.so")
@@ -72,6 +72,15 @@ class AttendDesc(ctypes.Structure):
                 ("block_table", c_void_p), ("page_size", c_int32), ("max_pages", c_int32), ("num_pages", c_int32)]
 
 
+class AttendBwdDesc(ctypes.Structure):
+    _fields_ = [("B", c_int32), ("T", c_int32), ("N", c_int32), ("Hq", c_int32), ("Hkv", c_int32),
+                ("d_qk", c_int32), ("d_v", c_int32), ("q", c_void_p), ("k", c_void_p),
+                ("k_stride_b", c_int64), ("k_stride_n", c_int64), ("k_stride_h", c_int64),
+                ("v", c_void_p), ("v_stride_b", c_int64), ("v_stride_n", c_int64), ("v_stride_h", c_int64),
+                ("idx", c_void_p), ("K", c_int32), ("softmax_scale", c_float), ("out", c_void_p),
+                ("lse", c_void_p), ("dout", c_void_p), ("dq", c_void_p), ("dk", c_void_p), ("dv", c_void_p)]
+
+
 class LSAError(RuntimeError):
     def __init__(self, fn: str, status: int, msg: str):
         super().__init__(f"{fn} -> {STATUS.get(status, status)}: {msg}")
@@ -103,6 +112,10 @@ def lib():
         L.lsa_select_workspace_bytes.restype = c_size_t
         L.lsa_attend_workspace_bytes.argtypes = [POINTER(AttendDesc)]
         L.lsa_attend_workspace_bytes.restype = c_size_t
+        L.lsa_attend_backward.argtypes = [POINTER(AttendBwdDesc), c_void_p, c_size_t, c_void_p]
+        L.lsa_attend_backward.restype = c_int32
+        L.lsa_attend_backward_workspace_bytes.argtypes = [POINTER(AttendBwdDesc)]
+        L.lsa_attend_backward_workspace_bytes.restype = c_size_t
         L.lsa_workspace_clear.argtypes = [c_void_p, c_size_t, c_void_p]
         L.lsa_workspace_clear.restype = c_int32
         L.lsa_status_str.argtypes = [c_int32]
@@ -388,6 +401,36 @@ def lsa_index_select_attend(qI, w, kI, K, sink, window, q, k, v, softmax_scale, 
     ds.workspace_state = LSA_WS_PRIMED
     _select_attend_call(ds, da, ent, q, stream)
     return scores, idx, out, lse
+
+
+def lsa_attend_backward(q, k, v, idx, softmax_scale, out, lse, dout, *, dq=None, dk=None, dv=None,
+                        workspace=None, stream=None):
+    """Gradients of lsa_attend for one layer, selection fixed. q, out, dout bf16 [B,T,Hq,d];
+    k, v bf16 [B,N,Hkv,d] (v=None: MLA latent rows); idx int32 [B,T,K] as lsa_select
+    writes it; lse fp32 [B,T,Hq]. Returns fp32 (dq [B,T,Hq,d_qk], dk [B,N,Hkv,d_qk], dv
+    [B,N,Hkv,d_v] or None for MLA, where dk is the latent row gradient)."""
+    import torch
+    B, T, Hq, dqk = q.shape
+    N, Hkv = k.shape[1], k.shape[2]
+    mla = v is None
+    if mla:
+        v = k
+    dv_ = 512 if mla else v.shape[-1]
+    dev = q.device
+    dq = torch.empty((B, T, Hq, dqk), dtype=torch.float32, device=dev) if dq is None else dq
+    dk = torch.empty((B, N, Hkv, dqk), dtype=torch.float32, device=dev) if dk is None else dk
+    if not mla and dv is None:
+        dv = torch.empty((B, N, Hkv, dv_), dtype=torch.float32, device=dev)
+    d = AttendBwdDesc(B=B, T=T, N=N, Hq=Hq, Hkv=Hkv, d_qk=dqk, d_v=dv_, q=_ptr(q), k=_ptr(k),
+                      k_stride_b=k.stride(0), k_stride_n=k.stride(1), k_stride_h=k.stride(2),
+                      v=_ptr(v), v_stride_b=v.stride(0), v_stride_n=v.stride(1), v_stride_h=v.stride(2),
+                      idx=_ptr(idx), K=idx.shape[-1], softmax_scale=softmax_scale, out=_ptr(out), lse=_ptr(lse),
+                      dout=_ptr(dout), dq=_ptr(dq), dk=_ptr(dk), dv=_ptr(None if mla else dv))
+    need = lib().lsa_attend_backward_workspace_bytes(ctypes.byref(d))
+    ws = workspace if workspace is not None else (_workspace("attend_bwd", need, dev)[0] if need else None)
+    _check("lsa_attend_backward", lib().lsa_attend_backward(ctypes.byref(d), _ptr(ws), 0 if ws is None else ws.numel(),
+                                                            _stream(stream)))
+    return dq, dk, (None if mla else dv)
 
 
 def lsa_cache_append(k_new, k_cache, *, k_scale=None, rows=(), pos0=None, kbar=None, block_size=0, stream=None):

@@ -400,6 +400,77 @@ int32_t lsa_select_attend(const lsa_select_desc *sd, const lsa_attend_desc *ad, 
                       "lsa_select_attend");
 }
 
+// ----------------------------------------------------------------------------- attention backward
+
+static int32_t attend_bwd_check(const lsa_attend_bwd_desc *d, lsa::AttendBwdArgs &a) {
+    if (!d) return fail(LSA_E_NULL, "lsa_attend_backward: desc is NULL");
+    if (d->B < 1 || d->T < 1 || d->N < 1 || d->Hq < 1 || d->Hkv < 1)
+        return fail(LSA_E_SHAPE, "lsa_attend_backward: B, T, N, Hq, Hkv must be >= 1");
+    if (d->K < 1) return fail(LSA_E_BUDGET, "lsa_attend_backward: K must be >= 1");
+    if (d->Hq % d->Hkv) return fail(LSA_E_SHAPE, "lsa_attend_backward: Hq=%d not a multiple of Hkv=%d", d->Hq, d->Hkv);
+    const bool mla = d->d_qk == 576 && d->d_v == 512;
+    if (!mla && !(d->d_qk == 128 && d->d_v == 128))
+        return fail(LSA_E_UNSUPPORTED, "lsa_attend_backward: no kernel for d_qk=%d d_v=%d", d->d_qk, d->d_v);
+    if (d->Hq / d->Hkv > 64) return fail(LSA_E_UNSUPPORTED, "lsa_attend_backward: more than 64 query heads per KV head");
+    const int64_t strides[] = {d->k_stride_b, d->k_stride_n, d->k_stride_h, d->v_stride_b, d->v_stride_n, d->v_stride_h};
+    for (int64_t st : strides)
+        if (st < 0 || st % 8) return fail(LSA_E_ALIGN, "lsa_attend_backward: strides must be non-negative multiples of 8 elements");
+    if (mla && (d->v != d->k || d->v_stride_b != d->k_stride_b || d->v_stride_n != d->k_stride_n ||
+                d->v_stride_h != d->k_stride_h))
+        return fail(LSA_E_UNSUPPORTED, "lsa_attend_backward: d_qk=576 is the MLA latent layout: v must alias k with equal strides");
+    if ((int64_t)d->B * d->T > kMaxGridY || d->Hkv > kMaxGridY)
+        return fail(LSA_E_UNSUPPORTED, "lsa_attend_backward: grid too large");
+    a = lsa::AttendBwdArgs{};
+    a.B = d->B;
+    a.T = d->T;
+    a.N = d->N;
+    a.Hq = d->Hq;
+    a.Hkv = d->Hkv;
+    a.K = d->K;
+    a.q = reinterpret_cast<const uint16_t *>(d->q);
+    a.k = reinterpret_cast<const uint16_t *>(d->k);
+    a.ksb = d->k_stride_b;
+    a.ksn = d->k_stride_n;
+    a.ksh = d->k_stride_h;
+    a.v = reinterpret_cast<const uint16_t *>(d->v);
+    a.vsb = d->v_stride_b;
+    a.vsn = d->v_stride_n;
+    a.vsh = d->v_stride_h;
+    a.idx = d->idx;
+    a.scale = d->softmax_scale;
+    a.out = reinterpret_cast<const uint16_t *>(d->out);
+    a.lse = d->lse;
+    a.dout = reinterpret_cast<const uint16_t *>(d->dout);
+    a.dq = d->dq;
+    a.dk = d->dk;
+    a.dv = mla ? nullptr : d->dv;
+    a.mla = mla;
+    return LSA_OK;
+}
+
+size_t lsa_attend_backward_workspace_bytes(const lsa_attend_bwd_desc *d) {
+    lsa::AttendBwdArgs a;
+    if (attend_bwd_check(d, a) != LSA_OK) return 0;
+    return lsa::attend_bwd_workspace_bytes(a);
+}
+
+int32_t lsa_attend_backward(const lsa_attend_bwd_desc *d, void *ws, size_t ws_bytes, void *stream) {
+    lsa::AttendBwdArgs a;
+    const int32_t rc = attend_bwd_check(d, a);
+    if (rc != LSA_OK) return rc;
+    if (!d->q || !d->k || !d->v || !d->idx || !d->out || !d->lse || !d->dout || !d->dq || !d->dk || (!a.mla && !d->dv))
+        return fail(LSA_E_NULL, "lsa_attend_backward: q, k, v, idx, out, lse, dout, dq, dk (and dv unless MLA) are required");
+    if (!aligned16(d->q) || !aligned16(d->k) || !aligned16(d->v) || !aligned16(d->out) || !aligned16(d->dout) ||
+        !aligned4(d->lse) || !aligned4(d->dq) || !aligned16(d->dk) || (!a.mla && !aligned16(d->dv)))
+        return fail(LSA_E_ALIGN, "lsa_attend_backward: q, k, v, out, dout, dk, dv must be 16-byte aligned, lse and dq 4-byte");
+    const size_t need = lsa::attend_bwd_workspace_bytes(a);
+    if (!ws || ws_bytes < need)
+        return fail(LSA_E_WORKSPACE, "lsa_attend_backward: workspace of %zu bytes needed, %zu given", need, ws_bytes);
+    if ((reinterpret_cast<uintptr_t>(ws) & 255u) != 0)
+        return fail(LSA_E_ALIGN, "lsa_attend_backward: workspace not 256-byte aligned");
+    return hip_status(lsa::launch_attend_bwd(a, ws, reinterpret_cast<hipStream_t>(stream)), "lsa_attend_backward");
+}
+
 int32_t lsa_cache_append(const lsa_cache_append_desc *d, void *stream) {
     if (!d) return fail(LSA_E_NULL, "lsa_cache_append: desc is NULL");
     if (!d->k_new || !d->k_cache) return fail(LSA_E_NULL, "lsa_cache_append: k_new and k_cache are required");

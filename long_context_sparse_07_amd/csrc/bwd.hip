@@ -1,0 +1,297 @@
+// Backward of the sparse attention (training): gradients of q and of the selected K/V rows,
+// the selection held fixed. LSA is trained with its sparse operators and those operators
+// are deterministic (molayo1419.me LongCat-2.0 article, sections "The sparse attention
+// problem at 1M tokens" and "Training on 50,000 Chinese ASICs"), so every sum below runs in
+// a fixed order and no floating-point atomics are used.
+//
+// With z = scale q . K_s, P = exp(z - lse), dP = dO . V_s, D = dO . O, dS = P (dP - D):
+//   dq_h = scale sum_s dS K_s,  dK_s = scale sum_(t,h) dS q_h,  dV_s = sum_(t,h) P dO_h.
+//
+// bwd_rows_kernel (one workgroup per query token, KV head and tile of 32 selected rows):
+//   the tile's K (and V) rows are gathered into LDS; P and scale * dS for every head of
+//   the group and row of the tile; then the rows' gradient contributions of this query
+//   (G: scale sum_h dS q_h, and sum_h P dO_h) and this tile's part of dq.
+// bwd_dq_kernel: dq = the tiles' parts, added in tile order.
+// bwd_kv_kernel (one workgroup per tile of 32 cache positions and KV head): the
+//   contributions G of every query that selected one of the positions, added in ascending
+//   query order; every position of the cache is written (zero where nothing selected it).
+#include "common.cuh"
+#include "kernels.h"
+
+namespace lsa {
+namespace {
+
+constexpr int kBT = 256;  // threads per workgroup
+constexpr int kRT = 32;   // selected rows per bwd_rows workgroup
+constexpr int kPT = 32;   // cache positions per bwd_kv workgroup
+constexpr int kMaxG = 64; // query heads per KV head
+
+__device__ __forceinline__ float dot8(u32x4 x, u32x4 y) {
+    float s = 0.0f;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) s += bf16lo(x[e]) * bf16lo(y[e]) + bf16hi(x[e]) * bf16hi(y[e]);
+    return s;
+}
+
+__device__ __forceinline__ float bf16_at(const uint16_t *p) { return u2f((uint32_t)*p << 16); }
+
+// G row width: MLA one latent row (dK + dV on its first DV columns); else K then V
+template <int DQK, int DV, bool MLA>
+constexpr int g_width() { return MLA ? DQK : DQK + DV; }
+
+template <int DQK, int DV, bool MLA>
+__global__ __launch_bounds__(kBT) void bwd_rows_kernel(AttendBwdArgs a, float *G, float *dqp) {
+    constexpr int GW = g_width<DQK, DV, MLA>();
+    __shared__ __attribute__((aligned(16))) uint16_t kt[kRT][DQK];
+    __shared__ __attribute__((aligned(16))) uint16_t vt[MLA ? 1 : kRT][DV];
+    __shared__ __attribute__((aligned(16))) float Ps[kMaxG][kRT];
+    __shared__ __attribute__((aligned(16))) float dSs[kMaxG][kRT];  // scale * dS
+    __shared__ float Dh[kMaxG], lseh[kMaxG];
+    __shared__ int rowpos[kRT];
+
+    const int tid = threadIdx.x;
+    const int tile = blockIdx.x, bt = blockIdx.y, kvh = blockIdx.z;
+    const int b = bt / a.T;
+    const int g = a.Hq / a.Hkv;
+    const int r0 = tile * kRT;
+    const int nrows = min(kRT, a.K - r0);
+    const int ntiles = gridDim.x;
+    const int64_t qh0 = (int64_t)bt * a.Hq + kvh * g;  // first query head row of the group
+
+    if (tid < kRT) {
+        const int s = tid < nrows ? a.idx[(int64_t)bt * a.K + r0 + tid] : -1;
+        rowpos[tid] = (s >= 0 && s < a.N) ? s : -1;
+    }
+    __syncthreads();
+    // gather the tile's rows (invalid rows: zeros)
+    const uint16_t *kb = a.k + b * a.ksb + kvh * a.ksh;
+    for (int i = tid; i < kRT * DQK / 8; i += kBT) {
+        const int r = i / (DQK / 8), c = i % (DQK / 8);
+        const int s = rowpos[r];
+        u32x4 v = {0, 0, 0, 0};
+        if (s >= 0) v = *reinterpret_cast<const u32x4 *>(kb + (int64_t)s * a.ksn + 8 * c);
+        *reinterpret_cast<u32x4 *>(&kt[r][8 * c]) = v;
+    }
+    if constexpr (!MLA) {
+        const uint16_t *vb = a.v + b * a.vsb + kvh * a.vsh;
+        for (int i = tid; i < kRT * DV / 8; i += kBT) {
+            const int r = i / (DV / 8), c = i % (DV / 8);
+            const int s = rowpos[r];
+            u32x4 v = {0, 0, 0, 0};
+            if (s >= 0) v = *reinterpret_cast<const u32x4 *>(vb + (int64_t)s * a.vsn + 8 * c);
+            *reinterpret_cast<u32x4 *>(&vt[r][8 * c]) = v;
+        }
+    }
+    // D = dO . O and lse per head: four threads per head
+    const int h = tid >> 2, part = tid & 3;
+    {
+        float d = 0.0f;
+        if (h < g) {
+            const uint16_t *o = a.out + (qh0 + h) * DV, *dob = a.dout + (qh0 + h) * DV;
+            for (int c = part; c < DV / 8; c += 4)
+                d += dot8(*reinterpret_cast<const u32x4 *>(o + 8 * c), *reinterpret_cast<const u32x4 *>(dob + 8 * c));
+        }
+        d += __shfl_xor(d, 1, 64);
+        d += __shfl_xor(d, 2, 64);
+        if (h < g && part == 0) {
+            Dh[h] = d;
+            lseh[h] = a.lse[qh0 + h];
+        }
+    }
+    __syncthreads();
+
+    // P and scale * dS: thread (h, part) takes rows part + 4 j
+    if (h < g) {
+        float z[kRT / 4], dp[kRT / 4];
+#pragma unroll
+        for (int j = 0; j < kRT / 4; ++j) z[j] = dp[j] = 0.0f;
+        const uint16_t *qrow = a.q + (qh0 + h) * DQK, *dorow = a.dout + (qh0 + h) * DV;
+        for (int c = 0; c < DQK / 8; ++c) {
+            const u32x4 qv = *reinterpret_cast<const u32x4 *>(qrow + 8 * c);
+#pragma unroll
+            for (int j = 0; j < kRT / 4; ++j) z[j] += dot8(qv, *reinterpret_cast<const u32x4 *>(&kt[part + 4 * j][8 * c]));
+        }
+        for (int c = 0; c < DV / 8; ++c) {
+            const u32x4 ov = *reinterpret_cast<const u32x4 *>(dorow + 8 * c);
+#pragma unroll
+            for (int j = 0; j < kRT / 4; ++j) {
+                const uint16_t *vr = MLA ? &kt[part + 4 * j][8 * c] : &vt[MLA ? 0 : part + 4 * j][8 * c];
+                dp[j] += dot8(ov, *reinterpret_cast<const u32x4 *>(vr));
+            }
+        }
+        const float lse = lseh[h], D = Dh[h];
+#pragma unroll
+        for (int j = 0; j < kRT / 4; ++j) {
+            const int r = part + 4 * j;
+            // a query with no valid row has lse = -inf and no row here with rowpos >= 0
+            const float p = (rowpos[r] >= 0 && lse > kNegInf) ? expf(a.scale * z[j] - lse) : 0.0f;
+            Ps[h][r] = p;
+            dSs[h][r] = a.scale * (p * (dp[j] - D));
+        }
+    }
+    __syncthreads();
+
+    // G rows of this query: column c of row r (heads in order)
+    float *gout = G + (((int64_t)bt * a.Hkv + kvh) * a.K + r0) * GW;
+    for (int c = tid; c < GW; c += kBT) {
+        float acc[kRT];
+#pragma unroll
+        for (int r = 0; r < kRT; ++r) acc[r] = 0.0f;
+        const bool kcol = c < DQK;                               // K part (scale dS q)
+        const bool vcol = MLA ? c < DV : c >= DQK;               // V part (P dO)
+        const int vc = MLA ? c : c - DQK;
+        for (int hh = 0; hh < g; ++hh) {
+            const float qv = kcol ? bf16_at(a.q + (qh0 + hh) * DQK + c) : 0.0f;
+            const float ov = vcol ? bf16_at(a.dout + (qh0 + hh) * DV + vc) : 0.0f;
+#pragma unroll
+            for (int r4 = 0; r4 < kRT / 4; ++r4) {
+                const f32x4 ds = *reinterpret_cast<const f32x4 *>(&dSs[hh][4 * r4]);
+                const f32x4 pp = *reinterpret_cast<const f32x4 *>(&Ps[hh][4 * r4]);
+#pragma unroll
+                for (int e = 0; e < 4; ++e) acc[4 * r4 + e] += ds[e] * qv + pp[e] * ov;
+            }
+        }
+#pragma unroll
+        for (int r = 0; r < kRT; ++r)
+            if (r < nrows) gout[(int64_t)r * GW + c] = acc[r];
+    }
+
+    // this tile's part of dq: scale sum_r dS K_r
+    float *dq = dqp + (((int64_t)bt * a.Hkv + kvh) * ntiles + tile) * g * DQK;
+    for (int e = tid; e < g * DQK; e += kBT) {
+        const int hh = e / DQK, d = e % DQK;
+        float s = 0.0f;
+#pragma unroll 8
+        for (int r = 0; r < kRT; ++r) s += dSs[hh][r] * u2f((uint32_t)kt[r][d] << 16);
+        dq[e] = s;
+    }
+}
+
+template <int DQK>
+__global__ __launch_bounds__(64) void bwd_dq_kernel(AttendBwdArgs a, const float *dqp, int ntiles) {
+    const int qh = blockIdx.x;  // (b, t, head) row
+    const int g = a.Hq / a.Hkv;
+    const int hq = qh % a.Hq, bt = qh / a.Hq;
+    const int kvh = hq / g, hh = hq % g;
+    const float *src = dqp + (((int64_t)bt * a.Hkv + kvh) * ntiles) * g * DQK + hh * DQK;
+    for (int d = threadIdx.x; d < DQK; d += 64) {
+        float s = 0.0f;
+        for (int t0 = 0; t0 < ntiles; t0 += 8) {  // eight loads in flight, added in tile order
+            float v[8];
+#pragma unroll
+            for (int j = 0; j < 8; ++j) v[j] = t0 + j < ntiles ? src[(int64_t)(t0 + j) * g * DQK + d] : 0.0f;
+#pragma unroll
+            for (int j = 0; j < 8; ++j) s += v[j];
+        }
+        a.dq[(int64_t)qh * DQK + d] = s;
+    }
+}
+
+template <int DQK, int DV, bool MLA>
+__global__ __launch_bounds__(kBT) void bwd_kv_kernel(AttendBwdArgs a, const float *G) {
+    constexpr int GW = g_width<DQK, DV, MLA>();
+    constexpr int NC = (GW + kBT - 1) / kBT;  // columns per thread
+    __shared__ __attribute__((aligned(16))) float acc[kPT][GW];
+    __shared__ int lo_s[kBT], cnt_s[kBT];
+    const int tid = threadIdx.x;
+    const int p0 = blockIdx.x * kPT, b = blockIdx.y, kvh = blockIdx.z;
+    bool touched = false;  // some query selected a position of the tile (uniform)
+    for (int t0 = 0; t0 < a.T; t0 += kBT) {
+        // thread j finds the slots of query t0 + j whose positions fall in [p0, p0 + kPT):
+        // valid entries ascend and padding (-1) comes last, so they are one run of slots
+        const int t = t0 + tid;
+        int lo = 0, cnt = 0;
+        if (t < a.T) {
+            const int32_t *row = a.idx + ((int64_t)b * a.T + t) * a.K;
+            auto key = [&](int slot) { const int s = row[slot]; return s < 0 ? 0x7FFFFFFF : s; };
+            int hi = a.K;
+            while (lo < hi) {  // first slot with key >= p0
+                const int mid = (lo + hi) >> 1;
+                if (key(mid) < p0) lo = mid + 1;
+                else hi = mid;
+            }
+            while (lo + cnt < a.K && cnt < kPT && key(lo + cnt) < p0 + kPT) ++cnt;
+        }
+        __syncthreads();  // the previous chunk is done with lo_s / cnt_s
+        lo_s[tid] = lo;
+        cnt_s[tid] = cnt;
+        const bool any = __syncthreads_or(cnt > 0);
+        if (!any) continue;
+        if (!touched) {  // first contributions: clear the accumulators
+            for (int i = tid; i < kPT * GW; i += kBT) (&acc[0][0])[i] = 0.0f;
+            __syncthreads();
+            touched = true;
+        }
+        const int nt = min(kBT, a.T - t0);
+        for (int j = 0; j < nt; ++j) {  // ascending query order
+            const int tt = t0 + j;
+            const int32_t *row = a.idx + ((int64_t)b * a.T + tt) * a.K;
+            const float *gq = G + (((int64_t)b * a.T + tt) * a.Hkv + kvh) * a.K * GW;
+            for (int e = 0; e < cnt_s[j]; ++e) {
+                const int slot = lo_s[j] + e;
+                const int pos = row[slot];
+                if (pos < p0 || pos >= p0 + kPT || pos >= a.N) continue;  // (rows not ascending: skipped)
+                const float *gr = gq + (int64_t)slot * GW;
+#pragma unroll
+                for (int i = 0; i < NC; ++i) {
+                    const int c = tid + kBT * i;
+                    if (c < GW) acc[pos - p0][c] += gr[c];
+                }
+            }
+        }
+    }
+    __syncthreads();
+    // every position of the tile: 16-byte stores (zeros when nothing selected the tile)
+    for (int e = tid; e < kPT * GW / 4; e += kBT) {
+        const int r = e / (GW / 4), c = 4 * (e % (GW / 4));
+        const int pos = p0 + r;
+        if (pos >= a.N) break;
+        const int64_t rowk = ((int64_t)b * a.N + pos) * a.Hkv + kvh;
+        f32x4 v = {0.0f, 0.0f, 0.0f, 0.0f};
+        if (touched) v = *reinterpret_cast<const f32x4 *>(&acc[r][c]);
+        float *dst = c < DQK ? a.dk + rowk * DQK + c : a.dv + rowk * DV + (c - DQK);
+        *reinterpret_cast<f32x4 *>(dst) = v;
+    }
+}
+
+struct BwdLayout {
+    size_t g_off, g_bytes, dq_off, dq_bytes, total;
+    int ntiles;
+};
+
+BwdLayout bwd_layout(const AttendBwdArgs &a) {
+    const int DQK = a.mla ? 576 : 128, DV = a.mla ? 512 : 128;
+    const int GW = a.mla ? DQK : DQK + DV;
+    BwdLayout l;
+    l.ntiles = (a.K + kRT - 1) / kRT;
+    l.g_off = 0;
+    l.g_bytes = (size_t)a.B * a.T * a.Hkv * a.K * GW * sizeof(float);
+    l.dq_off = (l.g_bytes + 255) / 256 * 256;
+    l.dq_bytes = (size_t)a.B * a.T * a.Hq * l.ntiles * DQK * sizeof(float);
+    l.total = l.dq_off + l.dq_bytes;
+    return l;
+}
+
+template <int DQK, int DV, bool MLA>
+hipError_t launch_bwd_t(const AttendBwdArgs &a, void *ws, hipStream_t s) {
+    const BwdLayout l = bwd_layout(a);
+    float *G = reinterpret_cast<float *>(static_cast<unsigned char *>(ws) + l.g_off);
+    float *dqp = reinterpret_cast<float *>(static_cast<unsigned char *>(ws) + l.dq_off);
+    hipLaunchKernelGGL((bwd_rows_kernel<DQK, DV, MLA>), dim3(l.ntiles, a.B * a.T, a.Hkv), dim3(kBT), 0, s, a, G, dqp);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL((bwd_dq_kernel<DQK>), dim3(a.B * a.T * a.Hq), dim3(64), 0, s, a, dqp, l.ntiles);
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+    hipLaunchKernelGGL((bwd_kv_kernel<DQK, DV, MLA>), dim3((a.N + kPT - 1) / kPT, a.B, a.Hkv), dim3(kBT), 0, s, a, G);
+    return hipGetLastError();
+}
+
+}  // namespace
+
+size_t attend_bwd_workspace_bytes(const AttendBwdArgs &a) { return bwd_layout(a).total; }
+
+hipError_t launch_attend_bwd(const AttendBwdArgs &a, void *ws, hipStream_t s) {
+    return a.mla ? launch_bwd_t<576, 512, true>(a, ws, s) : launch_bwd_t<128, 128, false>(a, ws, s);
+}
+
+}  // namespace lsa

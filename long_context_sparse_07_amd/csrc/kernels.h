@@ -70,6 +70,28 @@ struct CacheAppendArgs {
 };
 hipError_t launch_cache_append(const CacheAppendArgs &a, hipStream_t s);
 
+// Backward of the sparse attention for one layer (selection fixed): dq, and the gradients
+// of the selected K/V rows summed over the queries that selected them.
+struct AttendBwdArgs {
+    int B, T, N, Hq, Hkv, K;
+    const uint16_t *q;      // bf16 [B][T][Hq][d_qk]
+    const uint16_t *k;      // bf16, element (b, s, h, d) at b*ksb + s*ksn + h*ksh + d
+    int64_t ksb, ksn, ksh;
+    const uint16_t *v;      // bf16 (MLA: v == k, the first 512 columns)
+    int64_t vsb, vsn, vsh;
+    const int32_t *idx;     // [B][T][K]: valid entries ascending, then -1
+    float scale;
+    const uint16_t *out;    // bf16 [B][T][Hq][d_v] (forward output)
+    const float *lse;       // [B][T][Hq]
+    const uint16_t *dout;   // bf16 [B][T][Hq][d_v]
+    float *dq;              // [B][T][Hq][d_qk]
+    float *dk;              // [B][N][Hkv][d_qk] (MLA: dK + dV on the first d_v columns)
+    float *dv;              // [B][N][Hkv][d_v], null for MLA
+    bool mla;
+};
+size_t attend_bwd_workspace_bytes(const AttendBwdArgs &a);
+hipError_t launch_attend_bwd(const AttendBwdArgs &a, void *ws, hipStream_t s);
+
 struct SelectArgs {
     int B, T, N;
     const int32_t *ctx_len;

@@ -35,6 +35,7 @@ def test_library_exports_every_declared_function():
 def test_descriptor_layout_matches_c(tmp_path):
     structs = {"lsa_index_desc": L.IndexDesc, "lsa_block_means_desc": L.BlockMeansDesc,
                "lsa_select_desc": L.SelectDesc, "lsa_attend_desc": L.AttendDesc,
+               "lsa_attend_bwd_desc": L.AttendBwdDesc,
                "lsa_cache_append_desc": L.CacheAppendDesc}
     lines = ['#include <stdio.h>', '#include <stddef.h>', f'#include "{HEADER}"', "int main(void){"]
     for cname, py in structs.items():
@@ -265,3 +266,39 @@ def test_status_strings():
     assert lib.lsa_workspace_clear(None, 16, None) == -1
     assert lib.lsa_workspace_clear(FAKE + 4, 16, None) == -5
     assert lib.lsa_workspace_clear(None, 0, None) == 0
+
+
+def _bwd_desc(**kw):
+    base = dict(B=2, T=1, N=1024, Hq=64, Hkv=1, d_qk=576, d_v=512, q=FAKE, k=FAKE, k_stride_b=1024 * 576,
+                k_stride_n=576, k_stride_h=576, v=FAKE, v_stride_b=1024 * 576, v_stride_n=576, v_stride_h=576,
+                idx=FAKE, K=256, softmax_scale=0.04, out=FAKE, lse=FAKE, dout=FAKE, dq=FAKE, dk=FAKE)
+    base.update(kw)
+    return L.AttendBwdDesc(**base)
+
+
+def _bwd(d, ws=FAKE, nbytes=1 << 40):
+    return L.lib().lsa_attend_backward(ctypes.byref(d), ws, nbytes, None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(q=None), -1), (dict(dout=None), -1), (dict(lse=None), -1), (dict(dk=None), -1),
+    (dict(d_qk=128, d_v=128, Hkv=8, k_stride_h=128, v_stride_h=128, k_stride_n=1024, v_stride_n=1024,
+          k_stride_b=1 << 20, v_stride_b=1 << 20, v=FAKE + 4096), -1),   # GQA needs dv
+    (dict(K=0), -4), (dict(Hq=63, Hkv=2), -2), (dict(B=0), -2),
+    (dict(d_qk=64, d_v=64), -6), (dict(Hq=128), -6), (dict(v=FAKE + 256), -6),
+    (dict(k_stride_n=577, v_stride_n=577), -5), (dict(out=FAKE + 8), -5), (dict(dq=FAKE + 2), -5),
+    (dict(T=40000), -6),
+])
+def test_attend_backward_argument_errors(kw, code):
+    assert _bwd(_bwd_desc(**kw)) == code
+
+
+def test_attend_backward_workspace_rules():
+    d = _bwd_desc()
+    need = L.lib().lsa_attend_backward_workspace_bytes(ctypes.byref(d))
+    # per (query, KV head, selected row) one MLA row of fp32, then per 32-row tile a dq part
+    assert need == 2 * 256 * 576 * 4 + 2 * 64 * 8 * 576 * 4
+    assert _bwd(d, FAKE, need - 1) == -7
+    assert _bwd(d, None, need) == -7
+    assert _bwd(d, FAKE + 16, need) == -5
+    assert L.lib().lsa_attend_backward_workspace_bytes(ctypes.byref(_bwd_desc(K=0))) == 0

@@ -1,0 +1,174 @@
+"""lsa_attend_backward on the GPU against the oracle's attend_backward (reading R28).
+
+Inputs are seeded bf16 values; the forward's output and log-sum-exp given to both sides
+are the oracle's (float64) rounded to bf16 and fp32, as the forward kernel stores them.
+Both sides then compute the same function; the GPU in fp32 from the bf16 values, the
+oracle in float64. Tolerance, from the arithmetic: every gradient entry is a sum of at
+most K * (Hq / Hkv) * T products of O(1) values accumulated in fp32, so its error stays
+far below 1e-4 of the tensor's largest entry (the test asserts that bound and prints the
+measured one). Positions no query selected must be exactly zero.
+
+Cases: MLA (64 heads on one latent row; dk holds dK + dV), GQA (4 KV heads of 8 query
+heads), several query tokens selecting overlapping rows (the local window), padded
+index rows, a query with no valid entry, K not a multiple of the 32-row tile, two calls
+giving identical bits, and the 128K MLA decode shape (8 sequences, 2048 rows each) on
+its selected rows.
+"""
+import numpy as np
+import pytest
+import torch
+
+import long_context_sparse_07_amd as L
+from oracle import lsa_oracle as O
+
+pytestmark = pytest.mark.gpu
+
+
+def _bits(x):
+    return torch.from_numpy(np.ascontiguousarray(x, dtype=np.float32)).to(torch.bfloat16)
+
+
+def _f64(t):
+    return t.to(torch.float32).numpy().astype(np.float64)
+
+
+def _idx_rows(rng, B, T, N, K, window, n_valid):
+    """Ascending distinct positions, -1 padded: the last `window` positions (selected by
+    every query) plus random earlier ones."""
+    idx = np.full((B, T, K), -1, np.int32)
+    for b in range(B):
+        for t in range(T):
+            nv = n_valid[b][t]
+            if nv == 0:
+                continue
+            win = np.arange(N - window, N)[: nv]
+            rest = rng.choice(N - window, nv - win.size, replace=False)
+            idx[b, t, :nv] = np.sort(np.concatenate([win, rest]))
+    return idx
+
+
+def _case(rng, B, T, N, Hq, Hkv, mla, K, window, n_valid):
+    dqk, dv = (576, 512) if mla else (128, 128)
+    q = _bits(rng.standard_normal((B, T, Hq, dqk)) / np.sqrt(dqk))
+    k = _bits(rng.standard_normal((B, N, 1 if mla else Hkv, dqk)))
+    v = None if mla else _bits(rng.standard_normal((B, N, Hkv, dv)))
+    dout = _bits(rng.standard_normal((B, T, Hq, dv)))
+    idx = _idx_rows(rng, B, T, N, K, window, n_valid)
+    tau = dqk ** -0.5
+    # forward by the oracle, stored as the forward kernel stores it
+    kf = _f64(k)
+    vf = kf[..., :dv] if mla else _f64(v)
+    qf = _f64(q)
+    out = np.zeros((B, T, Hq, dv))
+    lse = np.zeros((B, T, Hq))
+    for b in range(B):
+        for t in range(T):
+            out[b, t], lse[b, t] = O.attend(qf[b, t], kf[b], vf[b], idx[b, t], tau)
+    out_b = _bits(out)
+    lse32 = lse.astype(np.float32)
+    return dict(q=q, k=k, v=v, dout=dout, idx=idx, tau=tau, out=out_b, lse=lse32, qf=qf, kf=kf, vf=vf, mla=mla,
+                dv=dv)
+
+
+def _oracle_grads(c):
+    B, T = c["idx"].shape[:2]
+    dq = np.zeros(c["qf"].shape)
+    dK = np.zeros(c["kf"].shape)
+    dV = np.zeros(c["vf"].shape)
+    outf, doutf = _f64(c["out"]), _f64(c["dout"])
+    for b in range(B):
+        for t in range(T):
+            g = O.attend_backward(c["qf"][b, t], c["kf"][b], c["vf"][b], c["idx"][b, t], c["tau"], outf[b, t],
+                                  c["lse"][b, t].astype(np.float64), doutf[b, t])
+            dq[b, t] = g[0]
+            dK[b] += g[1]
+            dV[b] += g[2]
+    if c["mla"]:
+        return dq, O.mla_row_grad(dK, dV), None
+    return dq, dK, dV
+
+
+def _gpu_grads(c):
+    return L.lsa_attend_backward(c["q"].cuda(), c["k"].cuda(), None if c["mla"] else c["v"].cuda(),
+                                 torch.from_numpy(c["idx"]).cuda(), c["tau"], c["out"].cuda(),
+                                 torch.from_numpy(c["lse"]).cuda(), c["dout"].cuda())
+
+
+def _close(got, want, what):
+    g = got.cpu().numpy().astype(np.float64)
+    scale = max(np.max(np.abs(want)), 1e-30)
+    err = np.max(np.abs(g - want)) / scale
+    assert err < 1e-4, f"{what}: error {err:.2e} of the largest entry"
+    assert np.array_equal(g == 0, want == 0) or what.startswith("dq"), f"{what}: zero pattern differs"
+    print(f"{what}: {err:.2e}")
+
+
+@pytest.mark.parametrize("mla", [True, False])
+def test_backward_matches_oracle(mla):
+    rng = np.random.default_rng(60 + mla)
+    B, T, N, K = 2, 3, 3000 if mla else 2000, 200
+    Hq, Hkv = (64, 1) if mla else (32, 4)
+    n_valid = [[200, 150, 77], [1, 200, 0]]   # padded rows, one row, a query with nothing
+    c = _case(rng, B, T, N, Hq, Hkv, mla, K, 48, n_valid)
+    dq, dk, dv = _gpu_grads(c)
+    torch.cuda.synchronize()
+    wq, wk, wv = _oracle_grads(c)
+    _close(dq, wq, "dq")
+    _close(dk, wk, "dk")
+    if not mla:
+        _close(dv, wv, "dv")
+    assert not dq[1, 2].any()  # no valid entry: no gradient
+    # deterministic: a second call gives the same bits
+    dq2, dk2, dv2 = _gpu_grads(c)
+    assert torch.equal(dq2, dq) and torch.equal(dk2, dk) and (mla or torch.equal(dv2, dv))
+
+
+def test_backward_ragged_k_and_single_row():
+    rng = np.random.default_rng(62)
+    c = _case(rng, 1, 2, 500, 16, 2, False, 77, 10, [[77, 1]])
+    dq, dk, dv = _gpu_grads(c)
+    wq, wk, wv = _oracle_grads(c)
+    _close(dq, wq, "dq ragged")
+    _close(dk, wk, "dk ragged")
+    _close(dv, wv, "dv ragged")
+
+
+def test_backward_128k_mla_decode_shape():
+    # 8 sequences of 131072 cached rows, one query token each, 2048 selected rows, MLA 64
+    # heads: the oracle works on the selected rows only (unselected rows are zero)
+    rng = np.random.default_rng(63)
+    B, N, K, Hq = 8, 131072, 2048, 64
+    idx = _idx_rows(rng, B, 1, N, K, 512, [[K]] * B)
+    q = _bits(rng.standard_normal((B, 1, Hq, 576)) / 24.0)
+    dout = _bits(rng.standard_normal((B, 1, Hq, 512)))
+    k = torch.empty((B, N, 1, 576), dtype=torch.bfloat16)
+    sel_rows = _bits(rng.standard_normal((B, K, 1, 576)))
+    for b in range(B):
+        k[b, idx[b, 0]] = sel_rows[b]
+    tau = 576 ** -0.5
+    out = np.zeros((B, 1, Hq, 512))
+    lse = np.zeros((B, 1, Hq))
+    ks = _f64(sel_rows)
+    qf = _f64(q)
+    local = np.arange(K)
+    for b in range(B):
+        out[b, 0], lse[b, 0] = O.attend(qf[b, 0], ks[b], ks[b][..., :512], local, tau)
+    out_b, lse32 = _bits(out), lse.astype(np.float32)
+    kg = k.cuda()  # unselected rows hold whatever the allocator left: they must not matter
+    dq, dk, _ = L.lsa_attend_backward(q.cuda(), kg, None, torch.from_numpy(idx).cuda(), tau, out_b.cuda(),
+                                      torch.from_numpy(lse32).cuda(), dout.cuda())
+    torch.cuda.synchronize()
+    outf, doutf = _f64(out_b), _f64(dout)
+    dk_sel = dk[torch.arange(B, device="cuda")[:, None], torch.from_numpy(idx[:, 0]).long().cuda()].cpu().numpy()
+    dq_c = dq.cpu().numpy()
+    for b in range(B):
+        g = O.attend_backward(qf[b, 0], ks[b], ks[b][..., :512], local, tau, outf[b, 0], lse32[b, 0].astype(np.float64),
+                              doutf[b, 0])
+        want_k = O.mla_row_grad(g[1], g[2])
+        for name, got, want in (("dq", dq_c[b, 0], g[0]), ("dk", dk_sel[b], want_k)):
+            err = np.max(np.abs(got - want)) / np.max(np.abs(want))
+            assert err < 1e-4, f"b={b} {name}: {err:.2e}"
+    # every other position is zero
+    mask = torch.ones((B, N), dtype=torch.bool, device="cuda")
+    mask[torch.arange(B, device="cuda")[:, None], torch.from_numpy(idx[:, 0]).long().cuda()] = False
+    assert not dk[mask].any()
