@@ -429,13 +429,16 @@ __global__ __launch_bounds__(PRE ? kThreads : 2 * kThreads) void index_tokens_ke
             const unsigned char *tile = ring + st * G::STAGE;
             const float *tscale = reinterpret_cast<const float *>(tile + G::BYTES);
             if (active) {
+                // the MFMAs of sub-tile sb + 1 are issued before the epilogue of sub-tile sb
+                // (accumulators alternate), so the matrix core and the VALU overlap
+                f32x16 acc[2][HB];
+                mfma_tile(tile, l32, acc[0]);
 #pragma unroll
                 for (int sb = 0; sb < 4; ++sb) {
                     const int row = sb * 32 + l32;
-                    f32x16 acc[HB];
-                    mfma_tile(tile, row, acc);
+                    if (sb + 1 < 4) mfma_tile(tile, row + 32, acc[(sb + 1) & 1]);
                     const int col = c0 + it * kKT + row;
-                    epilogue(acc, col, col < c1 && col < N ? col : -1, FP8 ? tscale[row] : 1.0f);
+                    epilogue(acc[sb & 1], col, col < c1 && col < N ? col : -1, FP8 ? tscale[row] : 1.0f);
                 }
             }
         }
