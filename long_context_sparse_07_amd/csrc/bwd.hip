@@ -23,7 +23,7 @@ namespace {
 
 constexpr int kBT = 256;  // threads per workgroup
 constexpr int kRT = 32;   // selected rows per bwd_rows workgroup
-constexpr int kPT = 32;   // cache positions per bwd_kv workgroup
+constexpr int kPT = 16;   // cache positions per bwd_kv workgroup (LDS: 16 x 576 fp32, four workgroups a CU)
 constexpr int kMaxG = 64; // query heads per KV head
 
 __device__ __forceinline__ float dot8(u32x4 x, u32x4 y) {
