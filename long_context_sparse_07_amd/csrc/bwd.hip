@@ -8,9 +8,10 @@
 //   dq_h = scale sum_s dS K_s,  dK_s = scale sum_(t,h) dS q_h,  dV_s = sum_(t,h) P dO_h.
 //
 // bwd_rows_kernel (one workgroup per query token, KV head and tile of 32 selected rows):
-//   the tile's K (and V) rows are gathered into LDS; P and scale * dS for every head of
-//   the group and row of the tile; then the rows' gradient contributions of this query
-//   (G: scale sum_h dS q_h, and sum_h P dO_h) and this tile's part of dq.
+//   the tile's K (and V) rows are gathered into LDS; q . K and dO . V for every head of
+//   the group and row of the tile on the matrix cores, then P and scale * dS; then the
+//   rows' gradient contributions of this query (G: scale sum_h dS q_h, and sum_h P dO_h)
+//   and this tile's part of dq.
 // bwd_dq_kernel: dq = the tiles' parts, added in tile order.
 // bwd_kv_kernel (one workgroup per tile of 32 cache positions and KV head): the
 //   contributions G of every query that selected one of the positions, added in ascending
@@ -46,6 +47,7 @@ __global__ __launch_bounds__(kBT) void bwd_rows_kernel(AttendBwdArgs a, float *G
     __shared__ __attribute__((aligned(16))) uint16_t vt[MLA ? 1 : kRT][DV];
     __shared__ __attribute__((aligned(16))) float Ps[kMaxG][kRT];
     __shared__ __attribute__((aligned(16))) float dSs[kMaxG][kRT];  // scale * dS
+    __shared__ float Zs[kMaxG][kRT], DPs[kMaxG][kRT];  // q . K_r and dO . V_r (unscaled)
     __shared__ float Dh[kMaxG], lseh[kMaxG];
     __shared__ int rowpos[kRT];
 
@@ -100,33 +102,58 @@ __global__ __launch_bounds__(kBT) void bwd_rows_kernel(AttendBwdArgs a, float *G
     }
     __syncthreads();
 
-    // P and scale * dS: thread (h, part) takes rows part + 4 j
-    if (h < g) {
-        float z[kRT / 4], dp[kRT / 4];
+    // z^T = K_tile q^T and dP^T = V_tile dO^T on v_mfma_f32_32x32x16_bf16 (bf16 products,
+    // fp32 sums): one 32 rows x 32 heads block per wave, z blocks first, then dP blocks
+    {
+        const int wave = tid >> 6, lane = tid & 63, l32 = lane & 31, half = lane >> 5;
+        const int nhb = (g + 31) / 32;
+        if (wave < 2 * nhb) {
+            const bool isdp = wave >= nhb;
+            const int head = 32 * (isdp ? wave - nhb : wave) + l32;
+            const bool hok = head < g;
+            f32x16 acc;
 #pragma unroll
-        for (int j = 0; j < kRT / 4; ++j) z[j] = dp[j] = 0.0f;
-        const uint16_t *qrow = a.q + (qh0 + h) * DQK, *dorow = a.dout + (qh0 + h) * DV;
-        for (int c = 0; c < DQK / 8; ++c) {
-            const u32x4 qv = *reinterpret_cast<const u32x4 *>(qrow + 8 * c);
+            for (int r = 0; r < 16; ++r) acc[r] = 0.0f;
+            // A: key row l32, dims 16 st + 8 half .. +8 (LDS); B: head `head`, the same dims
+            if (!isdp) {
+                const uint16_t *qp = a.q + (qh0 + (hok ? head : 0)) * DQK + 8 * half;
+#pragma unroll 4
+                for (int st = 0; st < DQK / 16; ++st) {
+                    u32x4 bv = {0, 0, 0, 0};
+                    if (hok) bv = *reinterpret_cast<const u32x4 *>(qp + 16 * st);
+                    const u32x4 av = *reinterpret_cast<const u32x4 *>(&kt[l32][16 * st + 8 * half]);
+                    acc = mfma32(__builtin_bit_cast(bf16x8, av), __builtin_bit_cast(bf16x8, bv), acc);
+                }
+            } else {
+                const uint16_t *op = a.dout + (qh0 + (hok ? head : 0)) * DV + 8 * half;
+#pragma unroll 4
+                for (int st = 0; st < DV / 16; ++st) {
+                    u32x4 bv = {0, 0, 0, 0};
+                    if (hok) bv = *reinterpret_cast<const u32x4 *>(op + 16 * st);
+                    const uint16_t *vr = MLA ? &kt[l32][16 * st + 8 * half] : &vt[MLA ? 0 : l32][16 * st + 8 * half];
+                    const u32x4 av = *reinterpret_cast<const u32x4 *>(vr);
+                    acc = mfma32(__builtin_bit_cast(bf16x8, av), __builtin_bit_cast(bf16x8, bv), acc);
+                }
+            }
+            // C: lane holds head column l32, rows 8 (r / 4) + 4 half + r % 4
+            float(*dst)[kRT] = isdp ? DPs : Zs;
+            if (hok) {
 #pragma unroll
-            for (int j = 0; j < kRT / 4; ++j) z[j] += dot8(qv, *reinterpret_cast<const u32x4 *>(&kt[part + 4 * j][8 * c]));
-        }
-        for (int c = 0; c < DV / 8; ++c) {
-            const u32x4 ov = *reinterpret_cast<const u32x4 *>(dorow + 8 * c);
-#pragma unroll
-            for (int j = 0; j < kRT / 4; ++j) {
-                const uint16_t *vr = MLA ? &kt[part + 4 * j][8 * c] : &vt[MLA ? 0 : part + 4 * j][8 * c];
-                dp[j] += dot8(ov, *reinterpret_cast<const u32x4 *>(vr));
+                for (int r = 0; r < 16; ++r) dst[head][8 * (r / 4) + 4 * half + (r % 4)] = acc[r];
             }
         }
+    }
+    __syncthreads();
+    // P and scale * dS: thread (h, part) takes rows part + 4 j
+    if (h < g) {
         const float lse = lseh[h], D = Dh[h];
 #pragma unroll
         for (int j = 0; j < kRT / 4; ++j) {
             const int r = part + 4 * j;
             // a query with no valid row has lse = -inf and no row here with rowpos >= 0
-            const float p = (rowpos[r] >= 0 && lse > kNegInf) ? expf(a.scale * z[j] - lse) : 0.0f;
+            const float p = (rowpos[r] >= 0 && lse > kNegInf) ? expf(a.scale * Zs[h][r] - lse) : 0.0f;
             Ps[h][r] = p;
-            dSs[h][r] = a.scale * (p * (dp[j] - D));
+            dSs[h][r] = a.scale * (p * (DPs[h][r] - D));
         }
     }
     __syncthreads();
