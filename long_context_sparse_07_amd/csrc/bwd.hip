@@ -158,39 +158,107 @@ __global__ __launch_bounds__(kBT) void bwd_rows_kernel(AttendBwdArgs a, float *G
     }
     __syncthreads();
 
-    // G rows of this query: column c of row r (heads in order)
+    // The two remaining products run on v_mfma_f32_32x32x16_bf16 too. Their fp32 factors
+    // (scale dS, P) enter as a sum of two bf16 values, hi = bf16(x) and lo = bf16(x - hi),
+    // so each product carries about 16 significant bits of the factor (two instructions);
+    // q, dO and the K rows are bf16 already. Heads past g count as zero.
+    const int wave = tid >> 6, lane = tid & 63, l32 = lane & 31, half = lane >> 5;
+    auto split8 = [](const float (&x)[8], bf16x8 &hi, bf16x8 &lo) {
+        u32x4 h, l;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            const uint32_t h0 = f2bf(x[2 * e]), h1 = f2bf(x[2 * e + 1]);
+            h[e] = h0 | (h1 << 16);
+            l[e] = f2bf(x[2 * e] - u2f(h0 << 16)) | (f2bf(x[2 * e + 1] - u2f(h1 << 16)) << 16);
+        }
+        hi = __builtin_bit_cast(bf16x8, h);
+        lo = __builtin_bit_cast(bf16x8, l);
+    };
+    const int nks = (g + 15) / 16;  // 16-head steps
+
+    // G rows of this query, 32 columns a block: row r, column c = sum_h A[r][h] B[h][c] with
+    // A = scale dS^T and B = q (K part), A = P^T and B = dO (V part; MLA: the first DV
+    // columns of the same row)
     float *gout = G + (((int64_t)bt * a.Hkv + kvh) * a.K + r0) * GW;
-    for (int c = tid; c < GW; c += kBT) {
-        float acc[kRT];
-#pragma unroll
-        for (int r = 0; r < kRT; ++r) acc[r] = 0.0f;
-        const bool kcol = c < DQK;                               // K part (scale dS q)
-        const bool vcol = MLA ? c < DV : c >= DQK;               // V part (P dO)
+    for (int cb = wave; cb < GW / 32; cb += kBT / 64) {
+        const int c = 32 * cb + l32;
+        const bool kpart = 32 * cb < DQK;
+        const bool vpart = MLA ? 32 * cb < DV : !kpart;
         const int vc = MLA ? c : c - DQK;
-        for (int hh = 0; hh < g; ++hh) {
-            const float qv = kcol ? bf16_at(a.q + (qh0 + hh) * DQK + c) : 0.0f;
-            const float ov = vcol ? bf16_at(a.dout + (qh0 + hh) * DV + vc) : 0.0f;
+        f32x16 acc;
 #pragma unroll
-            for (int r4 = 0; r4 < kRT / 4; ++r4) {
-                const f32x4 ds = *reinterpret_cast<const f32x4 *>(&dSs[hh][4 * r4]);
-                const f32x4 pp = *reinterpret_cast<const f32x4 *>(&Ps[hh][4 * r4]);
+        for (int r = 0; r < 16; ++r) acc[r] = 0.0f;
+        for (int ks = 0; ks < nks; ++ks) {
+            const int hb0 = 16 * ks + 8 * half;  // this lane's 8 heads
 #pragma unroll
-                for (int e = 0; e < 4; ++e) acc[4 * r4 + e] += ds[e] * qv + pp[e] * ov;
+            for (int part = 0; part < 2; ++part) {
+                if (part == 0 ? !kpart : !vpart) continue;
+                float x[8];
+                u32x4 bw;
+#pragma unroll
+                for (int e = 0; e < 8; ++e) {
+                    const int hh = hb0 + e;
+                    x[e] = hh < g ? (part == 0 ? dSs[hh][l32] : Ps[hh][l32]) : 0.0f;
+                }
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    uint32_t w2 = 0;
+#pragma unroll
+                    for (int u = 0; u < 2; ++u) {
+                        const int hh = hb0 + 2 * e + u;
+                        const uint32_t v = hh < g ? (uint32_t)(part == 0 ? a.q[(qh0 + hh) * DQK + c]
+                                                                           : a.dout[(qh0 + hh) * DV + vc])
+                                                  : 0u;
+                        w2 |= v << (16 * u);
+                    }
+                    bw[e] = w2;
+                }
+                bf16x8 ahi, alo;
+                split8(x, ahi, alo);
+                const bf16x8 bv = __builtin_bit_cast(bf16x8, bw);
+                acc = mfma32(ahi, bv, acc);
+                acc = mfma32(alo, bv, acc);
             }
         }
+        // C: lane holds column c, rows 8 (r / 4) + 4 half + r % 4
 #pragma unroll
-        for (int r = 0; r < kRT; ++r)
-            if (r < nrows) gout[(int64_t)r * GW + c] = acc[r];
+        for (int r = 0; r < 16; ++r) {
+            const int row = 8 * (r / 4) + 4 * half + (r % 4);
+            if (row < nrows) gout[(int64_t)row * GW + c] = acc[r];
+        }
     }
 
-    // this tile's part of dq: scale sum_r dS K_r
+    // this tile's part of dq: head h, dim d = sum_r (scale dS)[h][r] K_r[d]
     float *dq = dqp + (((int64_t)bt * a.Hkv + kvh) * ntiles + tile) * g * DQK;
-    for (int e = tid; e < g * DQK; e += kBT) {
-        const int hh = e / DQK, d = e % DQK;
-        float s = 0.0f;
-#pragma unroll 8
-        for (int r = 0; r < kRT; ++r) s += dSs[hh][r] * u2f((uint32_t)kt[r][d] << 16);
-        dq[e] = s;
+    const int nhb = (g + 31) / 32;
+    for (int blk = wave; blk < nhb * (DQK / 32); blk += kBT / 64) {
+        const int hb = blk / (DQK / 32), cb = blk % (DQK / 32);
+        const int head = 32 * hb + l32, d = 32 * cb + l32;
+        f32x16 acc;
+#pragma unroll
+        for (int r = 0; r < 16; ++r) acc[r] = 0.0f;
+#pragma unroll
+        for (int ks = 0; ks < kRT / 16; ++ks) {
+            const int rr0 = 16 * ks + 8 * half;  // this lane's 8 rows
+            float x[8];
+#pragma unroll
+            for (int e = 0; e < 8; ++e) x[e] = head < g ? dSs[head][rr0 + e] : 0.0f;
+            u32x4 bw;
+#pragma unroll
+            for (int e = 0; e < 4; ++e)
+                bw[e] = (uint32_t)kt[rr0 + 2 * e][d] | ((uint32_t)kt[rr0 + 2 * e + 1][d] << 16);
+            bf16x8 ahi, alo;
+            split8(x, ahi, alo);
+            const bf16x8 bv = __builtin_bit_cast(bf16x8, bw);
+            acc = mfma32(ahi, bv, acc);
+            acc = mfma32(alo, bv, acc);
+        }
+        // C: lane holds dim d, heads 32 hb + 8 (r / 4) + 4 half + r % 4
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+            const int hh = 32 * hb + 8 * (r / 4) + 4 * half + (r % 4);
+            if (hh < g) dq[hh * DQK + d] = acc[r];
+        }
     }
 }
 

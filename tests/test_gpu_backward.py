@@ -2,11 +2,13 @@
 
 Inputs are seeded bf16 values; the forward's output and log-sum-exp given to both sides
 are the oracle's (float64) rounded to bf16 and fp32, as the forward kernel stores them.
-Both sides then compute the same function; the GPU in fp32 from the bf16 values, the
-oracle in float64. Tolerance, from the arithmetic: every gradient entry is a sum of at
-most K * (Hq / Hkv) * T products of O(1) values accumulated in fp32, so its error stays
-far below 1e-4 of the tensor's largest entry (the test asserts that bound and prints the
-measured one). Positions no query selected must be exactly zero.
+Both sides then compute the same function; the GPU with fp32 sums of exact bf16
+products, its fp32 factors P and scale * dS entering the matrix products as two bf16
+parts (about 2^-17 relative error per factor), the oracle in float64. Tolerance, from the
+arithmetic: every gradient entry is a sum of at most K * (Hq / Hkv) * T such products of
+O(1) values, so its error stays far below 1e-4 of the tensor's largest entry (the test
+asserts that bound and prints the measured one). Positions no query selected must be
+exactly zero.
 
 Cases: MLA (64 heads on one latent row; dk holds dK + dV), GQA (4 KV heads of 8 query
 heads), several query tokens selecting overlapping rows (the local window), padded
