@@ -282,6 +282,31 @@ __global__ __launch_bounds__(64) void bwd_dq_kernel(AttendBwdArgs a, const float
     }
 }
 
+// One wave finds the run of slots of an index row (valid entries ascending, padding last)
+// whose positions lie in [p0, p0 + kPT): each round samples 64 slots at once and keeps the
+// interval where the first slot >= p0 lies, so a row of 2048 entries costs three rounds of
+// loads (a binary search by one thread: eleven, then up to kPT more for the run).
+__device__ __forceinline__ void wave_find_run(const int32_t *row, int K, int p0, int &lo, int &cnt) {
+    const int ln = threadIdx.x & 63;
+    auto key = [&](int slot) { const int s = row[slot]; return s < 0 ? 0x7FFFFFFF : s; };
+    int lb = 0, hb = K;  // the first slot with key >= p0 lies in [lb, hb] (hb: none below K)
+    while (hb - lb > 64) {
+        const int S = (hb - lb + 63) / 64;
+        const int sl = lb + ln * S;
+        const int n = __popcll(__ballot(sl < hb && key(sl) < p0));  // samples below p0 (a prefix)
+        if (n == 0) {
+            hb = lb;
+            break;
+        }
+        const int nlb = lb + (n - 1) * S + 1;
+        hb = min(lb + n * S, hb);
+        lb = nlb;
+    }
+    if (hb > lb) lb += __popcll(__ballot(lb + ln < hb && key(lb + ln) < p0));
+    lo = lb;
+    cnt = __popcll(__ballot(ln < kPT && lo + ln < K && key(lo + ln) < p0 + kPT));
+}
+
 template <int DQK, int DV, bool MLA>
 __global__ __launch_bounds__(kBT) void bwd_kv_kernel(AttendBwdArgs a, const float *G) {
     constexpr int GW = g_width<DQK, DV, MLA>();
@@ -295,8 +320,13 @@ __global__ __launch_bounds__(kBT) void bwd_kv_kernel(AttendBwdArgs a, const floa
         // thread j finds the slots of query t0 + j whose positions fall in [p0, p0 + kPT):
         // valid entries ascend and padding (-1) comes last, so they are one run of slots
         const int t = t0 + tid;
-        int lo = 0, cnt = 0;
-        if (t < a.T) {
+        int lo = 0, cnt = 0, entry = tid;  // entry: the lo_s / cnt_s slot this thread fills, or -1
+        if (a.T <= kBT / 64) {
+            // few queries (decode): wave w searches query w, 64 slots per round of loads
+            const int w = tid >> 6;
+            entry = (tid & 63) == 0 ? w : -1;
+            if (w < a.T) wave_find_run(a.idx + ((int64_t)b * a.T + w) * a.K, a.K, p0, lo, cnt);
+        } else if (t < a.T) {
             const int32_t *row = a.idx + ((int64_t)b * a.T + t) * a.K;
             auto key = [&](int slot) { const int s = row[slot]; return s < 0 ? 0x7FFFFFFF : s; };
             int hi = a.K;
@@ -308,9 +338,11 @@ __global__ __launch_bounds__(kBT) void bwd_kv_kernel(AttendBwdArgs a, const floa
             while (lo + cnt < a.K && cnt < kPT && key(lo + cnt) < p0 + kPT) ++cnt;
         }
         __syncthreads();  // the previous chunk is done with lo_s / cnt_s
-        lo_s[tid] = lo;
-        cnt_s[tid] = cnt;
-        const bool any = __syncthreads_or(cnt > 0);
+        if (entry >= 0) {
+            lo_s[entry] = lo;
+            cnt_s[entry] = cnt;
+        }
+        const bool any = __syncthreads_or(entry >= 0 && cnt > 0);
         if (!any) continue;
         if (!touched) {  // first contributions: clear the accumulators
             for (int i = tid; i < kPT * GW; i += kBT) (&acc[0][0])[i] = 0.0f;

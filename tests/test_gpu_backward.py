@@ -13,7 +13,8 @@ exactly zero.
 Cases: MLA (64 heads on one latent row; dk holds dK + dV), GQA (4 KV heads of 8 query
 heads), several query tokens selecting overlapping rows (the local window), padded
 index rows, a query with no valid entry, K not a multiple of the 32-row tile, two calls
-giving identical bits, and the 128K MLA decode shape (8 sequences, 2048 rows each) on
+giving identical bits, up to four query tokens (one wave searches each index row) and
+nine (one thread each), and the 128K MLA decode shape (8 sequences, 2048 rows each) on
 its selected rows.
 """
 import numpy as np
@@ -174,3 +175,17 @@ def test_backward_128k_mla_decode_shape():
     mask = torch.ones((B, N), dtype=torch.bool, device="cuda")
     mask[torch.arange(B, device="cuda")[:, None], torch.from_numpy(idx[:, 0]).long().cuda()] = False
     assert not dk[mask].any()
+
+
+def test_backward_many_query_tokens():
+    # more query tokens than the four the row-gradient kernel searches one wave each: one
+    # thread per query token searches its index row
+    rng = np.random.default_rng(64)
+    T = 9
+    n_valid = [[128, 100, 128, 1, 0, 77, 128, 128, 64]]
+    c = _case(rng, 1, T, 1500, 16, 2, False, 128, 40, n_valid)
+    dq, dk, dv = _gpu_grads(c)
+    wq, wk, wv = _oracle_grads(c)
+    _close(dq, wq, "dq T=9")
+    _close(dk, wk, "dk T=9")
+    _close(dv, wv, "dv T=9")
