@@ -249,6 +249,14 @@ int32_t lsa_select(const lsa_select_desc *desc, void *workspace, size_t workspac
  * the contiguous layout holding the same rows, bit for bit. Errors: LSA_E_SHAPE for
  * page_size, max_pages or num_pages < 1, or a pool above 2^31 - 1 rows.
  * With block_table == NULL the three sizes are ignored.
+ * Shared selection (idx_shared = 1; reading R29, for draft tokens that share one
+ * selection, the MTP extension of LSA in the molayo1419.me LongCat-2.0 article, "The
+ * sparse attention problem at 1M tokens"): idx is int32 [B][K], one row per sequence,
+ * and query token t of sequence b attends over the entries s of idx[b] with
+ * s <= p = ctx_len[b] - T + t (ctx_len: device int32 [B], or NULL for N), so no token sees
+ * a later position; a token left with no entry gets out = 0 and lse = -inf. With
+ * idx_shared = 0, ctx_len is ignored. lsa_select_attend rejects idx_shared
+ * (LSA_E_UNSUPPORTED).
  */
 typedef struct lsa_attend_desc {
     int32_t B, T, N;
@@ -269,6 +277,8 @@ typedef struct lsa_attend_desc {
     int32_t n_splits;
     const int32_t *block_table; /* paged caches: int32 [B][max_pages], or NULL (contiguous) */
     int32_t page_size, max_pages, num_pages;
+    int32_t idx_shared;         /* 1: idx is [B][K], one selection shared by the T tokens */
+    const int32_t *ctx_len;     /* with idx_shared: [B] visible rows, or NULL (= N) */
 } lsa_attend_desc;
 
 size_t lsa_attend_workspace_bytes(const lsa_attend_desc *desc);

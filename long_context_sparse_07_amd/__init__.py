@@ -69,7 +69,8 @@ class AttendDesc(ctypes.Structure):
                 ("out_dtype", c_int32), ("lse", c_void_p), ("n_layers", c_int32),
                 ("layer_stride_q", c_int64), ("layer_stride_k", c_int64), ("layer_stride_v", c_int64),
                 ("layer_stride_out", c_int64), ("layer_stride_lse", c_int64), ("n_splits", c_int32),
-                ("block_table", c_void_p), ("page_size", c_int32), ("max_pages", c_int32), ("num_pages", c_int32)]
+                ("block_table", c_void_p), ("page_size", c_int32), ("max_pages", c_int32), ("num_pages", c_int32),
+                ("idx_shared", c_int32), ("ctx_len", c_void_p)]
 
 
 class AttendBwdDesc(ctypes.Structure):
@@ -279,7 +280,8 @@ def lsa_index_select(q, w, k, K, sink, window, *, k_scale=None, ctx_len=None, ke
     return scores, idx
 
 
-def _attend_desc(q, k, v, idx, softmax_scale, out, lse, mla, n_splits, block_table=None, N=None):
+def _attend_desc(q, k, v, idx, softmax_scale, out, lse, mla, n_splits, block_table=None, N=None, shared=False,
+                 ctx_len=None):
     """q [L,B,T,Hq,dqk]; k,v [L,B,N,Hkv,d] (contiguous per layer). MLA: k [L,B,N,1,576], v=None.
     Paged (block_table int32 [B,max_pages]): k, v are page pools [L,num_pages,page_size,Hkv,d]
     and N (default max_pages * page_size) bounds the positions."""
@@ -314,14 +316,17 @@ def _attend_desc(q, k, v, idx, softmax_scale, out, lse, mla, n_splits, block_tab
                       out_dtype=LSA_F32 if out is not None and out.dtype.is_floating_point and out.element_size() == 4 else LSA_BF16,
                       lse=_ptr(lse), n_layers=L, layer_stride_q=q.stride(0), layer_stride_k=k.stride(0),
                       layer_stride_v=v.stride(0), layer_stride_out=out.stride(0) if out is not None else 0,
-                      layer_stride_lse=lse.stride(0) if lse is not None else 0, n_splits=n_splits, **paged)
+                      layer_stride_lse=lse.stride(0) if lse is not None else 0, n_splits=n_splits,
+                      idx_shared=int(bool(shared)), ctx_len=_ptr(ctx_len) if shared else None, **paged)
 
 
 def lsa_attend(q, k, v, idx, softmax_scale, *, out=None, lse=None, out_dtype=None, with_lse=True,
-               n_splits=0, workspace=None, block_table=None, N=None, stream=None):
+               n_splits=0, workspace=None, block_table=None, N=None, shared=False, ctx_len=None, stream=None):
     """Sparse attention for L layers sharing idx. q bf16 [L,B,T,Hq,dqk]; k, v bf16
     [L,B,N,Hkv,d] (v=None: MLA latent rows, V = k[..., :512]); idx int32 [B,T,K].
     With block_table (int32 [B,max_pages]) k, v are page pools [L,num_pages,page_size,Hkv,d].
+    shared=True: idx is int32 [B,K], one selection for all T tokens, token t masked to
+    positions <= ctx_len[b] - T + t (ctx_len int32 [B] or None for N).
     Returns (out [L,B,T,Hq,dv], lse fp32 [L,B,T,Hq] or None)."""
     import torch
     L, B, T, Hq, dqk = q.shape
@@ -331,7 +336,7 @@ def lsa_attend(q, k, v, idx, softmax_scale, *, out=None, lse=None, out_dtype=Non
         out = torch.empty((L, B, T, Hq, dv), dtype=out_dtype or torch.bfloat16, device=q.device)
     if lse is None and with_lse:
         lse = torch.empty((L, B, T, Hq), dtype=torch.float32, device=q.device)
-    d = _attend_desc(q, k, v, idx, softmax_scale, out, lse, mla, n_splits, block_table, N)
+    d = _attend_desc(q, k, v, idx, softmax_scale, out, lse, mla, n_splits, block_table, N, shared, ctx_len)
     s = _stream(stream)
     need = lib().lsa_attend_workspace_bytes(ctypes.byref(d))
     ws = workspace if workspace is not None else (_workspace("attend", need, q.device)[0] if need else None)

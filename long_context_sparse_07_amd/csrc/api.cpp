@@ -331,6 +331,8 @@ static int32_t attend_check(const lsa_attend_desc *d, lsa::AttendArgs &a) {
     a.lsv = d->layer_stride_v;
     a.lso = d->layer_stride_out;
     a.lsl = d->layer_stride_lse;
+    a.idx_shared = d->idx_shared != 0;
+    a.ctx_len = d->idx_shared ? d->ctx_len : nullptr;
     a.bt = d->block_table;
     a.page_size = d->block_table ? d->page_size : 1;
     a.max_pages = d->block_table ? d->max_pages : 0;
@@ -381,6 +383,7 @@ int32_t lsa_select_attend(const lsa_select_desc *sd, const lsa_attend_desc *ad, 
     if (sd->B != ad->B || sd->T != ad->T || sd->N != ad->N || sd->K != ad->K)
         return fail(LSA_E_SHAPE, "lsa_select_attend: selection and attention disagree on B, T, N or K");
     if (ad->idx && ad->idx != sd->idx) return fail(LSA_E_SHAPE, "lsa_select_attend: att->idx must be NULL or sel->idx");
+    if (ad->idx_shared) return fail(LSA_E_UNSUPPORTED, "lsa_select_attend: a shared index row (call lsa_select, then lsa_attend)");
     if (!sd->scores || !sd->idx || !ad->q || !ad->k || !ad->v || !ad->out)
         return fail(LSA_E_NULL, "lsa_select_attend: scores, idx, q, k, v, out are required");
     if (!aligned4(sd->scores) || !aligned4(sd->idx) || !aligned16(ad->q) || !aligned16(ad->k) || !aligned16(ad->v) ||

@@ -164,7 +164,10 @@ __global__ __launch_bounds__(64 * HW) void attend_kernel(AttendArgs a, uint16_t 
             __syncthreads();
         }
     }
-    const int32_t *idxrow = FUSED ? nullptr : a.idx + selrow * K + r0;
+    // shared selection (draft tokens): one index row per sequence; token t attends only
+    // over its entries at positions <= its own p
+    const int32_t *idxrow = FUSED ? nullptr : a.idx + (a.idx_shared ? (int64_t)b : selrow) * K + r0;
+    const int pmax = a.idx_shared ? (a.ctx_len ? a.ctx_len[b] : a.N) - T + t : 0x7FFFFFFF;
     const uint16_t *kbase = a.k + layer * a.lsk + bofs_k + kvh * a.ksh;
     const uint16_t *vbase = MLA ? kbase : a.v + layer * a.lsv + bofs_v + kvh * a.vsh;
 
@@ -201,7 +204,7 @@ __global__ __launch_bounds__(64 * HW) void attend_kernel(AttendArgs a, uint16_t 
             return (s >= 0 && (a.bt || s < a.N)) ? s : -1;
         } else {
             const int s = i < nrows ? idxrow[i] : -1;
-            return (s >= 0 && s < a.N) ? phys(s) : -1;
+            return (s >= 0 && s < a.N && s <= pmax) ? phys(s) : -1;
         }
     };
     const int lpos0 = rowpos(tid);  // this thread's first entry of the LDS position list

@@ -134,6 +134,8 @@ struct AttendArgs {
     int n_splits;           // resolved (>= 1)
     const int32_t *bt;      // paged caches: block table [B][max_pages] (pool page of each
     int page_size, max_pages, num_pages;  // logical page), else null; pool of num_pages pages
+    bool idx_shared;        // one index row per sequence for all T query tokens, each masked
+    const int32_t *ctx_len; // to positions <= its own p = ctx_len[b] - T + t (null: N)
 };
 constexpr int kAttendMaxSplits = 128;  // split partials merged by one combine workgroup
 int attend_default_splits(const AttendArgs &a);

@@ -44,6 +44,9 @@ Readings where the pages are silent (the pages give no formula at all):
       respect to q, K and V over the selected rows only, the selection held fixed;
       it takes the forward's output and log-sum-exp as inputs (D = dO . O and
       P = exp(z - lse)), and gradients of one row from several queries add up.
+  R29 shared selection for draft tokens (MTP, [P3]): one index row per sequence serves
+      its T query tokens; token t uses only the entries at positions <= its own p_t (R11),
+      so no token attends to a later position.
 """
 from __future__ import annotations
 
@@ -385,6 +388,20 @@ def mla_row_grad(dK, dV):
     d = dK.copy()
     d[..., : dV.shape[-1]] += dV
     return d
+
+
+def shared_selection_rows(idx_row, ctx: int, T: int) -> np.ndarray:
+    """R29: the per-token index rows of one shared selection. Token t sits at
+    p_t = ctx - T + t (R11) and keeps the entries s <= p_t; the rest become -1 (the
+    entries ascend, so the kept ones stay first). Returns int64 [T, K]."""
+    row = np.asarray(idx_row, dtype=np.int64)
+    out = np.empty((T, row.size), dtype=np.int64)
+    for t in range(T):
+        p = ctx - T + t
+        keep = row[(row >= 0) & (row <= p)]
+        out[t] = -1
+        out[t, : keep.size] = keep
+    return out
 
 
 def mla_kv(rows: np.ndarray, d_v: int):

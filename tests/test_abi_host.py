@@ -195,6 +195,7 @@ def _sel_att(ds, da, ws=FAKE, nbytes=1 << 40, wa=FAKE, na=1 << 40):
     (dict(scores=None), dict(), -1), (dict(), dict(q=None), -1), (dict(), dict(out=None), -1),
     (dict(K=0, sink=0, window=0), dict(), -4), (dict(), dict(Hq=48), -6),
     (dict(), dict(q=FAKE + 8), -5), (dict(idx=FAKE + 2), dict(idx=None), -5),
+    (dict(), dict(idx_shared=1), -6),   # a shared index row: the separate calls only
 ])
 def test_select_attend_argument_errors(skw, akw, code):
     assert _sel_att(_select_desc(**skw), _attend_desc(**akw)) == code

@@ -164,3 +164,37 @@ def test_primed_chain_equals_separate_calls():
         assert torch.equal(idx2, idx)
         assert torch.equal(out2.view(torch.int16), out.view(torch.int16))
         assert torch.equal(lse2, lse)
+
+
+@pytest.mark.parametrize("mla", [True, False])
+def test_shared_selection_for_draft_tokens(mla):
+    # one index row per sequence for T = 4 draft tokens (reading R29): each token attends
+    # over the entries at or before its own position; equal, bit for bit, to per-token
+    # rows with the later entries padded out, and to the oracle within the attention bound
+    from gpu_harness import check_attn
+    from oracle import lsa_oracle as O
+    rng = np.random.default_rng(900 + mla)
+    B, T, N, K = 2, 4, 5000, 512
+    ctx = np.array([N, N - 37], np.int32)
+    q, k, v, scale = _kv(rng, 1, B, N, 64 if mla else 16, 1, mla, T=T)
+    shared = np.full((B, K), -1, np.int32)
+    for b in range(B):
+        p_last = int(ctx[b]) - 1
+        win = np.arange(p_last - 5, p_last + 1)                      # the last draft positions
+        rest = np.sort(rng.choice(p_last - 5, K - 20 - win.size, replace=False))
+        row = np.concatenate([rest, win])
+        shared[b, :row.size] = row
+    per_tok = np.stack([O.shared_selection_rows(shared[b], int(ctx[b]), T) for b in range(B)]).astype(np.int32)
+    o1, l1 = L.lsa_attend(q, k, v, torch.from_numpy(shared).cuda(), scale, shared=True,
+                          ctx_len=torch.from_numpy(ctx).cuda())
+    o0, l0 = L.lsa_attend(q, k, v, torch.from_numpy(per_tok).cuda(), scale)
+    torch.cuda.synchronize()
+    assert torch.equal(o1.view(torch.int16), o0.view(torch.int16)) and torch.equal(l1, l0)
+    qf = q.float().cpu().numpy().astype(np.float64)
+    kf = k.float().cpu().numpy().astype(np.float64)
+    vf = kf[..., :512] if mla else v.float().cpu().numpy().astype(np.float64)
+    of = o1.float().cpu().numpy()
+    for b in range(B):
+        for t in range(T):
+            want, _ = O.attend(qf[0, b, t], kf[0, b], vf[0, b], per_tok[b, t], scale)
+            check_attn(of[0, b, t], want, f"shared b={b} t={t}")

@@ -606,3 +606,18 @@ def test_attention_backward_closed_forms():
     z = O.attend_backward(q, k, v, np.array([1, 4, 9]), 0.5, *O.attend(q, k, v, np.array([1, 4, 9]), 0.5),
                           np.zeros_like(dout))
     assert all(not a.any() for a in z)
+
+
+# ----------------------------------------------------------------------------- shared selection (R29)
+
+def test_shared_selection_rows_worked_example():
+    # context 12, three draft tokens at positions 9, 10, 11 sharing the row (0, 5, 9, 10, 11, -1)
+    rows = O.shared_selection_rows([0, 5, 9, 10, 11, -1], 12, 3)
+    assert rows.tolist() == [[0, 5, 9, -1, -1, -1], [0, 5, 9, 10, -1, -1], [0, 5, 9, 10, 11, -1]]
+    # one token: its own position is the last one, nothing is masked
+    assert O.shared_selection_rows([3, 7, -1], 8, 1).tolist() == [[3, 7, -1]]
+    # a token before every entry keeps nothing, and its attention is empty
+    r = O.shared_selection_rows([6, 7], 8, 3)
+    assert r[0].tolist() == [-1, -1]
+    o, lse = O.attend(np.ones((2, 4)), np.ones((8, 1, 4)), np.ones((8, 1, 4)), r[0], 0.5)
+    assert not o.any() and np.all(np.isneginf(lse))
