@@ -47,6 +47,12 @@ Readings where the pages are silent (the pages give no formula at all):
   R29 shared selection for draft tokens (MTP, [P3]): one index row per sequence serves
       its T query tokens; token t uses only the entries at positions <= its own p_t (R11),
       so no token attends to a later position.
+  R30 indexer distillation target (training the indexer, DSA-style, which [P3] says LSA
+      extends): for a query token, the target over its selected positions is the
+      attention distribution averaged over the query heads; the indexer's distribution
+      is the softmax of its scores over the same positions; the loss is KL(target ||
+      indexer) and its gradient with respect to the scores is indexer - target (the
+      target is held fixed).
 """
 from __future__ import annotations
 
@@ -388,6 +394,47 @@ def mla_row_grad(dK, dV):
     d = dK.copy()
     d[..., : dV.shape[-1]] += dV
     return d
+
+
+def indexer_target(q, k_rows, idx, tau, lse):
+    """R30 target of one query token: p[j] = (1/Hq) sum_h exp(tau q_h . K[idx[j], kvh(h)] -
+    lse_h) for valid entries j of idx (0 for padding). q [Hq, d_qk], k_rows [N, Hkv, d_qk],
+    lse [Hq] from the forward. Returns float64 [K]."""
+    idx = np.asarray(idx, dtype=np.int64)
+    Hq, Hkv = q.shape[0], k_rows.shape[1]
+    g = Hq // Hkv
+    p = np.zeros(idx.size)
+    ok = idx >= 0
+    if not ok.any():
+        return p
+    sel = idx[ok]
+    acc = np.zeros(sel.size)
+    for h in range(Hq):
+        z = tau * (k_rows[sel, h // g, :] @ q[h])
+        acc += np.exp(z - lse[h])
+    p[ok] = acc / Hq
+    return p
+
+
+def indexer_kl(target, scores_sel, valid):
+    """R30 loss and gradient of one query token: u = softmax of the indexer scores over
+    the valid entries; loss = sum_j target_j (log target_j - log u_j) over target_j > 0;
+    d loss / d score_j = u_j - target_j (0 at invalid entries). Returns (loss, grad [K])."""
+    target = np.asarray(target, dtype=np.float64)
+    sc = np.asarray(scores_sel, dtype=np.float64)
+    valid = np.asarray(valid, dtype=bool)
+    grad = np.zeros(sc.size)
+    if not valid.any():
+        return 0.0, grad
+    m = np.max(sc[valid])
+    e = np.exp(sc[valid] - m)
+    logu = (sc[valid] - m) - np.log(e.sum())
+    u = np.exp(logu)
+    t = target[valid]
+    pos = t > 0
+    loss = float(np.sum(t[pos] * (np.log(t[pos]) - logu[pos])))
+    grad[valid] = u - t
+    return loss, grad
 
 
 def shared_selection_rows(idx_row, ctx: int, T: int) -> np.ndarray:

@@ -621,3 +621,53 @@ def test_shared_selection_rows_worked_example():
     assert r[0].tolist() == [-1, -1]
     o, lse = O.attend(np.ones((2, 4)), np.ones((8, 1, 4)), np.ones((8, 1, 4)), r[0], 0.5)
     assert not o.any() and np.all(np.isneginf(lse))
+
+
+# ----------------------------------------------------------------------------- indexer distillation target (R30)
+
+def test_indexer_target_is_head_mean_of_attention():
+    # closed forms: the target sums to 1 over the valid entries; with one head it is that
+    # head's softmax; with identical heads the mean is any one of them
+    rng = np.random.default_rng(71)
+    N, K, tau = 30, 9, 0.4
+    k = rng.standard_normal((N, 2, 8))
+    idx = np.full(K, -1)
+    idx[:7] = np.sort(rng.choice(N, 7, replace=False))
+    q = rng.standard_normal((4, 8))
+    _, lse = O.attend(q, k, k, idx, tau)
+    p = O.indexer_target(q, k, idx, tau, lse)
+    assert abs(p.sum() - 1.0) < 1e-12 and np.all(p[7:] == 0)
+    q1 = q[:1]
+    _, lse1 = O.attend(q1, k[:, :1], k[:, :1], idx, tau)
+    z = tau * (k[idx[:7], 0] @ q1[0])
+    soft = np.exp(z - z.max()) / np.exp(z - z.max()).sum()
+    assert np.allclose(O.indexer_target(q1, k[:, :1], idx, tau, lse1)[:7], soft, atol=1e-15)
+    q2 = np.repeat(q[:1], 2, axis=0)
+    _, lse2 = O.attend(q2, k[:, :1], k[:, :1], idx, tau)
+    assert np.allclose(O.indexer_target(q2, k[:, :1], idx, tau, lse2)[:7], soft, atol=1e-15)
+
+
+def test_indexer_kl_zero_minimum_and_finite_differences():
+    rng = np.random.default_rng(72)
+    K = 8
+    valid = np.array([True] * 6 + [False] * 2)
+    t = np.zeros(K)
+    t[:6] = rng.random(6)
+    t[:6] /= t[:6].sum()
+    # scores equal to log target (plus a constant): the indexer matches, loss and gradient 0
+    loss, grad = O.indexer_kl(t, np.concatenate([np.log(t[:6]) + 3.0, [5.0, -2.0]]), valid)
+    assert abs(loss) < 1e-12 and np.allclose(grad, 0, atol=1e-12)
+    # elsewhere the loss is positive and the gradient is the derivative of the loss
+    sc = rng.standard_normal(K)
+    loss, grad = O.indexer_kl(t, sc, valid)
+    assert loss > 0 and grad[6] == 0 and grad[7] == 0 and abs(grad.sum()) < 1e-12
+    eps = 1e-6
+    for j in range(K):
+        up, dn = sc.copy(), sc.copy()
+        up[j] += eps
+        dn[j] -= eps
+        fd = (O.indexer_kl(t, up, valid)[0] - O.indexer_kl(t, dn, valid)[0]) / (2 * eps)
+        assert abs(fd - grad[j]) < 1e-8, j
+    # two entries by hand: target (1, 0), scores (0, 0): loss log 2, gradient (-1/2, 1/2)
+    loss, grad = O.indexer_kl([1.0, 0.0], [0.0, 0.0], [True, True])
+    assert abs(loss - np.log(2.0)) < 1e-15 and np.allclose(grad, [-0.5, 0.5])
