@@ -54,7 +54,7 @@ def parse():
     return ap.parse_args()
 
 
-def backward_inputs(B, N, K, Hq, seed=11):
+def backward_inputs(B, N, K, Hq, seed=11, with_target=False):
     """Device inputs of one lsa_attend_backward call on an MLA decode shape (one query token
     per sequence; forward output and lse from lsa_attend); returns the call."""
     import torch
@@ -68,6 +68,9 @@ def backward_inputs(B, N, K, Hq, seed=11):
     dout = torch.randn((B, 1, Hq, 512), device="cuda", generator=g).to(torch.bfloat16)
     dq = torch.empty((B, 1, Hq, 576), dtype=torch.float32, device="cuda")
     dk = torch.empty((B, N, 1, 576), dtype=torch.float32, device="cuda")
+    if with_target:  # the indexer distillation target on the same selection
+        sc = torch.randn((B, 1, N), device="cuda", generator=g)
+        return lambda: L.lsa_index_target(q[0], k[0], idx, 576 ** -0.5, lse[0], sc)
     return lambda: L.lsa_attend_backward(q[0], k[0], None, idx, 576 ** -0.5, out[0], lse[0], dout, dq=dq, dk=dk)
 
 
@@ -164,7 +167,7 @@ def measure_workloads(steps=50):
       paged KV: the c2 attention over a fixed selection from the contiguous cache and
       from page pools (pages in random order, block table lookups), us per call.
       backward: lsa_attend_backward on the c2 shape (one query token per sequence), us
-      per call."""
+      per call; and lsa_index_target (the indexer distillation target) on the same shape."""
     import numpy as np
     import torch
     import long_context_sparse_07_amd as L
@@ -358,11 +361,13 @@ def measure_workloads(steps=50):
         B, N, K, Hq = 8, 131072, 2048, 64
         f = backward_inputs(B, N, K, Hq)
         us = graph_us(f, reps=10)
+        us_t = graph_us(backward_inputs(B, N, K, Hq, with_target=True), reps=10)
         rows_flops = B * Hq * K * 2.0 * (3 * 576 + 2 * 512)
         dk_bytes = B * N * 576 * 4
         return {"workload": "backward: c2 shape (B=8, 128K, T=1, MLA 64 heads 576/512, K=2048), dq and the dense "
                             "fp32 latent-row gradient",
-                "us_per_call": us, "rows_gflop": rows_flops / 1e9, "dk_write_gb": dk_bytes / 1e9}
+                "us_per_call": us, "rows_gflop": rows_flops / 1e9, "dk_write_gb": dk_bytes / 1e9,
+                "us_index_target": us_t}
 
     for name, body in (("c1", w1), ("c3", w3), ("c4", w4), ("c5", w5), ("append", w_append), ("paged", w_paged),
                        ("backward", w_bwd)):

@@ -351,6 +351,41 @@ size_t lsa_attend_backward_workspace_bytes(const lsa_attend_bwd_desc *desc);
 int32_t lsa_attend_backward(const lsa_attend_bwd_desc *desc, void *workspace, size_t workspace_bytes, void *stream);
 
 /*
+ * lsa_index_target — the indexer distillation target and loss for training the indexer
+ * (reading R30; the indexer LSA builds on is DSA's, molayo1419.me LongCat-2.0 article,
+ * "The sparse attention problem at 1M tokens"). For query token (b,t) and each valid
+ * entry j of idx[b][t] (position s = idx[b][t][j] in [0, N)):
+ *   target[b][t][j] = (1/Hq) sum_hq exp(softmax_scale q[b][t][hq] . K[b][s][kvh] - lse[b][t][hq])
+ *     (the attention distribution of each head, from lsa_attend's lse, averaged over heads)
+ *   u_j = softmax over the valid entries of scores[b][t][s] (the indexer scores)
+ *   loss[b][t] = sum_j target_j (log target_j - log u_j) over target_j > 0
+ *   grad[b][t][j] = u_j - target_j  (d loss / d scores[b][t][s]; the target held fixed)
+ * Padding entries get target 0 and grad 0; a token with no valid entry gets loss 0.
+ * fp32 arithmetic from the bf16 inputs; sums in a fixed order (reproducible bits).
+ * Layouts: q bf16 [B][T][Hq][d_qk]; k as in lsa_attend (d_qk = 576 for MLA latent rows, or
+ * 128); idx int32 [B][T][K]; lse fp32 [B][T][Hq]; scores fp32 [B][T][n_cols] (flat
+ * indexer scores, column = position, n_cols >= N); target, grad fp32 [B][T][K]; loss fp32
+ * [B][T]. No workspace. Supported: d_qk in {128, 576}, Hq % Hkv == 0, Hq / Hkv <= 64,
+ * B * T <= 65535, strides multiples of 8 elements, q and k 16-byte aligned.
+ */
+typedef struct lsa_index_target_desc {
+    int32_t B, T, N;
+    int32_t Hq, Hkv, d_qk;
+    const void *q;
+    const void *k;
+    int64_t k_stride_b, k_stride_n, k_stride_h;
+    const int32_t *idx;
+    int32_t K;
+    float softmax_scale;
+    const float *lse;
+    const float *scores;
+    int32_t n_cols;
+    float *target, *grad, *loss;
+} lsa_index_target_desc;
+
+int32_t lsa_index_target(const lsa_index_target_desc *desc, void *stream);
+
+/*
  * lsa_cache_append — the write side of a decode step: T new tokens per sequence enter the
  * caches that lsa_index and lsa_attend read. SI's local window ends at the current token
  * (reading R4), so a step's rows are appended before the step; HI's coarse pass reads one

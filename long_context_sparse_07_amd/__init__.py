@@ -17,7 +17,7 @@ __all__ = ["lib", "LSAError", "lsa_index", "lsa_block_means", "lsa_select", "lsa
            "lsa_workspace_clear", "lsa_select_workspace_bytes", "lsa_attend_workspace_bytes",
            "LSA_BF16", "LSA_FP8_E4M3FN", "LSA_F32", "LSA_INDEX_TOKENS", "LSA_INDEX_BLOCKS",
            "LSA_WS_UNKNOWN", "LSA_WS_CLEAN", "LSA_WS_PRIMED", "lsa_select_attend", "lsa_index_select_attend",
-           "lsa_cache_append", "lsa_attend_backward", "IndexDesc", "BlockMeansDesc", "SelectDesc", "AttendDesc",
+           "lsa_cache_append", "lsa_attend_backward", "lsa_index_target", "IndexTargetDesc", "IndexDesc", "BlockMeansDesc", "SelectDesc", "AttendDesc",
            "AttendBwdDesc", "CacheAppendDesc", "STATUS"]
 
 HERE = os.path.dirname(os.path.abspath(__file__))
@@ -82,6 +82,15 @@ class AttendBwdDesc(ctypes.Structure):
                 ("lse", c_void_p), ("dout", c_void_p), ("dq", c_void_p), ("dk", c_void_p), ("dv", c_void_p)]
 
 
+class IndexTargetDesc(ctypes.Structure):
+    _fields_ = [("B", c_int32), ("T", c_int32), ("N", c_int32), ("Hq", c_int32), ("Hkv", c_int32),
+                ("d_qk", c_int32), ("q", c_void_p), ("k", c_void_p),
+                ("k_stride_b", c_int64), ("k_stride_n", c_int64), ("k_stride_h", c_int64),
+                ("idx", c_void_p), ("K", c_int32), ("softmax_scale", c_float), ("lse", c_void_p),
+                ("scores", c_void_p), ("n_cols", c_int32), ("target", c_void_p), ("grad", c_void_p),
+                ("loss", c_void_p)]
+
+
 class LSAError(RuntimeError):
     def __init__(self, fn: str, status: int, msg: str):
         super().__init__(f"{fn} -> {STATUS.get(status, status)}: {msg}")
@@ -99,7 +108,7 @@ def lib():
             raise RuntimeError(f"{LIB_PATH} is missing: build it with `python -m long_context_sparse_07_amd.build`")
         L = ctypes.CDLL(LIB_PATH)
         for name, desc in (("lsa_index", IndexDesc), ("lsa_block_means", BlockMeansDesc),
-                           ("lsa_cache_append", CacheAppendDesc)):
+                           ("lsa_cache_append", CacheAppendDesc), ("lsa_index_target", IndexTargetDesc)):
             getattr(L, name).argtypes = [POINTER(desc), c_void_p]
             getattr(L, name).restype = c_int32
         L.lsa_select.argtypes = [POINTER(SelectDesc), c_void_p, c_size_t, c_void_p]
@@ -436,6 +445,27 @@ def lsa_attend_backward(q, k, v, idx, softmax_scale, out, lse, dout, *, dq=None,
     _check("lsa_attend_backward", lib().lsa_attend_backward(ctypes.byref(d), _ptr(ws), 0 if ws is None else ws.numel(),
                                                             _stream(stream)))
     return dq, dk, (None if mla else dv)
+
+
+def lsa_index_target(q, k, idx, softmax_scale, lse, scores, *, target=None, grad=None, loss=None, stream=None):
+    """Indexer distillation target (one layer's attention). q bf16 [B,T,Hq,d_qk]; k bf16
+    [B,N,Hkv,d_qk] (MLA latent rows: d_qk 576); idx int32 [B,T,K]; lse fp32 [B,T,Hq] from
+    lsa_attend; scores fp32 [B,T,n_cols] (flat indexer scores). Returns (target [B,T,K],
+    grad [B,T,K], loss [B,T]), fp32."""
+    import torch
+    B, T, Hq, dqk = q.shape
+    N, Hkv = k.shape[1], k.shape[2]
+    K = idx.shape[-1]
+    dev = q.device
+    target = torch.empty((B, T, K), dtype=torch.float32, device=dev) if target is None else target
+    grad = torch.empty((B, T, K), dtype=torch.float32, device=dev) if grad is None else grad
+    loss = torch.empty((B, T), dtype=torch.float32, device=dev) if loss is None else loss
+    d = IndexTargetDesc(B=B, T=T, N=N, Hq=Hq, Hkv=Hkv, d_qk=dqk, q=_ptr(q), k=_ptr(k), k_stride_b=k.stride(0),
+                        k_stride_n=k.stride(1), k_stride_h=k.stride(2), idx=_ptr(idx), K=K,
+                        softmax_scale=softmax_scale, lse=_ptr(lse), scores=_ptr(scores), n_cols=scores.shape[-1],
+                        target=_ptr(target), grad=_ptr(grad), loss=_ptr(loss))
+    _check("lsa_index_target", lib().lsa_index_target(ctypes.byref(d), _stream(stream)))
+    return target, grad, loss
 
 
 def lsa_cache_append(k_new, k_cache, *, k_scale=None, rows=(), pos0=None, kbar=None, block_size=0, stream=None):

@@ -474,6 +474,50 @@ int32_t lsa_attend_backward(const lsa_attend_bwd_desc *d, void *ws, size_t ws_by
     return hip_status(lsa::launch_attend_bwd(a, ws, reinterpret_cast<hipStream_t>(stream)), "lsa_attend_backward");
 }
 
+// ----------------------------------------------------------------------------- indexer target
+
+int32_t lsa_index_target(const lsa_index_target_desc *d, void *stream) {
+    if (!d) return fail(LSA_E_NULL, "lsa_index_target: desc is NULL");
+    if (!d->q || !d->k || !d->idx || !d->lse || !d->scores || !d->target || !d->grad || !d->loss)
+        return fail(LSA_E_NULL, "lsa_index_target: q, k, idx, lse, scores, target, grad, loss are required");
+    if (d->B < 1 || d->T < 1 || d->N < 1 || d->Hq < 1 || d->Hkv < 1)
+        return fail(LSA_E_SHAPE, "lsa_index_target: B, T, N, Hq, Hkv must be >= 1");
+    if (d->K < 1) return fail(LSA_E_BUDGET, "lsa_index_target: K must be >= 1");
+    if (d->Hq % d->Hkv) return fail(LSA_E_SHAPE, "lsa_index_target: Hq=%d not a multiple of Hkv=%d", d->Hq, d->Hkv);
+    if (d->n_cols < d->N) return fail(LSA_E_SHAPE, "lsa_index_target: n_cols=%d below N=%d", d->n_cols, d->N);
+    if (d->d_qk != 128 && d->d_qk != 576) return fail(LSA_E_UNSUPPORTED, "lsa_index_target: no kernel for d_qk=%d", d->d_qk);
+    if (d->Hq / d->Hkv > 64) return fail(LSA_E_UNSUPPORTED, "lsa_index_target: more than 64 query heads per KV head");
+    if ((int64_t)d->B * d->T > kMaxGridY) return fail(LSA_E_UNSUPPORTED, "lsa_index_target: grid too large");
+    const int64_t strides[] = {d->k_stride_b, d->k_stride_n, d->k_stride_h};
+    for (int64_t st : strides)
+        if (st < 0 || st % 8) return fail(LSA_E_ALIGN, "lsa_index_target: strides must be non-negative multiples of 8 elements");
+    if (!aligned16(d->q) || !aligned16(d->k) || !aligned4(d->lse) || !aligned4(d->scores) || !aligned4(d->target) ||
+        !aligned4(d->grad) || !aligned4(d->loss))
+        return fail(LSA_E_ALIGN, "lsa_index_target: q, k must be 16-byte aligned, fp32 arrays 4-byte");
+    lsa::IndexTargetArgs a{};
+    a.B = d->B;
+    a.T = d->T;
+    a.N = d->N;
+    a.Hq = d->Hq;
+    a.Hkv = d->Hkv;
+    a.K = d->K;
+    a.dqk = d->d_qk;
+    a.q = reinterpret_cast<const uint16_t *>(d->q);
+    a.k = reinterpret_cast<const uint16_t *>(d->k);
+    a.ksb = d->k_stride_b;
+    a.ksn = d->k_stride_n;
+    a.ksh = d->k_stride_h;
+    a.idx = d->idx;
+    a.scale = d->softmax_scale;
+    a.lse = d->lse;
+    a.scores = d->scores;
+    a.n_cols = d->n_cols;
+    a.target = d->target;
+    a.grad = d->grad;
+    a.loss = d->loss;
+    return hip_status(lsa::launch_index_target(a, reinterpret_cast<hipStream_t>(stream)), "lsa_index_target");
+}
+
 int32_t lsa_cache_append(const lsa_cache_append_desc *d, void *stream) {
     if (!d) return fail(LSA_E_NULL, "lsa_cache_append: desc is NULL");
     if (!d->k_new || !d->k_cache) return fail(LSA_E_NULL, "lsa_cache_append: k_new and k_cache are required");

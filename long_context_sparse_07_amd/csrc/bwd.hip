@@ -381,6 +381,119 @@ __global__ __launch_bounds__(kBT) void bwd_kv_kernel(AttendBwdArgs a, const floa
     }
 }
 
+// ---- indexer distillation target
+// target_tile_kernel (one workgroup per query token and 32 selected rows): for each KV head
+// in turn, the rows are gathered into LDS and q . K of every head of the group comes from
+// the matrix cores; each row's thread adds exp(scale z - lse) over the heads (KV heads in
+// order), then divides by Hq.
+template <int DQK>
+__global__ __launch_bounds__(kBT) void target_tile_kernel(IndexTargetArgs a) {
+    __shared__ __attribute__((aligned(16))) uint16_t kt[kRT][DQK];
+    __shared__ float Zs[kMaxG][kRT];
+    __shared__ int rowpos[kRT];
+    const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, l32 = lane & 31, half = lane >> 5;
+    const int tile = blockIdx.x, bt = blockIdx.y;
+    const int b = bt / a.T;
+    const int g = a.Hq / a.Hkv;
+    const int r0 = tile * kRT;
+    const int nrows = min(kRT, a.K - r0);
+    if (tid < kRT) {
+        const int s = tid < nrows ? a.idx[(int64_t)bt * a.K + r0 + tid] : -1;
+        rowpos[tid] = (s >= 0 && s < a.N) ? s : -1;
+    }
+    float tgt = 0.0f;  // thread r < kRT: row r's sum over heads
+    for (int kvh = 0; kvh < a.Hkv; ++kvh) {
+        __syncthreads();  // rowpos written; the previous head's kt and Zs no longer read
+        const uint16_t *kb = a.k + b * a.ksb + kvh * a.ksh;
+        for (int i = tid; i < kRT * DQK / 8; i += kBT) {
+            const int r = i / (DQK / 8), c = i % (DQK / 8);
+            const int s = rowpos[r];
+            u32x4 v = {0, 0, 0, 0};
+            if (s >= 0) v = *reinterpret_cast<const u32x4 *>(kb + (int64_t)s * a.ksn + 8 * c);
+            *reinterpret_cast<u32x4 *>(&kt[r][8 * c]) = v;
+        }
+        __syncthreads();
+        const int64_t qh0 = (int64_t)bt * a.Hq + kvh * g;
+        if (wave < (g + 31) / 32) {  // z^T block: 32 rows x 32 heads
+            const int head = 32 * wave + l32;
+            const bool hok = head < g;
+            const uint16_t *qp = a.q + (qh0 + (hok ? head : 0)) * DQK + 8 * half;
+            f32x16 acc;
+#pragma unroll
+            for (int r = 0; r < 16; ++r) acc[r] = 0.0f;
+#pragma unroll 4
+            for (int st = 0; st < DQK / 16; ++st) {
+                u32x4 bv = {0, 0, 0, 0};
+                if (hok) bv = *reinterpret_cast<const u32x4 *>(qp + 16 * st);
+                const u32x4 av = *reinterpret_cast<const u32x4 *>(&kt[l32][16 * st + 8 * half]);
+                acc = mfma32(__builtin_bit_cast(bf16x8, av), __builtin_bit_cast(bf16x8, bv), acc);
+            }
+            if (hok) {
+#pragma unroll
+                for (int r = 0; r < 16; ++r) Zs[head][8 * (r / 4) + 4 * half + (r % 4)] = acc[r];
+            }
+        }
+        __syncthreads();
+        if (tid < kRT && rowpos[tid] >= 0) {
+            for (int hh = 0; hh < g; ++hh) {
+                const float lse = a.lse[qh0 + hh];
+                if (lse > kNegInf) tgt += expf(a.scale * Zs[hh][tid] - lse);
+            }
+        }
+    }
+    if (tid < nrows) a.target[(int64_t)bt * a.K + r0 + tid] = rowpos[tid] >= 0 ? tgt / (float)a.Hq : 0.0f;
+}
+
+// fixed-order sum or maximum over the workgroup (kBT threads)
+template <bool MAX>
+__device__ float block_reduce(float v, float *scr) {
+    const int tid = threadIdx.x;
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) {
+        const float w = __shfl_xor(v, o, 64);
+        v = MAX ? fmaxf(v, w) : v + w;
+    }
+    __syncthreads();  // scr free
+    if ((tid & 63) == 0) scr[tid >> 6] = v;
+    __syncthreads();
+    float r = scr[0];
+    for (int i = 1; i < kBT / 64; ++i) r = MAX ? fmaxf(r, scr[i]) : r + scr[i];
+    return r;
+}
+
+// kl_kernel (one workgroup per query token): u = softmax of the indexer scores over the
+// valid entries, loss = sum target (log target - log u), grad = u - target
+__global__ __launch_bounds__(kBT) void kl_kernel(IndexTargetArgs a) {
+    __shared__ float scr[kBT / 64];
+    const int tid = threadIdx.x, bt = blockIdx.x;
+    const int32_t *row = a.idx + (int64_t)bt * a.K;
+    const float *sc = a.scores + (int64_t)bt * a.n_cols;
+    const float *tg = a.target + (int64_t)bt * a.K;
+    float m = kNegInf;
+    for (int j = tid; j < a.K; j += kBT) {
+        const int s = row[j];
+        if (s >= 0 && s < a.N) m = fmaxf(m, sc[s]);
+    }
+    m = block_reduce<true>(m, scr);
+    float se = 0.0f;
+    for (int j = tid; j < a.K; j += kBT) {
+        const int s = row[j];
+        if (s >= 0 && s < a.N) se += expf(sc[s] - m);
+    }
+    se = block_reduce<false>(se, scr);
+    const float lz = m + logf(se);  // log of the softmax denominator
+    float loss = 0.0f;
+    for (int j = tid; j < a.K; j += kBT) {
+        const int s = row[j];
+        const bool ok = s >= 0 && s < a.N && m > kNegInf;
+        const float lu = ok ? sc[s] - lz : 0.0f, t = tg[j];
+        if (ok && t > 0.0f) loss += t * (logf(t) - lu);
+        a.grad[(int64_t)bt * a.K + j] = ok ? expf(lu) - t : 0.0f;
+    }
+    loss = block_reduce<false>(loss, scr);
+    if (tid == 0) a.loss[bt] = loss;
+}
+
 struct BwdLayout {
     size_t g_off, g_bytes, dq_off, dq_bytes, total;
     int ntiles;
@@ -416,6 +529,16 @@ hipError_t launch_bwd_t(const AttendBwdArgs &a, void *ws, hipStream_t s) {
 }  // namespace
 
 size_t attend_bwd_workspace_bytes(const AttendBwdArgs &a) { return bwd_layout(a).total; }
+
+hipError_t launch_index_target(const IndexTargetArgs &a, hipStream_t s) {
+    const dim3 grid((a.K + kRT - 1) / kRT, a.B * a.T);
+    if (a.dqk == 576) hipLaunchKernelGGL(target_tile_kernel<576>, grid, dim3(kBT), 0, s, a);
+    else hipLaunchKernelGGL(target_tile_kernel<128>, grid, dim3(kBT), 0, s, a);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL(kl_kernel, dim3(a.B * a.T), dim3(kBT), 0, s, a);
+    return hipGetLastError();
+}
 
 hipError_t launch_attend_bwd(const AttendBwdArgs &a, void *ws, hipStream_t s) {
     return a.mla ? launch_bwd_t<576, 512, true>(a, ws, s) : launch_bwd_t<128, 128, false>(a, ws, s);

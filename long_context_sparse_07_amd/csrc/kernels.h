@@ -90,6 +90,24 @@ struct AttendBwdArgs {
     bool mla;
 };
 size_t attend_bwd_workspace_bytes(const AttendBwdArgs &a);
+
+// Indexer distillation target: per query token, the head-averaged attention distribution
+// over its selected rows, the indexer's softmax over the same rows, their KL and its
+// gradient with respect to the indexer scores.
+struct IndexTargetArgs {
+    int B, T, N, Hq, Hkv, K, dqk;
+    const uint16_t *q;      // bf16 [B][T][Hq][dqk]
+    const uint16_t *k;      // bf16, element (b, s, h, d) at b*ksb + s*ksn + h*ksh + d
+    int64_t ksb, ksn, ksh;
+    const int32_t *idx;     // [B][T][K]
+    float scale;
+    const float *lse;       // [B][T][Hq]
+    const float *scores;    // [B][T][n_cols], column = position
+    int n_cols;
+    float *target, *grad;   // [B][T][K]
+    float *loss;            // [B][T]
+};
+hipError_t launch_index_target(const IndexTargetArgs &a, hipStream_t s);
 hipError_t launch_attend_bwd(const AttendBwdArgs &a, void *ws, hipStream_t s);
 
 struct SelectArgs {

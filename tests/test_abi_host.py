@@ -35,7 +35,7 @@ def test_library_exports_every_declared_function():
 def test_descriptor_layout_matches_c(tmp_path):
     structs = {"lsa_index_desc": L.IndexDesc, "lsa_block_means_desc": L.BlockMeansDesc,
                "lsa_select_desc": L.SelectDesc, "lsa_attend_desc": L.AttendDesc,
-               "lsa_attend_bwd_desc": L.AttendBwdDesc,
+               "lsa_attend_bwd_desc": L.AttendBwdDesc, "lsa_index_target_desc": L.IndexTargetDesc,
                "lsa_cache_append_desc": L.CacheAppendDesc}
     lines = ['#include <stdio.h>', '#include <stddef.h>', f'#include "{HEADER}"', "int main(void){"]
     for cname, py in structs.items():
@@ -303,3 +303,20 @@ def test_attend_backward_workspace_rules():
     assert _bwd(d, None, need) == -7
     assert _bwd(d, FAKE + 16, need) == -5
     assert L.lib().lsa_attend_backward_workspace_bytes(ctypes.byref(_bwd_desc(K=0))) == 0
+
+
+def _tgt_desc(**kw):
+    base = dict(B=2, T=1, N=1024, Hq=64, Hkv=1, d_qk=576, q=FAKE, k=FAKE, k_stride_b=1024 * 576, k_stride_n=576,
+                k_stride_h=576, idx=FAKE, K=256, softmax_scale=0.04, lse=FAKE, scores=FAKE, n_cols=1024,
+                target=FAKE, grad=FAKE, loss=FAKE)
+    base.update(kw)
+    return L.IndexTargetDesc(**base)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(q=None), -1), (dict(scores=None), -1), (dict(loss=None), -1), (dict(K=0), -4), (dict(B=0), -2),
+    (dict(Hq=63, Hkv=2), -2), (dict(n_cols=1000), -2), (dict(d_qk=64), -6), (dict(Hq=128), -6),
+    (dict(T=40000), -6), (dict(k_stride_n=577), -5), (dict(q=FAKE + 8), -5), (dict(grad=FAKE + 2), -5),
+])
+def test_index_target_argument_errors(kw, code):
+    assert L.lib().lsa_index_target(ctypes.byref(_tgt_desc(**kw)), None) == code
