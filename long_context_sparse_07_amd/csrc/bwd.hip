@@ -13,9 +13,12 @@
 //   rows' gradient contributions of this query (G: scale sum_h dS q_h, and sum_h P dO_h)
 //   and this tile's part of dq.
 // bwd_dq_kernel: dq = the tiles' parts, added in tile order.
-// bwd_kv_kernel (one workgroup per tile of 32 cache positions and KV head): the
+// bwd_kv_kernel (one workgroup per tile of 16 cache positions and KV head): the
 //   contributions G of every query that selected one of the positions, added in ascending
 //   query order; every position of the cache is written (zero where nothing selected it).
+// target_tile_kernel, kl_kernel: the indexer distillation target (head-averaged attention
+//   over the selected rows), its KL against the indexer's softmax, and the KL's gradient
+//   with respect to the indexer scores.
 #include "common.cuh"
 #include "kernels.h"
 
@@ -24,7 +27,7 @@ namespace {
 
 constexpr int kBT = 256;  // threads per workgroup
 constexpr int kRT = 32;   // selected rows per bwd_rows workgroup
-constexpr int kPT = 16;   // cache positions per bwd_kv workgroup (LDS: 16 x 576 fp32, four workgroups a CU)
+constexpr int kPT = 16;   // cache positions per bwd_kv workgroup (LDS: 16 x 576 fp32)
 constexpr int kMaxG = 64; // query heads per KV head
 
 __device__ __forceinline__ float dot8(u32x4 x, u32x4 y) {
