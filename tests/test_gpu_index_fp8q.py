@@ -14,7 +14,8 @@ candidates within that tolerance of the m-th score.
 Cases: 64 heads (two row blocks, one query per workgroup), the prefill kernel (64
 queries, four query groups sharing each key tile), 32 heads, 16/8/4 heads (several
 queries per row block), the HI fine stage through a kept map, per-sequence context
-lengths, and the primed index -> select chain.
+lengths, the primed index -> select chain, and the full 128K decode and 4096-token
+prefill workloads (sampled rows for the prefill).
 """
 import numpy as np
 import pytest
@@ -122,3 +123,35 @@ def test_fp8_query_hi_fine_stage():
         tol = np.zeros(cols.size)
         tol[ok] = _score_tol(inp["qI"][0, t], inp["w"][0, t], inp["kI_scale"][0][pos[ok]])
         _check_row(g[0, t], want, tol, f"hi t={t}")
+
+
+@pytest.mark.parametrize("cid", [2, 4])
+def test_fp8_query_full_size_sampled(cid):
+    # the 128K decode (8 sequences, every row) and the 4096-token prefill after 256K keys
+    # (sampled rows) at their full sizes, in the launch configuration the benchmark times
+    cfg = config(cid, q_fp8=True)
+    inp = make_inputs(cfg, with_kv=False)
+    d = upload(inp)
+    sc, idx = L.lsa_index_select(d["qI"], d["w"], d["kI"], cfg.K, cfg.S, cfg.W, k_scale=d["kI_scale"],
+                                 ctx_len=d["ctx_len"], q_fp8=True)
+    torch.cuda.synchronize()
+    if cid == 4:
+        rng = np.random.default_rng(4040)
+        rows = [(0, t) for t in sorted({0, 63, 64, 4095, *rng.integers(0, cfg.T, size=5).tolist()})]
+    else:
+        rows = [(b, 0) for b in range(cfg.B)]
+    ora = O.reference_step(inp, rows=rows, with_attend=False)
+    P = O.query_positions(inp["ctx_len"], cfg.T)
+    for b, t in rows:
+        p = int(P[b, t])
+        g = sc[b, t, : p + 1].cpu().numpy()
+        want = ora["scores"][(b, t)]
+        tol = _score_tol(inp["qI"][b, t], inp["w"][b, t], inp["kI_scale"][b][: p + 1])
+        err = _check_row(g, want, tol, f"c{cid} {b},{t}")
+        F = O.forced_positions(p, cfg.S, cfg.W)
+        C = np.setdiff1d(np.arange(p + 1), F)
+        m = cfg.K - F.size
+        tau = np.sort(want[C])[::-1][min(m, C.size) - 1]
+        rtol = 2.0 * float(np.max(tol[C])) / max(abs(tau), 1e-30) + 1e-4
+        check_band(idx[b, t].cpu().numpy(), C, want[C], F, cfg.K, rtol=rtol, what=f"c{cid} {b},{t}")
+        print(f"c{cid} {b},{t}: score error {err:.2e} of the row maximum")
