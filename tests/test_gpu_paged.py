@@ -8,7 +8,7 @@ the same arithmetic. Unmapped pages (entry -1 or past the pool) and positions at
 N are skipped like padding. One case also checks the paged path against the oracle's
 float64 attention directly. Cases: MLA (64 heads) and GQA (4 KV heads, two layers),
 page sizes 1, 16 and 64, one split and many, the fused select+attend and
-index+select+attend chains.
+index+select+attend chains, and the full 128K MLA decode shape (8 sequences, 2048 rows).
 """
 import numpy as np
 import pytest
@@ -164,3 +164,22 @@ def test_paged_primed_chain():
     torch.cuda.synchronize()
     assert torch.equal(got[0], ref[0]) and torch.equal(got[1], ref[1])
     _same(got[2], got[3], ref[2], ref[3])
+
+
+def test_paged_full_size_mla_decode():
+    # the 128K MLA decode shape the benchmark times: 8 sequences, 2048 selected rows each,
+    # 64-row pages in random pool order (the pool built on the device)
+    g = torch.Generator(device="cuda").manual_seed(990)
+    B, N, K, Hq, ps = 8, 131072, 2048, 64, 64
+    q = (torch.randn((1, B, 1, Hq, 576), device="cuda", generator=g) * 576 ** -0.5).to(torch.bfloat16)
+    k = torch.randn((1, B, N, 1, 576), device="cuda", generator=g).to(torch.bfloat16)
+    idx = torch.rand((B, N), device="cuda", generator=g).topk(K, dim=1).indices.sort(dim=1).values
+    idx = idx.to(torch.int32).view(B, 1, K).contiguous()
+    mp = N // ps
+    bt = torch.randperm(B * mp, device="cuda", generator=g).to(torch.int32).view(B, mp)
+    pool = torch.empty((1, B * mp, ps, 1, 576), dtype=torch.bfloat16, device="cuda")
+    pool[0, bt.flatten().long()] = k[0].reshape(B * mp, ps, 1, 576)
+    o0, l0 = L.lsa_attend(q, k, None, idx, 576 ** -0.5)
+    o1, l1 = L.lsa_attend(q, pool, None, idx, 576 ** -0.5, block_table=bt, N=N)
+    torch.cuda.synchronize()
+    _same(o1, l1, o0, l0)
