@@ -158,3 +158,46 @@ def test_token_by_token_equals_bulk():
     assert torch.equal(bulk[1], step[1])
     assert torch.equal(bulk[2].view(torch.int16), step[2].view(torch.int16))
     assert torch.equal(bulk[3], step[3])
+
+
+def test_append_full_size_cache_shapes():
+    # the two cache shapes the benchmark times: 8 sequences of 131072 rows (fp8 key of 128
+    # plus a 576-wide MLA row, one token each) and one sequence of 1M rows (bf16 key of 64,
+    # a 128-wide row, four tokens completing a block of 64 with its summary)
+    rng = np.random.default_rng(45)
+    # 128K fp8
+    B, N, D = 8, 131072, 128
+    k_new, k32 = _bf16_keys(rng, (B, 1, D))
+    row_new = _rows(rng, (B, 1, 576))
+    pos0 = rng.integers(0, N, B).astype(np.int32)
+    g_k = torch.zeros((B, N, D), dtype=torch.uint8, device="cuda").view(torch.float8_e4m3fn)
+    g_s = torch.zeros((B, N), dtype=torch.float32, device="cuda")
+    g_r = torch.zeros((B, N, 576), dtype=torch.bfloat16, device="cuda")
+    L.lsa_cache_append(k_new.cuda(), g_k, k_scale=g_s, rows=[(row_new.cuda(), g_r)],
+                       pos0=torch.from_numpy(pos0).cuda())
+    torch.cuda.synchronize()
+    codes, scale = O.quantize_key_rows(k32[:, 0])
+    kb = g_k.view(torch.uint8)
+    for b in range(B):
+        s = int(pos0[b])
+        assert np.array_equal(kb[b, s].cpu().numpy(), codes[b]) and g_s[b, s].item() == scale[b]
+        assert torch.equal(g_r[b, s].view(torch.int16).cpu(), row_new[b, 0].view(torch.int16))
+    assert int((kb != 0).any(dim=-1).sum()) <= B and int((g_s != 0).sum()) == B
+    del g_k, g_s, g_r
+    # 1M bf16 with a block summary
+    N, D, T, Bs = 1 << 20, 64, 4, 64
+    k_new, _ = _bf16_keys(rng, (1, T, D))
+    row_new = _rows(rng, (1, T, 128))
+    g_k = torch.from_numpy(rng.standard_normal((1, N, D)).astype(np.float32)).to(torch.bfloat16).cuda()
+    g_r = torch.zeros((1, N, 128), dtype=torch.bfloat16, device="cuda")
+    kbar = torch.full((1, N // Bs, D), -7.0, dtype=torch.float32, device="cuda")
+    p0 = (N // 2 // Bs) * Bs + Bs - T  # the four tokens complete one block
+    L.lsa_cache_append(k_new.cuda(), g_k, rows=[(row_new.cuda(), g_r)],
+                       pos0=torch.tensor([p0], dtype=torch.int32, device="cuda"), kbar=kbar, block_size=Bs)
+    torch.cuda.synchronize()
+    assert torch.equal(g_k[0, p0:p0 + T].view(torch.int16).cpu(), k_new[0].view(torch.int16))
+    j = (p0 + T - 1) // Bs
+    bits = g_k[0, j * Bs:(j + 1) * Bs].view(torch.int16).cpu().numpy().view(np.uint16)
+    want = O.block_means(O.index_keys_f64(bits, None), Bs, 1)[0]
+    assert np.allclose(kbar[0, j].cpu().numpy(), want, rtol=1e-5, atol=1e-6)
+    assert int((kbar != -7.0).any(dim=-1).sum()) == 1  # only the completed block
