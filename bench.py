@@ -230,6 +230,19 @@ def measure_workloads(steps=50):
             L.lsa_attend(d["q"], d["k"], d["v"], idx, cfg.tau, out=out, lse=lse)
         return fn
 
+    def fused_step(cfg, d, sc, idx, out, lse):
+        # the chained calls: lsa_index (priming the selection), then lsa_select_attend
+        def fn():
+            L.lsa_index_select_attend(d["qI"], d["w"], d["kI"], cfg.K, cfg.S, cfg.W, d["q"], d["k"], d["v"], cfg.tau,
+                                      k_scale=d["ks"], ctx_len=d["ctx"], scores=sc, idx=idx, out=out, lse=lse)
+        return fn
+
+    def both(cfg, d, sc, idx, out, lse, reps):
+        """Step time of the separate and the chained calls; the step is the faster one."""
+        us_sep = graph_us(flat_step(cfg, d, sc, idx, out, lse), reps=reps)
+        us_ch = graph_us(fused_step(cfg, d, sc, idx, out, lse), reps=reps)
+        return min(us_sep, us_ch), {"us_per_step_separate": us_sep, "us_per_step_chained": us_ch}
+
     def c_flat(cid):
         cfg = config(cid)
         d = upload(make_inputs(cfg), cfg)
@@ -242,12 +255,13 @@ def measure_workloads(steps=50):
 
     def w1():
         cfg, d, sc, idx, out, lse = c_flat(1)
+        us, ways = both(cfg, d, sc, idx, out, lse, 20)
         return {"workload": "c1 tiny decode (B=1, N=4096, T=8, 4x64 bf16 indexer, 16 heads MQA d=128, K=512)",
-                "us_per_step": graph_us(flat_step(cfg, d, sc, idx, out, lse), reps=20)}
+                "us_per_step": us, **ways}
 
     def w4():
         cfg, d, sc, idx, out, lse = c_flat(4)
-        us = graph_us(flat_step(cfg, d, sc, idx, out, lse))
+        us, ways = both(cfg, d, sc, idx, out, lse, 1)
         us_index = graph_us(lambda: L.lsa_index(d["qI"], d["w"], d["kI"], k_scale=d["ks"], ctx_len=d["ctx"], scores=sc))
         p0 = cfg.N - cfg.T
         pairs = sum(p0 + t + 1 for t in range(cfg.T))
@@ -256,7 +270,7 @@ def measure_workloads(steps=50):
         us_index_q8 = graph_us(lambda: L.lsa_index(d["qI"], d["w"], d["kI"], k_scale=d["ks"], ctx_len=d["ctx"],
                                                    scores=sc, q_fp8=True))
         return {"workload": "c4 chunked prefill (4096 queries after 256K, 64x128 fp8 indexer, GQA 64/8 d=128, K=2048)",
-                "us_per_step": us, "prefill_tokens_per_s": cfg.B * cfg.T / (us * 1e-6), "us_index": us_index,
+                "us_per_step": us, **ways, "prefill_tokens_per_s": cfg.B * cfg.T / (us * 1e-6), "us_index": us_index,
                 "index_tflops": flops / (us_index * 1e-6) / 1e12,
                 "index_mfma_frac_of_bf16_peak": flops / (us_index * 1e-6) / 2.5e15,
                 "us_index_fp8_query": us_index_q8, "index_fp8_query_tflops": flops / (us_index_q8 * 1e-6) / 1e12,
@@ -264,7 +278,7 @@ def measure_workloads(steps=50):
 
     def w5():
         cfg, d, sc, idx, out, lse = c_flat(5)
-        us = graph_us(flat_step(cfg, d, sc, idx, out, lse), reps=10)
+        us, ways = both(cfg, d, sc, idx, out, lse, 10)
         out1 = torch.empty((1,) + tuple(out.shape[1:]), dtype=out.dtype, device="cuda")
         lse1 = torch.empty((1,) + tuple(lse.shape[1:]), dtype=lse.dtype, device="cuda")
 
@@ -276,7 +290,7 @@ def measure_workloads(steps=50):
         us_rec = graph_us(recompute, reps=10)
         return {"workload": "c5 cross-layer decode (B=16, N=64K, 4 layers sharing one selection, 32x128 fp8 indexer, "
                             "GQA 32/4 d=128, K=2048)",
-                "us_per_step": us, "us_per_step_selection_per_layer": us_rec, "cli_speedup": us_rec / us}
+                "us_per_step": us, **ways, "us_per_step_selection_per_layer": us_rec, "cli_speedup": us_rec / us}
 
     def w3():
         cfg = config(3)
