@@ -300,11 +300,11 @@ int32_t lsa_attend(const lsa_attend_desc *desc, void *workspace, size_t workspac
  * attend_ws as for lsa_attend, with their own *_workspace_bytes() sizes; after a
  * successful call select_ws is clean, as after lsa_select.
  * Errors as for the two calls; LSA_E_UNSUPPORTED for a kept map.
- * Speed: every attention workgroup that shares a selection row (splits x KV heads x
- * layers) repeats the row-level part of the selection, so the chain pays off only when
- * few workgroups share a row and the grid leaves room for the repeats (one MLA head group,
- * one layer, a batch of single-token decodes); with several KV heads or layers, or many
- * query tokens, the two separate calls are faster (see the workload timings).
+ * Speed: every attention workgroup that shares a selection row repeats the row-level
+ * part of the selection, which pays off only with four waves a workgroup (more than 48
+ * query heads per KV head) and one KV head of one layer per row; for other shapes the
+ * call runs the selection's own resolve kernel and then the plain attention (the same
+ * results, never slower than the two calls).
  */
 int32_t lsa_select_attend(const lsa_select_desc *sel, const lsa_attend_desc *att, void *select_ws,
                           size_t select_ws_bytes, void *attend_ws, size_t attend_ws_bytes, void *stream);

@@ -524,6 +524,8 @@ hipError_t launch_t(const AttendArgs &a, void *ws, hipStream_t s, const FuseArgs
     using G = AttTile<DQK, DV, HW, MLA, OUTF32>;
     const size_t lds = (size_t)G::NST * G::STAGE + (size_t)kMaxR * sizeof(int) + (size_t)(kMaxR / 32) * sizeof(uint32_t);
     if (fuse) {
+        // (the chain runs only with four waves a workgroup: launch_select_attend decides)
+        if constexpr (HW != 4) return hipErrorInvalidValue;
         // the resolve's working set in the tile ring: histograms and scratch, the row
         // bitmap when it fits beside the first tie entries, the rest for ties
         FuseArgs f = *fuse;
@@ -534,7 +536,9 @@ hipError_t launch_t(const AttendArgs &a, void *ws, hipStream_t s, const FuseArgs
         static_assert(ring >= fixed + sel::kSliceTiesFirst * 8, "tile ring too small for the resolve");
         f.bits_lds = ring >= fixed + bb + (size_t)sel::kSliceTiesFirst * 8;
         f.tl = (int)(((ring - fixed - (f.bits_lds ? bb : 0)) / 8) & ~(size_t)1);
-        hipLaunchKernelGGL((attend_kernel<DQK, DV, HW, MLA, OUTF32, true>), grid, dim3(64 * HW), lds, s, a, po, pml, R, f);
+        if constexpr (HW == 4)
+            hipLaunchKernelGGL((attend_kernel<DQK, DV, HW, MLA, OUTF32, true>), grid, dim3(64 * HW), lds, s, a, po, pml,
+                               R, f);
     } else {
         hipLaunchKernelGGL((attend_kernel<DQK, DV, HW, MLA, OUTF32, false>), grid, dim3(64 * HW), lds, s, a, po, pml, R,
                            FuseArgs{});
@@ -597,6 +601,17 @@ hipError_t launch_attend(const AttendArgs &a, void *ws, hipStream_t s) {
 }
 
 hipError_t launch_select_attend(const SelectArgs &sa, void *sel_ws, const AttendArgs &a, void *ws, hipStream_t s) {
+    // Every attention workgroup sharing a selection row repeats the row-level part of the
+    // selection. That is paid back only when four waves resolve together (more than 48
+    // query heads per KV head) and one KV head of one layer reads each row; otherwise the
+    // selection's own resolve kernel and then the plain attention run (same results).
+    if (!(a.Hq / a.Hkv > 48 && a.Hkv * a.L == 1)) {
+        const hipError_t e = launch_select(sa, sel_ws, s);
+        if (e != hipSuccess) return e;
+        AttendArgs a2 = a;
+        a2.idx = sa.idx;
+        return launch_attend(a2, ws, s);
+    }
     const hipError_t e = launch_select_front(sa, sel_ws, s);
     if (e != hipSuccess) return e;
     FuseArgs f{};

@@ -3,6 +3,9 @@ workgroup the part of the index list it attends over) against the two separate c
 lsa_select + lsa_attend on the same inputs: the index list, the attention output and
 the log-sum-exp must be bit-identical. The separate calls are pinned to the oracle
 elsewhere; one case here also checks the fused index list against the oracle directly.
+The chain runs its fused kernel only for more than 48 query heads per KV head in one
+layer (MLA here); for the other shapes the call runs the selection's resolve kernel and
+the plain attention, which these cases check through the same entry point.
 
 Cases: MLA (64 heads, one wave per 16 heads) and GQA / MQA kernels (one wave); several
 layers and KV heads sharing one selection row; one split and many; fp32 output with one
@@ -198,3 +201,14 @@ def test_shared_selection_for_draft_tokens(mla):
         for t in range(T):
             want, _ = O.attend(qf[0, b, t], kf[0, b], vf[0, b], per_tok[b, t], scale)
             check_attn(of[0, b, t], want, f"shared b={b} t={t}")
+
+
+def test_mla_long_row_bitmap_in_workspace():
+    # 600000 columns: the fused kernel's row bitmap (18750 words, laid out for 256
+    # threads) no longer fits beside the tile ring and lives in the selection workspace
+    g = torch.Generator(device="cuda").manual_seed(410)
+    N = 600000
+    sc = torch.randn((1, 1, N), device="cuda", generator=g)
+    q = (torch.randn((1, 1, 1, 64, 576), device="cuda", generator=g) * 576 ** -0.5).to(torch.bfloat16)
+    k = torch.randn((1, 1, N, 1, 576), device="cuda", generator=g).to(torch.bfloat16)
+    _both(sc, 2048, 64, 512, q, k, None, 576 ** -0.5)
