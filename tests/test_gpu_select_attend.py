@@ -122,9 +122,10 @@ def test_many_equal_scores():
         _both(_scores(rows), 2048, 16, 64, q, k, v, scale)
 
 
-def test_tie_list_overflow_rescans_row():
+@pytest.mark.parametrize("mla", [False, True])
+def test_tie_list_overflow_rescans_row(mla):
     # 2048 rows x 16384 columns: the per-row tie list holds 8192 entries; row 7 has
-    # 10000 equal scores in its threshold bin
+    # 10000 equal scores in its threshold bin (MLA: the fused kernel rescans the row)
     rng = np.random.default_rng(600)
     T, N = 2048, 16384
     rows = rng.standard_normal((T, N)).astype(np.float32)
@@ -134,7 +135,7 @@ def test_tie_list_overflow_rescans_row():
     rows[hot, pos[:500]] = 3.0 + rng.random(500).astype(np.float32)
     rows[hot, pos[500:10500]] = 2.0
     sc = torch.from_numpy(rows).cuda().view(1, T, N)
-    q, k, v, scale = _kv(rng, 1, 1, N, 16, 1, False, T=T)
+    q, k, v, scale = _kv(rng, 1, 1, N, 64 if mla else 16, 1, mla, T=T)
     _both(sc, 2048, 16, 64, q, k, v, scale, repeat=1)
 
 
