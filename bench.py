@@ -118,14 +118,17 @@ def algorithmic_bytes(cfg):
 
 
 def cpu_baseline(inp, cfg):
-    """The oracle as it stands, timed on this host: one whole step (all 8 sequences)."""
+    """The oracle as it stands, timed on this host: whole steps (all 8 sequences). Its
+    BLAS pool is limited to the cores this process may run on, so `cores` is both the
+    visible core count and the number of threads the oracle used."""
     from oracle import lsa_oracle as O
+    cores = len(os.sched_getaffinity(0))
     try:
-        from threadpoolctl import threadpool_info
+        from threadpoolctl import threadpool_info, threadpool_limits
+        limiter = threadpool_limits(limits=cores)
         threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
     except Exception:
-        threads = 1
-    cores = len(os.sched_getaffinity(0))
+        limiter, threads = None, 1
     t0 = time.perf_counter()
     n = 0
     while True:  # whole steps until about 10 s of CPU work
@@ -134,9 +137,13 @@ def cpu_baseline(inp, cfg):
         dt = time.perf_counter() - t0
         if dt >= 10.0 or n >= 20:
             break
-    return {"value": n / dt, "unit": "steps/s", "cores": threads, "kind": "oracle",
+    if limiter is not None:
+        limiter.restore_original_limits()
+    used = min(cores, threads)
+    return {"value": n / dt, "unit": "steps/s", "cores": used, "kind": "oracle",
             "sample": f"{n} full steps (8 sequences x 131072 keys each: index + select + attend) in float64 "
-                      f"numpy, {dt:.1f} s wall; {cores} host cores visible, BLAS threads {threads}"}
+                      f"numpy, {dt:.1f} s wall; {cores} host cores visible to the process, BLAS pool of "
+                      f"{threads} threads"}
 
 
 def pmc_traffic(index_bytes_per_launch):
@@ -390,6 +397,80 @@ def measure_workloads(steps=50):
     return res
 
 
+def c2_chain(cfg, reps, dev):
+    """The 128K MLA decode step as the benchmark runs it, on the device replicas `reps`
+    (dicts of qI, w, kI, ks, q, k): prebuilt descriptors, one selection and one attention
+    workspace, and the ways of running the step (`ways`: name -> fn(replica index)), each
+    leaving scores, idx, out and lse in the returned buffers. The first call of any way
+    finds the selection workspace in an unknown state and clears it; later calls find it
+    clean (every selection leaves it so)."""
+    import ctypes
+    import types
+    import torch
+    import long_context_sparse_07_amd as L
+    B, T, N = cfg.B, cfg.T, cfg.N
+    scores = torch.empty((B, T, N), dtype=torch.float32, device=dev)
+    idx = torch.empty((B, T, cfg.K), dtype=torch.int32, device=dev)
+    out = torch.empty((1, B, T, cfg.Hq, cfg.d_v), dtype=torch.bfloat16, device=dev)
+    lse = torch.empty((1, B, T, cfg.Hq), dtype=torch.float32, device=dev)
+    stream = torch.cuda.current_stream()
+    sptr = ctypes.c_void_p(stream.cuda_stream)
+    lib = L.lib()
+
+    # prebuilt descriptors per replica (the timed loop only makes the C calls)
+    descs = []
+    for rp in reps:
+        ds = L.SelectDesc(B=B, T=T, N=N, scores=scores.data_ptr(), n_cols=N, K=cfg.K, sink=cfg.S,
+                          window=cfg.W, causal=1, idx=idx.data_ptr(), workspace_state=L.LSA_WS_PRIMED)
+        da = L._attend_desc(rp["q"], rp["k"], None, idx, cfg.tau, out, lse, True, 0)
+        descs.append([None, ds, da])
+    ws_sel = torch.empty(max(256, lib.lsa_select_workspace_bytes(ctypes.byref(descs[0][1]))), dtype=torch.uint8,
+                         device=dev)
+    ws_att = torch.empty(max(256, lib.lsa_attend_workspace_bytes(ctypes.byref(descs[0][2]))), dtype=torch.uint8,
+                         device=dev)
+    for rp, d in zip(reps, descs):
+        # the indexer primes the selection workspace (the selection then skips its
+        # histogram pass over the scores)
+        d[0] = L.IndexDesc(mode=L.LSA_INDEX_TOKENS, B=B, T=T, N=N, H=cfg.H_I, D=cfg.D_I, q=rp["qI"].data_ptr(),
+                           w=rp["w"].data_ptr(), k=rp["kI"].data_ptr(), k_dtype=L.LSA_FP8_E4M3FN,
+                           k_scale=rp["ks"].data_ptr(), sink=cfg.S, window=cfg.W, scores=scores.data_ptr(),
+                           select_ws=ws_sel.data_ptr(), select_ws_bytes=ws_sel.numel(),
+                           select_ws_state=L.LSA_WS_UNKNOWN)
+    first = [True]
+
+    def c_index(r):
+        L._check("lsa_index", lib.lsa_index(ctypes.byref(descs[r][0]), sptr))
+        if first[0]:  # from now on the workspace is known to be clean after each selection
+            first[0] = False
+            for d in descs:
+                d[0].select_ws_state = L.LSA_WS_CLEAN
+
+    def c_select(r):
+        L._check("lsa_select", lib.lsa_select(ctypes.byref(descs[r][1]), ws_sel.data_ptr(), ws_sel.numel(), sptr))
+
+    def c_attend(r):
+        L._check("lsa_attend", lib.lsa_attend(ctypes.byref(descs[r][2]), ws_att.data_ptr(), ws_att.numel(), sptr))
+
+    def c_fused(r):
+        L._check("lsa_select_attend", lib.lsa_select_attend(ctypes.byref(descs[r][1]), ctypes.byref(descs[r][2]),
+                                                            ws_sel.data_ptr(), ws_sel.numel(), ws_att.data_ptr(),
+                                                            ws_att.numel(), sptr))
+
+    def step(r):
+        c_index(r)
+        c_select(r)
+        c_attend(r)
+
+    def step_fused(r):
+        c_index(r)
+        c_fused(r)
+
+    return types.SimpleNamespace(scores=scores, idx=idx, out=out, lse=lse, stream=stream, lib=lib, descs=descs,
+                                 ws_sel=ws_sel, ws_att=ws_att, c_index=c_index, c_select=c_select,
+                                 c_attend=c_attend, c_fused=c_fused,
+                                 ways={"separate": step, "fused": step_fused})
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -436,62 +517,13 @@ def main():
         reps.append({k: v.to(dev) for k, v in host.items()})
         reps[-1]["kI"] = reps[-1]["kI"].view(torch.float8_e4m3fn)
     del host
+    ch = c2_chain(cfg, reps, dev)
     B, T, N = cfg.B, cfg.T, cfg.N
-    scores = torch.empty((B, T, N), dtype=torch.float32, device=dev)
-    idx = torch.empty((B, T, cfg.K), dtype=torch.int32, device=dev)
-    out = torch.empty((1, B, T, cfg.Hq, cfg.d_v), dtype=torch.bfloat16, device=dev)
-    lse = torch.empty((1, B, T, cfg.Hq), dtype=torch.float32, device=dev)
-    stream = torch.cuda.current_stream()
-    sptr = ctypes.c_void_p(stream.cuda_stream)
-    lib = L.lib()
-
-    # prebuilt descriptors per replica (the timed loop only makes the three C calls)
-    descs = []
-    for rp in reps:
-        ds = L.SelectDesc(B=B, T=T, N=N, scores=scores.data_ptr(), n_cols=N, K=cfg.K, sink=cfg.S,
-                          window=cfg.W, causal=1, idx=idx.data_ptr(), workspace_state=L.LSA_WS_PRIMED)
-        da = L._attend_desc(rp["q"], rp["k"], None, idx, cfg.tau, out, lse, True, 0)
-        descs.append([None, ds, da])
-    ws_sel = torch.empty(max(256, lib.lsa_select_workspace_bytes(ctypes.byref(descs[0][1]))), dtype=torch.uint8, device=dev)
-    ws_att = torch.empty(max(256, lib.lsa_attend_workspace_bytes(ctypes.byref(descs[0][2]))), dtype=torch.uint8, device=dev)
-    for rp, d in zip(reps, descs):
-        # the indexer primes the selection workspace (the selection then skips its
-        # histogram pass over the scores)
-        d[0] = L.IndexDesc(mode=L.LSA_INDEX_TOKENS, B=B, T=T, N=N, H=cfg.H_I, D=cfg.D_I, q=rp["qI"].data_ptr(),
-                           w=rp["w"].data_ptr(), k=rp["kI"].data_ptr(), k_dtype=L.LSA_FP8_E4M3FN,
-                           k_scale=rp["ks"].data_ptr(), sink=cfg.S, window=cfg.W, scores=scores.data_ptr(),
-                           select_ws=ws_sel.data_ptr(), select_ws_bytes=ws_sel.numel(),
-                           select_ws_state=L.LSA_WS_UNKNOWN)
-
-    def c_index(r):
-        L._check("lsa_index", lib.lsa_index(ctypes.byref(descs[r][0]), sptr))
-
-    def c_select(r):
-        L._check("lsa_select", lib.lsa_select(ctypes.byref(descs[r][1]), ws_sel.data_ptr(), ws_sel.numel(), sptr))
-
-    def c_attend(r):
-        L._check("lsa_attend", lib.lsa_attend(ctypes.byref(descs[r][2]), ws_att.data_ptr(), ws_att.numel(), sptr))
-
-    def c_fused(r):
-        L._check("lsa_select_attend", lib.lsa_select_attend(ctypes.byref(descs[r][1]), ctypes.byref(descs[r][2]),
-                                                            ws_sel.data_ptr(), ws_sel.numel(), ws_att.data_ptr(),
-                                                            ws_att.numel(), sptr))
-
-    def step(r):
-        c_index(r)
-        c_select(r)
-        c_attend(r)
-
-    def step_fused(r):
-        c_index(r)
-        c_fused(r)
-
-    # the first call clears the select workspace; every later call (same shape) finds it
-    # clean, since each selection leaves it so
-    step(0)
+    stream, lib, descs, ws_sel, ws_att = ch.stream, ch.lib, ch.descs, ch.ws_sel, ch.ws_att
+    c_index, c_select, c_attend = ch.c_index, ch.c_select, ch.c_attend
+    step, step_fused = ch.ways["separate"], ch.ways["fused"]
+    step(0)  # the first call clears the selection workspace
     torch.cuda.synchronize()
-    for d in descs:
-        d[0].select_ws_state = L.LSA_WS_CLEAN
 
     def timed(fn, n, warm):
         for i in range(warm):

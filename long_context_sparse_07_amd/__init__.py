@@ -21,7 +21,9 @@ __all__ = ["lib", "LSAError", "lsa_index", "lsa_block_means", "lsa_select", "lsa
            "AttendBwdDesc", "CacheAppendDesc", "STATUS"]
 
 HERE = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(HERE, "liblsa.so")
+# LSA_LIB_PATH selects another build of the same library (the host-sanitizer build that a
+# CPU test runs the ABI checks against); by default the in-tree liblsa.so.
+LIB_PATH = os.environ.get("LSA_LIB_PATH") or os.path.join(HERE, "liblsa.so")
 
 LSA_BF16, LSA_FP8_E4M3FN, LSA_F32 = 1, 2, 3
 LSA_INDEX_TOKENS, LSA_INDEX_BLOCKS = 0, 1

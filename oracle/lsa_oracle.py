@@ -510,20 +510,29 @@ def reference_step(inp: dict, rows=None, layers=None, with_attend: bool = True) 
 
 
 class _LazyRows:
-    """Decode KV rows on first access (full caches at 1M context are large in float64)."""
+    """Decode KV rows on first access (full caches at 1M context are large in float64).
 
-    def __init__(self, bits: np.ndarray, last: int = None):
+    rows[sel, h, :] decodes the selected rows of head h; rows[..., cols] (a column slice)
+    returns the same lazy rows restricted to those columns, so that mla_kv can take the
+    value columns of latent rows without decoding the whole cache."""
+
+    def __init__(self, bits: np.ndarray, cols: slice = slice(None)):
         self.bits = bits
-        self.last = last
-        self.shape = bits.shape if last is None else bits.shape[:-1] + (last,)
+        self.cols = cols
+        n = len(range(*cols.indices(bits.shape[-1])))
+        self.shape = bits.shape[:-1] + (n,)
 
     def __getitem__(self, key):
+        if isinstance(key, tuple) and len(key) == 2 and key[0] is Ellipsis and isinstance(key[1], slice):
+            if self.cols != slice(None):
+                raise NotImplementedError("one column slice of the raw rows")
+            return _LazyRows(self.bits, key[1])
         sel, h, sl = key
-        rows = decode_bf16(self.bits[sel, h, :])
-        return rows if self.last is None else rows[..., : self.last]
+        rows = decode_bf16(self.bits[sel, h, :])[..., self.cols]
+        return rows[..., sl]
 
 
 def _layer_kv(inp, cfg, layer, b):
     if cfg.mla:
-        return _LazyRows(inp["k"][layer, b]), _LazyRows(inp["k"][layer, b], cfg.d_v)
+        return mla_kv(_LazyRows(inp["k"][layer, b]), cfg.d_v)
     return _LazyRows(inp["k"][layer, b]), _LazyRows(inp["v"][layer, b])

@@ -118,3 +118,50 @@ def check_attn(gpu: np.ndarray, ora: np.ndarray, what=""):
 
 def oracle_rows(inp, rows):
     return O.reference_step(inp, rows=rows)
+
+
+def check_topm_all_rows(scores: torch.Tensor, idx: torch.Tensor, ctx_len, T: int, K: int, S: int, W: int,
+                        chunk: int = 64, what=""):
+    """Properties of the selection that hold at any size, checked on every row on the GPU
+    (torch ops as test infrastructure): idx ascending and unique with -1 only at the tail,
+    the sink [0,S) and window [p-W+1, p] present, nothing selected outside them and the
+    candidates, and the fill exactly the top m = K - |forced| candidates of the GPU's own
+    fp32 scores by (score descending, position ascending). Returns the number of rows."""
+    B, Tq, N = scores.shape
+    dev = scores.device
+    pos = torch.arange(N, device=dev)
+    ctx = [int(c) for c in (ctx_len.tolist() if hasattr(ctx_len, "tolist") else ctx_len)]
+    rows = 0
+    for b in range(B):
+        for t0 in range(0, Tq, chunk):
+            t1 = min(Tq, t0 + chunk)
+            sc = scores[b, t0:t1]
+            ix = idx[b, t0:t1].long()
+            p = torch.tensor([ctx[b] - T + t for t in range(t0, t1)], device=dev)[:, None]
+            valid = ix >= 0
+            nv = valid.sum(dim=1)
+            ar = torch.arange(K, device=dev)[None, :]
+            assert torch.equal(valid, ar < nv[:, None]), f"{what}: -1 padding not at the tail"
+            d = ix[:, 1:] - ix[:, :-1]
+            assert bool(((d > 0) | ~valid[:, 1:]).all()), f"{what}: not ascending/unique"
+            sel = torch.zeros_like(sc, dtype=torch.bool)
+            sel.scatter_(1, torch.where(valid, ix, torch.zeros_like(ix)), valid)
+            sink_end = torch.clamp(p + 1, max=S)
+            win_lo = torch.maximum(sink_end, p - W + 1) if W > 0 else p + 1
+            vis = pos[None, :] <= p
+            forced = vis & ((pos[None, :] < sink_end) | (pos[None, :] >= win_lo))
+            cand = vis & ~forced & torch.isfinite(sc)
+            assert bool((sel[forced]).all()), f"{what}: forced set missing"
+            assert not bool((sel & ~forced & ~cand).any()), f"{what}: selected a non-candidate"
+            fill = sel & cand
+            m = K - forced.sum(dim=1)
+            want_n = torch.minimum(m, cand.sum(dim=1))
+            assert torch.equal(fill.sum(dim=1), want_n), f"{what}: fill count"
+            inf = torch.tensor(float("inf"), device=dev)
+            smin = torch.where(fill, sc, inf).min(dim=1).values[:, None]
+            out = cand & ~fill
+            assert not bool((out & (sc > smin)).any()), f"{what}: a higher candidate was left out"
+            tmax = torch.where(fill & (sc == smin), pos[None, :], torch.full_like(pos[None, :], -1)).max(dim=1).values
+            assert not bool((out & (sc == smin) & (pos[None, :] < tmax[:, None])).any()), f"{what}: tie-break"
+            rows += t1 - t0
+    return rows

@@ -1,0 +1,93 @@
+"""The benchmark's headline chains at full size against the oracle.
+
+The 128K MLA decode step (8 sequences, every row) runs exactly as bench.py builds and
+times it (the same descriptors, workspaces and calls, every way of running the step the
+benchmark chooses among); the 4-layer cross-layer decode runs through the chained call
+the benchmark times; the 4096-token prefill has every row's selection checked against
+properties that hold at any size (top-m of the GPU's own scores, forced set, order)
+and sampled rows against the oracle. Selection by the band rule (membership may
+differ from the oracle's only within 1e-4 relative of the m-th score); attention
+within max-abs 2e-2 and mean-abs 2e-3; a second call of each way gives the same bytes.
+"""
+import numpy as np
+import pytest
+import torch
+
+import bench
+import long_context_sparse_07_amd as L
+from oracle import lsa_oracle as O
+from synth import config, make_inputs
+from gpu_harness import upload, check_band, check_attn, check_topm_all_rows
+
+pytestmark = pytest.mark.gpu
+
+
+def _check_rows(cfg, inp, ora, idx, out, lse, what):
+    P = O.query_positions(inp["ctx_len"], cfg.T)
+    swaps, worst = 0, 0.0
+    for b in range(cfg.B):
+        for t in range(cfg.T):
+            p = int(P[b, t])
+            F = O.forced_positions(p, cfg.S, cfg.W)
+            C = np.setdiff1d(np.arange(p + 1), F)
+            swaps += check_band(idx[b, t], C, ora["scores"][(b, t)][C], F, cfg.K, what=f"{what} idx {b},{t}")
+            for layer in range(cfg.layers):
+                worst = max(worst, check_attn(out[layer, b, t], ora["out"][(layer, b, t)],
+                                              f"{what} out L{layer} {b},{t}")[0])
+                assert np.allclose(lse[layer, b, t], ora["lse"][(layer, b, t)], atol=2e-3, rtol=1e-4)
+    print(f"[headline] {what}: band swaps {swaps}, worst max abs {worst:.2e}", flush=True)
+
+
+def test_c2_headline_chain_full_size():
+    cfg = config(2)
+    inp = make_inputs(cfg)
+    d = upload(inp)
+    rep = {"qI": d["qI"], "w": d["w"], "kI": d["kI"], "ks": d["kI_scale"], "q": d["q"], "k": d["k"]}
+    ch = bench.c2_chain(cfg, [rep], torch.device("cuda:0"))
+    print(f"[headline] c2 ways: {list(ch.ways)}", flush=True)
+    ora = O.reference_step(inp)
+    for name, fn in ch.ways.items():
+        fn(0)
+        torch.cuda.synchronize()
+        idx, out, lse = ch.idx.cpu().numpy(), ch.out.float().cpu().numpy(), ch.lse.cpu().numpy()
+        _check_rows(cfg, inp, ora, idx, out, lse, f"c2 {name}")
+        fn(0)
+        torch.cuda.synchronize()
+        assert np.array_equal(ch.idx.cpu().numpy(), idx) and np.array_equal(ch.out.float().cpu().numpy(), out), \
+            f"c2 {name}: second call differs"
+
+
+def test_c5_chained_call_full_size():
+    cfg = config(5)
+    inp = make_inputs(cfg)
+    d = upload(inp)
+    sc, idx, out, lse = L.lsa_index_select_attend(d["qI"], d["w"], d["kI"], cfg.K, cfg.S, cfg.W, d["q"], d["k"],
+                                                  d["v"], cfg.tau, k_scale=d["kI_scale"], ctx_len=d["ctx_len"])
+    torch.cuda.synchronize()
+    ora = O.reference_step(inp)
+    _check_rows(cfg, inp, ora, idx.cpu().numpy(), out.float().cpu().numpy(), lse.cpu().numpy(), "c5 chained")
+
+
+def test_c4_prefill_every_row_properties_and_sampled_oracle():
+    cfg = config(4)
+    inp = make_inputs(cfg)
+    d = upload(inp)
+    sc, idx = L.lsa_index_select(d["qI"], d["w"], d["kI"], cfg.K, cfg.S, cfg.W, k_scale=d["kI_scale"],
+                                 ctx_len=d["ctx_len"])
+    out, lse = L.lsa_attend(d["q"], d["k"], d["v"], idx, cfg.tau)
+    torch.cuda.synchronize()
+    n = check_topm_all_rows(sc, idx, inp["ctx_len"], cfg.T, cfg.K, cfg.S, cfg.W, what="c4")
+    assert n == cfg.T
+    rng = np.random.default_rng(4044)
+    ts = sorted({0, 1, 511, 512, 2048, 4094, 4095, *rng.integers(0, cfg.T, size=25).tolist()})
+    rows = [(0, t) for t in ts]
+    ora = O.reference_step(inp, rows=rows)
+    P = O.query_positions(inp["ctx_len"], cfg.T)
+    g_idx, g_out = idx.cpu().numpy(), out.float().cpu().numpy()
+    for b, t in rows:
+        p = int(P[b, t])
+        F = O.forced_positions(p, cfg.S, cfg.W)
+        C = np.setdiff1d(np.arange(p + 1), F)
+        check_band(g_idx[b, t], C, ora["scores"][(b, t)][C], F, cfg.K, what=f"c4 idx {b},{t}")
+        check_attn(g_out[0, b, t], ora["out"][(0, b, t)], f"c4 out {b},{t}")
+    print(f"[headline] c4: {n} rows checked by properties, {len(rows)} against the oracle", flush=True)

@@ -5,11 +5,15 @@ Each query row is quantised on both sides in fp32 with the same steps (scale = m
 the scores then differ only by the arithmetic of the contraction. Tolerance, from that
 arithmetic: the matrix unit adds the 64 products of one 32x32x64 fp8 instruction with a
 truncated alignment (measured on MI355X: error up to 2^-11.4 of the largest product of
-the instruction); allowing 2^-10 per instruction, a 128-long dot (two instructions) errs
-by at most 2^-9 * 448^2 (no code exceeds 448 in magnitude), so a score errs by at most
-k_scale[s] * 2^-9 * 448^2 * sum_h |w_h s_q,h|, plus fp32 rounding of the epilogue (1e-5
-of the row's largest score). The selection may then differ from the oracle's only for
-candidates within that tolerance of the m-th score.
+the instruction); allowing 2^-10 per instruction, a 128-long dot (two instructions) of
+head h with key s errs by at most 2^-9 * max_d |c_q[h,d] c_k[s,d]| (the codes' largest
+product), so a score errs by at most k_scale[s] * 2^-9 * sum_h |w_h s_q,h| *
+max_d |c_q[h,d] c_k[s,d]|, plus fp32 rounding of the epilogue (1e-5 of the row's largest
+score). Scores are checked against the cheaper bound with 448^2 in place of the largest
+product (no code exceeds 448). The selection band is the exact bound: it is computed
+from each candidate's own code products for the candidates whose score lies within the
+cheaper bound's band of the m-th score (the others are decided the same way under either
+bound), and membership may differ from the oracle's only inside it.
 
 Cases: 64 heads (two row blocks, one query per workgroup), the prefill kernel (64
 queries, four query groups sharing each key tile), 32 heads, 16/8/4 heads (several
@@ -36,6 +40,22 @@ def _score_tol(qI_bits, w, kscale):
     q = O.decode_bf16(qI_bits).astype(np.float32)
     _, sq = O.quantize_key_rows(q)
     return kscale.astype(np.float64) * E8 * float(np.sum(np.abs(w.astype(np.float64) * sq)))
+
+
+def _band_rtol(qI_bits, w, k_codes, kscale, C, want, m):
+    """Selection band (relative to |tau|, the m-th largest oracle score among the
+    candidates C) from the candidates' own code products (see the module docstring)."""
+    tau = np.sort(want[C])[::-1][min(m, C.size) - 1]
+    loose = _score_tol(qI_bits, w, kscale[C])
+    near = C[np.abs(want[C] - tau) <= 2.0 * float(np.max(loose)) + 1e-4 * abs(tau)]
+    q = O.decode_bf16(qI_bits).astype(np.float32)
+    cq, sq = O.quantize_key_rows(q)
+    aq = np.abs(O.decode_e4m3fn(cq))                        # [H, D] query codes
+    ak = np.abs(O.decode_e4m3fn(k_codes[near]))             # [n, D] key codes
+    mx = np.max(aq[None, :, :] * ak[:, None, :], axis=2)    # [n, H] largest product per head
+    ws = np.abs(w.astype(np.float64) * sq.astype(np.float64))
+    tol = kscale[near].astype(np.float64) * 2.0 ** -9 * (mx @ ws)
+    return 2.0 * float(np.max(tol)) / max(abs(tau), 1e-30) + 1e-4, 2.0 * float(np.max(loose)) / max(abs(tau), 1e-30)
 
 
 def _check_row(g, want, tol, what):
@@ -90,8 +110,7 @@ def test_fp8_query_scores_and_selection(name):
             C = np.setdiff1d(np.arange(p + 1), F)
             if C.size:
                 m = cfg.K - F.size
-                tau = np.sort(want[C])[::-1][min(m, C.size) - 1]
-                rtol = 2.0 * float(np.max(tol[C])) / max(abs(tau), 1e-30) + 1e-4
+                rtol, _ = _band_rtol(inp["qI"][b, t], inp["w"][b, t], inp["kI"][b], inp["kI_scale"][b], C, want, m)
                 check_band(gi[b, t], C, want[C], F, cfg.K, rtol=rtol, what=f"{name} {b},{t}")
     print(f"{name}: largest score error {worst:.2e} of the row maximum")
 
@@ -151,7 +170,7 @@ def test_fp8_query_full_size_sampled(cid):
         F = O.forced_positions(p, cfg.S, cfg.W)
         C = np.setdiff1d(np.arange(p + 1), F)
         m = cfg.K - F.size
-        tau = np.sort(want[C])[::-1][min(m, C.size) - 1]
-        rtol = 2.0 * float(np.max(tol[C])) / max(abs(tau), 1e-30) + 1e-4
+        rtol, rtol_loose = _band_rtol(inp["qI"][b, t], inp["w"][b, t], inp["kI"][b], inp["kI_scale"][b], C, want, m)
         check_band(idx[b, t].cpu().numpy(), C, want[C], F, cfg.K, rtol=rtol, what=f"c{cid} {b},{t}")
-        print(f"c{cid} {b},{t}: score error {err:.2e} of the row maximum")
+        print(f"c{cid} {b},{t}: score error {err:.2e} of the row maximum, selection band {rtol:.2e} "
+              f"(448^2 bound: {rtol_loose:.2e})")

@@ -73,6 +73,8 @@ def run_parity(cfg, rows=None, check_attend=True):
     torch.cuda.synchronize()
     idx_gpu = _to_np(r["idx"])
     swaps = 0
+    n_kept_same = n_kept_diff = 0
+    stagewise = {}  # HI rows whose GPU kept list differs: the oracle's idx on that list
     for (b, t) in rows:
         p = int(P[b, t])
         F = O.forced_positions(p, cfg.S, cfg.W)
@@ -95,10 +97,21 @@ def run_parity(cfg, rows=None, check_attend=True):
             check_band(kept_gpu, E, c[E], np.zeros(0, np.int64), cfg.n_keep, what=f"kept {b},{t}")
             kept_ora = ora["kept"][(b, t)]
             if np.array_equal(kept_gpu, kept_ora):
+                n_kept_same += 1
                 cand, sc = ora["cand"][(b, t)]
-                swaps += check_band(idx_gpu[b, t], cand, sc, F, cfg.K, what=f"hi idx {b},{t}")
-                cols = _fine_columns(inp, b, t, kept_ora, p)
-                check_scores(_to_np(r["fscores"][b, t]), cols, f"fine {b},{t}")
+            else:
+                # stage-wise: the oracle's fine stage run on the GPU's kept list (a band
+                # difference in kept would otherwise cascade into the fine selection)
+                n_kept_diff += 1
+                want_idx, cand, sc = O.select_fine_given_kept(q, w, keys, kept_gpu, p, cfg.K, cfg.S, cfg.W, cfg.Bs)
+                stagewise[(b, t)] = want_idx
+            swaps += check_band(idx_gpu[b, t], cand, sc, F, cfg.K, what=f"hi idx {b},{t}")
+            cols = _fine_columns(inp, b, t, kept_gpu, p)
+            check_scores(_to_np(r["fscores"][b, t]), cols, f"fine {b},{t}")
+    if cfg.hi:
+        assert n_kept_same + n_kept_diff == len(rows), "every HI row goes through one fine-stage check"
+        print(f"[parity] HI fine stage: {n_kept_same} rows on the oracle's kept list, {n_kept_diff} checked "
+              f"stage-wise on the GPU's", flush=True)
     print(f"[parity] selection ok, band swaps {swaps}", flush=True)
 
     # B: oracle scores (fp32) -> GPU select, bit-exact against the oracle on the same values
@@ -156,6 +169,9 @@ def run_parity(cfg, rows=None, check_attend=True):
             for (b, t) in rows:
                 want = ora["out"][(layer, b, t)]
                 check_attn(oc[layer, b, t], want, f"attend(oracle idx) L{layer} {b},{t}")
+                if (b, t) in stagewise:  # end to end against the stage-wise selection
+                    k_rows, v_rows = O._layer_kv(inp, cfg, layer, b)
+                    want, _ = O.attend(O.decode_bf16(inp["q"][layer, b, t]), k_rows, v_rows, stagewise[(b, t)], cfg.tau)
                 worst = max(worst, check_attn(od[layer, b, t], want, f"end-to-end L{layer} {b},{t}")[0])
                 assert np.allclose(lc[layer, b, t], ora["lse"][(layer, b, t)], atol=2e-3, rtol=1e-4)
         print(f"[parity] attention ok, worst end-to-end max abs {worst:.2e}", flush=True)
@@ -185,3 +201,35 @@ def test_parity_full_size_prefill_sampled():
     rng = np.random.default_rng(4004)
     ts = sorted({0, 1, 63, 64, 2047, 4095, *rng.integers(0, cfg.T, size=6).tolist()})
     run_parity(cfg, rows=[(0, t) for t in ts])
+
+
+def test_hi_fine_stage_on_given_kept_lists():
+    # The fine stage alone on kept lists that are not the coarse stage's choice (random
+    # ascending subsets of the eligible blocks, -1 padded, some empty): the GPU's fine
+    # scores and selection against the oracle's fine stage run on the same kept list.
+    cfg = config(3, **SMALL[3])
+    inp = make_inputs(cfg)
+    d = upload(inp)
+    P = O.query_positions(inp["ctx_len"], cfg.T)
+    rng = np.random.default_rng(3033)
+    kept = np.full((cfg.B, cfg.T, cfg.n_keep), -1, dtype=np.int32)
+    for b in range(cfg.B):
+        for t in range(cfg.T):
+            p = int(P[b, t])
+            E = np.nonzero(O.eligible_blocks(p, cfg.S, cfg.W, cfg.Bs, cfg.N // cfg.Bs))[0]
+            n = 0 if t == 1 else int(rng.integers(1, cfg.n_keep + 1))
+            kept[b, t, :n] = np.sort(rng.choice(E, size=n, replace=False))
+    kt = torch.from_numpy(kept).cuda()
+    fs = L.lsa_index(d["qI"], d["w"], d["kI"], k_scale=d["kI_scale"], kept=kt, block_size=cfg.Bs, ctx_len=d["ctx_len"])
+    idx = L.lsa_select(fs, cfg.K, cfg.S, cfg.W, N=cfg.N, ctx_len=d["ctx_len"], kept=kt, block_size=cfg.Bs)
+    torch.cuda.synchronize()
+    g_fs, g_idx = _to_np(fs), _to_np(idx)
+    for b in range(cfg.B):
+        keys = O.index_keys_f64(inp["kI"][b], None if inp["kI_scale"] is None else inp["kI_scale"][b])
+        for t in range(cfg.T):
+            p = int(P[b, t])
+            q, w = O.decode_bf16(inp["qI"][b, t]), inp["w"][b, t].astype(np.float64)
+            _, cand, sc = O.select_fine_given_kept(q, w, keys, kept[b, t], p, cfg.K, cfg.S, cfg.W, cfg.Bs)
+            F = O.forced_positions(p, cfg.S, cfg.W)
+            check_band(g_idx[b, t], cand, sc, F, cfg.K, what=f"given kept {b},{t}")
+            check_scores(g_fs[b, t], _fine_columns(inp, b, t, kept[b, t], p), f"given kept fine {b},{t}")

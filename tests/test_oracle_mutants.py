@@ -20,7 +20,8 @@ def _run_pins(names):
                         "test_selection_invariants", "test_hi_matches_brute_force",
                         "test_budget_covers_context_equals_dense_causal",
                         "test_hi_all_blocks_kept_equals_flat",
-                        "test_selection_without_forced_is_lexsort_and_partition"):
+                        "test_selection_without_forced_is_lexsort_and_partition",
+                        "test_fine_given_all_eligible_kept_equals_flat"):
                 for seed in range(4):
                     fn(seed)
             else:
@@ -38,7 +39,10 @@ ALL = ["test_golden_hand_worked_flat_and_hi", "test_indexer_single_head_is_relu_
        "test_attention_permutation_invariant_and_gqa_mapping", "test_e4m3fn_matches_torch_all_codes",
        "test_fp8_query_worked_example", "test_fp8_query_exact_for_representable_rows",
        "test_fp8_query_error_bound_rows_and_scaling", "test_fp8_query_score_is_the_fp8_contraction",
-       "test_attention_backward_finite_differences", "test_attention_backward_closed_forms"]
+       "test_attention_backward_finite_differences", "test_attention_backward_closed_forms",
+       "test_query_positions_hand_worked", "test_reference_step_positions_are_causal_prefixes",
+       "test_reference_step_mla_one_selected_row_is_its_value_prefix", "test_reference_step_mla_dense_matches_sdpa",
+       "test_fine_given_all_eligible_kept_equals_flat", "test_fine_given_kept_hand_worked"]
 
 
 def _no_relu(q, w, keys, p):
@@ -137,6 +141,26 @@ def _bwd_dk_without_tau(q, k_rows, v_rows, idx, tau, out, lse, dout):
     return dq, dK / tau, dV
 
 
+def _positions_reversed(ctx_len, T):
+    # token t at ctx - 1 - t: the right set of positions in the wrong token order
+    ctx = np.asarray(ctx_len, dtype=np.int64)
+    return ctx[:, None] - 1 - np.arange(T, dtype=np.int64)[None, :]
+
+
+def _mla_value_last_columns(rows, d_v):
+    # V taken from the last d_v columns of the latent row instead of the first
+    return rows, rows[..., rows.shape[-1] - d_v:]
+
+
+_real_fine = O.select_fine_given_kept
+
+
+def _fine_block_offset(q, w, keys, kept, p, K, S, W, Bs):
+    # kept block j read as the block after it
+    kept = np.asarray(kept)
+    return _real_fine(q, w, keys, np.where(kept >= 0, kept + 1, kept), p, K, S, W, Bs)
+
+
 MUTANTS = [
     ("indexer_scores", _no_relu),
     ("indexer_scores", _max_heads),
@@ -151,6 +175,9 @@ MUTANTS = [
     ("index_query_f64", _query_shared_scale),
     ("attend_backward", _bwd_no_delta),
     ("attend_backward", _bwd_dk_without_tau),
+    ("query_positions", _positions_reversed),
+    ("mla_kv", _mla_value_last_columns),
+    ("select_fine_given_kept", _fine_block_offset),
 ]
 
 

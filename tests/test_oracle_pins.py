@@ -671,3 +671,108 @@ def test_indexer_kl_zero_minimum_and_finite_differences():
     # two entries by hand: target (1, 0), scores (0, 0): loss log 2, gradient (-1/2, 1/2)
     loss, grad = O.indexer_kl([1.0, 0.0], [0.0, 0.0], [True, True])
     assert abs(loss - np.log(2.0)) < 1e-15 and np.allclose(grad, [-0.5, 0.5])
+
+
+# ----------------------------------------------------------------------------- positions, MLA value, HI fine stage
+
+def test_query_positions_hand_worked():
+    # R11 worked on paper: a sequence with ctx visible rows and T query tokens puts token t
+    # at position ctx - T + t, so the T queries are the last T rows in token order
+    # (ctx 12, T 3 -> 9 10 11; ctx 7 -> 4 5 6; ctx 3 -> 0 1 2).
+    got = O.query_positions(np.array([12, 7, 3]), 3)
+    assert got.tolist() == [[9, 10, 11], [4, 5, 6], [0, 1, 2]]
+    assert O.query_positions(np.array([5]), 1).tolist() == [[4]]
+
+
+def _dense_prefix_sdpa(q, k, v, tau, n):
+    """torch's float64 scaled dot-product attention of one query token's heads over rows
+    [0, n) (a library routine; the causal prefix written out by its length)."""
+    Hq, Hkv = q.shape[0], k.shape[1]
+    g = Hq // Hkv
+    out = np.zeros((Hq, v.shape[2]))
+    for hq in range(Hq):
+        out[hq] = _sdpa_dense(q[hq:hq + 1], k[:n, hq // g], v[:n, hq // g], tau)[0]
+    return out
+
+
+def test_reference_step_positions_are_causal_prefixes():
+    # Budget >= context: token t of T attends over exactly its causal prefix [0, N-T+t]
+    # (R11 with ctx = N), which the library's dense attention over that many rows fixes.
+    from synth import config, make_inputs
+    cfg = config(1, N=40, T=3, K=64, S=4, W=8, H_I=2, D_I=8, Hq=4, d_qk=16, d_v=16)
+    inp = make_inputs(cfg)
+    res = O.reference_step(inp)
+    k, v = O.decode_bf16(inp["k"][0, 0]), O.decode_bf16(inp["v"][0, 0])
+    for t in range(cfg.T):
+        n = cfg.N - cfg.T + t + 1
+        assert res["idx"][(0, t)][res["idx"][(0, t)] >= 0].tolist() == list(range(n))
+        q = O.decode_bf16(inp["q"][0, 0, t])
+        want = _dense_prefix_sdpa(q, k, v, cfg.tau, n)
+        assert np.allclose(res["out"][(0, 0, t)], want, atol=1e-12)
+
+
+def _mla_cfg(**kw):
+    from synth import config
+    base = dict(B=1, N=30, T=1, H_I=2, D_I=8, Hq=4, d_qk=24, d_v=16, salient="none")
+    base.update(kw)
+    return config(2, **base)
+
+
+def test_reference_step_mla_one_selected_row_is_its_value_prefix():
+    # One selected row (budget K = 1 taken by a sink of 1): o = V[0] exactly for every head,
+    # and V of an MLA latent row is its first d_v columns (R15: the configuration's 512
+    # latent + 64 rope columns, the rope part entering only q.K); lse = z_0.
+    from synth import make_inputs
+    cfg = _mla_cfg(K=1, S=1, W=0)
+    inp = make_inputs(cfg)
+    res = O.reference_step(inp)
+    assert res["idx"][(0, 0)].tolist() == [0]
+    row0 = O.decode_bf16(inp["k"][0, 0, 0, 0])
+    q = O.decode_bf16(inp["q"][0, 0, 0])
+    for h in range(cfg.Hq):
+        assert np.array_equal(res["out"][(0, 0, 0)][h], row0[: cfg.d_v])
+        assert res["lse"][(0, 0, 0)][h] == pytest.approx(cfg.tau * float(np.dot(q[h], row0)), abs=1e-12)
+
+
+def test_reference_step_mla_dense_matches_sdpa():
+    # Budget >= context on MLA rows: the library's dense attention with K = the whole
+    # latent row and V = its first d_v columns.
+    from synth import make_inputs
+    cfg = _mla_cfg(K=40, S=2, W=4)
+    inp = make_inputs(cfg)
+    res = O.reference_step(inp)
+    rows = O.decode_bf16(inp["k"][0, 0])                 # [N, 1, d_qk]
+    q = O.decode_bf16(inp["q"][0, 0, 0])
+    want = _dense_prefix_sdpa(q, rows, rows[..., : cfg.d_v], cfg.tau, cfg.N)
+    assert np.allclose(res["out"][(0, 0, 0)], want, atol=1e-12)
+
+
+@pytest.mark.parametrize("seed", range(6))
+def test_fine_given_all_eligible_kept_equals_flat(seed):
+    # R9: with every eligible block kept, the fine stage on that kept list is the flat
+    # selection, bit for bit.
+    rng = np.random.default_rng(700 + seed)
+    Bs = 8
+    N = int(rng.integers(4, 40)) * Bs + int(rng.integers(0, Bs))
+    H, D = 3, 6
+    q, w = rng.standard_normal((H, D)), rng.random(H)
+    keys = rng.standard_normal((N, D))
+    p = N - 1 - int(rng.integers(0, 3))
+    K, S, W = 24, 3, Bs + 2
+    flat = O.select_tokens(O.indexer_scores(q, w, keys[: p + 1], p), p, K, S, W)
+    elig = np.nonzero(O.eligible_blocks(p, S, W, Bs, N // Bs))[0]
+    kept = O.pad_sorted(elig, elig.size + 2)            # -1 padding is ignored
+    got, cand, sc = O.select_fine_given_kept(q, w, keys, kept, p, K, S, W, Bs)
+    assert np.array_equal(got, flat)
+    assert np.allclose(sc, O.indexer_scores(q, w, keys[: p + 1], p)[cand], atol=1e-12)
+
+
+def test_fine_given_kept_hand_worked():
+    # The hand-worked HI cases: the fine stage run on the kept list worked on paper gives
+    # the idx worked on paper.
+    g = _golden("hand_worked_select.json")
+    q, w, keys = np.array(g["q"]), np.array(g["w"]), np.array(g["keys"])
+    for c in g["hi_cases"]:
+        kept = np.array(c["kept"] + [-1], dtype=np.int64)
+        idx, _, _ = O.select_fine_given_kept(q, w, keys, kept, c["p"], c["K"], c["S"], c["W"], c["Bs"])
+        assert idx.tolist() == c["idx"], c["why"]
