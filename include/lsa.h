@@ -27,7 +27,8 @@
  *     aligned.
  *   - `stream` is a hipStream_t passed as void* (NULL = the default stream). Work
  *     is enqueued on it; no call synchronises, allocates device memory, or keeps
- *     a pointer after it returns. The library has no mutable global state.
+ *     a pointer after it returns. The library has no mutable global state, apart
+ *     from the static per-GPU buffer of lsa_attend_noalloc.
  *   - Query token t of sequence b sits at position p = ctx_len[b] - T + t
  *     (reading R11); ctx_len NULL means every sequence has N visible rows.
  *     Positions s > p are never visible to query t.
@@ -283,6 +284,20 @@ typedef struct lsa_attend_desc {
 
 size_t lsa_attend_workspace_bytes(const lsa_attend_desc *desc);
 int32_t lsa_attend(const lsa_attend_desc *desc, void *workspace, size_t workspace_bytes, void *stream);
+
+/*
+ * lsa_attend_noalloc — lsa_attend without a workspace argument, for callers that cannot
+ * allocate device memory (code under HIP graph capture, tight serving loops, harnesses
+ * that forbid allocation). Same descriptor, results bit-identical to lsa_attend with the
+ * same n_splits. The split partials go to a static device buffer of the library
+ * (32 MiB, one per GPU, held until the process ends; the call allocates nothing). Every
+ * call on a GPU shares that GPU's buffer, which keeps the last call's partials: calls that
+ * overlap on one GPU (concurrent streams, threads) race and must be ordered by the caller.
+ * Errors as lsa_attend; LSA_E_WORKSPACE when lsa_attend_workspace_bytes(desc) exceeds
+ * the buffer (fewer splits, n_splits, shrink it); LSA_E_HIP if the buffer's address cannot
+ * be found on the stream's device.
+ */
+int32_t lsa_attend_noalloc(const lsa_attend_desc *desc, void *stream);
 
 /*
  * lsa_select_attend — lsa_select(sel) followed by lsa_attend(att) on the positions it

@@ -17,7 +17,7 @@ __all__ = ["lib", "LSAError", "lsa_index", "lsa_block_means", "lsa_select", "lsa
            "lsa_workspace_clear", "lsa_select_workspace_bytes", "lsa_attend_workspace_bytes",
            "LSA_BF16", "LSA_FP8_E4M3FN", "LSA_F32", "LSA_INDEX_TOKENS", "LSA_INDEX_BLOCKS",
            "LSA_WS_UNKNOWN", "LSA_WS_CLEAN", "LSA_WS_PRIMED", "lsa_select_attend", "lsa_index_select_attend",
-           "lsa_cache_append", "lsa_attend_backward", "lsa_index_target", "IndexTargetDesc", "IndexDesc", "BlockMeansDesc", "SelectDesc", "AttendDesc",
+           "lsa_cache_append", "lsa_attend_backward", "lsa_attend_noalloc", "lsa_index_target", "IndexTargetDesc", "IndexDesc", "BlockMeansDesc", "SelectDesc", "AttendDesc",
            "AttendBwdDesc", "CacheAppendDesc", "STATUS"]
 
 HERE = os.path.dirname(os.path.abspath(__file__))
@@ -117,6 +117,8 @@ def lib():
         L.lsa_select.restype = c_int32
         L.lsa_attend.argtypes = [POINTER(AttendDesc), c_void_p, c_size_t, c_void_p]
         L.lsa_attend.restype = c_int32
+        L.lsa_attend_noalloc.argtypes = [POINTER(AttendDesc), c_void_p]
+        L.lsa_attend_noalloc.restype = c_int32
         L.lsa_select_attend.argtypes = [POINTER(SelectDesc), POINTER(AttendDesc), c_void_p, c_size_t, c_void_p,
                                         c_size_t, c_void_p]
         L.lsa_select_attend.restype = c_int32
@@ -352,6 +354,17 @@ def lsa_attend(q, k, v, idx, softmax_scale, *, out=None, lse=None, out_dtype=Non
     need = lib().lsa_attend_workspace_bytes(ctypes.byref(d))
     ws = workspace if workspace is not None else (_workspace("attend", need, q.device)[0] if need else None)
     _check("lsa_attend", lib().lsa_attend(ctypes.byref(d), _ptr(ws), 0 if ws is None else ws.numel(), s))
+    return out, lse
+
+
+def lsa_attend_noalloc(q, k, v, idx, softmax_scale, *, out=None, lse=None, out_dtype=None, with_lse=True,
+                       n_splits=0, block_table=None, N=None, shared=False, ctx_len=None, stream=None):
+    """lsa_attend without a workspace: the split partials go to the library's static
+    per-GPU buffer (calls that overlap on one GPU race). Same arguments and results as
+    lsa_attend (out and lse are allocated here only when not given)."""
+    out, lse = _attend_outputs(q, v, out, lse, out_dtype, with_lse)
+    d = _attend_desc(q, k, v, idx, softmax_scale, out, lse, v is None, n_splits, block_table, N, shared, ctx_len)
+    _check("lsa_attend_noalloc", lib().lsa_attend_noalloc(ctypes.byref(d), _stream(stream)))
     return out, lse
 
 

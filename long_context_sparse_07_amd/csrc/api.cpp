@@ -355,20 +355,47 @@ size_t lsa_attend_workspace_bytes(const lsa_attend_desc *d) {
     return lsa::attend_workspace_bytes(a);
 }
 
-int32_t lsa_attend(const lsa_attend_desc *d, void *ws, size_t ws_bytes, void *stream) {
-    lsa::AttendArgs a;
-    int32_t rc = attend_check(d, a);
-    if (rc != LSA_OK) return rc;
+static int32_t attend_pointers(const lsa_attend_desc *d) {
     if (!d->q || !d->k || !d->v || !d->idx || !d->out) return fail(LSA_E_NULL, "lsa_attend: q, k, v, idx, out are required");
     if (!aligned16(d->q) || !aligned16(d->k) || !aligned16(d->v) || !aligned16(d->out) || !aligned4(d->idx) ||
         (d->lse && !aligned4(d->lse)))
         return fail(LSA_E_ALIGN, "lsa_attend: q, k, v, out must be 16-byte aligned");
+    return LSA_OK;
+}
+
+int32_t lsa_attend(const lsa_attend_desc *d, void *ws, size_t ws_bytes, void *stream) {
+    lsa::AttendArgs a;
+    int32_t rc = attend_check(d, a);
+    if (rc != LSA_OK) return rc;
+    if ((rc = attend_pointers(d)) != LSA_OK) return rc;
     const size_t need = lsa::attend_workspace_bytes(a);
     if (need && (!ws || ws_bytes < need))
         return fail(LSA_E_WORKSPACE, "lsa_attend: workspace of %zu bytes needed, %zu given", need, ws_bytes);
     if (need && (reinterpret_cast<uintptr_t>(ws) & 255u) != 0)
         return fail(LSA_E_ALIGN, "lsa_attend: workspace not 256-byte aligned");
     return hip_status(lsa::launch_attend(a, ws, reinterpret_cast<hipStream_t>(stream)), "lsa_attend");
+}
+
+int32_t lsa_attend_noalloc(const lsa_attend_desc *d, void *stream) {
+    lsa::AttendArgs a;
+    int32_t rc = attend_check(d, a);
+    if (rc != LSA_OK) return rc;
+    if ((rc = attend_pointers(d)) != LSA_OK) return rc;
+    const size_t need = lsa::attend_workspace_bytes(a);
+    if (need > lsa::kAttendStaticScratchBytes)
+        return fail(LSA_E_WORKSPACE,
+                    "lsa_attend_noalloc: %zu bytes of split partials needed, the static buffer holds %zu "
+                    "(ask for fewer splits, or call lsa_attend with a workspace)",
+                    need, lsa::kAttendStaticScratchBytes);
+    void *ws = nullptr;
+    if (need) {
+        hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+        int dev = 0;
+        hipError_t e = s ? hipStreamGetDevice(s, &dev) : hipGetDevice(&dev);
+        if (e == hipSuccess) e = lsa::attend_static_scratch(dev, &ws);
+        if (e != hipSuccess) return hip_status(e, "lsa_attend_noalloc: static buffer");
+    }
+    return hip_status(lsa::launch_attend(a, ws, reinterpret_cast<hipStream_t>(stream)), "lsa_attend_noalloc");
 }
 
 int32_t lsa_select_attend(const lsa_select_desc *sd, const lsa_attend_desc *ad, void *sel_ws, size_t sel_ws_bytes,

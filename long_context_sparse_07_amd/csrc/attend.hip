@@ -24,10 +24,18 @@
 // then and holds the pass's working set, and the positions land straight in the LDS
 // position list, with no kernel boundary and no round trip of the index list through
 // memory in between.
+#include <mutex>
+
 #include "select_core.cuh"
 
 namespace lsa {
 namespace {
+
+// Split partials of lsa_attend_noalloc, for callers that cannot allocate: one copy per
+// GPU, held until the process ends, shared by every such call on that GPU (calls that
+// overlap on one GPU race for it). Host code takes its device address from
+// hipGetSymbolAddress, never from this name.
+static __device__ __align__(256) unsigned char scratch[kAttendStaticScratchBytes];
 
 constexpr int kRows = 32;     // selected rows per tile
 constexpr int kMaxR = 2048;   // selected rows per split (positions staged in LDS)
@@ -592,6 +600,33 @@ size_t attend_workspace_bytes(const AttendArgs &a) {
     const int S = (a.K + R - 1) / R;
     if (S <= 1) return 0;
     return partial_rows_bytes(a, S) + (size_t)a.L * a.B * a.T * a.Hq * S * 2 * sizeof(float);
+}
+
+namespace {
+constexpr int kMaxScratchDevices = 64;
+std::mutex g_scratch_mu;
+void *g_scratch_ptr[kMaxScratchDevices] = {};
+}  // namespace
+
+hipError_t attend_static_scratch(int dev, void **ptr) {
+    if (dev < 0 || dev >= kMaxScratchDevices) return hipErrorInvalidDevice;
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    if (!g_scratch_ptr[dev]) {
+        // each GPU holds its own copy of the array at its own address: look it up with
+        // that device current, once
+        int cur = 0;
+        hipError_t e = hipGetDevice(&cur);
+        if (e != hipSuccess) return e;
+        if (cur != dev && (e = hipSetDevice(dev)) != hipSuccess) return e;
+        void *p = nullptr;
+        e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+        const hipError_t e2 = cur != dev ? hipSetDevice(cur) : hipSuccess;
+        if (e != hipSuccess) return e;
+        if (e2 != hipSuccess) return e2;
+        g_scratch_ptr[dev] = p;
+    }
+    *ptr = g_scratch_ptr[dev];
+    return hipSuccess;
 }
 
 hipError_t launch_attend(const AttendArgs &a, void *ws, hipStream_t s) {

@@ -160,6 +160,10 @@ int attend_default_splits(const AttendArgs &a);
 size_t attend_workspace_bytes(const AttendArgs &a);
 bool attend_supported(int d_qk, int d_v, int g);
 hipError_t launch_attend(const AttendArgs &a, void *ws, hipStream_t s);
+// The split-partial buffer of lsa_attend_noalloc: a static device array of this size,
+// one per GPU; *ptr receives device dev's copy (looked up once per device).
+constexpr size_t kAttendStaticScratchBytes = (size_t)32 << 20;
+hipError_t attend_static_scratch(int dev, void **ptr);
 // Selection (flat rows, no kept map) and attention on its output in one chain: the
 // attention workgroups resolve their own slices of the selection (sa.idx written too).
 // a.idx is ignored; sa and a describe the same B, T, N, K.

@@ -1,0 +1,60 @@
+"""lsa_attend_noalloc (the attention call that allocates nothing: its split partials go
+to the library's static per-GPU buffer) against lsa_attend with a caller workspace, on
+the same inputs and split counts: bit-identical output and log-sum-exp, for two calls in
+a row (the second on a smaller input, so it reuses the buffer the first one left behind),
+and a shape whose partials exceed the buffer rejected before any launch."""
+import pytest
+import torch
+
+import long_context_sparse_07_amd as L
+
+pytestmark = pytest.mark.gpu
+
+
+def _mla(B, N, K, Hq, seed):
+    g = torch.Generator(device="cuda").manual_seed(seed)
+    q = (torch.randn((1, B, 1, Hq, 576), device="cuda", generator=g) * 576 ** -0.5).to(torch.bfloat16)
+    k = torch.randn((1, B, N, 1, 576), device="cuda", generator=g).to(torch.bfloat16)
+    idx = torch.rand((B, N), device="cuda", generator=g).topk(K, dim=1).indices.sort(dim=1).values
+    idx = idx.to(torch.int32).view(B, 1, K).contiguous()
+    idx[0, 0, K - 7:] = -1  # some padding
+    return q, k, None, idx, 576 ** -0.5
+
+
+def _gqa(B, T, N, K, Hq, Hkv, L_, seed):
+    g = torch.Generator(device="cuda").manual_seed(seed)
+    q = (torch.randn((L_, B, T, Hq, 128), device="cuda", generator=g) * 128 ** -0.5).to(torch.bfloat16)
+    k = (torch.randn((L_, B, N, Hkv, 128), device="cuda", generator=g) * 128 ** -0.5).to(torch.bfloat16)
+    v = (torch.randn((L_, B, N, Hkv, 128), device="cuda", generator=g) * 128 ** -0.5).to(torch.bfloat16)
+    idx = torch.rand((B * T, N), device="cuda", generator=g).topk(K, dim=1).indices.sort(dim=1).values
+    return q, k, v, idx.to(torch.int32).view(B, T, K).contiguous(), 128 ** -0.5
+
+
+def _same(args, n_splits):
+    q, k, v, idx, scale = args
+    ref_o, ref_l = L.lsa_attend(q, k, v, idx, scale, n_splits=n_splits)
+    got_o, got_l = L.lsa_attend_noalloc(q, k, v, idx, scale, n_splits=n_splits)
+    torch.cuda.synchronize()
+    assert torch.equal(got_o, ref_o), "output differs from lsa_attend"
+    assert torch.equal(got_l, ref_l), "log-sum-exp differs from lsa_attend"
+
+
+def test_noalloc_matches_attend_two_calls_second_smaller():
+    # first: the 128K-decode attention shape on fewer sequences, library-chosen splits
+    _same(_mla(4, 20000, 2048, 64, 1), 0)
+    # second, smaller: GQA over two layers and two query tokens, a few splits
+    _same(_gqa(2, 2, 3000, 512, 32, 4, 2, 2), 3)
+    # and once more the first shape with a different split count (the buffer holds the
+    # previous call's partials)
+    _same(_mla(2, 9000, 1024, 64, 3), 8)
+
+
+def test_noalloc_single_split_needs_no_buffer():
+    _same(_gqa(1, 1, 500, 64, 16, 1, 1, 4), 1)
+
+
+def test_noalloc_rejects_partials_beyond_the_buffer():
+    q, k, v, idx, scale = _mla(64, 2048, 2048, 64, 5)
+    with pytest.raises(L.LSAError) as e:
+        L.lsa_attend_noalloc(q, k, v, idx, scale, n_splits=32)
+    assert e.value.status == -7 and "static buffer" in str(e.value)
