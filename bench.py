@@ -30,7 +30,6 @@ sys.path.insert(0, ROOT)
 
 METRIC = "LSA decode steps/sec at 128K ctx (1 GPU); achieved HBM GB/s vs peak"
 PEAK_HBM_GBS = 8000.0
-PROFILE_PMC = os.path.join(ROOT, "profiles", "index_fp8_c2_pmc.json")
 
 
 def parse():
@@ -42,13 +41,16 @@ def parse():
     ap.add_argument("--no-graph", action="store_true", help="headline from plain stream launches")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--profile-only", action="store_true", help="few plain steps, no graphs (for rocprofv3)")
-    ap.add_argument("--fused", action="store_true", help="with --profile-only: the lsa_select_attend chain")
+    ap.add_argument("--way", default="index_select", choices=["separate", "fused", "index_select"],
+                    help="with --profile-only: which way of running the step")
     ap.add_argument("--no-workloads", action="store_true",
                     help="skip the other configurations' step times (extra.workloads)")
     ap.add_argument("--calib-copy", action="store_true",
                     help="with --profile-only: also run one elementwise add of known traffic (counter calibration)")
     ap.add_argument("--profile-c4-index", action="store_true",
                     help="only the c4 prefill indexer, bf16 then fp8 queries, `--steps` calls each (for rocprofv3)")
+    ap.add_argument("--profile-workload", default=None, choices=["c1", "c2s", "c2f", "c3", "c4", "c5"],
+                    help="only this workload's step, plain launches, `--steps` steps (for rocprofv3)")
     ap.add_argument("--profile-backward", action="store_true",
                     help="only lsa_attend_backward on the c2 shape, `--steps` calls (for rocprofv3)")
     return ap.parse_args()
@@ -146,19 +148,141 @@ def cpu_baseline(inp, cfg):
                       f"{threads} threads"}
 
 
-def pmc_traffic(index_bytes_per_launch):
-    """HBM traffic of the indexer from committed rocprofv3 counter runs, if they were
-    taken on the current kernel source; else None."""
+def _sources_sha(files):
+    src = b"".join(open(os.path.join(ROOT, "long_context_sparse_07_amd", "csrc", f), "rb").read() for f in files)
+    return hashlib.sha256(src).hexdigest()
+
+
+def pmc_traffic(record, files):
+    """HBM traffic per launch of the roofline kernel from a committed rocprofv3 counter
+    record under profiles/, if it was taken on the current kernel sources; else None."""
     try:
-        with open(PROFILE_PMC) as f:
+        with open(os.path.join(ROOT, "profiles", record)) as f:
             rec = json.load(f)
-        src = b"".join(open(os.path.join(ROOT, "long_context_sparse_07_amd", "csrc", f), "rb").read()
-                       for f in ("index.hip", "common.cuh"))
-        if rec.get("index_hip_sha256") != hashlib.sha256(src).hexdigest():
+        if rec.get("sources_sha256", rec.get("index_hip_sha256")) != _sources_sha(files):
             return None
         return rec["traffic_bytes_per_launch"]
     except Exception:
         return None
+
+
+def pmc_attend_traffic():
+    """Counter traffic of the c2 attention (attend + combine kernels) from the committed
+    record, if taken on the current attention source; else None."""
+    try:
+        with open(os.path.join(ROOT, "profiles", "attend_c2_pmc.json")) as f:
+            rec = json.load(f)
+        if rec.get("sources_sha256") != _sources_sha(("attend.hip", "common.cuh")):
+            return None
+        return {k: rec[k] for k in ("read_bytes_per_step", "write_bytes_per_step", "traffic_over_gather")}
+    except Exception:
+        return None
+
+
+def upload_workload(inp, cfg):
+    """Device copies of one workload's inputs (bench naming: ks = key scales, ctx = ctx_len)."""
+    import numpy as np
+    import torch
+
+    def bf16(a):
+        return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).view(torch.bfloat16).cuda()
+
+    d = {"qI": bf16(inp["qI"]), "w": torch.from_numpy(inp["w"]).cuda(),
+         "ctx": torch.from_numpy(inp["ctx_len"]).cuda(), "q": bf16(inp["q"]), "k": bf16(inp["k"]),
+         "v": bf16(inp["v"]) if inp["v"] is not None else None}
+    if cfg.k_fp8:
+        d["kI"] = torch.from_numpy(inp["kI"]).cuda().view(torch.float8_e4m3fn)
+        d["ks"] = torch.from_numpy(inp["kI_scale"]).cuda()
+    else:
+        d["kI"], d["ks"] = bf16(inp["kI"]), None
+    return d
+
+
+def c_flat(cid):
+    """Inputs and output buffers of a flat workload (no HI)."""
+    import torch
+    from synth import config, make_inputs
+    cfg = config(cid)
+    d = upload_workload(make_inputs(cfg), cfg)
+    B, T = cfg.B, cfg.T
+    sc = torch.empty((B, T, cfg.N), dtype=torch.float32, device="cuda")
+    idx = torch.empty((B, T, cfg.K), dtype=torch.int32, device="cuda")
+    out = torch.empty((cfg.layers, B, T, cfg.Hq, cfg.d_v), dtype=torch.bfloat16, device="cuda")
+    lse = torch.empty((cfg.layers, B, T, cfg.Hq), dtype=torch.float32, device="cuda")
+    return cfg, d, sc, idx, out, lse
+
+
+def flat_step(cfg, d, sc, idx, out, lse):
+    """The separate calls: lsa_index (priming the selection), lsa_select, lsa_attend."""
+    import long_context_sparse_07_amd as L
+
+    def fn():
+        L.lsa_index_select(d["qI"], d["w"], d["kI"], cfg.K, cfg.S, cfg.W, k_scale=d["ks"], ctx_len=d["ctx"],
+                           scores=sc, idx=idx)
+        L.lsa_attend(d["q"], d["k"], d["v"], idx, cfg.tau, out=out, lse=lse)
+    return fn
+
+
+def fused_step(cfg, d, sc, idx, out, lse):
+    """The chained calls: lsa_index (priming the selection), then lsa_select_attend."""
+    import long_context_sparse_07_amd as L
+
+    def fn():
+        L.lsa_index_select_attend(d["qI"], d["w"], d["kI"], cfg.K, cfg.S, cfg.W, d["q"], d["k"], d["v"], cfg.tau,
+                                  k_scale=d["ks"], ctx_len=d["ctx"], scores=sc, idx=idx, out=out, lse=lse)
+    return fn
+
+
+def hi_step(cfg, d):
+    """The c3 hierarchical step: coarse block scores, block selection, fine scores and
+    selection inside the kept blocks, attention (block means maintained outside the step)."""
+    import torch
+    import long_context_sparse_07_amd as L
+    B, T = cfg.B, cfg.T
+    nb = cfg.N // cfg.Bs
+    kbar = L.lsa_block_means(d["kI"], cfg.Bs, k_scale=d["ks"])
+    cs = torch.empty((B, T, nb), dtype=torch.float32, device="cuda")
+    kept = torch.empty((B, T, cfg.n_keep), dtype=torch.int32, device="cuda")
+    fs = torch.empty((B, T, cfg.n_keep * cfg.Bs), dtype=torch.float32, device="cuda")
+    idx = torch.empty((B, T, cfg.K), dtype=torch.int32, device="cuda")
+    out = torch.empty((1, B, T, cfg.Hq, cfg.d_v), dtype=torch.bfloat16, device="cuda")
+    lse = torch.empty((1, B, T, cfg.Hq), dtype=torch.float32, device="cuda")
+
+    def fn():
+        L.lsa_index(d["qI"], d["w"], kbar, mode=L.LSA_INDEX_BLOCKS, N=cfg.N, ctx_len=d["ctx"],
+                    block_size=cfg.Bs, sink=cfg.S, window=cfg.W, scores=cs)
+        L.lsa_select(cs, cfg.n_keep, 0, 0, causal=False, idx=kept)
+        L.lsa_index_select(d["qI"], d["w"], d["kI"], cfg.K, cfg.S, cfg.W, k_scale=d["ks"], ctx_len=d["ctx"],
+                           kept=kept, block_size=cfg.Bs, scores=fs, idx=idx)
+        L.lsa_attend(d["q"], d["k"], d["v"], idx, cfg.tau, out=out, lse=lse)
+    return fn, idx, out, lse
+
+
+def profile_workload(name, steps, warmup):
+    """Plain stream launches of one workload's step (for rocprofv3): c1, c3, c4 or c5 with
+    the separate calls (c3: the hierarchical step), or c2s / c2f (the 128K decode, separate
+    or chained calls, one input replica)."""
+    import torch
+    from synth import config, make_inputs
+    if name in ("c2s", "c2f"):
+        cfg, d, sc, idx, out, lse = c_flat(2)
+        fn = (flat_step if name == "c2s" else fused_step)(cfg, d, sc, idx, out, lse)
+    elif name == "c3":
+        cfg = config(3)
+        fn = hi_step(cfg, upload_workload(make_inputs(cfg), cfg))[0]
+    else:
+        cfg, d, sc, idx, out, lse = c_flat(int(name[1:]))
+        fn = flat_step(cfg, d, sc, idx, out, lse)
+    for _ in range(warmup):
+        fn()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(steps):
+        fn()
+    e1.record()
+    torch.cuda.synchronize()
+    print(json.dumps({"profile_workload": name, "us_per_step": e0.elapsed_time(e1) / steps * 1e3}))
 
 
 def measure_workloads(steps=50):
@@ -179,20 +303,6 @@ def measure_workloads(steps=50):
     import torch
     import long_context_sparse_07_amd as L
     from synth import config, make_inputs
-
-    def bf16(a):
-        return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).view(torch.bfloat16).cuda()
-
-    def upload(inp, cfg):
-        d = {"qI": bf16(inp["qI"]), "w": torch.from_numpy(inp["w"]).cuda(),
-             "ctx": torch.from_numpy(inp["ctx_len"]).cuda(), "q": bf16(inp["q"]), "k": bf16(inp["k"]),
-             "v": bf16(inp["v"]) if inp["v"] is not None else None}
-        if cfg.k_fp8:
-            d["kI"] = torch.from_numpy(inp["kI"]).cuda().view(torch.float8_e4m3fn)
-            d["ks"] = torch.from_numpy(inp["kI_scale"]).cuda()
-        else:
-            d["kI"], d["ks"] = bf16(inp["kI"]), None
-        return d
 
     def graph_us(fn, reps=1):
         # one graph holds `reps` consecutive steps, so that the replay's own launch cost
@@ -230,19 +340,6 @@ def measure_workloads(steps=50):
             res[name] = {"error": f"{type(e).__name__}: {e}"}
         torch.cuda.empty_cache()
 
-    def flat_step(cfg, d, sc, idx, out, lse, layers_out=None):
-        def fn():
-            L.lsa_index_select(d["qI"], d["w"], d["kI"], cfg.K, cfg.S, cfg.W, k_scale=d["ks"], ctx_len=d["ctx"],
-                               scores=sc, idx=idx)
-            L.lsa_attend(d["q"], d["k"], d["v"], idx, cfg.tau, out=out, lse=lse)
-        return fn
-
-    def fused_step(cfg, d, sc, idx, out, lse):
-        # the chained calls: lsa_index (priming the selection), then lsa_select_attend
-        def fn():
-            L.lsa_index_select_attend(d["qI"], d["w"], d["kI"], cfg.K, cfg.S, cfg.W, d["q"], d["k"], d["v"], cfg.tau,
-                                      k_scale=d["ks"], ctx_len=d["ctx"], scores=sc, idx=idx, out=out, lse=lse)
-        return fn
 
     def both(cfg, d, sc, idx, out, lse, reps):
         """Step time of the separate and the chained calls; the step is the faster one."""
@@ -250,15 +347,6 @@ def measure_workloads(steps=50):
         us_ch = graph_us(fused_step(cfg, d, sc, idx, out, lse), reps=reps)
         return min(us_sep, us_ch), {"us_per_step_separate": us_sep, "us_per_step_chained": us_ch}
 
-    def c_flat(cid):
-        cfg = config(cid)
-        d = upload(make_inputs(cfg), cfg)
-        B, T = cfg.B, cfg.T
-        sc = torch.empty((B, T, cfg.N), dtype=torch.float32, device="cuda")
-        idx = torch.empty((B, T, cfg.K), dtype=torch.int32, device="cuda")
-        out = torch.empty((cfg.layers, B, T, cfg.Hq, cfg.d_v), dtype=torch.bfloat16, device="cuda")
-        lse = torch.empty((cfg.layers, B, T, cfg.Hq), dtype=torch.float32, device="cuda")
-        return cfg, d, sc, idx, out, lse
 
     def w1():
         cfg, d, sc, idx, out, lse = c_flat(1)
@@ -301,24 +389,10 @@ def measure_workloads(steps=50):
 
     def w3():
         cfg = config(3)
-        d = upload(make_inputs(cfg), cfg)
+        d = upload_workload(make_inputs(cfg), cfg)
         B, T = cfg.B, cfg.T
         nb = cfg.N // cfg.Bs
-        kbar = L.lsa_block_means(d["kI"], cfg.Bs, k_scale=d["ks"])  # maintained once per block, not per step
-        cs = torch.empty((B, T, nb), dtype=torch.float32, device="cuda")
-        kept = torch.empty((B, T, cfg.n_keep), dtype=torch.int32, device="cuda")
-        fs = torch.empty((B, T, cfg.n_keep * cfg.Bs), dtype=torch.float32, device="cuda")
-        idx = torch.empty((B, T, cfg.K), dtype=torch.int32, device="cuda")
-        out = torch.empty((1, B, T, cfg.Hq, cfg.d_v), dtype=torch.bfloat16, device="cuda")
-        lse = torch.empty((1, B, T, cfg.Hq), dtype=torch.float32, device="cuda")
-
-        def hi():
-            L.lsa_index(d["qI"], d["w"], kbar, mode=L.LSA_INDEX_BLOCKS, N=cfg.N, ctx_len=d["ctx"],
-                        block_size=cfg.Bs, sink=cfg.S, window=cfg.W, scores=cs)
-            L.lsa_select(cs, cfg.n_keep, 0, 0, causal=False, idx=kept)
-            L.lsa_index_select(d["qI"], d["w"], d["kI"], cfg.K, cfg.S, cfg.W, k_scale=d["ks"], ctx_len=d["ctx"],
-                               kept=kept, block_size=cfg.Bs, scores=fs, idx=idx)
-            L.lsa_attend(d["q"], d["k"], d["v"], idx, cfg.tau, out=out, lse=lse)
+        hi, idx, out, lse = hi_step(cfg, d)
         us = graph_us(hi, reps=10)
         sc = torch.empty((B, T, cfg.N), dtype=torch.float32, device="cuda")
         us_flat = graph_us(flat_step(cfg, d, sc, idx, out, lse), reps=10)
@@ -436,7 +510,23 @@ def c2_chain(cfg, reps, dev):
                            k_scale=rp["ks"].data_ptr(), sink=cfg.S, window=cfg.W, scores=scores.data_ptr(),
                            select_ws=ws_sel.data_ptr(), select_ws_bytes=ws_sel.numel(),
                            select_ws_state=L.LSA_WS_UNKNOWN)
+    # the fused indexer + selection (lsa_index_select): the scores are not written
+    ws_is = None
+    for rp, d in zip(reps, descs):
+        di = L.IndexDesc(mode=L.LSA_INDEX_TOKENS, B=B, T=T, N=N, H=cfg.H_I, D=cfg.D_I, q=rp["qI"].data_ptr(),
+                         w=rp["w"].data_ptr(), k=rp["kI"].data_ptr(), k_dtype=L.LSA_FP8_E4M3FN,
+                         k_scale=rp["ks"].data_ptr(), sink=cfg.S, window=cfg.W, scores=None)
+        d.append(di)
+        if ws_is is None:
+            ws_is = torch.empty(max(256, lib.lsa_index_select_workspace_bytes(ctypes.byref(di), cfg.K)),
+                                dtype=torch.uint8, device=dev)
+    is_state = [L.LSA_WS_UNKNOWN]
     first = [True]
+
+    def c_index_select(r):
+        L._check("lsa_index_select", lib.lsa_index_select(ctypes.byref(descs[r][3]), cfg.K, idx.data_ptr(),
+                                                          ws_is.data_ptr(), ws_is.numel(), is_state[0], sptr))
+        is_state[0] = L.LSA_WS_CLEAN  # every call leaves the workspace clean
 
     def c_index(r):
         L._check("lsa_index", lib.lsa_index(ctypes.byref(descs[r][0]), sptr))
@@ -465,10 +555,14 @@ def c2_chain(cfg, reps, dev):
         c_index(r)
         c_fused(r)
 
+    def step_index_select(r):
+        c_index_select(r)
+        c_attend(r)
+
     return types.SimpleNamespace(scores=scores, idx=idx, out=out, lse=lse, stream=stream, lib=lib, descs=descs,
-                                 ws_sel=ws_sel, ws_att=ws_att, c_index=c_index, c_select=c_select,
-                                 c_attend=c_attend, c_fused=c_fused,
-                                 ways={"separate": step, "fused": step_fused})
+                                 ws_sel=ws_sel, ws_att=ws_att, ws_is=ws_is, c_index=c_index, c_select=c_select,
+                                 c_attend=c_attend, c_fused=c_fused, c_index_select=c_index_select,
+                                 ways={"separate": step, "fused": step_fused, "index_select": step_index_select})
 
 
 def main():
@@ -479,6 +573,9 @@ def main():
         sys.exit(2)
     if args.profile_c4_index:
         profile_c4_index(args.steps, args.warmup)
+        return
+    if args.profile_workload:
+        profile_workload(args.profile_workload, args.steps, args.warmup)
         return
     if args.profile_backward:
         import torch
@@ -522,8 +619,11 @@ def main():
     stream, lib, descs, ws_sel, ws_att = ch.stream, ch.lib, ch.descs, ch.ws_sel, ch.ws_att
     c_index, c_select, c_attend = ch.c_index, ch.c_select, ch.c_attend
     step, step_fused = ch.ways["separate"], ch.ways["fused"]
-    step(0)  # the first call clears the selection workspace
+    for fn in ch.ways.values():  # the first calls clear the workspaces
+        fn(0)
     torch.cuda.synchronize()
+    calls = {"separate": "lsa_index, lsa_select, lsa_attend", "fused": "lsa_index, lsa_select_attend",
+             "index_select": "lsa_index_select, lsa_attend"}
 
     def timed(fn, n, warm):
         for i in range(warm):
@@ -537,8 +637,22 @@ def main():
         torch.cuda.synchronize()
         return e0.elapsed_time(e1) / n
 
+    def per_launch(fn, n, warm):
+        """Mean duration of one call: a pair of events on the call's stream around each
+        call (the gaps between calls are not counted)."""
+        for i in range(warm):
+            fn(i % R)
+        torch.cuda.synchronize()
+        ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(n)]
+        for i in range(n):
+            ev[i][0].record(stream)
+            fn(i % R)
+            ev[i][1].record(stream)
+        torch.cuda.synchronize()
+        return sum(a.elapsed_time(b) for a, b in ev) / n
+
     if args.profile_only:
-        ms = timed(step_fused if args.fused else step, args.steps, args.warmup)
+        ms = timed(ch.ways[args.way], args.steps, args.warmup)
         if args.calib_copy:
             # a plain elementwise kernel of known traffic: c = a + b reads 2 GiB, writes 1 GiB
             # (the inputs are 8x the MALL, so they come from HBM)
@@ -548,58 +662,76 @@ def main():
             torch.cuda.synchronize()
             torch.add(x, y, out=z)
             torch.cuda.synchronize()
-        print(json.dumps({"profile_only": True, "ms_per_step_plain": ms}))
+        print(json.dumps({"profile_only": True, "way": args.way, "ms_per_step_plain": ms}))
         return
 
-    # plain stream launches
-    ms_plain = timed(step, args.steps, args.warmup)
-    ms_plain_fused = timed(step_fused, args.steps, args.warmup)
-    # per-call times (live, same stream, same replica rotation). A primed selection
-    # consumes what the indexer left, so it is timed as (index + select) - index; the
-    # workspace is cleared after the indexer-only loop, which leaves it unbalanced.
-    ms_index = timed(c_index, args.steps, args.warmup)
+    # plain stream launches, every way
+    ms_plain = {name: timed(fn, args.steps, args.warmup) for name, fn in ch.ways.items()}
+    # per-call times (live, same stream, same replica rotation, one event pair per call).
+    # A primed selection consumes what the indexer left, so it is timed as (index +
+    # select) - index; the workspace is cleared after the indexer-only loop, which leaves
+    # it unbalanced.
+    ms_index = per_launch(c_index, args.steps, args.warmup)
     L.lsa_workspace_clear(ws_sel)
-    ms_index_select = timed(lambda r: (c_index(r), c_select(r)), args.steps, args.warmup)
-    ms_select = ms_index_select - ms_index
-    ms_attend = timed(c_attend, args.steps, args.warmup)
-    ms_select_attend = timed(step_fused, args.steps, args.warmup) - ms_index
+    ms_select = per_launch(lambda r: (c_index(r), c_select(r)), args.steps, args.warmup) - ms_index
+    ms_attend = per_launch(c_attend, args.steps, args.warmup)
+    ms_index_select = per_launch(ch.c_index_select, args.steps, args.warmup)
 
-    # HIP graphs: one captured step per replica
-    ms_graph = ms_graph_fused = None
+    # HIP graphs: one captured step per replica and way (a way whose calls cannot be
+    # captured is left out and named in extra)
+    ms_graph, graph_errors = {}, {}
     if not args.no_graph:
-        graphs, graphs_fused = [], []
         side = torch.cuda.Stream()
         side.wait_stream(stream)
-        with torch.cuda.stream(side):
-            gptr = ctypes.c_void_p(side.cuda_stream)
-            for r in range(R):
-                g = torch.cuda.CUDAGraph()
-                with torch.cuda.graph(g, stream=side):
-                    lib.lsa_index(ctypes.byref(descs[r][0]), gptr)
-                    lib.lsa_select(ctypes.byref(descs[r][1]), ws_sel.data_ptr(), ws_sel.numel(), gptr)
-                    lib.lsa_attend(ctypes.byref(descs[r][2]), ws_att.data_ptr(), ws_att.numel(), gptr)
-                graphs.append(g)
-                g = torch.cuda.CUDAGraph()
-                with torch.cuda.graph(g, stream=side):
-                    lib.lsa_index(ctypes.byref(descs[r][0]), gptr)
-                    lib.lsa_select_attend(ctypes.byref(descs[r][1]), ctypes.byref(descs[r][2]), ws_sel.data_ptr(),
-                                          ws_sel.numel(), ws_att.data_ptr(), ws_att.numel(), gptr)
-                graphs_fused.append(g)
-        stream.wait_stream(side)
-        torch.cuda.synchronize()
-        ms_graph = timed(lambda r: graphs[r].replay(), args.steps, args.warmup)
-        ms_graph_fused = timed(lambda r: graphs_fused[r].replay(), args.steps, args.warmup)
+        for name in ch.ways:
+            graphs = []
+            try:
+                with torch.cuda.stream(side):
+                    gptr = ctypes.c_void_p(side.cuda_stream)
+                    for r in range(R):
+                        g = torch.cuda.CUDAGraph()
+                        with torch.cuda.graph(g, stream=side):
+                            d = descs[r]
+                            if name == "separate":
+                                lib.lsa_index(ctypes.byref(d[0]), gptr)
+                                lib.lsa_select(ctypes.byref(d[1]), ws_sel.data_ptr(), ws_sel.numel(), gptr)
+                                lib.lsa_attend(ctypes.byref(d[2]), ws_att.data_ptr(), ws_att.numel(), gptr)
+                            elif name == "fused":
+                                lib.lsa_index(ctypes.byref(d[0]), gptr)
+                                lib.lsa_select_attend(ctypes.byref(d[1]), ctypes.byref(d[2]), ws_sel.data_ptr(),
+                                                      ws_sel.numel(), ws_att.data_ptr(), ws_att.numel(), gptr)
+                            else:
+                                rc = lib.lsa_index_select(ctypes.byref(d[3]), cfg.K, ch.idx.data_ptr(),
+                                                          ch.ws_is.data_ptr(), ch.ws_is.numel(), L.LSA_WS_CLEAN, gptr)
+                                if rc != 0:
+                                    raise L.LSAError("lsa_index_select", rc, lib.lsa_last_error().decode())
+                                lib.lsa_attend(ctypes.byref(d[2]), ws_att.data_ptr(), ws_att.numel(), gptr)
+                        graphs.append(g)
+                stream.wait_stream(side)
+                torch.cuda.synchronize()
+                ms_graph[name] = timed(lambda r: graphs[r].replay(), args.steps, args.warmup)
+            except Exception as e:  # noqa: BLE001 (reported, never hides the headline)
+                graph_errors[name] = f"{type(e).__name__}: {e}"[:300]
+                torch.cuda.synchronize()
+                for fn in ch.ways.values():  # the workspaces' state is unknown after a failed capture
+                    fn(0)
+                torch.cuda.synchronize()
 
     # headline: the fastest of the ways of running the same step (all are reported)
-    ways = {("stream launches", "separate"): ms_plain, ("stream launches", "fused"): ms_plain_fused}
-    if ms_graph is not None:
-        ways[("hip graph replay", "separate")] = ms_graph
-        ways[("hip graph replay", "fused")] = ms_graph_fused
+    ways = {("stream launches", k): v for k, v in ms_plain.items()}
+    ways.update({("hip graph replay", k): v for k, v in ms_graph.items()})
     (launch, path), ms = min(ways.items(), key=lambda kv: kv[1])
     idx_b, gat_b, small_b = algorithmic_bytes(cfg)
     step_bytes = idx_b + gat_b + small_b
-    achieved_index = idx_b / (ms_index * 1e-3) / 1e9
-    traffic = pmc_traffic(idx_b)
+    if path == "index_select":
+        rk, ms_rk = "index_tokens_kernel SEL (lsa_index_select: fp8 key sweep and the selection in one launch)", \
+            ms_index_select
+        traffic = pmc_traffic("index_select_c2_pmc.json", ("index.hip", "common.cuh", "fuse_select.cuh",
+                                                            "select_core.cuh"))
+    else:
+        rk, ms_rk = "index_tokens_kernel (lsa_index, fp8 keys)", ms_index
+        traffic = pmc_traffic("index_fp8_c2_pmc.json", ("index.hip", "common.cuh"))
+    achieved = idx_b / (ms_rk * 1e-3) / 1e9
     res = {
         "metric": METRIC,
         "value": 1e3 / ms,
@@ -616,18 +748,18 @@ def main():
         "config": {"workload": "c2 LSA decode: B=8, 128K context, T=1, indexer 64x128 fp8-e4m3 + fp32 scale, "
                                "MLA 64 heads 576/512 bf16, K=2048 (sink 64, window 512)",
                    "batch": B, "context": N, "query_tokens": T, "topk": cfg.K,
-                   "launch": launch,
-                   "calls": "lsa_index, lsa_select_attend" if path == "fused" else "lsa_index, lsa_select, lsa_attend",
-                   "input_replicas": R},
-        "roofline": {"bound": "hbm", "kernel": "index_tokens_kernel (lsa_index, fp8 keys)",
-                     "achieved": achieved_index, "peak": PEAK_HBM_GBS, "unit": "GB/s",
-                     "frac": achieved_index / PEAK_HBM_GBS, "traffic": traffic},
+                   "launch": launch, "calls": calls[path], "input_replicas": R},
+        "roofline": {"bound": "hbm", "kernel": rk, "achieved": achieved, "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                     "frac": achieved / PEAK_HBM_GBS, "traffic": traffic},
         "extra": {"step_algorithmic_bytes": step_bytes, "step_hbm_gbs": step_bytes / (ms * 1e-3) / 1e9,
                   "step_frac_of_peak": step_bytes / (ms * 1e-3) / 1e9 / PEAK_HBM_GBS,
-                  "ms_per_step_plain": ms_plain, "ms_per_step_graph": ms_graph,
-                  "ms_per_step_plain_fused": ms_plain_fused, "ms_per_step_graph_fused": ms_graph_fused,
+                  "ms_per_step_plain": ms_plain, "ms_per_step_graph": ms_graph, "graph_errors": graph_errors,
                   "ms_index": ms_index, "ms_select": ms_select, "ms_attend": ms_attend,
-                  "ms_select_attend_fused": ms_select_attend,
+                  "ms_index_select": ms_index_select,
+                  "index_gbs": idx_b / (ms_index * 1e-3) / 1e9,
+                  "index_select_gbs": idx_b / (ms_index_select * 1e-3) / 1e9,
+                  "kv_gather_gbs": gat_b / (ms_attend * 1e-3) / 1e9,
+                  "attend_traffic": pmc_attend_traffic(),
                   "index_bytes_per_launch": idx_b, "gather_bytes": gat_b},
     }
     if not args.no_workloads:

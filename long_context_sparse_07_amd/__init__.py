@@ -117,6 +117,10 @@ def lib():
         L.lsa_select.restype = c_int32
         L.lsa_attend.argtypes = [POINTER(AttendDesc), c_void_p, c_size_t, c_void_p]
         L.lsa_attend.restype = c_int32
+        L.lsa_index_select.argtypes = [POINTER(IndexDesc), c_int32, c_void_p, c_void_p, c_size_t, c_int32, c_void_p]
+        L.lsa_index_select.restype = c_int32
+        L.lsa_index_select_workspace_bytes.argtypes = [POINTER(IndexDesc), c_int32]
+        L.lsa_index_select_workspace_bytes.restype = c_size_t
         L.lsa_attend_noalloc.argtypes = [POINTER(AttendDesc), c_void_p]
         L.lsa_attend_noalloc.restype = c_int32
         L.lsa_select_attend.argtypes = [POINTER(SelectDesc), POINTER(AttendDesc), c_void_p, c_size_t, c_void_p,
@@ -267,18 +271,36 @@ def lsa_select(scores, K, sink=0, window=0, *, N=None, ctx_len=None, kept=None, 
 
 
 def lsa_index_select(q, w, k, K, sink, window, *, k_scale=None, ctx_len=None, kept=None, block_size=0,
-                     scores=None, idx=None, q_fp8=False, stream=None):
-    """lsa_index with a primed selection workspace, then lsa_select on its scores
-    (causal token selection): the same result as the two calls made separately, without
-    the selection's first pass over the scores. Returns (scores, idx)."""
+                     scores=None, idx=None, q_fp8=False, with_scores=True, workspace=None, stream=None):
+    """The indexer's scores and the causal selection from them (lsa_index_select): one C call
+    (one launch where the shape allows) for flat rows; with a kept map (HI fine stage),
+    lsa_index priming the selection workspace, then lsa_select on its scores. Returns
+    (scores, idx); scores is None when with_scores is False and none was given (flat rows:
+    the scores are then not written)."""
     import torch
     B, T = q.shape[0], q.shape[1]
     N = k.shape[1]
     n_cols = kept.shape[-1] * block_size if kept is not None else N
-    if scores is None:
+    if scores is None and (with_scores or kept is not None):
         scores = torch.empty((B, T, n_cols), dtype=torch.float32, device=q.device)
     if idx is None:
         idx = torch.empty((B, T, K), dtype=torch.int32, device=q.device)
+    if kept is None:
+        H, D = q.shape[2], q.shape[3]
+        d = IndexDesc(mode=LSA_INDEX_TOKENS, B=B, T=T, N=N, ctx_len=_ptr(ctx_len), H=H, D=D, q=_ptr(q), w=_ptr(w),
+                      k=_ptr(k), k_dtype=_kdtype(k), k_scale=_ptr(k_scale), sink=sink, window=window,
+                      scores=_ptr(scores), q_dtype=LSA_FP8_E4M3FN if q_fp8 else 0)
+        need = lib().lsa_index_select_workspace_bytes(ctypes.byref(d), K)
+        if workspace is not None:
+            ws, ent, state = workspace, None, LSA_WS_UNKNOWN
+        else:
+            ent = _workspace("index_select", need, q.device, (B, T, N, H, D, d.k_dtype, d.q_dtype, scores is None))
+            ws, state = ent[0], (LSA_WS_CLEAN if ent[1] else LSA_WS_UNKNOWN)
+        _check("lsa_index_select", lib().lsa_index_select(ctypes.byref(d), K, idx.data_ptr(), ws.data_ptr(),
+                                                          ws.numel(), state, _stream(stream)))
+        if ent is not None:
+            ent[1] = True
+        return scores, idx
     d = _select_desc(scores, K, sink, window, N, ctx_len, kept, block_size, True, idx)
     need = lib().lsa_select_workspace_bytes(ctypes.byref(d))
     ent = _workspace("select", need, q.device, (B, T, n_cols))

@@ -57,36 +57,102 @@ const char *lsa_last_error(void) { return g_err; }
 
 // ----------------------------------------------------------------------------- index
 
+// lsa_index with a selection workspace: the scores, and the selection histogram from the
+// indexer epilogue when the kernel has one query per workgroup, else from the
+// selection's own histogram pass.
+static int32_t index_primed(const lsa_index_desc *d, lsa::IndexTokensArgs a, void *select_ws, bool ws_clean,
+                            hipStream_t s, const char *fn) {
+    const bool hi = d->kept != nullptr;
+    lsa::SelectArgs sa{};
+    sa.B = d->B;
+    sa.T = d->T;
+    sa.N = d->N;
+    sa.ctx_len = d->ctx_len;
+    sa.scores = a.scores;
+    sa.n_cols = a.n_out;
+    sa.kept = d->kept;
+    sa.n_keep = a.n_keep;
+    sa.block_size = hi ? d->block_size : 1;
+    sa.K = 0x3FFFFFFF;  // the histogram counts every candidate
+    sa.sink = d->sink;
+    sa.window = d->window;
+    sa.causal = true;
+    sa.ws_clean = ws_clean;
+    sa.vec = (a.n_out & 3) == 0;  // scores are 16-byte aligned
+    hipError_t e;
+    if (lsa::index_tokens_fused_hist(d->H, d->T, hi)) {
+        if (!sa.ws_clean) {
+            e = lsa::launch_clear(select_ws, lsa::select_zero_bytes(d->B * d->T), s);
+            if (e != hipSuccess) return hip_status(e, fn);
+        }
+        a.sel_hist = reinterpret_cast<uint32_t *>(select_ws);
+        a.sink = d->sink;
+        a.window = d->window;
+        return hip_status(lsa::launch_index_tokens(a, s), fn);
+    }
+    e = lsa::launch_index_tokens(a, s);
+    if (e != hipSuccess) return hip_status(e, fn);
+    return hip_status(lsa::launch_select_hist(sa, select_ws, s), fn);
+}
+
+// Checks of a TOKENS index descriptor shared by lsa_index and lsa_index_select (pointers
+// q, w, k; sizes; key and query types); fills the kernel arguments.
+static int32_t index_tokens_check(const lsa_index_desc *d, lsa::IndexTokensArgs &a, const char *fn) {
+    if (!d->q || !d->w || !d->k) return fail(LSA_E_NULL, "%s: q, w and k are required", fn);
+    if (d->B < 1 || d->T < 1 || d->N < 1 || d->H < 1 || d->D < 1)
+        return fail(LSA_E_SHAPE, "%s: B, T, N, H, D must be >= 1 (got %d %d %d %d %d)", fn, d->B, d->T, d->N, d->H, d->D);
+    if (d->T > d->N) return fail(LSA_E_SHAPE, "%s: T=%d exceeds N=%d", fn, d->T, d->N);
+    if (!aligned16(d->q) || !aligned16(d->k) || !aligned4(d->w) || (d->scores && !aligned16(d->scores)))
+        return fail(LSA_E_ALIGN, "%s: q, k, scores must be 16-byte aligned", fn);
+    if (d->B > kMaxGridY) return fail(LSA_E_UNSUPPORTED, "%s: B=%d too large", fn, d->B);
+    if (d->k_dtype != LSA_BF16 && d->k_dtype != LSA_FP8_E4M3FN)
+        return fail(LSA_E_DTYPE, "%s: TOKENS keys must be bf16 or fp8-e4m3fn (got %d)", fn, d->k_dtype);
+    const bool fp8 = d->k_dtype == LSA_FP8_E4M3FN;
+    if (fp8 && !d->k_scale) return fail(LSA_E_NULL, "%s: fp8 keys need k_scale", fn);
+    const bool hi = d->kept != nullptr;
+    if (hi) {
+        if (d->n_keep < 1 || d->block_size < 1)
+            return fail(LSA_E_SHAPE, "%s: HI fine stage needs n_keep >= 1 and block_size >= 1", fn);
+        if ((int64_t)d->n_keep * d->block_size > INT32_MAX / 2)
+            return fail(LSA_E_SHAPE, "%s: n_keep * block_size too large", fn);
+        if (d->T > kMaxGridY) return fail(LSA_E_UNSUPPORTED, "%s: T=%d too large", fn, d->T);
+    }
+    if (!lsa::index_tokens_supported(d->H, d->D, hi))
+        return fail(LSA_E_UNSUPPORTED, "%s: no token kernel for H=%d D=%d%s", fn, d->H, d->D, hi ? " (HI)" : "");
+    if (d->q_dtype != 0 && d->q_dtype != LSA_BF16 && d->q_dtype != LSA_FP8_E4M3FN)
+        return fail(LSA_E_DTYPE, "%s: q_dtype must be 0, LSA_BF16 or LSA_FP8_E4M3FN (got %d)", fn, d->q_dtype);
+    const bool qf8 = d->q_dtype == LSA_FP8_E4M3FN;
+    if (qf8 && (!fp8 || d->D != 128)) return fail(LSA_E_UNSUPPORTED, "%s: fp8 queries need fp8 keys and D=128", fn);
+    a = lsa::IndexTokensArgs{};
+    a.B = d->B;
+    a.T = d->T;
+    a.N = d->N;
+    a.H = d->H;
+    a.D = d->D;
+    a.ctx_len = d->ctx_len;
+    a.q = reinterpret_cast<const uint16_t *>(d->q);
+    a.w = d->w;
+    a.k = d->k;
+    a.fp8 = fp8;
+    a.qf8 = qf8;
+    a.k_scale = fp8 ? d->k_scale : nullptr;
+    a.kept = d->kept;
+    a.n_keep = hi ? d->n_keep : 0;
+    a.block_size = hi ? d->block_size : 0;
+    a.scores = d->scores;
+    a.n_out = hi ? d->n_keep * d->block_size : d->N;
+    return LSA_OK;
+}
+
 int32_t lsa_index(const lsa_index_desc *d, void *stream) {
     if (!d) return fail(LSA_E_NULL, "lsa_index: desc is NULL");
     if (!d->q || !d->w || !d->k || !d->scores) return fail(LSA_E_NULL, "lsa_index: q, w, k and scores are required");
-    if (d->B < 1 || d->T < 1 || d->N < 1 || d->H < 1 || d->D < 1)
-        return fail(LSA_E_SHAPE, "lsa_index: B, T, N, H, D must be >= 1 (got %d %d %d %d %d)", d->B, d->T, d->N, d->H, d->D);
-    if (d->T > d->N) return fail(LSA_E_SHAPE, "lsa_index: T=%d exceeds N=%d", d->T, d->N);
-    if (!aligned16(d->q) || !aligned16(d->k) || !aligned4(d->w) || !aligned16(d->scores))
-        return fail(LSA_E_ALIGN, "lsa_index: q, k, scores must be 16-byte aligned");
-    if (d->B > kMaxGridY) return fail(LSA_E_UNSUPPORTED, "lsa_index: B=%d too large", d->B);
     hipStream_t s = reinterpret_cast<hipStream_t>(stream);
     if (d->mode == LSA_INDEX_TOKENS) {
-        if (d->k_dtype != LSA_BF16 && d->k_dtype != LSA_FP8_E4M3FN)
-            return fail(LSA_E_DTYPE, "lsa_index: TOKENS keys must be bf16 or fp8-e4m3fn (got %d)", d->k_dtype);
-        const bool fp8 = d->k_dtype == LSA_FP8_E4M3FN;
-        if (fp8 && !d->k_scale) return fail(LSA_E_NULL, "lsa_index: fp8 keys need k_scale");
+        lsa::IndexTokensArgs a;
+        int32_t rc = index_tokens_check(d, a, "lsa_index");
+        if (rc != LSA_OK) return rc;
         const bool hi = d->kept != nullptr;
-        if (hi) {
-            if (d->n_keep < 1 || d->block_size < 1)
-                return fail(LSA_E_SHAPE, "lsa_index: HI fine stage needs n_keep >= 1 and block_size >= 1");
-            if ((int64_t)d->n_keep * d->block_size > INT32_MAX / 2)
-                return fail(LSA_E_SHAPE, "lsa_index: n_keep * block_size too large");
-            if (d->T > kMaxGridY) return fail(LSA_E_UNSUPPORTED, "lsa_index: T=%d too large", d->T);
-        }
-        if (!lsa::index_tokens_supported(d->H, d->D, hi))
-            return fail(LSA_E_UNSUPPORTED, "lsa_index: no token kernel for H=%d D=%d%s", d->H, d->D, hi ? " (HI)" : "");
-        if (d->q_dtype != 0 && d->q_dtype != LSA_BF16 && d->q_dtype != LSA_FP8_E4M3FN)
-            return fail(LSA_E_DTYPE, "lsa_index: q_dtype must be 0, LSA_BF16 or LSA_FP8_E4M3FN (got %d)", d->q_dtype);
-        const bool qf8 = d->q_dtype == LSA_FP8_E4M3FN;
-        if (qf8 && (!fp8 || d->D != 128))
-            return fail(LSA_E_UNSUPPORTED, "lsa_index: fp8 queries need fp8 keys and D=128");
         if (d->select_ws) {
             if (d->sink < 0 || d->window < 0) return fail(LSA_E_SHAPE, "lsa_index: sink and window must be >= 0");
             if (d->select_ws_state != LSA_WS_UNKNOWN && d->select_ws_state != LSA_WS_CLEAN)
@@ -100,59 +166,17 @@ int32_t lsa_index(const lsa_index_desc *d, void *stream) {
             if ((reinterpret_cast<uintptr_t>(d->select_ws) & 255u) != 0)
                 return fail(LSA_E_ALIGN, "lsa_index: select_ws not 256-byte aligned");
         }
-        lsa::IndexTokensArgs a{};
-        a.B = d->B;
-        a.T = d->T;
-        a.N = d->N;
-        a.H = d->H;
-        a.D = d->D;
-        a.ctx_len = d->ctx_len;
-        a.q = reinterpret_cast<const uint16_t *>(d->q);
-        a.w = d->w;
-        a.k = d->k;
-        a.fp8 = fp8;
-        a.qf8 = qf8;
-        a.k_scale = fp8 ? d->k_scale : nullptr;
-        a.kept = d->kept;
-        a.n_keep = hi ? d->n_keep : 0;
-        a.block_size = hi ? d->block_size : 0;
-        a.scores = d->scores;
-        a.n_out = hi ? d->n_keep * d->block_size : d->N;
         if (!d->select_ws) return hip_status(lsa::launch_index_tokens(a, s), "lsa_index");
-        // priming: the selection histogram, from the indexer epilogue when the kernel has
-        // one query per workgroup, else from the selection's own histogram pass
-        lsa::SelectArgs sa{};
-        sa.B = d->B;
-        sa.T = d->T;
-        sa.N = d->N;
-        sa.ctx_len = d->ctx_len;
-        sa.scores = d->scores;
-        sa.n_cols = a.n_out;
-        sa.kept = d->kept;
-        sa.n_keep = a.n_keep;
-        sa.block_size = hi ? d->block_size : 1;
-        sa.K = 0x3FFFFFFF;  // the histogram counts every candidate
-        sa.sink = d->sink;
-        sa.window = d->window;
-        sa.causal = true;
-        sa.ws_clean = d->select_ws_state == LSA_WS_CLEAN;
-        sa.vec = (a.n_out & 3) == 0;  // scores are 16-byte aligned
-        hipError_t e;
-        if (lsa::index_tokens_fused_hist(d->H, d->T, hi)) {
-            if (!sa.ws_clean) {
-                e = lsa::launch_clear(d->select_ws, lsa::select_zero_bytes(d->B * d->T), s);
-                if (e != hipSuccess) return hip_status(e, "lsa_index");
-            }
-            a.sel_hist = reinterpret_cast<uint32_t *>(d->select_ws);
-            a.sink = d->sink;
-            a.window = d->window;
-            return hip_status(lsa::launch_index_tokens(a, s), "lsa_index");
-        }
-        e = lsa::launch_index_tokens(a, s);
-        if (e != hipSuccess) return hip_status(e, "lsa_index");
-        return hip_status(lsa::launch_select_hist(sa, d->select_ws, s), "lsa_index");
+        return index_primed(d, a, d->select_ws, d->select_ws_state == LSA_WS_CLEAN, s, "lsa_index");
     }
     if (d->mode == LSA_INDEX_BLOCKS) {
+        if (d->B < 1 || d->T < 1 || d->N < 1 || d->H < 1 || d->D < 1)
+            return fail(LSA_E_SHAPE, "lsa_index: B, T, N, H, D must be >= 1 (got %d %d %d %d %d)", d->B, d->T, d->N, d->H,
+                        d->D);
+        if (d->T > d->N) return fail(LSA_E_SHAPE, "lsa_index: T=%d exceeds N=%d", d->T, d->N);
+        if (!aligned16(d->q) || !aligned16(d->k) || !aligned4(d->w) || !aligned16(d->scores))
+            return fail(LSA_E_ALIGN, "lsa_index: q, k, scores must be 16-byte aligned");
+        if (d->B > kMaxGridY) return fail(LSA_E_UNSUPPORTED, "lsa_index: B=%d too large", d->B);
         if (d->k_dtype != LSA_F32) return fail(LSA_E_DTYPE, "lsa_index: BLOCKS mode reads fp32 block means");
         if (d->block_size < 1 || d->n_blocks < 1 || (int64_t)d->n_blocks * d->block_size > d->N)
             return fail(LSA_E_SHAPE, "lsa_index: BLOCKS needs block_size >= 1, 1 <= n_blocks <= N / block_size");
@@ -269,6 +293,103 @@ int32_t lsa_select(const lsa_select_desc *d, void *ws, size_t ws_bytes, void *st
         return fail(LSA_E_WORKSPACE, "lsa_select: workspace of %zu bytes needed, %zu given", need, ws_bytes);
     if ((reinterpret_cast<uintptr_t>(ws) & 255u) != 0) return fail(LSA_E_ALIGN, "lsa_select: workspace not 256-byte aligned");
     return hip_status(lsa::launch_select(a, ws, reinterpret_cast<hipStream_t>(stream)), "lsa_select");
+}
+
+// ----------------------------------------------------------------------------- index + select
+
+// Checks of lsa_index_select's arguments; fills the indexer arguments and the plan (fused
+// launch or not) and the workspace size.
+static int32_t index_select_check(const lsa_index_desc *d, int32_t K, lsa::IndexTokensArgs &a, bool &fused, int &nc,
+                                  int &chunk, size_t &ws_need) {
+    if (!d) return fail(LSA_E_NULL, "lsa_index_select: desc is NULL");
+    if (d->mode != LSA_INDEX_TOKENS) return fail(LSA_E_UNSUPPORTED, "lsa_index_select: TOKENS mode only");
+    if (d->kept) return fail(LSA_E_UNSUPPORTED, "lsa_index_select: no kept map (call lsa_index, then lsa_select)");
+    int32_t rc = index_tokens_check(d, a, "lsa_index_select");
+    if (rc != LSA_OK) return rc;
+    if (K < 1 || d->sink < 0 || d->window < 0 || (int64_t)d->sink + d->window > K)
+        return fail(LSA_E_BUDGET, "lsa_index_select: need K >= 1 and 0 <= sink + window <= K (K=%d sink=%d window=%d)",
+                    K, d->sink, d->window);
+    if (K > 4096) return fail(LSA_E_UNSUPPORTED, "lsa_index_select: K=%d above 4096", K);
+    if ((int64_t)d->B * d->T > kMaxGridY) return fail(LSA_E_UNSUPPORTED, "lsa_index_select: B*T too large");
+    const int rows = d->B * d->T;
+    fused = lsa::index_select_plan(d->B, d->T, d->N, d->H, d->D, a.fp8, a.qf8, nc, chunk);
+    if (fused) {
+        ws_need = lsa::index_select_workspace_bytes(rows, nc, chunk);
+    } else {  // the indexer (priming) and the selection; scores in the workspace when not asked for
+        ws_need = lsa::select_workspace_bytes(rows, d->N, false);
+        if (!d->scores) ws_need += (size_t)rows * d->N * 4 + 256;
+    }
+    return LSA_OK;
+}
+
+size_t lsa_index_select_workspace_bytes(const lsa_index_desc *d, int32_t K) {
+    lsa::IndexTokensArgs a;
+    bool fused;
+    int nc = 0, chunk = 0;
+    size_t need = 0;
+    if (index_select_check(d, K, a, fused, nc, chunk, need) != LSA_OK) return 0;
+    return need;
+}
+
+int32_t lsa_index_select(const lsa_index_desc *d, int32_t K, int32_t *idx, void *ws, size_t ws_bytes,
+                         int32_t ws_state, void *stream) {
+    lsa::IndexTokensArgs a;
+    bool fused;
+    int nc = 0, chunk = 0;
+    size_t need = 0;
+    int32_t rc = index_select_check(d, K, a, fused, nc, chunk, need);
+    if (rc != LSA_OK) return rc;
+    if (!idx) return fail(LSA_E_NULL, "lsa_index_select: idx is required");
+    if (!aligned4(idx)) return fail(LSA_E_ALIGN, "lsa_index_select: misaligned idx");
+    if (ws_state != LSA_WS_UNKNOWN && ws_state != LSA_WS_CLEAN)
+        return fail(LSA_E_SHAPE, "lsa_index_select: workspace_state must be LSA_WS_UNKNOWN or LSA_WS_CLEAN");
+    if (!ws || ws_bytes < need)
+        return fail(LSA_E_WORKSPACE, "lsa_index_select: workspace of %zu bytes needed, %zu given", need, ws_bytes);
+    if ((reinterpret_cast<uintptr_t>(ws) & 255u) != 0)
+        return fail(LSA_E_ALIGN, "lsa_index_select: workspace not 256-byte aligned");
+    hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+    const int rows = d->B * d->T;
+    if (fused) {
+        hipError_t e;
+        if (ws_state != LSA_WS_CLEAN) {
+            e = lsa::launch_clear(ws, lsa::index_select_zero_bytes(rows), s);
+            if (e != hipSuccess) return hip_status(e, "lsa_index_select");
+        }
+        lsa::FusedSelArgs f = lsa::index_select_carve(ws, rows, nc, chunk);
+        f.K = K;
+        f.sink = d->sink;
+        f.window = d->window;
+        f.idx = idx;
+        f.write_scores = d->scores != nullptr;
+        a.sel_hist = f.hist;
+        a.sink = d->sink;
+        a.window = d->window;
+        return hip_status(lsa::launch_index_select(a, f, s), "lsa_index_select");
+    }
+    // not fusable here: lsa_index priming the selection workspace, then lsa_select
+    void *sel_ws = ws;
+    if (!a.scores) {
+        const size_t sel_bytes = lsa::select_workspace_bytes(rows, d->N, false);
+        a.scores = reinterpret_cast<float *>((reinterpret_cast<uintptr_t>(ws) + sel_bytes + 255) & ~(uintptr_t)255);
+    }
+    rc = index_primed(d, a, sel_ws, ws_state == LSA_WS_CLEAN, s, "lsa_index_select");
+    if (rc != LSA_OK) return rc;
+    lsa::SelectArgs sa{};
+    sa.B = d->B;
+    sa.T = d->T;
+    sa.N = d->N;
+    sa.ctx_len = d->ctx_len;
+    sa.scores = a.scores;
+    sa.n_cols = d->N;
+    sa.block_size = 1;
+    sa.K = K;
+    sa.sink = d->sink;
+    sa.window = d->window;
+    sa.causal = true;
+    sa.primed = true;
+    sa.vec = (d->N & 3) == 0;
+    sa.idx = idx;
+    return hip_status(lsa::launch_select(sa, sel_ws, s), "lsa_index_select");
 }
 
 // ----------------------------------------------------------------------------- attend

@@ -275,6 +275,81 @@ __device__ uint64_t radix_kth(const Src &src, uint32_t need, uint64_t pref, int 
     return pref;
 }
 
+// A radix source over a tie list read through an accessor (LDS array, or the workspace
+// read with coherent loads).
+template <class Get>
+struct FnSrc {
+    Get g;
+    int n;
+    __device__ int size() const { return n; }
+    __device__ bool get(int i, uint64_t &c) const {
+        c = g(i);
+        return true;
+    }
+};
+
+// The smallest composite to take from the tie list of threshold bin b1 (nl entries read by
+// get(i)), so that the entries >= it are the need1 largest (1 <= need1 <= nl): a
+// second-level histogram of the next 12 key bits (h: kB2 words, zeroed by the caller,
+// transposed as the sliced resolve stores it), then the final (b1, b2) group ranked
+// directly when small or by radix passes. Returns 0 when every tie is taken.
+template <int NT, class Get>
+__device__ uint64_t tie_threshold(Get get, uint32_t nl, uint32_t need1, uint32_t b1, uint32_t *h, uint32_t *h256,
+                                  uint32_t *scr) {
+    const int tid = threadIdx.x;
+    constexpr int PER = kB2 / NT;  // second-level bins per thread
+    auto hslot = [](int bin) {     // transposed slot of a second-level bin
+        const int rk = kB2 - 1 - bin;
+        return (rk % PER) * NT + rk / PER;
+    };
+    uint64_t thr = ~(uint64_t)0;
+    if (tid == 0) scr[24] = 0;
+    for (uint32_t i = tid; i < nl; i += NT) atomicAdd(&h[hslot((int)(((uint32_t)(get(i) >> 32) >> kL2Shift) & (kB2 - 1)))], 1u);
+    __syncthreads();
+    uint32_t v2[PER];
+#pragma unroll
+    for (int e = 0; e < PER; ++e) v2[e] = h[e * NT + tid];
+    const BinPick p2 = pick_bin<NT, PER>(v2, need1, scr);
+    if (p2.mode == 1) {
+        thr = 0;  // every tie
+    } else if (p2.mode == 2) {
+        const int b2 = p2.bin;
+        const uint32_t n2 = h[hslot(b2)];
+        const uint32_t need2 = need1 - p2.above;  // wanted from the (b1, b2) group
+        const uint64_t pre = (uint64_t)((b1 << kSelShift) | ((uint32_t)b2 << kL2Shift)) << 32;
+        __syncthreads();  // h is reused below
+        if (need2 == n2) {
+            thr = pre;  // the whole group
+        } else if (n2 <= (uint32_t)kTiny) {
+            uint64_t *tiny = reinterpret_cast<uint64_t *>(h);
+            for (uint32_t i = tid; i < nl; i += NT) {
+                const uint64_t c = get(i);
+                if ((c >> kGrpShift) == (pre >> kGrpShift)) {
+                    const uint32_t slot = atomicAdd(&scr[24], 1u);
+                    if (slot < (uint32_t)kTiny) tiny[slot] = c;
+                }
+            }
+            __syncthreads();
+            const uint32_t nt = min(scr[24], (uint32_t)kTiny);
+            for (uint32_t i = tid; i < nt; i += NT) {
+                const uint64_t c = tiny[i];
+                uint32_t rank = 0;  // composites are unique
+                for (uint32_t j = 0; j < nt; ++j) rank += tiny[j] > c;
+                if (rank == need2 - 1) {
+                    scr[20] = (uint32_t)c;
+                    scr[21] = (uint32_t)(c >> 32);
+                }
+            }
+            __syncthreads();
+            thr = ((uint64_t)scr[21] << 32) | scr[20];
+        } else {
+            thr = radix_kth<NT>(FnSrc<Get>{get, (int)nl}, need2, pre, kGrpShift, h256, scr);
+        }
+    }
+    __syncthreads();
+    return thr;
+}
+
 // Copy n 32-bit words global -> LDS with several loads per thread in flight (a plain
 // element loop would wait for each load before its LDS store): U 16-byte loads when
 // both pointers are 16-byte aligned, else 4 U word loads. (Native vector types: arrays
@@ -447,11 +522,6 @@ __device__ void resolve_slice(const SelectArgs &a, const Ws &w, int row, int k0,
             }
         }
     };
-    constexpr int PER = kB2 / NT;  // second-level bins per thread
-    auto hslot = [](int bin) {     // transposed slot of a second-level bin
-        const int rk = kB2 - 1 - bin;
-        return (rk % PER) * NT + rk / PER;
-    };
     if (f0 < f1 && mode == 2) {
         const uint32_t need1 = m > above ? m - above : 0u;
         if (!overflow && ties_lds && nl > (uint32_t)tfirst) {  // uniform
@@ -462,51 +532,7 @@ __device__ void resolve_slice(const SelectArgs &a, const Ws &w, int row, int k0,
         // rank the tie list where it lives (inlined at each call, so that the LDS copy is
         // read with LDS instructions)
         auto rank_and_mark = [&](const uint64_t *tl) __attribute__((always_inline)) {
-            uint64_t thr = ~(uint64_t)0;
-            uint32_t *h = S.h;  // zeroed with the first loads
-            for (uint32_t i = tid; i < nl; i += NT)
-                atomicAdd(&h[hslot((int)(((uint32_t)(tl[i] >> 32) >> kL2Shift) & (kB2 - 1)))], 1u);
-            __syncthreads();
-            uint32_t v2[PER];
-#pragma unroll
-            for (int e = 0; e < PER; ++e) v2[e] = h[e * NT + tid];
-            const BinPick p2 = pick_bin<NT, PER>(v2, need1, scr);
-            if (p2.mode == 1) {
-                thr = 0;  // every tie
-            } else if (p2.mode == 2) {
-                const int b2 = p2.bin;
-                const uint32_t n2 = h[hslot(b2)];
-                const uint32_t need2 = need1 - p2.above;  // wanted from the (b1, b2) group
-                const uint64_t pre = (uint64_t)((b1 << kSelShift) | ((uint32_t)b2 << kL2Shift)) << 32;
-                __syncthreads();  // h is reused below
-                if (need2 == n2) {
-                    thr = pre;  // the whole group
-                } else if (n2 <= (uint32_t)kTiny) {
-                    uint64_t *tiny = reinterpret_cast<uint64_t *>(h);
-                    for (uint32_t i = tid; i < nl; i += NT) {
-                        const uint64_t c = tl[i];
-                        if ((c >> kGrpShift) == (pre >> kGrpShift)) {
-                            const uint32_t slot = atomicAdd(&scr[24], 1u);
-                            if (slot < (uint32_t)kTiny) tiny[slot] = c;
-                        }
-                    }
-                    __syncthreads();
-                    const uint32_t nt = min(scr[24], (uint32_t)kTiny);
-                    for (uint32_t i = tid; i < nt; i += NT) {
-                        const uint64_t c = tiny[i];
-                        uint32_t rank = 0;  // composites are unique
-                        for (uint32_t j = 0; j < nt; ++j) rank += tiny[j] > c;
-                        if (rank == need2 - 1) {
-                            scr[20] = (uint32_t)c;
-                            scr[21] = (uint32_t)(c >> 32);
-                        }
-                    }
-                    __syncthreads();
-                    thr = ((uint64_t)scr[21] << 32) | scr[20];
-                } else {
-                    thr = radix_kth<NT>(ArrSrc{tl, (int)nl}, need2, pre, kGrpShift, S.h256, scr);
-                }
-            }
+            const uint64_t thr = tie_threshold<NT>([&](uint32_t i) { return tl[i]; }, nl, need1, b1, S.h, S.h256, scr);
             mark_all([&](int i) { return tl[i] >= thr ? comp_pos(tl[i]) : -1; }, (int)nl);
         };
         if (!overflow) {
