@@ -41,7 +41,7 @@ def parse():
     ap.add_argument("--no-graph", action="store_true", help="headline from plain stream launches")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--profile-only", action="store_true", help="few plain steps, no graphs (for rocprofv3)")
-    ap.add_argument("--way", default="index_select", choices=["separate", "fused", "index_select"],
+    ap.add_argument("--way", default="fused", choices=["separate", "fused"],
                     help="with --profile-only: which way of running the step")
     ap.add_argument("--no-workloads", action="store_true",
                     help="skip the other configurations' step times (extra.workloads)")
@@ -510,23 +510,7 @@ def c2_chain(cfg, reps, dev):
                            k_scale=rp["ks"].data_ptr(), sink=cfg.S, window=cfg.W, scores=scores.data_ptr(),
                            select_ws=ws_sel.data_ptr(), select_ws_bytes=ws_sel.numel(),
                            select_ws_state=L.LSA_WS_UNKNOWN)
-    # the fused indexer + selection (lsa_index_select): the scores are not written
-    ws_is = None
-    for rp, d in zip(reps, descs):
-        di = L.IndexDesc(mode=L.LSA_INDEX_TOKENS, B=B, T=T, N=N, H=cfg.H_I, D=cfg.D_I, q=rp["qI"].data_ptr(),
-                         w=rp["w"].data_ptr(), k=rp["kI"].data_ptr(), k_dtype=L.LSA_FP8_E4M3FN,
-                         k_scale=rp["ks"].data_ptr(), sink=cfg.S, window=cfg.W, scores=None)
-        d.append(di)
-        if ws_is is None:
-            ws_is = torch.empty(max(256, lib.lsa_index_select_workspace_bytes(ctypes.byref(di), cfg.K)),
-                                dtype=torch.uint8, device=dev)
-    is_state = [L.LSA_WS_UNKNOWN]
     first = [True]
-
-    def c_index_select(r):
-        L._check("lsa_index_select", lib.lsa_index_select(ctypes.byref(descs[r][3]), cfg.K, idx.data_ptr(),
-                                                          ws_is.data_ptr(), ws_is.numel(), is_state[0], sptr))
-        is_state[0] = L.LSA_WS_CLEAN  # every call leaves the workspace clean
 
     def c_index(r):
         L._check("lsa_index", lib.lsa_index(ctypes.byref(descs[r][0]), sptr))
@@ -555,14 +539,10 @@ def c2_chain(cfg, reps, dev):
         c_index(r)
         c_fused(r)
 
-    def step_index_select(r):
-        c_index_select(r)
-        c_attend(r)
-
     return types.SimpleNamespace(scores=scores, idx=idx, out=out, lse=lse, stream=stream, lib=lib, descs=descs,
-                                 ws_sel=ws_sel, ws_att=ws_att, ws_is=ws_is, c_index=c_index, c_select=c_select,
-                                 c_attend=c_attend, c_fused=c_fused, c_index_select=c_index_select,
-                                 ways={"separate": step, "fused": step_fused, "index_select": step_index_select})
+                                 ws_sel=ws_sel, ws_att=ws_att, c_index=c_index, c_select=c_select,
+                                 c_attend=c_attend, c_fused=c_fused,
+                                 ways={"separate": step, "fused": step_fused})
 
 
 def main():
@@ -622,8 +602,7 @@ def main():
     for fn in ch.ways.values():  # the first calls clear the workspaces
         fn(0)
     torch.cuda.synchronize()
-    calls = {"separate": "lsa_index, lsa_select, lsa_attend", "fused": "lsa_index, lsa_select_attend",
-             "index_select": "lsa_index_select, lsa_attend"}
+    calls = {"separate": "lsa_index, lsa_select, lsa_attend", "fused": "lsa_index, lsa_select_attend"}
 
     def timed(fn, n, warm):
         for i in range(warm):
@@ -675,7 +654,6 @@ def main():
     L.lsa_workspace_clear(ws_sel)
     ms_select = per_launch(lambda r: (c_index(r), c_select(r)), args.steps, args.warmup) - ms_index
     ms_attend = per_launch(c_attend, args.steps, args.warmup)
-    ms_index_select = per_launch(ch.c_index_select, args.steps, args.warmup)
 
     # HIP graphs: one captured step per replica and way (a way whose calls cannot be
     # captured is left out and named in extra)
@@ -696,16 +674,10 @@ def main():
                                 lib.lsa_index(ctypes.byref(d[0]), gptr)
                                 lib.lsa_select(ctypes.byref(d[1]), ws_sel.data_ptr(), ws_sel.numel(), gptr)
                                 lib.lsa_attend(ctypes.byref(d[2]), ws_att.data_ptr(), ws_att.numel(), gptr)
-                            elif name == "fused":
+                            else:
                                 lib.lsa_index(ctypes.byref(d[0]), gptr)
                                 lib.lsa_select_attend(ctypes.byref(d[1]), ctypes.byref(d[2]), ws_sel.data_ptr(),
                                                       ws_sel.numel(), ws_att.data_ptr(), ws_att.numel(), gptr)
-                            else:
-                                rc = lib.lsa_index_select(ctypes.byref(d[3]), cfg.K, ch.idx.data_ptr(),
-                                                          ch.ws_is.data_ptr(), ch.ws_is.numel(), L.LSA_WS_CLEAN, gptr)
-                                if rc != 0:
-                                    raise L.LSAError("lsa_index_select", rc, lib.lsa_last_error().decode())
-                                lib.lsa_attend(ctypes.byref(d[2]), ws_att.data_ptr(), ws_att.numel(), gptr)
                         graphs.append(g)
                 stream.wait_stream(side)
                 torch.cuda.synchronize()
@@ -723,14 +695,8 @@ def main():
     (launch, path), ms = min(ways.items(), key=lambda kv: kv[1])
     idx_b, gat_b, small_b = algorithmic_bytes(cfg)
     step_bytes = idx_b + gat_b + small_b
-    if path == "index_select":
-        rk, ms_rk = "index_tokens_kernel SEL (lsa_index_select: fp8 key sweep and the selection in one launch)", \
-            ms_index_select
-        traffic = pmc_traffic("index_select_c2_pmc.json", ("index.hip", "common.cuh", "fuse_select.cuh",
-                                                            "select_core.cuh"))
-    else:
-        rk, ms_rk = "index_tokens_kernel (lsa_index, fp8 keys)", ms_index
-        traffic = pmc_traffic("index_fp8_c2_pmc.json", ("index.hip", "common.cuh"))
+    rk, ms_rk = "index_tokens_kernel (lsa_index, fp8 keys)", ms_index
+    traffic = pmc_traffic("index_fp8_c2_pmc.json", ("index.hip", "common.cuh"))
     achieved = idx_b / (ms_rk * 1e-3) / 1e9
     res = {
         "metric": METRIC,
@@ -755,9 +721,7 @@ def main():
                   "step_frac_of_peak": step_bytes / (ms * 1e-3) / 1e9 / PEAK_HBM_GBS,
                   "ms_per_step_plain": ms_plain, "ms_per_step_graph": ms_graph, "graph_errors": graph_errors,
                   "ms_index": ms_index, "ms_select": ms_select, "ms_attend": ms_attend,
-                  "ms_index_select": ms_index_select,
                   "index_gbs": idx_b / (ms_index * 1e-3) / 1e9,
-                  "index_select_gbs": idx_b / (ms_index_select * 1e-3) / 1e9,
                   "kv_gather_gbs": gat_b / (ms_attend * 1e-3) / 1e9,
                   "attend_traffic": pmc_attend_traffic(),
                   "index_bytes_per_launch": idx_b, "gather_bytes": gat_b},

@@ -154,22 +154,18 @@ int32_t lsa_index(const lsa_index_desc *desc, void *stream);
  * the SI budget of a sink, a local window and a top-k fill) as one call: idx receives exactly
  * what lsa_select would select from the scores lsa_index computes ("LongCat-Flash-Lite-Sparse"
  * summary, aitrends.kr, "Good to know" and "Technical features", first bullet; the scores of
- * reading R1). Where the shape allows (H in {32, 64}, few enough query rows to give every row
- * several workgroups of their own on the GPU, no kept map), one launch scores the keys and
- * finishes the selection in-kernel: each query row's workgroups exchange their candidate
- * counts and threshold-bin ties through the workspace, so the score row is not read back
- * from memory; otherwise the call runs lsa_index priming the selection, then lsa_select.
+ * reading R1). The indexer primes the selection (its epilogue counts the candidates per
+ * first-level bin where the kernel has one query per workgroup), so the selection skips its
+ * first pass over the scores.
  * Arguments: desc as for lsa_index in TOKENS mode without a kept map, with desc->sink and
- * desc->window the forced set and desc->select_ws ignored; desc->scores may be NULL (then the
- * scores are not written); K the budget (1 <= K <= 4096, sink + window <= K); idx int32
- * [B][T][K] as lsa_select writes it (ascending positions, then -1).
- * Workspace: lsa_index_select_workspace_bytes(desc, K) bytes (it depends on whether
- * desc->scores is NULL), 256-byte aligned. workspace_state LSA_WS_UNKNOWN clears what must
- * start at zero (one fill kernel); LSA_WS_CLEAN skips that and is valid after a successful
- * call with the same B, T, N, H, D and key type (every call leaves the workspace clean).
- * Calls sharing a workspace must be ordered on one stream. The in-kernel exchange needs
- * every workgroup of the launch resident at once: it is a cooperative launch, which fails
- * (LSA_E_HIP) rather than waits if the GPU cannot hold it.
+ * desc->window the forced set and desc->select_ws ignored; desc->scores may be NULL (the
+ * scores then live in the workspace); K the budget (1 <= K <= 4096, sink + window <= K); idx
+ * int32 [B][T][K] as lsa_select writes it (ascending positions, then -1).
+ * Workspace: lsa_index_select_workspace_bytes(desc, K) bytes (larger when desc->scores is
+ * NULL), 256-byte aligned. workspace_state LSA_WS_UNKNOWN clears what must start at zero
+ * (one fill kernel); LSA_WS_CLEAN skips that and is valid after a successful call with the
+ * same B, T and N (every call leaves the workspace clean). Calls sharing a workspace must be
+ * ordered on one stream.
  * Errors as lsa_index and lsa_select; LSA_E_UNSUPPORTED for BLOCKS mode or a kept map.
  */
 size_t lsa_index_select_workspace_bytes(const lsa_index_desc *desc, int32_t K);

@@ -297,10 +297,8 @@ int32_t lsa_select(const lsa_select_desc *d, void *ws, size_t ws_bytes, void *st
 
 // ----------------------------------------------------------------------------- index + select
 
-// Checks of lsa_index_select's arguments; fills the indexer arguments and the plan (fused
-// launch or not) and the workspace size.
-static int32_t index_select_check(const lsa_index_desc *d, int32_t K, lsa::IndexTokensArgs &a, bool &fused, int &nc,
-                                  int &chunk, size_t &ws_need) {
+// Checks of lsa_index_select's arguments; fills the indexer arguments and the workspace size.
+static int32_t index_select_check(const lsa_index_desc *d, int32_t K, lsa::IndexTokensArgs &a, size_t &ws_need) {
     if (!d) return fail(LSA_E_NULL, "lsa_index_select: desc is NULL");
     if (d->mode != LSA_INDEX_TOKENS) return fail(LSA_E_UNSUPPORTED, "lsa_index_select: TOKENS mode only");
     if (d->kept) return fail(LSA_E_UNSUPPORTED, "lsa_index_select: no kept map (call lsa_index, then lsa_select)");
@@ -312,32 +310,24 @@ static int32_t index_select_check(const lsa_index_desc *d, int32_t K, lsa::Index
     if (K > 4096) return fail(LSA_E_UNSUPPORTED, "lsa_index_select: K=%d above 4096", K);
     if ((int64_t)d->B * d->T > kMaxGridY) return fail(LSA_E_UNSUPPORTED, "lsa_index_select: B*T too large");
     const int rows = d->B * d->T;
-    fused = lsa::index_select_plan(d->B, d->T, d->N, d->H, d->D, a.fp8, a.qf8, nc, chunk);
-    if (fused) {
-        ws_need = lsa::index_select_workspace_bytes(rows, nc, chunk);
-    } else {  // the indexer (priming) and the selection; scores in the workspace when not asked for
-        ws_need = lsa::select_workspace_bytes(rows, d->N, false);
-        if (!d->scores) ws_need += (size_t)rows * d->N * 4 + 256;
-    }
+    // the selection's workspace, then the scores when the caller does not ask for them
+    ws_need = lsa::select_workspace_bytes(rows, d->N, false);
+    if (!d->scores) ws_need += (size_t)rows * d->N * 4 + 256;
     return LSA_OK;
 }
 
 size_t lsa_index_select_workspace_bytes(const lsa_index_desc *d, int32_t K) {
     lsa::IndexTokensArgs a;
-    bool fused;
-    int nc = 0, chunk = 0;
     size_t need = 0;
-    if (index_select_check(d, K, a, fused, nc, chunk, need) != LSA_OK) return 0;
+    if (index_select_check(d, K, a, need) != LSA_OK) return 0;
     return need;
 }
 
 int32_t lsa_index_select(const lsa_index_desc *d, int32_t K, int32_t *idx, void *ws, size_t ws_bytes,
                          int32_t ws_state, void *stream) {
     lsa::IndexTokensArgs a;
-    bool fused;
-    int nc = 0, chunk = 0;
     size_t need = 0;
-    int32_t rc = index_select_check(d, K, a, fused, nc, chunk, need);
+    int32_t rc = index_select_check(d, K, a, need);
     if (rc != LSA_OK) return rc;
     if (!idx) return fail(LSA_E_NULL, "lsa_index_select: idx is required");
     if (!aligned4(idx)) return fail(LSA_E_ALIGN, "lsa_index_select: misaligned idx");
@@ -349,30 +339,12 @@ int32_t lsa_index_select(const lsa_index_desc *d, int32_t K, int32_t *idx, void 
         return fail(LSA_E_ALIGN, "lsa_index_select: workspace not 256-byte aligned");
     hipStream_t s = reinterpret_cast<hipStream_t>(stream);
     const int rows = d->B * d->T;
-    if (fused) {
-        hipError_t e;
-        if (ws_state != LSA_WS_CLEAN) {
-            e = lsa::launch_clear(ws, lsa::index_select_zero_bytes(rows), s);
-            if (e != hipSuccess) return hip_status(e, "lsa_index_select");
-        }
-        lsa::FusedSelArgs f = lsa::index_select_carve(ws, rows, nc, chunk);
-        f.K = K;
-        f.sink = d->sink;
-        f.window = d->window;
-        f.idx = idx;
-        f.write_scores = d->scores != nullptr;
-        a.sel_hist = f.hist;
-        a.sink = d->sink;
-        a.window = d->window;
-        return hip_status(lsa::launch_index_select(a, f, s), "lsa_index_select");
-    }
-    // not fusable here: lsa_index priming the selection workspace, then lsa_select
-    void *sel_ws = ws;
     if (!a.scores) {
         const size_t sel_bytes = lsa::select_workspace_bytes(rows, d->N, false);
         a.scores = reinterpret_cast<float *>((reinterpret_cast<uintptr_t>(ws) + sel_bytes + 255) & ~(uintptr_t)255);
     }
-    rc = index_primed(d, a, sel_ws, ws_state == LSA_WS_CLEAN, s, "lsa_index_select");
+    // the indexer priming the selection workspace, then the selection on its scores
+    rc = index_primed(d, a, ws, ws_state == LSA_WS_CLEAN, s, "lsa_index_select");
     if (rc != LSA_OK) return rc;
     lsa::SelectArgs sa{};
     sa.B = d->B;
@@ -389,7 +361,7 @@ int32_t lsa_index_select(const lsa_index_desc *d, int32_t K, int32_t *idx, void 
     sa.primed = true;
     sa.vec = (d->N & 3) == 0;
     sa.idx = idx;
-    return hip_status(lsa::launch_select(sa, sel_ws, s), "lsa_index_select");
+    return hip_status(lsa::launch_select(sa, ws, s), "lsa_index_select");
 }
 
 // ----------------------------------------------------------------------------- attend

@@ -19,7 +19,6 @@
 //
 // block_means_kernel: kbar[j] = mean of the dequantised keys of block j, fp32.
 #include "common.cuh"
-#include "fuse_select.cuh"
 #include "kernels.h"
 
 namespace lsa {
@@ -106,12 +105,9 @@ __device__ __forceinline__ void row_to_th(int grp, int i, int H, int T, int &t, 
 // HIST (one query per workgroup): the epilogue also counts the selection candidates of
 // its columns per first-level bin of the selection histogram (finite scores at visible
 // positions outside the sink and the window) and adds the counts to sel_hist.
-// SEL (with HIST, flat): the workgroup also keeps its chunk's scores in LDS (after the key
-// ring) and, once the indexer loop is done, finishes the selection of its query row with
-// the row's other workgroups (fuse_select.cuh); the global score write is optional.
-template <int D, bool FP8, bool QF8, int MODE, int HB, bool HI, bool PRE, bool HIST, int NST, bool SEL = false>
+template <int D, bool FP8, bool QF8, int MODE, int HB, bool HI, bool PRE, bool HIST, int NST>
 __global__ __launch_bounds__(PRE ? kThreads : 2 * kThreads) void index_tokens_kernel(IndexTokensArgs a, int groups,
-                                                                                      int chunk, FusedSelArgs f) {
+                                                                                      int chunk) {
     using G = Tile<D, FP8, NST>;
     static_assert(!QF8 || FP8, "fp8 queries need fp8 keys");
     // SPLIT (one query group per workgroup): waves 0-3 compute, waves 4-7 only stream the
@@ -126,8 +122,6 @@ __global__ __launch_bounds__(PRE ? kThreads : 2 * kThreads) void index_tokens_ke
     __shared__ int tpos[HI ? G::NST : 1][kKT];                            // HI: position of each row
     __shared__ uint32_t shist[HIST ? kSelBins : 1];                      // HIST: candidate counts
     static_assert(!HIST || (MODE == ONEQ && !PRE), "the histogram needs one query per workgroup");
-    static_assert(!SEL || (HIST && !HI), "the fused selection takes flat rows and the histogram");
-    float *lsc = reinterpret_cast<float *>(ring + G::NST * G::STAGE);  // SEL: the chunk's scores
 
     const int tid = threadIdx.x;
     const int lane = tid & 63, half = lane >> 5, l32 = lane & 31;
@@ -288,10 +282,6 @@ __global__ __launch_bounds__(PRE ? kThreads : 2 * kThreads) void index_tokens_ke
     };
 
     auto write_score = [&](int t, int col, float v) {
-        if constexpr (SEL) {
-            lsc[col - c0] = v;
-            if (!f.write_scores) return;
-        }
         a.scores[(int64_t)(b * T + t) * a.n_out + col] = v;
     };
 
@@ -514,10 +504,6 @@ __global__ __launch_bounds__(PRE ? kThreads : 2 * kThreads) void index_tokens_ke
             }
         }
     }
-    if constexpr (SEL) {
-        constexpr int RING = G::NST * G::STAGE;
-        fsel::run<NT>(f, b * T + grp, (int)blockIdx.x, c0, c1, ctx - T + grp, lsc, ring, RING, RING + chunk * 4);
-    }
 }
 
 // ---------------------------------------------------------------------------- blocks
@@ -617,31 +603,8 @@ hipError_t launch_tokens_t(const IndexTokensArgs &a, hipStream_t s) {
     dim3 grid(chunks, gy, a.B);
     const size_t lds = (size_t)G::NST * G::STAGE;
     hipLaunchKernelGGL((index_tokens_kernel<D, FP8, QF8, MODE, HB, HI, PRE, HIST, NST>), grid, dim3(PRE ? kThreads : 2 * kThreads), lds, s, a,
-                       groups, chunk, FusedSelArgs{});
+                       groups, chunk);
     return hipGetLastError();
-}
-
-// The fused indexer + selection: one query per workgroup, f.nc chunks of f.chunk columns
-// per row, every workgroup of the launch co-resident (cooperative launch: the rows'
-// workgroups wait for each other).
-template <int D, bool FP8, bool QF8, int HB>
-hipError_t launch_tokens_sel(const IndexTokensArgs &a, const FusedSelArgs &f, hipStream_t s) {
-    constexpr int NST = 4;
-    using G = Tile<D, FP8, NST>;
-    auto kern = index_tokens_kernel<D, FP8, QF8, ONEQ, HB, false, false, true, NST, true>;
-    const size_t lds = (size_t)G::NST * G::STAGE + (size_t)f.chunk * 4;
-    int groups = a.T, chunk = f.chunk;
-    IndexTokensArgs aa = a;
-    FusedSelArgs ff = f;
-    void *args[] = {&aa, &groups, &chunk, &ff};
-    return hipLaunchCooperativeKernel(reinterpret_cast<const void *>(kern), dim3(f.nc, a.T, a.B),
-                                      dim3(2 * kThreads), args, (unsigned)lds, s);
-}
-
-// LDS bytes of the fused kernel's key ring (the chunk's ties must fit below its end).
-int sel_ring_bytes(int D, bool fp8) {
-    const int rb = fp8 ? D : 2 * D;
-    return 4 * (kKT * rb + (fp8 ? kKT * 4 : 0));
 }
 
 template <int D, bool FP8, bool QF8 = false>
@@ -689,60 +652,6 @@ hipError_t launch_index_tokens(const IndexTokensArgs &a, hipStream_t s) {
     if (a.qf8) return launch_tokens_d<128, true, true>(a, s);  // fp8 keys, D = 128 (checked by the caller)
     if (a.D == 64) return a.fp8 ? launch_tokens_d<64, true>(a, s) : launch_tokens_d<64, false>(a, s);
     return a.fp8 ? launch_tokens_d<128, true>(a, s) : launch_tokens_d<128, false>(a, s);
-}
-
-bool index_select_plan(int B, int T, int N, int H, int D, bool fp8, bool qf8, int &nc, int &chunk) {
-    if (!(H == 32 || H == 64) || (D != 64 && D != 128) || T >= 64 || (qf8 && !(fp8 && D == 128))) return false;
-    const int64_t rows = (int64_t)B * T;
-    const int cus = compute_units();
-    if (rows > cus || rows > 65535) return false;
-    // chunks per row: as many as keep every workgroup on its own compute unit; the chunk's
-    // ties must fit in the key ring (8 bytes each after 1 KB) and its scores after it
-    const int max_chunk = min(8192, (sel_ring_bytes(D, fp8) - 1024) / 8 / kKT * kKT);
-    int n = (int)(cus / rows);
-    if (n > 256) n = 256;
-    if (n < 1) return false;
-    int c = (N + n - 1) / n;
-    c = (c + kKT - 1) / kKT * kKT;
-    if (c > max_chunk) return false;
-    nc = (N + c - 1) / c;
-    chunk = c;
-    return true;
-}
-
-size_t index_select_zero_bytes(int rows) {
-    return sel::align256((size_t)rows * kSelBins * 4) + sel::align256((size_t)rows * fsel::kFCtr * 4);
-}
-
-size_t index_select_workspace_bytes(int rows, int nc, int chunk) {
-    return index_select_zero_bytes(rows) + sel::align256((size_t)rows * nc * 8) +
-           sel::align256((size_t)rows * nc * chunk * 8);
-}
-
-FusedSelArgs index_select_carve(void *ws, int rows, int nc, int chunk) {
-    FusedSelArgs f{};
-    char *p = reinterpret_cast<char *>(ws);
-    f.hist = reinterpret_cast<uint32_t *>(p);
-    p += sel::align256((size_t)rows * kSelBins * 4);
-    f.ctr = reinterpret_cast<uint32_t *>(p);
-    p += sel::align256((size_t)rows * fsel::kFCtr * 4);
-    f.cnt = reinterpret_cast<uint64_t *>(p);
-    p += sel::align256((size_t)rows * nc * 8);
-    f.ties = reinterpret_cast<uint64_t *>(p);
-    f.nc = nc;
-    f.chunk = chunk;
-    return f;
-}
-
-hipError_t launch_index_select(const IndexTokensArgs &a, const FusedSelArgs &f, hipStream_t s) {
-    // (the plan admitted H in {32, 64} only)
-    if (a.qf8) return a.H == 32 ? launch_tokens_sel<128, true, true, 1>(a, f, s) : launch_tokens_sel<128, true, true, 2>(a, f, s);
-    if (a.D == 64) {
-        if (a.fp8) return a.H == 32 ? launch_tokens_sel<64, true, false, 1>(a, f, s) : launch_tokens_sel<64, true, false, 2>(a, f, s);
-        return a.H == 32 ? launch_tokens_sel<64, false, false, 1>(a, f, s) : launch_tokens_sel<64, false, false, 2>(a, f, s);
-    }
-    if (a.fp8) return a.H == 32 ? launch_tokens_sel<128, true, false, 1>(a, f, s) : launch_tokens_sel<128, true, false, 2>(a, f, s);
-    return a.H == 32 ? launch_tokens_sel<128, false, false, 1>(a, f, s) : launch_tokens_sel<128, false, false, 2>(a, f, s);
 }
 
 hipError_t launch_index_blocks(const IndexBlocksArgs &a, hipStream_t s) {

@@ -27,27 +27,6 @@ struct IndexTokensArgs {
 };
 hipError_t launch_index_tokens(const IndexTokensArgs &a, hipStream_t s);
 
-// The selection finished inside the indexer launch (lsa_index_select): flat token scores,
-// one query token per workgroup, nc workgroups (chunks of `chunk` columns) per query row,
-// all co-resident. Workspace per row: the first-level histogram and 4 counters (zero
-// between calls), then nc chunk counts and nc * chunk tie slots.
-struct FusedSelArgs {
-    int K, sink, window;
-    int32_t *idx;         // [rows][K]
-    uint32_t *hist;       // [rows][kSelBins]
-    uint32_t *ctr;        // [rows][4]
-    uint64_t *cnt;        // [rows][nc]: (candidates above the threshold bin << 32) | its ties
-    uint64_t *ties;       // [rows][nc][chunk]: each chunk's ties (composites)
-    int nc, chunk;
-    bool write_scores;    // also write the scores (a.scores), as lsa_index does
-};
-// The fused plan for these sizes: chunks per row and columns per chunk, false when the
-// fused launch cannot hold them (the caller then runs the indexer and the selection).
-bool index_select_plan(int B, int T, int N, int H, int D, bool fp8, bool qf8, int &nc, int &chunk);
-size_t index_select_workspace_bytes(int rows, int nc, int chunk);
-size_t index_select_zero_bytes(int rows);
-FusedSelArgs index_select_carve(void *ws, int rows, int nc, int chunk);
-hipError_t launch_index_select(const IndexTokensArgs &a, const FusedSelArgs &f, hipStream_t s);
 bool index_tokens_supported(int H, int D, bool hi);
 // true when the token kernel for (H, T, hi) builds sel_hist in its epilogue (one query
 // per workgroup); otherwise sel_hist must be built by launch_select_hist.

@@ -1,15 +1,12 @@
-"""lsa_index_select (the indexer and the selection in one call; one launch where the shape
-allows, the selection finished inside it) against lsa_index followed by lsa_select on the
-same inputs: the index lists must be identical (both decide in fp32 on the same scores),
-and so must the scores when they are written. Cases: the 128K decode shape (64 heads, fp8
-keys), 32 heads, bf16 keys of 64 dims, several query tokens per sequence, ragged context
-lengths, contexts shorter than the budget (everything visible taken), a budget of one,
-no sink or window, scores not written, fp8 queries, a row where every score is equal (the
-whole row ties: the tie list exceeds the LDS and is ranked from the workspace), workspace
-reuse, two calls giving the same bytes, and a shape the fused launch cannot hold (many
-query rows: the call runs the indexer and the selection). Against the oracle: the 128K
-decode shape through the benchmark's chains (test_gpu_headline.py) and the band rule
-here on a reduced shape.
+"""lsa_index_select (the indexer priming the selection, then the selection, as one call;
+the scores may stay in the workspace) against lsa_index followed by lsa_select on the same
+inputs: the index lists must be identical (both decide in fp32 on the same scores), and so
+must the scores when they are written. Cases: the 128K decode shape (64 heads, fp8 keys),
+32 heads, bf16 keys of 64 dims, several query tokens per sequence, ragged context lengths,
+contexts shorter than the budget (everything visible taken), a budget of one, no sink or
+window, scores not written, fp8 queries, rows where every score is equal (the whole row
+ties), workspace reuse, two calls giving the same bytes, and many query rows. Against the
+oracle: the band rule on a reduced shape.
 """
 import numpy as np
 import pytest
