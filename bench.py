@@ -69,7 +69,7 @@ def backward_inputs(B, N, K, Hq, seed=11, with_target=False):
     out, lse = L.lsa_attend(q, k, None, idx, 576 ** -0.5)
     dout = torch.randn((B, 1, Hq, 512), device="cuda", generator=g).to(torch.bfloat16)
     dq = torch.empty((B, 1, Hq, 576), dtype=torch.float32, device="cuda")
-    dk = torch.empty((B, N, 1, 576), dtype=torch.float32, device="cuda")
+    dk = torch.zeros((B, N, 1, 576), dtype=torch.float32, device="cuda")  # rows outside the selection stay 0
     if with_target:  # the indexer distillation target on the same selection
         sc = torch.randn((B, 1, N), device="cuda", generator=g)
         return lambda: L.lsa_index_target(q[0], k[0], idx, 576 ** -0.5, lse[0], sc)
@@ -458,9 +458,9 @@ def measure_workloads(steps=50):
         us = graph_us(f, reps=10)
         us_t = graph_us(backward_inputs(B, N, K, Hq, with_target=True), reps=10)
         rows_flops = B * Hq * K * 2.0 * (3 * 576 + 2 * 512)
-        dk_bytes = B * N * 576 * 4
-        return {"workload": "backward: c2 shape (B=8, 128K, T=1, MLA 64 heads 576/512, K=2048), dq and the dense "
-                            "fp32 latent-row gradient",
+        dk_bytes = B * K * 576 * 4  # the selected latent rows' gradients (the others are not written)
+        return {"workload": "backward: c2 shape (B=8, 128K, T=1, MLA 64 heads 576/512, K=2048), dq and the "
+                            "fp32 latent-row gradient of the selected rows",
                 "us_per_call": us, "rows_gflop": rows_flops / 1e9, "dk_write_gb": dk_bytes / 1e9,
                 "us_index_target": us_t}
 

@@ -362,13 +362,17 @@ int32_t lsa_select_attend(const lsa_select_desc *sel, const lsa_attend_desc *att
  * reproducible bit for bit; no atomics.
  * Layouts: q, out, dout bf16 [B][T][Hq][d]; lse fp32 [B][T][Hq]; k, v as in lsa_attend
  * (strides in elements); idx int32 [B][T][K] as lsa_select writes it (valid entries
- * strictly ascending, then -1; entries outside [0, N) skipped). Outputs fp32, written in
- * full: dq [B][T][Hq][d_qk]; dk [B][N][Hkv][d_qk] and dv [B][N][Hkv][d_v] (zero at
- * positions no query selected). MLA (d_qk = 576, d_v = 512, v aliasing k, reading R15):
- * dk is the latent row's gradient, dK plus dV on its first 512 columns, and dv is NULL.
+ * strictly ascending, then -1; entries outside [0, N) skipped). Outputs fp32: dq
+ * [B][T][Hq][d_qk], written in full; dk [B][N][Hkv][d_qk] and dv [B][N][Hkv][d_v], written
+ * only at the rows of positions some query selected: every other row keeps what the caller
+ * left there, so a buffer zeroed once (at allocation) receives the dense gradient, with zeros
+ * at the unselected positions, and the call moves only the selected rows. MLA (d_qk = 576,
+ * d_v = 512, v aliasing k, reading R15): dk is the latent row's gradient, dK plus dV on its
+ * first 512 columns, and dv is NULL.
  * Workspace: lsa_attend_backward_workspace_bytes(desc), 256-byte aligned, no initial
- * contents: per (query token, KV head, selected row) one row of fp32 contributions
- * (d_qk + d_v floats, MLA d_qk) plus per-tile parts of dq (32 rows a tile).
+ * contents: per-tile parts of dq (32 rows a tile) and, with T > 1, per (query token, KV
+ * head, selected row) one row of fp32 contributions (d_qk + d_v floats, MLA d_qk). With
+ * T = 1 each selected row has a single contribution, which goes straight to dk / dv.
  * Supported: (d_qk, d_v) in {(128, 128), (576, 512)}, Hq % Hkv == 0, Hq / Hkv <= 64,
  * B * T <= 65535, strides multiples of 8 elements; q, k, v, out, dout, dk, dv 16-byte
  * aligned. Errors as for lsa_attend.

@@ -459,7 +459,9 @@ def lsa_attend_backward(q, k, v, idx, softmax_scale, out, lse, dout, *, dq=None,
     """Gradients of lsa_attend for one layer, selection fixed. q, out, dout bf16 [B,T,Hq,d];
     k, v bf16 [B,N,Hkv,d] (v=None: MLA latent rows); idx int32 [B,T,K] as lsa_select
     writes it; lse fp32 [B,T,Hq]. Returns fp32 (dq [B,T,Hq,d_qk], dk [B,N,Hkv,d_qk], dv
-    [B,N,Hkv,d_v] or None for MLA, where dk is the latent row gradient)."""
+    [B,N,Hkv,d_v] or None for MLA, where dk is the latent row gradient). The call writes dk
+    and dv only at the selected positions: buffers allocated here start at zero; buffers
+    passed in keep their other rows."""
     import torch
     B, T, Hq, dqk = q.shape
     N, Hkv = k.shape[1], k.shape[2]
@@ -469,9 +471,9 @@ def lsa_attend_backward(q, k, v, idx, softmax_scale, out, lse, dout, *, dq=None,
     dv_ = 512 if mla else v.shape[-1]
     dev = q.device
     dq = torch.empty((B, T, Hq, dqk), dtype=torch.float32, device=dev) if dq is None else dq
-    dk = torch.empty((B, N, Hkv, dqk), dtype=torch.float32, device=dev) if dk is None else dk
+    dk = torch.zeros((B, N, Hkv, dqk), dtype=torch.float32, device=dev) if dk is None else dk
     if not mla and dv is None:
-        dv = torch.empty((B, N, Hkv, dv_), dtype=torch.float32, device=dev)
+        dv = torch.zeros((B, N, Hkv, dv_), dtype=torch.float32, device=dev)
     d = AttendBwdDesc(B=B, T=T, N=N, Hq=Hq, Hkv=Hkv, d_qk=dqk, d_v=dv_, q=_ptr(q), k=_ptr(k),
                       k_stride_b=k.stride(0), k_stride_n=k.stride(1), k_stride_h=k.stride(2),
                       v=_ptr(v), v_stride_b=v.stride(0), v_stride_n=v.stride(1), v_stride_h=v.stride(2),

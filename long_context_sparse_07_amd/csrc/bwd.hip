@@ -15,7 +15,9 @@
 // bwd_dq_kernel: dq = the tiles' parts, added in tile order.
 // bwd_kv_kernel (one workgroup per tile of 16 cache positions and KV head): the
 //   contributions G of every query that selected one of the positions, added in ascending
-//   query order; every position of the cache is written (zero where nothing selected it).
+//   query order; only the positions some query selected are written. With one query token
+//   per sequence each position has a single contribution, and bwd_rows_kernel writes the
+//   row gradients straight to dk / dv instead (no G, no position sweep).
 // target_tile_kernel, kl_kernel: the indexer distillation target (head-averaged attention
 //   over the selected rows), its KL against the indexer's softmax, and the KL's gradient
 //   with respect to the indexer scores.
@@ -43,7 +45,9 @@ __device__ __forceinline__ float bf16_at(const uint16_t *p) { return u2f((uint32
 template <int DQK, int DV, bool MLA>
 constexpr int g_width() { return MLA ? DQK : DQK + DV; }
 
-template <int DQK, int DV, bool MLA>
+// DIRECT (one query token per sequence): the contributions are the row gradients
+// themselves; row r goes to dk (and dv) at its position, not to G.
+template <int DQK, int DV, bool MLA, bool DIRECT>
 __global__ __launch_bounds__(kBT) void bwd_rows_kernel(AttendBwdArgs a, float *G, float *dqp) {
     constexpr int GW = g_width<DQK, DV, MLA>();
     __shared__ __attribute__((aligned(16))) uint16_t kt[kRT][DQK];
@@ -227,7 +231,16 @@ __global__ __launch_bounds__(kBT) void bwd_rows_kernel(AttendBwdArgs a, float *G
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
             const int row = 8 * (r / 4) + 4 * half + (r % 4);
-            if (row < nrows) gout[(int64_t)row * GW + c] = acc[r];
+            if constexpr (DIRECT) {
+                const int pos = rowpos[row];  // -1 for padding and rows past nrows
+                if (pos >= 0) {
+                    const int64_t rk = ((int64_t)b * a.N + pos) * a.Hkv + kvh;
+                    if (c < DQK) a.dk[rk * DQK + c] = acc[r];
+                    else a.dv[rk * DV + (c - DQK)] = acc[r];
+                }
+            } else {
+                if (row < nrows) gout[(int64_t)row * GW + c] = acc[r];
+            }
         }
     }
 
@@ -316,6 +329,7 @@ __global__ __launch_bounds__(kBT) void bwd_kv_kernel(AttendBwdArgs a, const floa
     constexpr int NC = (GW + kBT - 1) / kBT;  // columns per thread
     __shared__ __attribute__((aligned(16))) float acc[kPT][GW];
     __shared__ int lo_s[kBT], cnt_s[kBT];
+    __shared__ int hit[kPT];  // a query selected position p0 + r
     const int tid = threadIdx.x;
     const int p0 = blockIdx.x * kPT, b = blockIdx.y, kvh = blockIdx.z;
     bool touched = false;  // some query selected a position of the tile (uniform)
@@ -349,6 +363,7 @@ __global__ __launch_bounds__(kBT) void bwd_kv_kernel(AttendBwdArgs a, const floa
         if (!any) continue;
         if (!touched) {  // first contributions: clear the accumulators
             for (int i = tid; i < kPT * GW; i += kBT) (&acc[0][0])[i] = 0.0f;
+            if (tid < kPT) hit[tid] = 0;
             __syncthreads();
             touched = true;
         }
@@ -362,6 +377,7 @@ __global__ __launch_bounds__(kBT) void bwd_kv_kernel(AttendBwdArgs a, const floa
                 const int pos = row[slot];
                 if (pos < p0 || pos >= p0 + kPT || pos >= a.N) continue;  // (rows not ascending: skipped)
                 const float *gr = gq + (int64_t)slot * GW;
+                if (tid == 0) hit[pos - p0] = 1;
 #pragma unroll
                 for (int i = 0; i < NC; ++i) {
                     const int c = tid + kBT * i;
@@ -370,17 +386,17 @@ __global__ __launch_bounds__(kBT) void bwd_kv_kernel(AttendBwdArgs a, const floa
             }
         }
     }
+    if (!touched) return;  // nothing selected a position of the tile: nothing is written
     __syncthreads();
-    // every position of the tile: 16-byte stores (zeros when nothing selected the tile)
+    // the selected positions of the tile: 16-byte stores
     for (int e = tid; e < kPT * GW / 4; e += kBT) {
         const int r = e / (GW / 4), c = 4 * (e % (GW / 4));
         const int pos = p0 + r;
         if (pos >= a.N) break;
+        if (!hit[r]) continue;
         const int64_t rowk = ((int64_t)b * a.N + pos) * a.Hkv + kvh;
-        f32x4 v = {0.0f, 0.0f, 0.0f, 0.0f};
-        if (touched) v = *reinterpret_cast<const f32x4 *>(&acc[r][c]);
         float *dst = c < DQK ? a.dk + rowk * DQK + c : a.dv + rowk * DV + (c - DQK);
-        *reinterpret_cast<f32x4 *>(dst) = v;
+        *reinterpret_cast<f32x4 *>(dst) = *reinterpret_cast<const f32x4 *>(&acc[r][c]);
     }
 }
 
@@ -508,7 +524,7 @@ BwdLayout bwd_layout(const AttendBwdArgs &a) {
     BwdLayout l;
     l.ntiles = (a.K + kRT - 1) / kRT;
     l.g_off = 0;
-    l.g_bytes = (size_t)a.B * a.T * a.Hkv * a.K * GW * sizeof(float);
+    l.g_bytes = a.T == 1 ? 0 : (size_t)a.B * a.T * a.Hkv * a.K * GW * sizeof(float);  // T == 1: no G
     l.dq_off = (l.g_bytes + 255) / 256 * 256;
     l.dq_bytes = (size_t)a.B * a.T * a.Hq * l.ntiles * DQK * sizeof(float);
     l.total = l.dq_off + l.dq_bytes;
@@ -520,11 +536,13 @@ hipError_t launch_bwd_t(const AttendBwdArgs &a, void *ws, hipStream_t s) {
     const BwdLayout l = bwd_layout(a);
     float *G = reinterpret_cast<float *>(static_cast<unsigned char *>(ws) + l.g_off);
     float *dqp = reinterpret_cast<float *>(static_cast<unsigned char *>(ws) + l.dq_off);
-    hipLaunchKernelGGL((bwd_rows_kernel<DQK, DV, MLA>), dim3(l.ntiles, a.B * a.T, a.Hkv), dim3(kBT), 0, s, a, G, dqp);
+    const dim3 rgrid(l.ntiles, a.B * a.T, a.Hkv);
+    if (a.T == 1) hipLaunchKernelGGL((bwd_rows_kernel<DQK, DV, MLA, true>), rgrid, dim3(kBT), 0, s, a, G, dqp);
+    else hipLaunchKernelGGL((bwd_rows_kernel<DQK, DV, MLA, false>), rgrid, dim3(kBT), 0, s, a, G, dqp);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     hipLaunchKernelGGL((bwd_dq_kernel<DQK>), dim3(a.B * a.T * a.Hq), dim3(64), 0, s, a, dqp, l.ntiles);
-    if ((e = hipGetLastError()) != hipSuccess) return e;
+    if ((e = hipGetLastError()) != hipSuccess || a.T == 1) return e;
     hipLaunchKernelGGL((bwd_kv_kernel<DQK, DV, MLA>), dim3((a.N + kPT - 1) / kPT, a.B, a.Hkv), dim3(kBT), 0, s, a, G);
     return hipGetLastError();
 }

@@ -297,8 +297,12 @@ def test_attend_backward_argument_errors(kw, code):
 def test_attend_backward_workspace_rules():
     d = _bwd_desc()
     need = L.lib().lsa_attend_backward_workspace_bytes(ctypes.byref(d))
-    # per (query, KV head, selected row) one MLA row of fp32, then per 32-row tile a dq part
-    assert need == 2 * 256 * 576 * 4 + 2 * 64 * 8 * 576 * 4
+    # one query token per sequence: only the per-32-row-tile dq parts (the row gradients go
+    # straight to dk); with more query tokens, per (query, KV head, selected row) one MLA
+    # row of fp32 before them
+    assert need == 2 * 64 * 8 * 576 * 4
+    need3 = L.lib().lsa_attend_backward_workspace_bytes(ctypes.byref(_bwd_desc(T=3)))
+    assert need3 == 2 * 3 * 256 * 576 * 4 + 2 * 3 * 64 * 8 * 576 * 4
     assert _bwd(d, FAKE, need - 1) == -7
     assert _bwd(d, None, need) == -7
     assert _bwd(d, FAKE + 16, need) == -5

@@ -189,3 +189,38 @@ def test_backward_many_query_tokens():
     _close(dq, wq, "dq T=9")
     _close(dk, wk, "dk T=9")
     _close(dv, wv, "dv T=9")
+
+
+@pytest.mark.parametrize("T,mla", [(1, True), (1, False), (3, True), (3, False)])
+def test_backward_writes_only_selected_rows(T, mla):
+    # dk / dv given by the caller hold a sentinel: the call writes exactly the rows of the
+    # selected positions (their gradients match the oracle) and leaves every other row as
+    # it was. T = 1 takes the direct path (no per-position pass), T = 3 the position tiles.
+    rng = np.random.default_rng(70 + T + 10 * mla)
+    n_valid = [[96] * T, [40, 96, 5][:T]]
+    c = _case(rng, 2, T, 2500, 64 if mla else 16, 1 if mla else 2, mla, 96, 24, n_valid)
+    B, N = 2, 2500
+    dqk, dvd = (576, 512) if mla else (128, 128)
+    Hkv = 1 if mla else 2
+    sentinel = 7.25
+    dk = torch.full((B, N, Hkv, dqk), sentinel, dtype=torch.float32, device="cuda")
+    dv = None if mla else torch.full((B, N, Hkv, dvd), sentinel, dtype=torch.float32, device="cuda")
+    dq, dk, dv = L.lsa_attend_backward(c["q"].cuda(), c["k"].cuda(), None if mla else c["v"].cuda(),
+                                       torch.from_numpy(c["idx"]).cuda(), c["tau"], c["out"].cuda(),
+                                       torch.from_numpy(c["lse"]).cuda(), c["dout"].cuda(), dk=dk, dv=dv)
+    torch.cuda.synchronize()
+    wq, wk, wv = _oracle_grads(c)
+    sel = np.zeros((B, N), dtype=bool)
+    for b in range(B):
+        for t in range(T):
+            r = c["idx"][b, t]
+            sel[b, r[(r >= 0) & (r < N)]] = True
+    for name, got, want in (("dk", dk, wk), ("dv", dv, wv)):
+        if got is None:
+            continue
+        g = got.cpu().numpy().astype(np.float64)
+        assert np.all(g[~sel] == sentinel), f"{name}: an unselected row was written"
+        scale = max(np.max(np.abs(want)), 1e-30)
+        err = np.max(np.abs(g[sel] - want[sel])) / scale
+        assert err < 1e-4, f"{name}: selected rows off by {err:.2e} of the largest entry"
+    _close(dq, wq, "dq")
