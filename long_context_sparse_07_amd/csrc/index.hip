@@ -508,19 +508,32 @@ __global__ __launch_bounds__(PRE ? kThreads : 2 * kThreads) void index_tokens_ke
 
 // ---------------------------------------------------------------------------- blocks
 
-// One thread per block j; the query token's (H x D) rows staged in LDS as fp32.
+// One thread per block j; the query token's (H x D) rows staged in LDS as fp32, the
+// block's mean key held in registers (all its loads in flight at once), the head dots
+// summed in dimension order.
+template <int D>
 __global__ __launch_bounds__(256) void index_blocks_kernel(IndexBlocksArgs a) {
     extern __shared__ float qs[];  // [H][D]
     const int b = blockIdx.z, t = blockIdx.y;
-    const int H = a.H, D = a.D, T = a.T;
+    const int H = a.H, T = a.T;
     const int64_t qoff = ((int64_t)b * T + t) * H * D;
     for (int e = threadIdx.x; e < H * D; e += blockDim.x) {
         uint16_t bits = a.q[qoff + e];
         qs[e] = u2f((uint32_t)bits << 16);
     }
-    __syncthreads();
     const int j = blockIdx.x * blockDim.x + threadIdx.x;
-    if (j >= a.n_blocks) return;
+    const bool in = j < a.n_blocks;
+    float kv[D];
+    {
+        const float4 *kb4 = reinterpret_cast<const float4 *>(a.kbar + ((int64_t)b * a.n_blocks + (in ? j : 0)) * D);
+#pragma unroll
+        for (int d4 = 0; d4 < D / 4; ++d4) {
+            const float4 v = kb4[d4];
+            kv[4 * d4] = v.x, kv[4 * d4 + 1] = v.y, kv[4 * d4 + 2] = v.z, kv[4 * d4 + 3] = v.w;
+        }
+    }
+    __syncthreads();
+    if (!in) return;
     int ctx = a.ctx_len ? a.ctx_len[b] : a.N;
     ctx = min(max(ctx, 0), a.N);
     const int p = ctx - T + t;
@@ -543,23 +556,14 @@ __global__ __launch_bounds__(256) void index_blocks_kernel(IndexBlocksArgs a) {
     }
     float best = kNegInf;
     if (ok) {
-        const float *kb = a.kbar + ((int64_t)b * a.n_blocks + j) * D;
         const float *wt = a.w + ((int64_t)b * T + t) * H;
-        best = 0.0f;
-        bool first = true;
         for (int h = 0; h < H; ++h) {
             float dot = 0.0f;
             const float *qh = qs + h * D;
-            for (int d = 0; d < D; d += 4) {
-                float4 kv = *reinterpret_cast<const float4 *>(kb + d);
-                dot = fmaf(qh[d], kv.x, dot);
-                dot = fmaf(qh[d + 1], kv.y, dot);
-                dot = fmaf(qh[d + 2], kv.z, dot);
-                dot = fmaf(qh[d + 3], kv.w, dot);
-            }
-            float v = wt[h] * fmaxf(dot, 0.0f);
-            best = first ? v : fmaxf(best, v);
-            first = false;
+#pragma unroll
+            for (int d = 0; d < D; ++d) dot = fmaf(qh[d], kv[d], dot);
+            const float v = wt[h] * fmaxf(dot, 0.0f);
+            best = h == 0 ? v : fmaxf(best, v);
         }
     }
     a.scores[((int64_t)b * T + t) * a.n_blocks + j] = best;
@@ -657,7 +661,8 @@ hipError_t launch_index_tokens(const IndexTokensArgs &a, hipStream_t s) {
 hipError_t launch_index_blocks(const IndexBlocksArgs &a, hipStream_t s) {
     dim3 grid((a.n_blocks + 255) / 256, a.T, a.B);
     size_t lds = (size_t)a.H * a.D * sizeof(float);
-    hipLaunchKernelGGL(index_blocks_kernel, grid, dim3(256), lds, s, a);
+    if (a.D == 64) hipLaunchKernelGGL(index_blocks_kernel<64>, grid, dim3(256), lds, s, a);
+    else hipLaunchKernelGGL(index_blocks_kernel<128>, grid, dim3(256), lds, s, a);
     return hipGetLastError();
 }
 

@@ -375,13 +375,26 @@ __global__ __launch_bounds__(kRT) void select_resolve_kernel(SelectArgs a, Ws w,
         }
         if constexpr (KEPT) {
             nfill = min(nfill, (uint32_t)KPAD);
+            // a kept map whose valid entries ascend, then -1 (as lsa_select writes it), keeps
+            // the columns in position order: the fill is already sorted
+            if (tid == 0) cnt[3] = 0;
             __syncthreads();
-            for (int i = tid; i < KPAD; i += kRT)
+            for (int i = tid; i + 1 < a.n_keep; i += kRT) {
+                const int x = r.kept[i], y = r.kept[i + 1];
+                const bool vx = x >= 0 && x < r.nblk, vy = y >= 0 && y < r.nblk;
+                if (vy && (!vx || x >= y)) cnt[3] = 1;
+            }
+            __syncthreads();
+            const bool ascending = cnt[3] == 0;
+            int np = KPAD;  // the sort's size: the fill rounded up to a power of two
+            while (np / 2 >= (int)nfill && np > 1) np /= 2;
+            if (ascending) np = 1;
+            for (int i = tid; i < np; i += kRT)
                 if ((uint32_t)i >= nfill) fill[i] = 0x7FFFFFFF;
             __syncthreads();
-            for (int k = 2; k <= KPAD; k <<= 1) {
+            for (int k = 2; k <= np; k <<= 1) {
                 for (int j = k >> 1; j > 0; j >>= 1) {
-                    for (int i = tid; i < KPAD; i += kRT) {
+                    for (int i = tid; i < np; i += kRT) {
                         const int ixj = i ^ j;
                         if (ixj > i) {
                             const int x = fill[i], y = fill[ixj];

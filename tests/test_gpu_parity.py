@@ -203,10 +203,12 @@ def test_parity_full_size_prefill_sampled():
     run_parity(cfg, rows=[(0, t) for t in ts])
 
 
-def test_hi_fine_stage_on_given_kept_lists():
+@pytest.mark.parametrize("order", ["ascending", "shuffled"])
+def test_hi_fine_stage_on_given_kept_lists(order):
     # The fine stage alone on kept lists that are not the coarse stage's choice (random
-    # ascending subsets of the eligible blocks, -1 padded, some empty): the GPU's fine
-    # scores and selection against the oracle's fine stage run on the same kept list.
+    # subsets of the eligible blocks, -1 padded, some empty; ascending as lsa_select writes
+    # them, or shuffled with padding in between, which the selection must sort): the GPU's
+    # fine scores and selection against the oracle's fine stage run on the same kept list.
     cfg = config(3, **SMALL[3])
     inp = make_inputs(cfg)
     d = upload(inp)
@@ -219,6 +221,8 @@ def test_hi_fine_stage_on_given_kept_lists():
             E = np.nonzero(O.eligible_blocks(p, cfg.S, cfg.W, cfg.Bs, cfg.N // cfg.Bs))[0]
             n = 0 if t == 1 else int(rng.integers(1, cfg.n_keep + 1))
             kept[b, t, :n] = np.sort(rng.choice(E, size=n, replace=False))
+            if order == "shuffled":
+                kept[b, t] = rng.permutation(kept[b, t])
     kt = torch.from_numpy(kept).cuda()
     fs = L.lsa_index(d["qI"], d["w"], d["kI"], k_scale=d["kI_scale"], kept=kt, block_size=cfg.Bs, ctx_len=d["ctx_len"])
     idx = L.lsa_select(fs, cfg.K, cfg.S, cfg.W, N=cfg.N, ctx_len=d["ctx_len"], kept=kt, block_size=cfg.Bs)
