@@ -49,7 +49,7 @@ def parse():
                     help="with --profile-only: also run one elementwise add of known traffic (counter calibration)")
     ap.add_argument("--profile-c4-index", action="store_true",
                     help="only the c4 prefill indexer, bf16 then fp8 queries, `--steps` calls each (for rocprofv3)")
-    ap.add_argument("--profile-workload", default=None, choices=["c1", "c2s", "c2f", "c3", "c4", "c5"],
+    ap.add_argument("--profile-workload", default=None, choices=["c1", "c2s", "c2f", "c3", "c4", "c4l", "c5"],
                     help="only this workload's step, plain launches, `--steps` steps (for rocprofv3)")
     ap.add_argument("--profile-backward", action="store_true",
                     help="only lsa_attend_backward on the c2 shape, `--steps` calls (for rocprofv3)")
@@ -233,6 +233,18 @@ def fused_step(cfg, d, sc, idx, out, lse):
     return fn
 
 
+def lists_step(cfg, d, idx, out, lse):
+    """The prefill path without the score write: lsa_index_select through candidate lists
+    (the scores not kept), then lsa_attend."""
+    import long_context_sparse_07_amd as L
+
+    def fn():
+        L.lsa_index_select(d["qI"], d["w"], d["kI"], cfg.K, cfg.S, cfg.W, k_scale=d["ks"], ctx_len=d["ctx"],
+                           idx=idx, with_scores=False)
+        L.lsa_attend(d["q"], d["k"], d["v"], idx, cfg.tau, out=out, lse=lse)
+    return fn
+
+
 def hi_step(cfg, d):
     """The c3 hierarchical step: coarse block scores, block selection, fine scores and
     selection inside the kept blocks, attention (block means maintained outside the step)."""
@@ -260,8 +272,9 @@ def hi_step(cfg, d):
 
 def profile_workload(name, steps, warmup):
     """Plain stream launches of one workload's step (for rocprofv3): c1, c3, c4 or c5 with
-    the separate calls (c3: the hierarchical step), or c2s / c2f (the 128K decode, separate
-    or chained calls, one input replica)."""
+    the separate calls (c3: the hierarchical step), c4l (the prefill through candidate
+    lists, no scores written), or c2s / c2f (the 128K decode, separate or chained calls,
+    one input replica)."""
     import torch
     from synth import config, make_inputs
     if name in ("c2s", "c2f"):
@@ -270,6 +283,10 @@ def profile_workload(name, steps, warmup):
     elif name == "c3":
         cfg = config(3)
         fn = hi_step(cfg, upload_workload(make_inputs(cfg), cfg))[0]
+    elif name == "c4l":
+        cfg, d, sc, idx, out, lse = c_flat(4)
+        del sc
+        fn = lists_step(cfg, d, idx, out, lse)
     else:
         cfg, d, sc, idx, out, lse = c_flat(int(name[1:]))
         fn = flat_step(cfg, d, sc, idx, out, lse)
@@ -291,7 +308,8 @@ def measure_workloads(steps=50):
     cost shared by them), inputs resident.
       c1 tiny decode: us/step.  c3 hierarchical 1M decode: us/step, and the flat path
       (index + select over all 1M keys) on the same inputs for the HI/flat ratios.
-      c4 chunked prefill: tokens/s, and the indexer's MFMA utilisation (bf16 peak).
+      c4 chunked prefill: tokens/s (the step the fastest of the separate, chained and
+      candidate-list ways; the last writes no scores), and the indexer's MFMA utilisation.
       c5 cross-layer decode (4 layers, one selection): us/step, and the same work with
       the selection recomputed for every layer.
       cache append (the step's write side): us per call for the c2 and c3 cache shapes.
@@ -357,6 +375,14 @@ def measure_workloads(steps=50):
     def w4():
         cfg, d, sc, idx, out, lse = c_flat(4)
         us, ways = both(cfg, d, sc, idx, out, lse, 1)
+
+        def lists_select():  # the prefill path without the score write: candidate lists only
+            L.lsa_index_select(d["qI"], d["w"], d["kI"], cfg.K, cfg.S, cfg.W, k_scale=d["ks"], ctx_len=d["ctx"],
+                               idx=idx, with_scores=False)
+        us_lists = graph_us(lists_step(cfg, d, idx, out, lse))
+        ways["us_per_step_lists"] = us_lists
+        ways["us_index_select_lists"] = graph_us(lists_select)
+        us = min(us, us_lists)
         us_index = graph_us(lambda: L.lsa_index(d["qI"], d["w"], d["kI"], k_scale=d["ks"], ctx_len=d["ctx"], scores=sc))
         p0 = cfg.N - cfg.T
         pairs = sum(p0 + t + 1 for t in range(cfg.T))

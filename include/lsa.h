@@ -154,18 +154,25 @@ int32_t lsa_index(const lsa_index_desc *desc, void *stream);
  * the SI budget of a sink, a local window and a top-k fill) as one call: idx receives exactly
  * what lsa_select would select from the scores lsa_index computes ("LongCat-Flash-Lite-Sparse"
  * summary, aitrends.kr, "Good to know" and "Technical features", first bullet; the scores of
- * reading R1). The indexer primes the selection (its epilogue counts the candidates per
- * first-level bin where the kernel has one query per workgroup), so the selection skips its
- * first pass over the scores.
+ * reading R1). Two paths, by shape. Few query tokens per sequence: the indexer primes the
+ * selection (its epilogue counts the candidates per first-level bin where the kernel has
+ * one query per workgroup), so the selection skips its first pass over the scores. Prefill
+ * (H in {32, 64}, D in {64, 128}, T >= 64, at least 512 groups of four query tokens over
+ * the batch, N <= 2^19): each indexer wave scores one whole row and lists every candidate
+ * that can still be among the row's fill when it is scored (a running threshold from the
+ * row's histogram so far), and the selection ranks only the lists; the scores are written
+ * only when desc->scores is given.
  * Arguments: desc as for lsa_index in TOKENS mode without a kept map, with desc->sink and
  * desc->window the forced set and desc->select_ws ignored; desc->scores may be NULL (the
  * scores then live in the workspace); K the budget (1 <= K <= 4096, sink + window <= K); idx
  * int32 [B][T][K] as lsa_select writes it (ascending positions, then -1).
- * Workspace: lsa_index_select_workspace_bytes(desc, K) bytes (larger when desc->scores is
- * NULL), 256-byte aligned. workspace_state LSA_WS_UNKNOWN clears what must start at zero
- * (one fill kernel); LSA_WS_CLEAN skips that and is valid after a successful call with the
- * same B, T and N (every call leaves the workspace clean). Calls sharing a workspace must be
- * ordered on one stream.
+ * Workspace: lsa_index_select_workspace_bytes(desc, K) bytes, 256-byte aligned: on the
+ * prefill path the list lengths (4 bytes per row, rounded up to 256) and the lists (8 bytes
+ * per row and position: a list may hold the whole row); otherwise the selection workspace,
+ * plus the scores when desc->scores is NULL. workspace_state LSA_WS_UNKNOWN clears what
+ * must start at zero (one fill kernel; nothing on the prefill path); LSA_WS_CLEAN skips
+ * that and is valid after a successful call with the same B, T and N (every call leaves
+ * the workspace clean). Calls sharing a workspace must be ordered on one stream.
  * Errors as lsa_index and lsa_select; LSA_E_UNSUPPORTED for BLOCKS mode or a kept map.
  */
 size_t lsa_index_select_workspace_bytes(const lsa_index_desc *desc, int32_t K);

@@ -297,8 +297,15 @@ int32_t lsa_select(const lsa_select_desc *d, void *ws, size_t ws_bytes, void *st
 
 // ----------------------------------------------------------------------------- index + select
 
-// Checks of lsa_index_select's arguments; fills the indexer arguments and the workspace size.
-static int32_t index_select_check(const lsa_index_desc *d, int32_t K, lsa::IndexTokensArgs &a, size_t &ws_need) {
+// lsa_index_select's candidate-list layout: the per-row list lengths, then [rows][N]
+// composites (emission path only).
+static size_t cand_offset(int rows) { return ((size_t)rows * 4 + 255) & ~(size_t)255; }
+
+// Checks of lsa_index_select's arguments; fills the indexer arguments, the path (emit:
+// the indexer writes candidate lists that the selection reads instead of the scores) and
+// the workspace size.
+static int32_t index_select_check(const lsa_index_desc *d, int32_t K, lsa::IndexTokensArgs &a, size_t &ws_need,
+                                  bool &emit) {
     if (!d) return fail(LSA_E_NULL, "lsa_index_select: desc is NULL");
     if (d->mode != LSA_INDEX_TOKENS) return fail(LSA_E_UNSUPPORTED, "lsa_index_select: TOKENS mode only");
     if (d->kept) return fail(LSA_E_UNSUPPORTED, "lsa_index_select: no kept map (call lsa_index, then lsa_select)");
@@ -310,6 +317,12 @@ static int32_t index_select_check(const lsa_index_desc *d, int32_t K, lsa::Index
     if (K > 4096) return fail(LSA_E_UNSUPPORTED, "lsa_index_select: K=%d above 4096", K);
     if ((int64_t)d->B * d->T > kMaxGridY) return fail(LSA_E_UNSUPPORTED, "lsa_index_select: B*T too large");
     const int rows = d->B * d->T;
+    emit = lsa::index_tokens_emits(d->B, d->T, d->N, d->H, d->D, false) && lsa::select_cand_fits(d->N);
+    if (emit) {
+        // the list lengths and one list of up to N composites per row
+        ws_need = cand_offset(rows) + (size_t)rows * d->N * 8;
+        return LSA_OK;
+    }
     // the selection's workspace, then the scores when the caller does not ask for them
     ws_need = lsa::select_workspace_bytes(rows, d->N, false);
     if (!d->scores) ws_need += (size_t)rows * d->N * 4 + 256;
@@ -319,7 +332,8 @@ static int32_t index_select_check(const lsa_index_desc *d, int32_t K, lsa::Index
 size_t lsa_index_select_workspace_bytes(const lsa_index_desc *d, int32_t K) {
     lsa::IndexTokensArgs a;
     size_t need = 0;
-    if (index_select_check(d, K, a, need) != LSA_OK) return 0;
+    bool emit = false;
+    if (index_select_check(d, K, a, need, emit) != LSA_OK) return 0;
     return need;
 }
 
@@ -327,7 +341,8 @@ int32_t lsa_index_select(const lsa_index_desc *d, int32_t K, int32_t *idx, void 
                          int32_t ws_state, void *stream) {
     lsa::IndexTokensArgs a;
     size_t need = 0;
-    int32_t rc = index_select_check(d, K, a, need);
+    bool emit = false;
+    int32_t rc = index_select_check(d, K, a, need, emit);
     if (rc != LSA_OK) return rc;
     if (!idx) return fail(LSA_E_NULL, "lsa_index_select: idx is required");
     if (!aligned4(idx)) return fail(LSA_E_ALIGN, "lsa_index_select: misaligned idx");
@@ -339,6 +354,30 @@ int32_t lsa_index_select(const lsa_index_desc *d, int32_t K, int32_t *idx, void 
         return fail(LSA_E_ALIGN, "lsa_index_select: workspace not 256-byte aligned");
     hipStream_t s = reinterpret_cast<hipStream_t>(stream);
     const int rows = d->B * d->T;
+    lsa::SelectArgs sa{};
+    sa.B = d->B;
+    sa.T = d->T;
+    sa.N = d->N;
+    sa.ctx_len = d->ctx_len;
+    sa.n_cols = d->N;
+    sa.block_size = 1;
+    sa.K = K;
+    sa.sink = d->sink;
+    sa.window = d->window;
+    sa.causal = true;
+    sa.idx = idx;
+    if (emit) {
+        // the indexer lists each row's candidates that can still reach its fill (scores
+        // written only when asked for), the selection ranks the lists
+        a.cand_cnt = reinterpret_cast<uint32_t *>(ws);
+        a.cand = reinterpret_cast<uint64_t *>(reinterpret_cast<char *>(ws) + cand_offset(rows));
+        a.K = K;
+        a.sink = d->sink;
+        a.window = d->window;
+        hipError_t e = lsa::launch_index_tokens(a, s);
+        if (e != hipSuccess) return hip_status(e, "lsa_index_select");
+        return hip_status(lsa::launch_select_cand(sa, a.cand, a.cand_cnt, s), "lsa_index_select");
+    }
     if (!a.scores) {
         const size_t sel_bytes = lsa::select_workspace_bytes(rows, d->N, false);
         a.scores = reinterpret_cast<float *>((reinterpret_cast<uintptr_t>(ws) + sel_bytes + 255) & ~(uintptr_t)255);
@@ -346,21 +385,9 @@ int32_t lsa_index_select(const lsa_index_desc *d, int32_t K, int32_t *idx, void 
     // the indexer priming the selection workspace, then the selection on its scores
     rc = index_primed(d, a, ws, ws_state == LSA_WS_CLEAN, s, "lsa_index_select");
     if (rc != LSA_OK) return rc;
-    lsa::SelectArgs sa{};
-    sa.B = d->B;
-    sa.T = d->T;
-    sa.N = d->N;
-    sa.ctx_len = d->ctx_len;
     sa.scores = a.scores;
-    sa.n_cols = d->N;
-    sa.block_size = 1;
-    sa.K = K;
-    sa.sink = d->sink;
-    sa.window = d->window;
-    sa.causal = true;
     sa.primed = true;
     sa.vec = (d->N & 3) == 0;
-    sa.idx = idx;
     return hip_status(lsa::launch_select(sa, ws, s), "lsa_index_select");
 }
 

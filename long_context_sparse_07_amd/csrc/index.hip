@@ -46,6 +46,11 @@ __device__ __forceinline__ void lds_add_u32(uint32_t *p, uint32_t v) {
 }
 __device__ __forceinline__ void lds_wait_all() { asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory"); }
 
+// set lanes of mask below this lane
+__device__ __forceinline__ uint32_t lane_rank64(uint64_t mask) {
+    return __builtin_amdgcn_mbcnt_hi((uint32_t)(mask >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)mask, 0u));
+}
+
 // Workgroup barrier for the key ring: this wave's LDS operations complete first, its
 // outstanding vector memory operations do not (a workgroup fence would also wait for the
 // direct-to-LDS DMA still in flight, i.e. drain the ring). The memory clobber keeps the
@@ -105,7 +110,14 @@ __device__ __forceinline__ void row_to_th(int grp, int i, int H, int T, int &t, 
 // HIST (one query per workgroup): the epilogue also counts the selection candidates of
 // its columns per first-level bin of the selection histogram (finite scores at visible
 // positions outside the sink and the window) and adds the counts to sel_hist.
-template <int D, bool FP8, bool QF8, int MODE, int HB, bool HI, bool PRE, bool HIST, int NST>
+// EMIT (four query groups a workgroup, one query and its whole row per wave): each wave
+// keeps a histogram of its row's candidates over the top 10 order-key bits in LDS and,
+// from it, the running threshold: the bin where the candidates counted so far from the
+// top reach the fill size. The threshold only rises as candidates arrive, so a
+// candidate in a bin below it can no longer be among the row's K - |forced| largest; the
+// others are appended to the row's candidate list. At the end every candidate in a bin
+// at or above the final threshold, and so every one the selection can take, is listed.
+template <int D, bool FP8, bool QF8, int MODE, int HB, bool HI, bool PRE, bool HIST, int NST, bool EMIT = false>
 __global__ __launch_bounds__(PRE ? kThreads : 2 * kThreads) void index_tokens_kernel(IndexTokensArgs a, int groups,
                                                                                       int chunk) {
     using G = Tile<D, FP8, NST>;
@@ -122,6 +134,9 @@ __global__ __launch_bounds__(PRE ? kThreads : 2 * kThreads) void index_tokens_ke
     __shared__ int tpos[HI ? G::NST : 1][kKT];                            // HI: position of each row
     __shared__ uint32_t shist[HIST ? kSelBins : 1];                      // HIST: candidate counts
     static_assert(!HIST || (MODE == ONEQ && !PRE), "the histogram needs one query per workgroup");
+    static_assert(!EMIT || (MODE == ONEQ && PRE && !HI), "emission: one whole flat row per wave");
+    constexpr int kEB = 1024;  // EMIT: running-threshold bins (top 10 order-key bits)
+    __shared__ uint32_t whist[EMIT ? 4 : 1][EMIT ? kEB : 1];
 
     const int tid = threadIdx.x;
     const int lane = tid & 63, half = lane >> 5, l32 = lane & 31;
@@ -138,12 +153,23 @@ __global__ __launch_bounds__(PRE ? kThreads : 2 * kThreads) void index_tokens_ke
     constexpr bool OWN = !PRE;
     const int grp = PRE ? blockIdx.y * 4 + wave : blockIdx.y;
     const bool active = grp < groups;
-    int f_se = 0, f_wl = 0;  // HIST: forced set of the workgroup's query
+    int f_se = 0, f_wl = 0;  // HIST / EMIT: forced set of the workgroup's (wave's) query
     if constexpr (HIST) {
         for (int i = tid; i < kSelBins; i += NT) shist[i] = 0;
         forced_bounds(ctx - T + grp, a.sink, a.window, f_se, f_wl);
     }
     if constexpr (HIST) __syncthreads();
+    // EMIT: this wave's fill size, running threshold bin and list length (wave-uniform)
+    uint32_t e_m = 0, e_thr = 0, e_cnt = 0;
+    uint64_t *e_row = nullptr;
+    if constexpr (EMIT) {
+        forced_bounds(ctx - T + grp, a.sink, a.window, f_se, f_wl);
+        const int pq = ctx - T + grp;
+        e_m = (uint32_t)max(0, a.K - (f_se + max(0, pq - f_wl + 1)));
+        if (e_m == 0) e_thr = kEB;  // an empty fill lists nothing
+        for (int i = lane; i < kEB; i += 64) whist[wave][i] = 0;  // each wave only touches its own
+        e_row = a.cand + (int64_t)(b * T + min(grp, T - 1)) * a.N;
+    }
 
     // ---- query fragments (A operand, rows = query heads) and head weights (compute waves)
     // lane (l32, half) holds dims (D / 2) half .. +D/2 of row 32 hb + l32
@@ -365,12 +391,27 @@ __global__ __launch_bounds__(PRE ? kThreads : 2 * kThreads) void index_tokens_ke
             const float s = half_pair_sum((s4[0] + s4[1]) + (s4[2] + s4[3]));
             const int t = grp;
             const int p = ctx - T + t;
+            bool emit = false;
+            uint64_t comp = 0;
             if (half == 0 && col < c1) {
                 const bool vis = pos >= 0 && pos <= p;
                 const float v = vis ? s * sc : kNegInf;
-                write_score(t, col, v);
+                if (!EMIT || a.scores) write_score(t, col, v);
                 if constexpr (HIST)
                     if (vis && pos >= f_se && pos < f_wl && v > kNegInf) lds_add_u32(&shist[order_key(v) >> kSelShift], 1u);
+                if constexpr (EMIT) {
+                    if (vis && pos >= f_se && pos < f_wl && v > kNegInf) {
+                        const uint32_t key = order_key(v);
+                        lds_add_u32(&whist[wave][key >> 22], 1u);
+                        emit = (key >> 22) >= e_thr;
+                        comp = ((uint64_t)key << 32) | (uint32_t)~(uint32_t)pos;
+                    }
+                }
+            }
+            if constexpr (EMIT) {  // the whole wave takes part (uniform call)
+                const uint64_t eb = __ballot(emit);
+                if (emit) e_row[e_cnt + lane_rank64(eb)] = comp;
+                e_cnt += (uint32_t)__popcll(eb);
             }
         } else if constexpr (MODE == Q4) {
             float part[4] = {0.0f, 0.0f, 0.0f, 0.0f};
@@ -440,6 +481,38 @@ __global__ __launch_bounds__(PRE ? kThreads : 2 * kThreads) void index_tokens_ke
                     const int col = c0 + it * kKT + row;
                     epilogue(acc[sb & 1], col, col < c1 && col < N ? col : -1, FP8 ? tscale[row] : 1.0f);
                 }
+                if constexpr (EMIT) {
+                    // the running threshold, every fourth tile: lane l sums bins 1023 - 16 l - e
+                    // (from the top), a wave scan finds the lane where the count reaches the
+                    // fill size, that lane the bin (this wave's own adds are ordered before)
+                    if ((it & 3) == 3) {
+                        lds_wait_all();
+                        uint32_t hv[16], sum = 0;
+#pragma unroll
+                        for (int e = 0; e < 16; ++e) {
+                            hv[e] = whist[wave][kEB - 1 - 16 * lane - e];
+                            sum += hv[e];
+                        }
+                        uint32_t cum = sum;
+#pragma unroll
+                        for (int o = 1; o < 64; o <<= 1) {
+                            const uint32_t y = __shfl_up(cum, o, 64);
+                            if (lane >= o) cum += y;
+                        }
+                        const uint64_t reach = __ballot(e_m > 0 && cum >= e_m);
+                        if (reach) {
+                            const int L = __ffsll((unsigned long long)reach) - 1;
+                            int bin = 0;
+                            uint32_t acc2 = cum - sum;
+#pragma unroll
+                            for (int e = 0; e < 16; ++e) {
+                                acc2 += hv[e];
+                                if (bin == 0 && acc2 >= e_m) bin = kEB - 1 - 16 * lane - e;
+                            }
+                            e_thr = (uint32_t)__builtin_amdgcn_readlane(bin, L);
+                        }
+                    }
+                }
             }
         }
     } else {
@@ -480,6 +553,8 @@ __global__ __launch_bounds__(PRE ? kThreads : 2 * kThreads) void index_tokens_ke
             else epilogue(acc1, pcol, ppos, psc);
         }
     }
+    if constexpr (EMIT)
+        if (active && lane == 0) a.cand_cnt[b * T + grp] = e_cnt;
     {  // tiles past every query's position: -inf
         constexpr int NQ = PRE ? 4 : QPG;
         for (int e = nvis * kKT + tid; e < ntiles * kKT * NQ; e += NT) {
@@ -489,7 +564,7 @@ __global__ __launch_bounds__(PRE ? kThreads : 2 * kThreads) void index_tokens_ke
             if (off < nvis * kKT) continue;
             int col = c0 + off;
             int t = PRE ? ((int)blockIdx.y * 4 + q) : grp * QPG + q;
-            if (col < c1 && t < T) write_score(t, col, kNegInf);
+            if (col < c1 && t < T && (!EMIT || a.scores)) write_score(t, col, kNegInf);
         }
     }
     if constexpr (HIST) {
@@ -611,8 +686,24 @@ hipError_t launch_tokens_t(const IndexTokensArgs &a, hipStream_t s) {
     return hipGetLastError();
 }
 
+// Candidate emission (a.cand): the shared-tile kernel with one whole row per wave, a
+// 3-stage key ring (the four waves' running-threshold histograms take the fourth stage's
+// LDS, so two workgroups still fit on a compute unit).
+template <int D, bool FP8, bool QF8, int HB>
+hipError_t launch_tokens_emit(const IndexTokensArgs &a, hipStream_t s) {
+    constexpr int NST = 3;
+    using G = Tile<D, FP8, NST>;
+    const int groups = a.T;
+    const dim3 grid(1, (groups + 3) / 4, a.B);
+    const size_t lds = (size_t)G::NST * G::STAGE;
+    hipLaunchKernelGGL((index_tokens_kernel<D, FP8, QF8, ONEQ, HB, false, true, false, NST, true>), grid,
+                       dim3(kThreads), lds, s, a, groups, a.n_out);
+    return hipGetLastError();
+}
+
 template <int D, bool FP8, bool QF8 = false>
 hipError_t launch_tokens_d(const IndexTokensArgs &a, hipStream_t s) {
+    if (a.cand) return a.H == 32 ? launch_tokens_emit<D, FP8, QF8, 1>(a, s) : launch_tokens_emit<D, FP8, QF8, 2>(a, s);
     const bool hi = a.kept != nullptr;
     if (a.sel_hist) {  // one query per workgroup: the epilogue builds the selection histogram
         if (hi) {
@@ -644,6 +735,14 @@ hipError_t launch_tokens_d(const IndexTokensArgs &a, hipStream_t s) {
 bool index_tokens_fused_hist(int H, int T, bool hi) {
     if (hi) return true;
     return (H == 32 || H == 64) && T < 64;
+}
+
+bool index_tokens_emits(int B, int T, int N, int H, int D, bool hi) {
+    // the shared-tile kernel (T >= 64) with whole rows per workgroup: at least as many
+    // groups of four query tokens as the 512 workgroups it aims for
+    (void)N;
+    if (hi || !(H == 32 || H == 64) || (D != 64 && D != 128) || T < 64) return false;
+    return (int64_t)B * ((T + 3) / 4) >= 512;
 }
 
 bool index_tokens_supported(int H, int D, bool hi) {

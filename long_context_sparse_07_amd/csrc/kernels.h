@@ -23,9 +23,18 @@ struct IndexTokensArgs {
     float *scores;          // [B][T][n_out]
     int n_out;
     uint32_t *sel_hist;     // optional: selection histogram [B*T][kSelBins] to add candidates to
-    int sink, window;       // forced set excluded from sel_hist
+    int sink, window;       // forced set excluded from sel_hist (and from the emitted candidates)
+    // optional (four query rows a workgroup, whole rows): every candidate whose score can
+    // still be among its row's K - |forced| largest is appended to cand[row] as its 64-bit
+    // composite (order key << 32 | ~position); cand_cnt[row] receives the count
+    uint64_t *cand;         // [B*T][N]
+    uint32_t *cand_cnt;     // [B*T]
+    int K;                  // the selection budget (the fill is K - |forced|)
 };
 hipError_t launch_index_tokens(const IndexTokensArgs &a, hipStream_t s);
+// true when the indexer can emit its rows' candidates (a.cand): flat rows scored by the
+// kernel that gives each of four waves one whole query row (many query tokens)
+bool index_tokens_emits(int B, int T, int N, int H, int D, bool hi);
 
 bool index_tokens_supported(int H, int D, bool hi);
 // true when the token kernel for (H, T, hi) builds sel_hist in its epilogue (one query
@@ -128,6 +137,10 @@ struct SelectArgs {
 size_t select_workspace_bytes(int rows, int n_cols, bool kept);
 size_t select_zero_bytes(int rows);  // the part of the workspace kept at zero between calls
 hipError_t launch_select(const SelectArgs &a, void *ws, hipStream_t s);
+// The selection of flat rows from the candidate lists the indexer emitted (cand [rows][N],
+// cand_cnt [rows]); one workgroup per row, nothing else in the workspace.
+hipError_t launch_select_cand(const SelectArgs &a, const uint64_t *cand, const uint32_t *cand_cnt, hipStream_t s);
+bool select_cand_fits(int n_cols);
 // Histogram pass alone (the selection's first pass), for an index call that primes a
 // selection workspace with a kernel that cannot build it in its epilogue.
 hipError_t launch_select_hist(const SelectArgs &a, void *ws, hipStream_t s);

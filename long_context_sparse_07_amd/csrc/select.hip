@@ -423,6 +423,159 @@ __global__ __launch_bounds__(kRT) void select_resolve_kernel(SelectArgs a, Ws w,
     if (tid < kCtr) gctr[tid] = 0;
 }
 
+// ----------------------------------------------------------------------------- candidate lists
+// The selection of a flat row from the candidate list its indexer wrote (every candidate
+// whose bin could still reach the row's fill when it was scored; see the indexer), one
+// workgroup per row with the row's state in LDS. Every candidate in a bin at or above the
+// row's threshold bin is in the list, so the list's own first-level histogram agrees with
+// the row's from the threshold bin up, and the threshold bin and the count above it come
+// out the same. Then: candidates above the bin set their bit in an LDS bitmap of the row's
+// positions, those in it go to an LDS tie list, the ties are ranked as in the resolve
+// (or, when the LDS list overflows, by radix passes over the candidate list), and the
+// bitmap is compacted into ascending positions.
+constexpr int kCandT = 1024;
+constexpr int kCandMaxWords = 16384;  // positions per row up to 2^19 (bitmap in LDS)
+
+__global__ __launch_bounds__(kCandT) void select_cand_kernel(SelectArgs a, const uint64_t *cand,
+                                                             const uint32_t *cand_cnt, int words, int tcap) {
+    extern __shared__ __attribute__((aligned(16))) unsigned char dyn[];
+    uint32_t *lbits = reinterpret_cast<uint32_t *>(dyn);                                  // [words]
+    uint64_t *lties = reinterpret_cast<uint64_t *>(dyn + (size_t)((words + 3) & ~3) * 4);  // [tcap]
+    __shared__ __attribute__((aligned(16))) uint32_t h[kB2];  // first level, then second level
+    __shared__ uint32_t h256[256];
+    __shared__ uint32_t scr[32];
+    __shared__ uint32_t s_nt;
+    constexpr int NT = kCandT;
+    const int row = blockIdx.x, tid = threadIdx.x, lane = tid & 63;
+    const Row r = make_row(a, row);
+    const uint32_t m = (uint32_t)max(r.m, 0);
+    const uint32_t ne = cand_cnt[row];
+    const uint64_t *list = cand + (int64_t)row * a.N;
+
+    for (int i = tid; i < words; i += NT) lbits[i] = 0;
+    for (int i = tid; i < kSelBins; i += NT) h[i] = 0;
+    if (tid == 0) s_nt = 0;
+    __syncthreads();
+    // the list in rounds of U entries per thread (U loads in flight)
+    constexpr int U = 8;
+    auto round = [&](uint32_t base, uint64_t (&c)[U], bool (&ok)[U]) __attribute__((always_inline)) {
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            const uint32_t i = base + u * NT + tid;
+            ok[u] = i < ne;
+            c[u] = list[ok[u] ? i : 0];
+        }
+    };
+    // ---- first-level histogram of the list (lanes that share a bin add once)
+    for (uint32_t base = 0; base < ne; base += U * NT) {
+        uint64_t c[U];
+        bool ok[U];
+        round(base, c, ok);
+#pragma unroll
+        for (int u = 0; u < U; ++u) wave_hist_add(h, ok[u] ? (int)((uint32_t)(c[u] >> 32) >> kSelShift) : -1);
+    }
+    __syncthreads();
+    uint32_t hv[2];
+    hv[0] = h[kSelBins - 1 - 2 * tid];
+    hv[1] = h[kSelBins - 2 - 2 * tid];
+    const BinPick bp = pick_bin<NT, 2>(hv, m, scr);  // its barriers follow every thread's reads
+    const uint32_t b1 = (uint32_t)bp.bin;
+
+    // ---- classify: above the bin into the bitmap, in it into the tie list (one LDS
+    // reservation per wave and round)
+    if (bp.mode != 0) {
+        for (uint32_t base = 0; base < ne; base += U * NT) {
+            uint64_t c[U];
+            bool ok[U];
+            round(base, c, ok);
+            uint64_t tb[U];
+            uint32_t ntw = 0;
+#pragma unroll
+            for (int u = 0; u < U; ++u) {
+                const uint32_t d1 = (uint32_t)(c[u] >> kB1Shift);
+                if (ok[u] && (bp.mode == 1 || d1 > b1)) {
+                    const int pos = comp_pos(c[u]);
+                    atomicOr(&lbits[pos >> 5], 1u << (pos & 31));
+                }
+                tb[u] = __ballot(ok[u] && bp.mode == 2 && d1 == b1);
+                ntw += (uint32_t)__popcll(tb[u]);
+            }
+            if (ntw) {  // uniform per wave
+                uint32_t sb = 0;
+                if (lane == 0) sb = atomicAdd(&s_nt, ntw);
+                sb = __builtin_amdgcn_readfirstlane(sb);
+#pragma unroll
+                for (int u = 0; u < U; ++u) {
+                    if ((tb[u] >> lane) & 1ull) {
+                        const uint32_t slot = sb + lane_rank(tb[u]);
+                        if (slot < (uint32_t)tcap) lties[slot] = c[u];
+                    }
+                    sb += (uint32_t)__popcll(tb[u]);
+                }
+            }
+        }
+    }
+    __syncthreads();
+
+    // ---- the chosen ties
+    if (bp.mode == 2) {
+        const uint32_t ntie = s_nt;
+        const uint32_t need1 = m > bp.above ? m - bp.above : 0u;
+        if (ntie <= (uint32_t)tcap) {
+            for (int i = tid; i < kB2; i += NT) h[i] = 0;
+            __syncthreads();
+            const uint64_t thr = tie_threshold<NT>([&](uint32_t i) { return lties[i]; }, ntie, need1, b1, h, h256, scr);
+            for (uint32_t i = tid; i < ntie; i += NT) {
+                if (lties[i] >= thr) {
+                    const int pos = comp_pos(lties[i]);
+                    atomicOr(&lbits[pos >> 5], 1u << (pos & 31));
+                }
+            }
+        } else {
+            // the tie list did not fit: radix passes over the whole candidate list (entries
+            // outside bin b1 do not match the prefix and are left out)
+            const uint64_t pre = (uint64_t)b1 << kB1Shift;
+            auto get = [&](uint32_t i) { return list[i]; };
+            const uint64_t thr = radix_kth<NT>(FnSrc<decltype(get)>{get, (int)ne}, need1, pre, kB1Shift, h256, scr);
+            for (uint32_t i = tid; i < ne; i += NT) {
+                const uint64_t c = list[i];
+                if ((c >> kB1Shift) == (uint64_t)b1 && c >= thr) {
+                    const int pos = comp_pos(c);
+                    atomicOr(&lbits[pos >> 5], 1u << (pos & 31));
+                }
+            }
+        }
+    }
+    __syncthreads();
+
+    // ---- ascending output: sink, the fill, the window, then -1
+    int32_t *dst = a.idx + (int64_t)row * a.K;
+    const int nsink = a.causal ? r.f_sink_end : 0;
+    const int nwin = a.causal ? max(0, r.p - r.f_win_lo + 1) : 0;
+    uint32_t nfill = 0;
+    if (bp.mode != 0) {
+        const int per = (words + NT - 1) / NT;
+        const int w0 = min(words, tid * per), w1 = min(words, w0 + per);
+        uint32_t cn = 0;
+        for (int i = w0; i < w1; ++i) cn += __popc(lbits[i]);
+        uint32_t off = block_exscan<NT>(cn, scr, &nfill);
+        nfill = min(nfill, m);
+        for (int i = w0; i < w1; ++i) {
+            uint32_t bits = lbits[i];
+            while (bits && off < nfill) {
+                dst[nsink + off] = i * 32 + __ffs(bits) - 1;
+                bits &= bits - 1;
+                ++off;
+            }
+        }
+    }
+    for (int s = tid; s < nsink; s += NT) dst[s] = s;
+    const int wbase = nsink + (int)nfill;
+    for (int j = tid; j < nwin; j += NT)
+        if (wbase + j < a.K) dst[wbase + j] = r.f_win_lo + j;
+    for (int i = wbase + nwin + tid; i < a.K; i += NT) dst[i] = -1;
+}
+
 __global__ void clear_kernel(uint4 *p, size_t n16, uint8_t *tail, size_t ntail) {
     const size_t i = blockIdx.x * (size_t)blockDim.x + threadIdx.x;
     const size_t stride = (size_t)gridDim.x * blockDim.x;
@@ -492,6 +645,30 @@ hipError_t launch_select_front(const SelectArgs &a, void *wsp, hipStream_t s) {
     if (a.kept) hipLaunchKernelGGL(select_filter_kernel<true>, dim3(parts, rows), dim3(kHT), 0, s, a, w, pc);
     else hipLaunchKernelGGL(select_filter_kernel<false>, dim3(parts, rows), dim3(kHT), 0, s, a, w, pc);
     return hipGetLastError();
+}
+
+size_t select_cand_lds(int n_cols, int &words, int &tcap) {
+    words = bit_words(n_cols);
+    if (words > kCandMaxWords) return 0;
+    const size_t static_bytes = (size_t)kB2 * 4 + 256 * 4 + 32 * 4 + 16;
+    const size_t budget = 160 * 1024 - static_bytes - 512;
+    const size_t bits = (size_t)((words + 3) & ~3) * 4;
+    if (bits + 1024 * 8 > budget) return 0;
+    tcap = (int)min((size_t)16384, (budget - bits) / 8);
+    return bits + (size_t)tcap * 8;
+}
+
+hipError_t launch_select_cand(const SelectArgs &a, const uint64_t *cand, const uint32_t *cand_cnt, hipStream_t s) {
+    int words = 0, tcap = 0;
+    const size_t lds = select_cand_lds(a.n_cols, words, tcap);
+    if (!lds) return hipErrorInvalidValue;  // (callers check select_cand_fits first)
+    hipLaunchKernelGGL(select_cand_kernel, dim3(a.B * a.T), dim3(kCandT), lds, s, a, cand, cand_cnt, words, tcap);
+    return hipGetLastError();
+}
+
+bool select_cand_fits(int n_cols) {
+    int words, tcap;
+    return select_cand_lds(n_cols, words, tcap) != 0;
 }
 
 hipError_t launch_select(const SelectArgs &a, void *wsp, hipStream_t s) {

@@ -324,3 +324,22 @@ def _tgt_desc(**kw):
 ])
 def test_index_target_argument_errors(kw, code):
     assert L.lib().lsa_index_target(ctypes.byref(_tgt_desc(**kw)), None) == code
+
+
+def test_index_select_workspace_by_path():
+    # decode rows (one query token per sequence): the selection workspace, plus the scores
+    # when the caller does not take them; prefill rows (thousands of query tokens per
+    # sequence): the candidate lists, 4 bytes per row then 8 per row and position
+    lib = L.lib()
+    dec = _index_desc(B=2, T=1, N=8192, sink=64, window=512)
+    with_sc = lib.lsa_index_select_workspace_bytes(ctypes.byref(dec), 2048)
+    dec.scores = None
+    assert lib.lsa_index_select_workspace_bytes(ctypes.byref(dec), 2048) >= with_sc + 2 * 8192 * 4
+    pre = _index_desc(B=1, T=2048, N=8192, sink=64, window=512)
+    want = 2048 * 4 + 2048 * 8192 * 8
+    assert lib.lsa_index_select_workspace_bytes(ctypes.byref(pre), 2048) == want
+    pre.scores = None
+    assert lib.lsa_index_select_workspace_bytes(ctypes.byref(pre), 2048) == want
+    # H = 16 has no whole-row prefill kernel: the selection workspace again
+    pre16 = _index_desc(B=1, T=2048, N=8192, H=16, sink=64, window=512)
+    assert lib.lsa_index_select_workspace_bytes(ctypes.byref(pre16), 2048) != 2048 * 4 + 2048 * 8192 * 8
