@@ -428,6 +428,371 @@ __global__ __launch_bounds__(64 * HW) void attend_kernel(AttendArgs a, uint16_t 
     if constexpr (FUSED) sel::release_slice<NT>(f.w, (int)selrow, nslices, slice);
 }
 
+// ----------------------------------------------------------------------------- MLA, 32 heads
+// MLA latent rows (576 wide, V = the first 512 columns) with a multiple of 32 query heads
+// per KV head. One workgroup = (layer, sequence, query token, KV head, 32-head block, split
+// of the selected rows), 4 waves, rounds of 128 selected rows:
+//   - wave w gathers tile w of the round (32 rows, 36 KB) into its own LDS slot (the same
+//     block layout and DMA as above; each wave waits for its own loads only) and computes
+//     S^T = K Q^T for its 32 rows and the block's 32 heads on v_mfma_f32_32x32x16_bf16,
+//     with the 32 heads' Q held in registers;
+//   - the waves agree on each head's reference maximum through LDS and write their
+//     probabilities (bf16, in the B-operand layout of the value product) to LDS;
+//   - wave w accumulates O^T for value columns 128 w .. 128 w + 127 over the round's four
+//     tiles, V^T by LDS transpose reads.
+// Every K and V byte in LDS is read once per 32 heads (twice as few reads as the 16-head
+// layout above), and a split covers 128 rows, so the split partials of the 128K decode are
+// half as many.
+constexpr int kMRound = 128;   // selected rows per round (4 waves x 32)
+constexpr int kMMaxPos = 1024; // rows per split held in the LDS position list (fused resolve)
+constexpr int kMKB = 18;       // 64-byte blocks per 576-wide row
+constexpr int kMStage = kMKB * kBlk;
+constexpr int kMLdsFixed = 4 * kMStage + 8192 + 1024;  // slots, probabilities, maxima and sums
+
+template <bool OUTF32, bool FUSED>
+__global__ __launch_bounds__(256) void attend_mla_kernel(AttendArgs a, uint16_t *po, float *pml, int R, int HB,
+                                                         FuseArgs f) {
+    constexpr int NT = 256, KS = 36, DV = 512;
+    extern __shared__ __attribute__((aligned(16))) unsigned char lds[];
+    u32x4 *pbuf = reinterpret_cast<u32x4 *>(lds + 4 * kMStage);     // [4 tiles][2 K-blocks][64 lanes]
+    float *mx = reinterpret_cast<float *>(lds + 4 * kMStage + 8192);  // [4][32] tile maxima
+    float *lsm = mx + 128;                                            // [4][32] row sums
+    int *posbuf = reinterpret_cast<int *>(lds + kMLdsFixed);         // [R] (FUSED)
+
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int n32 = lane & 31, g = lane >> 5;
+    const int T = a.T, Hq = a.Hq, Hkv = a.Hkv, K = a.K;
+    const int nsplit = gridDim.x / HB;
+    const int split = blockIdx.x % nsplit, hb = blockIdx.x / nsplit;
+    const int t = blockIdx.y / Hkv, kvh = blockIdx.y % Hkv;
+    const int layer = blockIdx.z / a.B, b = blockIdx.z % a.B;
+    const int gq = Hq / Hkv;
+    const int hq = kvh * gq + 32 * hb + n32;  // this lane's query head
+    const int r0 = split * R;
+    const int nrows = max(0, min(K, r0 + R) - r0);
+    const int ntile = (nrows + 31) / 32;
+    const int nround = (ntile + 3) / 4;
+    const int64_t selrow = (int64_t)b * T + t;
+    const int64_t bofs = a.bt ? 0 : b * a.ksb;
+    auto phys = [&](int s) -> int {  // cache row of position s, -1 if its page is unmapped
+        if (!a.bt) return s;
+        const int pg = s / a.page_size;
+        if (pg >= a.max_pages) return -1;
+        const int pp = a.bt[(int64_t)b * a.max_pages + pg];
+        return (pp >= 0 && pp < a.num_pages) ? pp * a.page_size + (s - pg * a.page_size) : -1;
+    };
+    bf16x8 bq[KS];  // B operand of S^T: head n32, dims 16 ks + 8 g .. +8
+    auto load_q = [&]() __attribute__((always_inline)) {
+        const uint16_t *qp = a.q + layer * a.lsq + (selrow * Hq + hq) * 576 + 8 * g;
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks) bq[ks] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4 *>(qp + 16 * ks));
+    };
+    if constexpr (FUSED) load_q();  // its latency hidden under the selection's
+    const int nslices = nsplit * HB * Hkv * a.L;
+    const int slice = split + nsplit * (hb + HB * (kvh + Hkv * layer));
+    if constexpr (FUSED) {
+        sel::SliceLds S;
+        unsigned char *p = lds;
+        S.ties = reinterpret_cast<uint64_t *>(p);
+        p += (size_t)f.tl * 8;
+        S.h = reinterpret_cast<uint32_t *>(p);
+        p += sel::kB2 * 4;
+        S.h256 = reinterpret_cast<uint32_t *>(p);
+        p += 256 * 4;
+        S.scr = reinterpret_cast<uint32_t *>(p);
+        p += 32 * 4;
+        S.bits = reinterpret_cast<uint32_t *>(p);
+        S.tl = f.tl;
+        S.pw_log = f.pw_log;
+        S.bits_lds = f.bits_lds != 0;
+        sel::resolve_slice<NT>(f.sa, f.w, (int)selrow, r0, r0 + nrows, S, posbuf);  // ends with a barrier
+        if (kvh == 0 && layer == 0 && hb == 0) {
+            int32_t *dst = f.sa.idx + selrow * K + r0;
+            for (int i = tid; i < nrows; i += NT) dst[i] = posbuf[i];
+        }
+        if (a.bt) {  // positions -> cache rows (or -1), each thread its own entries
+            for (int i = tid; i < nrows; i += NT) {
+                const int ps = posbuf[i];
+                posbuf[i] = (ps >= 0 && ps < a.N) ? phys(ps) : -1;
+            }
+        }
+        __syncthreads();  // the resolve's working set (the slots) is free, the list complete
+    }
+    const int32_t *idxrow = FUSED ? nullptr : a.idx + (a.idx_shared ? (int64_t)b : selrow) * K + r0;
+    const int pmax = a.idx_shared ? (a.ctx_len ? a.ctx_len[b] : a.N) - T + t : 0x7FFFFFFF;
+    const uint16_t *kbase = a.k + layer * a.lsk + bofs + kvh * a.ksh;
+    auto rowpos = [&](int i) {  // cache row of selected row i of the split, -1 if none
+        if constexpr (FUSED) {
+            const int s = i < nrows ? posbuf[i] : -1;
+            return (s >= 0 && (a.bt || s < a.N)) ? s : -1;
+        } else {
+            const int s = i < nrows ? idxrow[i] : -1;
+            return (s >= 0 && s < a.N && s <= pmax) ? phys(s) : -1;
+        }
+    };
+    // ---- DMA of tile j into this wave's slot: instruction n fills block n / 2 for rows
+    // 16 (n & 1) .. +15; lane l writes row 16 (n & 1) + l / 4, physical chunk l & 3
+    const int drow = lane >> 2;
+    const int dchk0 = slot(lane & 3, drow), dchk1 = slot(lane & 3, drow + 16);
+    lds_u8 *myslot = (lds_u8 *)lds + wave * kMStage;
+    auto issue = [&](int p0, int p1) {  // positions (>= 0) of rows drow, drow + 16
+        const uint16_t *s0 = kbase + (int64_t)p0 * a.ksn, *s1 = kbase + (int64_t)p1 * a.ksn;
+#pragma unroll
+        for (int n = 0; n < 2 * kMKB; ++n) {
+            const int blk = n >> 1, hi = n & 1;
+            const uint16_t *src = (hi ? s1 : s0) + 8 * (4 * blk + (hi ? dchk1 : dchk0));
+            __builtin_amdgcn_global_load_lds((const glb_void_t *)src, (lds_void_t *)(myslot + blk * kBlk + 1024 * hi),
+                                             16, 0, 0);
+        }
+    };
+    // rows of this wave's tile in round rd: positions of rows drow, drow + 16, and the mask
+    // of valid rows (bit r: row r)
+    auto tile_rows = [&](int rd, int &p0, int &p1) {
+        const int j = 4 * rd + wave;
+        p0 = j < ntile ? rowpos(32 * j + drow) : -1;
+        p1 = j < ntile ? rowpos(32 * j + drow + 16) : -1;
+    };
+    auto tile_mask = [&](int p0, int p1) -> uint32_t {
+        const int a0 = __shfl(p0, 4 * (lane & 15), 64), a1 = __shfl(p1, 4 * (lane & 15), 64);
+        const bool ok = lane < 32 && (lane < 16 ? a0 : a1) >= 0;
+        return (uint32_t)__ballot(ok);
+    };
+    // the positions are requested first, then Q (its transfer overlaps their latency),
+    // then the DMA of the first tile
+    int cp0, cp1;
+    tile_rows(0, cp0, cp1);
+    if constexpr (!FUSED) load_q();
+    if (wave < ntile) issue(max(cp0, 0), max(cp1, 0));
+    uint32_t vm = tile_mask(cp0, cp1);
+
+    f32x16 o[4];
+#pragma unroll
+    for (int db = 0; db < 4; ++db)
+#pragma unroll
+        for (int e = 0; e < 16; ++e) o[db][e] = 0.0f;
+    float m_run = kNegInf, l_run = 0.0f;
+    const float sl2 = a.scale * kLog2e;
+    // K fragment (A operand of S^T): row n32, dims 16 ks + 8 g .. +8 = block ks / 2,
+    // logical chunk 2 (ks & 1) + g
+    const int koff0 = n32 * 64 + slot(g, n32) * 16, koff1 = n32 * 64 + slot(2 + g, n32) * 16;
+    // V^T transpose reads (A operand of O^T): 16-lane group c = lane / 16 reads rows
+    // 16 kb + 8 h + 4 g .. +3 and value columns 32 db + 16 (c & 1) .. +15: lane i of the
+    // group points at row +i/4, columns +4 (i & 3) (chunk 2 (c & 1) + (i & 3) / 2, bytes
+    // 8 (i & 1)) and receives the column 32 db + (lane & 31) of the four rows
+    const int vi = lane & 15, vc = (lane >> 4) & 1;
+    const int vchunk = 2 * vc + ((vi & 3) >> 1);
+    int voff[2][2];
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+            const int row = 16 * kb + 8 * h + 4 * g + (vi >> 2);
+            voff[kb][h] = row * 64 + slot(vchunk, row) * 16 + 8 * (vi & 1);
+        }
+
+    for (int rd = 0; rd < nround; ++rd) {
+        const int j = 4 * rd + wave;
+        const bool have = j < ntile;
+        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // this wave's tile (and Q) landed
+        int np0 = -1, np1 = -1;
+        if (rd + 1 < nround) tile_rows(rd + 1, np0, np1);
+        // ---- S^T for this wave's tile: st[e] = row 8 (e / 4) + 4 g + (e & 3), head n32
+        float z[16];
+        float mt = kNegInf;
+        if (have) {
+            f32x16 st;
+#pragma unroll
+            for (int e = 0; e < 16; ++e) st[e] = 0.0f;
+            const lds_u32x4 *k0 = (const lds_u32x4 *)(myslot + koff0);
+            const lds_u32x4 *k1 = (const lds_u32x4 *)(myslot + koff1);
+            auto kload = [&](int ks) { return (ks & 1) ? k1[(ks >> 1) * (kBlk / 16)] : k0[(ks >> 1) * (kBlk / 16)]; };
+            // K fragments four steps ahead, two accumulator chains (even and odd steps), so
+            // neither the LDS latency nor the accumulation dependency stalls each step
+            constexpr int PF = 4;
+            u32x4 kf[PF];
+#pragma unroll
+            for (int i = 0; i < PF; ++i) kf[i] = kload(i);
+            f32x16 st1;
+#pragma unroll
+            for (int e = 0; e < 16; ++e) st1[e] = 0.0f;
+#pragma unroll
+            for (int ks = 0; ks < KS; ++ks) {
+                const bf16x8 ka = __builtin_bit_cast(bf16x8, kf[ks % PF]);
+                if (ks + PF < KS) kf[ks % PF] = kload(ks + PF);
+                if (ks & 1) st1 = mfma32(ka, bq[ks], st1);
+                else st = mfma32(ka, bq[ks], st);
+                __builtin_amdgcn_sched_barrier(0);
+            }
+#pragma unroll
+            for (int e = 0; e < 16; ++e) st[e] += st1[e];
+#pragma unroll
+            for (int e = 0; e < 16; ++e) {
+                const int row = 8 * (e >> 2) + 4 * g + (e & 3);
+                const float v = ((vm >> row) & 1u) ? st[e] * sl2 : kNegInf;
+                z[e] = v;
+                mt = fmaxf(mt, v);
+            }
+            mt = fmaxf(mt, __shfl_xor(mt, 32, 64));
+        }
+        if (lane < 32) mx[wave * 32 + n32] = mt;
+        __syncthreads();
+        // ---- the round's reference: every wave takes the same decisions from the same maxima
+        const float mr = fmaxf(fmaxf(mx[n32], mx[32 + n32]), fmaxf(mx[64 + n32], mx[96 + n32]));
+        const bool bump = mr > m_run + 8.0f;  // also when m_run is -inf and the round is not empty
+        if (__ballot(bump)) {
+            const float m_new = bump ? mr : m_run;
+            const float alpha = m_run == kNegInf ? 0.0f : __builtin_amdgcn_exp2f(m_run - m_new);
+            if (__ballot(bump && m_run != kNegInf)) {
+#pragma unroll
+                for (int db = 0; db < 4; ++db) o[db] *= alpha;
+            }
+            l_run *= alpha;
+            m_run = m_new;
+        }
+        if (have) {
+            const float m_use = m_run == kNegInf ? 0.0f : m_run;
+            float p[16];
+            float psum = 0.0f;
+#pragma unroll
+            for (int e = 0; e < 16; ++e) {
+                p[e] = z[e] == kNegInf ? 0.0f : __builtin_amdgcn_exp2f(z[e] - m_use);
+                psum += p[e];
+            }
+            l_run += psum;
+            // P^T (B operand of O^T, K-block kb): k slot e of lane group g <-> row
+            // 16 kb + 8 (e / 4) + 4 g + (e & 3), i.e. this lane's own p[8 kb + e]
+            typedef __attribute__((__vector_size__(8 * sizeof(__bf16)))) __bf16 bf16v8;
+#pragma unroll
+            for (int kb = 0; kb < 2; ++kb) {
+                const bf16v8 pb = {(__bf16)p[8 * kb], (__bf16)p[8 * kb + 1], (__bf16)p[8 * kb + 2], (__bf16)p[8 * kb + 3],
+                                   (__bf16)p[8 * kb + 4], (__bf16)p[8 * kb + 5], (__bf16)p[8 * kb + 6], (__bf16)p[8 * kb + 7]};
+                pbuf[(wave * 2 + kb) * 64 + lane] = __builtin_bit_cast(u32x4, pb);
+            }
+        }
+        __syncthreads();
+        // ---- O^T += V^T P^T over the round's tiles, value columns 128 wave .. +127
+        // batches (tile jj, K-block kb) in order; the next batch's LDS reads are issued
+        // before the current batch's products (two register sets)
+        const int nb = 2 * min(4, ntile - 4 * rd);
+        struct VB {
+            s16x4 x[4][2];
+            bf16x8 bp;
+        };
+        auto vload = [&](int i, VB &v) __attribute__((always_inline)) {
+            const int jj = i >> 1, kb = i & 1;
+            const lds_u8 *vt = (const lds_u8 *)lds + jj * kMStage + 4 * wave * kBlk;
+            v.bp = __builtin_bit_cast(bf16x8, pbuf[i * 64 + lane]);
+#pragma unroll
+            for (int db = 0; db < 4; ++db)
+#pragma unroll
+                for (int h = 0; h < 2; ++h)
+                    v.x[db][h] = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                        const_cast<lds_s16x4 *>((const lds_s16x4 *)(vt + db * kBlk + (kb ? voff[1][h] : voff[0][h]))));
+        };
+        auto vmma = [&](const VB &v) __attribute__((always_inline)) {
+#pragma unroll
+            for (int db = 0; db < 4; ++db) {
+                const s16x8 av = __builtin_shufflevector(v.x[db][0], v.x[db][1], 0, 1, 2, 3, 4, 5, 6, 7);
+                o[db] = mfma32(__builtin_bit_cast(bf16x8, av), v.bp, o[db]);
+            }
+        };
+        VB va, vb;
+        vload(0, va);
+        if (nb == 8) {  // a full round, straight-line (exact LDS wait counts)
+#pragma unroll
+            for (int i = 0; i < 8; i += 2) {
+                vload(i + 1, vb);
+                __builtin_amdgcn_sched_barrier(0);
+                vmma(va);
+                __builtin_amdgcn_sched_barrier(0);
+                if (i + 2 < 8) vload(i + 2, va);
+                __builtin_amdgcn_sched_barrier(0);
+                vmma(vb);
+                __builtin_amdgcn_sched_barrier(0);
+            }
+        } else
+        for (int i = 0; i < nb; i += 2) {
+            if (i + 1 < nb) vload(i + 1, vb);
+            __builtin_amdgcn_sched_barrier(0);  // the next batch's reads stay ahead of these products
+            vmma(va);
+            __builtin_amdgcn_sched_barrier(0);
+            if (i + 1 < nb) {
+                if (i + 2 < nb) vload(i + 2, va);
+                __builtin_amdgcn_sched_barrier(0);
+                vmma(vb);
+                __builtin_amdgcn_sched_barrier(0);
+            }
+        }
+        if (rd + 1 < nround) {
+            __syncthreads();  // every wave is done with the slots, maxima and probabilities
+            if (4 * (rd + 1) + wave < ntile) issue(max(np0, 0), max(np1, 0));
+            vm = tile_mask(np0, np1);
+        }
+    }
+
+    // ---- finish: row sums over the lane pair and the four waves (fixed order)
+    const float lw = l_run + __shfl_xor(l_run, 32, 64);
+    if (lane < 32) lsm[wave * 32 + n32] = lw;
+    __syncthreads();  // also: every wave is done with the slots (staging below)
+    const float l_tot = ((lsm[n32] + lsm[32 + n32]) + lsm[64 + n32]) + lsm[96 + n32];
+    const float inv = l_tot > 0.0f ? 1.0f / l_tot : 0.0f;
+    const int64_t pbase = (int64_t)layer * a.B * T * Hq;  // heads before this layer
+    const int64_t ohead = selrow * Hq + hq;
+    // O^T value (column 32 db' + 8 (e / 4) + 4 g + (e & 3) of this wave's 128, head n32),
+    // staged per wave in LDS as rows of the 32 heads, then written in 16-byte pieces
+    if (OUTF32 && nsplit == 1) {
+        constexpr int RS = 512 + 16;  // bytes per staged row (128 fp32 + padding)
+        lds_u8 *wst = (lds_u8 *)lds + wave * 32 * RS;
+#pragma unroll
+        for (int db = 0; db < 4; ++db)
+#pragma unroll
+            for (int q = 0; q < 4; ++q)
+                *(__attribute__((address_space(3))) f32x4 *)(wst + n32 * RS + 4 * (32 * db + 8 * q + 4 * g)) =
+                    f32x4{o[db][4 * q] * inv, o[db][4 * q + 1] * inv, o[db][4 * q + 2] * inv, o[db][4 * q + 3] * inv};
+        asm volatile("" ::: "memory");  // the wave's staging writes before its reads
+#pragma unroll
+        for (int it = 0; it < 16; ++it) {
+            const int h = 2 * it + (lane >> 5);
+            const u32x4 v = *(const lds_u32x4 *)(wst + h * RS + 16 * (lane & 31));
+            const int64_t oh = selrow * Hq + kvh * gq + 32 * hb + h;
+            float *row = reinterpret_cast<float *>(a.out) + layer * a.lso + oh * DV + 128 * wave;
+            *reinterpret_cast<u32x4 *>(row + 4 * (lane & 31)) = v;
+        }
+    } else {
+        constexpr int RS = 256 + 16;  // bytes per staged row (128 bf16 + padding)
+        lds_u8 *wst = (lds_u8 *)lds + wave * 32 * RS;
+        typedef __attribute__((__vector_size__(4 * sizeof(__bf16)))) __bf16 bf16v4;
+#pragma unroll
+        for (int db = 0; db < 4; ++db)
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                const bf16v4 w4 = {(__bf16)(o[db][4 * q] * inv), (__bf16)(o[db][4 * q + 1] * inv),
+                                   (__bf16)(o[db][4 * q + 2] * inv), (__bf16)(o[db][4 * q + 3] * inv)};
+                *(__attribute__((address_space(3))) bf16v4 *)(wst + n32 * RS + 2 * (32 * db + 8 * q + 4 * g)) = w4;
+            }
+        asm volatile("" ::: "memory");  // the wave's staging writes before its reads
+#pragma unroll
+        for (int it = 0; it < 8; ++it) {
+            const int h = 4 * it + (lane >> 4);
+            const u32x4 v = *(const lds_u32x4 *)(wst + h * RS + 16 * (lane & 15));
+            const int64_t oh = selrow * Hq + kvh * gq + 32 * hb + h;
+            uint16_t *row = nsplit == 1 ? reinterpret_cast<uint16_t *>(a.out) + layer * a.lso + oh * DV
+                                        : po + ((pbase + oh) * nsplit + split) * DV;
+            *reinterpret_cast<u32x4 *>(row + 128 * wave + 8 * (lane & 15)) = v;
+        }
+    }
+    if (wave == 0 && lane < 32) {
+        if (nsplit == 1) {
+            if (a.lse) a.lse[layer * a.lsl + ohead] = l_tot > 0.0f ? (m_run + __builtin_log2f(l_tot)) * kLn2 : kNegInf;
+        } else {
+            const int64_t pidx = (pbase + ohead) * nsplit + split;
+            pml[2 * pidx] = m_run;
+            pml[2 * pidx + 1] = l_tot;
+        }
+    }
+    if constexpr (FUSED) sel::release_slice<NT>(f.w, (int)selrow, nslices, slice);
+}
+
 // Merge the split partials of HPW heads of one (layer, b, t) in split order. Lane l of
 // the head's lane group owns the 8 values 8 l .. 8 l + 7 of its row; one wave turns a
 // head's (m, l) pairs into weights l 2^(m - M) (M = the largest m) for the normalised
@@ -559,8 +924,47 @@ hipError_t launch_t(const AttendArgs &a, void *ws, hipStream_t s, const FuseArgs
     return hipGetLastError();
 }
 
+// The 32-head MLA kernel: MLA rows and a multiple of 32 query heads per KV head.
+bool mla32(const AttendArgs &a) { return a.d_qk == 576 && (a.Hq / a.Hkv) % 32 == 0; }
+
+template <bool OUTF32>
+hipError_t launch_mla(const AttendArgs &a, void *ws, hipStream_t s, const FuseArgs *fuse) {
+    const int R = rows_per_split(a);
+    const int S = (a.K + R - 1) / R;
+    const int HB = (a.Hq / a.Hkv) / 32;
+    uint16_t *po = reinterpret_cast<uint16_t *>(ws);
+    float *pml = S > 1 ? reinterpret_cast<float *>(reinterpret_cast<char *>(ws) + partial_rows_bytes(a, S)) : nullptr;
+    // the two 32-head blocks of a split S workgroups apart: on one XCD (one L2) when S % 8 == 0
+    dim3 grid(S * HB, a.T * a.Hkv, a.B * a.L);
+    if (fuse) {
+        if (R > kMMaxPos) return hipErrorInvalidValue;  // (launch_select_attend checks first)
+        FuseArgs f = *fuse;
+        constexpr size_t ring = (size_t)4 * kMStage;
+        constexpr size_t fixed = sel::kB2 * 4 + 256 * 4 + 32 * 4;
+        f.pw_log = sel::slice_pw_log(f.w.words, 256);
+        const size_t bb = ((size_t)256 << f.pw_log) * 4;  // transposed bitmap
+        static_assert(ring >= fixed + sel::kSliceTiesFirst * 8, "slots too small for the resolve");
+        f.bits_lds = ring >= fixed + bb + (size_t)sel::kSliceTiesFirst * 8;
+        f.tl = (int)(((ring - fixed - (f.bits_lds ? bb : 0)) / 8) & ~(size_t)1);
+        const size_t lds = kMLdsFixed + (size_t)R * sizeof(int);
+        hipLaunchKernelGGL((attend_mla_kernel<OUTF32, true>), grid, dim3(256), lds, s, a, po, pml, R, HB, f);
+    } else {
+        hipLaunchKernelGGL((attend_mla_kernel<OUTF32, false>), grid, dim3(256), (size_t)kMLdsFixed, s, a, po, pml, R, HB,
+                           FuseArgs{});
+    }
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess || S == 1) return e;
+    constexpr int HPW = kCombT / (512 / 8);
+    dim3 cgrid((a.Hq + HPW - 1) / HPW, a.B * a.T, a.L);
+    hipLaunchKernelGGL((attend_combine_kernel<512, OUTF32>), cgrid, dim3(kCombT), 0, s, a, po, pml, S);
+    return hipGetLastError();
+}
+
 template <int DQK, int DV, bool MLA>
 hipError_t launch_d(const AttendArgs &a, void *ws, hipStream_t s, const FuseArgs *fuse) {
+    if constexpr (MLA) {
+        if (mla32(a)) return a.out_f32 ? launch_mla<true>(a, ws, s, fuse) : launch_mla<false>(a, ws, s, fuse);
+    }
     const int g = a.Hq / a.Hkv;
     const int HW = (g + 15) / 16;
     if (a.out_f32) {
@@ -585,6 +989,15 @@ int attend_default_splits(const AttendArgs &a) {
     const int g = a.Hq / a.Hkv;
     const int HW = (g + 15) / 16;
     const long units = (long)a.L * a.B * a.T * a.Hkv;
+    if (mla32(a)) {
+        // 32-head blocks: about 256 workgroups, at least one round (128 rows) per split
+        const long wg = units * (g / 32);
+        long s = (256 + wg - 1) / wg;
+        const long smax = (a.K + kMRound - 1) / kMRound;
+        if (s > smax) s = smax;
+        if (s > kAttendMaxSplits) s = kAttendMaxSplits;
+        return (int)(s < 1 ? 1 : s);
+    }
     const long target = HW == 4 ? 256 : 1024;
     long s = (target + units - 1) / units;
     const long smax = (a.K + kRows - 1) / kRows;
@@ -640,7 +1053,7 @@ hipError_t launch_select_attend(const SelectArgs &sa, void *sel_ws, const Attend
     // selection. That is paid back only when four waves resolve together (more than 48
     // query heads per KV head) and one KV head of one layer reads each row; otherwise the
     // selection's own resolve kernel and then the plain attention run (same results).
-    if (!(a.Hq / a.Hkv > 48 && a.Hkv * a.L == 1)) {
+    if (!(a.Hq / a.Hkv > 48 && a.Hkv * a.L == 1) || (mla32(a) && rows_per_split(a) > kMMaxPos)) {
         const hipError_t e = launch_select(sa, sel_ws, s);
         if (e != hipSuccess) return e;
         AttendArgs a2 = a;
