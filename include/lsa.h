@@ -113,7 +113,10 @@ extern "C" {
  *   lsa_select_workspace_bytes() of that call (256-byte aligned workspace). With
  *   select_ws_state = LSA_WS_UNKNOWN the workspace is cleared first (one fill kernel);
  *   LSA_WS_CLEAN skips that (every successful lsa_select leaves its workspace clean).
- *   With the kept map, window >= block_size - 1 is required, as in lsa_select.
+ *   With the kept map, window >= block_size - 1 is required, as in lsa_select. Rows of
+ *   at most 4096 columns need no priming (lsa_select ranks them in one launch from the
+ *   scores alone): for them lsa_index only writes the scores, and the protocol above
+ *   still holds.
  *
  * Shapes: q bf16 [B][T][H][D]; w fp32 [B][T][H]; k per k_dtype: bf16 or fp8 [B][N][D]
  * (TOKENS) or fp32 [B][n_blocks][D] (BLOCKS); k_scale fp32 [B][N] (fp8 keys only);
@@ -223,6 +226,9 @@ int32_t lsa_block_means(const lsa_block_means_desc *desc, void *stream);
  * same B, T and n_cols (or right after lsa_workspace_clear) may pass LSA_WS_CLEAN to
  * skip the clear. LSA_WS_PRIMED: lsa_index already prepared the workspace for these
  * scores (see lsa_index), so the selection skips its first pass over them.
+ * Rows of at most 4096 columns are selected by one workgroup per row in a single
+ * launch (the row's keys held in LDS); the workspace state is then ignored and left
+ * clean. Longer rows take the histogram, filter and resolve passes.
  * Calls that share one workspace must be ordered on one stream.
  * Supported: 1 <= K <= 4096, n_cols >= 1; with a kept map and causal = 1,
  * window >= block_size - 1 (LSA_E_UNSUPPORTED otherwise).

@@ -80,6 +80,8 @@ static int32_t index_primed(const lsa_index_desc *d, lsa::IndexTokensArgs a, voi
     sa.ws_clean = ws_clean;
     sa.vec = (a.n_out & 3) == 0;  // scores are 16-byte aligned
     hipError_t e;
+    // rows the one-launch selection takes need no histogram (it leaves the workspace clean)
+    if (lsa::select_small(a.n_out)) return hip_status(lsa::launch_index_tokens(a, s), fn);
     if (lsa::index_tokens_fused_hist(d->H, d->T, hi)) {
         if (!sa.ws_clean) {
             e = lsa::launch_clear(select_ws, lsa::select_zero_bytes(d->B * d->T), s);

@@ -1053,7 +1053,8 @@ hipError_t launch_select_attend(const SelectArgs &sa, void *sel_ws, const Attend
     // selection. That is paid back only when four waves resolve together (more than 48
     // query heads per KV head) and one KV head of one layer reads each row; otherwise the
     // selection's own resolve kernel and then the plain attention run (same results).
-    if (!(a.Hq / a.Hkv > 48 && a.Hkv * a.L == 1) || (mla32(a) && rows_per_split(a) > kMMaxPos)) {
+    if (!(a.Hq / a.Hkv > 48 && a.Hkv * a.L == 1) || (mla32(a) && rows_per_split(a) > kMMaxPos) ||
+        select_small(sa.n_cols)) {
         const hipError_t e = launch_select(sa, sel_ws, s);
         if (e != hipSuccess) return e;
         AttendArgs a2 = a;

@@ -137,6 +137,10 @@ struct SelectArgs {
 size_t select_workspace_bytes(int rows, int n_cols, bool kept);
 size_t select_zero_bytes(int rows);  // the part of the workspace kept at zero between calls
 hipError_t launch_select(const SelectArgs &a, void *ws, hipStream_t s);
+// true when launch_select runs the one-launch selection of small rows (n_cols columns):
+// it reads no histogram from the workspace (a primed one is not needed) and leaves the
+// workspace clean
+bool select_small(int n_cols);
 // The selection of flat rows from the candidate lists the indexer emitted (cand [rows][N],
 // cand_cnt [rows]); one workgroup per row, nothing else in the workspace.
 hipError_t launch_select_cand(const SelectArgs &a, const uint64_t *cand, const uint32_t *cand_cnt, hipStream_t s);
