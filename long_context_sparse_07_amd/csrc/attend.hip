@@ -793,87 +793,121 @@ __global__ __launch_bounds__(256) void attend_mla_kernel(AttendArgs a, uint16_t 
     if constexpr (FUSED) sel::release_slice<NT>(f.w, (int)selrow, nslices, slice);
 }
 
-// Merge the split partials of HPW heads of one (layer, b, t) in split order. Lane l of
-// the head's lane group owns the 8 values 8 l .. 8 l + 7 of its row; one wave turns a
-// head's (m, l) pairs into weights l 2^(m - M) (M = the largest m) for the normalised
-// rows, then every lane accumulates its 8 values over the splits, 16-byte loads issued
-// eight splits at a time.
+// Merge the split partials of HPW heads of one (layer, b, t). Wave h < HPW turns head h's
+// (m, l) pairs into weights l 2^(m - M) (M = the largest m) for the normalised rows. A
+// head's DV values are split into 8-value chunks, one lane each, and its splits into SG
+// groups (split s to group s % SG): every thread has its group's loads in flight at once
+// and sums them in split order, then the group-0 thread of each chunk adds the SG partial
+// sums in group order (a fixed order: the same bits every run).
 constexpr int kCombT = 256;
 constexpr int kMaxSplits = kAttendMaxSplits;
 
-template <int DV, bool OUTF32>
+template <int DV, int HPW, bool OUTF32>
 __global__ __launch_bounds__(kCombT) void attend_combine_kernel(AttendArgs a, const uint16_t *po, const float *pml, int S) {
-    constexpr int LPR = DV / 8;          // lanes per head row
-    constexpr int HPW = kCombT / LPR;    // heads per workgroup
-    constexpr int HPV = HPW / 4;         // heads per wave
+    constexpr int LPR = DV / 8;                 // lanes per row (8 values each)
+    constexpr int SG = kCombT / (HPW * LPR);    // split groups per head
+    static_assert(SG >= 1 && HPW * SG * LPR == kCombT && HPW <= 4, "thread layout");
+    constexpr int PER = (kMaxSplits + SG - 1) / SG;  // splits per group at most
     __shared__ float wgt[HPW][kMaxSplits];
     __shared__ float linv[HPW];
+    __shared__ __attribute__((aligned(16))) float part[HPW][SG][DV];
     const int bt = blockIdx.y, layer = blockIdx.z;
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int64_t hbase = (int64_t)layer * a.B * a.T * a.Hq + (int64_t)bt * a.Hq;  // partial heads of (layer, b, t)
-    // ---- weights: wave w handles heads HPV w .. HPV w + HPV - 1 of the group
-    for (int k = 0; k < HPV; ++k) {
-        const int hl = wave * HPV + k;
-        const int hq = blockIdx.x * HPW + hl;
-        if (hq >= a.Hq) break;
-        const float *ml = pml + (hbase + hq) * S * 2;
-        float M = kNegInf;
-        for (int s = lane; s < S; s += 64) M = fmaxf(M, ml[2 * s]);
+    if (wave < HPW) {
+        const int hq = blockIdx.x * HPW + wave;
+        if (hq < a.Hq) {
+            const float *ml = pml + (hbase + hq) * S * 2;
+            float M = kNegInf;
+            for (int s = lane; s < S; s += 64) M = fmaxf(M, ml[2 * s]);
 #pragma unroll
-        for (int o = 32; o > 0; o >>= 1) M = fmaxf(M, __shfl_xor(M, o, 64));
-        float L = 0.0f;
-        for (int s = lane; s < S; s += 64) {
-            const float m = ml[2 * s];
-            const float wl = (M == kNegInf || m == kNegInf) ? 0.0f : __builtin_amdgcn_exp2f(m - M) * ml[2 * s + 1];
-            wgt[hl][s] = wl;
-            L += wl;
-        }
+            for (int o = 32; o > 0; o >>= 1) M = fmaxf(M, __shfl_xor(M, o, 64));
+            float L = 0.0f;
+            for (int s = lane; s < S; s += 64) {
+                const float m = ml[2 * s];
+                const float wl = (M == kNegInf || m == kNegInf) ? 0.0f : __builtin_amdgcn_exp2f(m - M) * ml[2 * s + 1];
+                wgt[wave][s] = wl;
+                L += wl;
+            }
 #pragma unroll
-        for (int o = 32; o > 0; o >>= 1) L += __shfl_xor(L, o, 64);  // the same tree every run
-        if (lane == 0) {
-            linv[hl] = L > 0.0f ? 1.0f / L : 0.0f;
-            if (a.lse) a.lse[layer * a.lsl + (int64_t)bt * a.Hq + hq] = L > 0.0f ? (M + __builtin_log2f(L)) * kLn2 : kNegInf;
+            for (int o = 32; o > 0; o >>= 1) L += __shfl_xor(L, o, 64);  // the same tree every run
+            if (lane == 0) {
+                linv[wave] = L > 0.0f ? 1.0f / L : 0.0f;
+                if (a.lse) a.lse[layer * a.lsl + (int64_t)bt * a.Hq + hq] = L > 0.0f ? (M + __builtin_log2f(L)) * kLn2 : kNegInf;
+            }
         }
     }
-    __syncthreads();
-    // ---- weighted sum of the rows
-    const int hl = tid / LPR, c = tid % LPR;
+    // ---- this thread's splits (group sg) of chunk c of head hl, all loads in flight
+    const int hl = tid / (SG * LPR), sg = (tid / LPR) % SG, c = tid % LPR;
     const int hq = blockIdx.x * HPW + hl;
-    if (hq >= a.Hq) return;
-    const u32x4 *src = reinterpret_cast<const u32x4 *>(po + (hbase + hq) * S * DV) + c;
+    const bool live = hq < a.Hq;
+    const u32x4 *src = reinterpret_cast<const u32x4 *>(po + (hbase + (live ? hq : 0)) * S * DV) + c;
     constexpr int RU = DV / 8;  // u32x4 per row
+    // rounds of up to 8 of the group's splits in flight (one round for the default splits)
+    constexpr int U = PER < 8 ? PER : 8;
     float acc[8];
 #pragma unroll
     for (int e = 0; e < 8; ++e) acc[e] = 0.0f;
-    auto add = [&](const u32x4 v, float w) {
+    for (int base = 0; base < PER; base += U) {
+        u32x4 v[U];
 #pragma unroll
-        for (int q = 0; q < 4; ++q) {
-            acc[2 * q] += w * bf16lo(v[q]);
-            acc[2 * q + 1] += w * bf16hi(v[q]);
+        for (int u = 0; u < U; ++u) {
+            const int sp = sg + (base + u) * SG;
+            v[u] = (live && sp < S) ? src[(int64_t)sp * RU] : u32x4{0u, 0u, 0u, 0u};
         }
-    };
-    int s = 0;
-    for (; s + 8 <= S; s += 8) {
-        u32x4 v[8];
+        if (base == 0) __syncthreads();  // the weights (uniform: every thread runs round 0)
 #pragma unroll
-        for (int u = 0; u < 8; ++u) v[u] = src[(int64_t)(s + u) * RU];
+        for (int u = 0; u < U; ++u) {
+            const int sp = sg + (base + u) * SG;
+            if (live && sp < S) {
+                const float w = wgt[hl][sp];
 #pragma unroll
-        for (int u = 0; u < 8; ++u) add(v[u], wgt[hl][s + u]);
+                for (int q = 0; q < 4; ++q) {
+                    acc[2 * q] += w * bf16lo(v[u][q]);
+                    acc[2 * q + 1] += w * bf16hi(v[u][q]);
+                }
+            }
+        }
+        if (sg + (base + U) * SG >= S) break;  // uniform per group; no barrier follows in the loop
     }
-    for (; s < S; ++s) add(src[(int64_t)s * RU], wgt[hl][s]);
+    *reinterpret_cast<f32x4 *>(&part[hl][sg][8 * c]) = f32x4{acc[0], acc[1], acc[2], acc[3]};
+    *reinterpret_cast<f32x4 *>(&part[hl][sg][8 * c + 4]) = f32x4{acc[4], acc[5], acc[6], acc[7]};
+    __syncthreads();
+    if (sg != 0 || !live) return;
+    float r[8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) r[e] = 0.0f;
+    for (int g = 0; g < SG; ++g) {
+        const f32x4 x0 = *reinterpret_cast<const f32x4 *>(&part[hl][g][8 * c]);
+        const f32x4 x1 = *reinterpret_cast<const f32x4 *>(&part[hl][g][8 * c + 4]);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            r[e] += x0[e];
+            r[4 + e] += x1[e];
+        }
+    }
     const float inv = linv[hl];
     const int64_t ob = layer * a.lso + ((int64_t)bt * a.Hq + hq) * DV + 8 * c;
     if constexpr (OUTF32) {
         float *out = reinterpret_cast<float *>(a.out) + ob;
-        *reinterpret_cast<f32x4 *>(out) = f32x4{acc[0] * inv, acc[1] * inv, acc[2] * inv, acc[3] * inv};
-        *reinterpret_cast<f32x4 *>(out + 4) = f32x4{acc[4] * inv, acc[5] * inv, acc[6] * inv, acc[7] * inv};
+        *reinterpret_cast<f32x4 *>(out) = f32x4{r[0] * inv, r[1] * inv, r[2] * inv, r[3] * inv};
+        *reinterpret_cast<f32x4 *>(out + 4) = f32x4{r[4] * inv, r[5] * inv, r[6] * inv, r[7] * inv};
     } else {
         typedef __attribute__((__vector_size__(8 * sizeof(__bf16)))) __bf16 bf16v8;
-        const bf16v8 w8 = {(__bf16)(acc[0] * inv), (__bf16)(acc[1] * inv), (__bf16)(acc[2] * inv),
-                           (__bf16)(acc[3] * inv), (__bf16)(acc[4] * inv), (__bf16)(acc[5] * inv),
-                           (__bf16)(acc[6] * inv), (__bf16)(acc[7] * inv)};
+        const bf16v8 w8 = {(__bf16)(r[0] * inv), (__bf16)(r[1] * inv), (__bf16)(r[2] * inv), (__bf16)(r[3] * inv),
+                           (__bf16)(r[4] * inv), (__bf16)(r[5] * inv), (__bf16)(r[6] * inv), (__bf16)(r[7] * inv)};
         *reinterpret_cast<bf16v8 *>(reinterpret_cast<uint16_t *>(a.out) + ob) = w8;
     }
+}
+
+// The merge launch: one head a workgroup for 128-wide rows (16 split groups), two for
+// 512-wide rows (2 split groups each).
+template <int DV, bool OUTF32>
+hipError_t launch_combine(const AttendArgs &a, const uint16_t *po, const float *pml, int S, hipStream_t s) {
+    constexpr int HPW = DV >= 512 ? 2 : 1;
+    dim3 cgrid((a.Hq + HPW - 1) / HPW, a.B * a.T, a.L);
+    hipLaunchKernelGGL((attend_combine_kernel<DV, HPW, OUTF32>), cgrid, dim3(kCombT), 0, s, a, po, pml, S);
+    return hipGetLastError();
 }
 
 int rows_per_split(const AttendArgs &a) {
@@ -918,10 +952,7 @@ hipError_t launch_t(const AttendArgs &a, void *ws, hipStream_t s, const FuseArgs
     }
     hipError_t e = hipGetLastError();
     if (e != hipSuccess || S == 1) return e;
-    constexpr int HPW = kCombT / (DV / 8);
-    dim3 cgrid((a.Hq + HPW - 1) / HPW, a.B * a.T, a.L);
-    hipLaunchKernelGGL((attend_combine_kernel<DV, OUTF32>), cgrid, dim3(kCombT), 0, s, a, po, pml, S);
-    return hipGetLastError();
+    return launch_combine<DV, OUTF32>(a, po, pml, S, s);
 }
 
 // The 32-head MLA kernel: MLA rows and a multiple of 32 query heads per KV head.
@@ -954,10 +985,7 @@ hipError_t launch_mla(const AttendArgs &a, void *ws, hipStream_t s, const FuseAr
     }
     hipError_t e = hipGetLastError();
     if (e != hipSuccess || S == 1) return e;
-    constexpr int HPW = kCombT / (512 / 8);
-    dim3 cgrid((a.Hq + HPW - 1) / HPW, a.B * a.T, a.L);
-    hipLaunchKernelGGL((attend_combine_kernel<512, OUTF32>), cgrid, dim3(kCombT), 0, s, a, po, pml, S);
-    return hipGetLastError();
+    return launch_combine<512, OUTF32>(a, po, pml, S, s);
 }
 
 template <int DQK, int DV, bool MLA>
