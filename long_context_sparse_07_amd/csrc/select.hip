@@ -231,10 +231,12 @@ __global__ __launch_bounds__(kRT) void select_resolve_kernel(SelectArgs a, Ws w,
     __shared__ uint32_t h256[256];
     __shared__ uint32_t scr[32];
     __shared__ uint32_t cnt[4];
+    __shared__ uint32_t s_desc;  // KEPT: the kept map's valid entries do not ascend
     __shared__ int32_t fill[KEPT ? KPAD : 1];
     const int row = blockIdx.x;
     const int tid = threadIdx.x;
     const Row r = make_row(a, row);
+    if (tid == 0) s_desc = 0;
     const uint32_t m = (uint32_t)max(r.m, 0);
     uint32_t *g1 = w.hist + (int64_t)row * kSelBins;
     uint32_t *gctr = w.ctr + (int64_t)row * kCtr;
@@ -257,7 +259,18 @@ __global__ __launch_bounds__(kRT) void select_resolve_kernel(SelectArgs a, Ws w,
         if (tid + kRT < tcap) tc1 = gtcols[tid + kRT];
     }
     if (lwords) copy_words_to_lds<kRT, 2>(gbits, lbits, lwords);
+    // KEPT: whether the kept map ascends (a kept map whose valid entries ascend, then -1,
+    // as lsa_select writes it, keeps the columns in position order), read with the first loads
+    bool desc = false;
+    if constexpr (KEPT) {
+        for (int i = tid; i + 1 < a.n_keep; i += kRT) {
+            const int x = r.kept[i], y = r.kept[i + 1];
+            const bool vx = x >= 0 && x < r.nblk, vy = y >= 0 && y < r.nblk;
+            desc = desc || (vy && (!vx || x >= y));
+        }
+    }
     const BinPick bp = pick_bin<kRT, 2>(hv, m, scr);  // its barriers follow every thread's reads
+    if (desc) s_desc = 1;  // (read after the compaction's barriers)
     const int b1 = bp.bin;
 
     auto mark = [&](int col) {
@@ -375,17 +388,9 @@ __global__ __launch_bounds__(kRT) void select_resolve_kernel(SelectArgs a, Ws w,
         }
         if constexpr (KEPT) {
             nfill = min(nfill, (uint32_t)KPAD);
-            // a kept map whose valid entries ascend, then -1 (as lsa_select writes it), keeps
-            // the columns in position order: the fill is already sorted
-            if (tid == 0) cnt[3] = 0;
+            // an ascending kept map leaves the fill sorted (checked with the first loads)
             __syncthreads();
-            for (int i = tid; i + 1 < a.n_keep; i += kRT) {
-                const int x = r.kept[i], y = r.kept[i + 1];
-                const bool vx = x >= 0 && x < r.nblk, vy = y >= 0 && y < r.nblk;
-                if (vy && (!vx || x >= y)) cnt[3] = 1;
-            }
-            __syncthreads();
-            const bool ascending = cnt[3] == 0;
+            const bool ascending = s_desc == 0;
             int np = KPAD;  // the sort's size: the fill rounded up to a power of two
             while (np / 2 >= (int)nfill && np > 1) np /= 2;
             if (ascending) np = 1;

@@ -110,7 +110,7 @@ def test_attend_padding_and_out_of_range_rows():
     assert np.all(o[0, 1, 0] == 0) and np.all(np.isneginf(l[0, 1, 0]))
 
 
-@pytest.mark.parametrize("splits", [1, 2, 7, 0])
+@pytest.mark.parametrize("splits", [1, 2, 7, 16, 0])
 def test_attend_split_counts(splits):
     cfg = config(2, B=2, N=6000, K=512, S=32, W=128)
     inp = make_inputs(cfg)
@@ -169,3 +169,22 @@ def test_select_workspace_reuse_is_clean():
     e = L.lsa_select(sc, cfg.K, cfg.S, cfg.W)
     assert torch.equal(a, b) and torch.equal(a, e)
     assert c.shape == (2, 1, 300)
+
+
+@pytest.mark.parametrize("cid", [2, 5])
+def test_attend_128_splits_merge_in_rounds(cid):
+    # 4096 selected rows in 128 splits of 32: the merge's split groups take several rounds
+    # of loads (MLA rows: 2 groups of 64 splits; 128-wide rows: 16 groups of 8)
+    kw = dict(B=2, N=9000, K=4096, S=64, W=512)
+    if cid == 5:
+        kw["layers"] = 1
+    cfg = config(cid, **kw)
+    inp = make_inputs(cfg)
+    d = upload(inp)
+    ora = O.reference_step(inp)
+    idx_o = torch.from_numpy(np.stack([[ora["idx"][(b, 0)] for b in range(cfg.B)]]).transpose(1, 0, 2).astype(np.int32)).cuda()
+    out, lse = gpu_attend(d, idx_o, n_splits=128)
+    o, l = _np(out), _np(lse)
+    for b in range(cfg.B):
+        check_attn(o[0, b, 0], ora["out"][(0, b, 0)], f"c{cid} 128 splits b={b}")
+        assert np.allclose(l[0, b, 0], ora["lse"][(0, b, 0)], atol=2e-3), f"c{cid} lse b={b}"
