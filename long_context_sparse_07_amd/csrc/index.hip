@@ -111,9 +111,10 @@ __device__ __forceinline__ void row_to_th(int grp, int i, int H, int T, int &t, 
 // its columns per first-level bin of the selection histogram (finite scores at visible
 // positions outside the sink and the window) and adds the counts to sel_hist.
 // EMIT (four query groups a workgroup, one query and its whole row per wave): each wave
-// keeps a histogram of its row's candidates over the top 10 order-key bits in LDS and,
-// from it, the running threshold: the bin where the candidates counted so far from the
-// top reach the fill size. The threshold only rises as candidates arrive, so a
+// keeps an LDS histogram of its row's candidates in 1024 bins (the positive scores by their
+// top 11 order-key bits, as the selection bins them; every negative score in the lowest
+// bin) and, from it, the running threshold: the bin where the candidates counted so far
+// from the top reach the fill size. The threshold only rises as candidates arrive, so a
 // candidate in a bin below it can no longer be among the row's K - |forced| largest; the
 // others are appended to the row's candidate list. At the end every candidate in a bin
 // at or above the final threshold, and so every one the selection can take, is listed.
@@ -135,7 +136,7 @@ __global__ __launch_bounds__(PRE ? kThreads : 2 * kThreads) void index_tokens_ke
     __shared__ uint32_t shist[HIST ? kSelBins : 1];                      // HIST: candidate counts
     static_assert(!HIST || (MODE == ONEQ && !PRE), "the histogram needs one query per workgroup");
     static_assert(!EMIT || (MODE == ONEQ && PRE && !HI), "emission: one whole flat row per wave");
-    constexpr int kEB = 1024;  // EMIT: running-threshold bins (top 10 order-key bits)
+    constexpr int kEB = 1024;  // EMIT: running-threshold bins
     __shared__ uint32_t whist[EMIT ? 4 : 1][EMIT ? kEB : 1];
 
     const int tid = threadIdx.x;
@@ -402,8 +403,11 @@ __global__ __launch_bounds__(PRE ? kThreads : 2 * kThreads) void index_tokens_ke
                 if constexpr (EMIT) {
                     if (vis && pos >= f_se && pos < f_wl && v > kNegInf) {
                         const uint32_t key = order_key(v);
-                        lds_add_u32(&whist[wave][key >> 22], 1u);
-                        emit = (key >> 22) >= e_thr;
+                        // the positive scores' quarter-octave bins (the selection's own
+                        // resolution); every negative score in bin 0, below them all
+                        const uint32_t bin = key >= 0x80000000u ? (key >> kSelShift) - 1024u : 0u;
+                        lds_add_u32(&whist[wave][bin], 1u);
+                        emit = bin >= e_thr;
                         comp = ((uint64_t)key << 32) | (uint32_t)~(uint32_t)pos;
                     }
                 }
