@@ -248,8 +248,9 @@ def lsa_select_workspace_bytes(scores, K, sink=0, window=0, *, N=None, kept=None
 
 
 def lsa_select(scores, K, sink=0, window=0, *, N=None, ctx_len=None, kept=None, block_size=0, causal=True,
-               idx=None, workspace=None, stream=None):
-    """SI selection: idx int32 [B,T,K], ascending, -1 padded."""
+               idx=None, workspace=None, workspace_state=LSA_WS_UNKNOWN, stream=None):
+    """SI selection: idx int32 [B,T,K], ascending, -1 padded. With a caller workspace,
+    workspace_state says what it holds (LSA_WS_PRIMED after lsa_index primed it)."""
     import torch
     B, T, n_cols = scores.shape
     N = n_cols if N is None else N
@@ -260,6 +261,7 @@ def lsa_select(scores, K, sink=0, window=0, *, N=None, ctx_len=None, kept=None, 
     need = lib().lsa_select_workspace_bytes(ctypes.byref(d))
     if workspace is not None:
         ws, ent = workspace, None
+        d.workspace_state = workspace_state
     else:
         ent = _workspace("select", need, scores.device, (B, T, n_cols))
         ws = ent[0]
