@@ -179,6 +179,19 @@ def pmc_attend_traffic():
         return None
 
 
+def sq_c4_mfma():
+    """MFMA busy fraction of the c4 prefill indexer from the committed shader-counter record,
+    if taken on the current indexer sources; else None."""
+    try:
+        with open(os.path.join(ROOT, "profiles", "index_c4_prefill_sq.json")) as f:
+            rec = json.load(f)
+        if rec.get("sources_sha256") != _sources_sha(("index.hip", "common.cuh")):
+            return None
+        return {k: rec[k] for k in ("mfma_busy_frac_bf16_query", "mfma_busy_frac_fp8_query", "valu_per_mfma_bf16_query")}
+    except Exception:
+        return None
+
+
 def upload_workload(inp, cfg):
     """Device copies of one workload's inputs (bench naming: ks = key scales, ctx = ctx_len)."""
     import numpy as np
@@ -750,6 +763,7 @@ def main():
                   "index_gbs": idx_b / (ms_index * 1e-3) / 1e9,
                   "kv_gather_gbs": gat_b / (ms_attend * 1e-3) / 1e9,
                   "attend_traffic": pmc_attend_traffic(),
+                  "index_c4_mfma_counters": sq_c4_mfma(),
                   "index_bytes_per_launch": idx_b, "gather_bytes": gat_b},
     }
     if not args.no_workloads:
