@@ -517,10 +517,11 @@ __global__ __launch_bounds__(kSmallT) void select_small_kernel(SelectArgs a, Ws 
         }
     }
     __syncthreads();
-    uint32_t hv[2];
-    hv[0] = h[kSelBins - 1 - 2 * tid];
-    hv[1] = h[kSelBins - 2 - 2 * tid];
-    const BinPick bp = pick_bin<NT, 2>(hv, m, scr);  // its barriers follow every thread's reads
+    constexpr int HP = kSelBins / NT;  // first-level bins per thread
+    uint32_t hv[HP];
+#pragma unroll
+    for (int e = 0; e < HP; ++e) hv[e] = h[kSelBins - 1 - HP * tid - e];
+    const BinPick bp = pick_bin<NT, HP>(hv, m, scr);  // its barriers follow every thread's reads
     const uint32_t b1 = (uint32_t)bp.bin;
     // ---- bits of the columns above the bin (every candidate in mode 1), ties into LDS;
     // each wave takes 64 columns at a time and writes their two bitmap words
