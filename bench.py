@@ -763,6 +763,10 @@ def main():
                   "index_gbs": idx_b / (ms_index * 1e-3) / 1e9,
                   "kv_gather_gbs": gat_b / (ms_attend * 1e-3) / 1e9,
                   "attend_traffic": pmc_attend_traffic(),
+                  # the attention's split count (library default), from its workspace size:
+                  # split rows bf16 d_v wide plus (m, l) per (head, split)
+                  "attend_splits": round(lib.lsa_attend_workspace_bytes(ctypes.byref(descs[0][2]))
+                                         / (B * T * cfg.Hq * (cfg.d_v * 2 + 8))),
                   "index_c4_mfma_counters": sq_c4_mfma(),
                   "index_bytes_per_launch": idx_b, "gather_bytes": gat_b},
     }

@@ -7,7 +7,8 @@ The chain runs its fused kernel only for more than 48 query heads per KV head in
 layer (MLA here); for the other shapes the call runs the selection's resolve kernel and
 the plain attention, which these cases check through the same entry point.
 
-Cases: MLA (64 heads, one wave per 16 heads) and GQA / MQA kernels (one wave); several
+Cases: MLA (64 heads, 32-head blocks), 64 query heads on one 128-wide KV head (the
+four-wave fused kernel of 128-wide rows) and GQA / MQA kernels (one wave); several
 layers and KV heads sharing one selection row; one split and many; fp32 output with one
 split (the kernel's early exit); the row bitmap in LDS and, for a long GQA row, in the
 workspace; ties ranked by radix passes and from the workspace copy of the tie list; a
@@ -213,3 +214,19 @@ def test_mla_long_row_bitmap_in_workspace():
     q = (torch.randn((1, 1, 1, 64, 576), device="cuda", generator=g) * 576 ** -0.5).to(torch.bfloat16)
     k = torch.randn((1, 1, N, 1, 576), device="cuda", generator=g).to(torch.bfloat16)
     _both(sc, 2048, 64, 512, q, k, None, 576 ** -0.5)
+
+
+@pytest.mark.parametrize("N,splits,ties", [(9000, 0, False), (9000, 1, False), (9000, 5, True), (600000, 0, False)])
+def test_gqa_64_heads_per_kv_head_fused_kernel(N, splits, ties):
+    # 64 query heads on one 128-wide KV head: the chain runs the four-wave fused kernel of
+    # 128-wide rows (the 32-head kernel is for MLA rows); one split and several, the row
+    # bitmap in LDS and (600000 columns) in the workspace, a threshold bin of equal scores
+    rng = np.random.default_rng(700 + N % 97 + splits)
+    rows = rng.standard_normal((2, N)).astype(np.float32)
+    if ties:
+        rows[1] = (rng.standard_normal(N) * 0.01 - 5.0).astype(np.float32)
+        pos = rng.permutation(np.arange(16, N - 600))
+        rows[1, pos[:300]] = 3.0 + rng.random(300).astype(np.float32)
+        rows[1, pos[300:3300]] = 2.0
+    q, k, v, scale = _kv(rng, 1, 2, N, 64, 1, False)
+    _both(_scores(rows), 1024, 32, 128, q, k, v, scale, n_splits=splits)
