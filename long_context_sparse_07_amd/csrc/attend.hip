@@ -40,6 +40,10 @@ static __device__ __align__(256) unsigned char scratch[kAttendStaticScratchBytes
 constexpr int kRows = 32;     // selected rows per tile
 constexpr int kMaxR = 2048;   // selected rows per split (positions staged in LDS)
 constexpr int kBlk = 2048;    // LDS bytes of one block (4 chunks) of the 32 rows
+// up to 16 query heads per KV head (one wave of heads): workgroups aimed for, three per
+// compute unit in one generation
+constexpr int kOneHeadTarget = 768;
+constexpr size_t kLdsPerCu = 160 * 1024;
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
 
@@ -58,6 +62,20 @@ __device__ __forceinline__ void wait_vmcnt() {
     __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
 }
 
+// Wait until at most n tiles' DMA instructions (PW per tile, n <= MAXN) are pending.
+template <int PW, int MAXN>
+__device__ __forceinline__ void wait_tiles(int n) {
+    if constexpr (MAXN > 0) {
+        if (n >= MAXN) {
+            wait_vmcnt<MAXN * PW>();
+            return;
+        }
+        wait_tiles<PW, MAXN - 1>(n);
+    } else {
+        wait_vmcnt<0>();
+    }
+}
+
 // Physical chunk slot (0..3) of logical chunk j of row r inside a block.
 __device__ __forceinline__ int slot(int j, int r) { return j ^ ((r >> 2) & 3); }
 
@@ -71,7 +89,7 @@ struct FuseArgs {
     int bits_lds;
 };
 
-template <int DQK, int DV, int HW, bool MLA, bool OUTF32>
+template <int DQK, int DV, int HW, bool MLA, bool OUTF32, int NSTC = 4>
 struct AttTile {
     static constexpr int NT = 64 * HW;
     static constexpr int KB = DQK * 2 / 64;           // K blocks per row (MLA 18, else 4)
@@ -81,25 +99,26 @@ struct AttTile {
     static_assert(INSTR % HW == 0, "tile must split evenly over the waves");
     static constexpr int PER_WAVE = INSTR / HW;
     // tiles in LDS: one computed, NST-1 in flight; as many as the LDS (with the position
-    // list) and the 6-bit vmcnt allow, at most 4
+    // list) and the 6-bit vmcnt allow, at most NSTC
     static constexpr int LDS_MAX = 160 * 1024 - kMaxR * 4 - kMaxR / 32 * 4;
     static constexpr int NST_LDS = LDS_MAX / STAGE;
     static constexpr int NST_V = 63 / PER_WAVE + 1;
-    static constexpr int NST = NST_LDS < NST_V ? (NST_LDS < 4 ? NST_LDS : 4) : (NST_V < 4 ? NST_V : 4);
+    static constexpr int NST_A = NST_LDS < NST_V ? NST_LDS : NST_V;
+    static constexpr int NST = NST_A < NSTC ? NST_A : NSTC;
     static_assert(NST >= 2, "two stages at least");
     static_assert(PER_WAVE * (NST - 1) < 64, "vmcnt budget");
     static_assert(!MLA || DV == 512, "MLA values are the first 512 columns (16 blocks)");
 };
 
-template <int DQK, int DV, int HW, bool MLA, bool OUTF32, bool FUSED>
+template <int DQK, int DV, int HW, bool MLA, bool OUTF32, bool FUSED, int NSTC = 4>
 __global__ __launch_bounds__(64 * HW) void attend_kernel(AttendArgs a, uint16_t *po, float *pml, int R, FuseArgs f) {
-    using G = AttTile<DQK, DV, HW, MLA, OUTF32>;
+    using G = AttTile<DQK, DV, HW, MLA, OUTF32, NSTC>;
     constexpr int NT = G::NT;
     constexpr int KSQ = DQK / 32;
     constexpr int NCB = DV / 16;
     extern __shared__ __attribute__((aligned(16))) unsigned char lds[];
-    int *posbuf = reinterpret_cast<int *>(lds + G::NST * G::STAGE);  // [kMaxR]
-    uint32_t *vmask = reinterpret_cast<uint32_t *>(posbuf + kMaxR);   // [kMaxR / 32] valid rows per tile
+    int *posbuf = reinterpret_cast<int *>(lds + G::NST * G::STAGE);  // [R] (R <= kMaxR, a multiple of 32)
+    uint32_t *vmask = reinterpret_cast<uint32_t *>(posbuf + R);       // [R / 32] valid rows per tile
 
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int hl = lane & 15, q4 = lane >> 4;
@@ -205,22 +224,74 @@ __global__ __launch_bounds__(64 * HW) void attend_kernel(AttendArgs a, uint16_t 
     // LDS position list need them), then tile 0's DMA, then Q (the first MFMA waits for
     // Q, and so for tile 0, but not for the later tiles), then the DMA of tiles
     // 1 .. NST-2. The position list is written to LDS last, ready by the loop's first
-    // barrier.
-    auto rowpos = [&](int i) {  // cache row of selected row i of the split, -1 if none
-        if constexpr (FUSED) {  // the position list holds cache rows when paged
-            const int s = i < nrows ? posbuf[i] : -1;
-            return (s >= 0 && (a.bt || s < a.N)) ? s : -1;
-        } else {
-            const int s = i < nrows ? idxrow[i] : -1;
-            return (s >= 0 && s < a.N && s <= pmax) ? phys(s) : -1;
-        }
-    };
-    const int lpos0 = rowpos(tid);  // this thread's first entry of the LDS position list
+    // barrier. Without the fused resolve the positions come from the index list: every
+    // entry this thread needs is requested at once (the DMA rows of the first tiles and
+    // its entries of the LDS list), then checked, then, for a paged cache, mapped to cache
+    // rows by a second batch of block-table loads, so the round trips overlap instead of
+    // following one another.
+    constexpr int PIT = kMaxR / NT;   // LDS list entries per thread, at most
+    const int nlist = ntile * kRows;  // LDS list length (whole tiles)
     int dpos[G::NST - 1][2];
+    int lpos[PIT];                    // entries tid + NT j of the LDS list (without the fused resolve)
+    if constexpr (FUSED) {
 #pragma unroll
-    for (int p = 0; p < G::NST - 1; ++p) {
-        dpos[p][0] = rowpos(p * kRows + drow);
-        dpos[p][1] = rowpos(p * kRows + drow + 16);
+        for (int p = 0; p < G::NST - 1; ++p)
+#pragma unroll
+            for (int r = 0; r < 2; ++r) {
+                const int i = p * kRows + drow + 16 * r;
+                const int ps = i < nrows ? posbuf[i] : -1;  // cache rows when paged
+                dpos[p][r] = (ps >= 0 && (a.bt || ps < a.N)) ? ps : -1;
+            }
+    } else {
+        auto raw = [&](int i) -> int {  // entry i of the split's index list (nrows > 0), -1 past it
+            const int v = idxrow[min(i, nrows - 1)];
+            return i < nrows ? v : -1;
+        };
+        auto check = [&](int ps) { return (ps >= 0 && ps < a.N && ps <= pmax) ? ps : -1; };
+#pragma unroll
+        for (int p = 0; p < G::NST - 1; ++p) dpos[p][0] = dpos[p][1] = -1;
+#pragma unroll
+        for (int j = 0; j < PIT; ++j) lpos[j] = -1;
+        if (nrows > 0) {  // unconditional loads (clamped indices), so they issue back to back
+#pragma unroll
+            for (int p = 0; p < G::NST - 1; ++p) {
+                dpos[p][0] = raw(p * kRows + drow);
+                dpos[p][1] = raw(p * kRows + drow + 16);
+            }
+#pragma unroll
+            for (int j = 0; j < PIT; ++j) lpos[j] = raw(tid + NT * j);
+        }
+#pragma unroll
+        for (int p = 0; p < G::NST - 1; ++p) {
+            dpos[p][0] = check(dpos[p][0]);
+            dpos[p][1] = check(dpos[p][1]);
+        }
+#pragma unroll
+        for (int j = 0; j < PIT; ++j) lpos[j] = check(lpos[j]);
+        if (a.bt) {
+            // page of each position (page 0 for none), its block-table entry, then the row
+            auto page = [&](int ps) { return ps >= 0 ? min(ps / a.page_size, a.max_pages - 1) : 0; };
+            auto row = [&](int ps, int pp) -> int {
+                if (ps < 0 || ps / a.page_size >= a.max_pages || pp < 0 || pp >= a.num_pages) return -1;
+                return pp * a.page_size + ps % a.page_size;
+            };
+            const int32_t *btrow = a.bt + (int64_t)b * a.max_pages;
+            int dpp[G::NST - 1][2], lpp[PIT];
+#pragma unroll
+            for (int p = 0; p < G::NST - 1; ++p) {
+                dpp[p][0] = btrow[page(dpos[p][0])];
+                dpp[p][1] = btrow[page(dpos[p][1])];
+            }
+#pragma unroll
+            for (int j = 0; j < PIT; ++j) lpp[j] = btrow[page(lpos[j])];
+#pragma unroll
+            for (int p = 0; p < G::NST - 1; ++p) {
+                dpos[p][0] = row(dpos[p][0], dpp[p][0]);
+                dpos[p][1] = row(dpos[p][1], dpp[p][1]);
+            }
+#pragma unroll
+            for (int j = 0; j < PIT; ++j) lpos[j] = row(lpos[j], lpp[j]);
+        }
     }
     // invalid rows read row 0 (finite values; zero probability)
     if (ntile > 0) issue_tile(0, max(dpos[0][0], 0), max(dpos[0][1], 0));
@@ -230,13 +301,23 @@ __global__ __launch_bounds__(64 * HW) void attend_kernel(AttendArgs a, uint16_t 
         if (p < ntile) issue_tile(p, max(dpos[p][0], 0), max(dpos[p][1], 0));
     // (FUSED: entries are rewritten in place, each by the thread that reads it; the DMA
     // positions read above take max(., 0) and so agree with either value)
-    for (int i = tid; i < ntile * kRows; i += NT) {
-        const int ps = i == tid ? lpos0 : rowpos(i);
-        posbuf[i] = max(ps, 0);
-        const uint64_t bal = __ballot(ps >= 0);
-        if (lane == 0) {
+#pragma unroll
+    for (int j = 0; j < PIT; ++j) {
+        if (NT * j >= nlist) break;
+        const int i = tid + NT * j;
+        const bool in = i < nlist;
+        int ps = -1;
+        if constexpr (FUSED) {
+            const int v = in && i < nrows ? posbuf[i] : -1;
+            ps = (v >= 0 && (a.bt || v < a.N)) ? v : -1;
+        } else {
+            ps = lpos[j];
+        }
+        if (in) posbuf[i] = max(ps, 0);
+        const uint64_t bal = __ballot(in && ps >= 0);
+        if (lane == 0 && in) {
             vmask[i >> 5] = (uint32_t)bal;
-            if (i + 32 < ntile * kRows) vmask[(i >> 5) + 1] = (uint32_t)(bal >> 32);
+            if (i + 32 < nlist) vmask[(i >> 5) + 1] = (uint32_t)(bal >> 32);
         }
     }
 
@@ -258,15 +339,7 @@ __global__ __launch_bounds__(64 * HW) void attend_kernel(AttendArgs a, uint16_t 
 
     for (int it = 0; it < ntile; ++it) {
         // this wave's loads of tile `it` have landed once at most (ahead * PER_WAVE) are pending
-        const int ahead = min(G::NST - 2, ntile - 1 - it);
-        if constexpr (G::NST >= 4) {
-            if (ahead >= 2) wait_vmcnt<(G::NST >= 4 ? 2 * G::PER_WAVE : 0)>();
-            else if (ahead == 1) wait_vmcnt<G::PER_WAVE>();
-            else wait_vmcnt<0>();
-        } else {
-            if (ahead >= 1) wait_vmcnt<G::PER_WAVE>();
-            else wait_vmcnt<0>();
-        }
+        wait_tiles<G::PER_WAVE, G::NST - 2>(min(G::NST - 2, ntile - 1 - it));
         __syncthreads();  // every wave's loads of tile `it` landed; tile it-1 no longer read
         if (it + G::NST - 1 < ntile) {
             const int nt = it + G::NST - 1;
@@ -275,6 +348,7 @@ __global__ __launch_bounds__(64 * HW) void attend_kernel(AttendArgs a, uint16_t 
         const lds_u8 *kt = (const lds_u8 *)lds + (it % G::NST) * G::STAGE;
         const lds_u8 *vt = MLA ? kt : kt + G::KB * kBlk;
         const uint32_t vm = vmask[it];
+        if (16 * wave >= g) continue;  // a wave without query heads only loads tiles
 
         // ---- S^T tile (32 rows x 16 heads): st[rb][r] = row 16 rb + 4 q4 + r, head hl
         f32x4 st[2] = {f32x4{0.0f, 0.0f, 0.0f, 0.0f}, f32x4{0.0f, 0.0f, 0.0f, 0.0f}};
@@ -521,14 +595,9 @@ __global__ __launch_bounds__(256) void attend_mla_kernel(AttendArgs a, uint16_t 
     const int32_t *idxrow = FUSED ? nullptr : a.idx + (a.idx_shared ? (int64_t)b : selrow) * K + r0;
     const int pmax = a.idx_shared ? (a.ctx_len ? a.ctx_len[b] : a.N) - T + t : 0x7FFFFFFF;
     const uint16_t *kbase = a.k + layer * a.lsk + bofs + kvh * a.ksh;
-    auto rowpos = [&](int i) {  // cache row of selected row i of the split, -1 if none
-        if constexpr (FUSED) {
-            const int s = i < nrows ? posbuf[i] : -1;
-            return (s >= 0 && (a.bt || s < a.N)) ? s : -1;
-        } else {
-            const int s = i < nrows ? idxrow[i] : -1;
-            return (s >= 0 && s < a.N && s <= pmax) ? phys(s) : -1;
-        }
+    auto rowpos = [&](int i) {  // (fused resolve) cache row of selected row i of the split, -1 if none
+        const int s = i < nrows ? posbuf[i] : -1;
+        return (s >= 0 && (a.bt || s < a.N)) ? s : -1;
     };
     // ---- DMA of tile j into this wave's slot: instruction n fills block n / 2 for rows
     // 16 (n & 1) .. +15; lane l writes row 16 (n & 1) + l / 4, physical chunk l & 3
@@ -549,8 +618,34 @@ __global__ __launch_bounds__(256) void attend_mla_kernel(AttendArgs a, uint16_t 
     // of valid rows (bit r: row r)
     auto tile_rows = [&](int rd, int &p0, int &p1) {
         const int j = 4 * rd + wave;
-        p0 = j < ntile ? rowpos(32 * j + drow) : -1;
-        p1 = j < ntile ? rowpos(32 * j + drow + 16) : -1;
+        if constexpr (FUSED) {
+            p0 = j < ntile ? rowpos(32 * j + drow) : -1;
+            p1 = j < ntile ? rowpos(32 * j + drow + 16) : -1;
+        } else {
+            // both entries requested together (clamped indices, unconditional loads), then
+            // checked and, paged, mapped to cache rows by a second pair of loads
+            p0 = p1 = -1;
+            if (nrows > 0) {
+                const int i0 = 32 * j + drow, i1 = i0 + 16;
+                const int v0 = idxrow[min(i0, nrows - 1)], v1 = idxrow[min(i1, nrows - 1)];
+                p0 = i0 < nrows ? v0 : -1;
+                p1 = i1 < nrows ? v1 : -1;
+            }
+            auto check = [&](int ps) { return (ps >= 0 && ps < a.N && ps <= pmax) ? ps : -1; };
+            p0 = check(p0);
+            p1 = check(p1);
+            if (a.bt) {
+                auto page = [&](int ps) { return ps >= 0 ? min(ps / a.page_size, a.max_pages - 1) : 0; };
+                auto row = [&](int ps, int pp) -> int {
+                    if (ps < 0 || ps / a.page_size >= a.max_pages || pp < 0 || pp >= a.num_pages) return -1;
+                    return pp * a.page_size + ps % a.page_size;
+                };
+                const int32_t *btrow = a.bt + (int64_t)b * a.max_pages;
+                const int pp0 = btrow[page(p0)], pp1 = btrow[page(p1)];
+                p0 = row(p0, pp0);
+                p1 = row(p1, pp1);
+            }
+        }
     };
     auto tile_mask = [&](int p0, int p1) -> uint32_t {
         const int a0 = __shfl(p0, 4 * (lane & 15), 64), a1 = __shfl(p1, 4 * (lane & 15), 64);
@@ -921,34 +1016,39 @@ size_t partial_rows_bytes(const AttendArgs &a, int S) {
     return ((size_t)a.L * a.B * a.T * a.Hq * S * a.d_v * 2 + 255) & ~(size_t)255;
 }
 
-template <int DQK, int DV, int HW, bool MLA, bool OUTF32>
+template <int DQK, int DV, int HW, bool MLA, bool OUTF32, int NSTC = 4>
 hipError_t launch_t(const AttendArgs &a, void *ws, hipStream_t s, const FuseArgs *fuse) {
     const int R = rows_per_split(a);
     const int S = (a.K + R - 1) / R;
     uint16_t *po = reinterpret_cast<uint16_t *>(ws);
     float *pml = S > 1 ? reinterpret_cast<float *>(reinterpret_cast<char *>(ws) + partial_rows_bytes(a, S)) : nullptr;
     dim3 grid(S, a.T * a.Hkv, a.B * a.L);
-    using G = AttTile<DQK, DV, HW, MLA, OUTF32>;
-    const size_t lds = (size_t)G::NST * G::STAGE + (size_t)kMaxR * sizeof(int) + (size_t)(kMaxR / 32) * sizeof(uint32_t);
+    using G = AttTile<DQK, DV, HW, MLA, OUTF32, NSTC>;
+    // the ring, then the split's position list and row masks (sized by the split, so that
+    // short splits leave room for more workgroups per compute unit)
+    const size_t lds = (size_t)G::NST * G::STAGE + (size_t)R * sizeof(int) + (size_t)(R / 32) * sizeof(uint32_t);
     if (fuse) {
-        // (the chain runs only with four waves a workgroup: launch_select_attend decides)
-        if constexpr (HW != 4) return hipErrorInvalidValue;
-        // the resolve's working set in the tile ring: histograms and scratch, the row
-        // bitmap when it fits beside the first tie entries, the rest for ties
-        FuseArgs f = *fuse;
-        constexpr size_t ring = (size_t)G::NST * G::STAGE;
-        constexpr size_t fixed = sel::kB2 * 4 + 256 * 4 + 32 * 4;
-        f.pw_log = sel::slice_pw_log(f.w.words, G::NT);
-        const size_t bb = ((size_t)G::NT << f.pw_log) * 4;  // transposed bitmap
-        static_assert(ring >= fixed + sel::kSliceTiesFirst * 8, "tile ring too small for the resolve");
-        f.bits_lds = ring >= fixed + bb + (size_t)sel::kSliceTiesFirst * 8;
-        f.tl = (int)(((ring - fixed - (f.bits_lds ? bb : 0)) / 8) & ~(size_t)1);
-        if constexpr (HW == 4)
-            hipLaunchKernelGGL((attend_kernel<DQK, DV, HW, MLA, OUTF32, true>), grid, dim3(64 * HW), lds, s, a, po, pml,
-                               R, f);
+        // (the chain runs only with four waves of heads and the 4-stage ring:
+        // launch_select_attend decides)
+        if constexpr (HW != 4 || NSTC != 4) {
+            return hipErrorInvalidValue;
+        } else {
+            // the resolve's working set in the tile ring: histograms and scratch, the row
+            // bitmap when it fits beside the first tie entries, the rest for ties
+            FuseArgs f = *fuse;
+            constexpr size_t ring = (size_t)G::NST * G::STAGE;
+            constexpr size_t fixed = sel::kB2 * 4 + 256 * 4 + 32 * 4;
+            f.pw_log = sel::slice_pw_log(f.w.words, G::NT);
+            const size_t bb = ((size_t)G::NT << f.pw_log) * 4;  // transposed bitmap
+            static_assert(ring >= fixed + sel::kSliceTiesFirst * 8, "tile ring too small for the resolve");
+            f.bits_lds = ring >= fixed + bb + (size_t)sel::kSliceTiesFirst * 8;
+            f.tl = (int)(((ring - fixed - (f.bits_lds ? bb : 0)) / 8) & ~(size_t)1);
+            hipLaunchKernelGGL((attend_kernel<DQK, DV, HW, MLA, OUTF32, true, NSTC>), grid, dim3(64 * HW), lds, s, a, po,
+                               pml, R, f);
+        }
     } else {
-        hipLaunchKernelGGL((attend_kernel<DQK, DV, HW, MLA, OUTF32, false>), grid, dim3(64 * HW), lds, s, a, po, pml, R,
-                           FuseArgs{});
+        hipLaunchKernelGGL((attend_kernel<DQK, DV, HW, MLA, OUTF32, false, NSTC>), grid, dim3(64 * HW), lds, s, a, po,
+                           pml, R, FuseArgs{});
     }
     hipError_t e = hipGetLastError();
     if (e != hipSuccess || S == 1) return e;
@@ -995,12 +1095,27 @@ hipError_t launch_d(const AttendArgs &a, void *ws, hipStream_t s, const FuseArgs
     }
     const int g = a.Hq / a.Hkv;
     const int HW = (g + 15) / 16;
+    if (HW == 1) {
+        // one wave of query heads: four waves share the tile loads (three of them compute
+        // nothing), so a workgroup keeps more DMA in flight than one wave's 6-bit vmcnt
+        // allows. A 3-stage ring when three workgroups then fit on a compute unit, else a
+        // 2-stage ring when that fits more of them (long splits: their position lists take
+        // the LDS).
+        using G3 = AttTile<DQK, DV, 4, MLA, false, 3>;
+        using G2 = AttTile<DQK, DV, 4, MLA, false, 2>;
+        const int R = rows_per_split(a);
+        const size_t list = (size_t)R * sizeof(int) + (size_t)(R / 32) * sizeof(uint32_t);
+        const int n3 = (int)(kLdsPerCu / ((size_t)G3::NST * G3::STAGE + list));
+        const int n2 = (int)(kLdsPerCu / ((size_t)G2::NST * G2::STAGE + list));
+        const bool two = n3 < 3 && n2 > n3;
+        if (a.out_f32)
+            return two ? launch_t<DQK, DV, 4, MLA, true, 2>(a, ws, s, fuse) : launch_t<DQK, DV, 4, MLA, true, 3>(a, ws, s, fuse);
+        return two ? launch_t<DQK, DV, 4, MLA, false, 2>(a, ws, s, fuse) : launch_t<DQK, DV, 4, MLA, false, 3>(a, ws, s, fuse);
+    }
     if (a.out_f32) {
-        if (HW == 1) return launch_t<DQK, DV, 1, MLA, true>(a, ws, s, fuse);
         if (HW == 2) return launch_t<DQK, DV, 2, MLA, true>(a, ws, s, fuse);
         return launch_t<DQK, DV, 4, MLA, true>(a, ws, s, fuse);
     }
-    if (HW == 1) return launch_t<DQK, DV, 1, MLA, false>(a, ws, s, fuse);
     if (HW == 2) return launch_t<DQK, DV, 2, MLA, false>(a, ws, s, fuse);
     return launch_t<DQK, DV, 4, MLA, false>(a, ws, s, fuse);
 }
@@ -1026,7 +1141,9 @@ int attend_default_splits(const AttendArgs &a) {
         if (s > kAttendMaxSplits) s = kAttendMaxSplits;
         return (int)(s < 1 ? 1 : s);
     }
-    const long target = HW == 4 ? 256 : 1024;
+    // four waves of heads: one workgroup per compute unit; one wave of heads: three per
+    // compute unit in one generation; else four workgroups per compute unit over the launch
+    const long target = HW == 4 ? 256 : HW == 1 ? kOneHeadTarget : 1024;
     long s = (target + units - 1) / units;
     const long smax = (a.K + kRows - 1) / kRows;
     const long smin = (a.K + kMaxR - 1) / kMaxR;

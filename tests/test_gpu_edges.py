@@ -146,15 +146,18 @@ def test_hi_with_all_blocks_kept_equals_flat():
     assert torch.equal(r_hi["idx"], r_flat["idx"])
 
 
-def test_cli_reuse_equals_per_layer_calls():
+@pytest.mark.parametrize("splits", [1, 8, 16])
+def test_cli_reuse_equals_per_layer_calls(splits):
+    # the same split count on both sides (the default count depends on the number of
+    # layers in the launch, and the split merge's order on the count)
     cfg = config(5, B=4, N=4000, K=512, S=32, W=128)
     inp = make_inputs(cfg)
     d = upload(inp)
     r = gpu_index_select(d)
-    out, lse = gpu_attend(d, r["idx"])
+    out, lse = gpu_attend(d, r["idx"], n_splits=splits)
     for layer in range(cfg.layers):
         o1, l1 = L.lsa_attend(d["q"][layer:layer + 1], d["k"][layer:layer + 1], d["v"][layer:layer + 1],
-                              r["idx"], cfg.tau)
+                              r["idx"], cfg.tau, n_splits=splits)
         assert torch.equal(o1[0], out[layer]) and torch.equal(l1[0], lse[layer])
 
 
