@@ -142,11 +142,21 @@ __global__ __launch_bounds__(kHT) void select_filter_kernel(SelectArgs a, Ws w, 
         // flat rows: branch-free (the column is the position); a kept map needs its load
         const int lo = a.causal ? r.f_sink_end : 0;
         const int hi = a.causal ? min(r.p + 1, r.f_win_lo) : end;  // candidates: lo <= col < hi
+        // kept map: the eight columns' entries requested together (clamped block index,
+        // unconditional loads), so their round trips overlap
+        int kbv[KEPT ? 8 : 1];
+        if constexpr (KEPT) {
+#pragma unroll
+            for (int i = 0; i < 8; ++i) {
+                const int col = (i < 4 ? ca : cb) + (i & 3);
+                kbv[i] = r.kept[min(col / a.block_size, a.n_keep - 1)];
+            }
+        }
         auto classify = [&](int i, int col, float x) {
             uint64_t comp = 0;
             bool cand;
             if constexpr (KEPT) {
-                cand = col < end && candidate_x(a, r, col, x, comp);
+                cand = col < end && candidate_kb(a, r, col, x, kbv[i], comp);
             } else {
                 cand = x > kNegInf && col < end && col >= lo && col < hi;
                 comp = ((uint64_t)order_key(x) << 32) | (uint32_t)~(uint32_t)col;
@@ -378,8 +388,7 @@ __global__ __launch_bounds__(kRT) void select_resolve_kernel(SelectArgs a, Ws w,
                 const int col = i * 32 + __ffs(bits) - 1;
                 bits &= bits - 1;
                 if constexpr (KEPT) {
-                    const int blk = col / a.block_size;
-                    if (off < (uint32_t)KPAD) fill[off] = r.kept[blk] * a.block_size + (col - blk * a.block_size);
+                    if (off < (uint32_t)KPAD) fill[off] = col;  // its position below
                 } else {
                     if (nsink + off < (uint32_t)a.K) dst[nsink + off] = col;
                 }
@@ -388,6 +397,13 @@ __global__ __launch_bounds__(kRT) void select_resolve_kernel(SelectArgs a, Ws w,
         }
         if constexpr (KEPT) {
             nfill = min(nfill, (uint32_t)KPAD);
+            // columns -> positions through the kept map, each thread its own entries, so the
+            // loads are independent (in the bit walk each waited for the previous one)
+            __syncthreads();
+            for (uint32_t i = tid; i < nfill; i += kRT) {
+                const int col = fill[i], blk = col / a.block_size;
+                fill[i] = r.kept[blk] * a.block_size + (col - blk * a.block_size);
+            }
             // an ascending kept map leaves the fill sorted (checked with the first loads)
             __syncthreads();
             const bool ascending = s_desc == 0;
@@ -594,12 +610,16 @@ __global__ __launch_bounds__(kSmallT) void select_small_kernel(SelectArgs a, Ws 
             while (bits && off < nfill) {
                 const int c = i * 32 + __ffs(bits) - 1;
                 bits &= bits - 1;
-                if constexpr (KEPT) fill[off] = pos_of(c);
+                if constexpr (KEPT) fill[off] = c;  // its position below
                 else dst[nsink + off] = c;
                 ++off;
             }
         }
         if constexpr (KEPT) {
+            // columns -> positions through the kept map, each thread its own entries (the
+            // loads independent of one another)
+            __syncthreads();
+            for (uint32_t i = tid; i < nfill; i += NT) fill[i] = pos_of(fill[i]);
             // a kept map whose valid entries ascend, then -1 (as lsa_select writes it), keeps
             // the columns in position order (checked with the loads); otherwise the fill is
             // sorted (bitonic, in LDS)

@@ -117,6 +117,18 @@ __device__ __forceinline__ bool candidate_x(const SelectArgs &a, const Row &r, i
     return true;
 }
 
+// candidate_x with the column's kept-map entry already loaded (kb = kept[col / block_size]
+// when that block index is below n_keep)
+__device__ __forceinline__ bool candidate_kb(const SelectArgs &a, const Row &r, int col, float x, int kb, uint64_t &comp) {
+    if (!(x > kNegInf)) return false;
+    const int blk = col / a.block_size;
+    if (blk >= a.n_keep || kb < 0 || kb >= r.nblk) return false;
+    const int pos = kb * a.block_size + (col - blk * a.block_size);
+    if (a.causal && (pos > r.p || pos < r.f_sink_end || pos >= r.f_win_lo)) return false;
+    comp = ((uint64_t)order_key(x) << 32) | (uint32_t)(~(uint32_t)pos);
+    return true;
+}
+
 __device__ __forceinline__ int comp_pos(uint64_t c) { return (int)(~(uint32_t)c); }
 
 __device__ __forceinline__ uint32_t lane_rank(uint64_t mask) {  // set lanes of mask below this lane
