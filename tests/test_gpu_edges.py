@@ -3,7 +3,9 @@
 Short and ragged contexts, per-sequence context lengths, ties everywhere (zero
 weights: every score equal), an empty fill (K = sink + window), K = 1, padded and
 out-of-range idx entries, explicit split counts, HI with every block kept equal to
-flat selection, CLI reuse equal to per-layer calls, fp32 output, workspace reuse.
+flat selection, CLI reuse equal to per-layer calls, fp32 output, workspace reuse, the
+split merge in several rounds, and the attention shapes with up to 16 query heads per KV
+head (MLA and GQA rows, 2- and 3-stage rings).
 """
 import numpy as np
 import pytest
@@ -191,3 +193,28 @@ def test_attend_128_splits_merge_in_rounds(cid):
     for b in range(cfg.B):
         check_attn(o[0, b, 0], ora["out"][(0, b, 0)], f"c{cid} 128 splits b={b}")
         assert np.allclose(l[0, b, 0], ora["lse"][(0, b, 0)], atol=2e-3), f"c{cid} lse b={b}"
+
+
+@pytest.mark.parametrize("cid,Hq,Hkv,K,splits", [
+    (2, 16, 1, 512, 0),     # MLA rows, one wave of heads: four waves load, 36 KB stages
+    (2, 8, 1, 1024, 1),     # MLA, one long split: the 2-stage ring
+    (5, 64, 4, 2048, 1),    # GQA 16 heads per KV head, one 2048-row split: the 2-stage ring
+    (5, 8, 4, 2048, 3),     # GQA 2 heads per KV head, 3 splits: the 3-stage ring
+    (5, 32, 4, 1024, 0),    # GQA 8 heads per KV head, the default split count
+])
+def test_attend_one_head_wave_shapes(cid, Hq, Hkv, K, splits):
+    # up to 16 query heads per KV head: a workgroup of four waves of which one computes;
+    # the ring depth follows the split length
+    kw = dict(B=2, N=6000, K=K, S=32, W=128, Hq=Hq, Hkv=Hkv)
+    if cid == 5:
+        kw["layers"] = 1
+    cfg = config(cid, **kw)
+    inp = make_inputs(cfg)
+    d = upload(inp)
+    ora = O.reference_step(inp)
+    idx_o = torch.from_numpy(np.stack([[ora["idx"][(b, 0)] for b in range(cfg.B)]]).transpose(1, 0, 2).astype(np.int32)).cuda()
+    out, lse = gpu_attend(d, idx_o, n_splits=splits)
+    o, l = _np(out), _np(lse)
+    for b in range(cfg.B):
+        check_attn(o[0, b, 0], ora["out"][(0, b, 0)], f"c{cid} Hq={Hq} Hkv={Hkv} b={b}")
+        assert np.allclose(l[0, b, 0], ora["lse"][(0, b, 0)], atol=2e-3), f"lse b={b}"
