@@ -146,8 +146,6 @@ __global__ __launch_bounds__(64 * HW) void attend_kernel(AttendArgs a, uint16_t 
             bq[ks] = __builtin_bit_cast(bf16x8, v);
         }
     };
-    // FUSED: Q is requested first, its latency hidden under the selection's
-    if constexpr (FUSED) load_q();
     const int64_t selrow = (int64_t)b * T + t;
     // paged caches: one row pool per layer (no per-sequence offset), position s of
     // sequence b at row bt[b][s / page_size] * page_size + s % page_size
@@ -178,7 +176,9 @@ __global__ __launch_bounds__(64 * HW) void attend_kernel(AttendArgs a, uint16_t 
         S.tl = f.tl;
         S.pw_log = f.pw_log;
         S.bits_lds = f.bits_lds != 0;
-        sel::resolve_slice<NT>(f.sa, f.w, (int)selrow, r0, r0 + nrows, S, posbuf);  // ends with a barrier
+        // Q is requested once the selection's first loads are (their wait does not cover it)
+        sel::resolve_slice<NT>(f.sa, f.w, (int)selrow, r0, r0 + nrows, S, posbuf,
+                               [&]() __attribute__((always_inline)) { load_q(); });  // ends with a barrier
         if (kvh == 0 && layer == 0) {
             int32_t *dst = f.sa.idx + selrow * K + r0;
             for (int i = tid; i < nrows; i += NT) dst[i] = posbuf[i];
@@ -561,7 +561,6 @@ __global__ __launch_bounds__(256) void attend_mla_kernel(AttendArgs a, uint16_t 
 #pragma unroll
         for (int ks = 0; ks < KS; ++ks) bq[ks] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4 *>(qp + 16 * ks));
     };
-    if constexpr (FUSED) load_q();  // its latency hidden under the selection's
     const int nslices = nsplit * HB * Hkv * a.L;
     const int slice = split + nsplit * (hb + HB * (kvh + Hkv * layer));
     if constexpr (FUSED) {
@@ -579,7 +578,10 @@ __global__ __launch_bounds__(256) void attend_mla_kernel(AttendArgs a, uint16_t 
         S.tl = f.tl;
         S.pw_log = f.pw_log;
         S.bits_lds = f.bits_lds != 0;
-        sel::resolve_slice<NT>(f.sa, f.w, (int)selrow, r0, r0 + nrows, S, posbuf);  // ends with a barrier
+        // Q is requested once the selection's first loads are (its latency then hides under
+        // the selection's later phases, and the selection's first wait does not cover it)
+        sel::resolve_slice<NT>(f.sa, f.w, (int)selrow, r0, r0 + nrows, S, posbuf,
+                               [&]() __attribute__((always_inline)) { load_q(); });  // ends with a barrier
         if (kvh == 0 && layer == 0 && hb == 0) {
             int32_t *dst = f.sa.idx + selrow * K + r0;
             for (int i = tid; i < nrows; i += NT) dst[i] = posbuf[i];

@@ -486,9 +486,16 @@ __device__ void copy_bits_transposed(const uint32_t *src, uint32_t *dst, int wor
     }
 }
 
-template <int NT>
+struct NoHook {
+    __device__ void operator()() const {}
+};
+
+// after_loads() is called once the first round of loads has been issued and before it is
+// waited for: loads the caller issues there are not waited for by that round (the vector
+// memory counter retires in issue order, so loads issued earlier would be).
+template <int NT, class Hook = NoHook>
 __device__ void resolve_slice(const SelectArgs &a, const Ws &w, int row, int k0, int k1, const SliceLds &S,
-                              int32_t *lpos) {
+                              int32_t *lpos, Hook after_loads = Hook{}) {
     const int tid = threadIdx.x;
     const Row r = make_row(a, row);
     const int nsink = a.causal ? r.f_sink_end : 0;
@@ -499,19 +506,64 @@ __device__ void resolve_slice(const SelectArgs &a, const Ws &w, int row, int k0,
     uint32_t *gbits = w.bits + (int64_t)row * w.words;
     uint32_t *scr = S.scr;
 
-    // ---- one round of loads: the counters (one thread), the bitmap, the tie list's start
-    if (tid == 0) {
-        scr[28] = gctr[0];
-        scr[29] = gctr[1];
-        scr[30] = gctr[2];
-        scr[31] = gctr[3];
-    }
+    // ---- one round of loads: the counters (one thread), the bitmap, the tie list's start.
+    // When each copy takes at most four 16-byte loads per thread, every load is requested
+    // before any is waited for, and after_loads() runs in between; otherwise the copies
+    // run one after another and after_loads() follows them.
     const int tfirst = min(w.cap, kSliceTiesFirst);
     const int pwl = S.pw_log;
-    if (S.bits_lds) copy_bits_transposed<NT>(gbits, S.bits, w.words, pwl);
-    copy_words_to_lds<NT, 4>(reinterpret_cast<const uint32_t *>(gties), reinterpret_cast<uint32_t *>(S.ties), 2 * tfirst);
-    for (int i = tid; i < kB2; i += NT) S.h[i] = 0;  // the second-level histogram
-    if (tid == 0) scr[24] = 0;
+    const int n4b = S.bits_lds ? w.words >> 2 : 0, n4t = tfirst >> 1;  // 16-byte pieces
+    const bool one_round = ((((uintptr_t)gbits | (uintptr_t)gties | (uintptr_t)gctr | (uintptr_t)S.ties) & 15) == 0) &&
+                           (w.words & 3) == 0 && n4b <= 4 * NT && n4t <= 4 * NT && (tfirst & 1) == 0;
+    if (one_round) {
+        const u32x4 *sb = reinterpret_cast<const u32x4 *>(gbits);
+        const u32x4 *st = reinterpret_cast<const u32x4 *>(gties);
+        u32x4 vb[4], vt[4], vc = {0u, 0u, 0u, 0u};
+        if (n4b > 0) {
+#pragma unroll
+            for (int u = 0; u < 4; ++u) vb[u] = sb[min(u * NT + tid, n4b - 1)];
+        }
+        if (n4t > 0) {
+#pragma unroll
+            for (int u = 0; u < 4; ++u) vt[u] = st[min(u * NT + tid, n4t - 1)];
+        }
+        if (tid == 0) vc = *reinterpret_cast<const u32x4 *>(gctr);
+        after_loads();
+        for (int i = tid; i < kB2; i += NT) S.h[i] = 0;  // the second-level histogram
+        if (n4b > 0) {
+#pragma unroll
+            for (int u = 0; u < 4; ++u) {
+                const int q = u * NT + tid;
+                if (q < n4b)
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) S.bits[bit_slot<NT>(4 * q + e, pwl)] = vb[u][e];
+            }
+        }
+        if (n4t > 0) {
+#pragma unroll
+            for (int u = 0; u < 4; ++u)
+                if (u * NT + tid < n4t) reinterpret_cast<u32x4 *>(S.ties)[u * NT + tid] = vt[u];
+        }
+        if (tid == 0) {
+            scr[28] = vc[0];
+            scr[29] = vc[1];
+            scr[30] = vc[2];
+            scr[31] = vc[3];
+            scr[24] = 0;
+        }
+    } else {
+        if (tid == 0) {
+            scr[28] = gctr[0];
+            scr[29] = gctr[1];
+            scr[30] = gctr[2];
+            scr[31] = gctr[3];
+        }
+        if (S.bits_lds) copy_bits_transposed<NT>(gbits, S.bits, w.words, pwl);
+        copy_words_to_lds<NT, 4>(reinterpret_cast<const uint32_t *>(gties), reinterpret_cast<uint32_t *>(S.ties), 2 * tfirst);
+        after_loads();
+        for (int i = tid; i < kB2; i += NT) S.h[i] = 0;  // the second-level histogram
+        if (tid == 0) scr[24] = 0;
+    }
     __syncthreads();
     const uint32_t ntie = scr[28], mode = scr[29], b1 = scr[30], above = scr[31];
     const uint32_t nfill = mode == 0 ? 0u : (mode == 1 ? min(above, m) : m);
