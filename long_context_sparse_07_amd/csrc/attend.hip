@@ -904,6 +904,7 @@ __global__ __launch_bounds__(kCombT) void attend_combine_kernel(AttendArgs a, co
     constexpr int LPR = DV / 8;                 // lanes per row (8 values each)
     constexpr int SG = kCombT / (HPW * LPR);    // split groups per head
     static_assert(SG >= 1 && HPW * SG * LPR == kCombT && HPW <= 4, "thread layout");
+    static_assert(kMaxSplits <= 128, "two (m, l) pairs per lane");
     constexpr int PER = (kMaxSplits + SG - 1) / SG;  // splits per group at most
     __shared__ float wgt[HPW][kMaxSplits];
     __shared__ float linv[HPW];
@@ -911,29 +912,35 @@ __global__ __launch_bounds__(kCombT) void attend_combine_kernel(AttendArgs a, co
     const int bt = blockIdx.y, layer = blockIdx.z;
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int64_t hbase = (int64_t)layer * a.B * a.T * a.Hq + (int64_t)bt * a.Hq;  // partial heads of (layer, b, t)
-    if (wave < HPW) {
-        const int hq = blockIdx.x * HPW + wave;
-        if (hq < a.Hq) {
-            const float *ml = pml + (hbase + hq) * S * 2;
-            float M = kNegInf;
-            for (int s = lane; s < S; s += 64) M = fmaxf(M, ml[2 * s]);
-#pragma unroll
-            for (int o = 32; o > 0; o >>= 1) M = fmaxf(M, __shfl_xor(M, o, 64));
-            float L = 0.0f;
-            for (int s = lane; s < S; s += 64) {
-                const float m = ml[2 * s];
-                const float wl = (M == kNegInf || m == kNegInf) ? 0.0f : __builtin_amdgcn_exp2f(m - M) * ml[2 * s + 1];
-                wgt[wave][s] = wl;
-                L += wl;
-            }
-#pragma unroll
-            for (int o = 32; o > 0; o >>= 1) L += __shfl_xor(L, o, 64);  // the same tree every run
-            if (lane == 0) {
-                linv[wave] = L > 0.0f ? 1.0f / L : 0.0f;
-                if (a.lse) a.lse[layer * a.lsl + (int64_t)bt * a.Hq + hq] = L > 0.0f ? (M + __builtin_log2f(L)) * kLn2 : kNegInf;
-            }
-        }
+    // The weights' inputs come first: wave w < HPW loads the (m, l) pairs of head w of the
+    // workgroup (two per lane at most). Then every thread requests its first round of
+    // partial rows, and only then are the weights formed, so that their wait does not
+    // cover the rows (the counter retires in order) and the rows' latency overlaps it.
+    const int hw = blockIdx.x * HPW + wave;
+    const bool wwave = wave < HPW && hw < a.Hq;  // uniform per wave
+    float2 ml0 = {kNegInf, 0.0f}, ml1 = {kNegInf, 0.0f};
+    if (wwave) {
+        const float2 *ml = reinterpret_cast<const float2 *>(pml + (hbase + hw) * S * 2);
+        if (lane < S) ml0 = ml[lane];
+        if (lane + 64 < S) ml1 = ml[lane + 64];
     }
+    auto form_weights = [&]() __attribute__((always_inline)) {
+        if (!wwave) return;
+        float M = fmaxf(ml0.x, ml1.x);
+#pragma unroll
+        for (int o = 32; o > 0; o >>= 1) M = fmaxf(M, __shfl_xor(M, o, 64));
+        auto weight = [&](float2 v) { return (M == kNegInf || v.x == kNegInf) ? 0.0f : __builtin_amdgcn_exp2f(v.x - M) * v.y; };
+        const float w0 = weight(ml0), w1 = weight(ml1);
+        if (lane < S) wgt[wave][lane] = w0;
+        if (lane + 64 < S) wgt[wave][lane + 64] = w1;
+        float L = w0 + w1;
+#pragma unroll
+        for (int o = 32; o > 0; o >>= 1) L += __shfl_xor(L, o, 64);  // the same tree every run
+        if (lane == 0) {
+            linv[wave] = L > 0.0f ? 1.0f / L : 0.0f;
+            if (a.lse) a.lse[layer * a.lsl + (int64_t)bt * a.Hq + hw] = L > 0.0f ? (M + __builtin_log2f(L)) * kLn2 : kNegInf;
+        }
+    };
     // ---- this thread's splits (group sg) of chunk c of head hl, all loads in flight
     const int hl = tid / (SG * LPR), sg = (tid / LPR) % SG, c = tid % LPR;
     const int hq = blockIdx.x * HPW + hl;
@@ -947,12 +954,17 @@ __global__ __launch_bounds__(kCombT) void attend_combine_kernel(AttendArgs a, co
     for (int e = 0; e < 8; ++e) acc[e] = 0.0f;
     for (int base = 0; base < PER; base += U) {
         u32x4 v[U];
+        // unconditional loads (a split past S reads the last one and is not accumulated), so
+        // every path issues the same loads and the waits below can count them
 #pragma unroll
         for (int u = 0; u < U; ++u) {
             const int sp = sg + (base + u) * SG;
-            v[u] = (live && sp < S) ? src[(int64_t)sp * RU] : u32x4{0u, 0u, 0u, 0u};
+            v[u] = src[(int64_t)min(sp, S - 1) * RU];
         }
-        if (base == 0) __syncthreads();  // the weights (uniform: every thread runs round 0)
+        if (base == 0) {  // (uniform: every thread runs round 0)
+            form_weights();
+            __syncthreads();  // the weights
+        }
 #pragma unroll
         for (int u = 0; u < U; ++u) {
             const int sp = sg + (base + u) * SG;
