@@ -138,6 +138,12 @@ __global__ __launch_bounds__(PRE ? kThreads : 2 * kThreads) void index_tokens_ke
     static_assert(!EMIT || (MODE == ONEQ && PRE && !HI), "emission: one whole flat row per wave");
     constexpr int kEB = 1024;  // EMIT: running-threshold bins
     __shared__ uint32_t whist[EMIT ? 4 : 1][EMIT ? kEB : 1];
+    // SPLIT with fp8 queries: the query's fp8 codes (64 rows x 128 bytes) and row scales,
+    // quantised once per workgroup (each compute wave a quarter of the rows) instead of by
+    // every compute wave for its whole A operand
+    constexpr bool QSHARE = SPLIT && QF8;
+    __shared__ __attribute__((aligned(16))) uint32_t sq8[QSHARE ? 64 * D / 4 : 1];
+    __shared__ float sqs[QSHARE ? 64 : 1];
 
     const int tid = threadIdx.x;
     const int lane = tid & 63, half = lane >> 5, l32 = lane & 31;
@@ -194,7 +200,7 @@ __global__ __launch_bounds__(PRE ? kThreads : 2 * kThreads) void index_tokens_ke
             if constexpr (!QF8) aq[hb][ks] = __builtin_bit_cast(bf16x8, v);
         }
         float qs = 1.0f;  // QF8: the row's scale, max(amax, 1e-12) / 448
-        if constexpr (QF8) {
+        if constexpr (QF8 && !QSHARE) {
             float amax = 0.0f;
 #pragma unroll
             for (int ks = 0; ks < KSTEPS; ++ks)
@@ -221,8 +227,47 @@ __global__ __launch_bounds__(PRE ? kThreads : 2 * kThreads) void index_tokens_ke
             const int i = 32 * hb + rb;
             row_to_th<MODE>(grp, i, H, T, t, h, ok);
             float wv = (ok && active && !producer) ? a.w[(int64_t)(b * T + t) * H + h] : 0.0f;
-            if constexpr (QF8) wv *= __shfl(qs, rb, 64);  // lane rb holds row rb's scale
+            if constexpr (QF8 && !QSHARE) wv *= __shfl(qs, rb, 64);  // lane rb holds row rb's scale
             wreg[hb][r] = wv;
+        }
+    }
+    if constexpr (QSHARE) {
+        // compute wave w, lane l: row 16 w + l / 4, dims 32 (l % 4) .. +32 of the query
+        if (!producer) {
+            const int i = 16 * wave + (lane >> 2), d0 = 32 * (lane & 3);
+            int t, h;
+            bool ok;
+            row_to_th<MODE>(grp, i, H, T, t, h, ok);
+            ok = ok && active && i < 32 * HB;
+            u32x4 qv[4];
+            const uint16_t *qrow = a.q + ((int64_t)(b * T + t) * H + h) * D + d0;
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                u32x4 v = {0, 0, 0, 0};
+                if (ok) v = *reinterpret_cast<const u32x4 *>(qrow + 8 * j);
+                qv[j] = v;
+            }
+            float amax = 0.0f;
+#pragma unroll
+            for (int j = 0; j < 4; ++j)
+#pragma unroll
+                for (int e = 0; e < 4; ++e)
+                    amax = fmaxf(amax, fmaxf(fabsf(bf16lo(qv[j][e])), fabsf(bf16hi(qv[j][e]))));
+            amax = fmaxf(amax, __shfl_xor(amax, 1, 64));  // the row's four lanes
+            amax = fmaxf(amax, __shfl_xor(amax, 2, 64));
+            const float qs = fmaxf(amax, 1e-12f) / 448.0f;
+            auto code = [&](float x) { return fminf(fmaxf(x / qs, -448.0f), 448.0f); };
+            uint32_t wv[8];
+#pragma unroll
+            for (int wi = 0; wi < 8; ++wi) {  // bytes 4 wi .. +3: dims d0 + 4 wi .. +3
+                const uint32_t lo = qv[wi / 2][2 * (wi % 2)], hi = qv[wi / 2][2 * (wi % 2) + 1];
+                uint32_t c = __builtin_amdgcn_cvt_pk_fp8_f32(code(bf16lo(lo)), code(bf16hi(lo)), 0, false);
+                wv[wi] = __builtin_amdgcn_cvt_pk_fp8_f32(code(bf16lo(hi)), code(bf16hi(hi)), c, true);
+            }
+            u32x4 *dst = reinterpret_cast<u32x4 *>(sq8 + i * (D / 4) + d0 / 4);
+            dst[0] = u32x4{wv[0], wv[1], wv[2], wv[3]};
+            dst[1] = u32x4{wv[4], wv[5], wv[6], wv[7]};
+            if ((lane & 3) == 0) sqs[i] = qs;
         }
     }
     // SPLIT: the compute waves wait for their query and weight loads here, before any
@@ -321,6 +366,24 @@ __global__ __launch_bounds__(PRE ? kThreads : 2 * kThreads) void index_tokens_ke
 #pragma unroll
         for (int p = 0; p < G::NST - 1; ++p)
             if (p < nvis) issue_tile(c0 + p * kKT, p);
+    }
+    if constexpr (QSHARE) {
+        lds_barrier();  // the codes and scales in LDS (the DMA above keeps streaming)
+        if (!producer) {
+#pragma unroll
+            for (int hb = 0; hb < HB; ++hb) {
+                // A operand: row 32 hb + l32, bytes (D / 2) half + 32 kk .. +32
+                const u32x4 *src = reinterpret_cast<const u32x4 *>(sq8 + (32 * hb + l32) * (D / 4) + (D / 8) * half);
+#pragma unroll
+                for (int kk = 0; kk < KF8; ++kk) {
+                    const u32x4 x0 = src[2 * kk], x1 = src[2 * kk + 1];
+                    aq8[hb][kk] = i32x8{(int)x0[0], (int)x0[1], (int)x0[2], (int)x0[3],
+                                        (int)x1[0], (int)x1[1], (int)x1[2], (int)x1[3]};
+                }
+#pragma unroll
+                for (int r = 0; r < 16; ++r) wreg[hb][r] *= sqs[32 * hb + 8 * (r / 4) + 4 * half + (r % 4)];
+            }
+        }
     }
     // the query and weight loads were issued before the ring DMA and so have landed once
     // at most the DMA instructions are pending; waiting here (no store is pending yet, so
