@@ -485,14 +485,41 @@ __global__ __launch_bounds__(kSmallT) void select_small_kernel(SelectArgs a, Ws 
             return c;
         }
     };
+    // ---- the row's keys and first-level histogram: the whole row in one round of loads
+    // (16 bytes per thread for 16-byte aligned rows), requested before the histogram is
+    // cleared so that their latency covers the clearing and its barrier
+    constexpr int U = (kSmallCols + 4 * NT - 1) / (4 * NT);  // 16-byte groups per thread
+    constexpr int US = (kSmallCols + NT - 1) / NT;          // columns per thread (unaligned rows)
+    f32x4 xv[U];
+    float xs[US];
+    if (a.vec) {
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            const int c = 4 * (u * NT + tid);
+            xv[u] = c < nc ? *reinterpret_cast<const f32x4 *>(r.sc + c) : f32x4{kNegInf, kNegInf, kNegInf, kNegInf};
+        }
+    } else {
+#pragma unroll
+        for (int u = 0; u < US; ++u) {
+            const int c = u * NT + tid;
+            xs[u] = c < nc ? r.sc[c] : kNegInf;
+        }
+    }
+    bool desc = false;  // KEPT: the kept map's valid entries do not ascend
+    if constexpr (KEPT) {
+        for (int i = tid; i + 1 < a.n_keep; i += NT) {
+            const int x = r.kept[i], y = r.kept[i + 1];
+            const bool vx = x >= 0 && x < r.nblk, vy = y >= 0 && y < r.nblk;
+            desc = desc || (vy && (!vx || x >= y));
+        }
+    }
     for (int i = tid; i < kSelBins; i += NT) h[i] = 0;
     if (tid == 0) {
         s_nt = 0;
         s_desc = 0;
     }
     __syncthreads();
-    // ---- the row's keys and first-level histogram: four loads in flight per thread,
-    // 16 bytes each for 16-byte aligned rows (the whole 16384-column row in one round)
+    if (desc) s_desc = 1;  // (read after the barriers below)
     auto take = [&](int c, float x) __attribute__((always_inline)) {
         uint64_t comp = 0;
         const bool cand = c < nc && candidate_x(a, r, c, x, comp);
@@ -500,37 +527,16 @@ __global__ __launch_bounds__(kSmallT) void select_small_kernel(SelectArgs a, Ws 
         if (c < nc) keys[c] = key;
         wave_hist_add(h, cand ? (int)(key >> kSelShift) : -1);
     };
-    if constexpr (KEPT) {
-        for (int i = tid; i + 1 < a.n_keep; i += NT) {
-            const int x = r.kept[i], y = r.kept[i + 1];
-            const bool vx = x >= 0 && x < r.nblk, vy = y >= 0 && y < r.nblk;
-            if (vy && (!vx || x >= y)) s_desc = 1;
-        }
-    }
     if (a.vec) {
-        for (int c0 = 0; c0 < nc; c0 += 16 * NT) {
-            f32x4 x[4];
 #pragma unroll
-            for (int u = 0; u < 4; ++u) {
-                const int c = c0 + 4 * (u * NT + tid);
-                x[u] = c < nc ? *reinterpret_cast<const f32x4 *>(r.sc + c) : f32x4{kNegInf, kNegInf, kNegInf, kNegInf};
-            }
+        for (int u = 0; u < U; ++u)
+            if (4 * u * NT < nc)  // uniform: groups past the row are not taken
 #pragma unroll
-            for (int u = 0; u < 4; ++u)
-#pragma unroll
-                for (int e = 0; e < 4; ++e) take(c0 + 4 * (u * NT + tid) + e, x[u][e]);
-        }
+                for (int e = 0; e < 4; ++e) take(4 * (u * NT + tid) + e, xv[u][e]);
     } else {
-        for (int c0 = 0; c0 < nc; c0 += 4 * NT) {
-            float x[4];
 #pragma unroll
-            for (int u = 0; u < 4; ++u) {
-                const int c = c0 + u * NT + tid;
-                x[u] = c < nc ? r.sc[c] : kNegInf;
-            }
-#pragma unroll
-            for (int u = 0; u < 4; ++u) take(c0 + u * NT + tid, x[u]);
-        }
+        for (int u = 0; u < US; ++u)
+            if (u * NT < nc) take(u * NT + tid, xs[u]);
     }
     __syncthreads();
     constexpr int HP = kSelBins / NT;  // first-level bins per thread
