@@ -522,6 +522,7 @@ constexpr int kMMaxPos = 1024; // rows per split held in the LDS position list (
 constexpr int kMKB = 18;       // 64-byte blocks per 576-wide row
 constexpr int kMStage = kMKB * kBlk;
 constexpr int kMLdsFixed = 4 * kMStage + 8192 + 1024;  // slots, probabilities, maxima and sums
+static_assert(32 * 576 * 2 == kMKB * kBlk && 4 * (kMKB / 2) * 1024 == kMKB * kBlk, "Q of 32 heads fills one slot");
 
 template <bool OUTF32, bool FUSED>
 __global__ __launch_bounds__(256) void attend_mla_kernel(AttendArgs a, uint16_t *po, float *pml, int R, int HB,
@@ -556,10 +557,25 @@ __global__ __launch_bounds__(256) void attend_mla_kernel(AttendArgs a, uint16_t 
         return (pp >= 0 && pp < a.num_pages) ? pp * a.page_size + (s - pg * a.page_size) : -1;
     };
     bf16x8 bq[KS];  // B operand of S^T: head n32, dims 16 ks + 8 g .. +8
-    auto load_q = [&]() __attribute__((always_inline)) {
-        const uint16_t *qp = a.q + layer * a.lsq + (selrow * Hq + hq) * 576 + 8 * g;
+    // The block's Q (32 rows of 1152 bytes, contiguous: 36 KB, one slot) is copied into
+    // slot 3 once per workgroup by DMA (while the fused selection runs in slots 0-2), and
+    // every wave takes its fragments from there: each wave loading all of Q from memory had
+    // made the workgroup take in 144 KB of Q beside its 147 KB of rows
+    lds_u8 *qslot = (lds_u8 *)lds + 3 * kMStage;
+    auto dma_q = [&]() __attribute__((always_inline)) {
+        const unsigned char *qsrc =
+            reinterpret_cast<const unsigned char *>(a.q + layer * a.lsq + (selrow * Hq + kvh * gq + 32 * hb) * 576);
 #pragma unroll
-        for (int ks = 0; ks < KS; ++ks) bq[ks] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4 *>(qp + 16 * ks));
+        for (int j = 0; j < kMKB / 2; ++j) {  // 1 KB pieces wave * 9 + j of 36
+            const int n = wave * (kMKB / 2) + j;
+            __builtin_amdgcn_global_load_lds((const glb_void_t *)(qsrc + 1024 * n + 16 * lane),
+                                             (lds_void_t *)(qslot + 1024 * n), 16, 0, 0);
+        }
+    };
+    auto lds_q = [&]() __attribute__((always_inline)) {
+        const lds_u8 *qp = qslot + n32 * 1152 + 16 * g;
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks) bq[ks] = __builtin_bit_cast(bf16x8, *(const lds_u32x4 *)(qp + 32 * ks));
     };
     const int nslices = nsplit * HB * Hkv * a.L;
     const int slice = split + nsplit * (hb + HB * (kvh + Hkv * layer));
@@ -578,10 +594,12 @@ __global__ __launch_bounds__(256) void attend_mla_kernel(AttendArgs a, uint16_t 
         S.tl = f.tl;
         S.pw_log = f.pw_log;
         S.bits_lds = f.bits_lds != 0;
-        // Q is requested once the selection's first loads are (its latency then hides under
-        // the selection's later phases, and the selection's first wait does not cover it)
+        // Q's DMA is issued once the selection's first loads are (its latency then hides
+        // under the selection's later phases, and the selection's first wait does not cover
+        // it); the selection's working set stays in slots 0-2
         sel::resolve_slice<NT>(f.sa, f.w, (int)selrow, r0, r0 + nrows, S, posbuf,
-                               [&]() __attribute__((always_inline)) { load_q(); });  // ends with a barrier
+                               [&]() __attribute__((always_inline)) { dma_q(); });  // ends with a barrier
+        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // this wave's share of Q landed
         if (kvh == 0 && layer == 0 && hb == 0) {
             int32_t *dst = f.sa.idx + selrow * K + r0;
             for (int i = tid; i < nrows; i += NT) dst[i] = posbuf[i];
@@ -592,7 +610,9 @@ __global__ __launch_bounds__(256) void attend_mla_kernel(AttendArgs a, uint16_t 
                 posbuf[i] = (ps >= 0 && ps < a.N) ? phys(ps) : -1;
             }
         }
-        __syncthreads();  // the resolve's working set (the slots) is free, the list complete
+        __syncthreads();  // the working set (slots 0-2) is free, the list complete, Q in slot 3
+        lds_q();
+        __syncthreads();  // slot 3 read by every wave (wave 3's tile goes there)
     }
     const int32_t *idxrow = FUSED ? nullptr : a.idx + (a.idx_shared ? (int64_t)b : selrow) * K + r0;
     const int pmax = a.idx_shared ? (a.ctx_len ? a.ctx_len[b] : a.N) - T + t : 0x7FFFFFFF;
@@ -654,12 +674,27 @@ __global__ __launch_bounds__(256) void attend_mla_kernel(AttendArgs a, uint16_t 
         const bool ok = lane < 32 && (lane < 16 ? a0 : a1) >= 0;
         return (uint32_t)__ballot(ok);
     };
-    // the positions are requested first, then Q (its transfer overlaps their latency),
-    // then the DMA of the first tile
+    // the positions first; without the fused resolve, Q then goes into slot 3 by DMA (once
+    // per workgroup) while waves 0-2 already request their tiles; once every wave has taken
+    // its Q fragments from slot 3, wave 3 requests its tile there
     int cp0, cp1;
     tile_rows(0, cp0, cp1);
-    if constexpr (!FUSED) load_q();
-    if (wave < ntile) issue(max(cp0, 0), max(cp1, 0));
+    if constexpr (FUSED) {
+        if (wave < ntile) issue(max(cp0, 0), max(cp1, 0));
+    } else {
+        dma_q();
+        const bool early = wave < 3 && wave < ntile;
+        if (early) {
+            issue(max(cp0, 0), max(cp1, 0));
+            wait_vmcnt<2 * kMKB>();  // this wave's share of Q landed (its tile may not have)
+        } else {
+            wait_vmcnt<0>();
+        }
+        __syncthreads();  // Q in slot 3
+        lds_q();
+        __syncthreads();  // slot 3 read by every wave
+        if (wave == 3 && wave < ntile) issue(max(cp0, 0), max(cp1, 0));
+    }
     uint32_t vm = tile_mask(cp0, cp1);
 
     f32x16 o[4];
@@ -1084,7 +1119,7 @@ hipError_t launch_mla(const AttendArgs &a, void *ws, hipStream_t s, const FuseAr
     if (fuse) {
         if (R > kMMaxPos) return hipErrorInvalidValue;  // (launch_select_attend checks first)
         FuseArgs f = *fuse;
-        constexpr size_t ring = (size_t)4 * kMStage;
+        constexpr size_t ring = (size_t)3 * kMStage;  // slot 3 takes Q meanwhile
         constexpr size_t fixed = sel::kB2 * 4 + 256 * 4 + 32 * 4;
         f.pw_log = sel::slice_pw_log(f.w.words, 256);
         const size_t bb = ((size_t)256 << f.pw_log) * 4;  // transposed bitmap
