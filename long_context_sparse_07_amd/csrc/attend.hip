@@ -561,6 +561,11 @@ __global__ __launch_bounds__(256) void attend_mla_kernel(AttendArgs a, uint16_t 
     // slot 3 once per workgroup by DMA (while the fused selection runs in slots 0-2), and
     // every wave takes its fragments from there: each wave loading all of Q from memory had
     // made the workgroup take in 144 KB of Q beside its 147 KB of rows
+    // In the slot, row n's 16-byte chunk c sits at chunk c ^ ((n >> 1) & 7) of the row (the
+    // XOR stays inside aligned groups of 8 of its 72 chunks), so that the 16 lanes of a
+    // fragment read (rows n32 .. n32 + 15, one chunk each) hit 16 distinct bank groups:
+    // unswizzled, the 1152-byte row stride put them on two. The permutation is applied
+    // on the global side of the DMA (each lane's LDS destination is fixed).
     lds_u8 *qslot = (lds_u8 *)lds + 3 * kMStage;
     auto dma_q = [&]() __attribute__((always_inline)) {
         const unsigned char *qsrc =
@@ -568,14 +573,21 @@ __global__ __launch_bounds__(256) void attend_mla_kernel(AttendArgs a, uint16_t 
 #pragma unroll
         for (int j = 0; j < kMKB / 2; ++j) {  // 1 KB pieces wave * 9 + j of 36
             const int n = wave * (kMKB / 2) + j;
-            __builtin_amdgcn_global_load_lds((const glb_void_t *)(qsrc + 1024 * n + 16 * lane),
+            const int L = 64 * n + lane, row = L / 72, pc = L % 72;  // LDS chunk L: row, physical chunk
+            __builtin_amdgcn_global_load_lds((const glb_void_t *)(qsrc + 1152 * row + 16 * (pc ^ ((row >> 1) & 7))),
                                              (lds_void_t *)(qslot + 1024 * n), 16, 0, 0);
         }
     };
     auto lds_q = [&]() __attribute__((always_inline)) {
-        const lds_u8 *qp = qslot + n32 * 1152 + 16 * g;
+        // fragment ks: logical chunk 2 ks + g = 8 (ks / 4) + 2 (ks % 4) + g of row n32
+        const int sw = (n32 >> 1) & 7;
+        const lds_u8 *qp = qslot + n32 * 1152;
+        int qo[4];
 #pragma unroll
-        for (int ks = 0; ks < KS; ++ks) bq[ks] = __builtin_bit_cast(bf16x8, *(const lds_u32x4 *)(qp + 32 * ks));
+        for (int k = 0; k < 4; ++k) qo[k] = 16 * ((2 * k + g) ^ sw);
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks)
+            bq[ks] = __builtin_bit_cast(bf16x8, *(const lds_u32x4 *)(qp + 128 * (ks / 4) + qo[ks % 4]));
     };
     const int nslices = nsplit * HB * Hkv * a.L;
     const int slice = split + nsplit * (hb + HB * (kvh + Hkv * layer));
