@@ -92,6 +92,14 @@ __device__ __forceinline__ void wait_tiles(int n) {
     }
 }
 
+// Chunk c (16 bytes) of bf16 query row n in the LDS copy of the query: XOR-permuted so that
+// 16 lanes reading one logical chunk of 16 consecutive rows hit 16 distinct bank groups.
+template <int D>
+__device__ __forceinline__ int qswz(int n, int c) {
+    constexpr int CPR = D / 8, RPB = CPR >= 16 ? 1 : 16 / CPR;
+    return c ^ ((n / RPB) & (CPR - 1));
+}
+
 // Row i of the (query, head) row space of group `grp` -> (t, h); ok = a real row.
 template <int MODE>
 __device__ __forceinline__ void row_to_th(int grp, int i, int H, int T, int &t, int &h, bool &ok) {
@@ -138,12 +146,13 @@ __global__ __launch_bounds__(PRE ? kThreads : 2 * kThreads) void index_tokens_ke
     static_assert(!EMIT || (MODE == ONEQ && PRE && !HI), "emission: one whole flat row per wave");
     constexpr int kEB = 1024;  // EMIT: running-threshold bins
     __shared__ uint32_t whist[EMIT ? 4 : 1][EMIT ? kEB : 1];
-    // SPLIT with fp8 queries: the query's fp8 codes (64 rows x 128 bytes) and row scales,
-    // quantised once per workgroup (each compute wave a quarter of the rows) instead of by
-    // every compute wave for its whole A operand
-    constexpr bool QSHARE = SPLIT && QF8;
-    __shared__ __attribute__((aligned(16))) uint32_t sq8[QSHARE ? 64 * D / 4 : 1];
-    __shared__ float sqs[QSHARE ? 64 : 1];
+    // SPLIT: the query's rows (64 rows: bf16, or fp8 codes with their row scales) and head
+    // weights pass through LDS, loaded (and quantised) once per workgroup, each compute wave
+    // a quarter of the rows, instead of by every compute wave for its whole A operand
+    constexpr bool QSHARE = SPLIT;
+    __shared__ __attribute__((aligned(16))) uint32_t sqb[QSHARE ? 64 * D / (QF8 ? 4 : 2) : 1];
+    __shared__ float sqs[QSHARE && QF8 ? 64 : 1];
+    __shared__ float sw[QSHARE ? 64 : 1];
 
     const int tid = threadIdx.x;
     const int lane = tid & 63, half = lane >> 5, l32 = lane & 31;
@@ -185,7 +194,7 @@ __global__ __launch_bounds__(PRE ? kThreads : 2 * kThreads) void index_tokens_ke
     i32x8 aq8[HB][QF8 ? KF8 : 1];
     float wreg[HB][16];
 #pragma unroll
-    for (int hb = 0; hb < HB; ++hb) {
+    for (int hb = 0; hb < HB && !QSHARE; ++hb) {
         int t, h;
         bool ok;
         row_to_th<MODE>(grp, 32 * hb + l32, H, T, t, h, ok);
@@ -232,42 +241,54 @@ __global__ __launch_bounds__(PRE ? kThreads : 2 * kThreads) void index_tokens_ke
         }
     }
     if constexpr (QSHARE) {
-        // compute wave w, lane l: row 16 w + l / 4, dims 32 (l % 4) .. +32 of the query
+        // compute wave w, lane l: row 16 w + l / 4, dims (D / 4) (l % 4) .. +D/4 of the query,
+        // and (l % 4 == 0) the row's head weight. bf16 rows keep their 16-byte chunks
+        // XOR-permuted (qswz), so the 16 lanes of an operand read hit 16 bank groups.
         if (!producer) {
-            const int i = 16 * wave + (lane >> 2), d0 = 32 * (lane & 3);
+            constexpr int DPL = D / 4;
+            const int i = 16 * wave + (lane >> 2), d0 = DPL * (lane & 3);
             int t, h;
             bool ok;
             row_to_th<MODE>(grp, i, H, T, t, h, ok);
             ok = ok && active && i < 32 * HB;
-            u32x4 qv[4];
+            u32x4 qv[DPL / 8];
             const uint16_t *qrow = a.q + ((int64_t)(b * T + t) * H + h) * D + d0;
 #pragma unroll
-            for (int j = 0; j < 4; ++j) {
+            for (int j = 0; j < DPL / 8; ++j) {
                 u32x4 v = {0, 0, 0, 0};
                 if (ok) v = *reinterpret_cast<const u32x4 *>(qrow + 8 * j);
                 qv[j] = v;
             }
-            float amax = 0.0f;
+            const float wv = ok ? a.w[(int64_t)(b * T + t) * H + h] : 0.0f;
+            if constexpr (QF8) {
+                static_assert(DPL == 32, "fp8 queries: D = 128");
+                float amax = 0.0f;
 #pragma unroll
-            for (int j = 0; j < 4; ++j)
+                for (int j = 0; j < 4; ++j)
 #pragma unroll
-                for (int e = 0; e < 4; ++e)
-                    amax = fmaxf(amax, fmaxf(fabsf(bf16lo(qv[j][e])), fabsf(bf16hi(qv[j][e]))));
-            amax = fmaxf(amax, __shfl_xor(amax, 1, 64));  // the row's four lanes
-            amax = fmaxf(amax, __shfl_xor(amax, 2, 64));
-            const float qs = fmaxf(amax, 1e-12f) / 448.0f;
-            auto code = [&](float x) { return fminf(fmaxf(x / qs, -448.0f), 448.0f); };
-            uint32_t wv[8];
+                    for (int e = 0; e < 4; ++e)
+                        amax = fmaxf(amax, fmaxf(fabsf(bf16lo(qv[j][e])), fabsf(bf16hi(qv[j][e]))));
+                amax = fmaxf(amax, __shfl_xor(amax, 1, 64));  // the row's four lanes
+                amax = fmaxf(amax, __shfl_xor(amax, 2, 64));
+                const float qs = fmaxf(amax, 1e-12f) / 448.0f;
+                auto code = [&](float x) { return fminf(fmaxf(x / qs, -448.0f), 448.0f); };
+                uint32_t cw[8];
 #pragma unroll
-            for (int wi = 0; wi < 8; ++wi) {  // bytes 4 wi .. +3: dims d0 + 4 wi .. +3
-                const uint32_t lo = qv[wi / 2][2 * (wi % 2)], hi = qv[wi / 2][2 * (wi % 2) + 1];
-                uint32_t c = __builtin_amdgcn_cvt_pk_fp8_f32(code(bf16lo(lo)), code(bf16hi(lo)), 0, false);
-                wv[wi] = __builtin_amdgcn_cvt_pk_fp8_f32(code(bf16lo(hi)), code(bf16hi(hi)), c, true);
+                for (int wi = 0; wi < 8; ++wi) {  // bytes 4 wi .. +3: dims d0 + 4 wi .. +3
+                    const uint32_t lo = qv[wi / 2][2 * (wi % 2)], hi = qv[wi / 2][2 * (wi % 2) + 1];
+                    uint32_t c = __builtin_amdgcn_cvt_pk_fp8_f32(code(bf16lo(lo)), code(bf16hi(lo)), 0, false);
+                    cw[wi] = __builtin_amdgcn_cvt_pk_fp8_f32(code(bf16lo(hi)), code(bf16hi(hi)), c, true);
+                }
+                u32x4 *dst = reinterpret_cast<u32x4 *>(sqb + i * (D / 4) + d0 / 4);
+                dst[0] = u32x4{cw[0], cw[1], cw[2], cw[3]};
+                dst[1] = u32x4{cw[4], cw[5], cw[6], cw[7]};
+                if ((lane & 3) == 0) sqs[i] = qs;
+            } else {
+                u32x4 *drow = reinterpret_cast<u32x4 *>(sqb + i * (D / 2));
+#pragma unroll
+                for (int j = 0; j < DPL / 8; ++j) drow[qswz<D>(i, (DPL / 8) * (lane & 3) + j)] = qv[j];
             }
-            u32x4 *dst = reinterpret_cast<u32x4 *>(sq8 + i * (D / 4) + d0 / 4);
-            dst[0] = u32x4{wv[0], wv[1], wv[2], wv[3]};
-            dst[1] = u32x4{wv[4], wv[5], wv[6], wv[7]};
-            if ((lane & 3) == 0) sqs[i] = qs;
+            if ((lane & 3) == 0) sw[i] = wv;
         }
     }
     // SPLIT: the compute waves wait for their query and weight loads here, before any
@@ -368,20 +389,32 @@ __global__ __launch_bounds__(PRE ? kThreads : 2 * kThreads) void index_tokens_ke
             if (p < nvis) issue_tile(c0 + p * kKT, p);
     }
     if constexpr (QSHARE) {
-        lds_barrier();  // the codes and scales in LDS (the DMA above keeps streaming)
+        lds_barrier();  // the query rows and weights in LDS (the DMA above keeps streaming)
         if (!producer) {
 #pragma unroll
             for (int hb = 0; hb < HB; ++hb) {
-                // A operand: row 32 hb + l32, bytes (D / 2) half + 32 kk .. +32
-                const u32x4 *src = reinterpret_cast<const u32x4 *>(sq8 + (32 * hb + l32) * (D / 4) + (D / 8) * half);
+                const int qr = 32 * hb + l32;
+                if constexpr (QF8) {
+                    // A operand: row qr, bytes (D / 2) half + 32 kk .. +32
+                    const u32x4 *src = reinterpret_cast<const u32x4 *>(sqb + qr * (D / 4) + (D / 8) * half);
 #pragma unroll
-                for (int kk = 0; kk < KF8; ++kk) {
-                    const u32x4 x0 = src[2 * kk], x1 = src[2 * kk + 1];
-                    aq8[hb][kk] = i32x8{(int)x0[0], (int)x0[1], (int)x0[2], (int)x0[3],
-                                        (int)x1[0], (int)x1[1], (int)x1[2], (int)x1[3]};
+                    for (int kk = 0; kk < KF8; ++kk) {
+                        const u32x4 x0 = src[2 * kk], x1 = src[2 * kk + 1];
+                        aq8[hb][kk] = i32x8{(int)x0[0], (int)x0[1], (int)x0[2], (int)x0[3],
+                                            (int)x1[0], (int)x1[1], (int)x1[2], (int)x1[3]};
+                    }
+                } else {
+                    // A operand: row qr, dims (D / 2) half + 8 ks .. +8 (chunk (D / 16) half + ks)
+                    const u32x4 *srow = reinterpret_cast<const u32x4 *>(sqb + qr * (D / 2));
+#pragma unroll
+                    for (int ks = 0; ks < KSTEPS; ++ks)
+                        aq[hb][ks] = __builtin_bit_cast(bf16x8, srow[qswz<D>(qr, (D / 16) * half + ks)]);
                 }
 #pragma unroll
-                for (int r = 0; r < 16; ++r) wreg[hb][r] *= sqs[32 * hb + 8 * (r / 4) + 4 * half + (r % 4)];
+                for (int r = 0; r < 16; ++r) {
+                    const int i = 32 * hb + 8 * (r / 4) + 4 * half + (r % 4);
+                    wreg[hb][r] = QF8 ? sw[i] * sqs[i] : sw[i];
+                }
             }
         }
     }
