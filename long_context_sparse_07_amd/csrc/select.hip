@@ -35,6 +35,7 @@ using namespace sel;
 
 constexpr int kHT = 256;             // histogram and filter threads
 constexpr int kRT = 1024;            // resolve threads (16 waves)
+constexpr int kKeptLds = 1024;       // kept-map entries the resolve keeps in LDS
 constexpr int kFC = 2048;            // filter round: 8 columns per thread
 // ----------------------------------------------------------------------------- hist
 __global__ __launch_bounds__(kHT) void select_hist_kernel(SelectArgs a, uint32_t *hist, int part_cols) {
@@ -243,6 +244,10 @@ __global__ __launch_bounds__(kRT) void select_resolve_kernel(SelectArgs a, Ws w,
     __shared__ uint32_t cnt[4];
     __shared__ uint32_t s_desc;  // KEPT: the kept map's valid entries do not ascend
     __shared__ int32_t fill[KEPT ? KPAD : 1];
+    // KEPT: the kept map in LDS when it fits (read with the first loads; the columns of
+    // the fill then map to positions without another round trip to memory)
+    __shared__ int32_t skept[KEPT ? kKeptLds : 1];
+    const bool kl = KEPT && a.n_keep <= kKeptLds;
     const int row = blockIdx.x;
     const int tid = threadIdx.x;
     const Row r = make_row(a, row);
@@ -273,10 +278,14 @@ __global__ __launch_bounds__(kRT) void select_resolve_kernel(SelectArgs a, Ws w,
     // as lsa_select writes it, keeps the columns in position order), read with the first loads
     bool desc = false;
     if constexpr (KEPT) {
-        for (int i = tid; i + 1 < a.n_keep; i += kRT) {
-            const int x = r.kept[i], y = r.kept[i + 1];
-            const bool vx = x >= 0 && x < r.nblk, vy = y >= 0 && y < r.nblk;
-            desc = desc || (vy && (!vx || x >= y));
+        for (int i = tid; i < a.n_keep; i += kRT) {
+            const int x = r.kept[i];
+            if (kl) skept[i] = x;
+            if (i + 1 < a.n_keep) {
+                const int y = r.kept[i + 1];
+                const bool vx = x >= 0 && x < r.nblk, vy = y >= 0 && y < r.nblk;
+                desc = desc || (vy && (!vx || x >= y));
+            }
         }
     }
     const BinPick bp = pick_bin<kRT, 2>(hv, m, scr);  // its barriers follow every thread's reads
@@ -402,7 +411,7 @@ __global__ __launch_bounds__(kRT) void select_resolve_kernel(SelectArgs a, Ws w,
             __syncthreads();
             for (uint32_t i = tid; i < nfill; i += kRT) {
                 const int col = fill[i], blk = col / a.block_size;
-                fill[i] = r.kept[blk] * a.block_size + (col - blk * a.block_size);
+                fill[i] = (kl ? skept[blk] : r.kept[blk]) * a.block_size + (col - blk * a.block_size);
             }
             // an ascending kept map leaves the fill sorted (checked with the first loads)
             __syncthreads();
@@ -829,8 +838,9 @@ template <bool KEPT, int KPAD>
 hipError_t launch_resolve_t(const SelectArgs &a, const Ws &w, hipStream_t s) {
     const int tcap = w.cap < kTieLds ? w.cap : kTieLds;
     const size_t tie_lds = (size_t)tcap * (KEPT ? 12 : 8);
-    // the bitmap goes to LDS when it fits beside the ties and the static arrays (<= 34 KB)
-    const int lwords = (w.words <= kBitsLds && tie_lds + (size_t)w.words * 4 <= 126 * 1024) ? w.words : 0;
+    // the bitmap goes to LDS when it fits beside the ties and the static arrays (<= 38 KB)
+    const size_t budget = (KEPT ? 122 : 126) * 1024;
+    const int lwords = (w.words <= kBitsLds && tie_lds + (size_t)w.words * 4 <= budget) ? w.words : 0;
     const size_t lds = tie_lds + (size_t)lwords * 4;
     hipLaunchKernelGGL((select_resolve_kernel<KEPT, KPAD>), dim3(a.B * a.T), dim3(kRT), lds, s, a, w, lwords);
     return hipGetLastError();

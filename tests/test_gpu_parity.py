@@ -203,13 +203,20 @@ def test_parity_full_size_prefill_sampled():
     run_parity(cfg, rows=[(0, t) for t in ts])
 
 
+@pytest.mark.parametrize("shape", ["small", "mid", "wide"])
 @pytest.mark.parametrize("order", ["ascending", "shuffled"])
-def test_hi_fine_stage_on_given_kept_lists(order):
+def test_hi_fine_stage_on_given_kept_lists(order, shape):
     # The fine stage alone on kept lists that are not the coarse stage's choice (random
     # subsets of the eligible blocks, -1 padded, some empty; ascending as lsa_select writes
     # them, or shuffled with padding in between, which the selection must sort): the GPU's
     # fine scores and selection against the oracle's fine stage run on the same kept list.
-    cfg = config(3, **SMALL[3])
+    # small: 2048 fine columns (the one-launch selection); mid: 300 kept blocks of 64,
+    # 19200 fine columns (the filter and resolve kernels, the kept map copied into the
+    # resolve's LDS); wide: 1100 kept blocks of 16, 17600 fine columns (the kept map too
+    # long for that copy).
+    kw = {"small": SMALL[3], "mid": dict(N=64 * 600, K=512, S=64, W=128, n_keep=300),
+          "wide": dict(N=16 * 3000, K=512, S=64, W=128, n_keep=1100, Bs=16)}[shape]
+    cfg = config(3, **kw)
     inp = make_inputs(cfg)
     d = upload(inp)
     P = O.query_positions(inp["ctx_len"], cfg.T)
