@@ -669,6 +669,25 @@ def main():
         torch.cuda.synchronize()
         return sum(a.elapsed_time(b) for a, b in ev) / n
 
+    def per_dispatch(fn, n, warm):
+        """Mean duration of the token-indexer kernel of one call, from events that its own
+        dispatch records (lsa_index_launch_events): the kernel's execution alone, as a
+        kernel-trace profiler reports it (an event pair around the call also counts the
+        launch latency)."""
+        for i in range(warm):
+            fn(i % R)
+        ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(n)]
+        for a, b in ev:  # created (first record) before the timed calls
+            a.record(stream)
+            b.record(stream)
+        torch.cuda.synchronize()
+        for i in range(n):
+            L.lsa_index_launch_events(ev[i][0], ev[i][1])
+            fn(i % R)
+        L.lsa_index_launch_events(None, None)
+        torch.cuda.synchronize()
+        return sum(a.elapsed_time(b) for a, b in ev) / n
+
     if args.profile_only:
         ms = timed(ch.ways[args.way], args.steps, args.warmup)
         if args.calib_copy:
@@ -689,9 +708,10 @@ def main():
     # A primed selection consumes what the indexer left, so it is timed as (index +
     # select) - index; the workspace is cleared after the indexer-only loop, which leaves
     # it unbalanced.
-    ms_index = per_launch(c_index, args.steps, args.warmup)
+    ms_index_call = per_launch(c_index, args.steps, args.warmup)
+    ms_index = per_dispatch(c_index, args.steps, args.warmup)
     L.lsa_workspace_clear(ws_sel)
-    ms_select = per_launch(lambda r: (c_index(r), c_select(r)), args.steps, args.warmup) - ms_index
+    ms_select = per_launch(lambda r: (c_index(r), c_select(r)), args.steps, args.warmup) - ms_index_call
     ms_attend = per_launch(c_attend, args.steps, args.warmup)
 
     # HIP graphs: one captured step per replica and way (a way whose calls cannot be
@@ -759,7 +779,8 @@ def main():
         "extra": {"step_algorithmic_bytes": step_bytes, "step_hbm_gbs": step_bytes / (ms * 1e-3) / 1e9,
                   "step_frac_of_peak": step_bytes / (ms * 1e-3) / 1e9 / PEAK_HBM_GBS,
                   "ms_per_step_plain": ms_plain, "ms_per_step_graph": ms_graph, "graph_errors": graph_errors,
-                  "ms_index": ms_index, "ms_select": ms_select, "ms_attend": ms_attend,
+                  "ms_index": ms_index, "ms_index_event_pair": ms_index_call,
+                  "ms_select": ms_select, "ms_attend": ms_attend,
                   "index_gbs": idx_b / (ms_index * 1e-3) / 1e9,
                   "kv_gather_gbs": gat_b / (ms_attend * 1e-3) / 1e9,
                   "attend_traffic": pmc_attend_traffic(),

@@ -488,6 +488,16 @@ typedef struct lsa_cache_append_desc {
 
 int32_t lsa_cache_append(const lsa_cache_append_desc *desc, void *stream);
 
+/* Measurement hook (not part of the method): the next launch of the token indexer kernel
+ * made by lsa_index or lsa_index_select on the calling host thread records its start in
+ * start_event and its end in stop_event (hipEvent_t handles created with timing enabled,
+ * owned by the caller; either may be NULL), taken from the kernel's own dispatch, so the
+ * elapsed time between them is the kernel's execution alone, without the launch latency
+ * that a separately recorded event pair around the call adds. The hook applies to one
+ * launch and is then cleared; NULL, NULL clears it. Calls that launch no token indexer
+ * kernel (BLOCKS mode, errors) leave it set. Returns LSA_OK. */
+int32_t lsa_index_launch_events(void *start_event, void *stop_event);
+
 /* Zero-fill `bytes` of device memory at `ptr` with a fill kernel (for workspaces). */
 int32_t lsa_workspace_clear(void *ptr, size_t bytes, void *stream);
 

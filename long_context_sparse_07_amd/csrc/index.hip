@@ -18,6 +18,8 @@
 // "Technical features", third bullet: coarse candidate blocks first).
 //
 // block_means_kernel: kbar[j] = mean of the dequantised keys of block j, fp32.
+#include <hip/hip_ext.h>
+
 #include "common.cuh"
 #include "kernels.h"
 
@@ -762,6 +764,21 @@ int compute_units() {
     return n;
 }
 
+// Measurement hook (lsa_index_launch_events): the next token-indexer launch on this host
+// thread records its own start and end into these events, from the dispatch itself.
+thread_local hipEvent_t t_ev_start = nullptr, t_ev_stop = nullptr;
+
+#define LSA_LAUNCH_TOKENS(K, GRID, BLOCK, LDS, S, ...)                                                      \
+    do {                                                                                                     \
+        if (t_ev_start || t_ev_stop) {                                                                       \
+            hipEvent_t e0_ = t_ev_start, e1_ = t_ev_stop;                                                    \
+            t_ev_start = t_ev_stop = nullptr;                                                                \
+            hipExtLaunchKernelGGL(K, GRID, BLOCK, (uint32_t)(LDS), S, e0_, e1_, 0, __VA_ARGS__);             \
+        } else {                                                                                             \
+            hipLaunchKernelGGL(K, GRID, BLOCK, LDS, S, __VA_ARGS__);                                         \
+        }                                                                                                    \
+    } while (0)
+
 template <int D, bool FP8, bool QF8, int MODE, int HB, bool HI, bool PRE, bool HIST = false>
 hipError_t launch_tokens_t(const IndexTokensArgs &a, hipStream_t s) {
     constexpr int NST = 4;  // one tile computed, three in flight (deeper rings measured no faster)
@@ -781,8 +798,8 @@ hipError_t launch_tokens_t(const IndexTokensArgs &a, hipStream_t s) {
     chunks = (a.n_out + chunk - 1) / chunk;
     dim3 grid(chunks, gy, a.B);
     const size_t lds = (size_t)G::NST * G::STAGE;
-    hipLaunchKernelGGL((index_tokens_kernel<D, FP8, QF8, MODE, HB, HI, PRE, HIST, NST>), grid, dim3(PRE ? kThreads : 2 * kThreads), lds, s, a,
-                       groups, chunk);
+    LSA_LAUNCH_TOKENS((index_tokens_kernel<D, FP8, QF8, MODE, HB, HI, PRE, HIST, NST>), grid,
+                      dim3(PRE ? kThreads : 2 * kThreads), lds, s, a, groups, chunk);
     return hipGetLastError();
 }
 
@@ -796,8 +813,8 @@ hipError_t launch_tokens_emit(const IndexTokensArgs &a, hipStream_t s) {
     const int groups = a.T;
     const dim3 grid(1, (groups + 3) / 4, a.B);
     const size_t lds = (size_t)G::NST * G::STAGE;
-    hipLaunchKernelGGL((index_tokens_kernel<D, FP8, QF8, ONEQ, HB, false, true, false, NST, true>), grid,
-                       dim3(kThreads), lds, s, a, groups, a.n_out);
+    LSA_LAUNCH_TOKENS((index_tokens_kernel<D, FP8, QF8, ONEQ, HB, false, true, false, NST, true>), grid,
+                      dim3(kThreads), lds, s, a, groups, a.n_out);
     return hipGetLastError();
 }
 
@@ -849,6 +866,11 @@ bool index_tokens_supported(int H, int D, bool hi) {
     if (D != 64 && D != 128) return false;
     if (hi) return H >= 1 && H <= 64;
     return H == 4 || H == 8 || H == 16 || H == 32 || H == 64;
+}
+
+void set_index_launch_events(hipEvent_t start, hipEvent_t stop) {
+    t_ev_start = start;
+    t_ev_stop = stop;
 }
 
 hipError_t launch_index_tokens(const IndexTokensArgs &a, hipStream_t s) {

@@ -51,6 +51,9 @@ struct IndexBlocksArgs {
     float *scores;          // [B][T][n_blocks]
 };
 hipError_t launch_index_blocks(const IndexBlocksArgs &a, hipStream_t s);
+// The next launch_index_tokens kernel launch on this host thread records its start and end
+// into these events (taken from the dispatch); null, null: none.
+void set_index_launch_events(hipEvent_t start, hipEvent_t stop);
 
 struct BlockMeansArgs {
     int B, N, D;

@@ -218,3 +218,22 @@ def test_attend_one_head_wave_shapes(cid, Hq, Hkv, K, splits):
     for b in range(cfg.B):
         check_attn(o[0, b, 0], ora["out"][(0, b, 0)], f"c{cid} Hq={Hq} Hkv={Hkv} b={b}")
         assert np.allclose(l[0, b, 0], ora["lse"][(0, b, 0)], atol=2e-3), f"lse b={b}"
+
+
+def test_index_launch_events_time_one_indexer_launch():
+    # the measurement hook: the next token-indexer launch records its own start and end;
+    # the scores are those of a plain call, and the hook is used up by that one launch
+    cfg = config(2, B=2, N=65536)
+    d = upload(make_inputs(cfg))
+    kw = dict(k_scale=d["kI_scale"], ctx_len=d["ctx_len"])
+    sc0 = L.lsa_index(d["qI"], d["w"], d["kI"], **kw)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    L.lsa_index_launch_events(e0, e1)
+    sc1 = L.lsa_index(d["qI"], d["w"], d["kI"], **kw)
+    torch.cuda.synchronize()
+    assert torch.equal(sc1, sc0)
+    ms = e0.elapsed_time(e1)
+    assert 0.0 < ms < 50.0
+    L.lsa_index(d["qI"], d["w"], d["kI"], **kw)
+    torch.cuda.synchronize()
+    assert e0.elapsed_time(e1) == ms
