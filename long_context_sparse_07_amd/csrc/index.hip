@@ -764,6 +764,13 @@ int compute_units() {
     return n;
 }
 
+// Decode (SPLIT) workgroups per compute unit over the launch (one resident at a time: the
+// ring takes more than half of the LDS); a build may set another count to compare.
+#ifndef LSA_DECODE_WG_PER_CU
+#define LSA_DECODE_WG_PER_CU 1
+#endif
+constexpr int kDecodeWgPerCu = LSA_DECODE_WG_PER_CU;
+
 // Measurement hook (lsa_index_launch_events): the next token-indexer launch on this host
 // thread records its own start and end into these events, from the dispatch itself.
 thread_local hipEvent_t t_ev_start = nullptr, t_ev_stop = nullptr;
@@ -790,7 +797,7 @@ hipError_t launch_tokens_t(const IndexTokensArgs &a, hipStream_t s) {
     // SPLIT kernels (8 waves, 2 per SIMD): one workgroup per CU, every wave of a CU the
     // same age, so no workgroup is starved by the oldest-first issue arbitration of an
     // older one on the same CU; shared tiles (4 waves): two per CU
-    const int target = PRE ? 512 : compute_units();
+    const int target = PRE ? 512 : kDecodeWgPerCu * compute_units();
     int want = (target + a.B * gy - 1) / (a.B * gy);
     int chunks = want < 1 ? 1 : (want > max_chunks ? max_chunks : want);
     int chunk = (a.n_out + chunks - 1) / chunks;
