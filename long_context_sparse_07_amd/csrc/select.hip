@@ -855,9 +855,12 @@ hipError_t launch_resolve(const SelectArgs &a, const Ws &w, hipStream_t s) {
 
 // Columns per filter (and histogram) workgroup: about 1024 workgroups in all, at least
 // 2048 columns each, a multiple of 32.
+#ifndef LSA_FILTER_MIN_COLS
+#define LSA_FILTER_MIN_COLS 2048
+#endif
 int part_columns(int rows, int n_cols, int &parts) {
     int p = (1024 + rows - 1) / rows;
-    const int max_parts = (n_cols + 2047) / 2048;
+    const int max_parts = (n_cols + LSA_FILTER_MIN_COLS - 1) / LSA_FILTER_MIN_COLS;
     if (p > max_parts) p = max_parts;
     if (p < 1) p = 1;
     int pc = (n_cols + p - 1) / p;
