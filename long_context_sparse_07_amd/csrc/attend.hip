@@ -1058,9 +1058,12 @@ __global__ __launch_bounds__(kCombT) void attend_combine_kernel(AttendArgs a, co
 
 // The merge launch: one head a workgroup for 128-wide rows (16 split groups), two for
 // 512-wide rows (2 split groups each).
+#ifndef LSA_COMBINE_HEADS_512
+#define LSA_COMBINE_HEADS_512 2
+#endif
 template <int DV, bool OUTF32>
 hipError_t launch_combine(const AttendArgs &a, const uint16_t *po, const float *pml, int S, hipStream_t s) {
-    constexpr int HPW = DV >= 512 ? 2 : 1;
+    constexpr int HPW = DV >= 512 ? LSA_COMBINE_HEADS_512 : 1;
     dim3 cgrid((a.Hq + HPW - 1) / HPW, a.B * a.T, a.L);
     hipLaunchKernelGGL((attend_combine_kernel<DV, HPW, OUTF32>), cgrid, dim3(kCombT), 0, s, a, po, pml, S);
     return hipGetLastError();
