@@ -3,7 +3,8 @@
 The 128K MLA decode step (8 sequences, every row) runs exactly as bench.py builds and
 times it (the same descriptors, workspaces and calls, every way of running the step the
 benchmark chooses among); the 4-layer cross-layer decode runs through the chained call
-the benchmark times; the 4096-token prefill has every row's selection checked against
+the benchmark times (and the 128K decode chain on sequences of different lengths); the
+4096-token prefill has every row's selection checked against
 properties that hold at any size (top-m of the GPU's own scores, forced set, order)
 and sampled rows against the oracle. Selection by the band rule (membership may
 differ from the oracle's only within 1e-4 relative of the m-th score); attention
@@ -55,6 +56,24 @@ def test_c2_headline_chain_full_size():
         torch.cuda.synchronize()
         assert np.array_equal(ch.idx.cpu().numpy(), idx) and np.array_equal(ch.out.float().cpu().numpy(), out), \
             f"c2 {name}: second call differs"
+
+
+def test_c2_chain_ragged_contexts_against_oracle():
+    # the decode chain (primed indexer, selection finished inside the MLA attention) on
+    # sequences of different lengths: a full row, two ragged ones (indexer chunks partly
+    # past the query position, a partial last tile) and one shorter than K (every
+    # position selected, the rest of the index row padding)
+    cfg = config(2, B=4, N=65536)
+    inp = make_inputs(cfg)
+    inp["ctx_len"] = np.array([65536, 40001, 8193, 1500], dtype=np.int32)
+    d = upload(inp)
+    sc, idx, out, lse = L.lsa_index_select_attend(d["qI"], d["w"], d["kI"], cfg.K, cfg.S, cfg.W, d["q"], d["k"],
+                                                  d["v"], cfg.tau, k_scale=d["kI_scale"], ctx_len=d["ctx_len"])
+    torch.cuda.synchronize()
+    g_idx = idx.cpu().numpy()
+    assert np.all(g_idx[3, 0, 1500:] == -1) and np.array_equal(g_idx[3, 0, :1500], np.arange(1500))
+    ora = O.reference_step(inp)
+    _check_rows(cfg, inp, ora, g_idx, out.float().cpu().numpy(), lse.cpu().numpy(), "c2 ragged")
 
 
 def test_c5_chained_call_full_size():
