@@ -669,11 +669,12 @@ def main():
         torch.cuda.synchronize()
         return sum(a.elapsed_time(b) for a, b in ev) / n
 
-    def per_dispatch(fn, n, warm):
-        """Mean duration of the token-indexer kernel of one call, from events that its own
-        dispatch records (lsa_index_launch_events): the kernel's execution alone, as a
-        kernel-trace profiler reports it (an event pair around the call also counts the
-        launch latency)."""
+    def per_dispatch(fn, n, warm, hook=None):
+        """Mean duration of the token-indexer kernel of one call (or, hook =
+        L.lsa_attend_launch_events, of the attention and its merge), from events that the
+        kernels' own dispatches record: the execution alone, as a kernel-trace profiler
+        reports it (an event pair around the call also counts the launch latency)."""
+        hook = hook or L.lsa_index_launch_events
         for i in range(warm):
             fn(i % R)
         ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(n)]
@@ -682,9 +683,9 @@ def main():
             b.record(stream)
         torch.cuda.synchronize()
         for i in range(n):
-            L.lsa_index_launch_events(ev[i][0], ev[i][1])
+            hook(ev[i][0], ev[i][1])
             fn(i % R)
-        L.lsa_index_launch_events(None, None)
+        hook(None, None)
         torch.cuda.synchronize()
         return sum(a.elapsed_time(b) for a, b in ev) / n
 
@@ -712,7 +713,8 @@ def main():
     ms_index = per_dispatch(c_index, args.steps, args.warmup)
     L.lsa_workspace_clear(ws_sel)
     ms_select = per_launch(lambda r: (c_index(r), c_select(r)), args.steps, args.warmup) - ms_index_call
-    ms_attend = per_launch(c_attend, args.steps, args.warmup)
+    ms_attend_call = per_launch(c_attend, args.steps, args.warmup)
+    ms_attend = per_dispatch(c_attend, args.steps, args.warmup, L.lsa_attend_launch_events)
 
     # HIP graphs: one captured step per replica and way (a way whose calls cannot be
     # captured is left out and named in extra)
@@ -780,7 +782,7 @@ def main():
                   "step_frac_of_peak": step_bytes / (ms * 1e-3) / 1e9 / PEAK_HBM_GBS,
                   "ms_per_step_plain": ms_plain, "ms_per_step_graph": ms_graph, "graph_errors": graph_errors,
                   "ms_index": ms_index, "ms_index_event_pair": ms_index_call,
-                  "ms_select": ms_select, "ms_attend": ms_attend,
+                  "ms_select": ms_select, "ms_attend": ms_attend, "ms_attend_event_pair": ms_attend_call,
                   "index_gbs": idx_b / (ms_index * 1e-3) / 1e9,
                   "kv_gather_gbs": gat_b / (ms_attend * 1e-3) / 1e9,
                   "attend_traffic": pmc_attend_traffic(),

@@ -498,6 +498,17 @@ int32_t lsa_cache_append(const lsa_cache_append_desc *desc, void *stream);
  * kernel (BLOCKS mode, errors) leave it set. Returns LSA_OK. */
 int32_t lsa_index_launch_events(void *start_event, void *stop_event);
 
+/* Measurement hook (not part of the method), as lsa_index_launch_events for the
+ * attention: the next lsa_attend, lsa_attend_noalloc or lsa_select_attend call on the
+ * calling host thread records the start of its attention kernel's dispatch in
+ * start_event and the end of its last kernel's dispatch (the split merge, or the
+ * attention itself when it runs one split) in stop_event, so the elapsed time spans the
+ * attention and its merge without the launch latency. The hook applies to one call and is
+ * then cleared; NULL, NULL clears it; calls that fail before launching leave it set. In
+ * lsa_select_attend the selection kernels that run before the attention are not in the
+ * span. Returns LSA_OK. */
+int32_t lsa_attend_launch_events(void *start_event, void *stop_event);
+
 /* Zero-fill `bytes` of device memory at `ptr` with a fill kernel (for workspaces). */
 int32_t lsa_workspace_clear(void *ptr, size_t bytes, void *stream);
 

@@ -18,7 +18,8 @@ __all__ = ["lib", "LSAError", "lsa_index", "lsa_block_means", "lsa_select", "lsa
            "LSA_BF16", "LSA_FP8_E4M3FN", "LSA_F32", "LSA_INDEX_TOKENS", "LSA_INDEX_BLOCKS",
            "LSA_WS_UNKNOWN", "LSA_WS_CLEAN", "LSA_WS_PRIMED", "lsa_select_attend", "lsa_index_select_attend",
            "lsa_cache_append", "lsa_attend_backward", "lsa_attend_noalloc", "lsa_index_target", "IndexTargetDesc", "IndexDesc", "BlockMeansDesc", "SelectDesc", "AttendDesc",
-           "AttendBwdDesc", "CacheAppendDesc", "STATUS", "lsa_index_launch_events"]
+           "AttendBwdDesc", "CacheAppendDesc", "STATUS", "lsa_index_launch_events",
+           "lsa_attend_launch_events"]
 
 HERE = os.path.dirname(os.path.abspath(__file__))
 # LSA_LIB_PATH selects another build of the same library (the host-sanitizer build that a
@@ -138,6 +139,8 @@ def lib():
         L.lsa_workspace_clear.restype = c_int32
         L.lsa_index_launch_events.argtypes = [c_void_p, c_void_p]
         L.lsa_index_launch_events.restype = c_int32
+        L.lsa_attend_launch_events.argtypes = [c_void_p, c_void_p]
+        L.lsa_attend_launch_events.restype = c_int32
         L.lsa_status_str.argtypes = [c_int32]
         L.lsa_status_str.restype = ctypes.c_char_p
         L.lsa_last_error.argtypes = []
@@ -192,20 +195,27 @@ def _workspace(kind: str, nbytes: int, device, shape_key=()):
     return ent
 
 
+def _event_handle(ev):
+    import torch
+    if ev is None:
+        return None
+    if not ev.cuda_event:  # torch creates the event on its first record
+        ev.record(torch.cuda.current_stream())
+    return ev.cuda_event
+
+
 def lsa_index_launch_events(start=None, stop=None):
     """The next token-indexer kernel launch (lsa_index, lsa_index_select) records its own
     start and end into these torch.cuda.Event objects (enable_timing=True); the events are
     created here if they have not been recorded yet. None, None clears the hook."""
-    import torch
+    _check("lsa_index_launch_events", lib().lsa_index_launch_events(_event_handle(start), _event_handle(stop)))
 
-    def handle(ev):
-        if ev is None:
-            return None
-        if not ev.cuda_event:  # torch creates the event on its first record
-            ev.record(torch.cuda.current_stream())
-        return ev.cuda_event
 
-    _check("lsa_index_launch_events", lib().lsa_index_launch_events(handle(start), handle(stop)))
+def lsa_attend_launch_events(start=None, stop=None):
+    """The next attention call (lsa_attend, lsa_attend_noalloc, lsa_select_attend) records
+    the start of its attention kernel and the end of its last kernel (the split merge)
+    into these torch.cuda.Event objects, as lsa_index_launch_events does for the indexer."""
+    _check("lsa_attend_launch_events", lib().lsa_attend_launch_events(_event_handle(start), _event_handle(stop)))
 
 
 def lsa_workspace_clear(buf, stream=None):

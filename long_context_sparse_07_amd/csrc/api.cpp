@@ -151,6 +151,11 @@ int32_t lsa_index_launch_events(void *start_event, void *stop_event) {
     return LSA_OK;
 }
 
+int32_t lsa_attend_launch_events(void *start_event, void *stop_event) {
+    lsa::set_attend_launch_events(reinterpret_cast<hipEvent_t>(start_event), reinterpret_cast<hipEvent_t>(stop_event));
+    return LSA_OK;
+}
+
 int32_t lsa_index(const lsa_index_desc *d, void *stream) {
     if (!d) return fail(LSA_E_NULL, "lsa_index: desc is NULL");
     if (!d->q || !d->w || !d->k || !d->scores) return fail(LSA_E_NULL, "lsa_index: q, w, k and scores are required");

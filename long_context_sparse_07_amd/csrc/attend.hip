@@ -26,6 +26,8 @@
 // memory in between.
 #include <mutex>
 
+#include <hip/hip_ext.h>
+
 #include "select_core.cuh"
 
 namespace lsa {
@@ -1056,6 +1058,23 @@ __global__ __launch_bounds__(kCombT) void attend_combine_kernel(AttendArgs a, co
     }
 }
 
+// Measurement hook (lsa_attend_launch_events): the next attention call on this host thread
+// records its start from the dispatch of its first kernel and its end from that of its
+// last one (the merge, or the attention itself with one split).
+thread_local hipEvent_t t_att_start = nullptr, t_att_stop = nullptr;
+
+#define LSA_LAUNCH_ATT(LAST, K, GRID, BLOCK, LDS, S, ...)                                                   \
+    do {                                                                                                     \
+        if (t_att_start || t_att_stop) {                                                                     \
+            hipEvent_t e0_ = t_att_start, e1_ = (LAST) ? t_att_stop : nullptr;                               \
+            t_att_start = nullptr;                                                                           \
+            if (LAST) t_att_stop = nullptr;                                                                  \
+            hipExtLaunchKernelGGL(K, GRID, BLOCK, (uint32_t)(LDS), S, e0_, e1_, 0, __VA_ARGS__);             \
+        } else {                                                                                             \
+            hipLaunchKernelGGL(K, GRID, BLOCK, LDS, S, __VA_ARGS__);                                         \
+        }                                                                                                    \
+    } while (0)
+
 // The merge launch: one head a workgroup for 128-wide rows (16 split groups), two for
 // 512-wide rows (2 split groups each).
 #ifndef LSA_COMBINE_HEADS_512
@@ -1065,7 +1084,7 @@ template <int DV, bool OUTF32>
 hipError_t launch_combine(const AttendArgs &a, const uint16_t *po, const float *pml, int S, hipStream_t s) {
     constexpr int HPW = DV >= 512 ? LSA_COMBINE_HEADS_512 : 1;
     dim3 cgrid((a.Hq + HPW - 1) / HPW, a.B * a.T, a.L);
-    hipLaunchKernelGGL((attend_combine_kernel<DV, HPW, OUTF32>), cgrid, dim3(kCombT), 0, s, a, po, pml, S);
+    LSA_LAUNCH_ATT(true, (attend_combine_kernel<DV, HPW, OUTF32>), cgrid, dim3(kCombT), 0, s, a, po, pml, S);
     return hipGetLastError();
 }
 
@@ -1107,12 +1126,12 @@ hipError_t launch_t(const AttendArgs &a, void *ws, hipStream_t s, const FuseArgs
             static_assert(ring >= fixed + sel::kSliceTiesFirst * 8, "tile ring too small for the resolve");
             f.bits_lds = ring >= fixed + bb + (size_t)sel::kSliceTiesFirst * 8;
             f.tl = (int)(((ring - fixed - (f.bits_lds ? bb : 0)) / 8) & ~(size_t)1);
-            hipLaunchKernelGGL((attend_kernel<DQK, DV, HW, MLA, OUTF32, true, NSTC>), grid, dim3(64 * HW), lds, s, a, po,
-                               pml, R, f);
+            LSA_LAUNCH_ATT(S == 1, (attend_kernel<DQK, DV, HW, MLA, OUTF32, true, NSTC>), grid, dim3(64 * HW), lds, s,
+                           a, po, pml, R, f);
         }
     } else {
-        hipLaunchKernelGGL((attend_kernel<DQK, DV, HW, MLA, OUTF32, false, NSTC>), grid, dim3(64 * HW), lds, s, a, po,
-                           pml, R, FuseArgs{});
+        LSA_LAUNCH_ATT(S == 1, (attend_kernel<DQK, DV, HW, MLA, OUTF32, false, NSTC>), grid, dim3(64 * HW), lds, s, a,
+                       po, pml, R, FuseArgs{});
     }
     hipError_t e = hipGetLastError();
     if (e != hipSuccess || S == 1) return e;
@@ -1142,10 +1161,10 @@ hipError_t launch_mla(const AttendArgs &a, void *ws, hipStream_t s, const FuseAr
         f.bits_lds = ring >= fixed + bb + (size_t)sel::kSliceTiesFirst * 8;
         f.tl = (int)(((ring - fixed - (f.bits_lds ? bb : 0)) / 8) & ~(size_t)1);
         const size_t lds = kMLdsFixed + (size_t)R * sizeof(int);
-        hipLaunchKernelGGL((attend_mla_kernel<OUTF32, true>), grid, dim3(256), lds, s, a, po, pml, R, HB, f);
+        LSA_LAUNCH_ATT(S == 1, (attend_mla_kernel<OUTF32, true>), grid, dim3(256), lds, s, a, po, pml, R, HB, f);
     } else {
-        hipLaunchKernelGGL((attend_mla_kernel<OUTF32, false>), grid, dim3(256), (size_t)kMLdsFixed, s, a, po, pml, R, HB,
-                           FuseArgs{});
+        LSA_LAUNCH_ATT(S == 1, (attend_mla_kernel<OUTF32, false>), grid, dim3(256), (size_t)kMLdsFixed, s, a, po, pml,
+                       R, HB, FuseArgs{});
     }
     hipError_t e = hipGetLastError();
     if (e != hipSuccess || S == 1) return e;
@@ -1190,6 +1209,11 @@ bool attend_supported(int d_qk, int d_v, int g) {
     // one wave per 16 query heads of a KV head: 1, 2 or 4 waves per workgroup
     if (g < 1 || g > 64 || (g + 15) / 16 == 3) return false;
     return (d_qk == 128 && d_v == 128) || (d_qk == 576 && d_v == 512);
+}
+
+void set_attend_launch_events(hipEvent_t start, hipEvent_t stop) {
+    t_att_start = start;
+    t_att_stop = stop;
 }
 
 int attend_default_splits(const AttendArgs &a) {

@@ -54,6 +54,9 @@ hipError_t launch_index_blocks(const IndexBlocksArgs &a, hipStream_t s);
 // The next launch_index_tokens kernel launch on this host thread records its start and end
 // into these events (taken from the dispatch); null, null: none.
 void set_index_launch_events(hipEvent_t start, hipEvent_t stop);
+// The next attention call's first kernel launch on this host thread records its start
+// into `start`, its last kernel launch its end into `stop` (taken from the dispatches).
+void set_attend_launch_events(hipEvent_t start, hipEvent_t stop);
 
 struct BlockMeansArgs {
     int B, N, D;

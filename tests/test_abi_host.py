@@ -267,7 +267,8 @@ def test_status_strings():
     assert lib.lsa_workspace_clear(None, 16, None) == -1
     assert lib.lsa_workspace_clear(FAKE + 4, 16, None) == -5
     assert lib.lsa_workspace_clear(None, 0, None) == 0
-    assert lib.lsa_index_launch_events(None, None) == 0  # the measurement hook, cleared
+    assert lib.lsa_index_launch_events(None, None) == 0  # the measurement hooks, cleared
+    assert lib.lsa_attend_launch_events(None, None) == 0
 
 
 def _bwd_desc(**kw):

@@ -237,3 +237,24 @@ def test_index_launch_events_time_one_indexer_launch():
     L.lsa_index(d["qI"], d["w"], d["kI"], **kw)
     torch.cuda.synchronize()
     assert e0.elapsed_time(e1) == ms
+
+
+@pytest.mark.parametrize("splits", [0, 1])
+def test_attend_launch_events_time_one_call(splits):
+    # the attention's measurement hook: the next call's first kernel records the start, its
+    # last (the merge, or the attention itself with one split) the end; same output as a
+    # plain call, and the hook is used up by that call
+    cfg = config(2, B=2, N=8192, K=512, S=32, W=128)
+    d = upload(make_inputs(cfg))
+    idx = L.lsa_select(L.lsa_index(d["qI"], d["w"], d["kI"], k_scale=d["kI_scale"]), cfg.K, cfg.S, cfg.W)
+    out0, lse0 = L.lsa_attend(d["q"], d["k"], d["v"], idx, cfg.tau, n_splits=splits)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    L.lsa_attend_launch_events(e0, e1)
+    out1, lse1 = L.lsa_attend(d["q"], d["k"], d["v"], idx, cfg.tau, n_splits=splits)
+    torch.cuda.synchronize()
+    assert torch.equal(out1.view(torch.int16), out0.view(torch.int16)) and torch.equal(lse1, lse0)
+    ms = e0.elapsed_time(e1)
+    assert 0.0 < ms < 50.0
+    L.lsa_attend(d["q"], d["k"], d["v"], idx, cfg.tau, n_splits=splits)
+    torch.cuda.synchronize()
+    assert e0.elapsed_time(e1) == ms
