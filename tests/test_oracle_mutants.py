@@ -24,6 +24,9 @@ def _run_pins(names):
                         "test_fine_given_all_eligible_kept_equals_flat"):
                 for seed in range(4):
                     fn(seed)
+            elif name == "test_attention_backward_matches_autograd":
+                fn(6, 1, 24, 16, True)  # the MLA case (one latent row is both K and V)
+                fn(8, 2, 16, 16, False)
             else:
                 fn()
         except (AssertionError, ValueError, IndexError):
@@ -42,7 +45,12 @@ ALL = ["test_golden_hand_worked_flat_and_hi", "test_indexer_single_head_is_relu_
        "test_attention_backward_finite_differences", "test_attention_backward_closed_forms",
        "test_query_positions_hand_worked", "test_reference_step_positions_are_causal_prefixes",
        "test_reference_step_mla_one_selected_row_is_its_value_prefix", "test_reference_step_mla_dense_matches_sdpa",
-       "test_fine_given_all_eligible_kept_equals_flat", "test_fine_given_kept_hand_worked"]
+       "test_fine_given_all_eligible_kept_equals_flat", "test_fine_given_kept_hand_worked",
+       "test_e4m3fn_encode_round_trips_every_finite_code", "test_e4m3fn_encode_ties_to_even_and_saturation",
+       "test_quantize_key_rows_scale_and_extremes", "test_cache_append_positions_rows_and_completed_blocks",
+       "test_hi_recovers_planted_blocks", "test_attention_backward_matches_autograd",
+       "test_shared_selection_rows_worked_example", "test_indexer_target_is_head_mean_of_attention",
+       "test_indexer_kl_zero_minimum_and_finite_differences", "test_hi_candidates_hand_worked"]
 
 
 def _no_relu(q, w, keys, p):
@@ -161,6 +169,96 @@ def _fine_block_offset(q, w, keys, kept, p, K, S, W, Bs):
     return _real_fine(q, w, keys, np.where(kept >= 0, kept + 1, kept), p, K, S, W, Bs)
 
 
+_real_table = O.decode_e4m3fn
+
+
+def _e4m3_encode_truncate(x):
+    # magnitudes rounded toward zero instead of to the nearest code
+    x = np.asarray(x, dtype=np.float64)
+    table = _real_table(np.arange(0x7F, dtype=np.uint8))
+    a = np.minimum(np.abs(x), table[-1])
+    code = np.clip(np.searchsorted(table, a, side="right") - 1, 0, 0x7E).astype(np.uint8)
+    return code | (np.signbit(x).astype(np.uint8) << np.uint8(7))
+
+
+_real_encode = O.encode_e4m3fn
+
+
+def _quantize_scale_240(k32):
+    # the scale taken against 240 (the e4m3fnuz maximum) instead of 448
+    k32 = np.asarray(k32, dtype=np.float32)
+    scale = np.maximum(np.max(np.abs(k32), axis=-1), np.float32(1e-12)) / np.float32(240.0)
+    y = np.clip(k32 / scale[..., None], np.float32(-448.0), np.float32(448.0))
+    return _real_encode(y), scale.astype(np.float32)
+
+
+_real_append = O.cache_append
+
+
+def _append_one_late(caches, k_new32, rows_new, pos0, fp8):
+    # token t written at pos0 + t + 1
+    return _real_append(caches, k_new32, rows_new, np.asarray(pos0) + 1, fp8)
+
+
+def _completed_first_row(written, Bs, n_blocks):
+    # a block counted complete when its first row is written
+    return sorted({(b, s // Bs) for b, s in written if s % Bs == 0 and s // Bs < n_blocks})
+
+
+_real_keep = O.keep_blocks
+
+
+def _keep_one_fewer(c, n_keep):
+    # one block fewer than n_keep kept (the last one dropped)
+    kept = _real_keep(c, n_keep)
+    n = int(np.count_nonzero(kept >= 0))
+    if n:
+        kept = kept.copy()
+        kept[n - 1] = -1
+    return kept
+
+
+_real_hi_cand = O.hi_candidates
+
+
+def _hi_cand_no_tail(p, S, W, Bs, kept):
+    # the incomplete visible block's candidates left out
+    c = _real_hi_cand(p, S, W, Bs, kept)
+    return c[c < ((p + 1) // Bs) * Bs]
+
+
+def _mla_grad_without_dv(dK, dV):
+    # the value part of the latent row's gradient dropped
+    return dK.copy()
+
+
+def _shared_rows_strict(idx_row, ctx, T):
+    # token t keeps only the entries before its own position
+    row = np.asarray(idx_row, dtype=np.int64)
+    out = np.full((T, row.size), -1, dtype=np.int64)
+    for t in range(T):
+        keep = row[(row >= 0) & (row < ctx - T + t)]
+        out[t, : keep.size] = keep
+    return out
+
+
+_real_target = O.indexer_target
+
+
+def _target_head_sum(q, k_rows, idx, tau, lse):
+    # summed over the heads instead of averaged
+    return _real_target(q, k_rows, idx, tau, lse) * q.shape[0]
+
+
+_real_kl = O.indexer_kl
+
+
+def _kl_grad_sign(target, scores_sel, valid):
+    # gradient target - u instead of u - target
+    loss, grad = _real_kl(target, scores_sel, valid)
+    return loss, -grad
+
+
 MUTANTS = [
     ("indexer_scores", _no_relu),
     ("indexer_scores", _max_heads),
@@ -178,6 +276,16 @@ MUTANTS = [
     ("query_positions", _positions_reversed),
     ("mla_kv", _mla_value_last_columns),
     ("select_fine_given_kept", _fine_block_offset),
+    ("encode_e4m3fn", _e4m3_encode_truncate),
+    ("quantize_key_rows", _quantize_scale_240),
+    ("cache_append", _append_one_late),
+    ("completed_blocks", _completed_first_row),
+    ("keep_blocks", _keep_one_fewer),
+    ("hi_candidates", _hi_cand_no_tail),
+    ("mla_row_grad", _mla_grad_without_dv),
+    ("shared_selection_rows", _shared_rows_strict),
+    ("indexer_target", _target_head_sum),
+    ("indexer_kl", _kl_grad_sign),
 ]
 
 

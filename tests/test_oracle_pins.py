@@ -776,3 +776,17 @@ def test_fine_given_kept_hand_worked():
         kept = np.array(c["kept"] + [-1], dtype=np.int64)
         idx, _, _ = O.select_fine_given_kept(q, w, keys, kept, c["p"], c["K"], c["S"], c["W"], c["Bs"])
         assert idx.tolist() == c["idx"], c["why"]
+
+
+def test_hi_candidates_hand_worked():
+    # Reading R9 on paper: the fine candidates are the positions of the kept blocks and of
+    # the incomplete visible block, at or before p, minus the forced set.
+    # p = 10, blocks of 4, sink 1, window 1: forced {0, 10}; kept block 0 gives 0..3, the
+    # incomplete block (positions 8..11, visible up to 10) gives 8..10.
+    assert O.hi_candidates(10, 1, 1, 4, np.array([0, -1])).tolist() == [1, 2, 3, 8, 9]
+    # kept blocks 2 and 0 (any order), p = 13, sink 2, window 3: forced {0, 1, 11, 12, 13};
+    # blocks 0 and 2 give 0..3 and 8..11, the incomplete block 12..13 is all forced.
+    assert O.hi_candidates(13, 2, 3, 4, np.array([2, 0])).tolist() == [2, 3, 8, 9, 10]
+    # positions past p are dropped: block 3 covers 12..15 and p = 12 leaves only 12, which
+    # the window forces
+    assert O.hi_candidates(12, 0, 1, 4, np.array([3])).tolist() == []
