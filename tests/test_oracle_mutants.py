@@ -50,7 +50,8 @@ ALL = ["test_golden_hand_worked_flat_and_hi", "test_indexer_single_head_is_relu_
        "test_quantize_key_rows_scale_and_extremes", "test_cache_append_positions_rows_and_completed_blocks",
        "test_hi_recovers_planted_blocks", "test_attention_backward_matches_autograd",
        "test_shared_selection_rows_worked_example", "test_indexer_target_is_head_mean_of_attention",
-       "test_indexer_kl_zero_minimum_and_finite_differences", "test_hi_candidates_hand_worked"]
+       "test_indexer_kl_zero_minimum_and_finite_differences", "test_hi_candidates_hand_worked",
+       "test_bf16_decode_matches_torch", "test_fp8_dequant_scale_multiplies"]
 
 
 def _no_relu(q, w, keys, p):
@@ -259,6 +260,34 @@ def _kl_grad_sign(target, scores_sel, valid):
     return loss, -grad
 
 
+def _block_means_shifted(keys, Bs, n_blocks):
+    # the mean of each block taken one row late
+    k = np.vstack([keys[1:], keys[-1:]])
+    return k[: n_blocks * Bs].reshape(n_blocks, Bs, keys.shape[1]).mean(axis=1)
+
+
+_real_keys = O.index_keys_f64
+
+
+def _keys_without_scale(kI, kI_scale):
+    # fp8 codes used without their per-token scale
+    return _real_keys(kI, None if kI_scale is None else np.ones_like(np.asarray(kI_scale)))
+
+
+def _bf16_low_half(bits):
+    # the bits placed one position too low in the fp32 word
+    u = np.asarray(bits, dtype=np.uint16).astype(np.uint32) << np.uint32(15)
+    return u.view(np.float32).astype(np.float64)
+
+
+def _pad_with_zero(sel, K):
+    # padding with position 0 instead of -1
+    out = np.zeros(K, dtype=np.int64)
+    s = np.sort(np.asarray(sel, dtype=np.int64))
+    out[: s.size] = s
+    return out
+
+
 MUTANTS = [
     ("indexer_scores", _no_relu),
     ("indexer_scores", _max_heads),
@@ -286,6 +315,10 @@ MUTANTS = [
     ("shared_selection_rows", _shared_rows_strict),
     ("indexer_target", _target_head_sum),
     ("indexer_kl", _kl_grad_sign),
+    ("block_means", _block_means_shifted),
+    ("index_keys_f64", _keys_without_scale),
+    ("decode_bf16", _bf16_low_half),
+    ("pad_sorted", _pad_with_zero),
 ]
 
 
