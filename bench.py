@@ -272,11 +272,14 @@ def hi_step(cfg, d):
     idx = torch.empty((B, T, cfg.K), dtype=torch.int32, device="cuda")
     out = torch.empty((1, B, T, cfg.Hq, cfg.d_v), dtype=torch.bfloat16, device="cuda")
     lse = torch.empty((1, B, T, cfg.Hq), dtype=torch.float32, device="cuda")
+    # the block scores prime the block selection (every selection leaves the workspace clean)
+    ws = torch.zeros(L.lsa_select_workspace_bytes(cs, cfg.n_keep, causal=False), dtype=torch.uint8, device="cuda")
 
     def fn():
         L.lsa_index(d["qI"], d["w"], kbar, mode=L.LSA_INDEX_BLOCKS, N=cfg.N, ctx_len=d["ctx"],
-                    block_size=cfg.Bs, sink=cfg.S, window=cfg.W, scores=cs)
-        L.lsa_select(cs, cfg.n_keep, 0, 0, causal=False, idx=kept)
+                    block_size=cfg.Bs, sink=cfg.S, window=cfg.W, scores=cs, select_ws=ws,
+                    select_ws_state=L.LSA_WS_CLEAN)
+        L.lsa_select(cs, cfg.n_keep, 0, 0, causal=False, idx=kept, workspace=ws, workspace_state=L.LSA_WS_PRIMED)
         L.lsa_index_select(d["qI"], d["w"], d["kI"], cfg.K, cfg.S, cfg.W, k_scale=d["ks"], ctx_len=d["ctx"],
                            kept=kept, block_size=cfg.Bs, scores=fs, idx=idx)
         L.lsa_attend(d["q"], d["k"], d["v"], idx, cfg.tau, out=out, lse=lse)

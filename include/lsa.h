@@ -103,7 +103,7 @@ extern "C" {
  *   block_size - 1 <= p) and holds at least one position outside the forced set
  *   sink [0,sink) U window [p-window+1, p]; -inf for every other block (reading R9).
  *
- * Priming a selection (TOKENS only): with select_ws != NULL, lsa_index also records in
+ * Priming a selection: with select_ws != NULL, lsa_index also records in
  *   select_ws what the selection would otherwise compute in a first pass over these
  *   scores (per query token, the distribution of the candidate scores: finite scores at
  *   visible positions outside sink [0,sink) and window [p-window+1, p]). The next
@@ -117,6 +117,12 @@ extern "C" {
  *   at most 4096 columns need no priming (lsa_select ranks them in one launch from the
  *   scores alone): for them lsa_index only writes the scores, and the protocol above
  *   still holds.
+ *   BLOCKS mode primes the coarse HI block selection the same way ("LongCat-Flash-Lite-
+ *   Sparse" summary, Technical features, third bullet: coarse blocks first): the
+ *   recorded distribution is that of every finite block score, and the next lsa_select
+ *   reads these scores with K = the number of blocks to keep, sink = window = 0,
+ *   causal = 0, no kept map and workspace_state = LSA_WS_PRIMED (select_ws_bytes: the
+ *   lsa_select_workspace_bytes() of that call).
  *
  * Shapes: q bf16 [B][T][H][D]; w fp32 [B][T][H]; k per k_dtype: bf16 or fp8 [B][N][D]
  * (TOKENS) or fp32 [B][n_blocks][D] (BLOCKS); k_scale fp32 [B][N] (fp8 keys only);
@@ -144,7 +150,7 @@ typedef struct lsa_index_desc {
     int32_t sink, window;    /* BLOCKS: forced set used for block eligibility;
                                 TOKENS with select_ws: the forced set of the selection */
     float *scores;           /* fp32 [B][T][n_out], written in full */
-    void *select_ws;         /* optional (TOKENS): workspace of the lsa_select that reads scores */
+    void *select_ws;         /* optional: workspace of the lsa_select that reads scores */
     size_t select_ws_bytes;
     int32_t select_ws_state; /* LSA_WS_UNKNOWN or LSA_WS_CLEAN: state of select_ws on entry */
     int32_t q_dtype;         /* TOKENS: 0 or LSA_BF16 (bf16 contraction), LSA_FP8_E4M3FN (reading R27) */

@@ -214,6 +214,24 @@ int32_t lsa_index(const lsa_index_desc *d, void *stream) {
         a.sink = d->sink;
         a.window = d->window;
         a.scores = d->scores;
+        if (d->select_ws) {  // priming the block selection (no causal mask, no forced set)
+            if (d->select_ws_state != LSA_WS_UNKNOWN && d->select_ws_state != LSA_WS_CLEAN)
+                return fail(LSA_E_SHAPE, "lsa_index: select_ws_state must be LSA_WS_UNKNOWN or LSA_WS_CLEAN");
+            if ((int64_t)d->B * d->T > kMaxGridY) return fail(LSA_E_UNSUPPORTED, "lsa_index: B*T too large to prime");
+            const size_t need = lsa::select_workspace_bytes(d->B * d->T, d->n_blocks, false);
+            if (d->select_ws_bytes < need)
+                return fail(LSA_E_WORKSPACE, "lsa_index: select_ws of %zu bytes needed, %zu given", need, d->select_ws_bytes);
+            if ((reinterpret_cast<uintptr_t>(d->select_ws) & 255u) != 0)
+                return fail(LSA_E_ALIGN, "lsa_index: select_ws not 256-byte aligned");
+            // rows the one-launch selection takes need no histogram (it leaves the workspace clean)
+            if (!lsa::select_small(d->n_blocks)) {
+                if (d->select_ws_state != LSA_WS_CLEAN) {
+                    const hipError_t e = lsa::launch_clear(d->select_ws, lsa::select_zero_bytes(d->B * d->T), s);
+                    if (e != hipSuccess) return hip_status(e, "lsa_index");
+                }
+                a.sel_hist = reinterpret_cast<uint32_t *>(d->select_ws);
+            }
+        }
         return hip_status(lsa::launch_index_blocks(a, s), "lsa_index");
     }
     return fail(LSA_E_SHAPE, "lsa_index: unknown mode %d", d->mode);
@@ -257,8 +275,9 @@ static int32_t select_check(const lsa_select_desc *d, lsa::SelectArgs &a) {
     if (d->workspace_state != LSA_WS_UNKNOWN && d->workspace_state != LSA_WS_CLEAN &&
         d->workspace_state != LSA_WS_PRIMED)
         return fail(LSA_E_SHAPE, "lsa_select: unknown workspace_state %d", d->workspace_state);
-    if (d->workspace_state == LSA_WS_PRIMED && !d->causal)
-        return fail(LSA_E_SHAPE, "lsa_select: a primed workspace needs causal = 1");
+    // causal = 0 reads a workspace primed by the BLOCKS indexer (every finite score counted)
+    if (d->workspace_state == LSA_WS_PRIMED && !d->causal && d->kept)
+        return fail(LSA_E_SHAPE, "lsa_select: a primed workspace with causal = 0 takes no kept map");
     if (!d->causal && (d->sink || d->window))
         return fail(LSA_E_BUDGET, "lsa_select: sink and window need causal = 1");
     if (d->kept && (d->n_keep < 1 || d->block_size < 1 || (int64_t)d->n_keep * d->block_size < d->n_cols))

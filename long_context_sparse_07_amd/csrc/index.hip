@@ -691,8 +691,14 @@ __global__ __launch_bounds__(PRE ? kThreads : 2 * kThreads) void index_tokens_ke
 template <int D>
 __global__ __launch_bounds__(256) void index_blocks_kernel(IndexBlocksArgs a) {
     extern __shared__ float qs[];  // [H][D]
+    // sel_hist (priming a selection without causal mask or forced set): this workgroup's
+    // count of finite scores per first-level bin, added to the row's histogram at the end
+    __shared__ uint32_t shist[kSelBins];
+    const bool prime = a.sel_hist != nullptr;
     const int b = blockIdx.z, t = blockIdx.y;
     const int H = a.H, T = a.T;
+    if (prime)
+        for (int i = threadIdx.x; i < kSelBins; i += blockDim.x) shist[i] = 0;
     const int64_t qoff = ((int64_t)b * T + t) * H * D;
     for (int e = threadIdx.x; e < H * D; e += blockDim.x) {
         uint16_t bits = a.q[qoff + e];
@@ -710,14 +716,14 @@ __global__ __launch_bounds__(256) void index_blocks_kernel(IndexBlocksArgs a) {
         }
     }
     __syncthreads();
-    if (!in) return;
+    if (!in && !prime) return;
     int ctx = a.ctx_len ? a.ctx_len[b] : a.N;
     ctx = min(max(ctx, 0), a.N);
     const int p = ctx - T + t;
     const int Bs = a.block_size;
     // eligibility: complete, visible, and at least one non-forced position (reading R9)
     const int64_t lo = (int64_t)j * Bs, hi = lo + Bs - 1;  // inclusive
-    bool ok = hi <= p;
+    bool ok = in && hi <= p;
     if (ok) {
         int64_t nf = 0;
         const int64_t s_hi = min((int64_t)a.sink, (int64_t)p + 1) - 1;  // sink [0, s_hi]
@@ -743,7 +749,16 @@ __global__ __launch_bounds__(256) void index_blocks_kernel(IndexBlocksArgs a) {
             best = h == 0 ? v : fmaxf(best, v);
         }
     }
-    a.scores[((int64_t)b * T + t) * a.n_blocks + j] = best;
+    if (in) a.scores[((int64_t)b * T + t) * a.n_blocks + j] = best;
+    if (prime) {
+        if (in && best > kNegInf) atomicAdd(&shist[order_key(best) >> kSelShift], 1u);
+        __syncthreads();
+        uint32_t *g = a.sel_hist + ((int64_t)b * T + t) * kSelBins;
+        for (int i = threadIdx.x; i < kSelBins; i += blockDim.x) {
+            const uint32_t v = shist[i];
+            if (v) atomicAdd(&g[i], v);
+        }
+    }
 }
 
 // ---------------------------------------------------------------------------- block means

@@ -49,6 +49,7 @@ struct IndexBlocksArgs {
     const float *kbar;      // [B][n_blocks][D]
     int n_blocks, block_size, sink, window;
     float *scores;          // [B][T][n_blocks]
+    uint32_t *sel_hist;     // optional: per (b, t) the first-level histogram of the finite scores
 };
 hipError_t launch_index_blocks(const IndexBlocksArgs &a, hipStream_t s);
 // The next launch_index_tokens kernel launch on this host thread records its start and end

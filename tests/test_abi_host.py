@@ -140,7 +140,9 @@ def test_select_argument_errors(kw, code):
 
 def test_select_workspace_state_errors():
     assert _sel(_select_desc(workspace_state=3)) == -2
-    assert _sel(_select_desc(workspace_state=L.LSA_WS_PRIMED, causal=0, sink=0, window=0)) == -2
+    # causal = 0 with a primed workspace is the BLOCKS indexer's block selection: no kept map
+    assert _sel(_select_desc(workspace_state=L.LSA_WS_PRIMED, causal=0, sink=0, window=0, kept=FAKE, n_keep=16,
+                             block_size=64)) == -2
 
 
 def test_select_workspace_and_pointer_errors():

@@ -175,6 +175,30 @@ def test_primed_hi_fine_selection_equals_plain():
     assert torch.equal(idx2, idx)
 
 
+@pytest.mark.parametrize("B,N,n_keep", [(1, 1048576, 256), (2, 320037, 256), (3, 19200, 32)])
+def test_primed_block_selection_equals_plain(B, N, n_keep):
+    # the BLOCKS indexer primes the coarse block selection (causal = 0, no forced set):
+    # scores and kept lists equal those of the plain calls, from a dirty workspace (cleared
+    # first) and from the clean one the selection leaves; 16384 blocks (the 1M cache),
+    # 5000 (a partial last workgroup of block scores, ragged contexts) and 300 (the
+    # one-launch selection: nothing primed)
+    cfg = config(3, B=B, N=N, n_keep=n_keep)
+    inp = make_inputs(cfg)
+    d = upload(inp)
+    kbar = L.lsa_block_means(d["kI"], cfg.Bs, k_scale=d["kI_scale"])
+    kw = dict(mode=L.LSA_INDEX_BLOCKS, N=cfg.N, ctx_len=d["ctx_len"], block_size=cfg.Bs, sink=cfg.S, window=cfg.W)
+    cs = L.lsa_index(d["qI"], d["w"], kbar, **kw)
+    kept = L.lsa_select(cs, cfg.n_keep, 0, 0, causal=False)
+    nbytes = L.lsa_select_workspace_bytes(cs, cfg.n_keep, causal=False)
+    ws = torch.full((nbytes,), 0xFF, dtype=torch.uint8, device="cuda")
+    for state in (L.LSA_WS_UNKNOWN, L.LSA_WS_CLEAN, L.LSA_WS_CLEAN):
+        cs2 = L.lsa_index(d["qI"], d["w"], kbar, select_ws=ws, select_ws_state=state, **kw)
+        kept2 = L.lsa_select(cs2, cfg.n_keep, 0, 0, causal=False, workspace=ws, workspace_state=L.LSA_WS_PRIMED)
+        torch.cuda.synchronize()
+        assert torch.equal(cs2, cs)
+        assert torch.equal(kept2, kept)
+
+
 def test_priming_clears_a_dirty_workspace():
     cfg = config(2, B=2, N=9000, K=512, S=32, W=128)
     inp = make_inputs(cfg)
